@@ -1,0 +1,45 @@
+"""CPU oracle for lossless draft verification and confidence-scheduled lengths.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package: only the tests, the smoke check of the
+graft entry point and the CPU-baseline leg of the benchmark use it.  The HIP
+library never routes through it and shares no code with it.
+
+It is a plain, slow, fp64 restatement of what the method computes, written
+from the DSpark pages:
+
+  * `verify`        -- rejection-sampling verification with the correction /
+                       bonus token (DSpark paper, §1 and §2.1; appendix
+                       counterexample for a length of zero);
+  * `verify_greedy` -- the greedy (argmax) verification rule;
+  * `schedule`      -- survival products and the budgeted length selector
+                       (DSpark paper, §3.2.2; Algorithm 1 as printed in the
+                       Chinese translation of the paper);
+  * `philox`        -- the counter-based generator the draws come from
+                       (Philox4x64-10, Salmon et al., SC'11).
+
+Every function states the passage it follows.  Pins that tie it to facts
+outside itself live in tests/test_oracle_*.py.
+"""
+
+from .philox import philox4x64_10, uniforms  # noqa: F401
+from .verification import (  # noqa: F401
+    STATUS_BAD_LENGTH,
+    STATUS_BAD_TEMPERATURE,
+    STATUS_BAD_TOKEN,
+    STATUS_BAD_TOPK,
+    STATUS_NONFINITE,
+    FLAG_ACCEPT_WINDOW,
+    FLAG_EMIT_WINDOW,
+    inverse_cdf,
+    kept_mask,
+    log_probs,
+    verify,
+    verify_greedy,
+)
+from .scheduling import (  # noqa: F401
+    survival,
+    schedule,
+    schedule_bruteforce,
+    theta_path,
+)
