@@ -1,0 +1,202 @@
+"""Benchmark: one step = the whole hot path on the confidence-scheduled workload.
+
+Workload (B=256 requests, gamma=16, V=151936, bf16 logits, 2048-token verify
+budget): spec_schedule_lengths picks per-request verify lengths from the
+confidences and the engine cost table, then spec_verify verifies exactly the
+selected prefixes (row statistics, acceptance tests, first rejection,
+correction / appended token).  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line:
+  value      verified draft positions per second (sum of scheduled lengths / step time)
+  roofline   achieved HBM GB/s of the row-streaming kernel (algorithmic bytes of the
+             rows it reads, each once, / its average launch time from HIP events
+             recorded around it on the launch stream), against 8 TB/s
+  cpu_baseline  the CPU oracle (numpy, one thread) on a bounded sample of the same
+             workload, in verified draft positions per second
+
+Two copies of the logits are used alternately so consecutive steps never read
+rows still resident in the 256 MB last-level cache.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="scheduled")
+    p.add_argument("--copies", type=int, default=2)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "stream_kernel_traffic.json"))
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this path runs on one GPU: every GPU box here has one, and the "
+                                   "verification kernels need no collective; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import draft_verification_04_amd as sv
+    import oracle
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    sv.load_library()
+    torch.cuda.synchronize()
+    w = make_workload(args.config, dev)
+    copies = [(w.target, w.draft)]
+    for c in range(1, args.copies):
+        copies.append((w.target.clone(), w.draft.clone()))
+    sps = torch.from_numpy(w.sps).to(dev)
+    B, G, V = w.B, w.gamma, w.V
+    es = w.elem_bytes
+    ws = torch.empty(sv.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+    sch_out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
+                   theta=torch.empty(1, dtype=torch.float64, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    ver_out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+                   accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(idx, events=None):
+        tgt, drf = copies[idx % len(copies)]
+        if w.conf is not None:
+            sv.schedule_lengths(w.conf, sps, w.budget, out=sch_out, stream=stream)
+            L = sch_out["lengths"]
+        else:
+            L = None
+        sv.verify(tgt, drf, w.draft_tokens, L, w.temperature, w.top_k, w.seed, out=ver_out, workspace=ws,
+                  stream=stream, events=events)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    K = args.steps
+    from draft_verification_04_amd.hipevents import HipEvent
+    evs = [(HipEvent(), HipEvent()) for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(K):
+        step(s, evs[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / K
+    ms_stream = float(np.mean([a.elapsed_ms(b) for a, b in evs]))
+
+    L = sch_out["lengths"].cpu().numpy().astype(np.int64) if w.conf is not None else np.full(B, G)
+    positions = int(L.sum())
+    rows = int((2 * L + 1).sum())
+    alg_bytes = rows * V * es
+    achieved = alg_bytes / (ms_stream * 1e-3) / 1e9
+    value = positions / (ms_step * 1e-3)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == args.config and tj.get("kernel_source_sha") == _kernel_sha():
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, oracle, args.cpu_seconds, L)
+
+    line = {
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: B={B} gamma={G} V={V} {w.dtype} logits, "
+                               f"schedule (budget {w.budget} tokens, early stop) + verify of the selected "
+                               f"prefixes",
+                   "B": B, "gamma": G, "V": V, "budget_tokens": w.budget,
+                   "scheduled_positions": positions, "rows_streamed": rows},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "stream_kernel<bf16>", "ms_per_launch": ms_stream,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+        "ms_breakdown": {"stream_kernel": ms_stream, "rest_of_step": ms_step - ms_stream},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("verify.hip", "verify_impl.hpp", "common.hpp", "philox.hpp"):
+        p = os.path.join(ROOT, "draft_verification_04_amd", "csrc", f)
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, oracle, budget_s, L):
+    """Time the oracle on the first requests of the same workload until the budget is spent."""
+    conf = w.conf.cpu().numpy() if w.conf is not None else None
+    t_start = time.perf_counter()
+    if conf is not None:
+        oracle.schedule(conf, w.sps, w.budget)
+    t_sched = time.perf_counter() - t_start
+    done = 0
+    positions = 0
+    t0 = time.perf_counter()
+    chunk = 4
+    while time.perf_counter() - t0 < budget_s and done < w.B:
+        req = list(range(done, min(w.B, done + chunk)))
+        oracle.verify(w.target, w.draft, w.draft_tokens,
+                      None if conf is None else L, w.temperature, w.top_k, w.seed, requests=req)
+        positions += int(L[req].sum())
+        done += len(req)
+    el = time.perf_counter() - t0
+    # the scheduler runs once per step for the whole batch: charge it pro rata
+    el_total = el + t_sched * done / w.B
+    return {"value": positions / el_total, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {w.B} requests ({positions} verified positions) of the same workload, "
+                      f"verify {el:.1f} s + scheduler {t_sched:.2f} s pro rata, numpy fp64 single thread"}
+
+
+if __name__ == "__main__":
+    main()

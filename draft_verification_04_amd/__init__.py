@@ -1,0 +1,244 @@
+"""Python binding of libspecverify: lossless draft verification on MI355X.
+
+A thin ctypes layer over the C ABI declared in include/spec_verify.h.  It
+only marshals arguments (torch CUDA tensors -> device pointers, the current
+HIP stream, a workspace tensor); every step of the computation runs in the
+library's HIP kernels.  If the library is missing the calls raise: there is
+no CPU fallback.
+
+    from draft_verification_04_amd import verify, verify_greedy, schedule_lengths
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_OK = 0
+SPEC_ERR_INVALID_ARG = 1
+SPEC_ERR_WORKSPACE = 2
+SPEC_ERR_UNSUPPORTED = 3
+SPEC_ERR_HIP = 4
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_SCHED_EARLY_STOP = 0
+SPEC_SCHED_GLOBAL = 1
+
+REQ_BAD_TOKEN = 1
+REQ_BAD_TEMPERATURE = 2
+REQ_NONFINITE = 4
+REQ_BAD_LENGTH = 8
+REQ_BAD_TOPK = 16
+REQ_BAD_CONFIDENCE = 32
+
+# name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_Z = ctypes.c_size_t
+EXPORTS = {
+    "spec_abi_version": (_I, []),
+    "spec_status_string": (ctypes.c_char_p, [_I]),
+    "spec_verify_workspace_size": (_Z, [_I, _I, _I]),
+    "spec_verify": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "spec_verify_profiled": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P,
+                                  _P, _P]),
+    "spec_verify_greedy_workspace_size": (_Z, [_I, _I]),
+    "spec_verify_greedy": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "spec_schedule_workspace_size": (_Z, [_I, _I]),
+    "spec_schedule_lengths": (_I, [_I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "spec_philox_uniforms": (_I, [_I, _P, _P, _P, _P, _P, _P]),
+}
+
+_lib_handle = None
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {status_string(code)} ({code})")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m draft_verification_04_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib_handle = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().spec_status_string(int(code)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, code):
+    if code != SPEC_OK:
+        raise SpecError(fn, code)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+def _logit_dtype(t):
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def verify_workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return int(load_library().spec_verify_workspace_size(B, gamma, V))
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+           lengths: Optional[torch.Tensor] = None, temperature: Optional[torch.Tensor] = None,
+           top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
+           out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+           events=None) -> dict:
+    """spec_verify on torch tensors.  Returns dict(num_accepted, out_tokens, accept_prob, status).
+
+    target [B, gamma+1, V] and draft [B, gamma, V] (float32 or bfloat16);
+    draft_tokens [B, gamma] int32; lengths [B] int32 or None; temperature [B]
+    float32 (default ones); top_k [B] int32 or None; seed [B] int64 holding
+    the uint64 bit pattern (default zeros).  `events` = (before, after)
+    torch.cuda.Event pair recorded around the row-streaming kernel.
+    """
+    lib = load_library()
+    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
+    _dev(draft, "draft", target.dtype, 3)
+    B, G1, V = target.shape
+    G = G1 - 1
+    if tuple(draft.shape) != (B, G, V):
+        raise ValueError("draft must be [B, gamma, V]")
+    _dev(draft_tokens, "draft_tokens", torch.int32, 2)
+    if tuple(draft_tokens.shape) != (B, G):
+        raise ValueError("draft_tokens must be [B, gamma]")
+    dev = target.device
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+    if seed is None:
+        seed = torch.zeros(B, dtype=torch.int64, device=dev)
+    _dev(lengths, "lengths", torch.int32, 1)
+    _dev(temperature, "temperature", torch.float32, 1)
+    _dev(top_k, "top_k", torch.int32, 1)
+    _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
+    if out is None:
+        out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    nbytes = int(lib.spec_verify_workspace_size(B, G, V))
+    ws = _workspace(nbytes, dev, workspace)
+    ev0 = ev1 = None
+    if events is not None:
+        ev0 = ctypes.c_void_p(events[0].cuda_event)
+        ev1 = ctypes.c_void_p(events[1].cuda_event)
+    code = lib.spec_verify_profiled(
+        B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
+        _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel(), _stream(stream), ev0, ev1)
+    _check("spec_verify", code)
+    return out
+
+
+def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, lengths: Optional[torch.Tensor] = None,
+                  out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """spec_verify_greedy on torch tensors.  Returns dict(num_accepted, out_tokens, status)."""
+    lib = load_library()
+    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
+    B, G1, V = target.shape
+    G = G1 - 1
+    _dev(draft_tokens, "draft_tokens", torch.int32, 2)
+    if tuple(draft_tokens.shape) != (B, G):
+        raise ValueError("draft_tokens must be [B, gamma]")
+    _dev(lengths, "lengths", torch.int32, 1)
+    dev = target.device
+    if out is None:
+        out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    nbytes = int(lib.spec_verify_greedy_workspace_size(B, G))
+    ws = _workspace(nbytes, dev, workspace)
+    code = lib.spec_verify_greedy(B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft_tokens),
+                                  _ptr(lengths), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+                                  _ptr(out.get("status")), _ptr(ws), ws.numel(), _stream(stream))
+    _check("spec_verify_greedy", code)
+    return out
+
+
+def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
+                     mode: int = SPEC_SCHED_EARLY_STOP, out: Optional[dict] = None, stream=None) -> dict:
+    """spec_schedule_lengths on torch tensors.  Returns dict(lengths, theta, status)."""
+    lib = load_library()
+    _dev(conf, "conf", torch.float32, 2)
+    _dev(sps, "sps", torch.float64, 1)
+    B, G = conf.shape
+    dev = conf.device
+    if out is None:
+        out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
+                   theta=torch.empty(1, dtype=torch.float64, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    code = lib.spec_schedule_lengths(B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode),
+                                     _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("status")),
+                                     None, 0, _stream(stream))
+    _check("spec_schedule_lengths", code)
+    return out
+
+
+def philox_uniforms(seed: torch.Tensor, request: torch.Tensor, position: torch.Tensor, stream=None):
+    """The library's (u_accept, u_emit) draws for each (seed, request, position) triple."""
+    lib = load_library()
+    _dev(seed, "seed", torch.int64, 1)
+    _dev(request, "request", torch.int32, 1)
+    _dev(position, "position", torch.int32, 1)
+    n = seed.numel()
+    ua = torch.empty(n, dtype=torch.float64, device=seed.device)
+    ue = torch.empty(n, dtype=torch.float64, device=seed.device)
+    code = lib.spec_philox_uniforms(n, _ptr(seed), _ptr(request), _ptr(position), _ptr(ua), _ptr(ue),
+                                    _stream(stream))
+    _check("spec_philox_uniforms", code)
+    return ua, ue

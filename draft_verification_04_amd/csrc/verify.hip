@@ -1,0 +1,972 @@
+// Lossless draft verification on gfx950: work list, row-streaming statistics
+// with the acceptance test, and the per-request finish (first rejection,
+// correction / appended token, outputs).
+//
+// What is computed follows the DSpark paper, §2.1 (accept x_k with
+// probability min(1, p_t(x_k) / p_d(x_k)), left to right, the first
+// rejection ends the block) and §1 (one extra token from the target after the
+// accepted prefix); a request verified at length 0 draws a fresh target token
+// (the paper's appendix counterexample).  The correction after a rejection
+// is drawn from the normalised max(0, p_t - p_d).
+//
+// Kernels
+//   worklist_kernel  one workgroup: (request, position) items in
+//                    position-major order for every position k <= L_i.
+//   stream_kernel    one workgroup per item: streams target row k (and draft
+//                    row k when k < L_i) once from HBM with 16-byte loads,
+//                    computes log2-sum-exp of z * log2(e) / T (or the argmax
+//                    for the greedy rule, or the top-k threshold first), then
+//                    the acceptance test of x_k with its Philox uniform.
+//   finish_kernel    one workgroup per request: first rejection n, outputs,
+//                    and the emitted token by an fp64 inverse CDF over row n.
+#include "common.hpp"
+#include "philox.hpp"
+#include "verify_impl.hpp"
+#include "spec_verify.h"
+
+#include <float.h>
+#include <math.h>
+
+namespace spec {
+
+static constexpr double kLn2 = 0.69314718055994530942;
+static constexpr double kLog2e = 1.44269504088896340736;
+
+// ---------------------------------------------------------------------------
+// worklist
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a) {
+  __shared__ int hist[SPEC_MAX_GAMMA + 2];
+  __shared__ int off[SPEC_MAX_GAMMA + 2];
+  __shared__ int carry[SPEC_MAX_GAMMA + 1];
+  __shared__ int cnt[kWorklistThreads / SPEC_WAVE][SPEC_MAX_GAMMA + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.G, B = a.B;
+  for (int t = tid; t < G + 2; t += blockDim.x) hist[t] = 0;
+  for (int t = tid; t < G + 1; t += blockDim.x) carry[t] = 0;
+  __syncthreads();
+  for (int i = tid; i < B; i += blockDim.x) {
+    a.req_status[i] = 0;
+    const int L = a.lengths ? a.lengths[i] : G;
+    if (L >= 0 && L <= G) atomicAdd(&hist[L], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // c_k = #{i : L_i >= k}; items of position k start at off[k]
+    int suffix = 0;
+    for (int l = G; l >= 0; --l) {
+      suffix += hist[l];
+      hist[l] = suffix;
+    }
+    off[0] = 0;
+    for (int k = 0; k <= G; ++k) off[k + 1] = off[k] + hist[k];
+    *a.nitems = off[G + 1];
+  }
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < B; base += blockDim.x) {
+    const int i = base + tid;
+    int L = -1;
+    if (i < B) {
+      L = a.lengths ? a.lengths[i] : G;
+      if (L < 0 || L > G) L = -1;
+    }
+    for (int k = 0; k <= G; ++k) {
+      const unsigned long long m = __ballot(L >= k);
+      if (lane == 0) cnt[wave][k] = __popcll(m);
+    }
+    __syncthreads();
+    if (tid <= G) {
+      int run = carry[tid];
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        const int c = cnt[w][tid];
+        cnt[w][tid] = run;
+        run += c;
+      }
+      carry[tid] = run;
+    }
+    __syncthreads();
+    for (int k = 0; k <= G; ++k) {
+      const unsigned long long m = __ballot(L >= k);
+      if (L >= k) {
+        const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
+        a.items[idx] = (i << 7) | k;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// streaming statistics
+// ---------------------------------------------------------------------------
+
+// Row geometry: elements before the first 16-byte boundary (head), whole
+// 16-byte vectors, and the elements after the last one (tail).
+struct RowGeom {
+  int head, nvec, tail;
+};
+
+template <bool BF16>
+__device__ __forceinline__ RowGeom row_geom(const char* row, int V) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+  int h = (int)(((16u - (unsigned)(addr & 15u)) & 15u) / ES);
+  if (h > V) h = V;
+  const int nv = (V - h) / EPV;
+  return RowGeom{h, nv, V - h - nv * EPV};
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack(const uint4& d, float (&z)[BF16 ? 8 : 4]) {
+  if constexpr (BF16) {
+    z[0] = bf16_lo(d.x); z[1] = bf16_hi(d.x);
+    z[2] = bf16_lo(d.y); z[3] = bf16_hi(d.y);
+    z[4] = bf16_lo(d.z); z[5] = bf16_hi(d.z);
+    z[6] = bf16_lo(d.w); z[7] = bf16_hi(d.w);
+  } else {
+    z[0] = __uint_as_float(d.x); z[1] = __uint_as_float(d.y);
+    z[2] = __uint_as_float(d.z); z[3] = __uint_as_float(d.w);
+  }
+}
+
+// Per-thread running sum S of 2^(z*c - M) with an integer-valued reference M
+// that only moves up.  z*c is formed as fma(z, c_lo, fma(z, c_hi, -M)), with
+// c_hi + c_lo = log2(e)/T to ~2^-48 relative and c_lo > 0 (so -inf logits give
+// -inf exponents).  M is raised only when a group's sum exceeds 2^32; then S
+// is rescaled by an exact power of two.  A NaN or +inf logit sets `bad`.
+template <int N>
+__device__ __forceinline__ void accum(const float (&z)[N], float c_hi, float c_lo, float& M, float& S,
+                                      int& bad) {
+  float e[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], c_lo, fmaf(z[j], c_hi, -M)));
+  float s = 0.f;
+#pragma unroll
+  for (int w = 1; w < N; w <<= 1)
+#pragma unroll
+    for (int j = 0; j + w < N; j += 2 * w) e[j] += e[j + w];
+  s = e[0];
+  if (!(s <= 0x1p32f)) {
+    float vmax = z[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) vmax = fmaxf(vmax, z[j]);
+    if (!(vmax < INFINITY)) {
+      bad = 1;
+      s = 0.f;
+    } else {
+      const float mc = ceilf(vmax * c_hi);
+      if (mc > M) {
+        const float d = M - mc;
+        S = (d < -126.f) ? 0.f : ldexpf(S, (int)d);
+        M = mc;
+      }
+#pragma unroll
+      for (int j = 0; j < N; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], c_lo, fmaf(z[j], c_hi, -M)));
+#pragma unroll
+      for (int w = 1; w < N; w <<= 1)
+#pragma unroll
+        for (int j = 0; j + w < N; j += 2 * w) e[j] += e[j + w];
+      s = e[0];
+      if (!(s <= 0x1p32f)) {
+        bad = 1;
+        s = 0.f;
+      }
+    }
+  }
+  S += s;
+}
+
+template <bool BF16>
+__device__ void stream_sum(const char* row, int V, float c_hi, float c_lo, int lt, int nthr, float& M,
+                           float& S, int& bad) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  constexpr int U = 4;
+  const RowGeom g = row_geom<BF16>(row, V);
+  const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
+  int v = lt;
+  for (; v + (U - 1) * nthr < g.nvec; v += U * nthr) {
+    uint4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = vp[v + u * nthr];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float z[EPV];
+      unpack<BF16>(d[u], z);
+      accum<EPV>(z, c_hi, c_lo, M, S, bad);
+    }
+  }
+  for (; v < g.nvec; v += nthr) {
+    float z[EPV];
+    unpack<BF16>(vp[v], z);
+    accum<EPV>(z, c_hi, c_lo, M, S, bad);
+  }
+  float z[2] = {-INFINITY, -INFINITY};
+  if (lt < g.head) z[0] = load_elem<BF16>(row, lt);
+  if (lt < g.tail) z[1] = load_elem<BF16>(row, g.head + g.nvec * EPV + lt);
+  accum<2>(z, c_hi, c_lo, M, S, bad);
+}
+
+// Greedy statistic: first-occurrence argmax; `bad` on NaN or +inf.
+template <bool BF16>
+__device__ void stream_argmax(const char* row, int V, int lt, int nthr, float& best, int& bidx, int& bad) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  constexpr int U = 4;
+  const RowGeom g = row_geom<BF16>(row, V);
+  const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
+  auto take = [&](const float (&z)[EPV], int vbase) {
+    float vmax = z[0];
+#pragma unroll
+    for (int j = 1; j < EPV; ++j) vmax = fmaxf(vmax, z[j]);
+    int nb = 0;
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) nb |= !(z[j] <= FLT_MAX);
+    bad |= nb;
+    if (vmax > best) {  // vectors of one thread arrive in increasing token order
+      int j = 0;
+      while (j < EPV - 1 && !(z[j] == vmax)) ++j;
+      best = vmax;
+      bidx = vbase + j;
+    }
+  };
+  int v = lt;
+  for (; v + (U - 1) * nthr < g.nvec; v += U * nthr) {
+    uint4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = vp[v + u * nthr];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float z[EPV];
+      unpack<BF16>(d[u], z);
+      take(z, g.head + (v + u * nthr) * EPV);
+    }
+  }
+  for (; v < g.nvec; v += nthr) {
+    float z[EPV];
+    unpack<BF16>(vp[v], z);
+    take(z, g.head + v * EPV);
+  }
+  // head and tail elements: compare with the index tie-break
+  if (lt < g.head) {
+    const float z = load_elem<BF16>(row, lt);
+    bad |= !(z <= FLT_MAX);
+    if (z > best || (z == best && lt < bidx)) { best = z; bidx = lt; }
+  }
+  if (lt < g.tail) {
+    const int idx = g.head + g.nvec * EPV + lt;
+    const float z = load_elem<BF16>(row, idx);
+    bad |= !(z <= FLT_MAX);
+    if (z > best || (z == best && idx < bidx)) { best = z; bidx = idx; }
+  }
+}
+
+// Order-preserving 32-bit key of a float (larger float -> larger key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+struct StreamShared {
+  float M[8];
+  double S[8];
+  int bad[8];
+  float best[8];
+  int bidx[8];
+  double lse2[2];
+  float theta[2];
+  // top-k
+  float tau_w[8];
+  float lane_max[8][64];
+  int cand_n[2];
+  int cnt[2][8];
+  float cand[2][kTopkCap];
+};
+
+// Combine the per-thread (M, S) of one row's waves; result in sh.lse2[which].
+__device__ __forceinline__ void row_combine_sum(StreamShared& sh, float M, float S, int bad, int wave, int lane,
+                                                int first_wave, int nwaves, int lt, int which) {
+  const float Mw = wave_max(M);
+  double Sd = (S > 0.f) ? ldexp((double)S, (int)fmaxf(M - Mw, -2000.f)) : 0.0;
+  Sd = wave_sum(Sd);
+  const int bw = wave_or_i(bad);
+  if (lane == 0) {
+    sh.M[wave] = Mw;
+    sh.S[wave] = Sd;
+    sh.bad[wave] = bw;
+  }
+  __syncthreads();
+  if (lt == 0) {
+    float Mr = -INFINITY;
+    int b = 0;
+    for (int w = first_wave; w < first_wave + nwaves; ++w) {
+      Mr = fmaxf(Mr, sh.M[w]);
+      b |= sh.bad[w];
+    }
+    double Sr = 0.0;
+    for (int w = first_wave; w < first_wave + nwaves; ++w)
+      if (sh.S[w] > 0.0) Sr += ldexp(sh.S[w], (int)fmaxf(sh.M[w] - Mr, -2000.f));
+    // no finite kept logit, or a NaN / +inf: invalid row
+    sh.lse2[which] = (b || !(Sr > 0.0)) ? NAN : (double)Mr + log2(Sr);
+  }
+}
+
+// Exact K-th largest raw logit of a row (ties counted) and the log2-sum-exp
+// over {z >= theta}.  Candidates z >= tau are collected in LDS, where tau is a
+// lower bound of the K-th largest value: every wave of the row contributes
+// ceil(K / waves) of its lane maxima over the first vectors, so at least K
+// logits are >= tau.  If more than kTopkCap candidates arrive, the threshold
+// is found by counting passes over the row instead.
+template <bool BF16>
+__device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, float c_hi, float c_lo, int lt,
+                           int nthr, int wave, int lane, int first_wave, int nwaves, int which) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  const RowGeom g = row_geom<BF16>(row, V);
+  const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
+  if (lt == 0) sh.cand_n[which] = 0;
+  // phase A: first vectors in registers, lane maxima
+  uint4 pre[kTopkPre];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kTopkPre; ++u) {
+    const int v = lt + u * nthr;
+    if (v < g.nvec) {
+      pre[u] = vp[v];
+      float z[EPV];
+      unpack<BF16>(pre[u], z);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) tmax = fmaxf(tmax, z[j]);
+    }
+  }
+  sh.lane_max[wave][lane] = tmax;
+  __syncthreads();
+  {
+    const int Kw = (K + nwaves - 1) / nwaves;
+    if (Kw <= 64) {
+      int rank = 0;
+      for (int s = 0; s < 64; ++s) {
+        const float o = sh.lane_max[wave][s];
+        rank += (o > tmax) || (o == tmax && s < lane);
+      }
+      if (rank == Kw - 1) sh.tau_w[wave] = tmax;
+    } else if (lane == 0) {
+      sh.tau_w[wave] = -INFINITY;
+    }
+  }
+  __syncthreads();
+  float tau = INFINITY;
+  for (int w = first_wave; w < first_wave + nwaves; ++w) tau = fminf(tau, sh.tau_w[w]);
+  if (!(tau > -INFINITY)) tau = -INFINITY;  // also catches NaN
+  // phase B: filter everything into the candidate buffer
+  int bad = 0;
+  float vmax_all = -INFINITY;
+  float* cand = sh.cand[which];
+  int* cn = &sh.cand_n[which];
+  auto push = [&](const float* z, int n) {
+    float vmax = z[0];
+    for (int j = 1; j < n; ++j) vmax = fmaxf(vmax, z[j]);
+    for (int j = 0; j < n; ++j) bad |= (z[j] != z[j]) || (z[j] == INFINITY);
+    vmax_all = fmaxf(vmax_all, vmax);
+    if (vmax >= tau) {
+      for (int j = 0; j < n; ++j)
+        if (z[j] >= tau) {
+          const int slot = atomicAdd(cn, 1);
+          if (slot < kTopkCap) cand[slot] = z[j];
+        }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kTopkPre; ++u) {
+    const int v = lt + u * nthr;
+    if (v < g.nvec) {
+      float z[EPV];
+      unpack<BF16>(pre[u], z);
+      push(z, EPV);
+    }
+  }
+  for (int v = lt + kTopkPre * nthr; v < g.nvec; v += nthr) {
+    float z[EPV];
+    unpack<BF16>(vp[v], z);
+    push(z, EPV);
+  }
+  {
+    float z[2];
+    int n = 0;
+    if (lt < g.head) z[n++] = load_elem<BF16>(row, lt);
+    if (lt < g.tail) z[n++] = load_elem<BF16>(row, g.head + g.nvec * EPV + lt);
+    if (n) push(z, n);
+  }
+  // row max and bad flag
+  {
+    const float wm = wave_max(vmax_all);
+    const int wb = wave_or_i(bad);
+    if (lane == 0) {
+      sh.M[wave] = wm;
+      sh.bad[wave] = wb;
+    }
+  }
+  __syncthreads();
+  float rmax = -INFINITY;
+  int rbad = 0;
+  for (int w = first_wave; w < first_wave + nwaves; ++w) {
+    rmax = fmaxf(rmax, sh.M[w]);
+    rbad |= sh.bad[w];
+  }
+  const int ncand = sh.cand_n[which];
+  const bool overflow = ncand > kTopkCap;
+  // threshold: the largest key t with #{key >= t} >= K (bitwise from the top)
+  uint32_t t = 0;
+  const int low_bit = BF16 ? 16 : 0;
+  for (int bit = 31; bit >= low_bit; --bit) {
+    const uint32_t trial = t | (1u << bit);
+    int c = 0;
+    if (!overflow) {
+      for (int s = lt; s < ncand; s += nthr) c += fkey(cand[s]) >= trial;
+    } else {
+      for (int v = lt; v < g.nvec; v += nthr) {
+        float z[EPV];
+        unpack<BF16>(vp[v], z);
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) c += (z[j] == z[j]) && fkey(z[j]) >= trial;
+      }
+      if (lt < g.head) { const float z = load_elem<BF16>(row, lt); c += (z == z) && fkey(z) >= trial; }
+      if (lt < g.tail) {
+        const float z = load_elem<BF16>(row, g.head + g.nvec * EPV + lt);
+        c += (z == z) && fkey(z) >= trial;
+      }
+    }
+    c = (int)wave_sum((double)c);
+    const int par = bit & 1;
+    if (lane == 0) sh.cnt[par][wave] = c;
+    __syncthreads();
+    int tot = 0;
+    for (int w = first_wave; w < first_wave + nwaves; ++w) tot += sh.cnt[par][w];
+    if (tot >= K) t = trial;
+  }
+  if (BF16 && t < 0x80000000u) t |= 0xffffu;  // negative bf16 keys end in 0xffff
+  const float theta = key_to_float(t);
+  // log2-sum-exp over the kept set, referenced at M = ceil(max * c_hi)
+  const float M = ceilf(rmax * c_hi);
+  float S = 0.f;
+  int b2 = 0;
+  if (!overflow) {
+    for (int s = lt; s < ncand; s += nthr) {
+      const float z = cand[s];
+      if (z >= theta) S += __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -M)));
+    }
+  } else {
+    float Mt = M;
+    for (int v = lt; v < g.nvec; v += nthr) {
+      float z[EPV];
+      unpack<BF16>(vp[v], z);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) z[j] = (z[j] >= theta) ? z[j] : -INFINITY;
+      accum<EPV>(z, c_hi, c_lo, Mt, S, b2);
+    }
+    float z[2] = {-INFINITY, -INFINITY};
+    if (lt < g.head) { z[0] = load_elem<BF16>(row, lt); z[0] = z[0] >= theta ? z[0] : -INFINITY; }
+    if (lt < g.tail) {
+      z[1] = load_elem<BF16>(row, g.head + g.nvec * EPV + lt);
+      z[1] = z[1] >= theta ? z[1] : -INFINITY;
+    }
+    accum<2>(z, c_hi, c_lo, Mt, S, b2);
+    // Mt == M unless the reference moved; fold back to M
+    if (Mt != M) S = ldexpf(S, (int)fmaxf(Mt - M, -2000.f));
+  }
+  row_combine_sum(sh, M, S, rbad | b2 | !(rmax < INFINITY), wave, lane, first_wave, nwaves, lt, which);
+  if (lt == 0) sh.theta[which] = theta;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
+  __shared__ StreamShared sh;
+  const int g = blockIdx.x;
+  if (g >= *a.nitems) return;
+  const int item = a.items[g];
+  const int i = item >> 7, k = item & 127;
+  const int G = a.G, V = a.V;
+  constexpr int ES = BF16 ? 2 : 4;
+  const float T = a.greedy_only ? 0.f : a.temperature[i];
+  if (!(T >= 0.f && T < INFINITY)) return;          // reported by the finish kernel
+  int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+  if (K < 0) return;
+  if (K >= V) K = 0;
+  const int L = a.lengths ? a.lengths[i] : G;
+  const bool greedy = (T == 0.f);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool two = !greedy && k < L;
+  const int nthr = two ? kStreamThreads / 2 : kStreamThreads;
+  const int which = two ? (tid >= nthr) : 0;
+  const int lt = tid - which * nthr;
+  const int nwaves = nthr >> 6, first_wave = which * nwaves;
+  const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + k) * V * ES;
+  const char* drow = two ? reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + k) * V * ES : nullptr;
+  const char* row = which ? drow : trow;
+
+  if (greedy) {
+    float best = -INFINITY;
+    int bidx = 0x7fffffff, bad = 0;
+    stream_argmax<BF16>(row, V, lt, nthr, best, bidx, bad);
+    // wave: max value, then lowest index among equal values
+    float wb = wave_max(best);
+    int cand = (best == wb) ? bidx : 0x7fffffff;
+    cand = wave_min_i(cand);
+    bad = wave_or_i(bad);
+    if (lane == 0) {
+      sh.best[wave] = wb;
+      sh.bidx[wave] = cand;
+      sh.bad[wave] = bad;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float rb = -INFINITY;
+      int ri = 0x7fffffff, rbad = 0;
+      for (int w = 0; w < nwaves; ++w) rb = fmaxf(rb, sh.best[w]);
+      for (int w = 0; w < nwaves; ++w) {
+        rbad |= sh.bad[w];
+        if (sh.best[w] == rb) ri = min(ri, sh.bidx[w]);
+      }
+      if (rbad || !(rb > -INFINITY)) {
+        atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
+        ri = 0;
+      }
+      a.rows_t[(size_t)i * (G + 1) + k] = RowStat{0.0, -INFINITY, ri};
+      if (k < L) {
+        const int x = a.tokens[(size_t)i * G + k];
+        const int m = (x == ri);
+        a.acc[(size_t)i * G + k] = AccRec{m ? 1.0 : 0.0, m, 1};
+      }
+    }
+    return;
+  }
+
+  const double c64 = kLog2e / (double)T;
+  const float c_hi = __double2float_rz(c64);
+  const float c_lo = fmaxf((float)(c64 - (double)c_hi), 1e-30f);
+  if (K == 0) {
+    float M = -0x1p30f, S = 0.f;
+    int bad = 0;
+    stream_sum<BF16>(row, V, c_hi, c_lo, lt, nthr, M, S, bad);
+    row_combine_sum(sh, M, S, bad, wave, lane, first_wave, nwaves, lt, which);
+    if (lt == 0) sh.theta[which] = -INFINITY;
+  } else {
+    topk_stats<BF16>(sh, row, V, K, c_hi, c_lo, lt, nthr, wave, lane, first_wave, nwaves, which);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double l2t = sh.lse2[0];
+    const float tht = sh.theta[0];
+    a.rows_t[(size_t)i * (G + 1) + k] = RowStat{l2t, tht, 0};
+    bool bad = !(l2t == l2t);
+    if (two) {
+      const double l2d = sh.lse2[1];
+      const float thd = sh.theta[1];
+      a.rows_d[(size_t)i * G + k] = RowStat{l2d, thd, 0};
+      bad |= !(l2d == l2d);
+      const int x = a.tokens[(size_t)i * G + k];
+      if (!bad && x >= 0 && x < V) {
+        const float zt = load_elem<BF16>(trow, x);
+        const float zd = load_elem<BF16>(drow, x);
+        // log p(x) = ln2 * (z_x * log2(e)/T - lse2), -inf outside the kept set
+        const double lpt = (zt >= tht) ? kLn2 * ((double)zt * c64 - l2t) : -INFINITY;
+        const double lpd = (zd >= thd) ? kLn2 * ((double)zd * c64 - l2d) : -INFINITY;
+        double r;
+        if (lpt == -INFINITY) r = 0.0;
+        else if (lpd == -INFINITY) r = 1.0;
+        else r = fmin(1.0, exp(lpt - lpd));
+        double ua, ue;
+        verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
+        a.acc[(size_t)i * G + k] = AccRec{r, ua < r ? 1 : 0, 1};
+      }
+    }
+    if (bad) atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finish: first rejection, emitted token (fp64 inverse CDF), outputs
+// ---------------------------------------------------------------------------
+
+constexpr int kEmitChunk = 8;                                  // elements per thread per tile
+constexpr int kEmitTile = kFinishThreads * kEmitChunk;         // 8192
+constexpr int kEmitMaxTiles = (SPEC_MAX_V + kEmitTile - 1) / kEmitTile;
+
+struct FinishShared {
+  double tw[kEmitMaxTiles][kFinishThreads / SPEC_WAVE];   // tile x wave partial sums
+  double red[2][kFinishThreads / SPEC_WAVE];
+  int ired[kFinishThreads / SPEC_WAVE];
+  int n;
+  int st;
+  int token;
+  int sel_tile, sel_wave, past_end, use_pt;
+  double sel_prefix, target;
+  double lse_t, lse_d;
+};
+
+// Weight of token v in the emit row (fp64): max(0, p_t - p_d) after a
+// rejection, p_t (up to a common factor) otherwise.
+template <bool BF16>
+__device__ __forceinline__ double emit_weight(const char* trow, const char* drow, int v, double invT,
+                                              float tht, float thd, double lse_t, double lse_d, bool resid) {
+  const float zt = load_elem<BF16>(trow, v);
+  const double pt = (zt >= tht) ? exp((double)zt * invT - lse_t) : 0.0;
+  if (!resid) return pt;
+  const float zd = load_elem<BF16>(drow, v);
+  const double pd = (zd >= thd) ? exp((double)zd * invT - lse_d) : 0.0;
+  return fmax(0.0, pt - pd);
+}
+
+template <bool BF16>
+__device__ int emit_token(FinishShared& sh, const char* trow, const char* drow, int V, double T, float tht,
+                          float thd, double R_t, double R_d, double u) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NW = kFinishThreads / SPEC_WAVE;
+  const bool resid = (drow != nullptr);
+  // y = z / T as one fp64 division per element
+  double lse_t = R_t, lse_d = R_d;
+  if (resid) {
+    double st = 0.0, sd = 0.0;
+    for (int v = tid; v < V; v += kFinishThreads) {
+      const float zt = load_elem<BF16>(trow, v);
+      const float zd = load_elem<BF16>(drow, v);
+      if (zt >= tht) st += exp((double)zt / T - R_t);
+      if (zd >= thd) sd += exp((double)zd / T - R_d);
+    }
+    st = wave_sum(st);
+    sd = wave_sum(sd);
+    if (lane == 0) {
+      sh.red[0][wave] = st;
+      sh.red[1][wave] = sd;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double a = 0.0, b = 0.0;
+      for (int w = 0; w < NW; ++w) {
+        a += sh.red[0][w];
+        b += sh.red[1][w];
+      }
+      sh.lse_t = R_t + log(a);
+      sh.lse_d = R_d + log(b);
+    }
+    __syncthreads();
+    lse_t = sh.lse_t;
+    lse_d = sh.lse_d;
+  }
+  const int ntiles = (V + kEmitTile - 1) / kEmitTile;
+  bool use_resid = resid;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    int last_pos = -1;
+    for (int t = 0; t < ntiles; ++t) {
+      const int base = t * kEmitTile + tid * kEmitChunk;
+      double s = 0.0;
+#pragma unroll
+      for (int j = 0; j < kEmitChunk; ++j) {
+        const int v = base + j;
+        if (v < V) {
+          const double w = emit_weight<BF16>(trow, drow, v, 1.0 / T, tht, thd, lse_t, lse_d, use_resid);
+          s += w;
+          if (w > 0.0) last_pos = v;
+        }
+      }
+      const double incl = wave_inclusive_sum(s, lane);
+      if (lane == 63) sh.tw[t][wave] = incl;
+    }
+    const int lp = wave_max_i(last_pos);
+    if (lane == 0) sh.ired[wave] = lp;
+    __syncthreads();
+    if (tid == 0) {
+      double W = 0.0;
+      for (int t = 0; t < ntiles; ++t)
+        for (int w = 0; w < NW; ++w) W += sh.tw[t][w];
+      sh.use_pt = 0;
+      if (use_resid && !(W > 0.0)) {
+        sh.use_pt = 1;  // no residual mass (rounding): fall back to p_t of the same row
+      } else {
+        const double target = u * W;
+        double P = 0.0;
+        int ft = -1, fw = -1;
+        for (int t = 0; t < ntiles && ft < 0; ++t)
+          for (int w = 0; w < NW; ++w) {
+            const double s = sh.tw[t][w];
+            if (P + s > target) {
+              ft = t;
+              fw = w;
+              break;
+            }
+            P += s;
+          }
+        int last = -1;
+        for (int w = 0; w < NW; ++w) last = max(last, sh.ired[w]);
+        sh.sel_tile = ft;
+        sh.sel_wave = fw;
+        sh.sel_prefix = P;
+        sh.target = target;
+        sh.past_end = (ft < 0);
+        sh.token = last;
+      }
+    }
+    __syncthreads();
+    if (!sh.use_pt) break;
+    use_resid = false;
+    __syncthreads();
+  }
+  if (sh.past_end) return sh.token;  // target beyond the total (rounding): last token with weight
+  // crossing wave: recompute its lanes' chunk sums in the same order
+  if (wave == sh.sel_wave) {
+    const int t = sh.sel_tile;
+    const int base = t * kEmitTile + tid * kEmitChunk;
+    double w[kEmitChunk];
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < kEmitChunk; ++j) {
+      const int v = base + j;
+      w[j] = (v < V) ? emit_weight<BF16>(trow, drow, v, 1.0 / T, tht, thd, lse_t, lse_d, !sh.use_pt && resid)
+                     : 0.0;
+      s += w[j];
+    }
+    const double incl = wave_inclusive_sum(s, lane);
+    const double excl = incl - s;
+    const double P = sh.sel_prefix, target = sh.target;
+    const bool crosses = (P + incl > target);
+    const unsigned long long m = __ballot(crosses);
+    const int fl = m ? __ffsll((long long)m) - 1 : 63;
+    if (lane == fl) {
+      double acc = P + (m ? excl : incl - s);
+      int tok = -1, lastpos = -1;
+      for (int j = 0; j < kEmitChunk; ++j) {
+        if (w[j] > 0.0) lastpos = base + j;
+        acc += w[j];
+        if (tok < 0 && acc > target && w[j] > 0.0) tok = base + j;
+      }
+      if (tok < 0) tok = lastpos;
+      sh.token = tok;
+    }
+  }
+  __syncthreads();
+  return sh.token;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kFinishThreads) void finish_kernel(VerifyArgs a) {
+  __shared__ FinishShared sh;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int G = a.G, V = a.V;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int L = a.lengths ? a.lengths[i] : G;
+  const float T = a.greedy_only ? 0.f : a.temperature[i];
+  const int K0 = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+  if (tid == 0) {
+    int st = 0;
+    if (L < 0 || L > G) {
+      st = SPEC_REQ_BAD_LENGTH;
+    } else {
+      if (!(T >= 0.f && T < INFINITY)) st |= SPEC_REQ_BAD_TEMPERATURE;
+      if (K0 < 0) st |= SPEC_REQ_BAD_TOPK;
+      for (int k = 0; k < L; ++k) {
+        const int x = a.tokens[(size_t)i * G + k];
+        if (x < 0 || x >= V) st |= SPEC_REQ_BAD_TOKEN;
+      }
+      if (st == 0) st |= a.req_status[i];
+    }
+    int n = 0;
+    if (st == 0) {
+      n = L;
+      for (int k = 0; k < L; ++k)
+        if (!a.acc[(size_t)i * G + k].accept) {
+          n = k;
+          break;
+        }
+    }
+    sh.st = st;
+    sh.n = n;
+  }
+  __syncthreads();
+  const int st = sh.st, n = sh.n;
+  if (a.status && tid == 0) a.status[i] = st;
+  if (st) {
+    if (tid == 0) a.num_accepted[i] = 0;
+    for (int k = tid; k <= G; k += blockDim.x) a.out_tokens[(size_t)i * (G + 1) + k] = -1;
+    if (a.accept_prob)
+      for (int k = tid; k < G; k += blockDim.x) a.accept_prob[(size_t)i * G + k] = NAN;
+    return;
+  }
+  if (a.accept_prob)
+    for (int k = tid; k < G; k += blockDim.x)
+      a.accept_prob[(size_t)i * G + k] = (k < L) ? (float)a.acc[(size_t)i * G + k].r : NAN;
+  int tok;
+  if (a.greedy_only || T == 0.f) {
+    tok = a.rows_t[(size_t)i * (G + 1) + n].argmax;
+  } else {
+    const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
+    const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + n) * V * ES;
+    const char* drow = nullptr;
+    float thd = -INFINITY;
+    double Rd = 0.0;
+    if (n < L) {
+      const RowStat rd = a.rows_d[(size_t)i * G + n];
+      drow = reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + n) * V * ES;
+      thd = rd.theta;
+      Rd = rd.lse2 * kLn2;
+    }
+    double ua, ue;
+    verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
+    tok = emit_token<BF16>(sh, trow, drow, V, (double)T, rt.theta, thd, rt.lse2 * kLn2, Rd, ue);
+  }
+  if (tid == 0) a.num_accepted[i] = n;
+  for (int k = tid; k <= G; k += blockDim.x) {
+    int o = -1;
+    if (k < n) o = a.tokens[(size_t)i * G + k];
+    else if (k == n) o = tok;
+    a.out_tokens[(size_t)i * (G + 1) + k] = o;
+  }
+}
+
+__global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, const int32_t* pos, double* ua,
+                              double* ue) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  double a, b;
+  verify_uniforms(seed[t], (uint64_t)(uint32_t)req[t], (uint64_t)(uint32_t)pos[t], &a, &b);
+  ua[t] = a;
+  ue[t] = b;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t rows_t, rows_d, acc, items, nitems, req_status, total;
+};
+
+static WsLayout ws_layout(int B, int G) {
+  WsLayout l;
+  size_t o = 0;
+  l.rows_t = o; o = align256(o + sizeof(RowStat) * (size_t)B * (G + 1));
+  l.rows_d = o; o = align256(o + sizeof(RowStat) * (size_t)B * G);
+  l.acc = o; o = align256(o + sizeof(AccRec) * (size_t)B * G);
+  l.items = o; o = align256(o + sizeof(int32_t) * (size_t)B * (G + 1));
+  l.nitems = o; o = align256(o + sizeof(int32_t));
+  l.req_status = o; o = align256(o + sizeof(int32_t) * (size_t)B);
+  l.total = o;
+  return l;
+}
+
+static bool shape_ok(int B, int G, int V, int dtype) {
+  if (B < 1 || B > (1 << 24)) return false;
+  if (G < 1 || G > SPEC_MAX_GAMMA) return false;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return false;
+  const int vmax = dtype == SPEC_BF16 ? SPEC_MAX_V : SPEC_MAX_V / 2;
+  if (V < 1 || V > vmax) return false;
+  return true;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
+                             void* ev1) {
+  const WsLayout l = ws_layout(a.B, a.G);
+  if (!ws || ws_bytes < l.total) return SPEC_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return SPEC_ERR_WORKSPACE;
+  char* w = reinterpret_cast<char*>(ws);
+  a.rows_t = reinterpret_cast<RowStat*>(w + l.rows_t);
+  a.rows_d = reinterpret_cast<RowStat*>(w + l.rows_d);
+  a.acc = reinterpret_cast<AccRec*>(w + l.acc);
+  a.items = reinterpret_cast<int32_t*>(w + l.items);
+  a.nitems = reinterpret_cast<int32_t*>(w + l.nitems);
+  a.req_status = reinterpret_cast<int32_t*>(w + l.req_status);
+  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
+  if (ev0) hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);
+  const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1));
+  if (dtype == SPEC_BF16)
+    hipLaunchKernelGGL(stream_kernel<true>, dim3(grid), dim3(kStreamThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
+  if (ev1) hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
+  if (dtype == SPEC_BF16)
+    hipLaunchKernelGGL(finish_kernel<true>, dim3(a.B), dim3(kFinishThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(finish_kernel<false>, dim3(a.B), dim3(kFinishThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace spec
+
+using namespace spec;
+
+extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V) {
+  (void)V;
+  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
+  return ws_layout(B, gamma).total;
+}
+
+extern "C" size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma) {
+  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
+  return ws_layout(B, gamma).total;
+}
+
+extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                                        const void* target_logits, const void* draft_logits,
+                                        const int32_t* draft_tokens, const int32_t* lengths,
+                                        const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                                        int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                                        int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
+                                        void* event_before, void* event_after) {
+  if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
+  if (!target_logits || !draft_logits || !draft_tokens || !temperature || !seed || !num_accepted || !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(target_logits) || !aligned16(draft_logits)) return SPEC_ERR_INVALID_ARG;
+  VerifyArgs a{};
+  a.B = B; a.G = gamma; a.V = V; a.greedy_only = 0;
+  a.target = target_logits; a.draft = draft_logits; a.tokens = draft_tokens; a.lengths = lengths;
+  a.temperature = temperature; a.top_k = top_k; a.seed = seed;
+  a.num_accepted = num_accepted; a.out_tokens = out_tokens; a.accept_prob = accept_prob; a.status = status;
+  return launch_verify(a, dtype, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), event_before,
+                       event_after);
+}
+
+extern "C" int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,
+                               const void* draft_logits, const int32_t* draft_tokens, const int32_t* lengths,
+                               const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                               int32_t* num_accepted, int32_t* out_tokens, float* accept_prob, int32_t* status,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return spec_verify_profiled(B, gamma, V, dtype, target_logits, draft_logits, draft_tokens, lengths, temperature,
+                              top_k, seed, num_accepted, out_tokens, accept_prob, status, workspace,
+                              workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" int32_t spec_verify_greedy(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                                      const void* target_logits, const int32_t* draft_tokens,
+                                      const int32_t* lengths, int32_t* num_accepted, int32_t* out_tokens,
+                                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
+  if (!target_logits || !draft_tokens || !num_accepted || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(target_logits)) return SPEC_ERR_INVALID_ARG;
+  VerifyArgs a{};
+  a.B = B; a.G = gamma; a.V = V; a.greedy_only = 1;
+  a.target = target_logits; a.tokens = draft_tokens; a.lengths = lengths;
+  a.num_accepted = num_accepted; a.out_tokens = out_tokens; a.status = status;
+  return launch_verify(a, dtype, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr,
+                       nullptr);
+}
+
+extern "C" int32_t spec_philox_uniforms(int32_t n, const uint64_t* seed, const int32_t* request,
+                                        const int32_t* position, double* u_accept, double* u_emit, void* stream) {
+  if (n < 0) return SPEC_ERR_INVALID_ARG;
+  if (n == 0) return SPEC_OK;
+  if (!seed || !request || !position || !u_accept || !u_emit) return SPEC_ERR_INVALID_ARG;
+  const int threads = 256;
+  hipLaunchKernelGGL(philox_kernel, dim3((n + threads - 1) / threads), dim3(threads), 0,
+                     reinterpret_cast<hipStream_t>(stream), n, seed, request, position, u_accept, u_emit);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}

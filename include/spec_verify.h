@@ -1,0 +1,222 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify, lossless draft verification and
+ * confidence-scheduled verify lengths on AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of speculative decoding as stated in the DSpark
+ * paper ("DSpark: Confidence-Scheduled Speculative Decoding with
+ * Semi-Autoregressive Generation"):
+ *   - spec_verify            -- rejection-sampling verification of a block of
+ *                               gamma draft tokens per request against target
+ *                               logits (paper §2.1), plus the token the target
+ *                               appends after the accepted prefix (paper §1),
+ *                               a fresh target token when nothing is verified
+ *                               (paper appendix counterexample);
+ *   - spec_verify_greedy     -- the same block verified by the argmax rule;
+ *   - spec_schedule_lengths  -- survival products of per-position confidences
+ *                               and the budgeted length selector (paper
+ *                               §3.2.2; Algorithm 1 of the paper's Chinese
+ *                               translation; the no-break search of §5.2).
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *     tensor's storage).  Scalars are passed by value.  The caller owns all
+ *     memory; the library keeps no state between calls and never allocates.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it asynchronously; nothing synchronises the host.
+ *   - Return value: SPEC_OK, or an error code returned synchronously before
+ *     anything is enqueued (bad pointer, shape, dtype, alignment, workspace)
+ *     -- or SPEC_ERR_HIP if a launch itself failed.
+ *   - Bad DATA (a draft token outside [0,V), a NaN/+inf logit in a needed
+ *     row, a bad temperature, length or confidence) is not an error of the
+ *     call: it is reported per request in `status` (SPEC_REQ_* bits) and
+ *     that request gets num_accepted = 0, out_tokens = -1, accept_prob = NaN.
+ *   - Two calls may run concurrently when they use different workspaces.
+ *
+ * Shapes (row-major, contiguous; B requests, gamma draft positions, vocabulary V):
+ *   target_logits [B, gamma+1, V]  row k < gamma: target distribution at draft
+ *                                   position k; row L: the row the appended
+ *                                   token is drawn from when all L drafts pass
+ *   draft_logits  [B, gamma, V]     draft distribution at position k
+ *   draft_tokens  [B, gamma] int32  x_k, the draft token at position k
+ *   lengths       [B] int32         verify length L_i in [0, gamma] (NULL = gamma)
+ * Logits are fp32 or bf16 (spec_dtype); the base pointers must be 16-byte
+ * aligned; any V >= 1 is accepted.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+/* Call status (return value of every entry point). */
+enum {
+    SPEC_OK = 0,
+    SPEC_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misalignment, bad enum */
+    SPEC_ERR_WORKSPACE = 2,   /* workspace missing or smaller than the size query returned */
+    SPEC_ERR_UNSUPPORTED = 3, /* a valid request this build does not support (e.g. V too large) */
+    SPEC_ERR_HIP = 4          /* a HIP launch reported an error */
+};
+
+/* Logit element type. */
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+/* Scheduler mode. */
+enum {
+    SPEC_SCHED_EARLY_STOP = 0, /* admit while Theta rises strictly; stop at the first
+                                  candidate that does not raise it (paper §3.2.2, Alg. 1) */
+    SPEC_SCHED_GLOBAL = 1      /* smallest admitted count maximising Theta over the whole
+                                  budget (the no-break search of paper §5.2) */
+};
+
+/* Per-request data status bits (the `status` outputs). */
+#define SPEC_REQ_BAD_TOKEN 1        /* a needed draft token outside [0, V) */
+#define SPEC_REQ_BAD_TEMPERATURE 2  /* temperature negative, NaN or infinite */
+#define SPEC_REQ_NONFINITE 4        /* NaN or +inf in a needed logit row */
+#define SPEC_REQ_BAD_LENGTH 8       /* lengths[i] outside [0, gamma] */
+#define SPEC_REQ_BAD_TOPK 16        /* top_k[i] < 0 */
+#define SPEC_REQ_BAD_CONFIDENCE 32  /* scheduler: a confidence outside [0, 1] or NaN */
+
+/* Limits of this build. */
+#define SPEC_MAX_GAMMA 64
+#define SPEC_MAX_V 524288           /* bf16; fp32 rows are limited to SPEC_MAX_V / 2 */
+#define SPEC_MAX_SCHED_CANDIDATES 16384 /* B * gamma for spec_schedule_lengths */
+
+int32_t spec_abi_version(void);
+const char* spec_status_string(int32_t status);
+
+/*
+ * spec_verify -- lossless rejection-sampling verification (paper §2.1).
+ *
+ * For request i with length L = lengths[i] (gamma if NULL), temperature
+ * T = temperature[i], top-k K = top_k[i] (0 if NULL), seed s = seed[i]:
+ *   p_t,k = softmax(target row k / T), p_d,k = softmax(draft row k / T), both
+ *   restricted to the kept set when K > 0 (every v whose raw logit is >= the
+ *   K-th largest raw logit of that row; ties kept; K >= V keeps all);
+ *   for k = 0 .. L-1 in order: accept x_k iff u_acc(k) < min(1, p_t,k(x_k) /
+ *   p_d,k(x_k)); the first rejection n ends the block (n = L if none);
+ *   the emitted token is drawn by inverse CDF (ascending token id, smallest
+ *   v with C(v) > u_emit(n) * W) from w = max(0, p_t,n - p_d,n) after a
+ *   rejection, or from w = p_t,L (target row L) when all L drafts passed
+ *   (with L = 0 this is a fresh token from target row 0).
+ *   T = 0 selects the greedy rule of spec_verify_greedy for that request.
+ * Draws: Philox4x64-10 (Salmon et al., SC'11), key (s, 0), block counter
+ * (k + 1, i, 0, 0); u_acc(k) = word0 >> 11 scaled by 2^-53, u_emit(k) = word1
+ * likewise.  The same seed and inputs give bitwise-identical outputs.
+ *
+ * Arguments
+ *   B >= 1, 1 <= gamma <= SPEC_MAX_GAMMA, 1 <= V <= SPEC_MAX_V (fp32: V/2)
+ *   dtype            SPEC_F32 or SPEC_BF16
+ *   target_logits    [B, gamma+1, V]  (only rows k <= L_i are read)
+ *   draft_logits     [B, gamma, V]    (only rows k < L_i are read)
+ *   draft_tokens     [B, gamma] int32 (only k < L_i are read)
+ *   lengths          [B] int32 or NULL
+ *   temperature      [B] float32 (>= 0; 0 = greedy rule)
+ *   top_k            [B] int32 or NULL
+ *   seed             [B] uint64
+ * Outputs (written for every request)
+ *   num_accepted     [B] int32: n_i
+ *   out_tokens       [B, gamma+1] int32: x_0 .. x_{n-1}, the emitted token, then -1
+ *   accept_prob      [B, gamma] float32 or NULL: min(1, p_t/p_d) at x_k for every
+ *                    k < L_i (also after the first rejection), NaN for k >= L_i;
+ *                    greedy requests get 1 (match) or 0
+ *   status           [B] int32 or NULL: SPEC_REQ_* bits, 0 when the data were valid
+ * Workspace
+ *   workspace        device scratch of at least spec_verify_workspace_size(B, gamma, V)
+ *                    bytes, 256-byte aligned; owned by the caller; must not be used
+ *                    by another call in flight.
+ */
+size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V);
+
+int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                    const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* lengths,
+                    const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                    int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                    int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_profiled -- spec_verify, recording two caller-created
+ * hipEvent_t (passed as void*) on `stream` immediately before and after the
+ * launch of the row-streaming kernel that reads the logits.  Either event
+ * may be NULL.  For measurement only; results are identical to spec_verify.
+ */
+int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                             const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const int32_t* lengths,
+                             const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                             int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                             int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
+                             void* event_before, void* event_after);
+
+/*
+ * spec_verify_greedy -- greedy verification.  a_k = argmax of raw target row k
+ * (lowest token id on ties); n = first k < L_i with x_k != a_k, else L_i;
+ * out_tokens = x_0 .. x_{n-1}, a_n, then -1.  Draft logits are never read.
+ * Arguments and outputs as for spec_verify (no temperature, top-k or seed).
+ */
+size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma);
+
+int32_t spec_verify_greedy(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                           const void* target_logits, const int32_t* draft_tokens,
+                           const int32_t* lengths, int32_t* num_accepted, int32_t* out_tokens,
+                           int32_t* status, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * spec_schedule_lengths -- confidence-scheduled verify lengths (paper §3.2.2).
+ *
+ *   a_{i,j} = c_{i,0} * ... * c_{i,j} (float32, left to right);
+ *   candidates (i, j) with a_{i,j} > 0, sorted by a descending, then i, then j;
+ *   admitting the first m gives batch tokens B + m and expected accepted tokens
+ *   tau(m) = B + sum of their survivals, held in fixed point with 50 fractional
+ *   bits (each survival floored to a multiple of 2^-50);
+ *   Theta(m) = fp64(tau(m)) * 2^-50 * sps[B + m];
+ *   m ranges over 0 .. min(#candidates, budget_tokens - B);
+ *   EARLY_STOP: m* = last m before the first Theta(m+1) <= Theta(m);
+ *   GLOBAL: m* = the smallest m maximising Theta.
+ *   lengths_out[i] = number of request i's candidates among the first m*.
+ *
+ * Arguments
+ *   B >= 1, 1 <= gamma <= SPEC_MAX_GAMMA, B * gamma <= SPEC_MAX_SCHED_CANDIDATES
+ *   conf          [B, gamma] float32 device, each in [0, 1]
+ *   sps           [sps_len] float64 device: engine throughput in steps/s for a
+ *                 forward batch of b tokens at index b (the profiled cost table)
+ *   sps_len       must exceed min(budget_tokens, B * (gamma + 1))
+ *   budget_tokens cap on batch tokens B + m (values below B admit nothing)
+ *   mode          SPEC_SCHED_EARLY_STOP or SPEC_SCHED_GLOBAL
+ * Outputs
+ *   lengths_out   [B] int32 device
+ *   theta_out     [1] float64 device or NULL: Theta(m*)
+ *   status        [B] int32 device or NULL: SPEC_REQ_BAD_CONFIDENCE when a
+ *                 confidence of that request is outside [0, 1] or NaN; such a
+ *                 request contributes no candidate (its length is 0)
+ *   workspace     at least spec_schedule_workspace_size(B, gamma) bytes
+ */
+size_t spec_schedule_workspace_size(int32_t B, int32_t gamma);
+
+int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const double* sps,
+                              int32_t sps_len, int32_t budget_tokens, int32_t mode,
+                              int32_t* lengths_out, double* theta_out, int32_t* status,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_philox_uniforms -- the library's draws, exposed for checking:
+ * for t < n, (u_accept[t], u_emit[t]) = the two uniforms used for request
+ * request[t] at draft position position[t] under seed[t] (see spec_verify).
+ * All arrays device, length n.
+ */
+int32_t spec_philox_uniforms(int32_t n, const uint64_t* seed, const int32_t* request,
+                             const int32_t* position, double* u_accept, double* u_emit,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

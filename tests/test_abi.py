@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments synchronously before touching the device."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+LIB = os.path.join(ROOT, "draft_verification_04_amd", "libspecverify.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(spec_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libspecverify.so is not built (run __graft_entry__.build())")
+    import draft_verification_04_amd as sv
+    return sv.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("spec_verify", "spec_verify_greedy", "spec_schedule_lengths", "spec_verify_workspace_size",
+              "spec_schedule_workspace_size", "spec_abi_version", "spec_status_string",
+              "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b[TW] (spec_\w+)$", out, flags=re.M))
+    for n in _declared():
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_binding_covers_every_symbol(lib):
+    import draft_verification_04_amd as sv
+    assert set(sv.EXPORTS) == set(_declared())
+
+
+def test_version_and_strings(lib):
+    assert lib.spec_abi_version() == 1
+    for code, text in ((0, "ok"), (1, "invalid argument"), (2, "workspace"), (3, "unsupported"), (4, "HIP")):
+        assert text in lib.spec_status_string(code).decode()
+    assert lib.spec_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    a = lib.spec_verify_workspace_size(256, 16, 151936)
+    b = lib.spec_verify_workspace_size(512, 16, 151936)
+    assert 0 < a < b and a % 256 == 0
+    assert lib.spec_verify_workspace_size(0, 16, 10) == 0
+    assert lib.spec_verify_workspace_size(4, 65, 10) == 0
+    assert lib.spec_verify_greedy_workspace_size(4, 8) > 0
+    assert lib.spec_schedule_workspace_size(256, 16) == 0
+
+
+def _fake(n=64):
+    # 16-byte aligned host buffers standing in for device pointers: validation
+    # must reject the call before any of them is dereferenced.
+    buf = (ctypes.c_uint8 * (n + 16))()
+    addr = (ctypes.addressof(buf) + 15) & ~15
+    return buf, ctypes.c_void_p(addr)
+
+
+def test_verify_rejects_bad_arguments_before_launch(lib):
+    keep, p = _fake()
+    ws = lib.spec_verify_workspace_size(2, 4, 100)
+    base = dict(B=2, G=4, V=100, dt=1, t=p, d=p, x=p, L=None, T=p, K=None, s=p, n=p, o=p, r=None, st=None,
+                ws=p, wsb=ws, stream=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.spec_verify(a["B"], a["G"], a["V"], a["dt"], a["t"], a["d"], a["x"], a["L"], a["T"], a["K"],
+                               a["s"], a["n"], a["o"], a["r"], a["st"], a["ws"], a["wsb"], a["stream"])
+
+    assert call(B=0) == 1
+    assert call(G=0) == 1
+    assert call(G=65) == 1
+    assert call(V=0) == 1
+    assert call(V=524289) == 1
+    assert call(dt=0, V=262145) == 1
+    assert call(dt=7) == 1
+    assert call(t=None) == 1
+    assert call(d=None) == 1
+    assert call(x=None) == 1
+    assert call(T=None) == 1
+    assert call(s=None) == 1
+    assert call(n=None) == 1
+    assert call(o=None) == 1
+    assert call(t=ctypes.c_void_p(p.value + 2)) == 1          # misaligned logits
+    assert call(ws=None) == 2
+    assert call(wsb=ws - 1) == 2
+    assert call(ws=ctypes.c_void_p(p.value + 16)) == 2        # workspace not 256-byte aligned
+
+
+def test_greedy_and_schedule_reject_bad_arguments(lib):
+    keep, p = _fake()
+    ws = lib.spec_verify_greedy_workspace_size(2, 4)
+    assert lib.spec_verify_greedy(0, 4, 10, 1, p, p, None, p, p, None, p, ws, None) == 1
+    assert lib.spec_verify_greedy(2, 4, 10, 1, None, p, None, p, p, None, p, ws, None) == 1
+    assert lib.spec_verify_greedy(2, 4, 10, 1, p, p, None, p, p, None, None, ws, None) == 2
+    # B, gamma, conf, sps, sps_len, budget, mode, lengths, theta, status, ws, wsb, stream
+    assert lib.spec_schedule_lengths(0, 4, p, p, 100, 10, 0, p, None, None, None, 0, None) == 1
+    assert lib.spec_schedule_lengths(4, 65, p, p, 100, 10, 0, p, None, None, None, 0, None) == 1
+    assert lib.spec_schedule_lengths(4, 4, p, p, 100, 10, 2, p, None, None, None, 0, None) == 1
+    assert lib.spec_schedule_lengths(4, 4, None, p, 100, 10, 0, p, None, None, None, 0, None) == 1
+    assert lib.spec_schedule_lengths(4, 4, p, p, 10, 10, 0, p, None, None, None, 0, None) == 1   # table short
+    assert lib.spec_schedule_lengths(4, 4, p, p, 4, 2, 0, p, None, None, None, 0, None) == 1     # needs sps[B]
+    assert lib.spec_schedule_lengths(2048, 16, p, p, 10 ** 6, 10, 0, p, None, None, None, 0, None) == 3
+    assert lib.spec_philox_uniforms(-1, p, p, p, p, p, None) == 1
+    assert lib.spec_philox_uniforms(0, None, None, None, None, None, None) == 0
