@@ -1,0 +1,548 @@
+// The emitted token of every request, on gfx950.
+//
+// After the first rejection n < L the target appends a token drawn from the
+// normalised residual max(0, p_t - p_d) of row n; when all L drafts passed it
+// appends a token from target row L (DSpark paper §1; with L = 0 this is the
+// fresh target token of the paper's appendix counterexample).  The draw is an
+// inverse CDF in ascending token order at the emit uniform: the smallest v
+// with C(v) > u * W.
+//
+// Every quantity here is fp64: tokens sit ~1/V apart on the CDF, so the
+// cumulative sums must be right to ~1e-12 relative for the draw to agree with
+// an exact computation except on a vanishing set of uniforms.
+//
+// One function gives every token's weight:  Q(z) = exp(z/T - R_t), R_t the
+// streaming kernel's log-normaliser of target row n (accurate to ~1e-8).
+// For both rows p = Q(z) / sum Q(z) over the row (the draft row's own offset
+// cancels), so with S_t = sum Q(z_t), S_d = sum Q(z_d) the residual weight of
+// token v is  w_v = max(0, Q(z_t,v)/S_t - Q(z_d,v)/S_d).
+//
+// emit_pass_kernel   (request, segment) workgroups read the emit row(s) once.
+//   bf16 rows: Q of every bf16 value with |z| in [2^-20, 128) is tabulated in
+//   LDS (6912 fp64 entries, each computed by the same formula as the direct
+//   path, so both give identical bits).  The sign of p_t - p_d is decided
+//   with the approximate normalisers (S_t ~ 1, S_d ~ exp(R_d - R_t)) whenever
+//   the ratio clears a 1e-5 margin, far above their error; the few tokens
+//   inside the margin are recorded and weighed exactly later.  Per range of
+//   2048 tokens a wave leaves A = sum Q(z_t) and D = sum Q(z_d) over tokens
+//   with p_t > p_d, and Tall = sum Q(z_t) over all tokens.
+// emit_final_kernel  one workgroup per request: S_t, S_d, range weights
+//   A/S_t - D/S_d (+ recorded tokens), prefix scan, and the range holding
+//   u * W recomputed token by token.  It also writes every output.
+#include "common.hpp"
+#include "philox.hpp"
+#include "verify_impl.hpp"
+
+#include <float.h>
+#include <math.h>
+
+namespace spec {
+
+constexpr double kAmbTol = 1e-5;
+constexpr int kQefLo = 107, kQefHi = 133;               // bf16 exponent fields tabulated
+constexpr int kQper = (kQefHi - kQefLo + 1) * 128;      // 3456 values per sign
+constexpr int kQsize = 2 * kQper;                       // 6912 entries, 55296 bytes
+constexpr int kSub = 512;                               // tokens per wave step (64 lanes x 8)
+constexpr int kSubPerRange = kRangeElems / kSub;        // 4
+
+// exp(x) in fp64 by Tang's table-driven method (ACM TOMS 15(2), 1989), for
+// x in [-1000, 709]: x = k ln2/64 + r with |r| <= ln2/128 (two-part ln2/64),
+// e^x = 2^(k div 64) * 2^((k mod 64)/64) * e^r, e^r by its degree-5 Taylor
+// polynomial (truncation < 4e-17); T64[j] = 2^(j/64).  Underflows to 0.
+__device__ __forceinline__ double exp_tang(double x, const double* T64) {
+  const double k = rint(x * 92.332482616893657);
+  double r = fma(-k, 0.010830424696249145, x);
+  r = fma(-k, 3.623510646634843e-19, r);
+  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = fma(r, p, 1.0 / 6.0);
+  p = fma(r, p, 0.5);
+  p = fma(r, p, 1.0);
+  p = fma(r, p, 1.0);
+  const int ki = (int)k;
+  return ldexp(T64[ki & 63] * p, ki >> 6);
+}
+
+// Q(z) = exp(z/T - R), z/T taken as the fp64 product z * (1/T); -inf -> 0.
+__device__ __forceinline__ double q_direct(float z, double invT, double R, const double* T64) {
+  return exp_tang(fmax(fma((double)z, invT, -R), -1000.0), T64);
+}
+
+// Q of a bf16 bit pattern, from the table when tabulated.
+__device__ __forceinline__ double q_bf16(uint32_t b, double invT, double R, const double* T64, const double* Qt) {
+  const uint32_t t = (b & 0x7fffu) - (uint32_t)(kQefLo << 7);
+  if (t < (uint32_t)kQper) return Qt[t + ((b & 0x8000u) ? kQper : 0)];
+  return q_direct(__uint_as_float(b << 16), invT, R, T64);
+}
+
+__device__ __forceinline__ void init_t64(double* T64) {
+  if (threadIdx.x < 64) T64[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
+}
+
+__device__ void build_qtab(double* Qt, double invT, double R, const double* T64) {
+  for (int idx = threadIdx.x; idx < kQsize; idx += blockDim.x) {
+    const uint32_t s = idx >= kQper;
+    const uint32_t t = idx - s * kQper;
+    const uint32_t bits = (s << 15) | ((uint32_t)(kQefLo << 7) + t);
+    Qt[idx] = q_direct(__uint_as_float(bits << 16), invT, R, T64);
+  }
+}
+
+struct EmitRows {
+  const char* t;
+  const char* d;  // nullptr: single target row (appended / fresh token)
+  double invT, R;
+  float tht, thd;
+  double cd;      // exp(R_t - R_d): p_d ~ cd * Q(z_d) with the approximate normalisers
+};
+
+template <bool BF16>
+__device__ __forceinline__ EmitRows emit_rows(const VerifyArgs& a, int i, int n) {
+  constexpr int ES = BF16 ? 2 : 4;
+  const int G = a.G, V = a.V;
+  const int L = a.lengths ? a.lengths[i] : G;
+  EmitRows e;
+  const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
+  e.t = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + n) * V * ES;
+  e.R = rt.lse2 * kLn2;
+  e.tht = rt.theta;
+  e.invT = 1.0 / (double)a.temperature[i];
+  e.d = nullptr;
+  e.thd = -INFINITY;
+  e.cd = 1.0;
+  if (n < L) {
+    const RowStat rd = a.rows_d[(size_t)i * G + n];
+    e.d = reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + n) * V * ES;
+    e.thd = rd.theta;
+    e.cd = exp(e.R - rd.lse2 * kLn2);
+  }
+  return e;
+}
+
+// Q of token v of a row (any dtype, any alignment), kept-set aware.
+template <bool BF16>
+__device__ __forceinline__ double q_at(const char* row, int v, float th, double invT, double R, const double* T64) {
+  const float z = load_elem<BF16>(row, v);
+  return (z >= th) ? q_direct(z, invT, R, T64) : 0.0;
+}
+
+// Per-lane accumulators for one range.
+struct Acc {
+  double st, sd;   // running totals over everything this lane saw
+  double A, D, T;  // this range
+};
+
+__device__ __forceinline__ void classify(Acc& c, double qt, double qd, double cdh, double cdl, int v,
+                                         const VerifyArgs& a, int i) {
+  c.st += qt;
+  c.sd += qd;
+  c.T += qt;
+  const bool pos = qt > cdh * qd;
+  c.A += pos ? qt : 0.0;
+  c.D += pos ? qd : 0.0;
+  if (!pos && qt > 0.0 && qt >= cdl * qd) {
+    const int slot = atomicAdd(&a.ereq[i].amb_n, 1);
+    if (slot < kAmbCap) a.amb[(size_t)i * kAmbCap + slot] = v;
+  }
+}
+
+struct PassShared {
+  double T64[64];
+  double Qt[kQsize];
+  double red[2][kPassThreads / SPEC_WAVE];
+  int st, n;
+};
+
+// Table slot of a bf16 bit pattern, or -1 when it is not tabulated.
+__device__ __forceinline__ int q_slot(uint32_t b) {
+  const uint32_t t = (b & 0x7fffu) - (uint32_t)(kQefLo << 7);
+  return (t < (uint32_t)kQper) ? (int)(t + ((b & 0x8000u) ? kQper : 0)) : -1;
+}
+
+__device__ __noinline__ double q_miss(uint32_t b, double invT, double R, const double* T64) {
+  return q_direct(__uint_as_float(b << 16), invT, R, T64);
+}
+
+// One step (64 lanes x 8 tokens) of a bf16 row pair from registers.
+__device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& dd, bool resid, const EmitRows& e,
+                                          double cdh, double cdl, int v0, const VerifyArgs& a, int i,
+                                          const double* T64, const double* Qt) {
+  const uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
+  const uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t bt = (j & 1) ? (wt[j >> 1] >> 16) : (wt[j >> 1] & 0xffffu);
+    const int st = q_slot(bt);
+    double qt = Qt[st < 0 ? 0 : st];
+    if (st < 0) qt = q_miss(bt, e.invT, e.R, T64);
+    if (resid) {
+      const uint32_t bd = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xffffu);
+      const int sd = q_slot(bd);
+      double qd = Qt[sd < 0 ? 0 : sd];
+      if (sd < 0) qd = q_miss(bd, e.invT, e.R, T64);
+      classify(c, qt, qd, cdh, cdl, v0 + j, a, i);
+    } else {
+      c.T += qt;
+    }
+  }
+}
+
+template <bool BF16, bool TOPK>
+__device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NWPB = kPassThreads / SPEC_WAVE;
+  constexpr int NWT = kEmitSegs * NWPB;
+  const int V = a.V, NR = num_ranges(V);
+  const bool resid = (e.d != nullptr);
+  const double cdh = e.cd * (1.0 + kAmbTol), cdl = e.cd * (1.0 - kAmbTol);
+  const bool aligned = ((reinterpret_cast<uintptr_t>(e.t) | reinterpret_cast<uintptr_t>(e.d)) & 15u) == 0;
+  // ranges a wave can read whole with 16-byte loads
+  const int NRfull = (BF16 && !TOPK && aligned) ? V / kRangeElems : 0;
+  Acc c{0.0, 0.0, 0.0, 0.0, 0.0};
+  int r = seg * NWPB + wave;
+  if (BF16 && !TOPK) {
+    // the 4 steps of a range are in flight at once; each register slot is refilled with
+    // the same step of the wave's next range as soon as it has been consumed
+    uint4 bt[kSubPerRange], bd[kSubPerRange];
+    auto load = [&](int rr, int sub, uint4& t, uint4& d) {
+      const size_t off = ((size_t)rr * kRangeElems + sub * kSub + lane * 8) * 2;
+      t = *reinterpret_cast<const uint4*>(e.t + off);
+      d = resid ? *reinterpret_cast<const uint4*>(e.d + off) : make_uint4(0, 0, 0, 0);
+    };
+    if (r < NRfull) {
+#pragma unroll
+      for (int sub = 0; sub < kSubPerRange; ++sub) load(r, sub, bt[sub], bd[sub]);
+    }
+    while (r < NRfull) {
+      const int rn = r + NWT;
+      c.A = c.D = c.T = 0.0;
+#pragma unroll
+      for (int sub = 0; sub < kSubPerRange; ++sub) {
+        step_bf16(c, bt[sub], bd[sub], resid, e, cdh, cdl, r * kRangeElems + sub * kSub + lane * 8, a, i, sh.T64,
+                  sh.Qt);
+        if (rn < NRfull) load(rn, sub, bt[sub], bd[sub]);
+      }
+      const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
+      if (lane == 0) a.ranges[(size_t)i * NR + r] = EmitRange{A, D, T};
+      r = rn;
+    }
+  }
+  // ranges with a ragged end, unaligned rows, fp32 rows and top-k rows: token by token
+  for (; r < NR; r += NWT) {
+    c.A = c.D = c.T = 0.0;
+    for (int sub = 0; sub < kSubPerRange; ++sub) {
+      const int base = r * kRangeElems + sub * kSub + lane * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int v = base + j;
+        if (v < V) {
+          const float zt = load_elem<BF16>(e.t, v);
+          const float zd = resid ? load_elem<BF16>(e.d, v) : -INFINITY;
+          if (!TOPK || zt >= e.tht || (resid && zd >= e.thd)) {
+            const double qt = (zt >= e.tht) ? q_direct(zt, e.invT, e.R, sh.T64) : 0.0;
+            if (resid) {
+              const double qd = (zd >= e.thd) ? q_direct(zd, e.invT, e.R, sh.T64) : 0.0;
+              classify(c, qt, qd, cdh, cdl, v, a, i);
+            } else {
+              c.T += qt;
+            }
+          }
+        }
+      }
+    }
+    const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
+    if (lane == 0) a.ranges[(size_t)i * NR + r] = EmitRange{A, D, T};
+  }
+  const double st = wave_sum(c.st), sd = wave_sum(c.sd);
+  if (lane == 0) {
+    sh.red[0][wave] = st;
+    sh.red[1][wave] = sd;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
+  __shared__ PassShared sh;
+  const int i = blockIdx.x / kEmitSegs, seg = blockIdx.x % kEmitSegs;
+  const int tid = threadIdx.x;
+  init_t64(sh.T64);
+  if (tid == 0) {
+    int st, n;
+    request_decision(a, i, &st, &n);
+    sh.st = st;
+    sh.n = n;
+  }
+  __syncthreads();
+  const int st = sh.st, n = sh.n;
+  if (st || a.temperature[i] == 0.f) return;
+  const EmitRows e = emit_rows<BF16>(a, i, n);
+  const int K = a.top_k ? a.top_k[i] : 0;
+  const bool topk = K > 0 && K < a.V;
+  if (BF16 && !topk) {
+    build_qtab(sh.Qt, e.invT, e.R, sh.T64);
+    __syncthreads();
+    pass_ranges<BF16, false>(sh, a, i, seg, e);
+  } else if (topk) {
+    pass_ranges<BF16, true>(sh, a, i, seg, e);
+  } else {
+    pass_ranges<BF16, false>(sh, a, i, seg, e);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double x = 0.0, y = 0.0;
+    for (int w = 0; w < kPassThreads / SPEC_WAVE; ++w) {
+      x += sh.red[0][w];
+      y += sh.red[1][w];
+    }
+    a.ereq[i].st_part[seg] = x;
+    a.ereq[i].sd_part[seg] = y;
+  }
+}
+
+constexpr int kMaxRanges = (SPEC_MAX_V + kRangeElems - 1) / kRangeElems;
+
+struct FinalShared {
+  double T64[64];
+  double R[kMaxRanges];     // range weights, then inclusive prefix sums
+  double corr[kMaxRanges];  // weights of the recorded uncertain-sign tokens
+  double wsum[kEmitThreads / SPEC_WAVE];
+  double amb_w[kAmbCap];
+  int amb_v[kAmbCap];
+  int amb_sorted[kAmbCap];
+  int st, n, slow, use_t, sel, past, token;
+  double St, Sd, target, before;
+};
+
+// Exact weight of token v: residual (resid) or Q(z_t) (target row, any scale).
+template <bool BF16>
+__device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, double St, double Sd,
+                                         const double* T64) {
+  const double qt = q_at<BF16>(e.t, v, e.tht, e.invT, e.R, T64);
+  if (!resid) return qt;
+  const double qd = q_at<BF16>(e.d, v, e.thd, e.invT, e.R, T64);
+  return fmax(0.0, qt / St - qd / Sd);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) {
+  __shared__ FinalShared sh;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NW = kEmitThreads / SPEC_WAVE;
+  const int G = a.G, V = a.V;
+  init_t64(sh.T64);
+  if (tid == 0) {
+    int st, n;
+    request_decision(a, i, &st, &n);
+    sh.st = st;
+    sh.n = n;
+  }
+  __syncthreads();
+  const int st = sh.st, n = sh.n;
+  const int L = a.lengths ? a.lengths[i] : G;
+  if (a.status && tid == 0) a.status[i] = st;
+  if (st) {
+    if (tid == 0) a.num_accepted[i] = 0;
+    for (int k = tid; k <= G; k += blockDim.x) a.out_tokens[(size_t)i * (G + 1) + k] = -1;
+    if (a.accept_prob)
+      for (int k = tid; k < G; k += blockDim.x) a.accept_prob[(size_t)i * G + k] = NAN;
+    return;
+  }
+  if (tid == 0) a.num_accepted[i] = n;
+  if (a.accept_prob)
+    for (int k = tid; k < G; k += blockDim.x)
+      a.accept_prob[(size_t)i * G + k] = (k < L) ? (float)a.acc[(size_t)i * G + k].r : NAN;
+  for (int k = tid; k <= G; k += blockDim.x) {
+    if (k < n) a.out_tokens[(size_t)i * (G + 1) + k] = a.tokens[(size_t)i * G + k];
+    else if (k > n) a.out_tokens[(size_t)i * (G + 1) + k] = -1;
+  }
+  const bool greedy = a.greedy_only || a.temperature[i] == 0.f;
+  if (greedy) {
+    if (tid == 0) a.out_tokens[(size_t)i * (G + 1) + n] = a.rows_t[(size_t)i * (G + 1) + n].argmax;
+    return;
+  }
+
+  const EmitRows e = emit_rows<BF16>(a, i, n);
+  const bool resid = (e.d != nullptr);
+  const int NR = num_ranges(V);
+  const EmitReq* er = &a.ereq[i];
+  double ua, ue;
+  verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
+  if (tid == 0) {
+    double x = 0.0, y = 0.0;
+    for (int s = 0; s < kEmitSegs; ++s) {
+      x += er->st_part[s];
+      y += er->sd_part[s];
+    }
+    sh.St = x;
+    sh.Sd = y;
+    // the sign classification assumed cd * S_d / S_t = 1 to within half its margin
+    const double rho = resid ? e.cd * y / x : 1.0;
+    sh.slow = resid && (!(fabs(rho - 1.0) <= 0.5 * kAmbTol) || er->amb_n > kAmbCap);
+    sh.use_t = !resid;
+  }
+  __syncthreads();
+  const double St = sh.St, Sd = sh.Sd;
+  const bool slow = sh.slow;
+
+  // range weights
+  if (resid && !slow) {
+    const int na = er->amb_n;
+    for (int q = tid; q < na; q += blockDim.x) sh.amb_v[q] = a.amb[(size_t)i * kAmbCap + q];
+    for (int r = tid; r < NR; r += blockDim.x) sh.corr[r] = 0.0;
+    __syncthreads();
+    for (int q = tid; q < na; q += blockDim.x) {
+      const int v = sh.amb_v[q];
+      int rank = 0;
+      for (int p = 0; p < na; ++p) rank += sh.amb_v[p] < v;
+      sh.amb_sorted[rank] = v;
+      sh.amb_w[rank] = weight<BF16>(e, v, true, St, Sd, sh.T64);
+    }
+    __syncthreads();
+    if (tid == 0)
+      for (int q = 0; q < na; ++q) sh.corr[sh.amb_sorted[q] / kRangeElems] += sh.amb_w[q];
+    __syncthreads();
+    for (int r = tid; r < NR; r += blockDim.x) {
+      const EmitRange g = a.ranges[(size_t)i * NR + r];
+      sh.R[r] = (g.a / St - g.d / Sd) + sh.corr[r];
+    }
+  } else if (resid && slow) {
+    // exact weight of every token (rare: nearly identical target and draft rows)
+    for (int r = 0; r < NR; ++r) {
+      double s = 0.0;
+      for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += blockDim.x)
+        s += weight<BF16>(e, v, true, St, Sd, sh.T64);
+      s = wave_sum(s);
+      if (lane == 0) sh.wsum[wave] = s;
+      __syncthreads();
+      if (tid == 0) {
+        double t = 0.0;
+        for (int w = 0; w < NW; ++w) t += sh.wsum[w];
+        sh.R[r] = t;
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = a.ranges[(size_t)i * NR + r].t;
+  }
+  __syncthreads();
+
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    // inclusive prefix over ranges (sequential: at most a few hundred ranges)
+    if (tid == 0) {
+      double run = 0.0;
+      for (int r = 0; r < NR; ++r) {
+        run += sh.R[r];
+        sh.R[r] = run;
+      }
+      const double W = run;
+      if (resid && !sh.use_t && !(W > 0.0)) {
+        sh.use_t = 2;  // no residual mass (rounding): fall back to p_t of the same row
+      } else {
+        const double target = ue * W;
+        int lo = 0, hi = NR;  // first r with prefix > target
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (sh.R[mid] > target) hi = mid;
+          else lo = mid + 1;
+        }
+        sh.target = target;
+        sh.past = (lo >= NR);
+        sh.sel = lo;
+        sh.before = (lo > 0 && lo < NR) ? sh.R[lo - 1] : 0.0;
+      }
+    }
+    __syncthreads();
+    if (sh.use_t != 2) break;
+    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = a.ranges[(size_t)i * NR + r].t;
+    if (tid == 0) sh.use_t = 1;
+    __syncthreads();
+  }
+  const bool wres = resid && sh.use_t == 0;
+
+  if (sh.past) {
+    // target at or beyond the total (rounding): the last token with positive weight
+    if (tid == 0) sh.token = -1;
+    __syncthreads();
+    for (int r = NR - 1; r >= 0; --r) {
+      int best = -1;
+      for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += blockDim.x)
+        if (weight<BF16>(e, v, wres, St, Sd, sh.T64) > 0.0) best = v;
+      best = wave_max_i(best);
+      if (lane == 0) sh.wsum[wave] = (double)best;
+      __syncthreads();
+      if (tid == 0) {
+        int b = -1;
+        for (int w = 0; w < NW; ++w) b = max(b, (int)sh.wsum[w]);
+        if (b >= 0) sh.token = b;
+      }
+      __syncthreads();
+      if (sh.token >= 0) break;
+    }
+  } else {
+    // the selected range, token by token: thread t holds tokens base + 8t .. base + 8t + 7
+  static_assert(kEmitThreads * 8 == kRangeElems, "one token octet per thread");
+    const int base = sh.sel * kRangeElems + tid * 8;
+    double w[8];
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int v = base + j;
+      w[j] = (v < V) ? weight<BF16>(e, v, wres, St, Sd, sh.T64) : 0.0;
+      s += w[j];
+    }
+    const double incl = wave_inclusive_sum(s, lane);
+    if (lane == 63) sh.wsum[wave] = incl;
+    __syncthreads();
+    double wb = 0.0;
+    for (int q = 0; q < wave; ++q) wb += sh.wsum[q];
+    const double P = sh.before + wb, target = sh.target;
+    const double excl = incl - s;
+    const bool cross = (P + incl > target);
+    // first thread whose running total passes the target
+    const unsigned long long m = __ballot(cross);
+    if (lane == 0) sh.amb_v[wave] = m ? (int)(__ffsll((long long)m) - 1) : 64;
+    const unsigned long long pos = __ballot(s > 0.0);
+    if (lane == 0) sh.amb_v[NW + wave] = pos ? 63 - __clzll((long long)pos) : -1;
+    __syncthreads();
+    int cw = -1, cl = -1;
+    for (int q = 0; q < NW && cw < 0; ++q)
+      if (sh.amb_v[q] < 64) {
+        cw = q;
+        cl = sh.amb_v[q];
+      }
+    if (cw < 0) {  // rounding left no crossing: the last thread with weight
+      for (int q = NW - 1; q >= 0 && cw < 0; --q)
+        if (sh.amb_v[NW + q] >= 0) {
+          cw = q;
+          cl = sh.amb_v[NW + q];
+        }
+    }
+    if (wave == cw && lane == cl) {
+      double acc = P + excl;
+      int tok = -1, lastpos = -1;
+      for (int j = 0; j < 8; ++j) {
+        if (w[j] > 0.0) lastpos = base + j;
+        acc += w[j];
+        if (tok < 0 && acc > target && w[j] > 0.0) tok = base + j;
+      }
+      sh.token = (tok >= 0) ? tok : lastpos;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) a.out_tokens[(size_t)i * (G + 1) + n] = sh.token;
+}
+
+void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s) {
+  if (!a.greedy_only) {
+    if (bf16)
+      hipLaunchKernelGGL(emit_pass_kernel<true>, dim3(a.B * kEmitSegs), dim3(kPassThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(emit_pass_kernel<false>, dim3(a.B * kEmitSegs), dim3(kPassThreads), 0, s, a);
+  }
+  if (bf16)
+    hipLaunchKernelGGL(emit_final_kernel<true>, dim3(a.B), dim3(kEmitThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(emit_final_kernel<false>, dim3(a.B), dim3(kEmitThreads), 0, s, a);
+}
+
+}  // namespace spec

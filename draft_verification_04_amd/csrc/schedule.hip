@@ -14,8 +14,9 @@
 //
 // Steps: survivals and 64-bit sort keys (inverted survival bits | candidate
 // index, so ascending key = survival descending, then request, then
-// position) -> bitonic sort in LDS -> exclusive int64 scan -> Theta(m) ->
-// first non-rise (early stop) or first maximum (global) -> per-request counts.
+// position) -> bitonic sort held in registers (lane shuffles, LDS only for the
+// longest strides) -> exclusive int64 scan -> Theta(m) -> first non-rise
+// (early stop) or first maximum (global) -> per-request counts.
 #include "common.hpp"
 #include "spec_verify.h"
 
@@ -43,7 +44,6 @@ struct SchedShared {
   int wm[kSchedThreads / SPEC_WAVE];
   int ncand;
   int mstar;
-  double theta_star;
 };
 
 __device__ __forceinline__ long long fixed_q(float a) {
@@ -55,90 +55,144 @@ __device__ __forceinline__ double theta_of(long long tau, double sps) {
   return ((double)tau * 0x1p-50) * sps;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedArgs a) {
-  __shared__ SchedShared sh;
+// Bitonic sort of NP = K * kSchedThreads keys, ascending; thread t holds positions t*K .. t*K+K-1.
+// Strides below K compare in registers, strides below 64*K across lanes of a wave, longer ones
+// through LDS.
+template <int K>
+__device__ __forceinline__ void bitonic_regs(unsigned long long (&key)[K], unsigned long long* lds, int tid,
+                                             int lane) {
+  constexpr int NP = K * kSchedThreads;
+  for (int size = 2; size <= NP; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < K) {
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+          const int pe = e ^ stride;
+          if (pe > e) {
+            const int pos = tid * K + e;
+            const bool up = (pos & size) == 0;
+            const unsigned long long x = key[e], y = key[pe];
+            if ((x > y) == up) {
+              key[e] = y;
+              key[pe] = x;
+            }
+          }
+        }
+      } else if (stride < 64 * K) {
+        const int lx = stride / K;
+        const bool lower = (lane & lx) == 0;
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+          const int pos = tid * K + e;
+          const bool up = (pos & size) == 0;
+          const unsigned long long y = __shfl_xor(key[e], lx, SPEC_WAVE);
+          const unsigned long long x = key[e];
+          // the lower position keeps the smaller key when ascending
+          key[e] = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+        }
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < K; ++e) lds[tid * K + e] = key[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+          const int pos = tid * K + e;
+          const bool up = (pos & size) == 0;
+          const bool lower = (pos & stride) == 0;
+          const unsigned long long y = lds[pos ^ stride];
+          const unsigned long long x = key[e];
+          key[e] = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+        }
+      }
+    }
+  }
+}
+
+template <int K>
+__device__ void schedule_body(const SchedArgs& a, SchedShared& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int NW = kSchedThreads / SPEC_WAVE;
   const int B = a.B, G = a.G;
   const int N = B * G;
-  int NP = 1;
-  while (NP < N) NP <<= 1;
+  constexpr int NP = K * kSchedThreads;
   if (tid == 0) sh.ncand = 0;
-  for (int p = N + tid; p < NP; p += kSchedThreads) sh.keys[p] = ~0ull;
+  // confidences staged in the key slots (coalesced loads); each request's thread then reads
+  // its slots and overwrites them with the keys
+  for (int p = tid; p < NP; p += kSchedThreads)
+    sh.keys[p] = (p < N) ? (unsigned long long)__float_as_uint(a.conf[p]) : ~0ull;
   __syncthreads();
 
   // survival products and keys, one request per thread
   for (int r = tid; r < B; r += kSchedThreads) {
-    const float* c = a.conf + (size_t)r * G;
+    unsigned long long* c = sh.keys + (size_t)r * G;   // confidence bits, read before overwritten
     int bad = 0;
-    for (int j = 0; j < G; ++j) bad |= !(c[j] >= 0.f && c[j] <= 1.f);
+    for (int j = 0; j < G; ++j) {
+      const float cj = __uint_as_float((unsigned)c[j]);
+      bad |= !(cj >= 0.f && cj <= 1.f);
+    }
     if (a.status) a.status[r] = bad ? SPEC_REQ_BAD_CONFIDENCE : 0;
     float s = 1.f;
     int n = 0;
     for (int j = 0; j < G; ++j) {
-      s = (j == 0) ? c[0] : __fmul_rn(s, c[j]);
+      const float cj = __uint_as_float((unsigned)c[j]);
+      s = (j == 0) ? cj : __fmul_rn(s, cj);
       unsigned long long key = ~0ull;
       if (!bad && s > 0.f) {
         key = ((unsigned long long)(~__float_as_uint(s)) << 32) | (unsigned)(r * G + j);
         ++n;
       }
-      sh.keys[r * G + j] = key;
+      c[j] = key;
     }
     if (n) atomicAdd(&sh.ncand, n);
   }
   __syncthreads();
-
-  // bitonic sort, ascending
-  for (int size = 2; size <= NP; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (NP >> 1); t += kSchedThreads) {
-        const int pos = 2 * t - (t & (stride - 1));
-        const int par = pos + stride;
-        const unsigned long long x = sh.keys[pos], y = sh.keys[par];
-        const bool up = (pos & size) == 0;
-        if ((x > y) == up) {
-          sh.keys[pos] = y;
-          sh.keys[par] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
+  unsigned long long key[K];
+#pragma unroll
+  for (int e = 0; e < K; ++e) key[e] = sh.keys[tid * K + e];
+  bitonic_regs<K>(key, sh.keys, tid, lane);
 
   const int E = sh.ncand;
   int m_max = a.budget - B;
   if (m_max > E) m_max = E;
   if (m_max < 0) m_max = 0;
 
-  // exclusive scan of q over sorted positions 0 .. m_max-1 (chunk per thread)
-  const int cpt = (NP + kSchedThreads - 1) / kSchedThreads;
-  const int p0 = tid * cpt;
+  // exclusive scan of q over sorted positions 0 .. m_max-1 (K per thread)
+  const int p0 = tid * K;
+  long long q[K];
   long long local = 0;
-  for (int p = p0; p < p0 + cpt; ++p)
-    if (p < m_max) local += fixed_q(__uint_as_float(~(unsigned)(sh.keys[p] >> 32)));
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    q[e] = (p0 + e < m_max) ? fixed_q(__uint_as_float(~(unsigned)(key[e] >> 32))) : 0;
+    local += q[e];
+  }
   long long incl = wave_inclusive_sum_i64(local, lane);
+  __syncthreads();
   if (lane == 63) sh.wsum[wave] = incl;
   __syncthreads();
   long long before = 0;
   for (int w = 0; w < wave; ++w) before += sh.wsum[w];
   long long tau = (long long)B * kOne + before + (incl - local);  // tau at m = p0
+  const long long tau_p0 = tau;
 
   // Theta along the path; admission m uses sorted position m-1
   const double th0 = theta_of((long long)B * kOne, a.sps[B]);
   int brk = 0x7fffffff;           // first m >= 1 with Theta(m) <= Theta(m-1)
   double best = -INFINITY;        // global: max Theta over this thread's m
   int best_m = 0x7fffffff;
-  for (int p = p0; p < p0 + cpt; ++p) {
-    const int m = p + 1;
-    if (m > m_max) break;
-    const long long prev = tau;
-    tau += fixed_q(__uint_as_float(~(unsigned)(sh.keys[p] >> 32)));
-    const double tm = theta_of(tau, a.sps[B + m]);
-    const double tp = theta_of(prev, a.sps[B + m - 1]);
-    if (!(tm > tp) && m < brk) brk = m;
-    if (tm > best) {
-      best = tm;
-      best_m = m;
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    const int m = p0 + e + 1;
+    if (m <= m_max) {
+      const long long prev = tau;
+      tau += q[e];
+      const double tm = theta_of(tau, a.sps[B + m]);
+      const double tp = theta_of(prev, a.sps[B + m - 1]);
+      if (!(tm > tp) && m < brk) brk = m;
+      if (tm > best) {
+        best = tm;
+        best_m = m;
+      }
     }
   }
   // block reductions
@@ -163,7 +217,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedArgs a) {
   __syncthreads();
   if (tid == 0) {
     int mstar;
-    double th;
     if (a.mode == SPEC_SCHED_EARLY_STOP) {
       int b = 0x7fffffff;
       for (int w = 0; w < NW; ++w) b = min(b, sh.wm[w]);
@@ -181,22 +234,35 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedArgs a) {
       }
       mstar = bm;
     }
-    // Theta at m*: recompute tau exactly
-    long long t = (long long)B * kOne;
-    for (int p = 0; p < mstar; ++p) t += fixed_q(__uint_as_float(~(unsigned)(sh.keys[p] >> 32)));
-    th = theta_of(t, a.sps[B + mstar]);
     sh.mstar = mstar;
-    sh.theta_star = th;
-    if (a.theta) a.theta[0] = th;
+    if (mstar == 0 && a.theta) a.theta[0] = th0;
   }
   for (int r = tid; r < B; r += kSchedThreads) a.lengths[r] = 0;
   __syncthreads();
   const int mstar = sh.mstar;
-  for (int p = tid; p < mstar; p += kSchedThreads) {
-    const unsigned idx = (unsigned)(sh.keys[p] & 0xffffffffu);
-    const int r = (int)(idx / (unsigned)G), j = (int)(idx % (unsigned)G);
-    atomicMax(&a.lengths[r], j + 1);
+  // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
+  if (mstar > 0 && mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
+    long long t = tau_p0;
+#pragma unroll
+    for (int e = 0; e < K; ++e)
+      if (p0 + e < mstar) t += q[e];
+    a.theta[0] = theta_of(t, a.sps[B + mstar]);
   }
+  // per-request counts: admitted positions form a prefix of each request's candidates
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    if (p0 + e < mstar) {
+      const unsigned idx = (unsigned)(key[e] & 0xffffffffu);
+      const int r = (int)(idx / (unsigned)G), j = (int)(idx % (unsigned)G);
+      atomicMax(&a.lengths[r], j + 1);
+    }
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedArgs a) {
+  __shared__ SchedShared sh;
+  schedule_body<K>(a, sh);
 }
 
 }  // namespace spec
@@ -224,6 +290,12 @@ extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* 
   if (m_cap > (long long)B * gamma) m_cap = (long long)B * gamma;
   if ((long long)sps_len <= (long long)B + m_cap) return SPEC_ERR_INVALID_ARG;
   SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, status};
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const long long n = (long long)B * gamma;
+  if (n <= 1 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, s, a);
+  else if (n <= 2 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, s, a);
+  else if (n <= 4 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, s, a);
+  else if (n <= 8 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<8>, dim3(1), dim3(kSchedThreads), 0, s, a);
+  else hipLaunchKernelGGL(schedule_kernel<16>, dim3(1), dim3(kSchedThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -1,6 +1,5 @@
 // Lossless draft verification on gfx950: work list, row-streaming statistics
-// with the acceptance test, and the per-request finish (first rejection,
-// correction / appended token, outputs).
+// with the acceptance test.  The emitted token is computed in emit.hip.
 //
 // What is computed follows the DSpark paper, §2.1 (accept x_k with
 // probability min(1, p_t(x_k) / p_d(x_k)), left to right, the first
@@ -17,8 +16,7 @@
 //                    computes log2-sum-exp of z * log2(e) / T (or the argmax
 //                    for the greedy rule, or the top-k threshold first), then
 //                    the acceptance test of x_k with its Philox uniform.
-//   finish_kernel    one workgroup per request: first rejection n, outputs,
-//                    and the emitted token by an fp64 inverse CDF over row n.
+//   (emit.hip)       the emitted token of every request and all outputs.
 #include "common.hpp"
 #include "philox.hpp"
 #include "verify_impl.hpp"
@@ -28,9 +26,6 @@
 #include <math.h>
 
 namespace spec {
-
-static constexpr double kLn2 = 0.69314718055994530942;
-static constexpr double kLog2e = 1.44269504088896340736;
 
 // ---------------------------------------------------------------------------
 // worklist
@@ -48,6 +43,7 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
   __syncthreads();
   for (int i = tid; i < B; i += blockDim.x) {
     a.req_status[i] = 0;
+    a.ereq[i].amb_n = 0;
     const int L = a.lengths ? a.lengths[i] : G;
     if (L >= 0 && L <= G) atomicAdd(&hist[L], 1);
   }
@@ -494,7 +490,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   const int G = a.G, V = a.V;
   constexpr int ES = BF16 ? 2 : 4;
   const float T = a.greedy_only ? 0.f : a.temperature[i];
-  if (!(T >= 0.f && T < INFINITY)) return;          // reported by the finish kernel
+  if (!(T >= 0.f && T < INFINITY)) return;          // reported by emit_final_kernel
   int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
   if (K < 0) return;
   if (K >= V) K = 0;
@@ -590,245 +586,6 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// finish: first rejection, emitted token (fp64 inverse CDF), outputs
-// ---------------------------------------------------------------------------
-
-constexpr int kEmitChunk = 8;                                  // elements per thread per tile
-constexpr int kEmitTile = kFinishThreads * kEmitChunk;         // 8192
-constexpr int kEmitMaxTiles = (SPEC_MAX_V + kEmitTile - 1) / kEmitTile;
-
-struct FinishShared {
-  double tw[kEmitMaxTiles][kFinishThreads / SPEC_WAVE];   // tile x wave partial sums
-  double red[2][kFinishThreads / SPEC_WAVE];
-  int ired[kFinishThreads / SPEC_WAVE];
-  int n;
-  int st;
-  int token;
-  int sel_tile, sel_wave, past_end, use_pt;
-  double sel_prefix, target;
-  double lse_t, lse_d;
-};
-
-// Weight of token v in the emit row (fp64): max(0, p_t - p_d) after a
-// rejection, p_t (up to a common factor) otherwise.
-template <bool BF16>
-__device__ __forceinline__ double emit_weight(const char* trow, const char* drow, int v, double invT,
-                                              float tht, float thd, double lse_t, double lse_d, bool resid) {
-  const float zt = load_elem<BF16>(trow, v);
-  const double pt = (zt >= tht) ? exp((double)zt * invT - lse_t) : 0.0;
-  if (!resid) return pt;
-  const float zd = load_elem<BF16>(drow, v);
-  const double pd = (zd >= thd) ? exp((double)zd * invT - lse_d) : 0.0;
-  return fmax(0.0, pt - pd);
-}
-
-template <bool BF16>
-__device__ int emit_token(FinishShared& sh, const char* trow, const char* drow, int V, double T, float tht,
-                          float thd, double R_t, double R_d, double u) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int NW = kFinishThreads / SPEC_WAVE;
-  const bool resid = (drow != nullptr);
-  // y = z / T as one fp64 division per element
-  double lse_t = R_t, lse_d = R_d;
-  if (resid) {
-    double st = 0.0, sd = 0.0;
-    for (int v = tid; v < V; v += kFinishThreads) {
-      const float zt = load_elem<BF16>(trow, v);
-      const float zd = load_elem<BF16>(drow, v);
-      if (zt >= tht) st += exp((double)zt / T - R_t);
-      if (zd >= thd) sd += exp((double)zd / T - R_d);
-    }
-    st = wave_sum(st);
-    sd = wave_sum(sd);
-    if (lane == 0) {
-      sh.red[0][wave] = st;
-      sh.red[1][wave] = sd;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double a = 0.0, b = 0.0;
-      for (int w = 0; w < NW; ++w) {
-        a += sh.red[0][w];
-        b += sh.red[1][w];
-      }
-      sh.lse_t = R_t + log(a);
-      sh.lse_d = R_d + log(b);
-    }
-    __syncthreads();
-    lse_t = sh.lse_t;
-    lse_d = sh.lse_d;
-  }
-  const int ntiles = (V + kEmitTile - 1) / kEmitTile;
-  bool use_resid = resid;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    int last_pos = -1;
-    for (int t = 0; t < ntiles; ++t) {
-      const int base = t * kEmitTile + tid * kEmitChunk;
-      double s = 0.0;
-#pragma unroll
-      for (int j = 0; j < kEmitChunk; ++j) {
-        const int v = base + j;
-        if (v < V) {
-          const double w = emit_weight<BF16>(trow, drow, v, 1.0 / T, tht, thd, lse_t, lse_d, use_resid);
-          s += w;
-          if (w > 0.0) last_pos = v;
-        }
-      }
-      const double incl = wave_inclusive_sum(s, lane);
-      if (lane == 63) sh.tw[t][wave] = incl;
-    }
-    const int lp = wave_max_i(last_pos);
-    if (lane == 0) sh.ired[wave] = lp;
-    __syncthreads();
-    if (tid == 0) {
-      double W = 0.0;
-      for (int t = 0; t < ntiles; ++t)
-        for (int w = 0; w < NW; ++w) W += sh.tw[t][w];
-      sh.use_pt = 0;
-      if (use_resid && !(W > 0.0)) {
-        sh.use_pt = 1;  // no residual mass (rounding): fall back to p_t of the same row
-      } else {
-        const double target = u * W;
-        double P = 0.0;
-        int ft = -1, fw = -1;
-        for (int t = 0; t < ntiles && ft < 0; ++t)
-          for (int w = 0; w < NW; ++w) {
-            const double s = sh.tw[t][w];
-            if (P + s > target) {
-              ft = t;
-              fw = w;
-              break;
-            }
-            P += s;
-          }
-        int last = -1;
-        for (int w = 0; w < NW; ++w) last = max(last, sh.ired[w]);
-        sh.sel_tile = ft;
-        sh.sel_wave = fw;
-        sh.sel_prefix = P;
-        sh.target = target;
-        sh.past_end = (ft < 0);
-        sh.token = last;
-      }
-    }
-    __syncthreads();
-    if (!sh.use_pt) break;
-    use_resid = false;
-    __syncthreads();
-  }
-  if (sh.past_end) return sh.token;  // target beyond the total (rounding): last token with weight
-  // crossing wave: recompute its lanes' chunk sums in the same order
-  if (wave == sh.sel_wave) {
-    const int t = sh.sel_tile;
-    const int base = t * kEmitTile + tid * kEmitChunk;
-    double w[kEmitChunk];
-    double s = 0.0;
-#pragma unroll
-    for (int j = 0; j < kEmitChunk; ++j) {
-      const int v = base + j;
-      w[j] = (v < V) ? emit_weight<BF16>(trow, drow, v, 1.0 / T, tht, thd, lse_t, lse_d, !sh.use_pt && resid)
-                     : 0.0;
-      s += w[j];
-    }
-    const double incl = wave_inclusive_sum(s, lane);
-    const double excl = incl - s;
-    const double P = sh.sel_prefix, target = sh.target;
-    const bool crosses = (P + incl > target);
-    const unsigned long long m = __ballot(crosses);
-    const int fl = m ? __ffsll((long long)m) - 1 : 63;
-    if (lane == fl) {
-      double acc = P + (m ? excl : incl - s);
-      int tok = -1, lastpos = -1;
-      for (int j = 0; j < kEmitChunk; ++j) {
-        if (w[j] > 0.0) lastpos = base + j;
-        acc += w[j];
-        if (tok < 0 && acc > target && w[j] > 0.0) tok = base + j;
-      }
-      if (tok < 0) tok = lastpos;
-      sh.token = tok;
-    }
-  }
-  __syncthreads();
-  return sh.token;
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(kFinishThreads) void finish_kernel(VerifyArgs a) {
-  __shared__ FinishShared sh;
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int G = a.G, V = a.V;
-  constexpr int ES = BF16 ? 2 : 4;
-  const int L = a.lengths ? a.lengths[i] : G;
-  const float T = a.greedy_only ? 0.f : a.temperature[i];
-  const int K0 = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
-  if (tid == 0) {
-    int st = 0;
-    if (L < 0 || L > G) {
-      st = SPEC_REQ_BAD_LENGTH;
-    } else {
-      if (!(T >= 0.f && T < INFINITY)) st |= SPEC_REQ_BAD_TEMPERATURE;
-      if (K0 < 0) st |= SPEC_REQ_BAD_TOPK;
-      for (int k = 0; k < L; ++k) {
-        const int x = a.tokens[(size_t)i * G + k];
-        if (x < 0 || x >= V) st |= SPEC_REQ_BAD_TOKEN;
-      }
-      if (st == 0) st |= a.req_status[i];
-    }
-    int n = 0;
-    if (st == 0) {
-      n = L;
-      for (int k = 0; k < L; ++k)
-        if (!a.acc[(size_t)i * G + k].accept) {
-          n = k;
-          break;
-        }
-    }
-    sh.st = st;
-    sh.n = n;
-  }
-  __syncthreads();
-  const int st = sh.st, n = sh.n;
-  if (a.status && tid == 0) a.status[i] = st;
-  if (st) {
-    if (tid == 0) a.num_accepted[i] = 0;
-    for (int k = tid; k <= G; k += blockDim.x) a.out_tokens[(size_t)i * (G + 1) + k] = -1;
-    if (a.accept_prob)
-      for (int k = tid; k < G; k += blockDim.x) a.accept_prob[(size_t)i * G + k] = NAN;
-    return;
-  }
-  if (a.accept_prob)
-    for (int k = tid; k < G; k += blockDim.x)
-      a.accept_prob[(size_t)i * G + k] = (k < L) ? (float)a.acc[(size_t)i * G + k].r : NAN;
-  int tok;
-  if (a.greedy_only || T == 0.f) {
-    tok = a.rows_t[(size_t)i * (G + 1) + n].argmax;
-  } else {
-    const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
-    const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + n) * V * ES;
-    const char* drow = nullptr;
-    float thd = -INFINITY;
-    double Rd = 0.0;
-    if (n < L) {
-      const RowStat rd = a.rows_d[(size_t)i * G + n];
-      drow = reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + n) * V * ES;
-      thd = rd.theta;
-      Rd = rd.lse2 * kLn2;
-    }
-    double ua, ue;
-    verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
-    tok = emit_token<BF16>(sh, trow, drow, V, (double)T, rt.theta, thd, rt.lse2 * kLn2, Rd, ue);
-  }
-  if (tid == 0) a.num_accepted[i] = n;
-  for (int k = tid; k <= G; k += blockDim.x) {
-    int o = -1;
-    if (k < n) o = a.tokens[(size_t)i * G + k];
-    else if (k == n) o = tok;
-    a.out_tokens[(size_t)i * (G + 1) + k] = o;
-  }
-}
-
 __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, const int32_t* pos, double* ua,
                               double* ue) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
@@ -846,10 +603,10 @@ __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, c
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t rows_t, rows_d, acc, items, nitems, req_status, total;
+  size_t rows_t, rows_d, acc, items, nitems, req_status, ereq, ranges, amb, total;
 };
 
-static WsLayout ws_layout(int B, int G) {
+static WsLayout ws_layout(int B, int G, int V) {
   WsLayout l;
   size_t o = 0;
   l.rows_t = o; o = align256(o + sizeof(RowStat) * (size_t)B * (G + 1));
@@ -858,6 +615,9 @@ static WsLayout ws_layout(int B, int G) {
   l.items = o; o = align256(o + sizeof(int32_t) * (size_t)B * (G + 1));
   l.nitems = o; o = align256(o + sizeof(int32_t));
   l.req_status = o; o = align256(o + sizeof(int32_t) * (size_t)B);
+  l.ereq = o; o = align256(o + sizeof(EmitReq) * (size_t)B);
+  l.ranges = o; o = align256(o + sizeof(EmitRange) * (size_t)B * num_ranges(V));
+  l.amb = o; o = align256(o + sizeof(int32_t) * (size_t)B * kAmbCap);
   l.total = o;
   return l;
 }
@@ -875,7 +635,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
                              void* ev1) {
-  const WsLayout l = ws_layout(a.B, a.G);
+  const WsLayout l = ws_layout(a.B, a.G, a.greedy_only ? 1 : a.V);  // greedy: no emit ranges
   if (!ws || ws_bytes < l.total) return SPEC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return SPEC_ERR_WORKSPACE;
   char* w = reinterpret_cast<char*>(ws);
@@ -885,6 +645,9 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   a.items = reinterpret_cast<int32_t*>(w + l.items);
   a.nitems = reinterpret_cast<int32_t*>(w + l.nitems);
   a.req_status = reinterpret_cast<int32_t*>(w + l.req_status);
+  a.ereq = reinterpret_cast<EmitReq*>(w + l.ereq);
+  a.ranges = reinterpret_cast<EmitRange*>(w + l.ranges);
+  a.amb = reinterpret_cast<int32_t*>(w + l.amb);
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   if (ev0) hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);
   const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1));
@@ -893,10 +656,7 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   else
     hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   if (ev1) hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
-  if (dtype == SPEC_BF16)
-    hipLaunchKernelGGL(finish_kernel<true>, dim3(a.B), dim3(kFinishThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(finish_kernel<false>, dim3(a.B), dim3(kFinishThreads), 0, s, a);
+  launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
@@ -905,14 +665,13 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
 using namespace spec;
 
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V) {
-  (void)V;
-  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
-  return ws_layout(B, gamma).total;
+  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_V) return 0;
+  return ws_layout(B, gamma, V).total;
 }
 
 extern "C" size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
-  return ws_layout(B, gamma).total;
+  return ws_layout(B, gamma, 1).total;
 }
 
 extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,

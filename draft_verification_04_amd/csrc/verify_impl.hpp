@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "spec_verify.h"
+
 namespace spec {
 
 // Per logit row, written by the streaming kernel.
@@ -18,6 +20,24 @@ struct AccRec {
   double r;        // min(1, p_t(x)/p_d(x)) (greedy: 1 match / 0 mismatch)
   int32_t accept;  // 1 accepted, 0 rejected
   int32_t valid;   // 1 when computed
+};
+
+// Emitted-token work: one range = kRangeElems consecutive tokens of the emit row.
+constexpr int kRangeElems = 2048; // tokens per emit range (one wave, 4 steps of 64 x 8)
+constexpr int kEmitSegs = 2;      // workgroups per request in the emit pass
+constexpr int kAmbCap = 256;      // tokens of uncertain residual sign recorded per request
+
+struct EmitRange {
+  double a;  // sum of E_t over tokens with p_t > p_d
+  double d;  // sum of E_d over the same tokens
+  double t;  // sum of E_t over every token
+};
+
+struct EmitReq {
+  double st_part[kEmitSegs];  // per-segment sums of E_t = exp(z_t/T - R_t)
+  double sd_part[kEmitSegs];  // per-segment sums of E_d = exp(z_d/T - R_d)
+  int32_t amb_n;              // number of uncertain-sign tokens seen
+  int32_t pad;
 };
 
 struct VerifyArgs {
@@ -41,12 +61,54 @@ struct VerifyArgs {
   int32_t* items;      // [B * (G+1)] work items, (request << 7) | position
   int32_t* nitems;     // [1]
   int32_t* req_status; // [B] SPEC_REQ_* bits raised while streaming
+  EmitReq* ereq;       // [B]
+  EmitRange* ranges;   // [B, ceil(V / kRangeElems)]
+  int32_t* amb;        // [B, kAmbCap]
 };
 
 constexpr int kStreamThreads = 512;
-constexpr int kFinishThreads = 1024;
 constexpr int kWorklistThreads = 1024;
+constexpr int kPassThreads = 512;    // emit pass workgroup
+constexpr int kEmitThreads = 256;    // emit final workgroup (x 8 tokens = one range)
 constexpr int kTopkCap = 4096;   // top-k candidates kept in LDS per row
 constexpr int kTopkPre = 4;      // vectors per thread sampled for the top-k lower bound
+
+static constexpr double kLn2 = 0.69314718055994530942;
+static constexpr double kLog2e = 1.44269504088896340736;
+
+__host__ __device__ inline int num_ranges(int V) { return (V + kRangeElems - 1) / kRangeElems; }
+
+// Status and first rejection of request i (call from one thread).
+__device__ inline void request_decision(const VerifyArgs& a, int i, int* st_out, int* n_out) {
+  const int G = a.G, V = a.V;
+  const int L = a.lengths ? a.lengths[i] : G;
+  int st = 0, n = 0;
+  if (L < 0 || L > G) {
+    st = SPEC_REQ_BAD_LENGTH;
+  } else {
+    const float T = a.greedy_only ? 0.f : a.temperature[i];
+    const int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+    if (!(T >= 0.f && T < __builtin_inff())) st |= SPEC_REQ_BAD_TEMPERATURE;
+    if (K < 0) st |= SPEC_REQ_BAD_TOPK;
+    for (int k = 0; k < L; ++k) {
+      const int x = a.tokens[(size_t)i * G + k];
+      if (x < 0 || x >= V) st |= SPEC_REQ_BAD_TOKEN;
+    }
+    if (st == 0) st |= a.req_status[i];
+    if (st == 0) {
+      n = L;
+      for (int k = 0; k < L; ++k)
+        if (!a.acc[(size_t)i * G + k].accept) {
+          n = k;
+          break;
+        }
+    }
+  }
+  *st_out = st;
+  *n_out = n;
+}
+
+// Launch the emitted-token kernels (defined in emit.hip).
+void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s);
 
 }  // namespace spec

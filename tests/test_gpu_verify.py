@@ -229,3 +229,26 @@ def test_full_mixed_sampled(sv):
     ref = run_oracle(w, requests=req)
     s = compare_verify(out, ref, requests=req)
     print("mixed", s)
+
+
+def test_nearly_identical_rows_take_the_exact_residual_path(sv):
+    """Draft equal to the target except one low-probability token: almost every
+    token's residual sign sits inside the classification margin, so the emit
+    must fall back to weighing every token exactly."""
+    rng = np.random.default_rng(41)
+    B, G, V = 256, 1, 40000
+    base = rng.normal(0, 3, (1, G + 1, V)).astype(np.float32)
+    t = np.repeat(base, B, axis=0)
+    d = t[:, :G].copy()
+    x = np.zeros((B, G), dtype=np.int32)
+    lo = int(np.argmin(base[0, 0]))
+    d[:, 0, lo] += 12.0                 # the draft over-weights one token
+    x[:, 0] = lo                        # ... and proposes it: r = p_t/p_d is small
+    for dt in (torch.float32, torch.bfloat16):
+        tt = torch.from_numpy(t).to(DEV).to(dt)
+        dd = torch.from_numpy(d).to(DEV).to(dt)
+        out = sv.verify(tt, dd, torch.from_numpy(x).to(DEV))
+        torch.cuda.synchronize()
+        ref = oracle.verify(tt, dd, x)
+        s = compare_verify(out, ref)
+        assert (ref["num_accepted"] == 0).sum() > B // 2, s   # mostly rejected -> residual draws
