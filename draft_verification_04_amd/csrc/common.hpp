@@ -10,6 +10,14 @@ namespace spec {
 
 // ---- element loads -------------------------------------------------------
 
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked nontemporal (streamed once; keeps caches for data that is reused).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bf16 -> fp32 is exact: a bf16 value is the high half of an fp32 word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -175,19 +175,20 @@ __device__ __forceinline__ void accum(const float (&z)[N], float c_hi, float c_l
   S += s;
 }
 
+// Vectors [vb, ve) of a row's 16-byte body, plus its scalar head and tail when `ends`.
 template <bool BF16>
-__device__ void stream_sum(const char* row, int V, float c_hi, float c_lo, int lt, int nthr, float& M,
-                           float& S, int& bad) {
+__device__ void stream_sum(const char* row, int V, int vb, int ve, bool ends, float c_hi, float c_lo, int lt,
+                           int nthr, float& M, float& S, int& bad) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int U = 4;
   const RowGeom g = row_geom<BF16>(row, V);
   const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
-  int v = lt;
-  for (; v + (U - 1) * nthr < g.nvec; v += U * nthr) {
+  int v = vb + lt;
+  for (; v + (U - 1) * nthr < ve; v += U * nthr) {
     uint4 d[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = vp[v + u * nthr];
+    for (int u = 0; u < U; ++u) d[u] = load_nt(vp + v + u * nthr);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float z[EPV];
@@ -195,20 +196,23 @@ __device__ void stream_sum(const char* row, int V, float c_hi, float c_lo, int l
       accum<EPV>(z, c_hi, c_lo, M, S, bad);
     }
   }
-  for (; v < g.nvec; v += nthr) {
+  for (; v < ve; v += nthr) {
     float z[EPV];
-    unpack<BF16>(vp[v], z);
+    unpack<BF16>(load_nt(vp + v), z);
     accum<EPV>(z, c_hi, c_lo, M, S, bad);
   }
-  float z[2] = {-INFINITY, -INFINITY};
-  if (lt < g.head) z[0] = load_elem<BF16>(row, lt);
-  if (lt < g.tail) z[1] = load_elem<BF16>(row, g.head + g.nvec * EPV + lt);
-  accum<2>(z, c_hi, c_lo, M, S, bad);
+  if (ends) {
+    float z[2] = {-INFINITY, -INFINITY};
+    if (lt < g.head) z[0] = load_elem<BF16>(row, lt);
+    if (lt < g.tail) z[1] = load_elem<BF16>(row, g.head + g.nvec * EPV + lt);
+    accum<2>(z, c_hi, c_lo, M, S, bad);
+  }
 }
 
 // Greedy statistic: first-occurrence argmax; `bad` on NaN or +inf.
 template <bool BF16>
-__device__ void stream_argmax(const char* row, int V, int lt, int nthr, float& best, int& bidx, int& bad) {
+__device__ void stream_argmax(const char* row, int V, int vb, int ve, bool ends, int lt, int nthr, float& best,
+                              int& bidx, int& bad) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int U = 4;
@@ -229,11 +233,11 @@ __device__ void stream_argmax(const char* row, int V, int lt, int nthr, float& b
       bidx = vbase + j;
     }
   };
-  int v = lt;
-  for (; v + (U - 1) * nthr < g.nvec; v += U * nthr) {
+  int v = vb + lt;
+  for (; v + (U - 1) * nthr < ve; v += U * nthr) {
     uint4 d[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = vp[v + u * nthr];
+    for (int u = 0; u < U; ++u) d[u] = load_nt(vp + v + u * nthr);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float z[EPV];
@@ -241,11 +245,12 @@ __device__ void stream_argmax(const char* row, int V, int lt, int nthr, float& b
       take(z, g.head + (v + u * nthr) * EPV);
     }
   }
-  for (; v < g.nvec; v += nthr) {
+  for (; v < ve; v += nthr) {
     float z[EPV];
-    unpack<BF16>(vp[v], z);
+    unpack<BF16>(load_nt(vp + v), z);
     take(z, g.head + v * EPV);
   }
+  if (!ends) return;
   // head and tail elements: compare with the index tie-break
   if (lt < g.head) {
     const float z = load_elem<BF16>(row, lt);
@@ -480,10 +485,85 @@ __device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, floa
   if (lt == 0) sh.theta[which] = theta;
 }
 
+// Acceptance test of item (i, k) from finished row statistics; one thread.
+template <bool BF16>
+__device__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double c64, double l2t, float tht,
+                            double l2d, float thd, const char* trow, const char* drow) {
+  const int G = a.G, V = a.V;
+  a.rows_t[(size_t)i * (G + 1) + k] = RowStat{l2t, tht, 0};
+  bool bad = !(l2t == l2t);
+  if (two) {
+    a.rows_d[(size_t)i * G + k] = RowStat{l2d, thd, 0};
+    bad |= !(l2d == l2d);
+    const int x = a.tokens[(size_t)i * G + k];
+    if (!bad && x >= 0 && x < V) {
+      const float zt = load_elem<BF16>(trow, x);
+      const float zd = load_elem<BF16>(drow, x);
+      // log p(x) = ln2 * (z_x * log2(e)/T - lse2), -inf outside the kept set
+      const double lpt = (zt >= tht) ? kLn2 * ((double)zt * c64 - l2t) : -INFINITY;
+      const double lpd = (zd >= thd) ? kLn2 * ((double)zd * c64 - l2d) : -INFINITY;
+      double r;
+      if (lpt == -INFINITY) r = 0.0;
+      else if (lpd == -INFINITY) r = 1.0;
+      else r = fmin(1.0, exp(lpt - lpd));
+      double ua, ue;
+      verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
+      a.acc[(size_t)i * G + k] = AccRec{r, ua < r ? 1 : 0, 1};
+    }
+  }
+  if (bad) atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
+}
+
+// Reduce the per-thread (M, S, bad) of one row's waves into a segment Partial (written by lt == 0).
+__device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float S, int bad, int wave, int lane,
+                                                int first_wave, int nwaves, int lt, Partial* out) {
+  const float Mw = wave_max(M);
+  double Sd = (S > 0.f) ? ldexp((double)S, (int)fmaxf(M - Mw, -2000.f)) : 0.0;
+  Sd = wave_sum(Sd);
+  const int bw = wave_or_i(bad);
+  if (lane == 0) {
+    sh.M[wave] = Mw;
+    sh.S[wave] = Sd;
+    sh.bad[wave] = bw;
+  }
+  __syncthreads();
+  if (lt == 0) {
+    float Mr = -INFINITY;
+    int b = 0;
+    for (int w = first_wave; w < first_wave + nwaves; ++w) {
+      Mr = fmaxf(Mr, sh.M[w]);
+      b |= sh.bad[w];
+    }
+    double Sr = 0.0;
+    for (int w = first_wave; w < first_wave + nwaves; ++w)
+      if (sh.S[w] > 0.0) Sr += ldexp(sh.S[w], (int)fmaxf(sh.M[w] - Mr, -2000.f));
+    *out = Partial{Sr, Mr, 0, b, 0};
+  }
+}
+
+// log2-sum-exp of a row from its segment partials (fixed segment order); NaN when invalid.
+__device__ __forceinline__ double combine_sum(const Partial* p, int nseg) {
+  float Mr = -INFINITY;
+  int bad = 0;
+  for (int s = 0; s < nseg; ++s) {
+    bad |= p[s].bad;
+    if (p[s].v > 0.0) Mr = fmaxf(Mr, p[s].m);
+  }
+  double Sr = 0.0;
+  for (int s = 0; s < nseg; ++s)
+    if (p[s].v > 0.0) Sr += ldexp(p[s].v, (int)fmaxf(p[s].m - Mr, -2000.f));
+  return (bad || !(Sr > 0.0)) ? NAN : (double)Mr + log2(Sr);
+}
+
+// One workgroup per (work item, segment).  Target row k and, when k < L, draft row k of
+// the item are streamed together by the two halves of the workgroup; a lone target row uses
+// all eight waves.  combine_kernel then finishes each item from its segment partials.
+// Top-k items are not segmented (segment 0 takes the whole rows and finishes the item).
 template <bool BF16>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   __shared__ StreamShared sh;
-  const int g = blockIdx.x;
+  const int nseg = a.nseg;
+  const int g = blockIdx.x / nseg, seg = blockIdx.x - g * nseg;
   if (g >= *a.nitems) return;
   const int item = a.items[g];
   const int i = item >> 7, k = item & 127;
@@ -505,13 +585,33 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + k) * V * ES;
   const char* drow = two ? reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + k) * V * ES : nullptr;
   const char* row = which ? drow : trow;
+  const double c64 = greedy ? 0.0 : kLog2e / (double)T;
+  const float c_hi = __double2float_rz(c64);
+  const float c_lo = fmaxf((float)(c64 - (double)c_hi), 1e-30f);
+
+  if (K > 0) {
+    if (seg != 0) return;
+    topk_stats<BF16>(sh, row, V, K, c_hi, c_lo, lt, nthr, wave, lane, first_wave, nwaves, which);
+    __syncthreads();
+    if (tid == 0) accept_item<BF16>(a, i, k, two, c64, sh.lse2[0], sh.theta[0], two ? sh.lse2[1] : 0.0,
+                                    two ? sh.theta[1] : -INFINITY, trow, drow);
+    return;
+  }
+
+  // this segment's share of the row's 16-byte body; segment 0 also takes the scalar ends
+  const RowGeom geo = row_geom<BF16>(row, V);
+  const int vb = (int)((long long)geo.nvec * seg / nseg);
+  const int ve = (int)((long long)geo.nvec * (seg + 1) / nseg);
+  const bool ends = (seg == 0);
+  Partial* pt = a.part_t + (size_t)g * nseg;
+  Partial* pd = a.part_d + (size_t)g * nseg;
 
   if (greedy) {
     float best = -INFINITY;
     int bidx = 0x7fffffff, bad = 0;
-    stream_argmax<BF16>(row, V, lt, nthr, best, bidx, bad);
+    stream_argmax<BF16>(row, V, vb, ve, ends, lt, nthr, best, bidx, bad);
     // wave: max value, then lowest index among equal values
-    float wb = wave_max(best);
+    const float wb = wave_max(best);
     int cand = (best == wb) ? bidx : 0x7fffffff;
     cand = wave_min_i(cand);
     bad = wave_or_i(bad);
@@ -529,61 +629,69 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
         rbad |= sh.bad[w];
         if (sh.best[w] == rb) ri = min(ri, sh.bidx[w]);
       }
-      if (rbad || !(rb > -INFINITY)) {
-        atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
-        ri = 0;
+      pt[seg] = Partial{(double)rb, 0.f, ri, rbad, 0};
+    }
+  } else {
+    float M = -0x1p30f, S = 0.f;
+    int bad = 0;
+    stream_sum<BF16>(row, V, vb, ve, ends, c_hi, c_lo, lt, nthr, M, S, bad);
+    row_partial_sum(sh, M, S, bad, wave, lane, first_wave, nwaves, lt, which ? &pd[seg] : &pt[seg]);
+  }
+}
+
+// Finish every segmented work item: combine its segment partials and run the acceptance
+// test (one thread per item).  Top-k items were finished by the streaming kernel.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= *a.nitems) return;
+  const int item = a.items[g];
+  const int i = item >> 7, k = item & 127;
+  const int G = a.G, V = a.V, nseg = a.nseg;
+  constexpr int ES = BF16 ? 2 : 4;
+  const float T = a.greedy_only ? 0.f : a.temperature[i];
+  if (!(T >= 0.f && T < INFINITY)) return;
+  int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+  if (K < 0) return;
+  if (K >= V) K = 0;
+  if (K > 0) return;
+  const int L = a.lengths ? a.lengths[i] : G;
+  const bool greedy = (T == 0.f);
+  const bool two = !greedy && k < L;
+  const Partial* pt = a.part_t + (size_t)g * nseg;
+  const Partial* pd = a.part_d + (size_t)g * nseg;
+  if (greedy) {
+    float rb = -INFINITY;
+    int ri = 0x7fffffff, rbad = 0;
+    for (int s = 0; s < nseg; ++s) {
+      const Partial q = pt[s];
+      rbad |= q.bad;
+      const float v = (float)q.v;
+      if (v > rb) {
+        rb = v;
+        ri = q.idx;
+      } else if (v == rb) {
+        ri = min(ri, q.idx);
       }
-      a.rows_t[(size_t)i * (G + 1) + k] = RowStat{0.0, -INFINITY, ri};
-      if (k < L) {
-        const int x = a.tokens[(size_t)i * G + k];
-        const int m = (x == ri);
-        a.acc[(size_t)i * G + k] = AccRec{m ? 1.0 : 0.0, m, 1};
-      }
+    }
+    if (rbad || !(rb > -INFINITY)) {
+      atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
+      ri = 0;
+    }
+    a.rows_t[(size_t)i * (G + 1) + k] = RowStat{0.0, -INFINITY, ri};
+    if (k < L) {
+      const int x = a.tokens[(size_t)i * G + k];
+      const int m = (x == ri);
+      a.acc[(size_t)i * G + k] = AccRec{m ? 1.0 : 0.0, m, 1};
     }
     return;
   }
-
+  const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + k) * V * ES;
+  const char* drow = two ? reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + k) * V * ES : nullptr;
   const double c64 = kLog2e / (double)T;
-  const float c_hi = __double2float_rz(c64);
-  const float c_lo = fmaxf((float)(c64 - (double)c_hi), 1e-30f);
-  if (K == 0) {
-    float M = -0x1p30f, S = 0.f;
-    int bad = 0;
-    stream_sum<BF16>(row, V, c_hi, c_lo, lt, nthr, M, S, bad);
-    row_combine_sum(sh, M, S, bad, wave, lane, first_wave, nwaves, lt, which);
-    if (lt == 0) sh.theta[which] = -INFINITY;
-  } else {
-    topk_stats<BF16>(sh, row, V, K, c_hi, c_lo, lt, nthr, wave, lane, first_wave, nwaves, which);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const double l2t = sh.lse2[0];
-    const float tht = sh.theta[0];
-    a.rows_t[(size_t)i * (G + 1) + k] = RowStat{l2t, tht, 0};
-    bool bad = !(l2t == l2t);
-    if (two) {
-      const double l2d = sh.lse2[1];
-      const float thd = sh.theta[1];
-      a.rows_d[(size_t)i * G + k] = RowStat{l2d, thd, 0};
-      bad |= !(l2d == l2d);
-      const int x = a.tokens[(size_t)i * G + k];
-      if (!bad && x >= 0 && x < V) {
-        const float zt = load_elem<BF16>(trow, x);
-        const float zd = load_elem<BF16>(drow, x);
-        // log p(x) = ln2 * (z_x * log2(e)/T - lse2), -inf outside the kept set
-        const double lpt = (zt >= tht) ? kLn2 * ((double)zt * c64 - l2t) : -INFINITY;
-        const double lpd = (zd >= thd) ? kLn2 * ((double)zd * c64 - l2d) : -INFINITY;
-        double r;
-        if (lpt == -INFINITY) r = 0.0;
-        else if (lpd == -INFINITY) r = 1.0;
-        else r = fmin(1.0, exp(lpt - lpd));
-        double ua, ue;
-        verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
-        a.acc[(size_t)i * G + k] = AccRec{r, ua < r ? 1 : 0, 1};
-      }
-    }
-    if (bad) atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
-  }
+  const double l2t = combine_sum(pt, nseg);
+  const double l2d = two ? combine_sum(pd, nseg) : 0.0;
+  accept_item<BF16>(a, i, k, two, c64, l2t, -INFINITY, l2d, -INFINITY, trow, drow);
 }
 
 __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, const int32_t* pos, double* ua,
@@ -603,10 +711,16 @@ __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, c
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t rows_t, rows_d, acc, items, nitems, req_status, ereq, ranges, amb, total;
+  size_t rows_t, rows_d, acc, items, nitems, req_status, ereq, ranges, amb, part_t, part_d, total;
 };
 
-static WsLayout ws_layout(int B, int G, int V) {
+// Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
+static int stream_segments(int V, int es) {
+  const long long n = (long long)V * es / 49152;
+  return (int)(n < 1 ? 1 : (n > 16 ? 16 : n));
+}
+
+static WsLayout ws_layout(int B, int G, int V, int nseg) {
   WsLayout l;
   size_t o = 0;
   l.rows_t = o; o = align256(o + sizeof(RowStat) * (size_t)B * (G + 1));
@@ -618,6 +732,8 @@ static WsLayout ws_layout(int B, int G, int V) {
   l.ereq = o; o = align256(o + sizeof(EmitReq) * (size_t)B);
   l.ranges = o; o = align256(o + sizeof(EmitRange) * (size_t)B * num_ranges(V));
   l.amb = o; o = align256(o + sizeof(int32_t) * (size_t)B * kAmbCap);
+  l.part_t = o; o = align256(o + sizeof(Partial) * (size_t)B * (G + 1) * nseg);
+  l.part_d = o; o = align256(o + sizeof(Partial) * (size_t)B * (G + 1) * nseg);
   l.total = o;
   return l;
 }
@@ -635,7 +751,8 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
                              void* ev1) {
-  const WsLayout l = ws_layout(a.B, a.G, a.greedy_only ? 1 : a.V);  // greedy: no emit ranges
+  a.nseg = stream_segments(a.V, dtype == SPEC_BF16 ? 2 : 4);
+  const WsLayout l = ws_layout(a.B, a.G, a.greedy_only ? 1 : a.V, a.nseg);  // greedy: no emit ranges
   if (!ws || ws_bytes < l.total) return SPEC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return SPEC_ERR_WORKSPACE;
   char* w = reinterpret_cast<char*>(ws);
@@ -648,14 +765,21 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   a.ereq = reinterpret_cast<EmitReq*>(w + l.ereq);
   a.ranges = reinterpret_cast<EmitRange*>(w + l.ranges);
   a.amb = reinterpret_cast<int32_t*>(w + l.amb);
+  a.part_t = reinterpret_cast<Partial*>(w + l.part_t);
+  a.part_d = reinterpret_cast<Partial*>(w + l.part_d);
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   if (ev0) hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);
-  const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1));
+  const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1) * a.nseg);
   if (dtype == SPEC_BF16)
     hipLaunchKernelGGL(stream_kernel<true>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   else
     hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   if (ev1) hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
+  const unsigned cgrid = (unsigned)(((size_t)a.B * (a.G + 1) + 255) / 256);
+  if (dtype == SPEC_BF16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(cgrid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(cgrid), dim3(256), 0, s, a);
   launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -666,12 +790,12 @@ using namespace spec;
 
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_V) return 0;
-  return ws_layout(B, gamma, V).total;
+  return ws_layout(B, gamma, V, 16).total;   // sized for the largest segment count and fp32 or bf16
 }
 
 extern "C" size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
-  return ws_layout(B, gamma, 1).total;
+  return ws_layout(B, gamma, 1, 16).total;
 }
 
 extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,

@@ -22,6 +22,15 @@ struct AccRec {
   int32_t valid;   // 1 when computed
 };
 
+// Statistics of one segment of a row (the streaming kernel splits every row into nseg segments).
+struct Partial {
+  double v;     // sampling: sum of 2^(z*c - m) over the segment; greedy: the segment's maximum
+  float m;      // sampling: the segment's integer reference
+  int32_t idx;  // greedy: first index of the maximum
+  int32_t bad;  // NaN or +inf seen
+  int32_t pad;
+};
+
 // Emitted-token work: one range = kRangeElems consecutive tokens of the emit row.
 constexpr int kRangeElems = 2048; // tokens per emit range (one wave, 4 steps of 64 x 8)
 constexpr int kEmitSegs = 2;      // workgroups per request in the emit pass
@@ -61,6 +70,9 @@ struct VerifyArgs {
   int32_t* items;      // [B * (G+1)] work items, (request << 7) | position
   int32_t* nitems;     // [1]
   int32_t* req_status; // [B] SPEC_REQ_* bits raised while streaming
+  int nseg;            // segments per row in the streaming kernel
+  Partial* part_t;     // [B*(G+1), nseg] by work item
+  Partial* part_d;     // [B*(G+1), nseg]
   EmitReq* ereq;       // [B]
   EmitRange* ranges;   // [B, ceil(V / kRangeElems)]
   int32_t* amb;        // [B, kAmbCap]
