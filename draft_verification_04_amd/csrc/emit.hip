@@ -158,30 +158,45 @@ __device__ __forceinline__ int q_slot(uint32_t b) {
   return (t < (uint32_t)kQper) ? (int)(t + ((b & 0x8000u) ? kQper : 0)) : -1;
 }
 
-__device__ __noinline__ double q_miss(uint32_t b, double invT, double R, const double* T64) {
-  return q_direct(__uint_as_float(b << 16), invT, R, T64);
+__device__ __forceinline__ uint32_t half16(const uint32_t (&w)[4], int j) {
+  return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
 }
 
-// One step (64 lanes x 8 tokens) of a bf16 row pair from registers.
+// One step (64 lanes x 8 tokens) of a bf16 row pair from registers.  A lane whose 16 tokens
+// are all tabulated reads Q from the table; otherwise (rare: |z| < 2^-20, |z| >= 128,
+// infinities) it evaluates the same formula directly for the whole step.
 __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& dd, bool resid, const EmitRows& e,
                                           double cdh, double cdl, int v0, const VerifyArgs& a, int i,
                                           const double* T64, const double* Qt) {
   const uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
   const uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
+  bool miss = false;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t bt = (j & 1) ? (wt[j >> 1] >> 16) : (wt[j >> 1] & 0xffffu);
-    const int st = q_slot(bt);
-    double qt = Qt[st < 0 ? 0 : st];
-    if (st < 0) qt = q_miss(bt, e.invT, e.R, T64);
-    if (resid) {
-      const uint32_t bd = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xffffu);
-      const int sd = q_slot(bd);
-      double qd = Qt[sd < 0 ? 0 : sd];
-      if (sd < 0) qd = q_miss(bd, e.invT, e.R, T64);
-      classify(c, qt, qd, cdh, cdl, v0 + j, a, i);
-    } else {
-      c.T += qt;
+    miss |= q_slot(half16(wt, j)) < 0;
+    if (resid) miss |= q_slot(half16(wd, j)) < 0;
+  }
+  if (!miss) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double qt = Qt[q_slot(half16(wt, j))];
+      if (resid) {
+        const double qd = Qt[q_slot(half16(wd, j))];
+        classify(c, qt, qd, cdh, cdl, v0 + j, a, i);
+      } else {
+        c.T += qt;
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) {
+      const double qt = q_direct(__uint_as_float(half16(wt, j) << 16), e.invT, e.R, T64);
+      if (resid) {
+        const double qd = q_direct(__uint_as_float(half16(wd, j) << 16), e.invT, e.R, T64);
+        classify(c, qt, qd, cdh, cdl, v0 + j, a, i);
+      } else {
+        c.T += qt;
+      }
     }
   }
 }
