@@ -71,6 +71,8 @@ def main():
     B, G, V = w.B, w.gamma, w.V
     es = w.elem_bytes
     ws = torch.empty(sv.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+    sch_ws = torch.empty(max(256, sv.load_library().spec_schedule_workspace_size(B, G)), dtype=torch.uint8,
+                         device=dev)
     sch_out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
                    theta=torch.empty(1, dtype=torch.float64, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
@@ -83,7 +85,7 @@ def main():
     def step(idx, events=None):
         tgt, drf = copies[idx % len(copies)]
         if w.conf is not None:
-            sv.schedule_lengths(w.conf, sps, w.budget, out=sch_out, stream=stream)
+            sv.schedule_lengths(w.conf, sps, w.budget, out=sch_out, stream=stream, workspace=sch_ws)
             L = sch_out["lengths"]
         else:
             L = None

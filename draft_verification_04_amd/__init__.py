@@ -180,7 +180,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     code = lib.spec_verify_profiled(
         B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
         _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
-        _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel(), _stream(stream), ev0, ev1)
+        _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream), ev0, ev1)
     _check("spec_verify", code)
     return out
 
@@ -205,13 +205,14 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, lengths: Opt
     ws = _workspace(nbytes, dev, workspace)
     code = lib.spec_verify_greedy(B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft_tokens),
                                   _ptr(lengths), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
-                                  _ptr(out.get("status")), _ptr(ws), ws.numel(), _stream(stream))
+                                  _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_verify_greedy", code)
     return out
 
 
 def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
-                     mode: int = SPEC_SCHED_EARLY_STOP, out: Optional[dict] = None, stream=None) -> dict:
+                     mode: int = SPEC_SCHED_EARLY_STOP, out: Optional[dict] = None, stream=None,
+                     workspace: Optional[torch.Tensor] = None) -> dict:
     """spec_schedule_lengths on torch tensors.  Returns dict(lengths, theta, status)."""
     lib = load_library()
     _dev(conf, "conf", torch.float32, 2)
@@ -222,9 +223,10 @@ def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
         out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
                    theta=torch.empty(1, dtype=torch.float64, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace)
     code = lib.spec_schedule_lengths(B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode),
                                      _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("status")),
-                                     None, 0, _stream(stream))
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_schedule_lengths", code)
     return out
 

@@ -46,6 +46,12 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, SPEC_WAVE);
+  return x;
+}
+
 __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, SPEC_WAVE));

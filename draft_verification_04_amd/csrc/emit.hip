@@ -280,11 +280,13 @@ __global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
   const int i = blockIdx.x / kEmitSegs, seg = blockIdx.x % kEmitSegs;
   const int tid = threadIdx.x;
   init_t64(sh.T64);
-  if (tid == 0) {
+  if (tid < SPEC_WAVE) {
     int st, n;
     request_decision(a, i, &st, &n);
-    sh.st = st;
-    sh.n = n;
+    if (tid == 0) {
+      sh.st = st;
+      sh.n = n;
+    }
   }
   __syncthreads();
   const int st = sh.st, n = sh.n;
@@ -345,11 +347,13 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
   constexpr int NW = kEmitThreads / SPEC_WAVE;
   const int G = a.G, V = a.V;
   init_t64(sh.T64);
-  if (tid == 0) {
+  if (tid < SPEC_WAVE) {
     int st, n;
     request_decision(a, i, &st, &n);
-    sh.st = st;
-    sh.n = n;
+    if (tid == 0) {
+      sh.st = st;
+      sh.n = n;
+    }
   }
   __syncthreads();
   const int st = sh.st, n = sh.n;

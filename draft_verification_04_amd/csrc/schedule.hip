@@ -1,4 +1,4 @@
-// Confidence-scheduled verify lengths on gfx950 (one workgroup).
+// Confidence-scheduled verify lengths on gfx950.
 //
 // Follows the DSpark paper, §3.2.2 (survival a_{r,j} = product of c_{r,1..j};
 // marginal gain of extending request r to j is a_{r,j}; admit candidates in
@@ -8,15 +8,25 @@
 // the search without the break of §5.2.
 //
 // Exactness: survivals are float32 products taken left to right; tau is an
-// int64 in fixed point with 50 fractional bits (each survival floored to a
-// multiple of 2^-50), so the parallel prefix sum is exact and independent of
-// its association; Theta(m) = fp64(tau(m)) * 2^-50 * sps[B + m].
+// int64 in fixed point with 47 fractional bits (each survival floored to a
+// multiple of 2^-47; tau <= B + B*gamma <= 2^15 leaves room below 2^63), so the
+// parallel prefix sum is exact and independent of its association;
+// Theta(m) = fp64(tau(m)) * 2^-47 * sps[B + m].
 //
-// Steps: survivals and 64-bit sort keys (inverted survival bits | candidate
-// index, so ascending key = survival descending, then request, then
-// position) -> bitonic sort held in registers (lane shuffles, LDS only for the
-// longest strides) -> exclusive int64 scan -> Theta(m) -> first non-rise
-// (early stop) or first maximum (global) -> per-request counts.
+// Candidates are ordered by the 32-bit key ~bits(a) (ascending key = descending
+// survival), ties by index r * gamma + j (request, then position).  One CU retires
+// only 64 lane operations per cycle, so the sort is spread over the chip:
+//   keys_kernel   one wave per chunk of 64 candidates: survivals, keys in index
+//                 order, and the chunk sorted by (key, index) in registers;
+//   rank_kernel   one workgroup per chunk: each key's place in the whole pool is
+//                 its place in its chunk plus, for every other chunk, the number of
+//                 keys there that precede it (binary search in LDS), and it is
+//                 written straight to that place;
+//   final_kernel  one workgroup: exclusive int64 scan of the fixed-point
+//                 survivals, Theta(m), first non-rise (early stop) or first maximum
+//                 (global), and per-request counts from the key at m* (keys below it
+//                 are admitted, and of the keys equal to it the first ones in index
+//                 order, as many as the admission count leaves).
 #include "common.hpp"
 #include "spec_verify.h"
 
@@ -24,9 +34,13 @@
 
 namespace spec {
 
-constexpr int kSchedThreads = 1024;
-constexpr int kSchedMaxKeys = SPEC_MAX_SCHED_CANDIDATES;  // power of two
-constexpr long long kOne = 1ll << 50;
+constexpr int kChunk = SPEC_WAVE;                 // candidates per sorted chunk
+constexpr int kKeysThreads = 256;                 // four chunks per keys workgroup
+constexpr int kRankParts = 8;                     // waves sharing one chunk's searches
+constexpr int kFinalThreads = 1024;
+constexpr int kFinalWaves = kFinalThreads / SPEC_WAVE;
+constexpr long long kOne = 1ll << 47;
+constexpr unsigned kNoCandidate = 0xffffffffu;
 
 struct SchedArgs {
   int B, G, budget, mode;
@@ -35,168 +49,236 @@ struct SchedArgs {
   int32_t* lengths;
   double* theta;
   int32_t* status;
+  unsigned* orig;     // [N] keys in index order
+  unsigned* chunked;  // [N] keys, each chunk of 64 sorted
+  unsigned* sorted;   // [N] keys, whole pool sorted
 };
 
-struct SchedShared {
-  unsigned long long keys[kSchedMaxKeys];
-  long long wsum[kSchedThreads / SPEC_WAVE];
-  double wth[kSchedThreads / SPEC_WAVE];
-  int wm[kSchedThreads / SPEC_WAVE];
-  int ncand;
-  int mstar;
-};
+__device__ __forceinline__ unsigned surv_key(float s) { return s > 0.f ? ~__float_as_uint(s) : kNoCandidate; }
+__device__ __forceinline__ float key_surv(unsigned k) { return __uint_as_float(~k); }
 
 __device__ __forceinline__ long long fixed_q(float a) {
-  // floor(a * 2^50): a is a float32 in [0, 1]; the product is exact in fp64
-  return (long long)floor((double)a * 0x1p50);
+  // floor(a * 2^47): a is a float32 in [0, 1]; the product is exact in fp64
+  return (long long)floor((double)a * 0x1p47);
 }
 
 __device__ __forceinline__ double theta_of(long long tau, double sps) {
-  return ((double)tau * 0x1p-50) * sps;
+  return ((double)tau * 0x1p-47) * sps;
 }
 
-// Bitonic sort of NP = K * kSchedThreads keys, ascending; thread t holds positions t*K .. t*K+K-1.
-// Strides below K compare in registers, strides below 64*K across lanes of a wave, longer ones
-// through LDS.
-template <int K>
-__device__ __forceinline__ void bitonic_regs(unsigned long long (&key)[K], unsigned long long* lds, int tid,
-                                             int lane) {
-  constexpr int NP = K * kSchedThreads;
-  for (int size = 2; size <= NP; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < K) {
-#pragma unroll
-        for (int e = 0; e < K; ++e) {
-          const int pe = e ^ stride;
-          if (pe > e) {
-            const int pos = tid * K + e;
-            const bool up = (pos & size) == 0;
-            const unsigned long long x = key[e], y = key[pe];
-            if ((x > y) == up) {
-              key[e] = y;
-              key[pe] = x;
-            }
-          }
-        }
-      } else if (stride < 64 * K) {
-        const int lx = stride / K;
-        const bool lower = (lane & lx) == 0;
-#pragma unroll
-        for (int e = 0; e < K; ++e) {
-          const int pos = tid * K + e;
-          const bool up = (pos & size) == 0;
-          const unsigned long long y = __shfl_xor(key[e], lx, SPEC_WAVE);
-          const unsigned long long x = key[e];
-          // the lower position keeps the smaller key when ascending
-          key[e] = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
-        }
-      } else {
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < K; ++e) lds[tid * K + e] = key[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < K; ++e) {
-          const int pos = tid * K + e;
-          const bool up = (pos & size) == 0;
-          const bool lower = (pos & stride) == 0;
-          const unsigned long long y = lds[pos ^ stride];
-          const unsigned long long x = key[e];
-          key[e] = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
-        }
-      }
+// ---- keys ----------------------------------------------------------------
+
+__global__ __launch_bounds__(kKeysThreads) void keys_kernel(SchedArgs a) {
+  __shared__ float cf[kKeysThreads + 2 * SPEC_MAX_GAMMA];  // confidences of the requests in reach
+  const int B = a.B, G = a.G, N = B * G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c0 = blockIdx.x * kKeysThreads;
+  const int cend = min(c0 + kKeysThreads, N);
+  const int f0 = (c0 / G) * G, f1 = ((cend - 1) / G + 1) * G;  // whole requests overlapping the block
+  for (int x = tid; x < f1 - f0; x += kKeysThreads) cf[x] = a.conf[f0 + x];
+  __syncthreads();
+
+  const int p = c0 + tid;
+  unsigned key = kNoCandidate;
+  if (p < N) {
+    const int r = p / G, j = p - r * G;
+    const float* c = cf + (r * G - f0);
+    bool bad = false;
+    float s = 0.f;
+    for (int t = 0; t < G; ++t) {
+      const float v = c[t];
+      bad |= !(v >= 0.f && v <= 1.f);
+      if (t <= j) s = (t == 0) ? v : __fmul_rn(s, v);
     }
+    key = bad ? kNoCandidate : surv_key(s);
+    if (j == 0 && a.status) a.status[r] = bad ? SPEC_REQ_BAD_CONFIDENCE : 0;
+    a.orig[p] = key;
+  }
+  // bitonic sort of the wave's 64 (key, index) pairs, one per lane; padding sorts last
+  unsigned long long x = ((unsigned long long)key << 32) | (unsigned)(p < N ? p : 0x7fffffff);
+  for (int size = 2; size <= SPEC_WAVE; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const unsigned long long y = __shfl_xor(x, stride, SPEC_WAVE);
+      const bool up = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
+      x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+    }
+  }
+  if (p < N) a.chunked[p] = (unsigned)(x >> 32);
+}
+
+// ---- ranks -----------------------------------------------------------------
+
+// For S chunks c[u] at once: the number of their keys that precede key k of chunk ck, i.e.
+// keys not larger than k in a chunk before ck (index order on ties) and keys smaller than k
+// in a chunk after it (a key v precedes k when v < k + [chunk before ck], compared in 64
+// bits).  Chunks hold up to 64 ascending keys.  The S searches advance in lockstep with
+// plain arithmetic, so their LDS reads are in flight together.
+template <int S>
+__device__ __forceinline__ int count_before(const unsigned* keys, const int (&c)[S], int ck, int N,
+                                            unsigned k) {
+  int base[S], len[S];
+  unsigned long long lim[S];
+#pragma unroll
+  for (int u = 0; u < S; ++u) {
+    base[u] = c[u] * kChunk;
+    len[u] = min(kChunk, N - base[u]);
+    lim[u] = (unsigned long long)k + (c[u] < ck ? 1ull : 0ull);
+  }
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {  // 7 halvings empty a range of 64
+    unsigned v[S];
+#pragma unroll
+    for (int u = 0; u < S; ++u) v[u] = keys[min(base[u] + (len[u] >> 1), N - 1)];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int half = len[u] >> 1;
+      const int go = (int)(len[u] > 0) & (int)((unsigned long long)v[u] < lim[u]);
+      base[u] += go * (half + 1);
+      len[u] = go ? len[u] - half - 1 : half;
+    }
+  }
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < S; ++u) n += (c[u] != ck) ? base[u] - c[u] * kChunk : 0;
+  return n;
+}
+
+__global__ __launch_bounds__(kChunk * kRankParts) void rank_kernel(SchedArgs a) {
+  __shared__ __align__(16) unsigned keys[SPEC_MAX_SCHED_CANDIDATES];
+  __shared__ int part[kRankParts][kChunk];
+  const int N = a.B * a.G;
+  const int tid = threadIdx.x, part_id = tid >> 6, lane = tid & 63;
+  constexpr int NT = kChunk * kRankParts;
+  // stage the chunk-sorted pool (16-byte loads for the aligned bulk)
+  const int n4 = N >> 2;
+  for (int x = tid; x < n4; x += NT)
+    reinterpret_cast<uint4*>(keys)[x] = reinterpret_cast<const uint4*>(a.chunked)[x];
+  for (int x = (n4 << 2) + tid; x < N; x += NT) keys[x] = a.chunked[x];
+  __syncthreads();
+  const int ck = blockIdx.x, nch = (N + kChunk - 1) / kChunk;
+  const int p = ck * kChunk + lane;
+  const bool valid = p < N;
+  const unsigned k = valid ? keys[p] : 0u;
+  int cnt = 0;
+  // this wave's share of the other chunks, eight searches in flight; chunks past the end are
+  // replaced by the own chunk, which counts nothing
+  for (int c = part_id; c < nch; c += 8 * kRankParts) {
+    int cs[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cs[u] = (c + u * kRankParts < nch) ? c + u * kRankParts : ck;
+    cnt += count_before<8>(keys, cs, ck, N, k);
+  }
+  part[part_id][lane] = cnt;
+  __syncthreads();
+  if (part_id == 0 && valid) {
+    int rank = lane;
+#pragma unroll
+    for (int w = 0; w < kRankParts; ++w) rank += part[w][lane];
+    a.sorted[rank] = k;
   }
 }
 
+// ---- Theta path and lengths -----------------------------------------------
+
 template <int K>
-__device__ void schedule_body(const SchedArgs& a, SchedShared& sh) {
+struct FinalShared {
+  unsigned sorted[K * kFinalThreads];
+  unsigned orig[K * kFinalThreads];
+  long long wsum[kFinalWaves];
+  double wth[kFinalWaves];
+  int wm[kFinalWaves];
+  int ncand, mstar, first, last;
+};
+
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
+__device__ __forceinline__ long long block_exclusive_sum(long long x, long long* wsum, long long* total) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int NW = kSchedThreads / SPEC_WAVE;
+  const long long incl = wave_inclusive_sum_i64(x, lane);
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  long long before = 0, all = 0;
+  for (int w = 0; w < kFinalWaves; ++w) {
+    before += (w < wave) ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  *total = all;
+  return before + incl - x;
+}
+
+template <int K>
+__global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
+  __shared__ FinalShared<K> sh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int B = a.B, G = a.G;
   const int N = B * G;
-  constexpr int NP = K * kSchedThreads;
+  // SPS entries of this thread's admissions, fetched with the keys
+  int m_cap = a.budget - B;
+  m_cap = m_cap < 0 ? 0 : (m_cap > N ? N : m_cap);
+  const int p0 = tid * K;
+  const double sps_B = a.sps[B];
+  const double sps_p0 = (p0 <= m_cap) ? a.sps[B + p0] : 0.0;
+  double sps_m[K];
+#pragma unroll
+  for (int e = 0; e < K; ++e) sps_m[e] = (p0 + e + 1 <= m_cap) ? a.sps[B + p0 + e + 1] : 0.0;
   if (tid == 0) sh.ncand = 0;
-  // confidences staged in the key slots (coalesced loads); each request's thread then reads
-  // its slots and overwrites them with the keys
-  for (int p = tid; p < NP; p += kSchedThreads)
-    sh.keys[p] = (p < N) ? (unsigned long long)__float_as_uint(a.conf[p]) : ~0ull;
-  __syncthreads();
-
-  // survival products and keys, one request per thread
-  for (int r = tid; r < B; r += kSchedThreads) {
-    unsigned long long* c = sh.keys + (size_t)r * G;   // confidence bits, read before overwritten
-    int bad = 0;
-    for (int j = 0; j < G; ++j) {
-      const float cj = __uint_as_float((unsigned)c[j]);
-      bad |= !(cj >= 0.f && cj <= 1.f);
-    }
-    if (a.status) a.status[r] = bad ? SPEC_REQ_BAD_CONFIDENCE : 0;
-    float s = 1.f;
-    int n = 0;
-    for (int j = 0; j < G; ++j) {
-      const float cj = __uint_as_float((unsigned)c[j]);
-      s = (j == 0) ? cj : __fmul_rn(s, cj);
-      unsigned long long key = ~0ull;
-      if (!bad && s > 0.f) {
-        key = ((unsigned long long)(~__float_as_uint(s)) << 32) | (unsigned)(r * G + j);
-        ++n;
-      }
-      c[j] = key;
-    }
-    if (n) atomicAdd(&sh.ncand, n);
+  for (int x = tid; x < N; x += kFinalThreads) {
+    sh.sorted[x] = a.sorted[x];
+    sh.orig[x] = a.orig[x];
   }
   __syncthreads();
-  unsigned long long key[K];
-#pragma unroll
-  for (int e = 0; e < K; ++e) key[e] = sh.keys[tid * K + e];
-  bitonic_regs<K>(key, sh.keys, tid, lane);
 
+  unsigned key[K];
+  int nvalid = 0;
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    key[e] = (p0 + e < N) ? sh.sorted[p0 + e] : kNoCandidate;
+    nvalid += key[e] != kNoCandidate;
+  }
+  nvalid = wave_sum_i(nvalid);
+  if (lane == 0 && nvalid) atomicAdd(&sh.ncand, nvalid);
+  __syncthreads();
   const int E = sh.ncand;
   int m_max = a.budget - B;
   if (m_max > E) m_max = E;
   if (m_max < 0) m_max = 0;
 
   // exclusive scan of q over sorted positions 0 .. m_max-1 (K per thread)
-  const int p0 = tid * K;
   long long q[K];
   long long local = 0;
 #pragma unroll
   for (int e = 0; e < K; ++e) {
-    q[e] = (p0 + e < m_max) ? fixed_q(__uint_as_float(~(unsigned)(key[e] >> 32))) : 0;
+    q[e] = (p0 + e < m_max) ? fixed_q(key_surv(key[e])) : 0;
     local += q[e];
   }
-  long long incl = wave_inclusive_sum_i64(local, lane);
-  __syncthreads();
-  if (lane == 63) sh.wsum[wave] = incl;
-  __syncthreads();
-  long long before = 0;
-  for (int w = 0; w < wave; ++w) before += sh.wsum[w];
-  long long tau = (long long)B * kOne + before + (incl - local);  // tau at m = p0
+  long long total;
+  const long long before = block_exclusive_sum(local, sh.wsum, &total);
+  long long tau = (long long)B * kOne + before;  // tau at m = p0
   const long long tau_p0 = tau;
 
   // Theta along the path; admission m uses sorted position m-1
-  const double th0 = theta_of((long long)B * kOne, a.sps[B]);
+  const double th0 = theta_of((long long)B * kOne, sps_B);
   int brk = 0x7fffffff;           // first m >= 1 with Theta(m) <= Theta(m-1)
   double best = -INFINITY;        // global: max Theta over this thread's m
   int best_m = 0x7fffffff;
+  double tp = (p0 < m_max) ? theta_of(tau, sps_p0) : 0.0;
 #pragma unroll
   for (int e = 0; e < K; ++e) {
     const int m = p0 + e + 1;
     if (m <= m_max) {
-      const long long prev = tau;
       tau += q[e];
-      const double tm = theta_of(tau, a.sps[B + m]);
-      const double tp = theta_of(prev, a.sps[B + m - 1]);
+      const double tm = theta_of(tau, sps_m[e]);
       if (!(tm > tp) && m < brk) brk = m;
       if (tm > best) {
         best = tm;
         best_m = m;
       }
+      tp = tm;
     }
   }
   // block reductions
-  int wb = wave_min_i(brk);
+  const int wb = wave_min_i(brk);
   double wbest = best;
   int wbm = best_m;
 #pragma unroll
@@ -219,12 +301,12 @@ __device__ void schedule_body(const SchedArgs& a, SchedShared& sh) {
     int mstar;
     if (a.mode == SPEC_SCHED_EARLY_STOP) {
       int b = 0x7fffffff;
-      for (int w = 0; w < NW; ++w) b = min(b, sh.wm[w]);
+      for (int w = 0; w < kFinalWaves; ++w) b = min(b, sh.wm[w]);
       mstar = (b == 0x7fffffff) ? m_max : b - 1;
     } else {
       double bt = th0;
       int bm = 0;
-      for (int w = 0; w < NW; ++w) {
+      for (int w = 0; w < kFinalWaves; ++w) {
         const double t = sh.wth[w];
         const int m = (int)sh.wsum[w];
         if (t > bt || (t == bt && m < bm)) {
@@ -235,52 +317,78 @@ __device__ void schedule_body(const SchedArgs& a, SchedShared& sh) {
       mstar = bm;
     }
     sh.mstar = mstar;
+    sh.first = sh.last = 0;
     if (mstar == 0 && a.theta) a.theta[0] = th0;
   }
-  for (int r = tid; r < B; r += kSchedThreads) a.lengths[r] = 0;
   __syncthreads();
   const int mstar = sh.mstar;
-  // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
-  if (mstar > 0 && mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
-    long long t = tau_p0;
-#pragma unroll
-    for (int e = 0; e < K; ++e)
-      if (p0 + e < mstar) t += q[e];
-    a.theta[0] = theta_of(t, a.sps[B + mstar]);
+  if (mstar == 0) {
+    for (int r = tid; r < B; r += kFinalThreads) a.lengths[r] = 0;
+    return;
   }
-  // per-request counts: admitted positions form a prefix of each request's candidates
+  // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
+  if (mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
+    long long t = tau_p0;
+    double sp = 0.0;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      if (p0 + e < mstar) t += q[e];
+      if (p0 + e + 1 == mstar) sp = sps_m[e];
+    }
+    a.theta[0] = theta_of(t, sp);
+  }
+  // the admitted candidates are the keys below thr plus the first (m* - first) keys equal to
+  // thr in index order, where [first, last] is thr's run in the sorted pool
+  const unsigned thr = sh.sorted[mstar - 1];
 #pragma unroll
   for (int e = 0; e < K; ++e) {
-    if (p0 + e < mstar) {
-      const unsigned idx = (unsigned)(key[e] & 0xffffffffu);
-      const int r = (int)(idx / (unsigned)G), j = (int)(idx % (unsigned)G);
-      atomicMax(&a.lengths[r], j + 1);
+    const int p = p0 + e;
+    if (p < N && key[e] == thr) {
+      if (p == 0 || sh.sorted[p - 1] != thr) sh.first = p;
+      if (p == N - 1 || sh.sorted[p + 1] != thr) sh.last = p;
     }
+  }
+  __syncthreads();
+  const int ties_admitted = mstar - sh.first;
+  const bool split = ties_admitted < sh.last - sh.first + 1;  // uniform
+  long long carry = 0;
+  for (int r0 = 0; r0 < B; r0 += kFinalThreads) {
+    const int r = r0 + tid;
+    int lt = 0, eq = 0;
+    if (r < B) {
+      for (int j = 0; j < G; ++j) {
+        const unsigned k = sh.orig[(size_t)r * G + j];
+        lt += k < thr;
+        eq += k == thr;
+      }
+    }
+    int len = lt + eq;
+    if (split) {
+      long long chunk;
+      const long long ex = carry + block_exclusive_sum(eq, sh.wsum, &chunk);
+      carry += chunk;
+      len = lt + (int)max(0ll, min((long long)eq, (long long)ties_admitted - ex));
+    }
+    if (r < B) a.lengths[r] = len;
   }
 }
 
-template <int K>
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedArgs a) {
-  __shared__ SchedShared sh;
-  schedule_body<K>(a, sh);
-}
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace spec
 
 using namespace spec;
 
 extern "C" size_t spec_schedule_workspace_size(int32_t B, int32_t gamma) {
-  (void)B;
-  (void)gamma;
-  return 0;
+  if (B < 1 || gamma < 1) return 0;
+  const size_t n = (size_t)B * (size_t)gamma;
+  return 3 * align256(n * sizeof(unsigned));
 }
 
 extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const double* sps,
                                          int32_t sps_len, int32_t budget_tokens, int32_t mode,
                                          int32_t* lengths_out, double* theta_out, int32_t* status,
                                          void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return SPEC_ERR_INVALID_ARG;
   if ((long long)B * gamma > SPEC_MAX_SCHED_CANDIDATES) return SPEC_ERR_UNSUPPORTED;
   if (mode != SPEC_SCHED_EARLY_STOP && mode != SPEC_SCHED_GLOBAL) return SPEC_ERR_INVALID_ARG;
@@ -289,13 +397,22 @@ extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* 
   if (m_cap < 0) m_cap = 0;
   if (m_cap > (long long)B * gamma) m_cap = (long long)B * gamma;
   if ((long long)sps_len <= (long long)B + m_cap) return SPEC_ERR_INVALID_ARG;
-  SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, status};
+  if (!workspace || workspace_bytes < spec_schedule_workspace_size(B, gamma) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SPEC_ERR_WORKSPACE;
+  const int n = B * gamma;
+  char* ws = static_cast<char*>(workspace);
+  const size_t seg = align256((size_t)n * sizeof(unsigned));
+  SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, status,
+              reinterpret_cast<unsigned*>(ws), reinterpret_cast<unsigned*>(ws + seg),
+              reinterpret_cast<unsigned*>(ws + 2 * seg)};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const long long n = (long long)B * gamma;
-  if (n <= 1 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, s, a);
-  else if (n <= 2 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, s, a);
-  else if (n <= 4 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, s, a);
-  else if (n <= 8 * kSchedThreads) hipLaunchKernelGGL(schedule_kernel<8>, dim3(1), dim3(kSchedThreads), 0, s, a);
-  else hipLaunchKernelGGL(schedule_kernel<16>, dim3(1), dim3(kSchedThreads), 0, s, a);
+  hipLaunchKernelGGL(keys_kernel, dim3((n + kKeysThreads - 1) / kKeysThreads), dim3(kKeysThreads), 0, s, a);
+  hipLaunchKernelGGL(rank_kernel, dim3((n + kChunk - 1) / kChunk), dim3(kChunk * kRankParts), 0, s, a);
+  if (n <= 1 * kFinalThreads) hipLaunchKernelGGL(final_kernel<1>, dim3(1), dim3(kFinalThreads), 0, s, a);
+  else if (n <= 2 * kFinalThreads) hipLaunchKernelGGL(final_kernel<2>, dim3(1), dim3(kFinalThreads), 0, s, a);
+  else if (n <= 4 * kFinalThreads) hipLaunchKernelGGL(final_kernel<4>, dim3(1), dim3(kFinalThreads), 0, s, a);
+  else if (n <= 8 * kFinalThreads) hipLaunchKernelGGL(final_kernel<8>, dim3(1), dim3(kFinalThreads), 0, s, a);
+  else hipLaunchKernelGGL(final_kernel<16>, dim3(1), dim3(kFinalThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -90,9 +90,11 @@ static constexpr double kLog2e = 1.44269504088896340736;
 
 __host__ __device__ inline int num_ranges(int V) { return (V + kRangeElems - 1) / kRangeElems; }
 
-// Status and first rejection of request i (call from one thread).
+// Status and first rejection of request i.  Called by a whole wave (lane k looks at draft
+// position k; gamma <= 64); every lane gets the result.
 __device__ inline void request_decision(const VerifyArgs& a, int i, int* st_out, int* n_out) {
   const int G = a.G, V = a.V;
+  const int lane = threadIdx.x & 63;
   const int L = a.lengths ? a.lengths[i] : G;
   int st = 0, n = 0;
   if (L < 0 || L > G) {
@@ -102,18 +104,16 @@ __device__ inline void request_decision(const VerifyArgs& a, int i, int* st_out,
     const int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
     if (!(T >= 0.f && T < __builtin_inff())) st |= SPEC_REQ_BAD_TEMPERATURE;
     if (K < 0) st |= SPEC_REQ_BAD_TOPK;
-    for (int k = 0; k < L; ++k) {
-      const int x = a.tokens[(size_t)i * G + k];
-      if (x < 0 || x >= V) st |= SPEC_REQ_BAD_TOKEN;
+    int x = 0, acc = 1;
+    if (lane < L) {
+      x = a.tokens[(size_t)i * G + lane];
+      acc = a.acc[(size_t)i * G + lane].accept;
     }
+    if (__ballot(lane < L && (x < 0 || x >= V))) st |= SPEC_REQ_BAD_TOKEN;
     if (st == 0) st |= a.req_status[i];
     if (st == 0) {
-      n = L;
-      for (int k = 0; k < L; ++k)
-        if (!a.acc[(size_t)i * G + k].accept) {
-          n = k;
-          break;
-        }
+      const unsigned long long rej = __ballot(lane < L && !acc);
+      n = rej ? (int)__ffsll((long long)rej) - 1 : L;
     }
   }
   *st_out = st;

@@ -1,7 +1,7 @@
 """Raw HIP events (via the HIP runtime library) for timing a kernel launched inside libspecverify.
 
 torch.cuda.Event objects cannot be recorded by foreign code, so the timing
-events handed to spec_verify_profiled are created here with hipEventCreate.
+events handed to spec_verify_profiled are created here with hipEventCreateWithFlags.
 """
 
 import ctypes
@@ -13,8 +13,8 @@ def _lib():
     global _hip
     if _hip is None:
         _hip = ctypes.CDLL("libamdhip64.so")
-        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        _hip.hipEventCreate.restype = ctypes.c_int
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        _hip.hipEventCreateWithFlags.restype = ctypes.c_int
         _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         _hip.hipEventDestroy.restype = ctypes.c_int
         _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
@@ -24,14 +24,19 @@ def _lib():
     return _hip
 
 
+# Timing-only events: recording them skips the system-scope fence (cache write-back and
+# invalidation) that would otherwise stall the stream around the timed kernel.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvent:
     """A HIP event; `.handle` is the hipEvent_t to pass as void*."""
 
-    def __init__(self):
+    def __init__(self, flags: int = HIP_EVENT_DISABLE_SYSTEM_FENCE):
         h = ctypes.c_void_p()
-        rc = _lib().hipEventCreate(ctypes.byref(h))
+        rc = _lib().hipEventCreateWithFlags(ctypes.byref(h), flags)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed ({rc})")
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         self.handle = h
 
     @property

@@ -174,9 +174,9 @@ int32_t spec_verify_greedy(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
  *   a_{i,j} = c_{i,0} * ... * c_{i,j} (float32, left to right);
  *   candidates (i, j) with a_{i,j} > 0, sorted by a descending, then i, then j;
  *   admitting the first m gives batch tokens B + m and expected accepted tokens
- *   tau(m) = B + sum of their survivals, held in fixed point with 50 fractional
- *   bits (each survival floored to a multiple of 2^-50);
- *   Theta(m) = fp64(tau(m)) * 2^-50 * sps[B + m];
+ *   tau(m) = B + sum of their survivals, held in fixed point with 47 fractional
+ *   bits (each survival floored to a multiple of 2^-47; tau < 2^16 always fits);
+ *   Theta(m) = fp64(tau(m)) * 2^-47 * sps[B + m];
  *   m ranges over 0 .. min(#candidates, budget_tokens - B);
  *   EARLY_STOP: m* = last m before the first Theta(m+1) <= Theta(m);
  *   GLOBAL: m* = the smallest m maximising Theta.
@@ -196,7 +196,13 @@ int32_t spec_verify_greedy(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
  *   status        [B] int32 device or NULL: SPEC_REQ_BAD_CONFIDENCE when a
  *                 confidence of that request is outside [0, 1] or NaN; such a
  *                 request contributes no candidate (its length is 0)
- *   workspace     at least spec_schedule_workspace_size(B, gamma) bytes
+ *   workspace     at least spec_schedule_workspace_size(B, gamma) bytes (12 per
+ *                 candidate, rounded up), 256-byte aligned, owned by the caller; it
+ *                 carries the sort keys between the call's kernels and must not be
+ *                 touched by other work until they finish on `stream`
+ * Errors (nothing is launched): SPEC_ERR_INVALID_ARG for the conditions above,
+ *   SPEC_ERR_UNSUPPORTED beyond SPEC_MAX_SCHED_CANDIDATES, SPEC_ERR_WORKSPACE for a
+ *   missing, short or misaligned workspace.
  */
 size_t spec_schedule_workspace_size(int32_t B, int32_t gamma);
 

@@ -19,8 +19,8 @@ Algorithm 1 as printed in the paper's Chinese translation:
   * l_r = number of admitted candidates of request r.
 
 Exact-arithmetic readings (so a parallel device scan can agree bit for bit):
-tau is kept in fixed point with 50 fractional bits, q(a) = floor(a * 2^50) as
-an exact integer; Theta(m) = float64(tau(m)) * 2^-50 * SPS[R + m], each step
+tau is kept in fixed point with 47 fractional bits, q(a) = floor(a * 2^47) as
+an exact integer; Theta(m) = float64(tau(m)) * 2^-47 * SPS[R + m], each step
 an IEEE fp64 operation.  The verify budget caps B_tok <= budget, so
 m <= budget - R.
 """
@@ -29,7 +29,7 @@ import math
 
 import numpy as np
 
-FRAC_BITS = 50
+FRAC_BITS = 47   # tau <= R + R*gamma <= 2^15 tokens must fit a signed 64-bit integer
 ONE = 1 << FRAC_BITS
 MODE_EARLY_STOP = 0
 MODE_GLOBAL = 1
@@ -48,7 +48,7 @@ def survival(conf):
 
 
 def fixed_point(a):
-    """q(a) = floor(a * 2^50) as an exact Python integer (a is a float32 value in [0, 1])."""
+    """q(a) = floor(a * 2^47) as an exact Python integer (a is a float32 value in [0, 1])."""
     return int(math.floor(float(a) * float(ONE)))
 
 
@@ -61,7 +61,7 @@ def candidates(a):
 
 
 def theta(tau_fixed, sps_value):
-    """Theta = fp64(tau) * 2^-50 * SPS, left to right."""
+    """Theta = fp64(tau) * 2^-47 * SPS, left to right."""
     return float(tau_fixed) * (2.0 ** -FRAC_BITS) * float(sps_value)
 
 

@@ -63,7 +63,7 @@ def test_workspace_sizes(lib):
     assert lib.spec_verify_workspace_size(0, 16, 10) == 0
     assert lib.spec_verify_workspace_size(4, 65, 10) == 0
     assert lib.spec_verify_greedy_workspace_size(4, 8) > 0
-    assert lib.spec_schedule_workspace_size(256, 16) == 0
+    assert lib.spec_schedule_workspace_size(256, 16) >= 12 * 256 * 16
 
 
 def _fake(n=64):
@@ -119,5 +119,10 @@ def test_greedy_and_schedule_reject_bad_arguments(lib):
     assert lib.spec_schedule_lengths(4, 4, p, p, 10, 10, 0, p, None, None, None, 0, None) == 1   # table short
     assert lib.spec_schedule_lengths(4, 4, p, p, 4, 2, 0, p, None, None, None, 0, None) == 1     # needs sps[B]
     assert lib.spec_schedule_lengths(2048, 16, p, p, 10 ** 6, 10, 0, p, None, None, None, 0, None) == 3
+    # valid shapes, no workspace
+    assert lib.spec_schedule_lengths(4, 4, p, p, 100, 10, 0, p, None, None, None, 0, None) == 2
+    n = lib.spec_schedule_workspace_size(256, 16)
+    assert n >= 12 * 256 * 16 and n % 256 == 0 and lib.spec_schedule_workspace_size(0, 16) == 0
+    assert lib.spec_schedule_lengths(4, 4, p, p, 100, 10, 0, p, None, None, p, 8, None) == 2   # short
     assert lib.spec_philox_uniforms(-1, p, p, p, p, p, None) == 1
     assert lib.spec_philox_uniforms(0, None, None, None, None, None, None) == 0

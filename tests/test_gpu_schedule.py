@@ -101,3 +101,31 @@ def test_bad_confidences(sv):
 def oracle_bad():
     import draft_verification_04_amd as m
     return m.REQ_BAD_CONFIDENCE
+
+
+@pytest.mark.parametrize("mode", [MODE_EARLY_STOP, MODE_GLOBAL])
+def test_ties_and_wide_shapes(sv, mode):
+    """Equal survivals across requests (the admission boundary splits a run of equal keys),
+    gamma above 16 and more than 1024 requests."""
+    rng = np.random.default_rng(41 + mode)
+    for B, G in ((2000, 8), (300, 40), (16384, 1), (128, 64), (1023, 16), (5, 64)):
+        for trial in range(3):
+            if trial == 0:
+                conf = np.full((B, G), np.float32(0.9))          # identical rows
+            elif trial == 1:
+                conf = rng.choice(np.array([0.5, 0.75, 1.0], dtype=np.float32), (B, G))
+            else:
+                conf = make_confidences(B, G, int(rng.integers(1 << 30))).numpy()
+                conf[:, : G // 2] = np.float32(1.0)
+            sps = make_sps_table(B * (G + 1) + 1, int(rng.integers(1 << 30)))
+            budget = int(rng.integers(B, B * (G + 1) + 1))
+            L, th, st = _gpu(sv, conf, sps, budget, mode)
+            L_ref, th_ref = oracle.schedule(conf, sps, budget, mode)
+            assert (st == 0).all()
+            bad = np.flatnonzero(L != L_ref)
+            if bad.size:
+                print("mismatch", B, G, trial, budget, "sum", int(L.sum()), int(L_ref.sum()), "theta", repr(th),
+                      repr(th_ref))
+            assert bad.size == 0, (B, G, trial, budget, int(L.sum()), int(L_ref.sum()), th, th_ref,
+                                   bad[:8].tolist(), L[bad[:8]].tolist(), L_ref[bad[:8]].tolist())
+            assert th == th_ref, (B, G, trial, th, th_ref)

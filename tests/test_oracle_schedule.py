@@ -193,3 +193,20 @@ def test_retrospective_scheduler_biases_output(golden_dir):
         obs = np.bincount(first, minlength=2)
         p = stats.chisquare(obs, np.array(expect) * n).pvalue
         assert p > 1e-4, (mode, obs / n, expect)
+
+
+def test_fixed_point_is_exact_and_fits_int64():
+    """q(a) = floor(a * 2^FRAC_BITS) is a * 2^FRAC_BITS itself for every float32 a >= 2^-24, and the
+    largest tau (every request admitted in full at the candidate limit) fits a signed int64."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    a = np.concatenate([rng.random(2000).astype(np.float32),
+                        np.float32(2.0) ** -rng.integers(0, 25, 200).astype(np.float32),
+                        np.array([1.0, np.nextafter(np.float32(1), np.float32(0))], dtype=np.float32)])
+    for x in a:
+        if x >= 2.0 ** -24:
+            assert Fraction(fixed_point(x)) == Fraction(float(x)) * ONE
+    tiny = np.float32(2.0 ** -30) * np.float32(1.5)
+    assert fixed_point(tiny) == int(Fraction(float(tiny)) * ONE)   # floor below 2^-24
+    max_candidates, max_requests = 16384, 16384
+    assert (max_requests + max_candidates) * ONE < 2 ** 63
