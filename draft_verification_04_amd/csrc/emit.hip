@@ -131,18 +131,24 @@ struct Acc {
   double A, D, T;  // this range
 };
 
-__device__ __forceinline__ void classify(Acc& c, double qt, double qd, double cdh, double cdl, int v,
-                                         const VerifyArgs& a, int i) {
+// Accumulate one token pair; returns whether its residual sign is uncertain (p_t and p_d
+// within the margin of each other with the approximate normalisers): such tokens are
+// recorded by the caller and weighed exactly later.  No branches, so the table reads of a
+// whole step can be in flight together.
+__device__ __forceinline__ bool classify(Acc& c, double qt, double qd, double cdh, double cdl) {
   c.st += qt;
   c.sd += qd;
   c.T += qt;
   const bool pos = qt > cdh * qd;
   c.A += pos ? qt : 0.0;
   c.D += pos ? qd : 0.0;
-  if (!pos && qt > 0.0 && qt >= cdl * qd) {
-    const int slot = atomicAdd(&a.ereq[i].amb_n, 1);
-    if (slot < kAmbCap) a.amb[(size_t)i * kAmbCap + slot] = v;
-  }
+  return !pos && qt > 0.0 && qt >= cdl * qd;
+}
+
+// Record token v as uncertain (rare).
+__device__ __forceinline__ void record_uncertain(const VerifyArgs& a, int i, int v) {
+  const int slot = atomicAdd(&a.ereq[i].amb_n, 1);
+  if (slot < kAmbCap) a.amb[(size_t)i * kAmbCap + slot] = v;
 }
 
 struct PassShared {
@@ -165,9 +171,11 @@ __device__ __forceinline__ uint32_t half16(const uint32_t (&w)[4], int j) {
 // One step (64 lanes x 8 tokens) of a bf16 row pair from registers.  A lane whose 16 tokens
 // are all tabulated reads Q from the table; otherwise (rare: |z| < 2^-20, |z| >= 128,
 // infinities) it evaluates the same formula directly for the whole step.
-__device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& dd, bool resid, const EmitRows& e,
+template <bool RESID>
+__device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& dd, const EmitRows& e,
                                           double cdh, double cdl, int v0, const VerifyArgs& a, int i,
                                           const double* T64, const double* Qt) {
+  constexpr bool resid = RESID;
   const uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
   const uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
   bool miss = false;
@@ -176,15 +184,21 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
     miss |= q_slot(half16(wt, j)) < 0;
     if (resid) miss |= q_slot(half16(wd, j)) < 0;
   }
+  unsigned amb = 0;
   if (!miss) {
+    // two halves of four tokens: eight table reads in flight, registers kept in check
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double qt = Qt[q_slot(half16(wt, j))];
-      if (resid) {
-        const double qd = Qt[q_slot(half16(wd, j))];
-        classify(c, qt, qd, cdh, cdl, v0 + j, a, i);
-      } else {
-        c.T += qt;
+    for (int h = 0; h < 8; h += 4) {
+      double qt[4], qd[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qt[j] = Qt[q_slot(half16(wt, h + j))];
+        qd[j] = resid ? Qt[q_slot(half16(wd, h + j))] : 0.0;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (resid) amb |= (unsigned)classify(c, qt[j], qd[j], cdh, cdl) << (h + j);
+        else c.T += qt[j];
       }
     }
   } else {
@@ -193,11 +207,16 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
       const double qt = q_direct(__uint_as_float(half16(wt, j) << 16), e.invT, e.R, T64);
       if (resid) {
         const double qd = q_direct(__uint_as_float(half16(wd, j) << 16), e.invT, e.R, T64);
-        classify(c, qt, qd, cdh, cdl, v0 + j, a, i);
+        amb |= (unsigned)classify(c, qt, qd, cdh, cdl) << j;
       } else {
         c.T += qt;
       }
     }
+  }
+  if (amb) {
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j)
+      if ((amb >> j) & 1u) record_uncertain(a, i, v0 + j);
   }
 }
 
@@ -205,7 +224,7 @@ template <bool BF16, bool TOPK>
 __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int NWPB = kPassThreads / SPEC_WAVE;
-  constexpr int NWT = kEmitSegs * NWPB;
+  const int NWT = a.emit_segs * NWPB;
   const int V = a.V, NR = num_ranges(V);
   const bool resid = (e.d != nullptr);
   const double cdh = e.cd * (1.0 + kAmbTol), cdl = e.cd * (1.0 - kAmbTol);
@@ -232,8 +251,9 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
       c.A = c.D = c.T = 0.0;
 #pragma unroll
       for (int sub = 0; sub < kSubPerRange; ++sub) {
-        step_bf16(c, bt[sub], bd[sub], resid, e, cdh, cdl, r * kRangeElems + sub * kSub + lane * 8, a, i, sh.T64,
-                  sh.Qt);
+        const int v0 = r * kRangeElems + sub * kSub + lane * 8;
+        if (resid) step_bf16<true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
+        else step_bf16<false>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
         if (rn < NRfull) load(rn, sub, bt[sub], bd[sub]);
       }
       const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
@@ -256,7 +276,7 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
             const double qt = (zt >= e.tht) ? q_direct(zt, e.invT, e.R, sh.T64) : 0.0;
             if (resid) {
               const double qd = (zd >= e.thd) ? q_direct(zd, e.invT, e.R, sh.T64) : 0.0;
-              classify(c, qt, qd, cdh, cdl, v, a, i);
+              if (classify(c, qt, qd, cdh, cdl)) record_uncertain(a, i, v);
             } else {
               c.T += qt;
             }
@@ -277,7 +297,7 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
 template <bool BF16>
 __global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
   __shared__ PassShared sh;
-  const int i = blockIdx.x / kEmitSegs, seg = blockIdx.x % kEmitSegs;
+  const int i = a.r0 + (int)blockIdx.x / a.emit_segs, seg = (int)blockIdx.x % a.emit_segs;
   const int tid = threadIdx.x;
   init_t64(sh.T64);
   if (tid < SPEC_WAVE) {
@@ -321,6 +341,8 @@ struct FinalShared {
   double T64[64];
   double R[kMaxRanges];     // range weights, then inclusive prefix sums
   double corr[kMaxRanges];  // weights of the recorded uncertain-sign tokens
+  EmitRange rg[kMaxRanges]; // the emit pass's range sums, fetched early
+  int na;                   // uncertain-sign tokens recorded
   double wsum[kEmitThreads / SPEC_WAVE];
   double amb_w[kAmbCap];
   int amb_v[kAmbCap];
@@ -342,17 +364,33 @@ __device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, d
 template <bool BF16>
 __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) {
   __shared__ FinalShared sh;
-  const int i = blockIdx.x;
+  const int i = a.r0 + (int)blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int NW = kEmitThreads / SPEC_WAVE;
   const int G = a.G, V = a.V;
   init_t64(sh.T64);
+  const int NR = num_ranges(V);
+  const EmitReq* er = &a.ereq[i];
   if (tid < SPEC_WAVE) {
     int st, n;
     request_decision(a, i, &st, &n);
     if (tid == 0) {
       sh.st = st;
       sh.n = n;
+    }
+  } else if (!a.greedy_only) {
+    // meanwhile the other waves fetch what the emit pass left for this request
+    const int t = tid - SPEC_WAVE;
+    for (int r = t; r < NR; r += kEmitThreads - SPEC_WAVE) sh.rg[r] = a.ranges[(size_t)i * NR + r];
+    if (t == 0) {
+      double x = 0.0, y = 0.0;
+      for (int q = 0; q < a.emit_segs; ++q) {
+        x += er->st_part[q];
+        y += er->sd_part[q];
+      }
+      sh.St = x;
+      sh.Sd = y;
+      sh.na = er->amb_n;
     }
   }
   __syncthreads();
@@ -382,30 +420,17 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
 
   const EmitRows e = emit_rows<BF16>(a, i, n);
   const bool resid = (e.d != nullptr);
-  const int NR = num_ranges(V);
-  const EmitReq* er = &a.ereq[i];
   double ua, ue;
   verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
-  if (tid == 0) {
-    double x = 0.0, y = 0.0;
-    for (int s = 0; s < kEmitSegs; ++s) {
-      x += er->st_part[s];
-      y += er->sd_part[s];
-    }
-    sh.St = x;
-    sh.Sd = y;
-    // the sign classification assumed cd * S_d / S_t = 1 to within half its margin
-    const double rho = resid ? e.cd * y / x : 1.0;
-    sh.slow = resid && (!(fabs(rho - 1.0) <= 0.5 * kAmbTol) || er->amb_n > kAmbCap);
-    sh.use_t = !resid;
-  }
-  __syncthreads();
   const double St = sh.St, Sd = sh.Sd;
-  const bool slow = sh.slow;
+  // the sign classification assumed cd * S_d / S_t = 1 to within half its margin
+  const double rho = resid ? e.cd * Sd / St : 1.0;
+  const bool slow = resid && (!(fabs(rho - 1.0) <= 0.5 * kAmbTol) || sh.na > kAmbCap);
+  if (tid == 0) sh.use_t = !resid;
 
   // range weights
   if (resid && !slow) {
-    const int na = er->amb_n;
+    const int na = sh.na;
     for (int q = tid; q < na; q += blockDim.x) sh.amb_v[q] = a.amb[(size_t)i * kAmbCap + q];
     for (int r = tid; r < NR; r += blockDim.x) sh.corr[r] = 0.0;
     __syncthreads();
@@ -420,10 +445,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
     if (tid == 0)
       for (int q = 0; q < na; ++q) sh.corr[sh.amb_sorted[q] / kRangeElems] += sh.amb_w[q];
     __syncthreads();
-    for (int r = tid; r < NR; r += blockDim.x) {
-      const EmitRange g = a.ranges[(size_t)i * NR + r];
-      sh.R[r] = (g.a / St - g.d / Sd) + sh.corr[r];
-    }
+    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = (sh.rg[r].a / St - sh.rg[r].d / Sd) + sh.corr[r];
   } else if (resid && slow) {
     // exact weight of every token (rare: nearly identical target and draft rows)
     for (int r = 0; r < NR; ++r) {
@@ -441,40 +463,59 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
       __syncthreads();
     }
   } else {
-    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = a.ranges[(size_t)i * NR + r].t;
+    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = sh.rg[r].t;
   }
   __syncthreads();
 
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // inclusive prefix over ranges (sequential: at most a few hundred ranges)
-    if (tid == 0) {
-      double run = 0.0;
-      for (int r = 0; r < NR; ++r) {
-        run += sh.R[r];
-        sh.R[r] = run;
+    // inclusive prefix over the ranges (wave 0, four per lane), then the first range whose
+    // prefix passes u * W
+    static_assert(kMaxRanges <= 4 * SPEC_WAVE, "four ranges per lane");
+    if (wave == 0) {
+      double v[4], t = 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = lane * 4 + u;
+        v[u] = (r < NR) ? sh.R[r] : 0.0;
+        t += v[u];
       }
-      const double W = run;
-      if (resid && !sh.use_t && !(W > 0.0)) {
-        sh.use_t = 2;  // no residual mass (rounding): fall back to p_t of the same row
-      } else {
-        const double target = ue * W;
-        int lo = 0, hi = NR;  // first r with prefix > target
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (sh.R[mid] > target) hi = mid;
-          else lo = mid + 1;
+      const double incl = wave_inclusive_sum(t, lane);
+      double run = incl - t;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = lane * 4 + u;
+        run += v[u];
+        if (r < NR) sh.R[r] = run;
+      }
+      const double W = __shfl(incl, 63, SPEC_WAVE);
+      if (lane == 0) {
+        if (resid && !sh.use_t && !(W > 0.0)) {
+          sh.use_t = 2;  // no residual mass (rounding): fall back to p_t of the same row
+        } else {
+          sh.use_t = sh.use_t ? 1 : 0;
+          sh.target = ue * W;
+          sh.sel = NR;
         }
-        sh.target = target;
-        sh.past = (lo >= NR);
-        sh.sel = lo;
-        sh.before = (lo > 0 && lo < NR) ? sh.R[lo - 1] : 0.0;
       }
     }
     __syncthreads();
-    if (sh.use_t != 2) break;
-    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = a.ranges[(size_t)i * NR + r].t;
-    if (tid == 0) sh.use_t = 1;
+    if (sh.use_t == 2) {
+      for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = sh.rg[r].t;
+      if (tid == 0) sh.use_t = 1;
+      __syncthreads();
+      continue;
+    }
+    const double target = sh.target;
+    for (int r = tid; r < NR; r += blockDim.x)
+      if (sh.R[r] > target && (r == 0 || !(sh.R[r - 1] > target))) sh.sel = r;
     __syncthreads();
+    if (tid == 0) {
+      const int lo = sh.sel;
+      sh.past = (lo >= NR);
+      sh.before = (lo > 0 && lo < NR) ? sh.R[lo - 1] : 0.0;
+    }
+    __syncthreads();
+    break;
   }
   const bool wres = resid && sh.use_t == 0;
 
@@ -552,16 +593,19 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
 }
 
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s) {
+  const unsigned nreq = (unsigned)(a.r1 - a.r0);
+  if (nreq == 0) return;
   if (!a.greedy_only) {
+    const dim3 grid(nreq * (unsigned)a.emit_segs);
     if (bf16)
-      hipLaunchKernelGGL(emit_pass_kernel<true>, dim3(a.B * kEmitSegs), dim3(kPassThreads), 0, s, a);
+      hipLaunchKernelGGL(emit_pass_kernel<true>, grid, dim3(kPassThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(emit_pass_kernel<false>, dim3(a.B * kEmitSegs), dim3(kPassThreads), 0, s, a);
+      hipLaunchKernelGGL(emit_pass_kernel<false>, grid, dim3(kPassThreads), 0, s, a);
   }
   if (bf16)
-    hipLaunchKernelGGL(emit_final_kernel<true>, dim3(a.B), dim3(kEmitThreads), 0, s, a);
+    hipLaunchKernelGGL(emit_final_kernel<true>, dim3(nreq), dim3(kEmitThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(emit_final_kernel<false>, dim3(a.B), dim3(kEmitThreads), 0, s, a);
+    hipLaunchKernelGGL(emit_final_kernel<false>, dim3(nreq), dim3(kEmitThreads), 0, s, a);
 }
 
 }  // namespace spec

@@ -33,7 +33,7 @@ struct Partial {
 
 // Emitted-token work: one range = kRangeElems consecutive tokens of the emit row.
 constexpr int kRangeElems = 2048; // tokens per emit range (one wave, 4 steps of 64 x 8)
-constexpr int kEmitSegs = 2;      // workgroups per request in the emit pass
+constexpr int kMaxEmitSegs = 16;  // workgroups per request in the emit pass, at most
 constexpr int kAmbCap = 256;      // tokens of uncertain residual sign recorded per request
 
 struct EmitRange {
@@ -43,8 +43,8 @@ struct EmitRange {
 };
 
 struct EmitReq {
-  double st_part[kEmitSegs];  // per-segment sums of E_t = exp(z_t/T - R_t)
-  double sd_part[kEmitSegs];  // per-segment sums of E_d = exp(z_d/T - R_d)
+  double st_part[kMaxEmitSegs];  // per-segment sums of E_t = exp(z_t/T - R_t)
+  double sd_part[kMaxEmitSegs];  // per-segment sums of E_d = exp(z_d/T - R_d)
   int32_t amb_n;              // number of uncertain-sign tokens seen
   int32_t pad;
 };
@@ -76,6 +76,8 @@ struct VerifyArgs {
   EmitReq* ereq;       // [B]
   EmitRange* ranges;   // [B, ceil(V / kRangeElems)]
   int32_t* amb;        // [B, kAmbCap]
+  int r0, r1;          // the emit kernels handle requests [r0, r1)
+  int emit_segs;       // emit-pass workgroups per request (2 .. kMaxEmitSegs)
 };
 
 constexpr int kStreamThreads = 512;
