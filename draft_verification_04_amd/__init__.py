@@ -53,6 +53,7 @@ EXPORTS = {
     "spec_schedule_workspace_size": (_Z, [_I, _I]),
     "spec_schedule_lengths": (_I, [_I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "spec_philox_uniforms": (_I, [_I, _P, _P, _P, _P, _P, _P]),
+    "spec_read_ceiling": (_I, [_P, _Z, _I, _P, _P]),
 }
 
 _lib_handle = None
@@ -229,6 +230,15 @@ def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_schedule_lengths", code)
     return out
+
+
+def read_ceiling(data: torch.Tensor, nbytes: int, grid: int, sink: torch.Tensor, stream=None) -> None:
+    """spec_read_ceiling: one plain read of the first `nbytes` of `data` (a measurement aid)."""
+    lib = load_library()
+    if not data.is_cuda or nbytes > data.numel() * data.element_size():
+        raise ValueError("data must be a device tensor of at least nbytes")
+    _check("spec_read_ceiling", lib.spec_read_ceiling(_ptr(data), int(nbytes), int(grid), _ptr(sink),
+                                                      _stream(stream)))
 
 
 def philox_uniforms(seed: torch.Tensor, request: torch.Tensor, position: torch.Tensor, stream=None):

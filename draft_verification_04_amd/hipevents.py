@@ -21,6 +21,8 @@ def _lib():
         _hip.hipEventElapsedTime.restype = ctypes.c_int
         _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         _hip.hipEventSynchronize.restype = ctypes.c_int
+        _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventRecord.restype = ctypes.c_int
     return _hip
 
 
@@ -42,6 +44,13 @@ class HipEvent:
     @property
     def cuda_event(self):
         return self.handle.value
+
+    def record(self, stream) -> None:
+        """Record on a torch stream (or a raw hipStream_t as int / None for the null stream)."""
+        h = getattr(stream, "cuda_stream", stream)
+        rc = _lib().hipEventRecord(self.handle, ctypes.c_void_p(h) if h else None)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, end: "HipEvent") -> float:
         _lib().hipEventSynchronize(end.handle)

@@ -221,6 +221,18 @@ int32_t spec_philox_uniforms(int32_t n, const uint64_t* seed, const int32_t* req
                              const int32_t* position, double* u_accept, double* u_emit,
                              void* stream);
 
+/*
+ * spec_read_ceiling -- measurement aid, not part of verification: reads
+ * floor(bytes / 16) 16-byte vectors starting at `data` once (nontemporal,
+ * grid-stride over `grid` workgroups of 512 threads) so that a caller can time
+ * the device's achievable HBM read rate on the same number of bytes the
+ * streaming kernel reads.  `data` device, 16-byte aligned, at least `bytes`
+ * long; `sink` [1] uint32 device, written only in a case that does not arise in
+ * practice.  Asynchronous on `stream`.  SPEC_ERR_INVALID_ARG for a null or
+ * misaligned pointer, bytes < 16 or grid outside [1, 2^20].
+ */
+int32_t spec_read_ceiling(const void* data, size_t bytes, int32_t grid, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

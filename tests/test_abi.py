@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("spec_verify", "spec_verify_greedy", "spec_schedule_lengths", "spec_verify_workspace_size",
               "spec_schedule_workspace_size", "spec_abi_version", "spec_status_string",
-              "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size"):
+              "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size",
+              "spec_read_ceiling"):
         assert n in names, n
 
 
@@ -126,3 +127,12 @@ def test_greedy_and_schedule_reject_bad_arguments(lib):
     assert lib.spec_schedule_lengths(4, 4, p, p, 100, 10, 0, p, None, None, p, 8, None) == 2   # short
     assert lib.spec_philox_uniforms(-1, p, p, p, p, p, None) == 1
     assert lib.spec_philox_uniforms(0, None, None, None, None, None, None) == 0
+
+
+def test_read_ceiling_rejects_bad_arguments(lib):
+    keep, p = _fake()
+    assert lib.spec_read_ceiling(None, 1024, 64, p, None) == 1
+    assert lib.spec_read_ceiling(ctypes.c_void_p(p.value + 4), 1024, 64, p, None) == 1   # misaligned
+    assert lib.spec_read_ceiling(p, 8, 64, p, None) == 1
+    assert lib.spec_read_ceiling(p, 1024, 0, p, None) == 1
+    assert lib.spec_read_ceiling(p, 1024, 64, None, None) == 1
