@@ -127,7 +127,7 @@ __device__ __forceinline__ double q_at(const char* row, int v, float th, double 
 
 // Per-lane accumulators for one range.
 struct Acc {
-  double st, sd;   // running totals over everything this lane saw
+  double sd;       // running total of E_d over everything this lane saw
   double A, D, T;  // this range
 };
 
@@ -136,12 +136,14 @@ struct Acc {
 // recorded by the caller and weighed exactly later.  No branches, so the table reads of a
 // whole step can be in flight together.
 __device__ __forceinline__ bool classify(Acc& c, double qt, double qd, double cdh, double cdl) {
-  c.st += qt;
   c.sd += qd;
   c.T += qt;
   const bool pos = qt > cdh * qd;
-  c.A += pos ? qt : 0.0;
-  c.D += pos ? qd : 0.0;
+  // fma(1, q, s) = s + q and fma(0, q, s) = s, rounded as the plain sums (q is finite here, or
+  // the normaliser check sends the request to the exact path): one select instead of four
+  const double one = pos ? 1.0 : 0.0;
+  c.A = fma(one, qt, c.A);
+  c.D = fma(one, qd, c.D);
   return !pos && qt > 0.0 && qt >= cdl * qd;
 }
 
@@ -151,10 +153,12 @@ __device__ __forceinline__ void record_uncertain(const VerifyArgs& a, int i, int
   if (slot < kAmbCap) a.amb[(size_t)i * kAmbCap + slot] = v;
 }
 
+constexpr int kMaxWaves = 1024 / SPEC_WAVE;  // largest emit workgroup, in waves
+
 struct PassShared {
   double T64[64];
   double Qt[kQsize];
-  double red[2][kPassThreads / SPEC_WAVE];
+  double red[2][kMaxWaves];
   int st, n;
 };
 
@@ -220,10 +224,14 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
   }
 }
 
+// The ranges of request i that segment `seg` owns, each written as an EmitRange to out[r]
+// (global memory, or LDS when the same workgroup finishes the request); each wave's sum of
+// E_d goes to sh.red[1][wave].
 template <bool BF16, bool TOPK>
-__device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e) {
+__device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e,
+                            EmitRange* out) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int NWPB = kPassThreads / SPEC_WAVE;
+  const int NWPB = (int)(blockDim.x >> 6);
   const int NWT = a.emit_segs * NWPB;
   const int V = a.V, NR = num_ranges(V);
   const bool resid = (e.d != nullptr);
@@ -231,7 +239,7 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
   const bool aligned = ((reinterpret_cast<uintptr_t>(e.t) | reinterpret_cast<uintptr_t>(e.d)) & 15u) == 0;
   // ranges a wave can read whole with 16-byte loads
   const int NRfull = (BF16 && !TOPK && aligned) ? V / kRangeElems : 0;
-  Acc c{0.0, 0.0, 0.0, 0.0, 0.0};
+  Acc c{0.0, 0.0, 0.0, 0.0};
   int r = seg * NWPB + wave;
   if (BF16 && !TOPK) {
     // the 4 steps of a range are in flight at once; each register slot is refilled with
@@ -257,7 +265,7 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
         if (rn < NRfull) load(rn, sub, bt[sub], bd[sub]);
       }
       const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
-      if (lane == 0) a.ranges[(size_t)i * NR + r] = EmitRange{A, D, T};
+      if (lane == 0) out[r] = EmitRange{A, D, T};
       r = rn;
     }
   }
@@ -285,52 +293,57 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
       }
     }
     const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
-    if (lane == 0) a.ranges[(size_t)i * NR + r] = EmitRange{A, D, T};
+    if (lane == 0) out[r] = EmitRange{A, D, T};
   }
-  const double st = wave_sum(c.st), sd = wave_sum(c.sd);
+  const double sd = wave_sum(c.sd);
   if (lane == 0) {
-    sh.red[0][wave] = st;
     sh.red[1][wave] = sd;
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
-  __shared__ PassShared sh;
-  const int i = a.r0 + (int)blockIdx.x / a.emit_segs, seg = (int)blockIdx.x % a.emit_segs;
-  const int tid = threadIdx.x;
-  init_t64(sh.T64);
-  if (tid < SPEC_WAVE) {
+// Decision of request i by wave 0 into sh.st / sh.n (the whole block waits for it).
+__device__ __forceinline__ void decide_into(PassShared& sh, const VerifyArgs& a, int i) {
+  if (threadIdx.x < SPEC_WAVE) {
     int st, n;
     request_decision(a, i, &st, &n);
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
       sh.st = st;
       sh.n = n;
     }
   }
   __syncthreads();
-  const int st = sh.st, n = sh.n;
-  if (st || a.temperature[i] == 0.f) return;
+}
+
+// The emit pass over segment `seg` of request i (after its decision, sampling only).
+template <bool BF16>
+__device__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, int n, EmitRange* out) {
   const EmitRows e = emit_rows<BF16>(a, i, n);
   const int K = a.top_k ? a.top_k[i] : 0;
   const bool topk = K > 0 && K < a.V;
   if (BF16 && !topk) {
     build_qtab(sh.Qt, e.invT, e.R, sh.T64);
     __syncthreads();
-    pass_ranges<BF16, false>(sh, a, i, seg, e);
+    pass_ranges<BF16, false>(sh, a, i, seg, e, out);
   } else if (topk) {
-    pass_ranges<BF16, true>(sh, a, i, seg, e);
+    pass_ranges<BF16, true>(sh, a, i, seg, e, out);
   } else {
-    pass_ranges<BF16, false>(sh, a, i, seg, e);
+    pass_ranges<BF16, false>(sh, a, i, seg, e, out);
   }
   __syncthreads();
-  if (tid == 0) {
-    double x = 0.0, y = 0.0;
-    for (int w = 0; w < kPassThreads / SPEC_WAVE; ++w) {
-      x += sh.red[0][w];
-      y += sh.red[1][w];
-    }
-    a.ereq[i].st_part[seg] = x;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
+  __shared__ PassShared sh;
+  const int i = a.r0 + (int)blockIdx.x / a.emit_segs, seg = (int)blockIdx.x % a.emit_segs;
+  init_t64(sh.T64);
+  decide_into(sh, a, i);
+  const int st = sh.st, n = sh.n;
+  if (st || a.temperature[i] == 0.f) return;
+  run_pass<BF16>(sh, a, i, seg, n, a.ranges + (size_t)i * num_ranges(a.V));
+  if (threadIdx.x == 0) {
+    double y = 0.0;
+    for (int w = 0; w < kPassThreads / SPEC_WAVE; ++w) y += sh.red[1][w];
     a.ereq[i].sd_part[seg] = y;
   }
 }
@@ -343,7 +356,7 @@ struct FinalShared {
   double corr[kMaxRanges];  // weights of the recorded uncertain-sign tokens
   EmitRange rg[kMaxRanges]; // the emit pass's range sums, fetched early
   int na;                   // uncertain-sign tokens recorded
-  double wsum[kEmitThreads / SPEC_WAVE];
+  double wsum[kMaxWaves];
   double amb_w[kAmbCap];
   int amb_v[kAmbCap];
   int amb_sorted[kAmbCap];
@@ -361,40 +374,17 @@ __device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, d
   return fmax(0.0, qt / St - qd / Sd);
 }
 
+// Everything after request i's decision (st, n): status and outputs, then, for a sampling
+// request, the emitted token from the emit pass's range sums (sh.rg, sh.St, sh.Sd, sh.na
+// filled).  Works for any block of 256 .. 1024 threads (a multiple of 256); the token octets
+// of the crossing range belong to the first 256 threads, the others only join loops and
+// barriers.
 template <bool BF16>
-__global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) {
-  __shared__ FinalShared sh;
-  const int i = a.r0 + (int)blockIdx.x;
+__device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int st, int n) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int NW = kEmitThreads / SPEC_WAVE;
+  const int NW = (int)(blockDim.x >> 6);
   const int G = a.G, V = a.V;
-  init_t64(sh.T64);
   const int NR = num_ranges(V);
-  const EmitReq* er = &a.ereq[i];
-  if (tid < SPEC_WAVE) {
-    int st, n;
-    request_decision(a, i, &st, &n);
-    if (tid == 0) {
-      sh.st = st;
-      sh.n = n;
-    }
-  } else if (!a.greedy_only) {
-    // meanwhile the other waves fetch what the emit pass left for this request
-    const int t = tid - SPEC_WAVE;
-    for (int r = t; r < NR; r += kEmitThreads - SPEC_WAVE) sh.rg[r] = a.ranges[(size_t)i * NR + r];
-    if (t == 0) {
-      double x = 0.0, y = 0.0;
-      for (int q = 0; q < a.emit_segs; ++q) {
-        x += er->st_part[q];
-        y += er->sd_part[q];
-      }
-      sh.St = x;
-      sh.Sd = y;
-      sh.na = er->amb_n;
-    }
-  }
-  __syncthreads();
-  const int st = sh.st, n = sh.n;
   const int L = a.lengths ? a.lengths[i] : G;
   if (a.status && tid == 0) a.status[i] = st;
   if (st) {
@@ -541,13 +531,14 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
   } else {
     // the selected range, token by token: thread t holds tokens base + 8t .. base + 8t + 7
   static_assert(kEmitThreads * 8 == kRangeElems, "one token octet per thread");
+    const bool mine = tid < kEmitThreads;
     const int base = sh.sel * kRangeElems + tid * 8;
     double w[8];
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int v = base + j;
-      w[j] = (v < V) ? weight<BF16>(e, v, wres, St, Sd, sh.T64) : 0.0;
+      w[j] = (mine && v < V) ? weight<BF16>(e, v, wres, St, Sd, sh.T64) : 0.0;
       s += w[j];
     }
     const double incl = wave_inclusive_sum(s, lane);
@@ -565,13 +556,14 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
     if (lane == 0) sh.amb_v[NW + wave] = pos ? 63 - __clzll((long long)pos) : -1;
     __syncthreads();
     int cw = -1, cl = -1;
-    for (int q = 0; q < NW && cw < 0; ++q)
+    constexpr int NWO = kEmitThreads / SPEC_WAVE;  // waves holding the range's octets
+    for (int q = 0; q < NWO && cw < 0; ++q)
       if (sh.amb_v[q] < 64) {
         cw = q;
         cl = sh.amb_v[q];
       }
     if (cw < 0) {  // rounding left no crossing: the last thread with weight
-      for (int q = NW - 1; q >= 0 && cw < 0; --q)
+      for (int q = NWO - 1; q >= 0 && cw < 0; --q)
         if (sh.amb_v[NW + q] >= 0) {
           cw = q;
           cl = sh.amb_v[NW + q];
@@ -592,9 +584,88 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
   if (tid == 0) a.out_tokens[(size_t)i * (G + 1) + n] = sh.token;
 }
 
+template <bool BF16>
+__global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) {
+  __shared__ FinalShared sh;
+  const int i = a.r0 + (int)blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.G, V = a.V;
+  init_t64(sh.T64);
+  const int NR = num_ranges(V);
+  const EmitReq* er = &a.ereq[i];
+  if (tid < SPEC_WAVE) {
+    int st, n;
+    request_decision(a, i, &st, &n);
+    if (tid == 0) {
+      sh.st = st;
+      sh.n = n;
+    }
+  } else if (!a.greedy_only) {
+    // meanwhile the other waves fetch what the emit pass left for this request
+    const int t = tid - SPEC_WAVE;
+    for (int r = t; r < NR; r += kEmitThreads - SPEC_WAVE) sh.rg[r] = a.ranges[(size_t)i * NR + r];
+    if (t == 0) {
+      double y = 0.0;
+      for (int q = 0; q < a.emit_segs; ++q) y += er->sd_part[q];
+      sh.Sd = y;
+      sh.na = er->amb_n;
+    }
+  }
+  __syncthreads();
+  if (tid < SPEC_WAVE && !a.greedy_only) {
+    // S_t = the sum of the range totals of E_t (wave 0, four ranges per lane)
+    double x = 0.0;
+    for (int r = tid; r < NR; r += SPEC_WAVE) x += sh.rg[r].t;
+    x = wave_sum(x);
+    if (tid == 0) sh.St = x;
+  }
+  __syncthreads();
+  finish_request<BF16>(sh, a, i, sh.st, sh.n);
+}
+
+// One 1024-thread workgroup per request does the whole emit: decision, the pass over all of
+// the emit row pair (16 waves), then finish_request from the range sums it keeps in LDS.
+// Used when there are at least as many requests as compute units.
+template <bool BF16>
+__global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a) {
+  __shared__ PassShared ps;
+  __shared__ FinalShared fs;
+  const int i = a.r0 + (int)blockIdx.x;
+  const int tid = threadIdx.x;
+  const int NR = num_ranges(a.V);
+  init_t64(ps.T64);
+  init_t64(fs.T64);
+  decide_into(ps, a, i);
+  const int st = ps.st, n = ps.n;
+  if (!st && !a.greedy_only && a.temperature[i] != 0.f) {
+    run_pass<BF16>(ps, a, i, 0, n, fs.rg);
+    if (tid < SPEC_WAVE) {
+      double x = 0.0;
+      for (int r = tid; r < NR; r += SPEC_WAVE) x += fs.rg[r].t;
+      x = wave_sum(x);
+      if (tid == 0) {
+        double y = 0.0;
+        for (int w = 0; w < kFusedThreads / SPEC_WAVE; ++w) y += ps.red[1][w];
+        fs.St = x;
+        fs.Sd = y;
+        fs.na = atomicAdd(&a.ereq[i].amb_n, 0);   // read at L2, where the pass counted
+      }
+    }
+    __syncthreads();
+  }
+  finish_request<BF16>(fs, a, i, st, n);
+}
+
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s) {
   const unsigned nreq = (unsigned)(a.r1 - a.r0);
   if (nreq == 0) return;
+  if (!a.greedy_only && a.emit_segs == 1) {
+    if (bf16)
+      hipLaunchKernelGGL(emit_fused_kernel<true>, dim3(nreq), dim3(kFusedThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(emit_fused_kernel<false>, dim3(nreq), dim3(kFusedThreads), 0, s, a);
+    return;
+  }
   if (!a.greedy_only) {
     const dim3 grid(nreq * (unsigned)a.emit_segs);
     if (bf16)

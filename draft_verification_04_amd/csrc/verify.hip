@@ -784,8 +784,9 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
     hipLaunchKernelGGL(combine_kernel<false>, dim3(cgrid), dim3(256), 0, s, a);
   a.r0 = 0;
   a.r1 = a.B;
-  // about 512 emit-pass workgroups, so that small batches still cover the chip
-  a.emit_segs = std::max(2, std::min(kMaxEmitSegs, (512 + a.B - 1) / a.B));
+  // one workgroup per request doing the whole emit when that covers the chip, else about 512
+  // emit-pass workgroups so that small batches still do, and a separate finishing kernel
+  a.emit_segs = a.B >= kFuseMinRequests ? 1 : std::max(2, std::min(kMaxEmitSegs, (512 + a.B - 1) / a.B));
   launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

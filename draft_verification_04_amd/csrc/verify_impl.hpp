@@ -43,8 +43,7 @@ struct EmitRange {
 };
 
 struct EmitReq {
-  double st_part[kMaxEmitSegs];  // per-segment sums of E_t = exp(z_t/T - R_t)
-  double sd_part[kMaxEmitSegs];  // per-segment sums of E_d = exp(z_d/T - R_d)
+  double sd_part[kMaxEmitSegs];  // per-segment sums of E_d = exp(z_d/T - R) (E_t sums are the ranges')
   int32_t amb_n;              // number of uncertain-sign tokens seen
   int32_t pad;
 };
@@ -77,13 +76,15 @@ struct VerifyArgs {
   EmitRange* ranges;   // [B, ceil(V / kRangeElems)]
   int32_t* amb;        // [B, kAmbCap]
   int r0, r1;          // the emit kernels handle requests [r0, r1)
-  int emit_segs;       // emit-pass workgroups per request (2 .. kMaxEmitSegs)
+  int emit_segs;       // emit-pass workgroups per request (1 = one fused workgroup, else 2 .. kMaxEmitSegs)
 };
 
 constexpr int kStreamThreads = 512;
 constexpr int kWorklistThreads = 1024;
 constexpr int kPassThreads = 512;    // emit pass workgroup
 constexpr int kEmitThreads = 256;    // emit final workgroup (x 8 tokens = one range)
+constexpr int kFusedThreads = 1024;  // one workgroup per request doing the whole emit
+constexpr int kFuseMinRequests = 256; // fuse when every compute unit gets a request (MI355X: 256 CUs)
 constexpr int kTopkCap = 4096;   // top-k candidates kept in LDS per row
 constexpr int kTopkPre = 4;      // vectors per thread sampled for the top-k lower bound
 
