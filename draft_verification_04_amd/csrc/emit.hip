@@ -623,9 +623,92 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
   finish_request<BF16>(sh, a, i, sh.st, sh.n);
 }
 
-// One 1024-thread workgroup per request does the whole emit: decision, the pass over all of
-// the emit row pair (16 waves), then finish_request from the range sums it keeps in LDS.
-// Used when there are at least as many requests as compute units.
+// The acceptance test of every position of request i and its first rejection, taken by wave 0
+// (lane per position) straight from the streaming kernel's segment partials: row statistics,
+// r = min(1, p_t(x)/p_d(x)) with the logits at x the partials carry, the Philox uniform; top-k
+// positions were finished by the streaming kernel.  Writes the row and acceptance records
+// (read by the emit pass and finish_request) and sh.st / sh.n.
+__device__ void decide_full(PassShared& sh, const VerifyArgs& a, int i) {
+  const int lane = threadIdx.x;
+  const int G = a.G, V = a.V, nseg = a.nseg;
+  const int L = a.lengths ? a.lengths[i] : G;
+  int st = 0;
+  if (L < 0 || L > G) {
+    if (lane == 0) {
+      sh.st = SPEC_REQ_BAD_LENGTH;
+      sh.n = 0;
+    }
+    return;
+  }
+  const float T = a.temperature[i];
+  const int K0 = a.top_k ? a.top_k[i] : 0;
+  if (!(T >= 0.f && T < INFINITY)) st |= SPEC_REQ_BAD_TEMPERATURE;
+  if (K0 < 0) st |= SPEC_REQ_BAD_TOPK;
+  const int x = (lane < L) ? a.tokens[(size_t)i * G + lane] : 0;
+  if (__ballot(lane < L && (x < 0 || x >= V))) st |= SPEC_REQ_BAD_TOKEN;
+  if (st == 0) st |= a.req_status[i];
+  if (st) {
+    if (lane == 0) {
+      sh.st = st;
+      sh.n = 0;
+    }
+    return;
+  }
+  const bool greedy = (T == 0.f);
+  const bool topk = !greedy && K0 > 0 && K0 < V;
+  const double c64 = greedy ? 0.0 : kLog2e / (double)T;
+  int accept = 1, bad = 0;
+  for (int k = lane; k <= L; k += SPEC_WAVE) {
+    const size_t rt_i = (size_t)i * (G + 1) + k, rd_i = (size_t)i * G + k;
+    const Partial* pt = a.part_t + rt_i * nseg;
+    const Partial* pd = a.part_d + rt_i * nseg;
+    int acc_k = 1;
+    if (topk) {
+      bad |= !(a.rows_t[rt_i].lse2 == a.rows_t[rt_i].lse2);
+      if (k < L) acc_k = a.acc[rd_i].accept;
+    } else if (greedy) {
+      const int am = combine_argmax(pt, nseg);
+      bad |= am < 0;
+      a.rows_t[rt_i] = RowStat{0.0, -INFINITY, am < 0 ? 0 : am};
+      if (k < L) {
+        acc_k = (x == am);
+        a.acc[rd_i] = AccRec{acc_k ? 1.0 : 0.0, acc_k, 1};
+      }
+    } else {
+      const double l2t = combine_sum(pt, nseg);
+      bad |= !(l2t == l2t);
+      a.rows_t[rt_i] = RowStat{l2t, -INFINITY, 0};
+      if (k < L) {
+        const double l2d = combine_sum(pd, nseg);
+        bad |= !(l2d == l2d);
+        a.rows_d[rd_i] = RowStat{l2d, -INFINITY, 0};
+        const double r = acceptance_ratio(pt[0].zx, pd[0].zx, c64, l2t, -INFINITY, l2d, -INFINITY);
+        double ua, ue;
+        verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
+        acc_k = ua < r;
+        a.acc[rd_i] = AccRec{r, acc_k, 1};
+      }
+    }
+    if (k < L) accept = acc_k;   // k < L <= 64: the lane's first round
+  }
+  if (__ballot(bad)) {
+    if (lane == 0) {
+      sh.st = SPEC_REQ_NONFINITE;
+      sh.n = 0;
+    }
+    return;
+  }
+  const unsigned long long rej = __ballot(lane < L && !accept);
+  if (lane == 0) {
+    sh.st = 0;
+    sh.n = rej ? (int)__ffsll((long long)rej) - 1 : L;
+  }
+}
+
+// One 1024-thread workgroup per request does all of the request's work after the streaming:
+// the acceptance decision from the segment partials, the emit pass over the whole emit row pair
+// (16 waves), then finish_request from the range sums it keeps in LDS.  Used when there are
+// at least as many requests as compute units.
 template <bool BF16>
 __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a) {
   __shared__ PassShared ps;
@@ -635,7 +718,8 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
   const int NR = num_ranges(a.V);
   init_t64(ps.T64);
   init_t64(fs.T64);
-  decide_into(ps, a, i);
+  if (tid < SPEC_WAVE) decide_full(ps, a, i);
+  __syncthreads();
   const int st = ps.st, n = ps.n;
   if (!st && !a.greedy_only && a.temperature[i] != 0.f) {
     run_pass<BF16>(ps, a, i, 0, n, fs.rg);

@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
       if (L >= k) {
         const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
         a.items[idx] = (i << 7) | k;
+        a.items_x[idx] = (k < L) ? a.tokens[(size_t)i * G + k] : -1;
       }
     }
     __syncthreads();
@@ -499,15 +500,8 @@ __device__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double 
     bad |= !(l2d == l2d);
     const int x = a.tokens[(size_t)i * G + k];
     if (!bad && x >= 0 && x < V) {
-      const float zt = load_elem<BF16>(trow, x);
-      const float zd = load_elem<BF16>(drow, x);
-      // log p(x) = ln2 * (z_x * log2(e)/T - lse2), -inf outside the kept set
-      const double lpt = (zt >= tht) ? kLn2 * ((double)zt * c64 - l2t) : -INFINITY;
-      const double lpd = (zd >= thd) ? kLn2 * ((double)zd * c64 - l2d) : -INFINITY;
-      double r;
-      if (lpt == -INFINITY) r = 0.0;
-      else if (lpd == -INFINITY) r = 1.0;
-      else r = fmin(1.0, exp(lpt - lpd));
+      const double r = acceptance_ratio(load_elem<BF16>(trow, x), load_elem<BF16>(drow, x), c64, l2t, tht, l2d,
+                                        thd);
       double ua, ue;
       verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
       a.acc[(size_t)i * G + k] = AccRec{r, ua < r ? 1 : 0, 1};
@@ -518,7 +512,7 @@ __device__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double 
 
 // Reduce the per-thread (M, S, bad) of one row's waves into a segment Partial (written by lt == 0).
 __device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float S, int bad, int wave, int lane,
-                                                int first_wave, int nwaves, int lt, Partial* out) {
+                                                int first_wave, int nwaves, int lt, float zx, Partial* out) {
   const float Mw = wave_max(M);
   double Sd = (S > 0.f) ? ldexp((double)S, (int)fmaxf(M - Mw, -2000.f)) : 0.0;
   Sd = wave_sum(Sd);
@@ -539,23 +533,11 @@ __device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float
     double Sr = 0.0;
     for (int w = first_wave; w < first_wave + nwaves; ++w)
       if (sh.S[w] > 0.0) Sr += ldexp(sh.S[w], (int)fmaxf(sh.M[w] - Mr, -2000.f));
-    *out = Partial{Sr, Mr, 0, b, 0};
+    *out = Partial{Sr, Mr, 0, b, zx};
   }
 }
 
 // log2-sum-exp of a row from its segment partials (fixed segment order); NaN when invalid.
-__device__ __forceinline__ double combine_sum(const Partial* p, int nseg) {
-  float Mr = -INFINITY;
-  int bad = 0;
-  for (int s = 0; s < nseg; ++s) {
-    bad |= p[s].bad;
-    if (p[s].v > 0.0) Mr = fmaxf(Mr, p[s].m);
-  }
-  double Sr = 0.0;
-  for (int s = 0; s < nseg; ++s)
-    if (p[s].v > 0.0) Sr += ldexp(p[s].v, (int)fmaxf(p[s].m - Mr, -2000.f));
-  return (bad || !(Sr > 0.0)) ? NAN : (double)Mr + log2(Sr);
-}
 
 // One workgroup per (work item, segment).  Target row k and, when k < L, draft row k of
 // the item are streamed together by the two halves of the workgroup; a lone target row uses
@@ -605,8 +587,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   const int vb = (int)((long long)geo.nvec * seg / nseg);
   const int ve = (int)((long long)geo.nvec * (seg + 1) / nseg);
   const bool ends = (seg == 0);
-  Partial* pt = a.part_t + (size_t)g * nseg;
-  Partial* pd = a.part_d + (size_t)g * nseg;
+  Partial* pt = a.part_t + ((size_t)i * (G + 1) + k) * nseg;
+  Partial* pd = a.part_d + ((size_t)i * (G + 1) + k) * nseg;
 
   if (greedy) {
     float best = -INFINITY;
@@ -631,69 +613,68 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
         rbad |= sh.bad[w];
         if (sh.best[w] == rb) ri = min(ri, sh.bidx[w]);
       }
-      pt[seg] = Partial{(double)rb, 0.f, ri, rbad, 0};
+      pt[seg] = Partial{(double)rb, 0.f, ri, rbad, NAN};
     }
   } else {
+    // the writer of segment 0 also fetches the row's logit at the draft token, which the
+    // acceptance test needs (its load overlaps the streaming)
+    float zx = NAN;
+    if (seg == 0 && two && lt == 0) {
+      const int x = a.items_x[g];
+      if (x >= 0 && x < V) zx = load_elem<BF16>(row, x);
+    }
     float M = -0x1p30f, S = 0.f;
     int bad = 0;
     stream_sum<BF16>(row, V, vb, ve, ends, c_hi, c_lo, lt, nthr, M, S, bad);
-    row_partial_sum(sh, M, S, bad, wave, lane, first_wave, nwaves, lt, which ? &pd[seg] : &pt[seg]);
+    row_partial_sum(sh, M, S, bad, wave, lane, first_wave, nwaves, lt, zx, which ? &pd[seg] : &pt[seg]);
   }
 }
 
 // Finish every segmented work item: combine its segment partials and run the acceptance
 // test (one thread per item).  Top-k items were finished by the streaming kernel.
-template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a) {
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= *a.nitems) return;
   const int item = a.items[g];
   const int i = item >> 7, k = item & 127;
   const int G = a.G, V = a.V, nseg = a.nseg;
-  constexpr int ES = BF16 ? 2 : 4;
   const float T = a.greedy_only ? 0.f : a.temperature[i];
   if (!(T >= 0.f && T < INFINITY)) return;
-  int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
-  if (K < 0) return;
-  if (K >= V) K = 0;
-  if (K > 0) return;
+  const int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+  if (K < 0 || (K > 0 && K < V)) return;
   const int L = a.lengths ? a.lengths[i] : G;
-  const bool greedy = (T == 0.f);
-  const bool two = !greedy && k < L;
-  const Partial* pt = a.part_t + (size_t)g * nseg;
-  const Partial* pd = a.part_d + (size_t)g * nseg;
-  if (greedy) {
-    float rb = -INFINITY;
-    int ri = 0x7fffffff, rbad = 0;
-    for (int s = 0; s < nseg; ++s) {
-      const Partial q = pt[s];
-      rbad |= q.bad;
-      const float v = (float)q.v;
-      if (v > rb) {
-        rb = v;
-        ri = q.idx;
-      } else if (v == rb) {
-        ri = min(ri, q.idx);
-      }
-    }
-    if (rbad || !(rb > -INFINITY)) {
+  const Partial* pt = a.part_t + ((size_t)i * (G + 1) + k) * nseg;
+  const Partial* pd = a.part_d + ((size_t)i * (G + 1) + k) * nseg;
+  if (T == 0.f) {
+    int am = combine_argmax(pt, nseg);
+    if (am < 0) {
       atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
-      ri = 0;
+      am = 0;
     }
-    a.rows_t[(size_t)i * (G + 1) + k] = RowStat{0.0, -INFINITY, ri};
+    a.rows_t[(size_t)i * (G + 1) + k] = RowStat{0.0, -INFINITY, am};
     if (k < L) {
-      const int x = a.tokens[(size_t)i * G + k];
-      const int m = (x == ri);
+      const int m = (a.items_x[g] == am);
       a.acc[(size_t)i * G + k] = AccRec{m ? 1.0 : 0.0, m, 1};
     }
     return;
   }
-  const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + k) * V * ES;
-  const char* drow = two ? reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + k) * V * ES : nullptr;
   const double c64 = kLog2e / (double)T;
   const double l2t = combine_sum(pt, nseg);
-  const double l2d = two ? combine_sum(pd, nseg) : 0.0;
-  accept_item<BF16>(a, i, k, two, c64, l2t, -INFINITY, l2d, -INFINITY, trow, drow);
+  a.rows_t[(size_t)i * (G + 1) + k] = RowStat{l2t, -INFINITY, 0};
+  bool bad = !(l2t == l2t);
+  if (k < L) {
+    const double l2d = combine_sum(pd, nseg);
+    a.rows_d[(size_t)i * G + k] = RowStat{l2d, -INFINITY, 0};
+    bad |= !(l2d == l2d);
+    const int x = a.items_x[g];
+    if (!bad && x >= 0 && x < V) {
+      const double r = acceptance_ratio(pt[0].zx, pd[0].zx, c64, l2t, -INFINITY, l2d, -INFINITY);
+      double ua, ue;
+      verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
+      a.acc[(size_t)i * G + k] = AccRec{r, ua < r ? 1 : 0, 1};
+    }
+  }
+  if (bad) atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
 }
 
 __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, const int32_t* pos, double* ua,
@@ -713,7 +694,7 @@ __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, c
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t rows_t, rows_d, acc, items, nitems, req_status, ereq, ranges, amb, part_t, part_d, total;
+  size_t rows_t, rows_d, acc, items, items_x, nitems, req_status, ereq, ranges, amb, part_t, part_d, total;
 };
 
 // Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
@@ -729,6 +710,7 @@ static WsLayout ws_layout(int B, int G, int V, int nseg) {
   l.rows_d = o; o = align256(o + sizeof(RowStat) * (size_t)B * G);
   l.acc = o; o = align256(o + sizeof(AccRec) * (size_t)B * G);
   l.items = o; o = align256(o + sizeof(int32_t) * (size_t)B * (G + 1));
+  l.items_x = o; o = align256(o + sizeof(int32_t) * (size_t)B * (G + 1));
   l.nitems = o; o = align256(o + sizeof(int32_t));
   l.req_status = o; o = align256(o + sizeof(int32_t) * (size_t)B);
   l.ereq = o; o = align256(o + sizeof(EmitReq) * (size_t)B);
@@ -762,6 +744,7 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   a.rows_d = reinterpret_cast<RowStat*>(w + l.rows_d);
   a.acc = reinterpret_cast<AccRec*>(w + l.acc);
   a.items = reinterpret_cast<int32_t*>(w + l.items);
+  a.items_x = reinterpret_cast<int32_t*>(w + l.items_x);
   a.nitems = reinterpret_cast<int32_t*>(w + l.nitems);
   a.req_status = reinterpret_cast<int32_t*>(w + l.req_status);
   a.ereq = reinterpret_cast<EmitReq*>(w + l.ereq);
@@ -777,16 +760,17 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   else
     hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   if (ev1) hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
-  const unsigned cgrid = (unsigned)(((size_t)a.B * (a.G + 1) + 255) / 256);
-  if (dtype == SPEC_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(cgrid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(cgrid), dim3(256), 0, s, a);
   a.r0 = 0;
   a.r1 = a.B;
-  // one workgroup per request doing the whole emit when that covers the chip, else about 512
-  // emit-pass workgroups so that small batches still do, and a separate finishing kernel
-  a.emit_segs = a.B >= kFuseMinRequests ? 1 : std::max(2, std::min(kMaxEmitSegs, (512 + a.B - 1) / a.B));
+  // one workgroup per request doing acceptance and the whole emit when that covers the chip;
+  // else a combining kernel, about 512 emit-pass workgroups so that small batches still cover
+  // the chip, and a separate finishing kernel
+  const bool fused = !a.greedy_only && a.B >= kFuseMinRequests;
+  a.emit_segs = fused ? 1 : std::max(2, std::min(kMaxEmitSegs, (512 + a.B - 1) / a.B));
+  if (!fused) {
+    const unsigned cgrid = (unsigned)(((size_t)a.B * (a.G + 1) + 255) / 256);
+    hipLaunchKernelGGL(combine_kernel, dim3(cgrid), dim3(256), 0, s, a);
+  }
   launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -28,7 +28,7 @@ struct Partial {
   float m;      // sampling: the segment's integer reference
   int32_t idx;  // greedy: first index of the maximum
   int32_t bad;  // NaN or +inf seen
-  int32_t pad;
+  float zx;     // segment 0 of a row with a draft token x: the row's raw logit at x (else NaN)
 };
 
 // Emitted-token work: one range = kRangeElems consecutive tokens of the emit row.
@@ -67,11 +67,12 @@ struct VerifyArgs {
   RowStat* rows_d;     // [B, G]
   AccRec* acc;         // [B, G]
   int32_t* items;      // [B * (G+1)] work items, (request << 7) | position
+  int32_t* items_x;    // [B * (G+1)] the item's draft token x_k (-1 for a bonus row)
   int32_t* nitems;     // [1]
   int32_t* req_status; // [B] SPEC_REQ_* bits raised while streaming
   int nseg;            // segments per row in the streaming kernel
-  Partial* part_t;     // [B*(G+1), nseg] by work item
-  Partial* part_d;     // [B*(G+1), nseg]
+  Partial* part_t;     // [B, G+1, nseg] by (request, position, segment)
+  Partial* part_d;     // [B, G+1, nseg]
   EmitReq* ereq;       // [B]
   EmitRange* ranges;   // [B, ceil(V / kRangeElems)]
   int32_t* amb;        // [B, kAmbCap]
@@ -92,6 +93,51 @@ static constexpr double kLn2 = 0.69314718055994530942;
 static constexpr double kLog2e = 1.44269504088896340736;
 
 __host__ __device__ inline int num_ranges(int V) { return (V + kRangeElems - 1) / kRangeElems; }
+
+// lse2 of a row from its nseg segment partials (NaN when a segment saw NaN/+inf or the kept set
+// is empty): partial sums brought to the largest reference and added in fp64.
+__device__ inline double combine_sum(const Partial* p, int nseg) {
+  float Mr = -__builtin_inff();
+  int bad = 0;
+  for (int s = 0; s < nseg; ++s) {
+    bad |= p[s].bad;
+    if (p[s].v > 0.0) Mr = fmaxf(Mr, p[s].m);
+  }
+  double Sr = 0.0;
+  for (int s = 0; s < nseg; ++s)
+    if (p[s].v > 0.0) Sr += ldexp(p[s].v, (int)fmaxf(p[s].m - Mr, -2000.f));
+  return (bad || !(Sr > 0.0)) ? __builtin_nan("") : (double)Mr + log2(Sr);
+}
+
+// First-occurrence argmax of a row from its segment partials (greedy rows); -1 when a segment
+// saw NaN/+inf or no logit above -inf.
+__device__ inline int combine_argmax(const Partial* p, int nseg) {
+  float rb = -__builtin_inff();
+  int ri = 0x7fffffff, bad = 0;
+  for (int s = 0; s < nseg; ++s) {
+    bad |= p[s].bad;
+    const float v = (float)p[s].v;
+    if (v > rb) {
+      rb = v;
+      ri = p[s].idx;
+    } else if (v == rb) {
+      ri = min(ri, p[s].idx);
+    }
+  }
+  return (bad || !(rb > -__builtin_inff())) ? -1 : ri;
+}
+
+// Acceptance ratio r = min(1, p_t(x) / p_d(x)) from the raw logits at x, c = log2(e)/T, the rows'
+// lse2 and kept-set thresholds: log p(x) = ln2 (z_x c - lse2), -inf outside the kept set;
+// r = 0 when p_t(x) = 0, r = 1 when p_d(x) = 0 < p_t(x).
+__device__ inline double acceptance_ratio(float zt, float zd, double c64, double l2t, float tht, double l2d,
+                                          float thd) {
+  const double lpt = (zt >= tht) ? kLn2 * ((double)zt * c64 - l2t) : -__builtin_inf();
+  const double lpd = (zd >= thd) ? kLn2 * ((double)zd * c64 - l2d) : -__builtin_inf();
+  if (lpt == -__builtin_inf()) return 0.0;
+  if (lpd == -__builtin_inf()) return 1.0;
+  return fmin(1.0, exp(lpt - lpd));
+}
 
 // Status and first rejection of request i.  Called by a whole wave (lane k looks at draft
 // position k; gamma <= 64); every lane gets the result.
