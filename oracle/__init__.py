@@ -15,6 +15,9 @@ from the DSpark pages:
   * `schedule`      -- survival products and the budgeted length selector
                        (DSpark paper, §3.2.2; Algorithm 1 as printed in the
                        Chinese translation of the paper);
+  * `overlap_mass`  -- the per-position overlap sum_v min(p_t, p_d) of the
+                       target and draft distributions (DSpark paper, §3.2.1,
+                       Eq. 8);
   * `philox`        -- the counter-based generator the draws come from
                        (Philox4x64-10, Salmon et al., SC'11).
 
@@ -37,6 +40,7 @@ from .verification import (  # noqa: F401
     verify,
     verify_greedy,
 )
+from .overlap import overlap_mass  # noqa: F401
 from .scheduling import (  # noqa: F401
     survival,
     schedule,

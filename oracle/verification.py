@@ -130,8 +130,9 @@ def inverse_cdf(w, u):
 
 
 def _bad_rows(z):
-    """True for rows (last axis) holding a NaN or a +inf."""
-    return np.isnan(z).any(axis=-1) | np.isposinf(z).any(axis=-1)
+    """True for rows (last axis) holding a NaN or a +inf, or no finite logit at all (every kept
+    set contains the row's maximum, so such a row has no finite logit in its kept set either)."""
+    return np.isnan(z).any(axis=-1) | np.isposinf(z).any(axis=-1) | ~np.isfinite(z).any(axis=-1)
 
 
 def _verify_chunk(i0, tgt, drf, tok, L, T, K, S):

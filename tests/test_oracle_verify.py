@@ -263,12 +263,14 @@ def test_status_words():
     L[4] = G + 1                        # bad length
     d[5, 2, 0] = np.inf                 # +inf in a needed draft row
     T[6] = np.nan
+    t[7, 2, :] = -np.inf                # a needed row with no finite logit (reading R22)
     out = oracle.verify(t, d, toks, lengths=L, temperature=T)
     st = out["status"]
     assert st[0] == ov.STATUS_BAD_TOKEN
     assert st[1] == ov.STATUS_BAD_TEMPERATURE
     assert st[2] == ov.STATUS_NONFINITE
-    assert st[3] == 0 and st[7] == 0
+    assert st[3] == 0
+    assert st[7] == ov.STATUS_NONFINITE
     assert st[4] == ov.STATUS_BAD_LENGTH
     assert st[5] == ov.STATUS_NONFINITE
     assert st[6] & ov.STATUS_BAD_TEMPERATURE
