@@ -54,6 +54,8 @@ EXPORTS = {
     "spec_schedule_lengths": (_I, [_I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "spec_philox_uniforms": (_I, [_I, _P, _P, _P, _P, _P, _P]),
     "spec_read_ceiling": (_I, [_P, _Z, _I, _P, _P]),
+    "spec_overlap_workspace_size": (_Z, [_I, _I, _I]),
+    "spec_overlap_mass": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
 }
 
 _lib_handle = None
@@ -229,6 +231,34 @@ def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
                                      _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("status")),
                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_schedule_lengths", code)
+    return out
+
+
+def overlap_mass(target: torch.Tensor, draft: torch.Tensor, lengths: Optional[torch.Tensor] = None,
+                 temperature: Optional[torch.Tensor] = None, top_k: Optional[torch.Tensor] = None,
+                 out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """spec_overlap_mass on torch tensors.  Returns dict(overlap [B, gamma] float64, status [B])."""
+    lib = load_library()
+    B, G1, V = target.shape
+    G = G1 - 1
+    _dev(target, "target", None, 3)
+    _dev(draft, "draft", target.dtype, 3)
+    _dev(lengths, "lengths", torch.int32, 1)
+    _dev(temperature, "temperature", torch.float32, 1)
+    _dev(top_k, "top_k", torch.int32, 1)
+    if tuple(draft.shape) != (B, G, V):
+        raise ValueError("draft must be [B, gamma, V] with target [B, gamma+1, V]")
+    dev = target.device
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+    if out is None:
+        out = dict(overlap=torch.empty((B, G), dtype=torch.float64, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = _workspace(lib.spec_overlap_workspace_size(B, G, V), dev, workspace)
+    code = lib.spec_overlap_mass(B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(lengths),
+                                 _ptr(temperature), _ptr(top_k), _ptr(out["overlap"]), _ptr(out.get("status")),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("spec_overlap_mass", code)
     return out
 
 

@@ -33,6 +33,14 @@ namespace spec {
 // worklist
 // ---------------------------------------------------------------------------
 
+// Last position k of request i that gets a work item: L_i (verification: the rows k <= L_i), or
+// L_i - 1 when only the draft positions' statistics are wanted; -1 for none or a bad length.
+__device__ __forceinline__ int last_item(const VerifyArgs& a, int i) {
+  const int L = a.lengths ? a.lengths[i] : a.G;
+  if (L < 0 || L > a.G) return -1;
+  return a.overlap_only ? L - 1 : L;
+}
+
 __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a) {
   __shared__ int hist[SPEC_MAX_GAMMA + 2];
   __shared__ int off[SPEC_MAX_GAMMA + 2];
@@ -46,8 +54,8 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
   for (int i = tid; i < B; i += blockDim.x) {
     a.req_status[i] = 0;
     a.ereq[i].amb_n = 0;
-    const int L = a.lengths ? a.lengths[i] : G;
-    if (L >= 0 && L <= G) atomicAdd(&hist[L], 1);
+    const int L = last_item(a, i);
+    if (L >= 0) atomicAdd(&hist[L], 1);
   }
   __syncthreads();
   if (tid == 0) {
@@ -66,10 +74,7 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
   for (int base = 0; base < B; base += blockDim.x) {
     const int i = base + tid;
     int L = -1;
-    if (i < B) {
-      L = a.lengths ? a.lengths[i] : G;
-      if (L < 0 || L > G) L = -1;
-    }
+    if (i < B) L = last_item(a, i);
     for (int k = 0; k <= G; ++k) {
       const unsigned long long m = __ballot(L >= k);
       if (lane == 0) cnt[wave][k] = __popcll(m);
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
       if (L >= k) {
         const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
         a.items[idx] = (i << 7) | k;
-        a.items_x[idx] = (k < L) ? a.tokens[(size_t)i * G + k] : -1;
+        a.items_x[idx] = (a.tokens && !a.overlap_only && k < L) ? a.tokens[(size_t)i * G + k] : -1;
       }
     }
     __syncthreads();
@@ -498,7 +503,7 @@ __device__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double 
   if (two) {
     a.rows_d[(size_t)i * G + k] = RowStat{l2d, thd, 0};
     bad |= !(l2d == l2d);
-    const int x = a.tokens[(size_t)i * G + k];
+    const int x = (a.tokens && !a.overlap_only) ? a.tokens[(size_t)i * G + k] : -1;
     if (!bad && x >= 0 && x < V) {
       const double r = acceptance_ratio(load_elem<BF16>(trow, x), load_elem<BF16>(drow, x), c64, l2t, tht, l2d,
                                         thd);
@@ -560,6 +565,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   if (K >= V) K = 0;
   const int L = a.lengths ? a.lengths[i] : G;
   const bool greedy = (T == 0.f);
+  if (greedy && a.overlap_only) return;   // no draft distribution to overlap with
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool two = !greedy && k < L;
   const int nthr = two ? kStreamThreads / 2 : kStreamThreads;
@@ -645,6 +651,7 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a) {
   const int L = a.lengths ? a.lengths[i] : G;
   const Partial* pt = a.part_t + ((size_t)i * (G + 1) + k) * nseg;
   const Partial* pd = a.part_d + ((size_t)i * (G + 1) + k) * nseg;
+  if (T == 0.f && a.overlap_only) return;   // not streamed: no draft distribution to overlap with
   if (T == 0.f) {
     int am = combine_argmax(pt, nseg);
     if (am < 0) {
@@ -722,7 +729,7 @@ static WsLayout ws_layout(int B, int G, int V, int nseg) {
   return l;
 }
 
-static bool shape_ok(int B, int G, int V, int dtype) {
+bool shape_ok(int B, int G, int V, int dtype) {
   if (B < 1 || B > (1 << 24)) return false;
   if (G < 1 || G > SPEC_MAX_GAMMA) return false;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return false;
@@ -731,13 +738,13 @@ static bool shape_ok(int B, int G, int V, int dtype) {
   return true;
 }
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
-                             void* ev1) {
+int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size_t extra_bytes, char** extra) {
   a.nseg = stream_segments(a.V, dtype == SPEC_BF16 ? 2 : 4);
-  const WsLayout l = ws_layout(a.B, a.G, a.greedy_only ? 1 : a.V, a.nseg);  // greedy: no emit ranges
-  if (!ws || ws_bytes < l.total) return SPEC_ERR_WORKSPACE;
+  // greedy and overlap calls have no emit ranges
+  const WsLayout l = ws_layout(a.B, a.G, (a.greedy_only || a.overlap_only) ? 1 : a.V, a.nseg);
+  if (!ws || ws_bytes < l.total + extra_bytes) return SPEC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return SPEC_ERR_WORKSPACE;
   char* w = reinterpret_cast<char*>(ws);
   a.rows_t = reinterpret_cast<RowStat*>(w + l.rows_t);
@@ -752,6 +759,15 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   a.amb = reinterpret_cast<int32_t*>(w + l.amb);
   a.part_t = reinterpret_cast<Partial*>(w + l.part_t);
   a.part_d = reinterpret_cast<Partial*>(w + l.part_d);
+  if (extra) *extra = w + l.total;
+  return SPEC_OK;
+}
+
+size_t workspace_bytes(int B, int G, int V, bool emit) {
+  return ws_layout(B, G, emit ? V : 1, 16).total;   // the largest segment count, fp32 or bf16
+}
+
+void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1) {
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   if (ev0) hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);
   const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1) * a.nseg);
@@ -760,6 +776,18 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   else
     hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   if (ev1) hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
+}
+
+void launch_combine(const VerifyArgs& a, hipStream_t s) {
+  const unsigned cgrid = (unsigned)(((size_t)a.B * (a.G + 1) + 255) / 256);
+  hipLaunchKernelGGL(combine_kernel, dim3(cgrid), dim3(256), 0, s, a);
+}
+
+static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
+                             void* ev1) {
+  const int32_t rc = bind_workspace(a, dtype, ws, ws_bytes, 0, nullptr);
+  if (rc != SPEC_OK) return rc;
+  launch_statistics(a, dtype, s, ev0, ev1);
   a.r0 = 0;
   a.r1 = a.B;
   // one workgroup per request doing acceptance and the whole emit when that covers the chip;
@@ -767,10 +795,7 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   // the chip, and a separate finishing kernel
   const bool fused = !a.greedy_only && a.B >= kFuseMinRequests;
   a.emit_segs = fused ? 1 : std::max(2, std::min(kMaxEmitSegs, (512 + a.B - 1) / a.B));
-  if (!fused) {
-    const unsigned cgrid = (unsigned)(((size_t)a.B * (a.G + 1) + 255) / 256);
-    hipLaunchKernelGGL(combine_kernel, dim3(cgrid), dim3(256), 0, s, a);
-  }
+  if (!fused) launch_combine(a, s);
   launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -781,12 +806,12 @@ using namespace spec;
 
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_V) return 0;
-  return ws_layout(B, gamma, V, 16).total;   // sized for the largest segment count and fp32 or bf16
+  return workspace_bytes(B, gamma, V, true);
 }
 
 extern "C" size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
-  return ws_layout(B, gamma, 1, 16).total;
+  return workspace_bytes(B, gamma, 1, false);
 }
 
 extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,

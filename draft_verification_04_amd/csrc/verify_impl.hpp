@@ -51,6 +51,7 @@ struct EmitReq {
 struct VerifyArgs {
   int B, G, V;
   int greedy_only;
+  int overlap_only;    // statistics of the draft positions' row pairs only (no bonus rows, no test)
   const void* target;
   const void* draft;
   const int32_t* tokens;
@@ -171,5 +172,17 @@ __device__ inline void request_decision(const VerifyArgs& a, int i, int* st_out,
 
 // Launch the emitted-token kernels (defined in emit.hip).
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s);
+
+// Host steps shared by the entry points (defined in verify.hip).
+bool shape_ok(int B, int G, int V, int dtype);
+bool aligned16(const void* p);
+// Point the workspace arrays of `a` into ws (after `extra_bytes` more for the caller at *extra,
+// 256-byte aligned); SPEC_ERR_WORKSPACE when it is missing, short or misaligned.
+int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size_t extra_bytes, char** extra);
+size_t workspace_bytes(int B, int G, int V, bool emit);
+// Work list, then the streaming statistics (events, when given, bracket the streaming kernel).
+void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1);
+// Segment partials -> row records and (with draft tokens) the acceptance test.
+void launch_combine(const VerifyArgs& a, hipStream_t s);
 
 }  // namespace spec

@@ -222,6 +222,37 @@ int32_t spec_philox_uniforms(int32_t n, const uint64_t* seed, const int32_t* req
                              void* stream);
 
 /*
+ * spec_overlap_mass -- per draft position, the overlap of the target and draft
+ * distributions, c*_{i,k} = sum_v min(p_t,i,k(v), p_d,i,k(v)) (DSpark paper,
+ * §3.2.1, Eq. 8: the probability that position k is accepted once it is
+ * reached; the confidence head's label).  p = softmax(z / T_i) over the kept
+ * set, exactly as in spec_verify.
+ *
+ * Arguments as for spec_verify (target [B, gamma+1, V] with row gamma unused,
+ * draft [B, gamma, V], lengths or NULL, temperature, top_k or NULL); no draft
+ * tokens and no seeds.
+ * Outputs
+ *   overlap_out [B, gamma] float64 device: c*_{i,k} for k < L_i; NaN for
+ *               k >= L_i, for greedy requests (T_i = 0) and for requests with
+ *               bad data.  Computed with fp32 probabilities summed in fp64:
+ *               relative error ~1e-6.
+ *   status      [B] int32 device or NULL: the spec_verify status bits (no token
+ *               check).
+ *   workspace   at least spec_overlap_workspace_size(B, gamma, V) bytes,
+ *               256-byte aligned, owned by the caller, busy until the call's
+ *               kernels finish on `stream`.
+ * Cost: every row pair (target k, draft k), k < L_i, is read twice (row
+ * statistics, then the overlap); the bonus rows are not read.
+ * Errors as for spec_verify.
+ */
+size_t spec_overlap_workspace_size(int32_t B, int32_t gamma, int32_t V);
+
+int32_t spec_overlap_mass(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,
+                          const void* draft_logits, const int32_t* lengths, const float* temperature,
+                          const int32_t* top_k, double* overlap_out, int32_t* status, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * spec_read_ceiling -- measurement aid, not part of verification: reads
  * floor(bytes / 16) 16-byte vectors starting at `data` once (nontemporal,
  * grid-stride over `grid` workgroups of 512 threads) so that a caller can time

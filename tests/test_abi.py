@@ -68,10 +68,11 @@ def test_workspace_sizes(lib):
 
 
 def _fake(n=64):
-    # 16-byte aligned host buffers standing in for device pointers: validation
-    # must reject the call before any of them is dereferenced.
-    buf = (ctypes.c_uint8 * (n + 16))()
-    addr = (ctypes.addressof(buf) + 15) & ~15
+    # Host buffers standing in for device pointers: validation must reject the call before any
+    # of them is dereferenced.  The address is 16-byte aligned (as logits must be) but never
+    # 256-byte aligned, so used as a workspace it is always refused and nothing is launched.
+    buf = (ctypes.c_uint8 * (n + 512))()
+    addr = ((ctypes.addressof(buf) + 255) & ~255) + 16
     return buf, ctypes.c_void_p(addr)
 
 
@@ -136,3 +137,21 @@ def test_read_ceiling_rejects_bad_arguments(lib):
     assert lib.spec_read_ceiling(p, 8, 64, p, None) == 1
     assert lib.spec_read_ceiling(p, 1024, 0, p, None) == 1
     assert lib.spec_read_ceiling(p, 1024, 64, None, None) == 1
+
+
+def test_overlap_rejects_bad_arguments(lib):
+    keep, p = _fake()
+    ws = lib.spec_overlap_workspace_size(2, 4, 10)
+    assert ws > 0 and ws % 256 == 0 and lib.spec_overlap_workspace_size(0, 4, 10) == 0
+
+    def call(B=2, G=4, V=10, dt=1, t=p, d=p, T=p, o=p, w=p, wsb=ws):
+        return lib.spec_overlap_mass(B, G, V, dt, t, d, None, T, None, o, None, w, wsb, None)
+    assert call(B=0) == 1
+    assert call(G=65) == 1
+    assert call(dt=7) == 1
+    assert call(t=None) == 1
+    assert call(T=None) == 1
+    assert call(o=None) == 1
+    assert call(d=ctypes.c_void_p(p.value + 2)) == 1
+    assert call(w=None) == 2
+    assert call(wsb=ws - 1) == 2
