@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-overlap", action="store_true", help="skip the overlap-mass measurement")
     p.add_argument("--pool", type=int, default=8, help="worker processes for the pooled CPU-oracle timing")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
@@ -123,6 +124,7 @@ def main():
     value = positions / (ms_step * 1e-3)
 
     ceiling = read_ceiling(sv, torch, copies, alg_bytes, stream)
+    overlap = None if args.no_overlap else overlap_leg(sv, torch, w, copies, sch_out["lengths"], stream)
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -172,6 +174,7 @@ def main():
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": achieved / ceiling["gbps"]},
         "cpu_baseline": cpu,
+        "overlap_mass": overlap,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory},
         "ms_breakdown": {"stream_kernel": ms_stream, "rest_of_step": ms_step - ms_stream},
@@ -209,6 +212,36 @@ def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
         if best is None or gbps > best["gbps"]:
             best = {"gbps": gbps, "ms": ms, "grid": grid, "bytes": nbytes, "kernel": "spec_read_ceiling"}
     return best
+
+
+def overlap_leg(sv, torch, w, copies, lengths, stream, reps=20):
+    """spec_overlap_mass (per-position sum_v min(p_t, p_d)) on the same workload and lengths,
+    timed with HIP events; not part of the step.  Each draft position's row pair is read twice
+    (statistics, then the overlap)."""
+    from draft_verification_04_amd.hipevents import HipEvent
+    B, G = w.B, w.gamma
+    out = dict(overlap=torch.empty((B, G), dtype=torch.float64, device=w.target.device),
+               status=torch.empty(B, dtype=torch.int32, device=w.target.device))
+    ws = torch.empty(sv.load_library().spec_overlap_workspace_size(B, G, w.V), dtype=torch.uint8,
+                     device=w.target.device)
+    call = lambda r: sv.overlap_mass(copies[r % len(copies)][0], copies[r % len(copies)][1], lengths,
+                                     w.temperature, w.top_k, out=out, workspace=ws, stream=stream)
+    for r in range(2):
+        call(r)
+    e0, e1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for r in range(reps):
+        call(r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    pos = int(lengths.sum().item())
+    row_bytes = w.V * w.elem_bytes
+    once = 2 * pos * row_bytes
+    return {"ms_per_call": ms, "positions": pos, "positions_per_s": pos / (ms * 1e-3),
+            "rows_per_pass": 2 * pos, "bytes_read_per_call": 2 * once,
+            "gbps_read": 2 * once / (ms * 1e-3) / 1e9, "algorithmic_bytes_once": once}
 
 
 _POOL = {}
