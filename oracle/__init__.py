@@ -15,6 +15,8 @@ from the DSpark pages:
   * `schedule`      -- survival products and the budgeted length selector
                        (DSpark paper, §3.2.2; Algorithm 1 as printed in the
                        Chinese translation of the paper);
+  * `capacity`, `schedule_topk` -- the asynchronous scheduler of §5.2 (a
+                       capacity from an earlier step, top-K admission now);
   * `overlap_mass`  -- the per-position overlap sum_v min(p_t, p_d) of the
                        target and draft distributions (DSpark paper, §3.2.1,
                        Eq. 8);
@@ -42,8 +44,10 @@ from .verification import (  # noqa: F401
 )
 from .overlap import overlap_mass  # noqa: F401
 from .scheduling import (  # noqa: F401
+    capacity,
     survival,
     schedule,
     schedule_bruteforce,
+    schedule_topk,
     theta_path,
 )

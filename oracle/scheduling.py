@@ -16,6 +16,9 @@ Algorithm 1 as printed in the paper's Chinese translation:
     strictly; stop at the first candidate whose Theta is not above the best;
   * global mode (the search of §5.2, no break): the smallest m maximising
     Theta over the admissible range;
+  * asynchronous mode (§5.2): the capacity K is the global search's admission
+    count on confidences from two steps earlier; the current candidates are
+    admitted in sorted order up to K (top-K, rank-preserving);
   * l_r = number of admitted candidates of request r.
 
 Exact-arithmetic readings (so a parallel device scan can agree bit for bit):
@@ -110,6 +113,25 @@ def schedule(conf, sps, budget, mode=MODE_EARLY_STOP):
     for r, _ in pool[:m_star]:
         lengths[r] += 1
     return lengths, best
+
+
+def capacity(conf_hist, sps, budget):
+    """Capacity K of the asynchronous scheduler (DSpark paper, §5.2): the number of candidates the
+    global search (no early-stop break) admits on the confidences predicted two steps earlier."""
+    lengths, _ = schedule(conf_hist, sps, budget, MODE_GLOBAL)
+    return int(lengths.sum())
+
+
+def schedule_topk(conf, K):
+    """Lengths of the asynchronous scheduler (DSpark paper, §5.2): the current candidates, sorted by
+    their up-to-date survival (ties: request, then position), admitted in that order up to K (the
+    capacity fixed earlier) -- a rank-preserving top-K selection.  Returns lengths int64 [R]."""
+    a = survival(conf)
+    pool = candidates(a)
+    lengths = np.zeros(a.shape[0], dtype=np.int64)
+    for r, _ in pool[:max(0, int(K))]:
+        lengths[r] += 1
+    return lengths
 
 
 def schedule_bruteforce(conf, sps, budget):

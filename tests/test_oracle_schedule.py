@@ -210,3 +210,67 @@ def test_fixed_point_is_exact_and_fits_int64():
     assert fixed_point(tiny) == int(Fraction(float(tiny)) * ONE)   # floor below 2^-24
     max_candidates, max_requests = 16384, 16384
     assert (max_requests + max_candidates) * ONE < 2 ** 63
+
+
+def test_topk_at_the_global_capacity_is_the_global_schedule():
+    """With the current confidences equal to the earlier ones, the asynchronous scheduler admits
+    exactly what the global search admits (§5.2 keeps the sort and only moves the capacity)."""
+    rng = np.random.default_rng(71)
+    for trial in range(30):
+        B, G = int(rng.integers(1, 40)), int(rng.integers(1, 9))
+        conf = rng.uniform(0.0, 1.0, (B, G)).astype(np.float32)
+        conf[rng.random((B, G)) < 0.1] = np.float32(0.75)
+        b = np.arange(B * (G + 1) + 1, dtype=np.float64)
+        sps = np.zeros_like(b)
+        sps[1:] = rng.uniform(0.5, 2.0) * (1 - np.exp(-b[1:] / rng.uniform(1, 10 * B))) / b[1:]
+        budget = int(rng.integers(B, B * (G + 1) + 1))
+        K = oracle.capacity(conf, sps, budget)
+        lg, _ = oracle.schedule(conf, sps, budget, MODE_GLOBAL)
+        assert int(lg.sum()) == K
+        assert (oracle.schedule_topk(conf, K) == lg).all()
+
+
+def test_topk_admits_the_most_likely_prefixes():
+    """Brute force over prefix-closed admissions of size K: none has a larger total survival than
+    the top-K selection (the rank-preserving property of §5.2; fixed-batch optimality of §3.2.2)."""
+    rng = np.random.default_rng(72)
+    for trial in range(40):
+        B, G = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        conf = rng.uniform(0.05, 1.0, (B, G)).astype(np.float32)
+        a = survival(conf).astype(np.float64)
+        K = int(rng.integers(0, B * G + 2))
+        L = oracle.schedule_topk(conf, K)
+        assert int(L.sum()) == min(K, B * G)
+        got = sum(a[r, :L[r]].sum() for r in range(B))
+        best = -1.0
+        for lens in itertools.product(range(G + 1), repeat=B):
+            if sum(lens) == min(K, B * G):
+                best = max(best, sum(a[r, :lens[r]].sum() for r in range(B)))
+        assert got >= best - 1e-12
+
+
+def test_asynchronous_scheduler_keeps_the_target_distribution(golden_dir):
+    """The appendix example once more: with the capacity taken from confidences that precede the
+    first draft token (two steps earlier) and top-K admission of the current candidates, the first
+    output token follows the target (0.7, 0.3) although c_2 depends on x_1 (§5.2)."""
+    g = _golden(golden_dir)
+    sps = _sps_from(g)
+    n = 400_000
+    rng = np.random.default_rng(73)
+    pt = np.array([g["p_target"], [0.5, 0.5], [0.5, 0.5]])
+    pd = np.array([g["p_draft"], [0.5, 0.5]])
+    target = np.broadcast_to(np.log(pt), (n, 3, 2))
+    draft = np.broadcast_to(np.log(pd), (n, 2, 2))
+    toks = np.stack([rng.choice(2, size=n, p=pd[k]) for k in range(2)], axis=1)
+    conf_A = np.array([[g["a1"], g["case_high"]["c2"]]], dtype=np.float32)
+    conf_B = np.array([[g["a1"], g["case_low"]["c2"]]], dtype=np.float32)
+    # the earlier step saw either realisation with the draft's probabilities; its capacity
+    # cannot know which one the current step drew
+    hist = np.where(rng.random(n) < 0.5, 0, 1)
+    K = np.array([oracle.capacity(conf_A, sps, 3), oracle.capacity(conf_B, sps, 3)])[hist]
+    LA = [int(oracle.schedule_topk(conf_A, k)[0]) for k in (0, 1, 2)]
+    LB = [int(oracle.schedule_topk(conf_B, k)[0]) for k in (0, 1, 2)]
+    L = np.where(toks[:, 0] == 0, np.take(LA, K), np.take(LB, K))
+    out = oracle.verify(target, draft, toks, lengths=L)
+    obs = np.bincount(out["out_tokens"][:, 0], minlength=2)
+    assert stats.chisquare(obs, np.array(g["lossless_output"]) * n).pvalue > 1e-4, obs / n
