@@ -125,6 +125,7 @@ def main():
 
     ceiling = read_ceiling(sv, torch, copies, alg_bytes, stream)
     overlap = None if args.no_overlap else overlap_leg(sv, torch, w, copies, sch_out["lengths"], stream)
+    async_sched = async_scheduler_leg(sv, torch, w, sps, stream) if w.conf is not None else None
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -175,6 +176,7 @@ def main():
                      "frac_of_read_ceiling": achieved / ceiling["gbps"]},
         "cpu_baseline": cpu,
         "overlap_mass": overlap,
+        "async_scheduler": async_sched,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory},
         "ms_breakdown": {"stream_kernel": ms_stream, "rest_of_step": ms_step - ms_stream},
@@ -242,6 +244,36 @@ def overlap_leg(sv, torch, w, copies, lengths, stream, reps=20):
     return {"ms_per_call": ms, "positions": pos, "positions_per_s": pos / (ms * 1e-3),
             "rows_per_pass": 2 * pos, "bytes_read_per_call": 2 * once,
             "gbps_read": 2 * once / (ms * 1e-3) / 1e9, "algorithmic_bytes_once": once}
+
+
+def async_scheduler_leg(sv, torch, w, sps, stream, reps=20):
+    """The asynchronous scheduler of the same workload: spec_schedule_capacity (the global search,
+    off the critical path in a pipeline) and spec_schedule_topk (the per-step top-K admission),
+    each timed with HIP events; the synchronous early-stop scheduler of the step for comparison."""
+    from draft_verification_04_amd.hipevents import HipEvent
+    ws = torch.empty(max(256, sv.load_library().spec_schedule_workspace_size(w.B, w.gamma)), dtype=torch.uint8,
+                     device=w.conf.device)
+    cap = sv.schedule_capacity(w.conf, sps, w.budget, stream=stream, workspace=ws)
+    top = sv.schedule_topk(w.conf, cap["capacity"], stream=stream, workspace=ws)
+    sync = sv.schedule_lengths(w.conf, sps, w.budget, stream=stream, workspace=ws)
+
+    def timed(fn):
+        fn()
+        e0, e1 = HipEvent(), HipEvent()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / reps
+
+    t_cap = timed(lambda: sv.schedule_capacity(w.conf, sps, w.budget, out=cap, stream=stream, workspace=ws))
+    t_top = timed(lambda: sv.schedule_topk(w.conf, cap["capacity"], out=top, stream=stream, workspace=ws))
+    t_es = timed(lambda: sv.schedule_lengths(w.conf, sps, w.budget, out=sync, stream=stream, workspace=ws))
+    return {"capacity_ms": t_cap, "topk_ms": t_top, "early_stop_ms": t_es,
+            "capacity": int(cap["capacity"].item()), "topk_positions": int(top["lengths"].sum().item()),
+            "early_stop_positions": int(sync["lengths"].sum().item())}
 
 
 _POOL = {}

@@ -55,6 +55,8 @@ EXPORTS = {
     "spec_philox_uniforms": (_I, [_I, _P, _P, _P, _P, _P, _P]),
     "spec_read_ceiling": (_I, [_P, _Z, _I, _P, _P]),
     "spec_overlap_workspace_size": (_Z, [_I, _I, _I]),
+    "spec_schedule_capacity": (_I, [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "spec_schedule_topk": (_I, [_I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_overlap_mass": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
 }
 
@@ -269,6 +271,44 @@ def read_ceiling(data: torch.Tensor, nbytes: int, grid: int, sink: torch.Tensor,
         raise ValueError("data must be a device tensor of at least nbytes")
     _check("spec_read_ceiling", lib.spec_read_ceiling(_ptr(data), int(nbytes), int(grid), _ptr(sink),
                                                       _stream(stream)))
+
+
+def schedule_capacity(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int, out: Optional[dict] = None,
+                      stream=None, workspace: Optional[torch.Tensor] = None) -> dict:
+    """spec_schedule_capacity: dict(capacity [1] int32, theta [1] float64, status [B])."""
+    lib = load_library()
+    _dev(conf, "conf", torch.float32, 2)
+    _dev(sps, "sps", torch.float64, 1)
+    B, G = conf.shape
+    dev = conf.device
+    if out is None:
+        out = dict(capacity=torch.empty(1, dtype=torch.int32, device=dev),
+                   theta=torch.empty(1, dtype=torch.float64, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace)
+    code = lib.spec_schedule_capacity(B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens),
+                                      _ptr(out["capacity"]), _ptr(out.get("theta")), _ptr(out.get("status")),
+                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("spec_schedule_capacity", code)
+    return out
+
+
+def schedule_topk(conf: torch.Tensor, capacity: torch.Tensor, out: Optional[dict] = None, stream=None,
+                  workspace: Optional[torch.Tensor] = None) -> dict:
+    """spec_schedule_topk: dict(lengths [B] int32, status [B]) admitting up to capacity[0] candidates."""
+    lib = load_library()
+    _dev(conf, "conf", torch.float32, 2)
+    _dev(capacity, "capacity", torch.int32, 1)
+    B, G = conf.shape
+    dev = conf.device
+    if out is None:
+        out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace)
+    code = lib.spec_schedule_topk(B, G, _ptr(conf), _ptr(capacity), _ptr(out["lengths"]), _ptr(out.get("status")),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("spec_schedule_topk", code)
+    return out
 
 
 def philox_uniforms(seed: torch.Tensor, request: torch.Tensor, position: torch.Tensor, stream=None):

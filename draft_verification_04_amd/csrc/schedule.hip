@@ -52,7 +52,11 @@ struct SchedArgs {
   unsigned* orig;     // [N] keys in index order
   unsigned* chunked;  // [N] keys, each chunk of 64 sorted
   unsigned* sorted;   // [N] keys, whole pool sorted
+  const int32_t* capacity_in;  // top-K mode: [1] device, the number of candidates to admit
+  int32_t* capacity_out;       // [1] device or NULL: the number admitted (m*)
 };
+
+constexpr int kSchedTopK = 2;   // internal mode: admit the first K sorted candidates
 
 __device__ __forceinline__ unsigned surv_key(float s) { return s > 0.f ? ~__float_as_uint(s) : kNoCandidate; }
 __device__ __forceinline__ float key_surv(unsigned k) { return __uint_as_float(~k); }
@@ -217,11 +221,12 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
   int m_cap = a.budget - B;
   m_cap = m_cap < 0 ? 0 : (m_cap > N ? N : m_cap);
   const int p0 = tid * K;
-  const double sps_B = a.sps[B];
-  const double sps_p0 = (p0 <= m_cap) ? a.sps[B + p0] : 0.0;
+  const bool topk = a.mode == kSchedTopK;   // no cost table: the capacity is given
+  const double sps_B = topk ? 0.0 : a.sps[B];
+  const double sps_p0 = (!topk && p0 <= m_cap) ? a.sps[B + p0] : 0.0;
   double sps_m[K];
 #pragma unroll
-  for (int e = 0; e < K; ++e) sps_m[e] = (p0 + e + 1 <= m_cap) ? a.sps[B + p0 + e + 1] : 0.0;
+  for (int e = 0; e < K; ++e) sps_m[e] = (!topk && p0 + e + 1 <= m_cap) ? a.sps[B + p0 + e + 1] : 0.0;
   if (tid == 0) sh.ncand = 0;
   for (int x = tid; x < N; x += kFinalThreads) {
     sh.sorted[x] = a.sorted[x];
@@ -240,12 +245,22 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
   if (lane == 0 && nvalid) atomicAdd(&sh.ncand, nvalid);
   __syncthreads();
   const int E = sh.ncand;
+  long long q[K];
+  long long tau_p0 = 0;
+  if (topk) {
+    if (tid == 0) {
+      const int cap = *a.capacity_in;
+      sh.mstar = cap < 0 ? 0 : (cap > E ? E : cap);
+      sh.first = sh.last = 0;
+    }
+#pragma unroll
+    for (int e = 0; e < K; ++e) q[e] = 0;
+  } else {
   int m_max = a.budget - B;
   if (m_max > E) m_max = E;
   if (m_max < 0) m_max = 0;
 
   // exclusive scan of q over sorted positions 0 .. m_max-1 (K per thread)
-  long long q[K];
   long long local = 0;
 #pragma unroll
   for (int e = 0; e < K; ++e) {
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
   long long total;
   const long long before = block_exclusive_sum(local, sh.wsum, &total);
   long long tau = (long long)B * kOne + before;  // tau at m = p0
-  const long long tau_p0 = tau;
+  tau_p0 = tau;
 
   // Theta along the path; admission m uses sorted position m-1
   const double th0 = theta_of((long long)B * kOne, sps_B);
@@ -320,14 +335,17 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
     sh.first = sh.last = 0;
     if (mstar == 0 && a.theta) a.theta[0] = th0;
   }
+  }  // search for m*
   __syncthreads();
   const int mstar = sh.mstar;
+  if (tid == 0 && a.capacity_out) a.capacity_out[0] = mstar;
+  if (!a.lengths) return;
   if (mstar == 0) {
     for (int r = tid; r < B; r += kFinalThreads) a.lengths[r] = 0;
     return;
   }
   // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
-  if (mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
+  if (!topk && mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
     long long t = tau_p0;
     double sp = 0.0;
 #pragma unroll
@@ -385,28 +403,17 @@ extern "C" size_t spec_schedule_workspace_size(int32_t B, int32_t gamma) {
   return 3 * align256(n * sizeof(unsigned));
 }
 
-extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const double* sps,
-                                         int32_t sps_len, int32_t budget_tokens, int32_t mode,
-                                         int32_t* lengths_out, double* theta_out, int32_t* status,
-                                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return SPEC_ERR_INVALID_ARG;
-  if ((long long)B * gamma > SPEC_MAX_SCHED_CANDIDATES) return SPEC_ERR_UNSUPPORTED;
-  if (mode != SPEC_SCHED_EARLY_STOP && mode != SPEC_SCHED_GLOBAL) return SPEC_ERR_INVALID_ARG;
-  if (!conf || !sps || !lengths_out) return SPEC_ERR_INVALID_ARG;
-  long long m_cap = (long long)budget_tokens - B;
-  if (m_cap < 0) m_cap = 0;
-  if (m_cap > (long long)B * gamma) m_cap = (long long)B * gamma;
-  if ((long long)sps_len <= (long long)B + m_cap) return SPEC_ERR_INVALID_ARG;
+static int32_t launch_schedule(SchedArgs a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  const int B = a.B, gamma = a.G;
   if (!workspace || workspace_bytes < spec_schedule_workspace_size(B, gamma) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return SPEC_ERR_WORKSPACE;
   const int n = B * gamma;
   char* ws = static_cast<char*>(workspace);
   const size_t seg = align256((size_t)n * sizeof(unsigned));
-  SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, status,
-              reinterpret_cast<unsigned*>(ws), reinterpret_cast<unsigned*>(ws + seg),
-              reinterpret_cast<unsigned*>(ws + 2 * seg)};
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  a.orig = reinterpret_cast<unsigned*>(ws);
+  a.chunked = reinterpret_cast<unsigned*>(ws + seg);
+  a.sorted = reinterpret_cast<unsigned*>(ws + 2 * seg);
   hipLaunchKernelGGL(keys_kernel, dim3((n + kKeysThreads - 1) / kKeysThreads), dim3(kKeysThreads), 0, s, a);
   hipLaunchKernelGGL(rank_kernel, dim3((n + kChunk - 1) / kChunk), dim3(kChunk * kRankParts), 0, s, a);
   if (n <= 1 * kFinalThreads) hipLaunchKernelGGL(final_kernel<1>, dim3(1), dim3(kFinalThreads), 0, s, a);
@@ -415,4 +422,52 @@ extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* 
   else if (n <= 8 * kFinalThreads) hipLaunchKernelGGL(final_kernel<8>, dim3(1), dim3(kFinalThreads), 0, s, a);
   else hipLaunchKernelGGL(final_kernel<16>, dim3(1), dim3(kFinalThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+static int32_t check_search_args(int32_t B, int32_t gamma, const float* conf, const double* sps, int32_t sps_len,
+                                 int32_t budget_tokens) {
+  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return SPEC_ERR_INVALID_ARG;
+  if ((long long)B * gamma > SPEC_MAX_SCHED_CANDIDATES) return SPEC_ERR_UNSUPPORTED;
+  if (!conf || !sps) return SPEC_ERR_INVALID_ARG;
+  long long m_cap = (long long)budget_tokens - B;
+  if (m_cap < 0) m_cap = 0;
+  if (m_cap > (long long)B * gamma) m_cap = (long long)B * gamma;
+  if ((long long)sps_len <= (long long)B + m_cap) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const double* sps,
+                                         int32_t sps_len, int32_t budget_tokens, int32_t mode,
+                                         int32_t* lengths_out, double* theta_out, int32_t* status,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t rc = check_search_args(B, gamma, conf, sps, sps_len, budget_tokens);
+  if (rc != SPEC_OK) return rc;
+  if (mode != SPEC_SCHED_EARLY_STOP && mode != SPEC_SCHED_GLOBAL) return SPEC_ERR_INVALID_ARG;
+  if (!lengths_out) return SPEC_ERR_INVALID_ARG;
+  SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, status,
+              nullptr, nullptr, nullptr, nullptr, nullptr};
+  return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t spec_schedule_capacity(int32_t B, int32_t gamma, const float* conf, const double* sps,
+                                          int32_t sps_len, int32_t budget_tokens, int32_t* capacity_out,
+                                          double* theta_out, int32_t* status, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  const int32_t rc = check_search_args(B, gamma, conf, sps, sps_len, budget_tokens);
+  if (rc != SPEC_OK) return rc;
+  if (!capacity_out) return SPEC_ERR_INVALID_ARG;
+  SchedArgs a{B, gamma, budget_tokens, SPEC_SCHED_GLOBAL, conf, sps, nullptr, theta_out, status,
+              nullptr, nullptr, nullptr, nullptr, capacity_out};
+  return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t spec_schedule_topk(int32_t B, int32_t gamma, const float* conf, const int32_t* capacity,
+                                      int32_t* lengths_out, int32_t* status, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return SPEC_ERR_INVALID_ARG;
+  if ((long long)B * gamma > SPEC_MAX_SCHED_CANDIDATES) return SPEC_ERR_UNSUPPORTED;
+  if (!conf || !capacity || !lengths_out) return SPEC_ERR_INVALID_ARG;
+  SchedArgs a{B, gamma, 0, kSchedTopK, conf, nullptr, lengths_out, nullptr, status,
+              nullptr, nullptr, nullptr, capacity, nullptr};
+  return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }

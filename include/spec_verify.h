@@ -212,6 +212,37 @@ int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Asynchronous scheduling (DSpark paper, §5.2): the admission capacity of a
+ * step is fixed from confidences predicted two steps earlier (the global
+ * search, without the early-stop break), and the step then admits its current
+ * candidates, sorted by their up-to-date survival, up to that capacity -- a
+ * rank-preserving top-K selection.  The capacity never sees the current
+ * tokens, so admission stays non-anticipating.
+ *
+ * spec_schedule_capacity -- the global search of spec_schedule_lengths
+ *   (mode SPEC_SCHED_GLOBAL) on `conf` (the earlier step's confidences);
+ *   writes K = m*, the number of candidates it admits, to capacity_out [1]
+ *   int32 device, and Theta(m*) to theta_out [1] or NULL.  Arguments, status
+ *   and errors as for spec_schedule_lengths (no lengths are written).
+ *
+ * spec_schedule_topk -- lengths_out [B] int32 device: request i's share of
+ *   the first min(K, #candidates) candidates of `conf` in sorted order (the
+ *   order of spec_schedule_lengths), K = capacity [1] int32 device (written
+ *   by an earlier spec_schedule_capacity, or by the caller; negative = 0).
+ *   No cost table and no budget: the capacity carries both.  status [B] or
+ *   NULL as for spec_schedule_lengths.  Workspace:
+ *   spec_schedule_workspace_size(B, gamma) bytes for either call.
+ */
+int32_t spec_schedule_capacity(int32_t B, int32_t gamma, const float* conf, const double* sps,
+                               int32_t sps_len, int32_t budget_tokens, int32_t* capacity_out,
+                               double* theta_out, int32_t* status, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+int32_t spec_schedule_topk(int32_t B, int32_t gamma, const float* conf, const int32_t* capacity,
+                           int32_t* lengths_out, int32_t* status, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * spec_philox_uniforms -- the library's draws, exposed for checking:
  * for t < n, (u_accept[t], u_emit[t]) = the two uniforms used for request
  * request[t] at draft position position[t] under seed[t] (see spec_verify).

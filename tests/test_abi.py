@@ -155,3 +155,19 @@ def test_overlap_rejects_bad_arguments(lib):
     assert call(d=ctypes.c_void_p(p.value + 2)) == 1
     assert call(w=None) == 2
     assert call(wsb=ws - 1) == 2
+
+
+def test_async_scheduler_rejects_bad_arguments(lib):
+    keep, p = _fake()
+    assert lib.spec_schedule_capacity(0, 4, p, p, 100, 10, p, None, None, p, 4096, None) == 1
+    assert lib.spec_schedule_capacity(4, 4, None, p, 100, 10, p, None, None, p, 4096, None) == 1
+    assert lib.spec_schedule_capacity(4, 4, p, p, 100, 10, None, None, None, p, 4096, None) == 1
+    assert lib.spec_schedule_capacity(4, 4, p, p, 10, 10, p, None, None, p, 4096, None) == 1   # table short
+    assert lib.spec_schedule_capacity(2048, 16, p, p, 10 ** 6, 10, p, None, None, p, 4096, None) == 3
+    assert lib.spec_schedule_capacity(4, 4, p, p, 100, 10, p, None, None, p, 4096, None) == 2   # workspace
+    assert lib.spec_schedule_topk(0, 4, p, p, p, None, p, 4096, None) == 1
+    assert lib.spec_schedule_topk(4, 65, p, p, p, None, p, 4096, None) == 1
+    assert lib.spec_schedule_topk(4, 4, None, p, p, None, p, 4096, None) == 1
+    assert lib.spec_schedule_topk(4, 4, p, None, p, None, p, 4096, None) == 1
+    assert lib.spec_schedule_topk(4, 4, p, p, None, None, p, 4096, None) == 1
+    assert lib.spec_schedule_topk(4, 4, p, p, p, None, p, 4096, None) == 2                  # workspace

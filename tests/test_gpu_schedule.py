@@ -129,3 +129,47 @@ def test_ties_and_wide_shapes(sv, mode):
             assert bad.size == 0, (B, G, trial, budget, int(L.sum()), int(L_ref.sum()), th, th_ref,
                                    bad[:8].tolist(), L[bad[:8]].tolist(), L_ref[bad[:8]].tolist())
             assert th == th_ref, (B, G, trial, th, th_ref)
+
+
+
+def test_capacity_and_topk(sv):
+    """spec_schedule_capacity = the oracle's global admission count; spec_schedule_topk = the
+    oracle's top-K lengths, for capacities below, at and above the pool (bit for bit)."""
+    rng = np.random.default_rng(81)
+    for trial in range(12):
+        B = int(rng.integers(1, 1500))
+        G = int(rng.integers(1, 17))
+        if B * G > 16384:
+            G = 16384 // B
+        conf = make_confidences(B, G, int(rng.integers(1 << 30))).numpy()
+        conf[rng.random((B, G)) < 0.05] = np.float32(1.0)
+        conf[rng.random((B, G)) < 0.05] = np.float32(0.75)
+        sps = make_sps_table(B * (G + 1) + 1, int(rng.integers(1 << 30)))
+        budget = int(rng.integers(B, B * (G + 1) + 1))
+        c = sv.schedule_capacity(torch.from_numpy(conf).to(DEV), torch.from_numpy(sps).to(DEV), budget)
+        torch.cuda.synchronize()
+        K = int(to_np(c["capacity"])[0])
+        assert K == oracle.capacity(conf, sps, budget), (trial, B, G)
+        now = make_confidences(B, G, int(rng.integers(1 << 30))).numpy()
+        now[rng.random((B, G)) < 0.05] = np.float32(1.0)
+        for cap in (K, 0, int(rng.integers(0, B * G + 1)), B * G + 5, -3):
+            t = sv.schedule_topk(torch.from_numpy(now).to(DEV), torch.tensor([cap], dtype=torch.int32, device=DEV))
+            torch.cuda.synchronize()
+            L = to_np(t["lengths"])
+            assert (L == oracle.schedule_topk(now, cap)).all(), (trial, cap)
+            assert (to_np(t["status"]) == 0).all()
+
+
+def test_asynchronous_pipeline_on_device(sv):
+    """The capacity computed from one step's confidences feeds the next call without the host
+    reading it in between."""
+    w = make_workload("scheduled", "cpu", V=16)
+    conf = w.conf.to(DEV)
+    sps = torch.from_numpy(w.sps).to(DEV)
+    c = sv.schedule_capacity(conf, sps, w.budget)
+    now = make_confidences(w.B, w.gamma, 4242).to(DEV)
+    t = sv.schedule_topk(now, c["capacity"])
+    torch.cuda.synchronize()
+    K = oracle.capacity(w.conf.numpy(), w.sps, w.budget)
+    assert int(to_np(c["capacity"])[0]) == K
+    assert (to_np(t["lengths"]) == oracle.schedule_topk(now.cpu().numpy(), K)).all()
