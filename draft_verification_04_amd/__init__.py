@@ -48,6 +48,7 @@ EXPORTS = {
     "spec_verify": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_verify_profiled": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P,
                                   _P, _P]),
+    "spec_verify_flat": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_verify_greedy_workspace_size": (_Z, [_I, _I]),
     "spec_verify_greedy": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_schedule_workspace_size": (_Z, [_I, _I]),
@@ -187,6 +188,46 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
         _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
         _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream), ev0, ev1)
     _check("spec_verify", code)
+    return out
+
+
+def verify_flat(target_rows: torch.Tensor, draft_rows: torch.Tensor, draft_tokens: torch.Tensor,
+                lengths: torch.Tensor, temperature: Optional[torch.Tensor] = None,
+                top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
+                out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """spec_verify_flat on torch tensors: target_rows [sum(L+1), V], draft_rows [sum(L), V] hold only
+    the verified rows, request after request; draft_tokens [B, gamma]; lengths [B] int32."""
+    lib = load_library()
+    _dev(target_rows, "target_rows", (torch.float32, torch.bfloat16), 2)
+    _dev(draft_rows, "draft_rows", target_rows.dtype, 2)
+    _dev(draft_tokens, "draft_tokens", torch.int32, 2)
+    _dev(lengths, "lengths", torch.int32, 1)
+    B, G = draft_tokens.shape
+    V = target_rows.shape[1]
+    if draft_rows.shape[1] != V or lengths.numel() != B:
+        raise ValueError("draft_rows must be [sum(L), V] and lengths [B]")
+    dev = target_rows.device
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+    if seed is None:
+        seed = torch.zeros(B, dtype=torch.int64, device=dev)
+    _dev(temperature, "temperature", torch.float32, 1)
+    _dev(top_k, "top_k", torch.int32, 1)
+    _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
+    if out is None:
+        out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+                   accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = _workspace(int(lib.spec_verify_workspace_size(B, G, V)), dev, workspace)
+    # an empty draft_rows tensor (every length 0) still needs an aligned non-null pointer
+    drows = draft_rows if draft_rows.numel() else torch.empty((1, V), dtype=target_rows.dtype, device=dev)
+    code = lib.spec_verify_flat(
+        B, G, V, _logit_dtype(target_rows), _ptr(target_rows), _ptr(drows), _ptr(draft_tokens), _ptr(lengths),
+        _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream))
+    _check("spec_verify_flat", code)
     return out
 
 

@@ -102,7 +102,7 @@ __device__ __forceinline__ EmitRows emit_rows(const VerifyArgs& a, int i, int n)
   const int L = a.lengths ? a.lengths[i] : G;
   EmitRows e;
   const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
-  e.t = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + n) * V * ES;
+  e.t = target_row<ES>(a, i, n);
   e.R = rt.lse2 * kLn2;
   e.tht = rt.theta;
   e.invT = 1.0 / (double)a.temperature[i];
@@ -111,7 +111,7 @@ __device__ __forceinline__ EmitRows emit_rows(const VerifyArgs& a, int i, int n)
   e.cd = 1.0;
   if (n < L) {
     const RowStat rd = a.rows_d[(size_t)i * G + n];
-    e.d = reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + n) * V * ES;
+    e.d = draft_row<ES>(a, i, n);
     e.thd = rd.theta;
     e.cd = exp(e.R - rd.lse2 * kLn2);
   }

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kOverlapThreads) void overlap_pass_kernel(VerifyArg
   const float c_lo = (float)(c64 - (double)c_hi);
   const float lt_hi = (float)rt.lse2, lt_lo = (float)(rt.lse2 - (double)lt_hi);
   const float ld_hi = (float)rd.lse2, ld_lo = (float)(rd.lse2 - (double)ld_hi);
-  const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + k) * V * ES;
-  const char* drow = reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + k) * V * ES;
+  const char* trow = target_row<ES>(a, i, k);
+  const char* drow = draft_row<ES>(a, i, k);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   double acc = 0.0;
   const bool vec = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;

@@ -46,8 +46,41 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
   __shared__ int off[SPEC_MAX_GAMMA + 2];
   __shared__ int carry[SPEC_MAX_GAMMA + 1];
   __shared__ int cnt[kWorklistThreads / SPEC_WAVE][SPEC_MAX_GAMMA + 1];
+  __shared__ long long woff_t[kWorklistThreads / SPEC_WAVE], woff_d[kWorklistThreads / SPEC_WAVE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G, B = a.B;
+  if (a.flat) {
+    // first target / draft row of every request in the flattened layout (a bad length counts
+    // as no rows): exclusive prefix sums of L_i + 1 and L_i, block by block
+    long long carry_t = 0, carry_d = 0;
+    for (int b0 = 0; b0 < B; b0 += blockDim.x) {
+      const int i = b0 + tid;
+      const int L = (i < B) ? (a.lengths ? a.lengths[i] : G) : -1;
+      const long long nt = (L >= 0 && L <= G) ? L + 1 : 0, nd = (L >= 0 && L <= G) ? L : 0;
+      const long long it = wave_inclusive_sum_i64(nt, lane), id = wave_inclusive_sum_i64(nd, lane);
+      __syncthreads();
+      if (lane == 63) {
+        woff_t[wave] = it;
+        woff_d[wave] = id;
+      }
+      __syncthreads();
+      long long bt = carry_t, bd = carry_d, tt = 0, td = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        if (w < wave) {
+          bt += woff_t[w];
+          bd += woff_d[w];
+        }
+        tt += woff_t[w];
+        td += woff_d[w];
+      }
+      if (i < B) {
+        a.t_off[i] = bt + it - nt;
+        a.d_off[i] = bd + id - nd;
+      }
+      carry_t += tt;
+      carry_d += td;
+    }
+  }
   for (int t = tid; t < G + 2; t += blockDim.x) hist[t] = 0;
   for (int t = tid; t < G + 1; t += blockDim.x) carry[t] = 0;
   __syncthreads();
@@ -572,8 +605,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
   const int which = two ? (tid >= nthr) : 0;
   const int lt = tid - which * nthr;
   const int nwaves = nthr >> 6, first_wave = which * nwaves;
-  const char* trow = reinterpret_cast<const char*>(a.target) + ((size_t)i * (G + 1) + k) * V * ES;
-  const char* drow = two ? reinterpret_cast<const char*>(a.draft) + ((size_t)i * G + k) * V * ES : nullptr;
+  const char* trow = target_row<ES>(a, i, k);
+  const char* drow = two ? draft_row<ES>(a, i, k) : nullptr;
   const char* row = which ? drow : trow;
   const double c64 = greedy ? 0.0 : kLog2e / (double)T;
   const float c_hi = __double2float_rz(c64);
@@ -701,7 +734,8 @@ __global__ void philox_kernel(int n, const uint64_t* seed, const int32_t* req, c
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t rows_t, rows_d, acc, items, items_x, nitems, req_status, ereq, ranges, amb, part_t, part_d, total;
+  size_t rows_t, rows_d, acc, items, items_x, nitems, req_status, ereq, ranges, amb, part_t, part_d, t_off, d_off,
+      total;
 };
 
 // Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
@@ -725,6 +759,8 @@ static WsLayout ws_layout(int B, int G, int V, int nseg) {
   l.amb = o; o = align256(o + sizeof(int32_t) * (size_t)B * kAmbCap);
   l.part_t = o; o = align256(o + sizeof(Partial) * (size_t)B * (G + 1) * nseg);
   l.part_d = o; o = align256(o + sizeof(Partial) * (size_t)B * (G + 1) * nseg);
+  l.t_off = o; o = align256(o + sizeof(int64_t) * (size_t)B);
+  l.d_off = o; o = align256(o + sizeof(int64_t) * (size_t)B);
   l.total = o;
   return l;
 }
@@ -759,6 +795,8 @@ int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size
   a.amb = reinterpret_cast<int32_t*>(w + l.amb);
   a.part_t = reinterpret_cast<Partial*>(w + l.part_t);
   a.part_d = reinterpret_cast<Partial*>(w + l.part_d);
+  a.t_off = reinterpret_cast<int64_t*>(w + l.t_off);
+  a.d_off = reinterpret_cast<int64_t*>(w + l.d_off);
   if (extra) *extra = w + l.total;
   return SPEC_OK;
 }
@@ -842,6 +880,25 @@ extern "C" int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtyp
   return spec_verify_profiled(B, gamma, V, dtype, target_logits, draft_logits, draft_tokens, lengths, temperature,
                               top_k, seed, num_accepted, out_tokens, accept_prob, status, workspace,
                               workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_rows,
+                                    const void* draft_rows, const int32_t* draft_tokens, const int32_t* lengths,
+                                    const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                                    int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                                    int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
+  if (!target_rows || !draft_rows || !draft_tokens || !lengths || !temperature || !seed || !num_accepted ||
+      !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(target_rows) || !aligned16(draft_rows)) return SPEC_ERR_INVALID_ARG;
+  VerifyArgs a{};
+  a.B = B; a.G = gamma; a.V = V; a.greedy_only = 0; a.flat = 1;
+  a.target = target_rows; a.draft = draft_rows; a.tokens = draft_tokens; a.lengths = lengths;
+  a.temperature = temperature; a.top_k = top_k; a.seed = seed;
+  a.num_accepted = num_accepted; a.out_tokens = out_tokens; a.accept_prob = accept_prob; a.status = status;
+  return launch_verify(a, dtype, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), nullptr,
+                       nullptr);
 }
 
 extern "C" int32_t spec_verify_greedy(int32_t B, int32_t gamma, int32_t V, int32_t dtype,

@@ -52,6 +52,7 @@ struct VerifyArgs {
   int B, G, V;
   int greedy_only;
   int overlap_only;    // statistics of the draft positions' row pairs only (no bonus rows, no test)
+  int flat;            // rows stored flattened: only request i's verified rows, request after request
   const void* target;
   const void* draft;
   const int32_t* tokens;
@@ -77,6 +78,8 @@ struct VerifyArgs {
   EmitReq* ereq;       // [B]
   EmitRange* ranges;   // [B, ceil(V / kRangeElems)]
   int32_t* amb;        // [B, kAmbCap]
+  int64_t* t_off;      // [B] flattened layout: first target row of request i (else unused)
+  int64_t* d_off;      // [B] flattened layout: first draft row of request i
   int r0, r1;          // the emit kernels handle requests [r0, r1)
   int emit_segs;       // emit-pass workgroups per request (1 = one fused workgroup, else 2 .. kMaxEmitSegs)
 };
@@ -168,6 +171,20 @@ __device__ inline void request_decision(const VerifyArgs& a, int i, int* st_out,
   }
   *st_out = st;
   *n_out = n;
+}
+
+// Row k of request i: the padded layout [B, G+1, V] (target) / [B, G, V] (draft), or, when
+// a.flat is set, the flattened layout in which request i's rows start at t_off[i] / d_off[i].
+template <int ES>
+__device__ inline const char* target_row(const VerifyArgs& a, int i, int k) {
+  const size_t r = a.flat ? (size_t)a.t_off[i] + k : (size_t)i * (a.G + 1) + k;
+  return reinterpret_cast<const char*>(a.target) + r * (size_t)a.V * ES;
+}
+
+template <int ES>
+__device__ inline const char* draft_row(const VerifyArgs& a, int i, int k) {
+  const size_t r = a.flat ? (size_t)a.d_off[i] + k : (size_t)i * a.G + k;
+  return reinterpret_cast<const char*>(a.draft) + r * (size_t)a.V * ES;
 }
 
 // Launch the emitted-token kernels (defined in emit.hip).

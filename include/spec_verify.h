@@ -155,6 +155,26 @@ int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                              void* event_before, void* event_after);
 
 /*
+ * spec_verify_flat -- spec_verify on the flattened variable-length layout in
+ * which only the verified rows are stored, request after request (DSpark
+ * paper, §5.3: every verified token of every request is one flat row):
+ *   target_rows [sum_i (L_i + 1), V]: target rows 0 .. L_i of request i start
+ *               at row T_i = sum_{j<i} (L_j + 1);
+ *   draft_rows  [sum_i L_i, V]: draft rows 0 .. L_i - 1 of request i start at
+ *               row D_i = sum_{j<i} L_j.
+ * `lengths` is required (it defines the layout); a length outside [0, gamma]
+ * makes that request BAD_LENGTH and counts as no rows.  The row offsets are
+ * derived on the device.  Everything else -- arguments, outputs, status,
+ * workspace (spec_verify_workspace_size), errors -- as for spec_verify, and the
+ * results equal spec_verify's on the padded layout holding the same rows.
+ */
+int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_rows,
+                         const void* draft_rows, const int32_t* draft_tokens, const int32_t* lengths,
+                         const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                         int32_t* num_accepted, int32_t* out_tokens, float* accept_prob, int32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spec_verify_greedy -- greedy verification.  a_k = argmax of raw target row k
  * (lowest token id on ties); n = first k < L_i with x_k != a_k, else L_i;
  * out_tokens = x_0 .. x_{n-1}, a_n, then -1.  Draft logits are never read.

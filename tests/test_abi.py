@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ("spec_verify", "spec_verify_greedy", "spec_schedule_lengths", "spec_verify_workspace_size",
               "spec_schedule_workspace_size", "spec_abi_version", "spec_status_string",
               "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size",
-              "spec_read_ceiling"):
+              "spec_read_ceiling", "spec_verify_flat", "spec_overlap_mass", "spec_schedule_capacity",
+              "spec_schedule_topk"):
         assert n in names, n
 
 
@@ -171,3 +172,14 @@ def test_async_scheduler_rejects_bad_arguments(lib):
     assert lib.spec_schedule_topk(4, 4, p, None, p, None, p, 4096, None) == 1
     assert lib.spec_schedule_topk(4, 4, p, p, None, None, p, 4096, None) == 1
     assert lib.spec_schedule_topk(4, 4, p, p, p, None, p, 4096, None) == 2                  # workspace
+
+
+def test_verify_flat_requires_lengths(lib):
+    keep, p = _fake()
+    ws = lib.spec_verify_workspace_size(2, 4, 100)
+    args = [2, 4, 100, 1, p, p, p, p, p, None, p, p, p, None, None, p, ws, None]
+    assert lib.spec_verify_flat(*args) == 2                      # fake workspace is refused
+    bad = list(args); bad[7] = None
+    assert lib.spec_verify_flat(*bad) == 1                       # no lengths
+    bad = list(args); bad[5] = ctypes.c_void_p(p.value + 2)
+    assert lib.spec_verify_flat(*bad) == 1                       # misaligned rows

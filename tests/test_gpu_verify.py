@@ -252,3 +252,48 @@ def test_nearly_identical_rows_take_the_exact_residual_path(sv):
         ref = oracle.verify(tt, dd, x)
         s = compare_verify(out, ref)
         assert (ref["num_accepted"] == 0).sum() > B // 2, s   # mostly rejected -> residual draws
+
+
+
+def _flatten(w, L):
+    Lh = to_np(L).astype(np.int64)
+    G = w.gamma
+    ok = (Lh >= 0) & (Lh <= G)
+    trows = torch.cat([w.target[i, :Lh[i] + 1] for i in range(w.B) if ok[i]], 0)
+    drows = [w.draft[i, :Lh[i]] for i in range(w.B) if ok[i] and Lh[i] > 0]
+    drows = torch.cat(drows, 0) if drows else w.draft[:0, 0]
+    return trows.contiguous(), drows.contiguous()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(B=40, gamma=6, V=999, seed=5)),
+    ("mid", dict(B=6, gamma=5, V=20011, seed=7)),
+    ("mixed", dict(B=12, gamma=4, V=30001, seed=9)),
+    ("scheduled", dict(B=300, gamma=8, V=4096, seed=11)),
+])
+def test_flat_layout_equals_padded(sv, name, kw):
+    """spec_verify_flat on the rows gathered request after request gives spec_verify's outputs
+    (and the oracle's); a bad length counts as no rows.  Bit for bit when rows are a multiple of
+    16 bytes; otherwise the two layouts start rows at other 16-byte offsets, which changes the
+    order of the row sums, so r agrees to rounding and the decisions are held to the oracle."""
+    w = make_workload(name, DEV, **kw)
+    rng = np.random.default_rng(91)
+    Lh = rng.integers(0, w.gamma + 1, w.B).astype(np.int32)
+    Lh[rng.random(w.B) < 0.05] = w.gamma + 2
+    L = torch.from_numpy(Lh).to(DEV)
+    ref = sv.verify(w.target, w.draft, w.draft_tokens, L, w.temperature, w.top_k, w.seed)
+    trows, drows = _flatten(w, L)
+    got = sv.verify_flat(trows, drows, w.draft_tokens, L, w.temperature, w.top_k, w.seed)
+    torch.cuda.synchronize()
+    a, b = to_np(got["accept_prob"]), to_np(ref["accept_prob"])
+    if (w.V * w.elem_bytes) % 16 == 0:
+        for k in ("num_accepted", "out_tokens", "status"):
+            assert (to_np(got[k]) == to_np(ref[k])).all(), k
+        assert ((a == b) | (np.isnan(a) & np.isnan(b))).all()
+    else:
+        assert (to_np(got["status"]) == to_np(ref["status"])).all()
+        assert (np.isnan(a) == np.isnan(b)).all()
+        ok = ~np.isnan(a)
+        assert (np.abs(a[ok] - b[ok]) <= 1e-6 * np.abs(b[ok]) + 1e-12).all()
+    o = run_oracle(w, lengths=L)
+    compare_verify(got, o)
