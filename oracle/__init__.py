@@ -20,6 +20,9 @@ from the DSpark pages:
   * `overlap_mass`  -- the per-position overlap sum_v min(p_t, p_d) of the
                        target and draft distributions (DSpark paper, §3.2.1,
                        Eq. 8);
+  * `markov_draft`  -- the Markov-head sequential draft sampler and the
+                       confidence head (DSpark paper, §3.1 Eq. 4-5, §3.2.1
+                       Eq. 7);
   * `philox`        -- the counter-based generator the draws come from
                        (Philox4x64-10, Salmon et al., SC'11).
 
@@ -27,7 +30,7 @@ Every function states the passage it follows.  Pins that tie it to facts
 outside itself live in tests/test_oracle_*.py.
 """
 
-from .philox import philox4x64_10, uniforms  # noqa: F401
+from .philox import draft_uniform, philox4x64_10, uniforms  # noqa: F401
 from .verification import (  # noqa: F401
     STATUS_BAD_LENGTH,
     STATUS_BAD_TEMPERATURE,
@@ -43,6 +46,7 @@ from .verification import (  # noqa: F401
     verify_greedy,
 )
 from .overlap import overlap_mass  # noqa: F401
+from .drafting import markov_draft, round_bf16  # noqa: F401
 from .scheduling import (  # noqa: F401
     capacity,
     survival,

@@ -7,10 +7,13 @@ two fixed odd constants, splits each 128-bit product into high and low
 halves, and permutes/xors them with words 1 and 3 and the key; between
 rounds the key is advanced by two Weyl constants.
 
-The DSpark pages fix no generator; the draws for request i and draft
-position k come from the block at counter (k+1, i, 0, 0) under key
+The DSpark pages fix no generator; the verifier's draws for request i and
+draft position k come from the block at counter (k+1, i, 0, 0) under key
 (seed_i, 0).  Word 0 gives the acceptance uniform, word 1 the uniform for
-the emitted token.  Uniforms are 53-bit: (w >> 11) * 2^-53, in [0, 1).
+the emitted token.  The draft sampler's draw for the same (i, k) is word 0 of
+the block at counter (k+1, i, 1, 0): a separate counter, so one seed can key
+both stages without the draft and the acceptance draws coinciding.
+Uniforms are 53-bit: (w >> 11) * 2^-53, in [0, 1).
 
 Test infrastructure only (see the package docstring).  Pinned bit for bit
 to numpy.random.Philox in tests/test_oracle_philox.py.
@@ -74,3 +77,14 @@ def uniforms(seed, request, position):
     w0, w1, _, _ = philox4x64_10(position + np.uint64(1), request, np.uint64(0), np.uint64(0),
                                  seed, np.uint64(0))
     return to_uniform53(w0), to_uniform53(w1)
+
+
+def draft_uniform(seed, request, position):
+    """The draft sampler's uniform for request i and draft position k (0-based): word 0 of the
+    block at counter (k + 1, i, 1, 0) under key (seed, 0)."""
+    seed = np.asarray(seed, dtype=np.uint64)
+    request = np.asarray(request, dtype=np.uint64)
+    position = np.asarray(position, dtype=np.uint64)
+    w0, _, _, _ = philox4x64_10(position + np.uint64(1), request, np.uint64(1), np.uint64(0),
+                                seed, np.uint64(0))
+    return to_uniform53(w0)

@@ -51,3 +51,19 @@ def test_uniform53_range_and_resolution():
     assert u[0] == 0.0 and u[1] == 0.0
     assert u[2] == 2.0 ** -53
     assert u[3] == 1.0 - 2.0 ** -53 and u[3] < 1.0
+
+
+def test_draft_uniform_matches_numpy_generator():
+    # the draft sampler's block is at counter (k+1, i, 1, 0); numpy's counter [k, i, 1, 0]
+    # advanced once is that block, and Generator.random() is (w >> 11) * 2^-53 of word 0
+    from oracle.philox import draft_uniform
+    rng = np.random.default_rng(13)
+    for _ in range(300):
+        s = int(rng.integers(0, 2 ** 64, dtype=np.uint64))
+        i = int(rng.integers(0, 4096))
+        k = int(rng.integers(0, 32))
+        g = np.random.Generator(np.random.Philox(key=np.array([s, 0], dtype=np.uint64),
+                                                 counter=np.array([k, i, 1, 0], dtype=np.uint64)))
+        assert float(draft_uniform(np.uint64(s), i, k)) == g.random()
+        ua, ue = uniforms(np.uint64(s), i, k)
+        assert float(draft_uniform(np.uint64(s), i, k)) not in (float(ua), float(ue))
