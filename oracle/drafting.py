@@ -22,8 +22,8 @@ k = 1 .. G in order:
      running sum of exp(z / T - max) in ascending token order, W its total,
      u the draft uniform of (i, k) from `oracle.philox.draft_uniform`);
      T = 0: x_k = the first-occurrence argmax of the stored z_k;
-  4. c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]) (Eq. 7) when hidden states h and
-     the head's weight w are given.
+  4. c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]) (Eq. 7) when the head's weight w
+     is given (with no hidden states, d = 0, the h_k part is empty).
 
 Status (request-wide, as in `verify`): bad temperature (NaN, negative,
 infinite), bad token (anchor outside [0, V)), non-finite (a stored row with
@@ -32,10 +32,13 @@ and confidences NaN; its logits are not defined.
 
 Flags (comparison aid, as in `verify`): a draw is flagged when u * W lies
 within `window` of either end of the chosen interval, window = 1e-10 * W
-plus, when an accumulation error bound is given, twice the total weight the
-ambiguous elements could move (an element is ambiguous when its rounding to
-the storage type changes across [z - e, z + e], e the bound).  A greedy
-decision is flagged when an ambiguous element could change the argmax.
+plus, when an accumulation error bound e is given, twice the total weight the
+ambiguous elements could move.  An element is ambiguous when the rounding of
+its exact value to the storage type is not the same across [z - e, z + e];
+any stored value from round(z - e) to round(z + e) is then possible (near
+zero, where U and the bias cancel, that range can span several values).  A
+greedy decision is flagged when an ambiguous element could change the
+argmax.
 """
 
 import numpy as np
@@ -87,12 +90,12 @@ def _inverse_cdf_margin(w, u):
     return tk, min(t - lo, C[tk] - t), W
 
 
-def _greedy_ambiguous(z, zalt, amb):
-    """True when some combination of the ambiguous elements' alternative values could move the
+def _greedy_ambiguous(z, zlo, zhi, amb):
+    """True when some choice of values within the ambiguous elements' ranges could move the
     first-occurrence argmax of z."""
     top = int(np.argmax(z))
-    hi = np.where(amb, np.maximum(z, zalt), z)
-    lo_top = min(z[top], zalt[top]) if amb[top] else z[top]
+    hi = np.where(amb, zhi, z)
+    lo_top = zlo[top] if amb[top] else z[top]
     others = hi.copy()
     others[top] = -np.inf
     best = others.max()
@@ -108,14 +111,16 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
     """Draft G tokens per request (see the module docstring).
 
     base [B, G, V] (U); W1 [V, r]; W2t [V, r]; anchor [B]; temperature [B] (default 1);
-    seed [B] uint64 bit patterns (default 0); hidden [B, G, d] and conf_w [d + r] (both or
-    neither); store "bf16" | "fp32"; acc_err_unit: unit roundoff u of the arithmetic being
-    compared (None: no ambiguity), the bound per element being (r + 2) u (sum_j |W1 W2t| + |U|).
+    seed [B] uint64 bit patterns (default 0); hidden [B, G, d] and conf_w [d + r] (conf_w alone
+    when d = 0; no confidences without conf_w); store "bf16" | "fp32"; acc_err_unit: unit
+    roundoff u of the arithmetic being compared (None: no ambiguity), the bound per element
+    being (r + 2) u (sum_j |W1 W2t| + |U|).
     `requests` restricts the work to a subset (others keep status 0, tokens -1).
 
     Returns a dict: tokens [B, G] int64, logits [B, G, V] fp64 (stored values; NaN where not
-    computed), alt [B, G, V] (the other rounding of ambiguous elements, NaN elsewhere), conf
-    [B, G], status [B], flag [B, G] bool, margin [B, G] (u*W distance / W; inf for greedy).
+    computed), amb_lo / amb_hi [B, G, V] (the range of possible stored values of ambiguous
+    elements, NaN elsewhere), conf [B, G], status [B], flag [B, G] bool, margin [B, G] (u*W
+    distance / W; inf for greedy).
     """
     B, G, V = base.shape
     W1 = _as_np(W1).astype(np.float64)
@@ -132,7 +137,8 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
     wc = None if conf_w is None else _as_np(conf_w).astype(np.float64)
     tokens = np.full((B, G), -1, dtype=np.int64)
     logits = np.full((B, G, V), np.nan)
-    alt = np.full((B, G, V), np.nan)
+    amb_lo = np.full((B, G, V), np.nan)
+    amb_hi = np.full((B, G, V), np.nan)
     conf = np.full((B, G), np.nan)
     status = np.zeros(B, dtype=np.int64)
     flag = np.zeros((B, G), dtype=bool)
@@ -161,19 +167,22 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
                 st |= STATUS_NONFINITE
                 break
             amb = np.zeros(V, dtype=bool)
-            za = np.full(V, np.nan)
+            zlo = zhi = z
             if acc_err_unit is not None:
                 e = (r + 2) * acc_err_unit * (np.abs(W2t) @ np.abs(a) + np.abs(U[k]))
                 zlo, zhi = round_store(zx - e, store), round_store(zx + e, store)
                 amb = zlo != zhi
-                za = np.where(amb, np.where(z == zlo, zhi, zlo), np.nan)
-                alt[i, k] = za
-            if h is not None:
-                t = float(wc[:h.shape[1]] @ h[k] + wc[h.shape[1]:] @ a)      # Eq. 7
+                amb_lo[i, k] = np.where(amb, zlo, np.nan)
+                amb_hi[i, k] = np.where(amb, zhi, np.nan)
+            if wc is not None:
+                dh = len(wc) - r
+                t = float(wc[dh:] @ a)                                       # Eq. 7
+                if dh:
+                    t += float(wc[:dh] @ h[k])
                 conf[i, k] = 1.0 / (1.0 + np.exp(-t))
             if T == 0.0:
                 xk = int(np.argmax(z))
-                flag[i, k] = bool(amb.any()) and _greedy_ambiguous(z, za, amb)
+                flag[i, k] = bool(amb.any()) and _greedy_ambiguous(z, zlo, zhi, amb)
             else:
                 y = z / T
                 ymax = np.max(y)
@@ -182,8 +191,7 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
                 xk, mg, W = _inverse_cdf_margin(w, u)
                 window = FLAG_EMIT_WINDOW * W
                 if amb.any():
-                    wa = np.exp(za[amb] / T - ymax)
-                    window += 2.0 * np.abs(wa - w[amb]).sum()
+                    window += 2.0 * (np.exp(zhi[amb] / T - ymax) - np.exp(zlo[amb] / T - ymax)).sum()
                 margin[i, k] = mg / W
                 flag[i, k] = mg < window
             tokens[i, k] = xk
@@ -192,5 +200,5 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
         if st:
             tokens[i] = -1
             conf[i] = np.nan
-    return dict(tokens=tokens, logits=logits, alt=alt, conf=conf, status=status, flag=flag,
-                margin=margin)
+    return dict(tokens=tokens, logits=logits, amb_lo=amb_lo, amb_hi=amb_hi, conf=conf, status=status,
+                flag=flag, margin=margin)

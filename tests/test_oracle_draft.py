@@ -119,6 +119,17 @@ def test_low_temperature_is_argmax_and_greedy_ties():
     assert out["tokens"][0].tolist() == [1, 1]
 
 
+def test_confidence_head_without_hidden_states():
+    """d = 0: Eq. 7 reduces to sigmoid(w . W1[x_{k-1}])."""
+    V, r = 12, 16
+    W1 = round_bf16(np.random.default_rng(2).normal(0, 1, (V, r)))
+    w = np.zeros(r)
+    w[3] = 1.0
+    out = markov_draft(np.zeros((2, 3, V)), W1, np.zeros((V, r)), [4, 7], temperature=[0.0, 0.0], conf_w=w)
+    prev = np.concatenate([[[4], [7]], out["tokens"][:, :-1]], axis=1)
+    assert np.allclose(out["conf"], expit(W1[prev, 3]), rtol=1e-15, atol=0)
+
+
 def test_confidence_head_picks_concatenation_parts():
     """Eq. 7 with w a basis vector: c_k = sigmoid(h_k[j]) for j < d, and
     sigmoid(W1[x_{k-1}, j - d]) beyond (x_0 = the anchor), against scipy's expit."""
@@ -179,14 +190,20 @@ def test_ambiguity_marks_elements_near_a_rounding_boundary():
     U[0, 0, 1] = 1.0 + 2.0 ** -8 - 2.0 ** -9  # U + b = 1 + 2^-8: exactly a midpoint
     out = markov_draft(U, W1, W2t, [0], temperature=[0.0], acc_err_unit=2.0 ** -23)
     assert out["logits"][0, 0, 1] == 1.0                      # ties to even
-    assert out["alt"][0, 0, 1] == 1.0 + 2.0 ** -7
-    assert np.isnan(out["alt"][0, 0, [0, 2, 3]]).all()
+    assert out["amb_lo"][0, 0, 1] == 1.0 and out["amb_hi"][0, 0, 1] == 1.0 + 2.0 ** -7
+    assert np.isnan(out["amb_lo"][0, 0, [0, 2, 3]]).all()
     # the same value with no error bound is not ambiguous
     out = markov_draft(U, W1, W2t, [0], temperature=[0.0])
-    assert np.isnan(out["alt"]).all() and not out["flag"].any()
+    assert np.isnan(out["amb_lo"]).all() and not out["flag"].any()
     # a value 2^-12 away from the midpoint is ambiguous only when the bound reaches it
     U[0, 0, 1] += 2.0 ** -12
     near = markov_draft(U, W1, W2t, [0], temperature=[0.0], acc_err_unit=2.0 ** -12)
     far = markov_draft(U, W1, W2t, [0], temperature=[0.0], acc_err_unit=2.0 ** -23)
-    assert near["alt"][0, 0, 1] == 1.0 and far["logits"][0, 0, 1] == 1.0 + 2.0 ** -7
-    assert np.isnan(far["alt"]).all()
+    assert near["amb_lo"][0, 0, 1] == 1.0 and far["logits"][0, 0, 1] == 1.0 + 2.0 ** -7
+    assert np.isnan(far["amb_lo"]).all()
+    # near zero, where U and the bias cancel, the range spans several bf16 values
+    U2 = np.zeros((1, 1, V))
+    U2[0, 0, 1] = -(2.0 ** -9) + 2.0 ** -20
+    wide = markov_draft(U2, W1, W2t, [0], temperature=[0.0], acc_err_unit=2.0 ** -12)
+    lo, hi = wide["amb_lo"][0, 0, 1], wide["amb_hi"][0, 0, 1]
+    assert lo < wide["logits"][0, 0, 1] < hi
