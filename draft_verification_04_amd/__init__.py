@@ -59,6 +59,9 @@ EXPORTS = {
     "spec_schedule_capacity": (_I, [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "spec_schedule_topk": (_I, [_I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_overlap_mass": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "spec_draft_workspace_size": (_Z, [_I, _I, _I]),
+    "spec_draft_markov": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z,
+                               _P]),
 }
 
 _lib_handle = None
@@ -302,6 +305,58 @@ def overlap_mass(target: torch.Tensor, draft: torch.Tensor, lengths: Optional[to
                                  _ptr(temperature), _ptr(top_k), _ptr(out["overlap"]), _ptr(out.get("status")),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_overlap_mass", code)
+    return out
+
+
+def draft_markov(base: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, anchor: torch.Tensor,
+                 temperature: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
+                 hidden: Optional[torch.Tensor] = None, conf_w: Optional[torch.Tensor] = None,
+                 out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                 in_place: bool = False) -> dict:
+    """spec_draft_markov on torch tensors.  Returns dict(tokens, logits, conf, status).
+
+    base [B, gamma, V] (float32 or bfloat16); W1 and W2t [V, r] bfloat16 (W2t row v = column v of
+    the r x V projection); anchor [B] int32; temperature [B] float32 (default ones); seed [B] int64
+    (uint64 bit patterns, default zeros); hidden [B, gamma, d] (base's dtype) and conf_w [d + r]
+    float32 for the confidences (conf_w alone when d = 0).  in_place writes the draft logits over
+    `base`.
+    """
+    lib = load_library()
+    _dev(base, "base", (torch.float32, torch.bfloat16), 3)
+    B, G, V = base.shape
+    _dev(W1, "W1", torch.bfloat16, 2)
+    _dev(W2t, "W2t", torch.bfloat16, 2)
+    r = W1.shape[1]
+    if tuple(W1.shape) != (V, r) or tuple(W2t.shape) != (V, r):
+        raise ValueError("W1 and W2t must be [V, r]")
+    _dev(anchor, "anchor", torch.int32, 1)
+    dev = base.device
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+    _dev(temperature, "temperature", torch.float32, 1)
+    _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
+    d = 0
+    if hidden is not None:
+        _dev(hidden, "hidden", base.dtype, 3)
+        if tuple(hidden.shape[:2]) != (B, G):
+            raise ValueError("hidden must be [B, gamma, d]")
+        d = hidden.shape[2]
+    if conf_w is not None:
+        _dev(conf_w, "conf_w", torch.float32, 1)
+        if conf_w.numel() != d + r:
+            raise ValueError("conf_w must hold d + r values")
+    if out is None:
+        out = dict(tokens=torch.empty((B, G), dtype=torch.int32, device=dev),
+                   logits=base if in_place else torch.empty_like(base),
+                   conf=torch.empty((B, G), dtype=torch.float32, device=dev) if conf_w is not None else None,
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    nbytes = int(lib.spec_draft_workspace_size(B, G, V))
+    ws = _workspace(nbytes, dev, workspace)
+    code = lib.spec_draft_markov(B, G, V, r, _logit_dtype(base), _ptr(base), _ptr(W1), _ptr(W2t), _ptr(anchor),
+                                 _ptr(temperature), _ptr(seed), d, _ptr(hidden), _ptr(conf_w), _ptr(out["tokens"]),
+                                 _ptr(out["logits"]), _ptr(out.get("conf")), _ptr(out["status"]), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check("spec_draft_markov", code)
     return out
 
 

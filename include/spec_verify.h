@@ -15,7 +15,10 @@
  *   - spec_schedule_lengths  -- survival products of per-position confidences
  *                               and the budgeted length selector (paper
  *                               §3.2.2; Algorithm 1 of the paper's Chinese
- *                               translation; the no-break search of §5.2).
+ *                               translation; the no-break search of §5.2);
+ *   - spec_draft_markov      -- the draft block itself: the Markov-head
+ *                               sequential sampler and the confidence head
+ *                               (paper §3.1, §3.2.1).
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
@@ -301,6 +304,70 @@ size_t spec_overlap_workspace_size(int32_t B, int32_t gamma, int32_t V);
 int32_t spec_overlap_mass(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,
                           const void* draft_logits, const int32_t* lengths, const float* temperature,
                           const int32_t* top_k, double* overlap_out, int32_t* status, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * spec_draft_markov -- the Markov-head sequential draft sampler and the
+ * confidence head (DSpark paper, §3.1, Eq. 4 and Eq. 5; §3.2.1, Eq. 7).
+ *
+ * For each request i and k = 0 .. gamma-1 in order (x_{-1} = anchor[i]):
+ *   z_k = U_k + W1[x_{k-1}] W2                  (Eq. 5: the Markov head's
+ *         transition bias; the product is accumulated in fp32 from the bf16
+ *         weights, U_k added in fp32, the sum rounded once to `dtype`, ties
+ *         to even);
+ *   x_k ~ softmax(z_k / T_i) over the whole vocabulary (Eq. 4): the smallest
+ *         token v whose running sum of exp(z / T) in ascending token order
+ *         exceeds u * total, u = word 0 of the Philox4x64-10 block at counter
+ *         (k + 1, i, 1, 0) under key (seed_i, 0), as (w >> 11) * 2^-53 (the
+ *         verifier's draws use counter word 2 = 0, so one seed may key both);
+ *         T_i = 0: the first-occurrence argmax of z_k;
+ *   conf_k = sigmoid(w . [h_k ; W1[x_{k-1}]])  (Eq. 7), when `conf` is given.
+ * The stored draft_logits rows ARE the draft distribution: hand them to
+ * spec_verify (with the same temperatures and top_k = 0) and the pair is
+ * lossless.  Sums are fp64 (exponentials evaluated in fp64 against exact
+ * power-of-two references), so the drawn token is that of an exact
+ * computation on the stored row except within ~1e-15 of a CDF boundary.
+ *
+ * Arguments
+ *   B >= 1, 1 <= gamma <= SPEC_MAX_GAMMA, 1 <= V <= SPEC_MAX_V (fp32: V/2),
+ *   r in {16, 32, ..., 256} (the paper's default is 256), d >= 0
+ *   dtype         SPEC_BF16 or SPEC_F32: base_logits, draft_logits, hidden
+ *   base_logits   [B, gamma, V] device: U_k from the parallel stage
+ *   W1            [V, r] bf16 device: the Markov embedding table
+ *   W2t           [V, r] bf16 device: the projection W2 (r x V) stored token-
+ *                 major, row v = column v of W2
+ *   anchor        [B] int32 device: x_{-1}, the last token of the previous
+ *                 verification cycle
+ *   temperature   [B] float32 device (0 = greedy)
+ *   seed          [B] uint64 device, or NULL for all 0
+ *   hidden        [B, gamma, d] device (dtype) or NULL when d = 0; conf_w
+ *                 [d + r] float32 device: the confidence head's weight, the
+ *                 first d entries against h_k; both ignored when conf = NULL
+ * Outputs (device)
+ *   tokens        [B, gamma] int32: x_k (all -1 for a request with a status)
+ *   draft_logits  [B, gamma, V] dtype: the stored z_k (may be base_logits
+ *                 itself: each element is read before it is overwritten);
+ *                 rows of a request with a status are not defined
+ *   conf          [B, gamma] float32 or NULL: conf_k (NaN for a request with
+ *                 a status), evaluated in fp64 and rounded
+ *   status        [B] int32: SPEC_REQ_BAD_TEMPERATURE, SPEC_REQ_BAD_TOKEN
+ *                 (anchor outside [0, V)), SPEC_REQ_NONFINITE (a stored row
+ *                 with a NaN or +inf, or with no finite value)
+ *   workspace     at least spec_draft_workspace_size(B, gamma, V) bytes,
+ *                 256-byte aligned, owned by the caller, busy until the
+ *                 call's kernels finish on `stream`.
+ * base_logits, draft_logits, W1 and W2t must be 16-byte aligned.  The call
+ * enqueues 2 gamma + 1 kernels; it never synchronises the host.
+ * Errors: SPEC_ERR_INVALID_ARG (shape, r, dtype, null or misaligned pointer,
+ * conf without conf_w or without hidden when d > 0), SPEC_ERR_WORKSPACE.
+ */
+size_t spec_draft_workspace_size(int32_t B, int32_t gamma, int32_t V);
+
+int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t dtype,
+                          const void* base_logits, const void* W1, const void* W2t,
+                          const int32_t* anchor, const float* temperature, const uint64_t* seed,
+                          int32_t d, const void* hidden, const float* conf_w, int32_t* tokens,
+                          void* draft_logits, float* conf, int32_t* status, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /*

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "spec_schedule_workspace_size", "spec_abi_version", "spec_status_string",
               "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size",
               "spec_read_ceiling", "spec_verify_flat", "spec_overlap_mass", "spec_schedule_capacity",
-              "spec_schedule_topk"):
+              "spec_schedule_topk", "spec_draft_markov", "spec_draft_workspace_size"):
         assert n in names, n
 
 
@@ -183,3 +183,37 @@ def test_verify_flat_requires_lengths(lib):
     assert lib.spec_verify_flat(*bad) == 1                       # no lengths
     bad = list(args); bad[5] = ctypes.c_void_p(p.value + 2)
     assert lib.spec_verify_flat(*bad) == 1                       # misaligned rows
+
+
+def test_draft_rejects_bad_arguments(lib):
+    keep, p = _fake()
+    ws = lib.spec_draft_workspace_size(3, 4, 1000)
+    assert ws > 0 and ws % 256 == 0 and lib.spec_draft_workspace_size(0, 4, 1000) == 0
+    assert lib.spec_draft_workspace_size(3, 65, 1000) == 0
+
+    def call(B=3, G=4, V=1000, r=256, dt=1, U=p, w1=p, w2=p, x0=p, T=p, d=0, h=None, cw=None,
+             tok=p, z=p, conf=None, st=p, w=p, wsb=ws):
+        return lib.spec_draft_markov(B, G, V, r, dt, U, w1, w2, x0, T, None, d, h, cw, tok, z, conf, st,
+                                     w, wsb, None)
+    assert call(w=None) == 2                       # every other argument is valid
+    assert call(B=0) == 1
+    assert call(G=0) == 1
+    assert call(G=65) == 1
+    assert call(r=8) == 1                          # rank not a multiple of 16
+    assert call(r=264) == 1                        # rank above 256
+    assert call(r=24) == 1
+    assert call(dt=5) == 1
+    assert call(U=None) == 1
+    assert call(w2=None) == 1
+    assert call(x0=None) == 1
+    assert call(T=None) == 1
+    assert call(tok=None) == 1
+    assert call(st=None) == 1
+    assert call(z=ctypes.c_void_p(p.value + 4)) == 1
+    assert call(w1=ctypes.c_void_p(p.value + 8)) == 1
+    assert call(conf=p) == 1                       # confidences without the head's weight
+    assert call(conf=p, cw=p, d=16) == 1           # ... or without hidden states
+    assert call(conf=p, cw=p, d=0) == 2            # d = 0 needs no hidden states
+    assert call(d=-1) == 1
+    assert call(wsb=ws - 1) == 2
+    assert call(w=ctypes.c_void_p(p.value + 16)) == 2

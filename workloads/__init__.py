@@ -12,6 +12,10 @@ the Gumbel-max trick (argmax of logits/T plus Gumbel noise, restricted to the
 top-k set where one applies).  That is the drafter's job upstream of the
 verifier, so it lives with the inputs.
 
+`workloads.drafting` makes the draft sampler's inputs (base logits, the
+Markov head's weights, anchors, hidden states); it too holds random numbers
+only.
+
 Shapes follow the statement of the problem in the DSpark paper, §2.1
 (gamma draft tokens per request, target and draft distributions per draft
 position over a vocabulary) plus one extra target row per request for the
@@ -29,3 +33,4 @@ from .configs import (  # noqa: F401
     make_sps_table,
     sample_draft_tokens,
 )
+from .drafting import DraftInputs, make_draft_inputs  # noqa: F401
