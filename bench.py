@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-overlap", action="store_true", help="skip the overlap-mass measurement")
+    p.add_argument("--no-draft", action="store_true", help="skip the draft-sampler measurement")
     p.add_argument("--pool", type=int, default=8, help="worker processes for the pooled CPU-oracle timing")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
@@ -126,6 +127,9 @@ def main():
     ceiling = read_ceiling(sv, torch, copies, alg_bytes, stream)
     overlap = None if args.no_overlap else overlap_leg(sv, torch, w, copies, sch_out["lengths"], stream)
     async_sched = async_scheduler_leg(sv, torch, w, sps, stream) if w.conf is not None else None
+    draft = None
+    if not args.no_draft:
+        draft = draft_leg(sv, torch, oracle, dev, stream, with_cpu=not args.no_cpu)
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -177,6 +181,7 @@ def main():
         "cpu_baseline": cpu,
         "overlap_mass": overlap,
         "async_scheduler": async_sched,
+        "draft_sampler": draft,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory},
         "ms_breakdown": {"stream_kernel": ms_stream, "rest_of_step": ms_step - ms_stream},
@@ -244,6 +249,55 @@ def overlap_leg(sv, torch, w, copies, lengths, stream, reps=20):
     return {"ms_per_call": ms, "positions": pos, "positions_per_s": pos / (ms * 1e-3),
             "rows_per_pass": 2 * pos, "bytes_read_per_call": 2 * once,
             "gbps_read": 2 * once / (ms * 1e-3) / 1e9, "algorithmic_bytes_once": once}
+
+
+def draft_leg(sv, torch, oracle, dev, stream, reps=10, with_cpu=True):
+    """spec_draft_markov (the Markov-head sequential sampler and the confidence head) on the
+    draft block of the same shape: B=256 requests, gamma=16, V=151936, r=256, hidden size 4096,
+    bf16, temperatures U[0.6, 1.2] with every fifth request greedy; HIP events around whole calls.
+    Not part of the step (the verifier's input is the drafter's output)."""
+    from draft_verification_04_amd.hipevents import HipEvent
+    from workloads import make_draft_inputs
+    B, G, V, r, d = 256, 16, 151936, 256, 4096
+    w = make_draft_inputs(B, G, V, r, d, "bf16", "gaussian", "mixed", 2024, dev)
+    out = dict(tokens=torch.empty((B, G), dtype=torch.int32, device=dev), logits=torch.empty_like(w.base),
+               conf=torch.empty((B, G), dtype=torch.float32, device=dev),
+               status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = torch.empty(sv.load_library().spec_draft_workspace_size(B, G, V), dtype=torch.uint8, device=dev)
+    call = lambda: sv.draft_markov(w.base, w.W1, w.W2t, w.anchor, w.temperature, w.seed, w.hidden, w.conf_w,
+                                   out=out, workspace=ws, stream=stream)
+    for _ in range(2):
+        call()
+    e0, e1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    nwg = (V + 127) // 128
+    step_bytes = 2 * B * V * 2 + V * r * 2 + B * r * 2 + B * nwg * 32   # U_k in, z_k out, W2, W1 rows, tiles
+    flops = 2.0 * B * V * r * G
+    res = {"config": f"B={B} gamma={G} V={V} r={r} d={d} bf16", "ms_per_call": ms,
+           "draft_tokens_per_s": B * G / (ms * 1e-3), "status_ok": int((out["status"] == 0).sum().item()),
+           "bytes_per_step_kernel": step_bytes, "gbps_per_call": G * step_bytes / (ms * 1e-3) / 1e9,
+           "mfma_tflops_per_call": flops / (ms * 1e-3) / 1e12}
+    if with_cpu:
+        from threadpoolctl import threadpool_limits
+        sample = [0, 1]
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            oracle.markov_draft(w.base, w.W1.cpu(), w.W2t.cpu(), w.anchor.cpu(), w.temperature.cpu(), w.seed.cpu(),
+                                w.hidden, w.conf_w.cpu(), requests=sample)
+            el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(sample) * G / el, "unit": "draft tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"requests {sample} x {G} positions, numpy fp64, one BLAS thread, "
+                                         f"{el:.1f} s"}
+    del w, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def async_scheduler_leg(sv, torch, w, sps, stream, reps=20):

@@ -34,6 +34,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDraftThreads = 256;   // markov_logits_kernel: 4 waves
 constexpr int kTileTokens = 128;     // tokens per workgroup (32 per wave)
@@ -48,14 +50,13 @@ struct Stat {
   double s;     // sum of 2^(z c - m) (sampling rows), else 0
   double m;     // integer reference of s (-inf while s == 0)
   float zmax;   // largest stored value (-inf when none)
-  int32_t idx;  // first token holding zmax
   int32_t bad;  // NaN or +inf seen
 };
 
 struct alignas(16) DPart {
   double s, m;
   float zmax;
-  int32_t idx, bad, pad;
+  int32_t bad, pad0, pad1;
 };
 
 struct DraftArgs {
@@ -81,13 +82,11 @@ __device__ __forceinline__ Stat stat_empty() {
   s.s = 0.0;
   s.m = -__builtin_inf();
   s.zmax = -__builtin_inff();
-  s.idx = 0x7fffffff;
   s.bad = 0;
   return s;
 }
 
-// a <- a (+) b.  Sums are brought to the larger reference by exact power-of-two scaling; the
-// maximum keeps the lower token on equal values.
+// a <- a (+) b.  Sums are brought to the larger reference by exact power-of-two scaling.
 __device__ __forceinline__ void stat_merge(Stat& a, const Stat& b) {
   if (b.s > 0.0) {
     if (a.s > 0.0) {
@@ -99,10 +98,7 @@ __device__ __forceinline__ void stat_merge(Stat& a, const Stat& b) {
       a.m = b.m;
     }
   }
-  if (b.zmax > a.zmax || (b.zmax == a.zmax && b.idx < a.idx)) {
-    a.zmax = b.zmax;
-    a.idx = b.idx;
-  }
+  a.zmax = fmaxf(a.zmax, b.zmax);
   a.bad |= b.bad;
 }
 
@@ -111,7 +107,6 @@ __device__ __forceinline__ Stat stat_shfl_xor(const Stat& a, int o) {
   b.s = __shfl_xor(a.s, o, SPEC_WAVE);
   b.m = __shfl_xor(a.m, o, SPEC_WAVE);
   b.zmax = __shfl_xor(a.zmax, o, SPEC_WAVE);
-  b.idx = __shfl_xor(a.idx, o, SPEC_WAVE);
   b.bad = __shfl_xor(a.bad, o, SPEC_WAVE);
   return b;
 }
@@ -121,9 +116,26 @@ __device__ __forceinline__ Stat from_part(const DPart& p) {
   s.s = p.s;
   s.m = p.m;
   s.zmax = p.zmax;
-  s.idx = p.idx;
   s.bad = p.bad;
   return s;
+}
+
+// 2^t for t <= 0 in fp64, table-driven (P. T. P. Tang, "Table-driven implementation of the
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989): t = n + j/64 + r
+// with |r| <= 1/128, 2^t = 2^n * 2^(j/64) * 2^r; the 64 values 2^(j/64) come from `tab`, 2^r from
+// its Taylor series to degree 5 (truncation below 4e-17 relative).  t below -1100 (or -inf) gives 0.
+__device__ __forceinline__ double exp2_tab(double t, const double* tab) {
+  t = fmax(t, -1100.0);
+  const double N = rint(t * 64.0);
+  const double r = fma(N, -0.015625, t);  // exact
+  const int Ni = (int)N;
+  double p = 0x1.5d87fe78a6731p-10;       // (ln 2)^k / k!, k = 5 .. 0
+  p = fma(p, r, 0x1.3b2ab6fba4e77p-7);
+  p = fma(p, r, 0x1.c6b08d704a0c0p-5);
+  p = fma(p, r, 0x1.ebfbdff82c58fp-3);
+  p = fma(p, r, 0x1.62e42fefa39efp-1);
+  p = fma(p, r, 1.0);
+  return ldexp(tab[Ni & 63] * p, Ni >> 6);
 }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
@@ -144,117 +156,205 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
 }
 
 // Step k: draft logits z_k = U_k + W1[x_{k-1}] W2 for every request, and per-tile statistics.
+// Per request block, the MFMA chain runs on operands loaded during the previous block, and the
+// epilogue works on U_k values loaded during the previous block too, so HBM and L2 latency overlap
+// the chain and the epilogue.  Operand steps beyond r/16 are zero on both sides (exact zeros).
 template <int ES>
 __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs a) {
+  constexpr int UW = ES == 2 ? 2 : 4;  // 32-bit words per group of 4 logits
+  constexpr int RS = kMaxSteps * 16 + 8;  // LDS row stride of the embedding rows (bf16; +16 B breaks bank aliasing)
   __shared__ Stat sp[2][kDraftThreads / 64][kReqBlock];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ double tab[64];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kReqBlock * RS];
+  __shared__ int sPrev[2][kReqBlock];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int tl = lane & 31, h = lane >> 5;
-  const int V = a.V, r = a.r, G = a.G, k = a.k;
+  const int V = a.V, r = a.r, G = a.G, k = a.k, B = a.B;
   const int nk = r >> 4;
   const int n0 = blockIdx.x * kTileTokens + wv * 32;
+  const bf16x8 zero8 = {};
+  if (tid < 64) tab[tid] = exp2((double)tid * 0.015625);
 
   // Projection operand (MFMA A: row = token, 8 consecutive k per lane half): token n0 + tl.
   const uint16_t* w2 = a.W2t + (size_t)min(n0 + tl, V - 1) * r + 8 * h;
   bf16x8 wop[kMaxSteps];
 #pragma unroll
-  for (int kk = 0; kk < kMaxSteps; ++kk)
-    if (kk < nk) wop[kk] = load_bf16x8(w2 + kk * 16);
+  for (int kk = 0; kk < kMaxSteps; ++kk) {
+    const bf16x8 v = load_bf16x8(w2 + min(kk, nk - 1) * 16);
+    wop[kk] = kk < nk ? v : zero8;
+  }
 
-  const bool vec = (V & 3) == 0;
-  const int nrb = (a.B + kReqBlock - 1) / kReqBlock;
+  // x_{k-1} of request j (index clamped; a bad value selects row 0: a bad request's rows are
+  // not defined)
+  const int* prevp = (k == 0) ? a.anchor : a.tokens + (k - 1);
+  const int pstride = (k == 0) ? 1 : G;
+  auto prev_of = [&](int j) -> int {
+    const int p = prevp[(size_t)min(j, B - 1) * pstride];
+    return (p < 0 || p >= V) ? 0 : p;
+  };
+  // The embedding rows W1[x_{k-1}] of a request block go to LDS once per workgroup: 32 rows of
+  // r bf16, 16-byte chunks, consecutive threads on consecutive chunks of a row.
+  const int cpr = r >> 3;                  // 16-byte chunks per row
+  const int nchunk = kReqBlock * cpr;      // <= 1024: at most 4 per thread
+  v4u32 gw[4];
+  auto load_rows = [&](int pb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * kDraftThreads;
+      if (c < nchunk) {
+        const int row = c / cpr, col = c - row * cpr;
+        gw[i] = *reinterpret_cast<const v4u32*>(a.W1 + (size_t)sPrev[pb][row] * r + col * 8);
+      }
+    }
+  };
+  auto store_rows = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * kDraftThreads;
+      if (c < nchunk) {
+        const int row = c / cpr, col = c - row * cpr;
+        *reinterpret_cast<v4u32*>(&sB[buf][row * RS + col * 8]) = gw[i];
+      }
+    }
+  };
+  const bool fast_tile = ((V & 3) == 0) && (n0 + 32 <= V);
+  auto load_u = [&](int j, uint32_t (&ur)[4][UW]) {
+    const size_t row = ((size_t)j * G + k) * V;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int t0 = n0 + 8 * g + 4 * h;
+      if constexpr (ES == 2) {
+        const v2u32 w = __builtin_nontemporal_load(
+            reinterpret_cast<const v2u32*>(reinterpret_cast<const uint16_t*>(a.base) + row + t0));
+        ur[g][0] = w.x; ur[g][1] = w.y;
+      } else {
+        const v4u32 w = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u32*>(reinterpret_cast<const float*>(a.base) + row + t0));
+        ur[g][0] = w.x; ur[g][1] = w.y; ur[g][2] = w.z; ur[g][3] = w.w;
+      }
+    }
+  };
+
+  const int nrb = (B + kReqBlock - 1) / kReqBlock;
+  if (tid < kReqBlock) {
+    sPrev[0][tid] = prev_of(tid);
+    sPrev[1][tid] = prev_of(tid + kReqBlock);
+  }
+  uint32_t ucur[4][UW], unext[4][UW];
+  if (fast_tile && tl < B) load_u(tl, ucur);
+  __syncthreads();  // tab, sPrev
+  load_rows(0);
+  store_rows(0);
+  __syncthreads();
+
   for (int rb = 0; rb < nrb; ++rb) {
     const int j = rb * kReqBlock + tl;
-    const bool valid = j < a.B;
-    int prev = 0;
-    float T = 0.f;
-    if (valid) {
-      prev = (k == 0) ? a.anchor[j] : a.tokens[(size_t)j * G + k - 1];
-      T = a.temperature[j];
-    }
-    if (prev < 0 || prev >= V) prev = 0;  // a bad request: its rows are not defined
+    const bool valid = j < B;
+    const bool fast = valid && fast_tile;
+    const int buf = rb & 1;
+    const float T = a.temperature[min(j, B - 1)];
+    const bool more = rb + 1 < nrb;
+    if (more) load_rows(buf ^ 1);        // rows of block rb + 1 (their ids were stored a block ago)
+    int pn2 = 0;
+    if (tid < kReqBlock) pn2 = prev_of((rb + 2) * kReqBlock + tid);
 
-    // Embedding operand (MFMA B: column = request, 8 consecutive k per lane half).
-    const uint16_t* w1 = a.W1 + (size_t)prev * r + 8 * h;
+    // Embedding operand (MFMA B: column = request, 8 consecutive k per lane half) from LDS.
+    const uint16_t* rowp = &sB[buf][tl * RS + 8 * h];
     f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < kMaxSteps; ++kk)
-      if (kk < nk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kk], load_bf16x8(w1 + kk * 16), acc, 0, 0, 0);
+    for (int kk = 0; kk < kMaxSteps; ++kk) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(rowp + min(kk, nk - 1) * 16));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kk], kk < nk ? b : zero8, acc, 0, 0, 0);
+    }
+    if (fast_tile && j + kReqBlock < B) load_u(j + kReqBlock, unext);
 
     // Epilogue: lane holds D[token n0 + 8g + 4h + p][request j] in acc[4g + p].
     const size_t row = ((size_t)(valid ? j : 0) * G + k) * V;
-    Stat st = stat_empty();
     float zq[16];
+    int bad = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int t0 = n0 + 8 * g + 4 * h;
       float u[4];
-      if (valid && vec && t0 + 3 < V) {
+      if (fast) {
         if constexpr (ES == 2) {
-          const v2u32 w = __builtin_nontemporal_load(reinterpret_cast<const v2u32*>(
-              reinterpret_cast<const uint16_t*>(a.base) + row + t0));
-          u[0] = bf16_lo(w.x); u[1] = bf16_hi(w.x); u[2] = bf16_lo(w.y); u[3] = bf16_hi(w.y);
+          u[0] = bf16_lo(ucur[g][0]); u[1] = bf16_hi(ucur[g][0]); u[2] = bf16_lo(ucur[g][1]); u[3] = bf16_hi(ucur[g][1]);
         } else {
-          const v4u32 w = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(
-              reinterpret_cast<const float*>(a.base) + row + t0));
-          u[0] = __uint_as_float(w.x); u[1] = __uint_as_float(w.y);
-          u[2] = __uint_as_float(w.z); u[3] = __uint_as_float(w.w);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) u[p] = __uint_as_float(ucur[g][p]);
         }
       } else {
 #pragma unroll
         for (int p = 0; p < 4; ++p) u[p] = (valid && t0 + p < V) ? load_logit<ES>(a.base, row + t0 + p) : 0.f;
       }
       float zs[4];
+      uint32_t wd[2];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float z = u[p] + acc[4 * g + p];
-        if constexpr (ES == 2) zs[p] = __uint_as_float(f32_to_bf16_rne(z) << 16);
-        else zs[p] = z;
+      for (int p = 0; p < 4; ++p) zs[p] = u[p] + acc[4 * g + p];
+      if constexpr (ES == 2) {
+        // round to nearest even (hardware conversion), keep the stored values
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x2 v = {zs[2 * q], zs[2 * q + 1]};
+          wd[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+          zs[2 * q] = bf16_lo(wd[q]);
+          zs[2 * q + 1] = bf16_hi(wd[q]);
+        }
       }
-      if (valid && vec && t0 + 3 < V) {
+      if (fast) {
         if constexpr (ES == 2) {
           uint2 w;
-          w.x = (__float_as_uint(zs[0]) >> 16) | (__float_as_uint(zs[1]) & 0xffff0000u);
-          w.y = (__float_as_uint(zs[2]) >> 16) | (__float_as_uint(zs[3]) & 0xffff0000u);
+          w.x = wd[0];
+          w.y = wd[1];
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.logits) + row + t0) = w;
         } else {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.logits) + row + t0) =
               make_float4(zs[0], zs[1], zs[2], zs[3]);
         }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          zq[4 * g + p] = zs[p];
+          bad |= __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
+        }
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          if (valid && t0 + p < V) {
+        for (int p = 0; p < 4; ++p) {
+          const bool in = valid && t0 + p < V;
+          if (in) {
             if constexpr (ES == 2)
               reinterpret_cast<uint16_t*>(a.logits)[row + t0 + p] = (uint16_t)(__float_as_uint(zs[p]) >> 16);
             else
               reinterpret_cast<float*>(a.logits)[row + t0 + p] = zs[p];
           }
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const bool in = valid && t0 + p < V;
-        const float z = in ? zs[p] : -__builtin_inff();
-        zq[4 * g + p] = z;
-        if (in && (z != z || z == __builtin_inff())) st.bad = 1;
-        if (z > st.zmax) {  // tokens visited in ascending order: the first maximum is kept
-          st.zmax = z;
-          st.idx = t0 + p;
+          zq[4 * g + p] = in ? zs[p] : -__builtin_inff();
+          bad |= in && __builtin_amdgcn_classf(zs[p], 0x203);
         }
       }
     }
-    if (valid && T > 0.f && T < __builtin_inff() && st.zmax > -__builtin_inff() && !st.bad) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q = 0; q < UW; ++q) ucur[g][q] = unext[g][q];
+    Stat st = stat_empty();
+    st.bad = bad;
+    float zm = zq[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) zm = fmaxf(zm, zq[i]);
+    st.zmax = zm;
+    if (valid && T > 0.f && T < __builtin_inff() && zm > -__builtin_inff() && !bad) {
       const double c = kLog2eD / (double)T;
-      const double m = ceil((double)st.zmax * c);
+      const double m = ceil((double)zm * c);
       double s = 0.0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s += exp2((double)zq[i] * c - m);
+      for (int i = 0; i < 16; ++i) s += exp2_tab(fma((double)zq[i], c, -m), tab);
       st.s = s;
       st.m = m;
     }
     // the two lane halves hold the same request
     stat_merge(st, stat_shfl_xor(st, 32));
-    const int buf = rb & 1;
     if (h == 0) sp[buf][wv][tl] = st;
+    if (more) store_rows(buf ^ 1);                 // read after the barrier below
+    if (tid < kReqBlock) sPrev[buf][tid] = pn2;    // ids of block rb + 2
     __syncthreads();
     if (wv == 0 && h == 0 && valid) {
       Stat t = sp[buf][0][tl];
@@ -264,20 +364,26 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       p.s = t.s;
       p.m = t.m;
       p.zmax = t.zmax;
-      p.idx = t.idx;
       p.bad = t.bad;
-      p.pad = 0;
+      p.pad0 = p.pad1 = 0;
       a.part[(size_t)j * a.nwg + blockIdx.x] = p;
     }
   }
 }
 
-// Step k: draw x_k for every request (one wave each).
+// Step k: draw x_k for every request (one workgroup each).  Every thread takes a contiguous run of
+// tiles; the workgroup finds the common reference, the total and the tile where the running sum
+// (tile order = token order) passes u * total; wave 0 then walks that tile's 128 tokens.
 template <int ES>
 __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(DraftArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
-  if (j >= a.B) return;
+  constexpr int NW = kSampleThreads / 64;
+  __shared__ Stat red[NW];
+  __shared__ double wtot[NW];
+  __shared__ int hitw[NW], lastw[NW];
+  __shared__ int sel_w, first_max;
+  __shared__ double sel_before;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j = blockIdx.x;
   const int k = a.k, V = a.V, nwg = a.nwg;
   int st = (k == 0) ? 0 : a.req_status[j];
   const float T = a.temperature[j];
@@ -287,65 +393,116 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(DraftArgs
     if (x0 < 0 || x0 >= V) st |= SPEC_REQ_BAD_TOKEN;
   }
   const DPart* P = a.part + (size_t)j * nwg;
-  const int per = (nwg + 63) / 64;
-  const int w0 = min(nwg, lane * per), w1 = min(nwg, w0 + per);
+  const int per = (nwg + kSampleThreads - 1) / kSampleThreads;
+  const int w0 = min(nwg, tid * per), w1 = min(nwg, w0 + per);
   Stat acc = stat_empty();
   for (int w = w0; w < w1; ++w) stat_merge(acc, from_part(P[w]));
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) stat_merge(acc, stat_shfl_xor(acc, o));
+  if (lane == 0) red[wv] = acc;
+  __syncthreads();
+  acc = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) stat_merge(acc, red[w]);
+
+  if (st == 0 && (acc.bad || !(acc.zmax > -__builtin_inff()))) st |= SPEC_REQ_NONFINITE;
+  // the first tile holding the row's maximum (greedy rows; a fallback of the draw)
+  int myw = 0x7fffffff;
+  if (st == 0)
+    for (int w = w0; w < w1; ++w)
+      if (P[w].zmax == acc.zmax) {
+        myw = w;
+        break;
+      }
+  myw = wave_min_i(myw);
+  if (lane == 0) hitw[wv] = myw;
+  __syncthreads();
+  int wmax = hitw[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) wmax = min(wmax, hitw[w]);
+  __syncthreads();
+  const size_t row = ((size_t)j * a.G + k) * V;
+  // wave 0: the first token of tile w holding the maximum
+  auto first_max_token = [&](int w) -> int {
+    const int t0 = w * kTileTokens + 2 * lane;
+    const bool q0 = t0 < V && load_logit<ES>(a.logits, row + t0) == acc.zmax;
+    const bool q1 = t0 + 1 < V && load_logit<ES>(a.logits, row + t0 + 1) == acc.zmax;
+    const unsigned long long hb = __ballot(q0 || q1);
+    const int L = hb ? __ffsll((long long)hb) - 1 : 0;
+    return __shfl(q0 ? t0 : t0 + 1, L, SPEC_WAVE);
+  };
 
   int x = -1;
-  if (st == 0) {
-    if (acc.bad || !(acc.zmax > -__builtin_inff())) {
-      st |= SPEC_REQ_NONFINITE;
-    } else if (T == 0.f) {
-      x = acc.idx;
-    } else {
-      const double M = acc.m;
-      const double c = kLog2eD / (double)T;
-      // this lane's tiles, scaled to the common reference, in token order
-      double ls = 0.0;
-      int mylast = -1;
+  if (st == 0 && T == 0.f && wv == 0) x = first_max_token(wmax);
+  if (st == 0 && T != 0.f) {  // uniform over the workgroup
+    const double M = acc.m;
+    const double c = kLog2eD / (double)T;
+    double ls = 0.0;
+    int mylast = -1;
+    for (int w = w0; w < w1; ++w) {
+      if (!(P[w].s > 0.0)) continue;
+      const double e = ldexp(P[w].s, (int)fmax(P[w].m - M, -2000.0));
+      ls += e;
+      if (e > 0.0) mylast = w;
+    }
+    const double iw = wave_inclusive_sum(ls, lane);
+    if (lane == 63) wtot[wv] = iw;
+    __syncthreads();
+    double base = 0.0, S = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wv) base += wtot[w];
+      S += wtot[w];
+    }
+    const double incl = base + iw;
+    const uint64_t seed = a.seed ? a.seed[j] : 0ull;
+    const Philox4x64 blk = philox4x64_10((uint64_t)k + 1, (uint64_t)j, 1, 0, seed, 0);
+    const double target = uniform53(blk.w0) * S;
+    const unsigned long long hit = __ballot(incl > target);
+    const int wl = wave_max_i(mylast);
+    if (lane == 0) {
+      hitw[wv] = hit ? wv * 64 + (__ffsll((long long)hit) - 1) : 0x7fffffff;
+      lastw[wv] = wl;
+    }
+    __syncthreads();
+    int first = 0x7fffffff, lastt = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      first = min(first, hitw[w]);
+      lastt = max(lastt, lastw[w]);
+    }
+    if (tid == 0) {
+      sel_w = lastt;                 // u * S rounded up to S: the last weighted tile,
+      sel_before = -__builtin_inf(); // and in it the last weighted token
+    }
+    __syncthreads();
+    if (tid == first) {  // the first thread whose running sum passes the target walks its tiles
+      double cum = incl - ls;
+      int ws = -1;
+      double before = 0.0;
       for (int w = w0; w < w1; ++w) {
         if (!(P[w].s > 0.0)) continue;
         const double e = ldexp(P[w].s, (int)fmax(P[w].m - M, -2000.0));
-        ls += e;
-        if (e > 0.0) mylast = w;
-      }
-      const double incl = wave_inclusive_sum(ls, lane);
-      const double S = __shfl(incl, 63, SPEC_WAVE);
-      const uint64_t seed = a.seed ? a.seed[j] : 0ull;
-      const Philox4x64 blk = philox4x64_10((uint64_t)k + 1, (uint64_t)j, 1, 0, seed, 0);
-      const double target = uniform53(blk.w0) * S;
-      // the first lane whose running sum passes the target walks its tiles
-      const unsigned long long hit = __ballot(incl > target);
-      int wsel = -1;
-      double before = -__builtin_inf();  // -inf: no crossing, take the tile's last weighted token
-      if (hit) {
-        const int L = __ffsll((long long)hit) - 1;
-        if (lane == L) {
-          double cum = incl - ls;
-          for (int w = w0; w < w1; ++w) {
-            if (!(P[w].s > 0.0)) continue;
-            const double e = ldexp(P[w].s, (int)fmax(P[w].m - M, -2000.0));
-            if (!(e > 0.0)) continue;
-            if (cum + e > target) {
-              wsel = w;
-              before = cum;
-              break;
-            }
-            cum += e;
-          }
-          if (wsel < 0) wsel = mylast;  // rounding: the last weighted tile, its last token
+        if (!(e > 0.0)) continue;
+        if (cum + e > target) {
+          ws = w;
+          before = cum;
+          break;
         }
-        wsel = __shfl(wsel, L, SPEC_WAVE);
-        before = __shfl(before, L, SPEC_WAVE);
-      } else {  // u * S rounded up to S: the last weighted tile, its last token
-        wsel = wave_max_i(mylast);
+        cum += e;
       }
-      if (wsel < 0) wsel = acc.idx / kTileTokens;  // cannot happen when S > 0
-      // the chosen tile's tokens, two per lane, in ascending order
-      const size_t row = ((size_t)j * a.G + k) * V;
+      if (ws >= 0) {
+        sel_w = ws;
+        sel_before = before;
+      } else if (mylast >= 0) {  // rounding: this run's last weighted tile, its last token
+        sel_w = mylast;
+      }
+    }
+    __syncthreads();
+    int wsel = sel_w;
+    const double before = sel_before;
+    if (wsel < 0) wsel = wmax;  // cannot happen when S > 0
+    if (wv == 0) {
       const int t0 = wsel * kTileTokens + 2 * lane;
       double e0 = 0.0, e1 = 0.0;
       if (t0 < V) e0 = exp2((double)load_logit<ES>(a.logits, row + t0) * c - M);
@@ -361,26 +518,26 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(DraftArgs
       const unsigned long long hb = __ballot(p0 || p1);
       if (hb) {
         const int Lb = __ffsll((long long)hb) - 1;
-        const int pick = __shfl(p0 ? t0 : t0 + 1, Lb, SPEC_WAVE);
-        x = pick;
+        x = __shfl(p0 ? t0 : t0 + 1, Lb, SPEC_WAVE);
       } else {  // past the end of the tile: its last weighted token
         const unsigned long long nz = __ballot(e0 > 0.0 || e1 > 0.0);
         if (nz) {
           const int Ln = 63 - __clzll((long long)nz);
           x = __shfl(e1 > 0.0 ? t0 + 1 : t0, Ln, SPEC_WAVE);
-        } else {
-          x = acc.idx;
+        } else {  // cannot happen: the tile's largest token has weight
+          x = first_max_token(wmax);
         }
       }
     }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     a.tokens[(size_t)j * a.G + k] = (st == 0) ? x : -1;
     a.req_status[j] = st;
   }
 }
 
-// After the last step: status, the tokens of bad requests, and the confidences (Eq. 7).
+// After the last step: status, the tokens of bad requests, and the confidences (Eq. 7), one
+// wave per (request, position), fp64 dot products.
 template <int ES>
 __global__ __launch_bounds__(kSampleThreads) void markov_finish_kernel(DraftArgs a) {
   const int lane = threadIdx.x & 63;
@@ -398,12 +555,42 @@ __global__ __launch_bounds__(kSampleThreads) void markov_finish_kernel(DraftArgs
   }
   if (!a.conf) return;
   const int prev = (k == 0) ? a.anchor[j] : a.tokens[wid - 1];
+  const int d = a.d;
   double t = 0.0;
-  for (int i = lane; i < a.d; i += 64)
-    t += (double)a.conf_w[i] * (double)load_logit<ES>(a.hidden, wid * (size_t)a.d + i);
-  const uint16_t* e = a.W1 + (size_t)prev * a.r;
-  for (int i = lane; i < a.r; i += 64)
-    t += (double)a.conf_w[a.d + i] * (double)__uint_as_float((uint32_t)e[i] << 16);
+  constexpr int VE = 16 / ES;  // elements per 16-byte vector
+  const char* hrow = reinterpret_cast<const char*>(a.hidden) + wid * (size_t)d * ES;
+  if ((d % VE) == 0 && ((reinterpret_cast<uintptr_t>(hrow) & 15) == 0)) {
+    for (int v = lane; v < d / VE; v += 64) {
+      const v4u32 q = *reinterpret_cast<const v4u32*>(hrow + (size_t)v * 16);
+      const float* wp = a.conf_w + v * VE;
+      if constexpr (ES == 2) {
+        const uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          t += (double)wp[2 * i] * (double)bf16_lo(qs[i]);
+          t += (double)wp[2 * i + 1] * (double)bf16_hi(qs[i]);
+        }
+      } else {
+        t += (double)wp[0] * (double)__uint_as_float(q.x);
+        t += (double)wp[1] * (double)__uint_as_float(q.y);
+        t += (double)wp[2] * (double)__uint_as_float(q.z);
+        t += (double)wp[3] * (double)__uint_as_float(q.w);
+      }
+    }
+  } else {
+    for (int i = lane; i < d; i += 64) t += (double)a.conf_w[i] * (double)load_logit<ES>(a.hidden, wid * (size_t)d + i);
+  }
+  const uint16_t* e = a.W1 + (size_t)prev * a.r;  // rows are 16-byte aligned (r % 16 == 0)
+  for (int v = lane; v < a.r / 8; v += 64) {
+    const v4u32 q = *reinterpret_cast<const v4u32*>(e + v * 8);
+    const float* wp = a.conf_w + d + v * 8;
+    const uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t += (double)wp[2 * i] * (double)bf16_lo(qs[i]);
+      t += (double)wp[2 * i + 1] * (double)bf16_hi(qs[i]);
+    }
+  }
   t = wave_sum(t);
   if (lane == 0) a.conf[wid] = (float)(1.0 / (1.0 + exp(-t)));
 }
@@ -464,7 +651,7 @@ extern "C" int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_
   a.part = reinterpret_cast<DPart*>(ws);
   a.req_status = reinterpret_cast<int32_t*>(ws + align256((size_t)B * a.nwg * sizeof(DPart)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const unsigned sgrid = (unsigned)((B + 3) / 4);
+  const unsigned sgrid = (unsigned)B;
   for (int k = 0; k < gamma; ++k) {
     a.k = k;
     if (dtype == SPEC_BF16) {
