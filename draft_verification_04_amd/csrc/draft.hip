@@ -156,22 +156,32 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
 }
 
 // Step k: draft logits z_k = U_k + W1[x_{k-1}] W2 for every request, and per-tile statistics.
-// Per request block, the MFMA chain runs on operands loaded during the previous block, and the
-// epilogue works on U_k values loaded during the previous block too, so HBM and L2 latency overlap
-// the chain and the epilogue.  Operand steps beyond r/16 are zero on both sides (exact zeros).
+//
+// A workgroup owns 128 tokens (32 per wave) and walks the requests 32 at a time.  Per request
+// block: the MFMA chain multiplies the wave's projection rows (registers) by the block's embedding
+// rows (LDS); the epilogue reads U_k from an LDS tile, writes the rounded z_k back in place and
+// folds the values into statistics; after the block's barrier the workgroup stores the z_k tile
+// with whole-line 16-byte stores.  The embedding rows and the U_k tile of the next block are
+// loaded (whole lines, 16 bytes per thread) while the current block computes.  Tiles that are not
+// whole (the last one, or rows not 16-byte aligned) take per-element global accesses instead.
+// Operand steps beyond r/16 are zero on both sides (exact zeros).
 template <int ES>
 __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs a) {
-  constexpr int UW = ES == 2 ? 2 : 4;  // 32-bit words per group of 4 logits
-  constexpr int RS = kMaxSteps * 16 + 8;  // LDS row stride of the embedding rows (bf16; +16 B breaks bank aliasing)
+  constexpr int RS = kMaxSteps * 16 + 8;            // LDS row stride of the embedding rows (bf16)
+  constexpr int USB = kTileTokens * ES + 16;        // LDS row stride of the U/z tile (bytes)
+  constexpr int UCPR = kTileTokens * ES / 16;       // 16-byte chunks per tile row
+  constexpr int UPT = kReqBlock * UCPR / kDraftThreads;  // chunks per thread (2 bf16, 4 fp32)
   __shared__ Stat sp[2][kDraftThreads / 64][kReqBlock];
   __shared__ double tab[64];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kReqBlock * RS];
+  __shared__ __attribute__((aligned(16))) unsigned char sU[3][kReqBlock * USB];
   __shared__ int sPrev[2][kReqBlock];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int tl = lane & 31, h = lane >> 5;
   const int V = a.V, r = a.r, G = a.G, k = a.k, B = a.B;
   const int nk = r >> 4;
-  const int n0 = blockIdx.x * kTileTokens + wv * 32;
+  const int tile0 = blockIdx.x * kTileTokens;
+  const int n0 = tile0 + wv * 32;
   const bf16x8 zero8 = {};
   if (tid < 64) tab[tid] = exp2((double)tid * 0.015625);
 
@@ -192,10 +202,9 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
     const int p = prevp[(size_t)min(j, B - 1) * pstride];
     return (p < 0 || p >= V) ? 0 : p;
   };
-  // The embedding rows W1[x_{k-1}] of a request block go to LDS once per workgroup: 32 rows of
-  // r bf16, 16-byte chunks, consecutive threads on consecutive chunks of a row.
-  const int cpr = r >> 3;                  // 16-byte chunks per row
-  const int nchunk = kReqBlock * cpr;      // <= 1024: at most 4 per thread
+  // Embedding rows W1[x_{k-1}] of a request block: 32 rows of r bf16, 16-byte chunks.
+  const int cpr = r >> 3;
+  const int nchunk = kReqBlock * cpr;  // <= 1024: at most 4 per thread
   v4u32 gw[4];
   auto load_rows = [&](int pb) {
 #pragma unroll
@@ -217,21 +226,40 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       }
     }
   };
-  const bool fast_tile = ((V & 3) == 0) && (n0 + 32 <= V);
-  auto load_u = [&](int j, uint32_t (&ur)[4][UW]) {
-    const size_t row = ((size_t)j * G + k) * V;
+  // U_k tile of a request block (whole tiles only): row = request, 16-byte chunks.
+  const bool fast_tile = (((size_t)V * ES) % 16 == 0) && (tile0 + kTileTokens <= V);
+  const size_t rowstep = (size_t)G * V;  // elements between consecutive requests' rows
+  const char* ubase = reinterpret_cast<const char*>(a.base) + ((size_t)k * V + tile0) * ES;
+  char* zbase = reinterpret_cast<char*>(a.logits) + ((size_t)k * V + tile0) * ES;
+  v4u32 gu[UPT];
+  auto load_tile = [&](int rb) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int t0 = n0 + 8 * g + 4 * h;
-      if constexpr (ES == 2) {
-        const v2u32 w = __builtin_nontemporal_load(
-            reinterpret_cast<const v2u32*>(reinterpret_cast<const uint16_t*>(a.base) + row + t0));
-        ur[g][0] = w.x; ur[g][1] = w.y;
-      } else {
-        const v4u32 w = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u32*>(reinterpret_cast<const float*>(a.base) + row + t0));
-        ur[g][0] = w.x; ur[g][1] = w.y; ur[g][2] = w.z; ur[g][3] = w.w;
-      }
+    for (int i = 0; i < UPT; ++i) {
+      const int c = tid + i * kDraftThreads;
+      const int row = c / UCPR, col = c - row * UCPR;
+      const int j = rb * kReqBlock + row;
+      if (j < B)
+        gu[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u32*>(ubase + (size_t)j * rowstep * ES + col * 16));
+    }
+  };
+  auto store_tile_lds = [&](int ub) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int c = tid + i * kDraftThreads;
+      const int row = c / UCPR, col = c - row * UCPR;
+      *reinterpret_cast<v4u32*>(&sU[ub][row * USB + col * 16]) = gu[i];
+    }
+  };
+  auto store_tile_global = [&](int rb, int ub) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int c = tid + i * kDraftThreads;
+      const int row = c / UCPR, col = c - row * UCPR;
+      const int j = rb * kReqBlock + row;
+      if (j < B)
+        *reinterpret_cast<v4u32*>(zbase + (size_t)j * rowstep * ES + col * 16) =
+            *reinterpret_cast<const v4u32*>(&sU[ub][row * USB + col * 16]);
     }
   };
 
@@ -240,21 +268,23 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
     sPrev[0][tid] = prev_of(tid);
     sPrev[1][tid] = prev_of(tid + kReqBlock);
   }
-  uint32_t ucur[4][UW], unext[4][UW];
-  if (fast_tile && tl < B) load_u(tl, ucur);
+  if (fast_tile) load_tile(0);
   __syncthreads();  // tab, sPrev
   load_rows(0);
   store_rows(0);
+  if (fast_tile) store_tile_lds(0);
   __syncthreads();
 
   for (int rb = 0; rb < nrb; ++rb) {
     const int j = rb * kReqBlock + tl;
     const bool valid = j < B;
-    const bool fast = valid && fast_tile;
-    const int buf = rb & 1;
+    const int buf = rb & 1, ub = rb % 3;
     const float T = a.temperature[min(j, B - 1)];
     const bool more = rb + 1 < nrb;
-    if (more) load_rows(buf ^ 1);        // rows of block rb + 1 (their ids were stored a block ago)
+    if (more) {
+      load_rows(buf ^ 1);                 // rows of block rb + 1 (their ids were stored a block ago)
+      if (fast_tile) load_tile(rb + 1);
+    }
     int pn2 = 0;
     if (tid < kReqBlock) pn2 = prev_of((rb + 2) * kReqBlock + tid);
 
@@ -266,75 +296,61 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(rowp + min(kk, nk - 1) * 16));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kk], kk < nk ? b : zero8, acc, 0, 0, 0);
     }
-    if (fast_tile && j + kReqBlock < B) load_u(j + kReqBlock, unext);
 
     // Epilogue: lane holds D[token n0 + 8g + 4h + p][request j] in acc[4g + p].
     const size_t row = ((size_t)(valid ? j : 0) * G + k) * V;
+    unsigned char* urow = &sU[ub][tl * USB + (wv * 32 + 4 * h) * ES];
     float zq[16];
     int bad = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int t0 = n0 + 8 * g + 4 * h;
-      float u[4];
-      if (fast) {
-        if constexpr (ES == 2) {
-          u[0] = bf16_lo(ucur[g][0]); u[1] = bf16_hi(ucur[g][0]); u[2] = bf16_lo(ucur[g][1]); u[3] = bf16_hi(ucur[g][1]);
-        } else {
-#pragma unroll
-          for (int p = 0; p < 4; ++p) u[p] = __uint_as_float(ucur[g][p]);
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) u[p] = (valid && t0 + p < V) ? load_logit<ES>(a.base, row + t0 + p) : 0.f;
-      }
       float zs[4];
-      uint32_t wd[2];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) zs[p] = u[p] + acc[4 * g + p];
-      if constexpr (ES == 2) {
-        // round to nearest even (hardware conversion), keep the stored values
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const f32x2 v = {zs[2 * q], zs[2 * q + 1]};
-          wd[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-          zs[2 * q] = bf16_lo(wd[q]);
-          zs[2 * q + 1] = bf16_hi(wd[q]);
-        }
-      }
-      if (fast) {
+      if (fast_tile) {
+        unsigned char* q = urow + 8 * g * ES;
         if constexpr (ES == 2) {
-          uint2 w;
-          w.x = wd[0];
-          w.y = wd[1];
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.logits) + row + t0) = w;
+          const uint2 w = *reinterpret_cast<const uint2*>(q);
+          zs[0] = bf16_lo(w.x) + acc[4 * g];
+          zs[1] = bf16_hi(w.x) + acc[4 * g + 1];
+          zs[2] = bf16_lo(w.y) + acc[4 * g + 2];
+          zs[3] = bf16_hi(w.y) + acc[4 * g + 3];
+          uint2 o;
+          const f32x2 v0 = {zs[0], zs[1]}, v1 = {zs[2], zs[3]};
+          o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2));
+          o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2));
+          *reinterpret_cast<uint2*>(q) = o;
+          zs[0] = bf16_lo(o.x); zs[1] = bf16_hi(o.x); zs[2] = bf16_lo(o.y); zs[3] = bf16_hi(o.y);
         } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.logits) + row + t0) =
-              make_float4(zs[0], zs[1], zs[2], zs[3]);
+          const float4 w = *reinterpret_cast<const float4*>(q);
+          zs[0] = w.x + acc[4 * g];
+          zs[1] = w.y + acc[4 * g + 1];
+          zs[2] = w.z + acc[4 * g + 2];
+          zs[3] = w.w + acc[4 * g + 3];
+          *reinterpret_cast<float4*>(q) = make_float4(zs[0], zs[1], zs[2], zs[3]);
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          zq[4 * g + p] = zs[p];
-          bad |= __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
+          zq[4 * g + p] = valid ? zs[p] : -__builtin_inff();
+          bad |= valid && __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
         }
       } else {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const bool in = valid && t0 + p < V;
-          if (in) {
-            if constexpr (ES == 2)
-              reinterpret_cast<uint16_t*>(a.logits)[row + t0 + p] = (uint16_t)(__float_as_uint(zs[p]) >> 16);
-            else
-              reinterpret_cast<float*>(a.logits)[row + t0 + p] = zs[p];
+          float z = (in ? load_logit<ES>(a.base, row + t0 + p) : 0.f) + acc[4 * g + p];
+          if constexpr (ES == 2) {
+            const f32x2 v = {z, 0.f};
+            const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+            z = bf16_lo(o);
+            if (in) reinterpret_cast<uint16_t*>(a.logits)[row + t0 + p] = (uint16_t)o;
+          } else {
+            if (in) reinterpret_cast<float*>(a.logits)[row + t0 + p] = z;
           }
-          zq[4 * g + p] = in ? zs[p] : -__builtin_inff();
-          bad |= in && __builtin_amdgcn_classf(zs[p], 0x203);
+          zq[4 * g + p] = in ? z : -__builtin_inff();
+          bad |= in && __builtin_amdgcn_classf(z, 0x203);
         }
       }
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int q = 0; q < UW; ++q) ucur[g][q] = unext[g][q];
     Stat st = stat_empty();
     st.bad = bad;
     float zm = zq[0];
@@ -353,9 +369,13 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
     // the two lane halves hold the same request
     stat_merge(st, stat_shfl_xor(st, 32));
     if (h == 0) sp[buf][wv][tl] = st;
-    if (more) store_rows(buf ^ 1);                 // read after the barrier below
-    if (tid < kReqBlock) sPrev[buf][tid] = pn2;    // ids of block rb + 2
+    if (more) {
+      store_rows(buf ^ 1);                            // read after the barrier below
+      if (fast_tile) store_tile_lds((rb + 1) % 3);
+    }
+    if (tid < kReqBlock) sPrev[buf][tid] = pn2;       // ids of block rb + 2
     __syncthreads();
+    if (fast_tile) store_tile_global(rb, ub);
     if (wv == 0 && h == 0 && valid) {
       Stat t = sp[buf][0][tl];
 #pragma unroll
