@@ -24,6 +24,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "philox.hpp"
 #include "spec_verify.h"
@@ -198,10 +200,9 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
   // not defined)
   const int* prevp = (k == 0) ? a.anchor : a.tokens + (k - 1);
   const int pstride = (k == 0) ? 1 : G;
-  auto prev_of = [&](int j) -> int {
-    const int p = prevp[(size_t)min(j, B - 1) * pstride];
-    return (p < 0 || p >= V) ? 0 : p;
-  };
+  auto prev_raw = [&](int j) -> int { return prevp[(size_t)min(j, B - 1) * pstride]; };
+  auto prev_ok = [&](int p) -> int { return (p < 0 || p >= V) ? 0 : p; };
+  auto prev_of = [&](int j) -> int { return prev_ok(prev_raw(j)); };
   // Embedding rows W1[x_{k-1}] of a request block: 32 rows of r bf16, 16-byte chunks.
   const int cpr = r >> 3;
   const int nchunk = kReqBlock * cpr;  // <= 1024: at most 4 per thread
@@ -285,21 +286,31 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       load_rows(buf ^ 1);                 // rows of block rb + 1 (their ids were stored a block ago)
       if (fast_tile) load_tile(rb + 1);
     }
-    int pn2 = 0;
-    if (tid < kReqBlock) pn2 = prev_of((rb + 2) * kReqBlock + tid);
+    int pn2 = 0;  // wave 1 fetches the ids of block rb + 2; clamped when stored
+    const bool idw = tid >= 64 && tid < 64 + kReqBlock;
+    if (idw) pn2 = prev_raw((rb + 2) * kReqBlock + tid - 64);
+    // this lane's U_k values of the current block (stored in LDS before the last barrier)
+    unsigned char* urow = &sU[ub][tl * USB + (wv * 32 + 4 * h) * ES];
+    typedef typename std::conditional<ES == 2, uint2, float4>::type UVec;
+    UVec uv[4];
+    if (fast_tile) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) uv[g] = *reinterpret_cast<const UVec*>(urow + 8 * g * ES);
+    }
 
     // Embedding operand (MFMA B: column = request, 8 consecutive k per lane half) from LDS.
     const uint16_t* rowp = &sB[buf][tl * RS + 8 * h];
+    bf16x8 bop[kMaxSteps];  // every step's operand is read before the chain: the reads overlap
+#pragma unroll
+    for (int kk = 0; kk < kMaxSteps; ++kk)
+      bop[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(rowp + min(kk, nk - 1) * 16));
     f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < kMaxSteps; ++kk) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(rowp + min(kk, nk - 1) * 16));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kk], kk < nk ? b : zero8, acc, 0, 0, 0);
-    }
+    for (int kk = 0; kk < kMaxSteps; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kk], kk < nk ? bop[kk] : zero8, acc, 0, 0, 0);
 
     // Epilogue: lane holds D[token n0 + 8g + 4h + p][request j] in acc[4g + p].
     const size_t row = ((size_t)(valid ? j : 0) * G + k) * V;
-    unsigned char* urow = &sU[ub][tl * USB + (wv * 32 + 4 * h) * ES];
     float zq[16];
     int bad = 0;
 #pragma unroll
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       if (fast_tile) {
         unsigned char* q = urow + 8 * g * ES;
         if constexpr (ES == 2) {
-          const uint2 w = *reinterpret_cast<const uint2*>(q);
+          const uint2 w = uv[g];
           zs[0] = bf16_lo(w.x) + acc[4 * g];
           zs[1] = bf16_hi(w.x) + acc[4 * g + 1];
           zs[2] = bf16_lo(w.y) + acc[4 * g + 2];
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
           *reinterpret_cast<uint2*>(q) = o;
           zs[0] = bf16_lo(o.x); zs[1] = bf16_hi(o.x); zs[2] = bf16_lo(o.y); zs[3] = bf16_hi(o.y);
         } else {
-          const float4 w = *reinterpret_cast<const float4*>(q);
+          const float4 w = uv[g];
           zs[0] = w.x + acc[4 * g];
           zs[1] = w.y + acc[4 * g + 1];
           zs[2] = w.z + acc[4 * g + 2];
@@ -373,10 +384,10 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       store_rows(buf ^ 1);                            // read after the barrier below
       if (fast_tile) store_tile_lds((rb + 1) % 3);
     }
-    if (tid < kReqBlock) sPrev[buf][tid] = pn2;       // ids of block rb + 2
+    if (idw) sPrev[buf][tid - 64] = prev_ok(pn2);    // ids of block rb + 2
     __syncthreads();
     if (fast_tile) store_tile_global(rb, ub);
-    if (wv == 0 && h == 0 && valid) {
+    if (wv == 3 && h == 0 && valid) {
       Stat t = sp[buf][0][tl];
 #pragma unroll
       for (int w = 1; w < kDraftThreads / 64; ++w) stat_merge(t, sp[buf][w][tl]);
