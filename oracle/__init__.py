@@ -23,6 +23,9 @@ from the DSpark pages:
   * `markov_draft`  -- the Markov-head sequential draft sampler and the
                        confidence head (DSpark paper, §3.1 Eq. 4-5, §3.2.1
                        Eq. 7);
+  * `sts_fit`, `sts_apply` -- Sequential Temperature Scaling of the
+                       confidences (DSpark paper, §3.2.1, post-hoc
+                       calibration);
   * `philox`        -- the counter-based generator the draws come from
                        (Philox4x64-10, Salmon et al., SC'11).
 
@@ -47,6 +50,7 @@ from .verification import (  # noqa: F401
 )
 from .overlap import overlap_mass  # noqa: F401
 from .drafting import markov_draft, round_bf16  # noqa: F401
+from .calibration import ece, sts_apply, sts_fit  # noqa: F401
 from .scheduling import (  # noqa: F401
     capacity,
     survival,

@@ -23,7 +23,9 @@ k = 1 .. G in order:
      u the draft uniform of (i, k) from `oracle.philox.draft_uniform`);
      T = 0: x_k = the first-occurrence argmax of the stored z_k;
   4. c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]) (Eq. 7) when the head's weight w
-     is given (with no hidden states, d = 0, the h_k part is empty).
+     is given (with no hidden states, d = 0, the h_k part is empty); with
+     per-position temperatures tau_k from Sequential Temperature Scaling
+     (§3.2.1) the calibrated c_k = sigmoid(w . [...] / tau_k).
 
 Status (request-wide, as in `verify`): bad temperature (NaN, negative,
 infinite), bad token (anchor outside [0, V)), non-finite (a stored row with
@@ -107,7 +109,7 @@ def _greedy_ambiguous(z, zlo, zhi, amb):
 
 
 def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None, conf_w=None,
-                 store="bf16", acc_err_unit=None, requests=None):
+                 store="bf16", acc_err_unit=None, requests=None, conf_tau=None):
     """Draft G tokens per request (see the module docstring).
 
     base [B, G, V] (U); W1 [V, r]; W2t [V, r]; anchor [B]; temperature [B] (default 1);
@@ -115,7 +117,8 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
     when d = 0; no confidences without conf_w); store "bf16" | "fp32"; acc_err_unit: unit
     roundoff u of the arithmetic being compared (None: no ambiguity), the bound per element
     being (r + 2) u (sum_j |W1 W2t| + |U|).
-    `requests` restricts the work to a subset (others keep status 0, tokens -1).
+    `requests` restricts the work to a subset (others keep status 0, tokens -1); conf_tau [G]
+    the per-position temperatures of the confidences (default 1).
 
     Returns a dict: tokens [B, G] int64, logits [B, G, V] fp64 (stored values; NaN where not
     computed), amb_lo / amb_hi [B, G, V] (the range of possible stored values of ambiguous
@@ -135,6 +138,7 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
         Ss = s.view(np.uint64) if s.dtype == np.int64 else s.astype(np.uint64)
     H = None if hidden is None else hidden
     wc = None if conf_w is None else _as_np(conf_w).astype(np.float64)
+    ctau = np.ones(G) if conf_tau is None else _as_np(conf_tau).astype(np.float64)
     tokens = np.full((B, G), -1, dtype=np.int64)
     logits = np.full((B, G, V), np.nan)
     amb_lo = np.full((B, G, V), np.nan)
@@ -179,7 +183,7 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
                 t = float(wc[dh:] @ a)                                       # Eq. 7
                 if dh:
                     t += float(wc[:dh] @ h[k])
-                conf[i, k] = 1.0 / (1.0 + np.exp(-t))
+                conf[i, k] = 1.0 / (1.0 + np.exp(-t / ctau[k]))
             if T == 0.0:
                 xk = int(np.argmax(z))
                 flag[i, k] = bool(amb.any()) and _greedy_ambiguous(z, zlo, zhi, amb)

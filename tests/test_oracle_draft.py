@@ -130,6 +130,24 @@ def test_confidence_head_without_hidden_states():
     assert np.allclose(out["conf"], expit(W1[prev, 3]), rtol=1e-15, atol=0)
 
 
+def test_confidence_temperatures():
+    """Per-position temperatures divide the head's logit: conf(tau) = sigmoid(logit(conf(1)) / tau)."""
+    rng = np.random.default_rng(12)
+    B, G, V, r, d = 4, 3, 50, 16, 8
+    U = round_bf16(rng.normal(0, 2, (B, G, V)))
+    W1 = round_bf16(rng.normal(0, 1, (V, r)))
+    W2t = round_bf16(rng.normal(0, 0.1, (V, r)))
+    h = rng.normal(0, 1, (B, G, d))
+    w = rng.normal(0, 0.5, d + r)
+    kw = dict(seed=np.arange(B, dtype=np.uint64), hidden=h, conf_w=w)
+    plain = markov_draft(U, W1, W2t, np.arange(B), **kw)
+    tau = np.array([2.0, 0.5, 1.3])
+    cal = markov_draft(U, W1, W2t, np.arange(B), conf_tau=tau, **kw)
+    assert np.array_equal(plain["tokens"], cal["tokens"])
+    t = np.log(plain["conf"] / (1 - plain["conf"]))
+    assert np.allclose(cal["conf"], expit(t / tau), rtol=1e-12, atol=0)
+
+
 def test_confidence_head_picks_concatenation_parts():
     """Eq. 7 with w a basis vector: c_k = sigmoid(h_k[j]) for j < d, and
     sigmoid(W1[x_{k-1}, j - d]) beyond (x_0 = the anchor), against scipy's expit."""
