@@ -44,8 +44,7 @@ def ece(a, y, bins=DEFAULT_BINS):
     if np.isnan(a).any():
         return np.nan
     b = np.minimum(np.floor(a * bins), bins - 1).astype(np.int64)
-    s = np.zeros(bins)
-    np.add.at(s, b, a - y)
+    s = np.bincount(b, weights=a - y, minlength=bins)      # per-bin sums of (a - y)
     return float(np.abs(s).sum() / len(a))
 
 
