@@ -60,8 +60,11 @@ EXPORTS = {
     "spec_schedule_topk": (_I, [_I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_overlap_mass": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_draft_workspace_size": (_Z, [_I, _I, _I]),
-    "spec_draft_markov": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z,
-                               _P]),
+    "spec_draft_markov": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _Z, _P]),
+    "spec_sts_workspace_size": (_Z, [_I, _I, _I]),
+    "spec_sts_fit": (_I, [_I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
+    "spec_sts_apply": (_I, [_I, _I, _P, _P, _P, _P]),
 }
 
 _lib_handle = None
@@ -312,13 +315,14 @@ def draft_markov(base: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, anchor
                  temperature: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
                  hidden: Optional[torch.Tensor] = None, conf_w: Optional[torch.Tensor] = None,
                  out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-                 in_place: bool = False) -> dict:
+                 in_place: bool = False, conf_tau: Optional[torch.Tensor] = None) -> dict:
     """spec_draft_markov on torch tensors.  Returns dict(tokens, logits, conf, status).
 
     base [B, gamma, V] (float32 or bfloat16); W1 and W2t [V, r] bfloat16 (W2t row v = column v of
     the r x V projection); anchor [B] int32; temperature [B] float32 (default ones); seed [B] int64
     (uint64 bit patterns, default zeros); hidden [B, gamma, d] (base's dtype) and conf_w [d + r]
-    float32 for the confidences (conf_w alone when d = 0).  in_place writes the draft logits over
+    float32 for the confidences (conf_w alone when d = 0); conf_tau [gamma] float64 per-position
+    temperatures of the confidences (sts_fit's output).  in_place writes the draft logits over
     `base`.
     """
     lib = load_library()
@@ -345,6 +349,10 @@ def draft_markov(base: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, anchor
         _dev(conf_w, "conf_w", torch.float32, 1)
         if conf_w.numel() != d + r:
             raise ValueError("conf_w must hold d + r values")
+    if conf_tau is not None:
+        _dev(conf_tau, "conf_tau", torch.float64, 1)
+        if conf_tau.numel() != G:
+            raise ValueError("conf_tau must hold gamma values")
     if out is None:
         out = dict(tokens=torch.empty((B, G), dtype=torch.int32, device=dev),
                    logits=base if in_place else torch.empty_like(base),
@@ -353,10 +361,50 @@ def draft_markov(base: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, anchor
     nbytes = int(lib.spec_draft_workspace_size(B, G, V))
     ws = _workspace(nbytes, dev, workspace)
     code = lib.spec_draft_markov(B, G, V, r, _logit_dtype(base), _ptr(base), _ptr(W1), _ptr(W2t), _ptr(anchor),
-                                 _ptr(temperature), _ptr(seed), d, _ptr(hidden), _ptr(conf_w), _ptr(out["tokens"]),
+                                 _ptr(temperature), _ptr(seed), d, _ptr(hidden), _ptr(conf_w), _ptr(conf_tau),
+                                 _ptr(out["tokens"]),
                                  _ptr(out["logits"]), _ptr(out.get("conf")), _ptr(out["status"]), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_draft_markov", code)
+    return out
+
+
+def sts_fit(conf_logits: torch.Tensor, labels: torch.Tensor, taus: torch.Tensor, bins: int = 15,
+            out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """spec_sts_fit: conf_logits [N, gamma] float32, labels [N, gamma] uint8, taus [ntau] float64.
+    Returns dict(tau [gamma] float64, index [gamma] int32, ece [gamma, ntau] float64)."""
+    lib = load_library()
+    _dev(conf_logits, "conf_logits", torch.float32, 2)
+    _dev(labels, "labels", torch.uint8, 2)
+    _dev(taus, "taus", torch.float64, 1)
+    N, G = conf_logits.shape
+    if tuple(labels.shape) != (N, G):
+        raise ValueError("labels must be [N, gamma]")
+    ntau = taus.numel()
+    dev = conf_logits.device
+    if out is None:
+        out = dict(tau=torch.empty(G, dtype=torch.float64, device=dev),
+                   index=torch.empty(G, dtype=torch.int32, device=dev),
+                   ece=torch.empty((G, ntau), dtype=torch.float64, device=dev))
+    nbytes = int(lib.spec_sts_workspace_size(N, ntau, bins))
+    ws = _workspace(nbytes, dev, workspace)
+    code = lib.spec_sts_fit(N, G, _ptr(conf_logits), _ptr(labels), ntau, _ptr(taus), bins, _ptr(out["tau"]),
+                            _ptr(out.get("index")), _ptr(out.get("ece")), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _check("spec_sts_fit", code)
+    return out
+
+
+def sts_apply(conf_logits: torch.Tensor, tau: torch.Tensor, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """spec_sts_apply: sigmoid(conf_logits / tau) per position, float32 [B, gamma]."""
+    lib = load_library()
+    _dev(conf_logits, "conf_logits", torch.float32, 2)
+    _dev(tau, "tau", torch.float64, 1)
+    B, G = conf_logits.shape
+    if out is None:
+        out = torch.empty_like(conf_logits)
+    _check("spec_sts_apply", lib.spec_sts_apply(B, G, _ptr(conf_logits), _ptr(tau), _ptr(out), _stream(stream)))
     return out
 
 

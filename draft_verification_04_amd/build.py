@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 
-SOURCES = ["verify.hip", "emit.hip", "schedule.hip", "overlap.hip", "draft.hip", "measure.hip", "api.cpp"]
+SOURCES = ["verify.hip", "emit.hip", "schedule.hip", "overlap.hip", "draft.hip", "calibrate.hip", "measure.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",

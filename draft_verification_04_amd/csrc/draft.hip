@@ -71,6 +71,7 @@ struct DraftArgs {
   const uint64_t* seed;      // [B] or null (all 0)
   const void* hidden;        // [B, G, d] or null
   const float* conf_w;       // [d + r] or null
+  const double* conf_tau;    // [G] per-position temperatures of the confidences, or null (1)
   int32_t* tokens;           // [B, G]
   void* logits;              // [B, G, V]
   float* conf;               // [B, G] or null
@@ -623,6 +624,7 @@ __global__ __launch_bounds__(kSampleThreads) void markov_finish_kernel(DraftArgs
     }
   }
   t = wave_sum(t);
+  if (a.conf_tau) t /= a.conf_tau[k];
   if (lane == 0) a.conf[wid] = (float)(1.0 / (1.0 + exp(-t)));
 }
 
@@ -658,7 +660,8 @@ extern "C" size_t spec_draft_workspace_size(int32_t B, int32_t gamma, int32_t V)
 extern "C" int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t dtype,
                                      const void* base_logits, const void* W1, const void* W2t,
                                      const int32_t* anchor, const float* temperature, const uint64_t* seed,
-                                     int32_t d, const void* hidden, const float* conf_w, int32_t* tokens,
+                                     int32_t d, const void* hidden, const float* conf_w, const double* conf_tau,
+                                     int32_t* tokens,
                                      void* draft_logits, float* conf, int32_t* status, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   if (!draft_shape_ok(B, gamma, V, r, d, dtype)) return SPEC_ERR_INVALID_ARG;
@@ -676,7 +679,7 @@ extern "C" int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_
   a.W1 = reinterpret_cast<const uint16_t*>(W1);
   a.W2t = reinterpret_cast<const uint16_t*>(W2t);
   a.anchor = anchor; a.temperature = temperature; a.seed = seed;
-  a.hidden = hidden; a.conf_w = conf_w;
+  a.hidden = hidden; a.conf_w = conf_w; a.conf_tau = conf_tau;
   a.tokens = tokens; a.logits = draft_logits; a.conf = conf; a.status = status;
   char* ws = reinterpret_cast<char*>(workspace);
   a.part = reinterpret_cast<DPart*>(ws);

@@ -18,7 +18,9 @@
  *                               translation; the no-break search of §5.2);
  *   - spec_draft_markov      -- the draft block itself: the Markov-head
  *                               sequential sampler and the confidence head
- *                               (paper §3.1, §3.2.1).
+ *                               (paper §3.1, §3.2.1);
+ *   - spec_sts_fit / _apply  -- Sequential Temperature Scaling of the
+ *                               confidences (paper §3.2.1).
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
@@ -321,7 +323,9 @@ int32_t spec_overlap_mass(int32_t B, int32_t gamma, int32_t V, int32_t dtype, co
  *         (k + 1, i, 1, 0) under key (seed_i, 0), as (w >> 11) * 2^-53 (the
  *         verifier's draws use counter word 2 = 0, so one seed may key both);
  *         T_i = 0: the first-occurrence argmax of z_k;
- *   conf_k = sigmoid(w . [h_k ; W1[x_{k-1}]])  (Eq. 7), when `conf` is given.
+ *   conf_k = sigmoid(w . [h_k ; W1[x_{k-1}]] / tau_k)  (Eq. 7; tau_k the
+ *         per-position temperature of Sequential Temperature Scaling, §3.2.1,
+ *         1 without conf_tau), when `conf` is given.
  * The stored draft_logits rows ARE the draft distribution: hand them to
  * spec_verify (with the same temperatures and top_k = 0) and the pair is
  * lossless.  Sums are fp64 (exponentials evaluated in fp64 against exact
@@ -342,7 +346,9 @@ int32_t spec_overlap_mass(int32_t B, int32_t gamma, int32_t V, int32_t dtype, co
  *   seed          [B] uint64 device, or NULL for all 0
  *   hidden        [B, gamma, d] device (dtype) or NULL when d = 0; conf_w
  *                 [d + r] float32 device: the confidence head's weight, the
- *                 first d entries against h_k; both ignored when conf = NULL
+ *                 first d entries against h_k; conf_tau [gamma] float64
+ *                 device or NULL (spec_sts_fit's output); all ignored when
+ *                 conf = NULL
  * Outputs (device)
  *   tokens        [B, gamma] int32: x_k (all -1 for a request with a status)
  *   draft_logits  [B, gamma, V] dtype: the stored z_k (may be base_logits
@@ -366,9 +372,51 @@ size_t spec_draft_workspace_size(int32_t B, int32_t gamma, int32_t V);
 int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t dtype,
                           const void* base_logits, const void* W1, const void* W2t,
                           const int32_t* anchor, const float* temperature, const uint64_t* seed,
-                          int32_t d, const void* hidden, const float* conf_w, int32_t* tokens,
+                          int32_t d, const void* hidden, const float* conf_w, const double* conf_tau,
+                          int32_t* tokens,
                           void* draft_logits, float* conf, int32_t* status, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * spec_sts_fit -- Sequential Temperature Scaling of the confidence head (DSpark
+ * paper, §3.2.1, post-hoc calibration).  Per position k = 0 .. gamma-1 in
+ * order, tau_k = the first grid value minimising the Expected Calibration
+ * Error of the survival product a_k = prod_{i<=k} sigmoid(t_i / tau_i) over
+ * the N held-out instances, the temperatures of earlier positions fixed.
+ * ECE = (1/N) sum over `bins` equal-width bins of |sum_{n in bin} (a_n - y_n)|,
+ * a value a falling in bin min(floor(a * bins), bins - 1).  Sums are fp64 in a
+ * fixed order (the result does not depend on scheduling).
+ *
+ * Arguments (device pointers)
+ *   1 <= N <= 2^26, 1 <= gamma <= SPEC_MAX_GAMMA, 1 <= ntau <= 4096, 1 <= bins <= 32
+ *   conf_logits [N, gamma] float32: the head's logits t (before the sigmoid)
+ *   labels      [N, gamma] uint8: nonzero when draft positions 0 .. k of the
+ *               instance were all accepted (the event a_k predicts)
+ *   taus        [ntau] float64: the grid (any values; a NaN result never wins)
+ * Outputs (device)
+ *   tau_out     [gamma] float64: tau_k (NaN when every ECE of position k is
+ *               NaN -- a NaN logit makes its position's ECE NaN)
+ *   index_out   [gamma] int32 or NULL: the grid index (-1 for NaN)
+ *   ece_out     [gamma, ntau] float64 or NULL: the ECE of every grid value
+ *   workspace   at least spec_sts_workspace_size(N, ntau, bins) bytes,
+ *               256-byte aligned, owned by the caller.
+ * Enqueues 4 gamma + 1 kernels on `stream`.  Errors: SPEC_ERR_INVALID_ARG,
+ * SPEC_ERR_WORKSPACE.
+ */
+size_t spec_sts_workspace_size(int32_t N, int32_t ntau, int32_t bins);
+
+int32_t spec_sts_fit(int32_t N, int32_t gamma, const float* conf_logits, const uint8_t* labels, int32_t ntau,
+                     const double* taus, int32_t bins, double* tau_out, int32_t* index_out, double* ece_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_sts_apply -- calibrated confidences conf_out[i, k] = sigmoid(t[i, k] /
+ * tau[k]) (fp64, rounded to float32) for B x gamma logits t (device float32),
+ * tau [gamma] float64 device; the scheduler's input.  (spec_draft_markov
+ * applies the same temperatures itself through conf_tau.)
+ */
+int32_t spec_sts_apply(int32_t B, int32_t gamma, const float* conf_logits, const double* tau, float* conf_out,
+                       void* stream);
 
 /*
  * spec_read_ceiling -- measurement aid, not part of verification: reads

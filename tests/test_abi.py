@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
               "spec_schedule_workspace_size", "spec_abi_version", "spec_status_string",
               "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size",
               "spec_read_ceiling", "spec_verify_flat", "spec_overlap_mass", "spec_schedule_capacity",
-              "spec_schedule_topk", "spec_draft_markov", "spec_draft_workspace_size"):
+              "spec_schedule_topk", "spec_draft_markov", "spec_draft_workspace_size", "spec_sts_fit",
+              "spec_sts_apply", "spec_sts_workspace_size"):
         assert n in names, n
 
 
@@ -193,7 +194,7 @@ def test_draft_rejects_bad_arguments(lib):
 
     def call(B=3, G=4, V=1000, r=256, dt=1, U=p, w1=p, w2=p, x0=p, T=p, d=0, h=None, cw=None,
              tok=p, z=p, conf=None, st=p, w=p, wsb=ws):
-        return lib.spec_draft_markov(B, G, V, r, dt, U, w1, w2, x0, T, None, d, h, cw, tok, z, conf, st,
+        return lib.spec_draft_markov(B, G, V, r, dt, U, w1, w2, x0, T, None, d, h, cw, None, tok, z, conf, st,
                                      w, wsb, None)
     assert call(w=None) == 2                       # every other argument is valid
     assert call(B=0) == 1
@@ -217,3 +218,30 @@ def test_draft_rejects_bad_arguments(lib):
     assert call(d=-1) == 1
     assert call(wsb=ws - 1) == 2
     assert call(w=ctypes.c_void_p(p.value + 16)) == 2
+
+
+def test_sts_rejects_bad_arguments(lib):
+    keep, p = _fake()
+    ws = lib.spec_sts_workspace_size(1000, 64, 15)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.spec_sts_workspace_size(0, 64, 15) == 0 and lib.spec_sts_workspace_size(10, 64, 33) == 0
+
+    def fit(N=1000, G=5, t=p, y=p, nt=64, tau=p, bins=15, out=p, w=p, wsb=ws):
+        return lib.spec_sts_fit(N, G, t, y, nt, tau, bins, out, None, None, w, wsb, None)
+    assert fit(w=None) == 2                        # every other argument is valid
+    assert fit(N=0) == 1
+    assert fit(G=65) == 1
+    assert fit(nt=0) == 1
+    assert fit(nt=5000) == 1
+    assert fit(bins=0) == 1
+    assert fit(bins=33) == 1
+    assert fit(t=None) == 1
+    assert fit(y=None) == 1
+    assert fit(tau=None) == 1
+    assert fit(out=None) == 1
+    assert fit(wsb=ws - 1) == 2
+    assert lib.spec_sts_apply(0, 4, p, p, p, None) == 1
+    assert lib.spec_sts_apply(4, 65, p, p, p, None) == 1
+    assert lib.spec_sts_apply(4, 4, None, p, p, None) == 1
+    assert lib.spec_sts_apply(4, 4, p, None, p, None) == 1
+    assert lib.spec_sts_apply(4, 4, p, p, None, None) == 1

@@ -34,3 +34,4 @@ from .configs import (  # noqa: F401
     sample_draft_tokens,
 )
 from .drafting import DraftInputs, make_draft_inputs  # noqa: F401
+from .calibration import make_sts_inputs, tau_grid  # noqa: F401
