@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-overlap", action="store_true", help="skip the overlap-mass measurement")
     p.add_argument("--no-draft", action="store_true", help="skip the draft-sampler measurement")
+    p.add_argument("--no-sts", action="store_true", help="skip the temperature-scaling measurement")
     p.add_argument("--pool", type=int, default=8, help="worker processes for the pooled CPU-oracle timing")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
@@ -130,6 +131,7 @@ def main():
     draft = None
     if not args.no_draft:
         draft = draft_leg(sv, torch, oracle, dev, stream, with_cpu=not args.no_cpu)
+    sts = None if args.no_sts else sts_leg(sv, torch, oracle, dev, stream, with_cpu=not args.no_cpu)
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -182,6 +184,7 @@ def main():
         "overlap_mass": overlap,
         "async_scheduler": async_sched,
         "draft_sampler": draft,
+        "temperature_scaling": sts,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory},
         "ms_breakdown": {"stream_kernel": ms_stream, "rest_of_step": ms_step - ms_stream},
@@ -297,6 +300,42 @@ def draft_leg(sv, torch, oracle, dev, stream, reps=10, with_cpu=True):
                                          f"{el:.1f} s"}
     del w, out, ws
     torch.cuda.empty_cache()
+    return res
+
+
+def sts_leg(sv, torch, oracle, dev, stream, reps=3, with_cpu=True):
+    """spec_sts_fit (Sequential Temperature Scaling) on 2^20 held-out instances x 16 positions with
+    a 256-value temperature grid and 15 bins; HIP events around whole fits.  One evaluation = one
+    (instance, position, grid value): a sigmoid, a product and a bin update, all fp64."""
+    from draft_verification_04_amd.hipevents import HipEvent
+    from workloads import make_sts_inputs, tau_grid
+    N, G, T = 1 << 20, 16, 256
+    t, y, kappa = make_sts_inputs(N, G, 11, device=dev)
+    taus = tau_grid(T, device=dev)
+    ws = torch.empty(sv.load_library().spec_sts_workspace_size(N, T, 15), dtype=torch.uint8, device=dev)
+    out = sv.sts_fit(t, y, taus, 15, workspace=ws, stream=stream)
+    e0, e1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        sv.sts_fit(t, y, taus, 15, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    evals = N * G * T
+    res = {"config": f"N={N} gamma={G} grid={T} bins=15", "ms_per_fit": ms, "evaluations_per_s": evals / (ms * 1e-3),
+           "tau": [round(float(v), 4) for v in out["tau"].cpu().tolist()],
+           "kappa_synthetic": [round(float(v), 4) for v in kappa]}
+    if with_cpu:
+        from threadpoolctl import threadpool_limits
+        n_cpu = 1 << 16
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            oracle.sts_fit(t[:n_cpu, :2].cpu().numpy(), y[:n_cpu, :2].cpu().numpy(), taus.cpu().numpy(), 15)
+            el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n_cpu * 2 * T / el, "unit": "evaluations/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n_cpu} instances x 2 positions x {T} grid values, numpy fp64, one "
+                                         f"BLAS thread, {el:.1f} s"}
     return res
 
 
