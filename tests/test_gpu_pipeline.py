@@ -1,0 +1,72 @@
+"""End to end on the GPU: draft a block (Markov head, calibrated confidences) -> schedule the verify
+lengths -> verify against target logits; the same chain through the oracle.
+
+The oracle chain never reads a GPU result: it drafts its own block, and both chains build their
+target logits as (their own draft logits) + the same seeded noise.  On grid inputs the drafter is
+exact, so the two chains see the same numbers and must agree step for step: draft tokens, the
+confidences (fp64 sigmoid rounded to fp32, within 1 ulp, then compared as the scheduler reads
+them), the lengths, and the verification outcome (within the oracle's flags).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle
+from oracle.drafting import round_bf16
+from parity import to_np
+from workloads import make_draft_inputs, make_sps_table
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_verification_04_amd as m
+    m.load_library()
+    return m
+
+
+def test_draft_schedule_verify(sv):
+    B, G, V, r, d = 48, 6, 3001, 64, 32
+    w = make_draft_inputs(B, G, V, r, d, "bf16", "grid", 1.0, 17, DEV)
+    tau = torch.tensor([1.4, 1.1, 2.0, 0.8, 1.7, 1.2], dtype=torch.float64, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    noise = (torch.randn((B, G + 1, V), generator=g, device=DEV) * 0.5).to(torch.bfloat16)
+    sps = make_sps_table(B * (G + 1) + 1, 77)
+    budget = 4 * B
+
+    # GPU chain
+    d_out = sv.draft_markov(w.base, w.W1, w.W2t, w.anchor, w.temperature, w.seed, w.hidden, w.conf_w, conf_tau=tau)
+    zg = torch.cat([d_out["logits"], torch.zeros((B, 1, V), dtype=torch.bfloat16, device=DEV)], dim=1)
+    target_g = (zg.float() + noise.float()).to(torch.bfloat16)
+    sch = sv.schedule_lengths(d_out["conf"], torch.from_numpy(sps).to(DEV), budget)
+    ver = sv.verify(target_g.contiguous(), d_out["logits"], d_out["tokens"], sch["lengths"], w.temperature, None,
+                    w.seed)
+    torch.cuda.synchronize()
+
+    # oracle chain
+    ref = oracle.markov_draft(w.base, w.W1.cpu(), w.W2t.cpu(), w.anchor.cpu(), w.temperature.cpu(), w.seed.cpu(),
+                              w.hidden, w.conf_w.cpu(), conf_tau=to_np(tau))
+    assert np.array_equal(to_np(d_out["tokens"]), ref["tokens"])
+    assert np.array_equal(to_np(d_out["logits"]).astype(np.float64) if d_out["logits"].dtype == torch.float32
+                          else to_np(d_out["logits"].float()).astype(np.float64), ref["logits"])
+    conf_ref = ref["conf"].astype(np.float32)
+    conf_gpu = to_np(d_out["conf"])
+    assert np.all(np.abs(conf_gpu - conf_ref) <= np.spacing(conf_ref))
+    assert np.array_equal(conf_gpu, conf_ref), "a confidence rounded differently: the schedules may differ"
+    L_ref, _ = oracle.schedule(conf_ref, sps, budget)
+    assert np.array_equal(to_np(sch["lengths"]), L_ref)
+    zr = np.concatenate([ref["logits"], np.zeros((B, 1, V))], axis=1)
+    target_r = round_bf16(zr + to_np(noise.float()).astype(np.float64))
+    v_ref = oracle.verify(target_r, ref["logits"], ref["tokens"], L_ref, to_np(w.temperature), None, to_np(w.seed))
+    ok = ~(v_ref["emit_flag"] | (v_ref["accept_flags"] > 0))
+    assert ok.sum() >= B - 2
+    assert np.array_equal(to_np(ver["num_accepted"])[ok], v_ref["num_accepted"][ok])
+    assert np.array_equal(to_np(ver["out_tokens"])[ok], v_ref["out_tokens"][ok])
+    assert (to_np(ver["status"]) == 0).all()
