@@ -70,13 +70,15 @@ def main():
     sv.load_library()
     torch.cuda.synchronize()
     w = make_workload(args.config, dev)
+    greedy = w.draft is None  # the greedy workload has no draft logits: spec_verify_greedy
     copies = [(w.target, w.draft)]
     for c in range(1, args.copies):
-        copies.append((w.target.clone(), w.draft.clone()))
-    sps = torch.from_numpy(w.sps).to(dev)
+        copies.append((w.target.clone(), None if greedy else w.draft.clone()))
+    sps = torch.from_numpy(w.sps).to(dev) if w.sps is not None else None
     B, G, V = w.B, w.gamma, w.V
     es = w.elem_bytes
-    ws = torch.empty(sv.verify_workspace_bytes(B, G, V), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(sv.verify_workspace_bytes(B, G, V),
+                         int(sv.load_library().spec_verify_greedy_workspace_size(B, G))), dtype=torch.uint8, device=dev)
     sch_ws = torch.empty(max(256, sv.load_library().spec_schedule_workspace_size(B, G)), dtype=torch.uint8,
                          device=dev)
     sch_out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
@@ -95,8 +97,11 @@ def main():
             L = sch_out["lengths"]
         else:
             L = None
-        sv.verify(tgt, drf, w.draft_tokens, L, w.temperature, w.top_k, w.seed, out=ver_out, workspace=ws,
-                  stream=stream, events=events)
+        if greedy:
+            sv.verify_greedy(tgt, w.draft_tokens, L, out=ver_out, workspace=ws, stream=stream)
+        else:
+            sv.verify(tgt, drf, w.draft_tokens, L, w.temperature, w.top_k, w.seed, out=ver_out, workspace=ws,
+                      stream=stream, events=events)
 
     for s in range(args.warmup):
         step(s)
@@ -114,19 +119,24 @@ def main():
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / K
-    per_launch = [a.elapsed_ms(b) for a, b in evs]
-    ms_stream = float(np.mean(per_launch))
-    ms_stream_median = float(np.median(per_launch))
+    if greedy:  # no events inside the greedy call: the whole call bounds the streaming kernel
+        ms_stream = ms_stream_median = ms_step
+    else:
+        per_launch = [a.elapsed_ms(b) for a, b in evs]
+        ms_stream = float(np.mean(per_launch))
+        ms_stream_median = float(np.median(per_launch))
 
     L = sch_out["lengths"].cpu().numpy().astype(np.int64) if w.conf is not None else np.full(B, G)
     positions = int(L.sum())
-    rows = int((2 * L + 1).sum())
+    rows = int((L + 1).sum()) if greedy else int((2 * L + 1).sum())
     alg_bytes = rows * V * es
     achieved = alg_bytes / (ms_stream * 1e-3) / 1e9
     value = positions / (ms_step * 1e-3)
 
     ceiling = read_ceiling(sv, torch, copies, alg_bytes, stream)
-    overlap = None if args.no_overlap else overlap_leg(sv, torch, w, copies, sch_out["lengths"], stream)
+    overlap = None
+    if not args.no_overlap and not greedy:
+        overlap = overlap_leg(sv, torch, w, copies, sch_out["lengths"] if w.conf is not None else None, stream)
     async_sched = async_scheduler_leg(sv, torch, w, sps, stream) if w.conf is not None else None
     draft = None
     if not args.no_draft:
@@ -205,16 +215,20 @@ def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
     """Best rate of spec_read_ceiling (a plain 16-byte read kernel) over `nbytes` of the logits,
     alternating the input copies as the timed steps do, over a few grid sizes."""
     from draft_verification_04_amd.hipevents import HipEvent
-    sink = torch.zeros(1, dtype=torch.int32, device=copies[0][0].device)
+    dev = copies[0][0].device
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    src = [c[0] for c in copies]
+    if src[0].numel() * src[0].element_size() < nbytes:  # more bytes than the target rows hold
+        src = [torch.empty(nbytes + 16, dtype=torch.uint8, device=dev) for _ in range(len(copies))]
     best = None
     for grid in (1024, 2048, 4096):
         for r in range(2):   # warm-up
-            sv.read_ceiling(copies[r % len(copies)][0], nbytes, grid, sink, stream)
+            sv.read_ceiling(src[r % len(src)], nbytes, grid, sink, stream)
         e0, e1 = HipEvent(), HipEvent()
         torch.cuda.synchronize()
         e0.record(stream)
         for r in range(reps):
-            sv.read_ceiling(copies[r % len(copies)][0], nbytes, grid, sink, stream)
+            sv.read_ceiling(src[r % len(src)], nbytes, grid, sink, stream)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_ms(e1) / reps
@@ -246,7 +260,7 @@ def overlap_leg(sv, torch, w, copies, lengths, stream, reps=20):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_ms(e1) / reps
-    pos = int(lengths.sum().item())
+    pos = int(lengths.sum().item()) if lengths is not None else w.B * w.gamma
     row_bytes = w.V * w.elem_bytes
     once = 2 * pos * row_bytes
     return {"ms_per_call": ms, "positions": pos, "positions_per_s": pos / (ms * 1e-3),

@@ -237,10 +237,17 @@ __device__ void stream_sum(const char* row, int V, int vb, int ve, bool ends, fl
       accum<EPV>(z, c_hi, c_lo, M, S, bad);
     }
   }
-  for (; v < ve; v += nthr) {
-    float z[EPV];
-    unpack<BF16>(load_nt(vp + v), z);
-    accum<EPV>(z, c_hi, c_lo, M, S, bad);
+  if (v < ve) {  // the last (fewer than U) vectors: loads issued together, clamped in bounds
+    uint4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = load_nt(vp + min(v + u * nthr, ve - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v + u * nthr < ve) {
+        float z[EPV];
+        unpack<BF16>(d[u], z);
+        accum<EPV>(z, c_hi, c_lo, M, S, bad);
+      }
   }
   if (ends) {
     float z[2] = {-INFINITY, -INFINITY};
@@ -286,10 +293,17 @@ __device__ void stream_argmax(const char* row, int V, int vb, int ve, bool ends,
       take(z, g.head + (v + u * nthr) * EPV);
     }
   }
-  for (; v < ve; v += nthr) {
-    float z[EPV];
-    unpack<BF16>(load_nt(vp + v), z);
-    take(z, g.head + v * EPV);
+  if (v < ve) {  // the last (fewer than U) vectors: loads issued together, clamped in bounds
+    uint4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = load_nt(vp + min(v + u * nthr, ve - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v + u * nthr < ve) {
+        float z[EPV];
+        unpack<BF16>(d[u], z);
+        take(z, g.head + (v + u * nthr) * EPV);
+      }
   }
   if (!ends) return;
   // head and tail elements: compare with the index tie-break
@@ -433,10 +447,20 @@ __device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, floa
       push(z, EPV);
     }
   }
-  for (int v = lt + kTopkPre * nthr; v < g.nvec; v += nthr) {
-    float z[EPV];
-    unpack<BF16>(vp[v], z);
-    push(z, EPV);
+  {
+    constexpr int U = 4;  // the rest of the row, U vectors per thread in flight
+    for (int v0 = lt + kTopkPre * nthr; v0 < g.nvec; v0 += U * nthr) {
+      uint4 d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) d[u] = load_nt(vp + min(v0 + u * nthr, g.nvec - 1));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v0 + u * nthr < g.nvec) {
+          float z[EPV];
+          unpack<BF16>(d[u], z);
+          push(z, EPV);
+        }
+    }
   }
   {
     float z[2];
