@@ -44,6 +44,7 @@ constexpr int kQper = (kQefHi - kQefLo + 1) * 128;      // 3456 values per sign
 constexpr int kQsize = 2 * kQper;                       // 6912 entries, 55296 bytes
 constexpr int kSub = 512;                               // tokens per wave step (64 lanes x 8)
 constexpr int kSubPerRange = kRangeElems / kSub;        // 4
+constexpr uint32_t kFill2 = 0x3f803f80u;                // two bf16 ones: tabulated filler bits
 
 // exp(x) in fp64 by Tang's table-driven method (ACM TOMS 15(2), 1989), for
 // x in [-1000, 709]: x = k ln2/64 + r with |r| <= ln2/128 (two-part ln2/64),
@@ -67,22 +68,16 @@ __device__ __forceinline__ double q_direct(float z, double invT, double R, const
   return exp_tang(fmax(fma((double)z, invT, -R), -1000.0), T64);
 }
 
-// Q of a bf16 bit pattern, from the table when tabulated.
-__device__ __forceinline__ double q_bf16(uint32_t b, double invT, double R, const double* T64, const double* Qt) {
-  const uint32_t t = (b & 0x7fffu) - (uint32_t)(kQefLo << 7);
-  if (t < (uint32_t)kQper) return Qt[t + ((b & 0x8000u) ? kQper : 0)];
-  return q_direct(__uint_as_float(b << 16), invT, R, T64);
-}
-
 __device__ __forceinline__ void init_t64(double* T64) {
   if (threadIdx.x < 64) T64[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
 }
 
+// The table of Q over the tabulated bf16 values.  Entry 2 (m - m0) + s holds the value with sign
+// s and magnitude bits m (m0 the first tabulated magnitude): the index is the bf16 bit pattern
+// rotated left by one, less 2 m0, which two 16-bit integer instructions give for a pair of values.
 __device__ void build_qtab(double* Qt, double invT, double R, const double* T64) {
   for (int idx = threadIdx.x; idx < kQsize; idx += blockDim.x) {
-    const uint32_t s = idx >= kQper;
-    const uint32_t t = idx - s * kQper;
-    const uint32_t bits = (s << 15) | ((uint32_t)(kQefLo << 7) + t);
+    const uint32_t bits = ((uint32_t)(idx & 1) << 15) | ((uint32_t)(kQefLo << 7) + ((uint32_t)idx >> 1));
     Qt[idx] = q_direct(__uint_as_float(bits << 16), invT, R, T64);
   }
 }
@@ -93,36 +88,68 @@ struct EmitRows {
   double invT, R;
   float tht, thd;
   double cd;      // exp(R_t - R_d): p_d ~ cd * Q(z_d) with the approximate normalisers
+  int* amb_n;     // uncertain-sign tokens: count and list (global memory, or LDS in the fused kernel)
+  int* amb_v;
+  const double* Qt;  // the Q table when it holds this row's values (bf16 rows without top-k), else null
 };
 
+// The emit row(s) of request i at position n from the row records of target row n and, when
+// n < L, draft row n.
 template <bool BF16>
-__device__ __forceinline__ EmitRows emit_rows(const VerifyArgs& a, int i, int n) {
+__device__ __forceinline__ EmitRows emit_rows_from(const VerifyArgs& a, int i, int n, int L, float T,
+                                                   const RowStat& rt, const RowStat& rd) {
   constexpr int ES = BF16 ? 2 : 4;
-  const int G = a.G, V = a.V;
-  const int L = a.lengths ? a.lengths[i] : G;
   EmitRows e;
-  const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
   e.t = target_row<ES>(a, i, n);
   e.R = rt.lse2 * kLn2;
   e.tht = rt.theta;
-  e.invT = 1.0 / (double)a.temperature[i];
+  e.invT = 1.0 / (double)T;
   e.d = nullptr;
   e.thd = -INFINITY;
   e.cd = 1.0;
   if (n < L) {
-    const RowStat rd = a.rows_d[(size_t)i * G + n];
     e.d = draft_row<ES>(a, i, n);
     e.thd = rd.theta;
     e.cd = exp(e.R - rd.lse2 * kLn2);
   }
+  e.amb_n = &a.ereq[i].amb_n;
+  e.amb_v = a.amb + (size_t)i * kAmbCap;
+  e.Qt = nullptr;
   return e;
 }
 
-// Q of token v of a row (any dtype, any alignment), kept-set aware.
 template <bool BF16>
-__device__ __forceinline__ double q_at(const char* row, int v, float th, double invT, double R, const double* T64) {
-  const float z = load_elem<BF16>(row, v);
-  return (z >= th) ? q_direct(z, invT, R, T64) : 0.0;
+__device__ __forceinline__ EmitRows emit_rows(const VerifyArgs& a, int i, int n) {
+  const int G = a.G;
+  const int L = a.lengths ? a.lengths[i] : G;
+  const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
+  const RowStat rd = (n < L) ? a.rows_d[(size_t)i * G + n] : RowStat{0.0, -INFINITY, 0};
+  return emit_rows_from<BF16>(a, i, n, L, a.temperature[i], rt, rd);
+}
+
+// Table slot of one bf16 value (see build_qtab); kQsize or more when it is not tabulated.
+__device__ __forceinline__ uint32_t q_slot1(uint32_t b) {
+  return (((b << 1) | (b >> 15)) - (uint32_t)(2 * (kQefLo << 7))) & 0xffffu;
+}
+
+// Q of token v of a row (any dtype, any alignment), kept-set aware; from the table Qt when given
+// and the value is tabulated (the same bits as the direct evaluation).
+template <bool BF16>
+__device__ __forceinline__ double q_at(const char* row, int v, float th, double invT, double R, const double* T64,
+                                       const double* Qt) {
+  if constexpr (BF16) {
+    const uint32_t b = reinterpret_cast<const uint16_t*>(row)[v];
+    const float z = __uint_as_float(b << 16);
+    if (!(z >= th)) return 0.0;
+    if (Qt) {
+      const uint32_t k = q_slot1(b);
+      if (k < (uint32_t)kQsize) return Qt[k];
+    }
+    return q_direct(z, invT, R, T64);
+  } else {
+    const float z = load_elem<false>(row, v);
+    return (z >= th) ? q_direct(z, invT, R, T64) : 0.0;
+  }
 }
 
 // Per-lane accumulators for one range.
@@ -131,10 +158,16 @@ struct Acc {
   double A, D, T;  // this range
 };
 
-// Accumulate one token pair; returns whether its residual sign is uncertain (p_t and p_d
-// within the margin of each other with the approximate normalisers): such tokens are
-// recorded by the caller and weighed exactly later.  No branches, so the table reads of a
-// whole step can be in flight together.
+// Whether the residual sign of a token pair is uncertain: not clearly positive, yet p_t is above
+// p_d less the margin, with the approximate normalisers.  A pair with p_t = p_d = 0 is not (its
+// residual is 0), nor one exactly at the lower margin, whose residual is negative since the
+// normalisers are checked to be within half the margin.  Such tokens are weighed exactly later.
+__device__ __forceinline__ bool uncertain(double qt, double qd, double cdh, double cdl) {
+  return !(qt > cdh * qd) && qt > cdl * qd;
+}
+
+// Accumulate one token pair; returns uncertain(qt, qd, ...).  No branches, so the table reads
+// of a whole step can be in flight together.
 __device__ __forceinline__ bool classify(Acc& c, double qt, double qd, double cdh, double cdl) {
   c.sd += qd;
   c.T += qt;
@@ -144,28 +177,51 @@ __device__ __forceinline__ bool classify(Acc& c, double qt, double qd, double cd
   const double one = pos ? 1.0 : 0.0;
   c.A = fma(one, qt, c.A);
   c.D = fma(one, qd, c.D);
-  return !pos && qt > 0.0 && qt >= cdl * qd;
+  return !pos && qt > cdl * qd;
 }
 
 // Record token v as uncertain (rare).
-__device__ __forceinline__ void record_uncertain(const VerifyArgs& a, int i, int v) {
-  const int slot = atomicAdd(&a.ereq[i].amb_n, 1);
-  if (slot < kAmbCap) a.amb[(size_t)i * kAmbCap + slot] = v;
+__device__ __forceinline__ void record_uncertain(const EmitRows& e, int v) {
+  const int slot = atomicAdd(e.amb_n, 1);
+  if (slot < kAmbCap) e.amb_v[slot] = v;
 }
 
 constexpr int kMaxWaves = 1024 / SPEC_WAVE;  // largest emit workgroup, in waves
 
 struct PassShared {
   double T64[64];
-  double Qt[kQsize];
+  union {
+    double Qt[kQsize];
+    // the fused decision's copy of the request's segment partials (target rows, then draft rows),
+    // used before the table is built
+    Partial stage[2 * (SPEC_MAX_GAMMA + 1) * kMaxStreamSegs];
+  };
   double red[2][kMaxWaves];
-  int st, n;
+  // the fused decision, per draft position: row records, acceptance ratios, draft tokens
+  RowStat rt[SPEC_MAX_GAMMA + 1], rd[SPEC_MAX_GAMMA];
+  double accr[SPEC_MAX_GAMMA];
+  double ua[SPEC_MAX_GAMMA];
+  int tacc[SPEC_MAX_GAMMA];
+  int x[SPEC_MAX_GAMMA];
+  int st, n, L, greedy, bad_t, bad_d;
+  // the fused kernel's uncertain-sign tokens
+  int amb_cnt;
+  int amb_list[kAmbCap];
 };
+static_assert(sizeof(Partial) * 2 * (SPEC_MAX_GAMMA + 1) * kMaxStreamSegs <= sizeof(double) * kQsize,
+              "the staged partials fit in the table's memory");
 
-// Table slot of a bf16 bit pattern, or -1 when it is not tabulated.
-__device__ __forceinline__ int q_slot(uint32_t b) {
-  const uint32_t t = (b & 0x7fffu) - (uint32_t)(kQefLo << 7);
-  return (t < (uint32_t)kQper) ? (int)(t + ((b & 0x8000u) ? kQper : 0)) : -1;
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// Table slots of the two bf16 values of a word, one per 16-bit half; a slot is below kQsize
+// exactly when its value is tabulated (otherwise it wrapped past it).
+__device__ __forceinline__ us2 q_slots(uint32_t w) {
+  const us2 v = __builtin_bit_cast(us2, w);
+  return ((v << (unsigned short)1) | (v >> (unsigned short)15)) - (us2)(unsigned short)(2 * (kQefLo << 7));
+}
+
+__device__ __forceinline__ uint32_t slot_of(const us2 (&k)[4], int j) {
+  return (j & 1) ? (uint32_t)k[j >> 1].y : (uint32_t)k[j >> 1].x;
 }
 
 __device__ __forceinline__ uint32_t half16(const uint32_t (&w)[4], int j) {
@@ -174,35 +230,54 @@ __device__ __forceinline__ uint32_t half16(const uint32_t (&w)[4], int j) {
 
 // One step (64 lanes x 8 tokens) of a bf16 row pair from registers.  A lane whose 16 tokens
 // are all tabulated reads Q from the table; otherwise (rare: |z| < 2^-20, |z| >= 128,
-// infinities) it evaluates the same formula directly for the whole step.
-template <bool RESID>
+// infinities) it evaluates the same formula directly for the whole step.  MASK: the step of a
+// row's last, partial range, where a lane past the row's end (live = false) holds tabulated
+// filler bits and adds nothing.  Uncertain tokens are rare: the table path only notes that the
+// lane saw one and then finds and records it in a second look at its 8 tokens.
+template <bool RESID, bool MASK = false>
 __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& dd, const EmitRows& e,
                                           double cdh, double cdl, int v0, const VerifyArgs& a, int i,
-                                          const double* T64, const double* Qt) {
+                                          const double* T64, const double* Qt, bool live = true) {
   constexpr bool resid = RESID;
   const uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
   const uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
-  bool miss = false;
+  us2 kt[4], kd[4];
+  us2 kmax = (us2)(unsigned short)0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    miss |= q_slot(half16(wt, j)) < 0;
-    if (resid) miss |= q_slot(half16(wd, j)) < 0;
+  for (int q = 0; q < 4; ++q) {
+    kt[q] = q_slots(wt[q]);
+    kmax = __builtin_elementwise_max(kmax, kt[q]);
+    if (resid) {
+      kd[q] = q_slots(wd[q]);
+      kmax = __builtin_elementwise_max(kmax, kd[q]);
+    }
   }
-  unsigned amb = 0;
+  const bool miss = max((uint32_t)kmax.x, (uint32_t)kmax.y) >= (uint32_t)kQsize;
   if (!miss) {
+    bool any = false;
     // two halves of four tokens: eight table reads in flight, registers kept in check
 #pragma unroll
     for (int h = 0; h < 8; h += 4) {
       double qt[4], qd[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        qt[j] = Qt[q_slot(half16(wt, h + j))];
-        qd[j] = resid ? Qt[q_slot(half16(wd, h + j))] : 0.0;
+        qt[j] = Qt[slot_of(kt, h + j)];
+        qd[j] = resid ? Qt[slot_of(kd, h + j)] : 0.0;
+        if (MASK && !live) qt[j] = qd[j] = 0.0;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (resid) amb |= (unsigned)classify(c, qt[j], qd[j], cdh, cdl) << (h + j);
+        if (resid) any |= classify(c, qt[j], qd[j], cdh, cdl);
         else c.T += qt[j];
+      }
+    }
+    if (resid && any) {
+      // the slots again from the loaded words (kept, unlike the slots, until the next refill)
+#pragma unroll 1
+      for (int j = 0; j < 8; ++j) {
+        const us2 st = q_slots(wt[j >> 1]), sd = q_slots(wd[j >> 1]);
+        const uint32_t it = (j & 1) ? st.y : st.x, id = (j & 1) ? sd.y : sd.x;
+        if (uncertain(Qt[it], Qt[id], cdh, cdl)) record_uncertain(e, v0 + j);
       }
     }
   } else {
@@ -211,22 +286,18 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
       const double qt = q_direct(__uint_as_float(half16(wt, j) << 16), e.invT, e.R, T64);
       if (resid) {
         const double qd = q_direct(__uint_as_float(half16(wd, j) << 16), e.invT, e.R, T64);
-        amb |= (unsigned)classify(c, qt, qd, cdh, cdl) << j;
+        if (classify(c, qt, qd, cdh, cdl)) record_uncertain(e, v0 + j);
       } else {
         c.T += qt;
       }
     }
   }
-  if (amb) {
-#pragma unroll 1
-    for (int j = 0; j < 8; ++j)
-      if ((amb >> j) & 1u) record_uncertain(a, i, v0 + j);
-  }
 }
 
 // The ranges of request i that segment `seg` owns, each written as an EmitRange to out[r]
 // (global memory, or LDS when the same workgroup finishes the request); each wave's sum of
-// E_d goes to sh.red[1][wave].
+// E_d goes to sh.red[1][wave].  bf16 rows without top-k build the Q table in sh.Qt here (the
+// whole workgroup calls this function).
 template <bool BF16, bool TOPK>
 __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e,
                             EmitRange* out) {
@@ -242,27 +313,48 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
   Acc c{0.0, 0.0, 0.0, 0.0};
   int r = seg * NWPB + wave;
   if (BF16 && !TOPK) {
-    // the 4 steps of a range are in flight at once; each register slot is refilled with
-    // the same step of the wave's next range as soon as it has been consumed
+    // the 4 steps of a range are in flight at once; each register slot is refilled with the
+    // same step of the wave's next range as soon as it has been consumed.  When V is a multiple
+    // of 8 the row's last, partial range is read the same way, lanes past the end masked.
+    const int NRv = (aligned && (V & 7) == 0) ? NR : NRfull;
     uint4 bt[kSubPerRange], bd[kSubPerRange];
     auto load = [&](int rr, int sub, uint4& t, uint4& d) {
-      const size_t off = ((size_t)rr * kRangeElems + sub * kSub + lane * 8) * 2;
-      t = *reinterpret_cast<const uint4*>(e.t + off);
-      d = resid ? *reinterpret_cast<const uint4*>(e.d + off) : make_uint4(0, 0, 0, 0);
+      const int v0 = rr * kRangeElems + sub * kSub + lane * 8;
+      if (v0 < V) {
+        const size_t off = (size_t)v0 * 2;
+        t = *reinterpret_cast<const uint4*>(e.t + off);
+        d = resid ? *reinterpret_cast<const uint4*>(e.d + off) : make_uint4(0, 0, 0, 0);
+      } else {
+        t = d = make_uint4(kFill2, kFill2, kFill2, kFill2);
+      }
     };
-    if (r < NRfull) {
+    if (r < NRv) {
 #pragma unroll
       for (int sub = 0; sub < kSubPerRange; ++sub) load(r, sub, bt[sub], bd[sub]);
     }
-    while (r < NRfull) {
+    // the table of Q over the bf16 values, built while the first loads are in flight
+    build_qtab(sh.Qt, e.invT, e.R, sh.T64);
+    __syncthreads();
+    while (r < NRv) {
       const int rn = r + NWT;
       c.A = c.D = c.T = 0.0;
+      if (r < NRfull) {
 #pragma unroll
-      for (int sub = 0; sub < kSubPerRange; ++sub) {
-        const int v0 = r * kRangeElems + sub * kSub + lane * 8;
-        if (resid) step_bf16<true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
-        else step_bf16<false>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
-        if (rn < NRfull) load(rn, sub, bt[sub], bd[sub]);
+        for (int sub = 0; sub < kSubPerRange; ++sub) {
+          const int v0 = r * kRangeElems + sub * kSub + lane * 8;
+          if (resid) step_bf16<true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
+          else step_bf16<false>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
+          if (rn < NRv) load(rn, sub, bt[sub], bd[sub]);
+        }
+      } else {
+        // the last range (rn is past it): steps wholly past the row's end are skipped
+#pragma unroll
+        for (int sub = 0; sub < kSubPerRange; ++sub) {
+          const int vs = r * kRangeElems + sub * kSub, v0 = vs + lane * 8;
+          if (vs >= V) break;
+          if (resid) step_bf16<true, true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt, v0 < V);
+          else step_bf16<false, true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt, v0 < V);
+        }
       }
       const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
       if (lane == 0) out[r] = EmitRange{A, D, T};
@@ -284,7 +376,7 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
             const double qt = (zt >= e.tht) ? q_direct(zt, e.invT, e.R, sh.T64) : 0.0;
             if (resid) {
               const double qd = (zd >= e.thd) ? q_direct(zd, e.invT, e.R, sh.T64) : 0.0;
-              if (classify(c, qt, qd, cdh, cdl)) record_uncertain(a, i, v);
+              if (classify(c, qt, qd, cdh, cdl)) record_uncertain(e, v);
             } else {
               c.T += qt;
             }
@@ -316,19 +408,10 @@ __device__ __forceinline__ void decide_into(PassShared& sh, const VerifyArgs& a,
 
 // The emit pass over segment `seg` of request i (after its decision, sampling only).
 template <bool BF16>
-__device__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, int n, EmitRange* out) {
-  const EmitRows e = emit_rows<BF16>(a, i, n);
+__device__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e, EmitRange* out) {
   const int K = a.top_k ? a.top_k[i] : 0;
-  const bool topk = K > 0 && K < a.V;
-  if (BF16 && !topk) {
-    build_qtab(sh.Qt, e.invT, e.R, sh.T64);
-    __syncthreads();
-    pass_ranges<BF16, false>(sh, a, i, seg, e, out);
-  } else if (topk) {
-    pass_ranges<BF16, true>(sh, a, i, seg, e, out);
-  } else {
-    pass_ranges<BF16, false>(sh, a, i, seg, e, out);
-  }
+  if (K > 0 && K < a.V) pass_ranges<BF16, true>(sh, a, i, seg, e, out);
+  else pass_ranges<BF16, false>(sh, a, i, seg, e, out);
   __syncthreads();
 }
 
@@ -340,7 +423,7 @@ __global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
   decide_into(sh, a, i);
   const int st = sh.st, n = sh.n;
   if (st || a.temperature[i] == 0.f) return;
-  run_pass<BF16>(sh, a, i, seg, n, a.ranges + (size_t)i * num_ranges(a.V));
+  run_pass<BF16>(sh, a, i, seg, emit_rows<BF16>(a, i, n), a.ranges + (size_t)i * num_ranges(a.V));
   if (threadIdx.x == 0) {
     double y = 0.0;
     for (int w = 0; w < kPassThreads / SPEC_WAVE; ++w) y += sh.red[1][w];
@@ -357,6 +440,7 @@ struct FinalShared {
   EmitRange rg[kMaxRanges]; // the emit pass's range sums, fetched early
   int na;                   // uncertain-sign tokens recorded
   double wsum[kMaxWaves];
+  int cross_lane[kMaxWaves], last_lane[kMaxWaves];
   double amb_w[kAmbCap];
   int amb_v[kAmbCap];
   int amb_sorted[kAmbCap];
@@ -368,23 +452,21 @@ struct FinalShared {
 template <bool BF16>
 __device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, double St, double Sd,
                                          const double* T64) {
-  const double qt = q_at<BF16>(e.t, v, e.tht, e.invT, e.R, T64);
+  const double qt = q_at<BF16>(e.t, v, e.tht, e.invT, e.R, T64, e.Qt);
   if (!resid) return qt;
-  const double qd = q_at<BF16>(e.d, v, e.thd, e.invT, e.R, T64);
+  const double qd = q_at<BF16>(e.d, v, e.thd, e.invT, e.R, T64, e.Qt);
   return fmax(0.0, qt / St - qd / Sd);
 }
 
+template <bool BF16, int NT>
+__device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, const EmitRows& e);
+
 // Everything after request i's decision (st, n): status and outputs, then, for a sampling
-// request, the emitted token from the emit pass's range sums (sh.rg, sh.St, sh.Sd, sh.na
-// filled).  Works for any block of 256 .. 1024 threads (a multiple of 256); the token octets
-// of the crossing range belong to the first 256 threads, the others only join loops and
-// barriers.
+// request, the emitted token (sample_emit).
 template <bool BF16>
 __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int st, int n) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int NW = (int)(blockDim.x >> 6);
-  const int G = a.G, V = a.V;
-  const int NR = num_ranges(V);
+  const int tid = threadIdx.x;
+  const int G = a.G;
   const int L = a.lengths ? a.lengths[i] : G;
   if (a.status && tid == 0) a.status[i] = st;
   if (st) {
@@ -407,8 +489,21 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
     if (tid == 0) a.out_tokens[(size_t)i * (G + 1) + n] = a.rows_t[(size_t)i * (G + 1) + n].argmax;
     return;
   }
+  sample_emit<BF16, kEmitThreads>(sh, a, i, n, emit_rows<BF16>(a, i, n));
+}
 
-  const EmitRows e = emit_rows<BF16>(a, i, n);
+// The emitted token of sampling request i at position n (rows e), from the emit pass's range sums
+// (sh.rg, sh.St, sh.Sd, sh.na filled; the uncertain-sign tokens listed at e.amb_v), written to
+// out_tokens.  Called by a block of NT threads; each holds kRangeElems / NT consecutive tokens
+// of the range where the draw lands.
+template <bool BF16, int NT>
+__device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, const EmitRows& e) {
+  constexpr int TPT = kRangeElems / NT;
+  constexpr int NW = NT / SPEC_WAVE;
+  static_assert(TPT * NT == kRangeElems && NW * SPEC_WAVE == NT && NW <= kMaxWaves, "block shape");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.G, V = a.V;
+  const int NR = num_ranges(V);
   const bool resid = (e.d != nullptr);
   double ua, ue;
   verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
@@ -416,15 +511,14 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
   // the sign classification assumed cd * S_d / S_t = 1 to within half its margin
   const double rho = resid ? e.cd * Sd / St : 1.0;
   const bool slow = resid && (!(fabs(rho - 1.0) <= 0.5 * kAmbTol) || sh.na > kAmbCap);
-  if (tid == 0) sh.use_t = !resid;
 
   // range weights
   if (resid && !slow) {
     const int na = sh.na;
-    for (int q = tid; q < na; q += blockDim.x) sh.amb_v[q] = a.amb[(size_t)i * kAmbCap + q];
-    for (int r = tid; r < NR; r += blockDim.x) sh.corr[r] = 0.0;
+    for (int q = tid; q < na; q += NT) sh.amb_v[q] = e.amb_v[q];
+    for (int r = tid; r < NR; r += NT) sh.corr[r] = 0.0;
     __syncthreads();
-    for (int q = tid; q < na; q += blockDim.x) {
+    for (int q = tid; q < na; q += NT) {
       const int v = sh.amb_v[q];
       int rank = 0;
       for (int p = 0; p < na; ++p) rank += sh.amb_v[p] < v;
@@ -435,15 +529,15 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
     if (tid == 0)
       for (int q = 0; q < na; ++q) sh.corr[sh.amb_sorted[q] / kRangeElems] += sh.amb_w[q];
     __syncthreads();
-    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = (sh.rg[r].a / St - sh.rg[r].d / Sd) + sh.corr[r];
+    for (int r = tid; r < NR; r += NT) sh.R[r] = (sh.rg[r].a / St - sh.rg[r].d / Sd) + sh.corr[r];
   } else if (resid && slow) {
     // exact weight of every token (rare: nearly identical target and draft rows)
     for (int r = 0; r < NR; ++r) {
-      double s = 0.0;
-      for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += blockDim.x)
-        s += weight<BF16>(e, v, true, St, Sd, sh.T64);
-      s = wave_sum(s);
-      if (lane == 0) sh.wsum[wave] = s;
+      double x = 0.0;
+      for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += NT)
+        x += weight<BF16>(e, v, true, St, Sd, sh.T64);
+      x = wave_sum(x);
+      if (lane == 0) sh.wsum[wave] = x;
       __syncthreads();
       if (tid == 0) {
         double t = 0.0;
@@ -453,60 +547,63 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
       __syncthreads();
     }
   } else {
-    for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = sh.rg[r].t;
+    for (int r = tid; r < NR; r += NT) sh.R[r] = sh.rg[r].t;
   }
   __syncthreads();
 
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    // inclusive prefix over the ranges (wave 0, four per lane), then the first range whose
-    // prefix passes u * W
-    static_assert(kMaxRanges <= 4 * SPEC_WAVE, "four ranges per lane");
-    if (wave == 0) {
-      double v[4], t = 0.0;
+  // wave 0: inclusive prefix over the ranges (four per lane), the total W, the target u * W and
+  // the first range whose prefix passes it; the whole block then waits once
+  static_assert(kMaxRanges <= 4 * SPEC_WAVE, "four ranges per lane");
+  if (wave == 0) {
+    int use_t = !resid;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      double v[4], pre[4], t = 0.0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = lane * 4 + u;
-        v[u] = (r < NR) ? sh.R[r] : 0.0;
+        v[u] = (r < NR) ? (attempt ? sh.rg[r].t : sh.R[r]) : 0.0;
         t += v[u];
       }
       const double incl = wave_inclusive_sum(t, lane);
       double run = incl - t;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int r = lane * 4 + u;
         run += v[u];
-        if (r < NR) sh.R[r] = run;
+        pre[u] = run;
       }
       const double W = __shfl(incl, 63, SPEC_WAVE);
-      if (lane == 0) {
-        if (resid && !sh.use_t && !(W > 0.0)) {
-          sh.use_t = 2;  // no residual mass (rounding): fall back to p_t of the same row
-        } else {
-          sh.use_t = sh.use_t ? 1 : 0;
-          sh.target = ue * W;
-          sh.sel = NR;
+      if (attempt == 0 && !use_t && !(W > 0.0)) {
+        use_t = 1;   // no residual mass (rounding): fall back to p_t of the same row
+        continue;
+      }
+      const double target = ue * W;
+      int f = 4;
+#pragma unroll
+      for (int u = 3; u >= 0; --u)
+        if (lane * 4 + u < NR && pre[u] > target) f = u;
+      const unsigned long long m = __ballot(f < 4);
+      int sel = NR;
+      double before = 0.0;
+      if (m) {
+        const int fl = (int)__ffsll((long long)m) - 1;
+        sel = fl * 4 + __shfl(f, fl, SPEC_WAVE);
+        if (sel > 0) {
+          const int ub = (sel - 1) & 3;
+          const double mine = ub == 0 ? pre[0] : ub == 1 ? pre[1] : ub == 2 ? pre[2] : pre[3];
+          before = __shfl(mine, (sel - 1) >> 2, SPEC_WAVE);
         }
       }
+      if (lane == 0) {
+        sh.use_t = use_t;
+        sh.target = target;
+        sh.sel = sel;
+        sh.past = (sel >= NR);
+        sh.before = before;
+      }
+      break;
     }
-    __syncthreads();
-    if (sh.use_t == 2) {
-      for (int r = tid; r < NR; r += blockDim.x) sh.R[r] = sh.rg[r].t;
-      if (tid == 0) sh.use_t = 1;
-      __syncthreads();
-      continue;
-    }
-    const double target = sh.target;
-    for (int r = tid; r < NR; r += blockDim.x)
-      if (sh.R[r] > target && (r == 0 || !(sh.R[r - 1] > target))) sh.sel = r;
-    __syncthreads();
-    if (tid == 0) {
-      const int lo = sh.sel;
-      sh.past = (lo >= NR);
-      sh.before = (lo > 0 && lo < NR) ? sh.R[lo - 1] : 0.0;
-    }
-    __syncthreads();
-    break;
   }
+  __syncthreads();
   const bool wres = resid && sh.use_t == 0;
 
   if (sh.past) {
@@ -515,64 +612,63 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
     __syncthreads();
     for (int r = NR - 1; r >= 0; --r) {
       int best = -1;
-      for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += blockDim.x)
+      for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += NT)
         if (weight<BF16>(e, v, wres, St, Sd, sh.T64) > 0.0) best = v;
       best = wave_max_i(best);
-      if (lane == 0) sh.wsum[wave] = (double)best;
+      if (lane == 0) sh.last_lane[wave] = best;
       __syncthreads();
       if (tid == 0) {
         int b = -1;
-        for (int w = 0; w < NW; ++w) b = max(b, (int)sh.wsum[w]);
+        for (int w = 0; w < NW; ++w) b = max(b, sh.last_lane[w]);
         if (b >= 0) sh.token = b;
       }
       __syncthreads();
       if (sh.token >= 0) break;
     }
   } else {
-    // the selected range, token by token: thread t holds tokens base + 8t .. base + 8t + 7
-  static_assert(kEmitThreads * 8 == kRangeElems, "one token octet per thread");
-    const bool mine = tid < kEmitThreads;
-    const int base = sh.sel * kRangeElems + tid * 8;
-    double w[8];
-    double s = 0.0;
+    // the selected range, token by token: thread t holds tokens base + TPT t .. + TPT - 1
+    const int base = sh.sel * kRangeElems + tid * TPT;
+    double w[TPT];
+    double x = 0.0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < TPT; ++j) {
       const int v = base + j;
-      w[j] = (mine && v < V) ? weight<BF16>(e, v, wres, St, Sd, sh.T64) : 0.0;
-      s += w[j];
+      w[j] = (v < V) ? weight<BF16>(e, v, wres, St, Sd, sh.T64) : 0.0;
+      x += w[j];
     }
-    const double incl = wave_inclusive_sum(s, lane);
+    const double incl = wave_inclusive_sum(x, lane);
     if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
     double wb = 0.0;
     for (int q = 0; q < wave; ++q) wb += sh.wsum[q];
     const double P = sh.before + wb, target = sh.target;
-    const double excl = incl - s;
-    const bool cross = (P + incl > target);
-    // first thread whose running total passes the target
-    const unsigned long long m = __ballot(cross);
-    if (lane == 0) sh.amb_v[wave] = m ? (int)(__ffsll((long long)m) - 1) : 64;
-    const unsigned long long pos = __ballot(s > 0.0);
-    if (lane == 0) sh.amb_v[NW + wave] = pos ? 63 - __clzll((long long)pos) : -1;
+    const double excl = incl - x;
+    // first thread whose running total passes the target; the last thread with weight
+    const unsigned long long m = __ballot(P + incl > target);
+    const unsigned long long pos = __ballot(x > 0.0);
+    if (lane == 0) {
+      sh.cross_lane[wave] = m ? (int)(__ffsll((long long)m) - 1) : 64;
+      sh.last_lane[wave] = pos ? 63 - __clzll((long long)pos) : -1;
+    }
     __syncthreads();
     int cw = -1, cl = -1;
-    constexpr int NWO = kEmitThreads / SPEC_WAVE;  // waves holding the range's octets
-    for (int q = 0; q < NWO && cw < 0; ++q)
-      if (sh.amb_v[q] < 64) {
+    for (int q = 0; q < NW && cw < 0; ++q)
+      if (sh.cross_lane[q] < 64) {
         cw = q;
-        cl = sh.amb_v[q];
+        cl = sh.cross_lane[q];
       }
     if (cw < 0) {  // rounding left no crossing: the last thread with weight
-      for (int q = NWO - 1; q >= 0 && cw < 0; --q)
-        if (sh.amb_v[NW + q] >= 0) {
+      for (int q = NW - 1; q >= 0 && cw < 0; --q)
+        if (sh.last_lane[q] >= 0) {
           cw = q;
-          cl = sh.amb_v[NW + q];
+          cl = sh.last_lane[q];
         }
     }
     if (wave == cw && lane == cl) {
       double acc = P + excl;
       int tok = -1, lastpos = -1;
-      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
         if (w[j] > 0.0) lastpos = base + j;
         acc += w[j];
         if (tok < 0 && acc > target && w[j] > 0.0) tok = base + j;
@@ -623,30 +719,121 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
   finish_request<BF16>(sh, a, i, sh.st, sh.n);
 }
 
-// The acceptance test of every position of request i and its first rejection, taken by wave 0
-// (lane per position) straight from the streaming kernel's segment partials: row statistics,
-// r = min(1, p_t(x)/p_d(x)) with the logits at x the partials carry, the Philox uniform; top-k
-// positions were finished by the streaming kernel.  Writes the row and acceptance records
-// (read by the emit pass and finish_request) and sh.st / sh.n.
-__device__ void decide_full(PassShared& sh, const VerifyArgs& a, int i) {
+// What the fused decision of request i reads besides the segment partials: loaded by wave 0 before
+// the partials are staged, so that every load of the decision is in flight at once.
+struct DecideIn {
+  uint64_t seed;
+  int L, K0, rs, x;
+  float T;
+};
+
+__device__ __forceinline__ DecideIn decide_loads(const VerifyArgs& a, int i) {
+  const int lane = threadIdx.x & 63;
+  DecideIn d;
+  d.seed = a.seed[i];
+  d.L = a.lengths ? a.lengths[i] : a.G;
+  d.T = a.temperature[i];
+  d.K0 = a.top_k ? a.top_k[i] : 0;
+  d.rs = a.req_status[i];
+  d.x = (lane < a.G) ? a.tokens[(size_t)i * a.G + lane] : 0;
+  return d;
+}
+
+// The segment partials of every row of request i (target rows, then draft rows; those of rows
+// past L are read but not used) copied to sh.stage by the whole workgroup.
+__device__ __forceinline__ void stage_partials(PassShared& sh, const VerifyArgs& a, int i) {
+  const int per = (a.G + 1) * a.nseg;
+  const Partial* gt = a.part_t + (size_t)i * per;
+  const Partial* gd = a.part_d + (size_t)i * per;
+  for (int q = threadIdx.x; q < 2 * per; q += blockDim.x) sh.stage[q] = (q < per) ? gt[q] : gd[q - per];
+}
+
+// Status of request i from its arguments (every lane of a wave gets it; 0 when well formed).
+__device__ __forceinline__ int decide_status(const VerifyArgs& a, const DecideIn& in) {
+  const int lane = threadIdx.x & 63;
+  const int L = in.L;
+  if (L < 0 || L > a.G) return SPEC_REQ_BAD_LENGTH;
+  int st = 0;
+  if (!(in.T >= 0.f && in.T < INFINITY)) st |= SPEC_REQ_BAD_TEMPERATURE;
+  if (in.K0 < 0) st |= SPEC_REQ_BAD_TOPK;
+  if (__ballot(lane < L && (in.x < 0 || in.x >= a.V))) st |= SPEC_REQ_BAD_TOKEN;
+  if (st == 0) st |= in.rs;
+  return st;
+}
+
+// First half of the fused decision of request i, three waves at once (lane per position), from
+// the staged segment partials:
+//   wave 0: target row statistics of positions k <= L (log2-sum-exp, or the argmax for the
+//           greedy rule; top-k rows were finished by the streaming kernel),
+//   wave 1: draft row statistics of positions k < L (top-k: the streaming kernel's test),
+//   wave 2: the acceptance uniforms of positions k < L (sampling rows without top-k).
+__device__ void decide_stats(PassShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = a.G, V = a.V, nseg = a.nseg;
+  const int L = in.L;
+  if (decide_status(a, in)) return;
+  const float T = in.T;
+  const bool greedy = (T == 0.f);
+  const bool topk = !greedy && in.K0 > 0 && in.K0 < V;
+  if (wave == 0) {
+    int bad = 0;
+    for (int k = lane; k <= L; k += SPEC_WAVE) {
+      const Partial* pt = sh.stage + k * nseg;
+      if (topk) {
+        const RowStat rt = a.rows_t[(size_t)i * (G + 1) + k];
+        bad |= !(rt.lse2 == rt.lse2);
+        sh.rt[k] = rt;
+      } else if (greedy) {
+        const int am = combine_argmax(pt, nseg);
+        bad |= am < 0;
+        sh.rt[k] = RowStat{0.0, -INFINITY, am < 0 ? 0 : am};
+      } else {
+        const double l2t = combine_sum(pt, nseg);
+        bad |= !(l2t == l2t);
+        sh.rt[k] = RowStat{l2t, -INFINITY, 0};
+      }
+    }
+    const int any = __ballot(bad) != 0ull;
+    if (lane == 0) sh.bad_t = any;
+  } else if (wave == 1) {
+    int bad = 0;
+    const Partial* stage_d = sh.stage + (G + 1) * nseg;
+    for (int k = lane; k < L; k += SPEC_WAVE) {
+      if (topk) {
+        const AccRec ar = a.acc[(size_t)i * G + k];
+        sh.tacc[k] = ar.accept;
+        sh.accr[k] = ar.r;
+        sh.rd[k] = a.rows_d[(size_t)i * G + k];
+      } else if (!greedy) {
+        const double l2d = combine_sum(stage_d + k * nseg, nseg);
+        bad |= !(l2d == l2d);
+        sh.rd[k] = RowStat{l2d, -INFINITY, 0};
+      }
+    }
+    const int any = __ballot(bad) != 0ull;
+    if (lane == 0) sh.bad_d = any;
+  } else if (!greedy && !topk) {
+    for (int k = lane; k < L; k += SPEC_WAVE) {
+      double ua, ue;
+      verify_uniforms(in.seed, (uint64_t)i, (uint64_t)k, &ua, &ue);
+      sh.ua[k] = ua;
+    }
+  }
+}
+
+// Second half (wave 0, after a barrier): r = min(1, p_t(x)/p_d(x)) with the logits at x the
+// partials carry, the test, the first rejection.  Leaves in sh: st, n, L, greedy, and per position
+// the acceptance ratio and the draft token.
+__device__ void decide_final(PassShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
   const int lane = threadIdx.x;
   const int G = a.G, V = a.V, nseg = a.nseg;
-  const int L = a.lengths ? a.lengths[i] : G;
-  int st = 0;
-  if (L < 0 || L > G) {
-    if (lane == 0) {
-      sh.st = SPEC_REQ_BAD_LENGTH;
-      sh.n = 0;
-    }
-    return;
+  const int L = in.L;
+  const float T = in.T;
+  if (lane == 0) {
+    sh.L = L;
+    sh.greedy = (T == 0.f);
   }
-  const float T = a.temperature[i];
-  const int K0 = a.top_k ? a.top_k[i] : 0;
-  if (!(T >= 0.f && T < INFINITY)) st |= SPEC_REQ_BAD_TEMPERATURE;
-  if (K0 < 0) st |= SPEC_REQ_BAD_TOPK;
-  const int x = (lane < L) ? a.tokens[(size_t)i * G + lane] : 0;
-  if (__ballot(lane < L && (x < 0 || x >= V))) st |= SPEC_REQ_BAD_TOKEN;
-  if (st == 0) st |= a.req_status[i];
+  const int st = decide_status(a, in);
   if (st) {
     if (lane == 0) {
       sh.st = st;
@@ -654,49 +841,36 @@ __device__ void decide_full(PassShared& sh, const VerifyArgs& a, int i) {
     }
     return;
   }
-  const bool greedy = (T == 0.f);
-  const bool topk = !greedy && K0 > 0 && K0 < V;
-  const double c64 = greedy ? 0.0 : kLog2e / (double)T;
-  int accept = 1, bad = 0;
-  for (int k = lane; k <= L; k += SPEC_WAVE) {
-    const size_t rt_i = (size_t)i * (G + 1) + k, rd_i = (size_t)i * G + k;
-    const Partial* pt = a.part_t + rt_i * nseg;
-    const Partial* pd = a.part_d + rt_i * nseg;
-    int acc_k = 1;
-    if (topk) {
-      bad |= !(a.rows_t[rt_i].lse2 == a.rows_t[rt_i].lse2);
-      if (k < L) acc_k = a.acc[rd_i].accept;
-    } else if (greedy) {
-      const int am = combine_argmax(pt, nseg);
-      bad |= am < 0;
-      a.rows_t[rt_i] = RowStat{0.0, -INFINITY, am < 0 ? 0 : am};
-      if (k < L) {
-        acc_k = (x == am);
-        a.acc[rd_i] = AccRec{acc_k ? 1.0 : 0.0, acc_k, 1};
-      }
-    } else {
-      const double l2t = combine_sum(pt, nseg);
-      bad |= !(l2t == l2t);
-      a.rows_t[rt_i] = RowStat{l2t, -INFINITY, 0};
-      if (k < L) {
-        const double l2d = combine_sum(pd, nseg);
-        bad |= !(l2d == l2d);
-        a.rows_d[rd_i] = RowStat{l2d, -INFINITY, 0};
-        const double r = acceptance_ratio(pt[0].zx, pd[0].zx, c64, l2t, -INFINITY, l2d, -INFINITY);
-        double ua, ue;
-        verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)k, &ua, &ue);
-        acc_k = ua < r;
-        a.acc[rd_i] = AccRec{r, acc_k, 1};
-      }
-    }
-    if (k < L) accept = acc_k;   // k < L <= 64: the lane's first round
-  }
-  if (__ballot(bad)) {
+  if (sh.bad_t | sh.bad_d) {
     if (lane == 0) {
       sh.st = SPEC_REQ_NONFINITE;
       sh.n = 0;
     }
     return;
+  }
+  if (lane < G) sh.x[lane] = in.x;
+  const bool greedy = (T == 0.f);
+  const bool topk = !greedy && in.K0 > 0 && in.K0 < V;
+  const double c64 = greedy ? 0.0 : kLog2e / (double)T;
+  const Partial* stage_d = sh.stage + (G + 1) * nseg;
+  int accept = 1;
+  if (lane < L) {   // L <= 64: one position per lane
+    const int k = lane;
+    int acc_k;
+    double r;
+    if (topk) {
+      acc_k = sh.tacc[k];
+      r = sh.accr[k];
+    } else if (greedy) {
+      acc_k = (in.x == sh.rt[k].argmax);
+      r = acc_k ? 1.0 : 0.0;
+    } else {
+      r = acceptance_ratio(sh.stage[k * nseg].zx, stage_d[k * nseg].zx, c64, sh.rt[k].lse2, -INFINITY,
+                           sh.rd[k].lse2, -INFINITY);
+      acc_k = sh.ua[k] < r;
+    }
+    accept = acc_k;
+    sh.accr[k] = r;
   }
   const unsigned long long rej = __ballot(lane < L && !accept);
   if (lane == 0) {
@@ -705,10 +879,28 @@ __device__ void decide_full(PassShared& sh, const VerifyArgs& a, int i) {
   }
 }
 
+// Status, num_accepted, accept_prob and the output tokens of request i from the fused decision
+// in sh (threads 0 .. G); the emitted token of a sampling request is left to sample_emit.
+__device__ __forceinline__ void decided_outputs(const PassShared& sh, const VerifyArgs& a, int i) {
+  const int tid = threadIdx.x, G = a.G;
+  const int st = sh.st, n = sh.n, L = sh.L;
+  if (tid == 0) {
+    if (a.status) a.status[i] = st;
+    a.num_accepted[i] = st ? 0 : n;
+  }
+  if (a.accept_prob && tid < G) a.accept_prob[(size_t)i * G + tid] = (!st && tid < L) ? (float)sh.accr[tid] : NAN;
+  if (tid <= G) {
+    int v = -1;
+    if (!st && tid < n) v = sh.x[tid];
+    else if (!st && tid == n && sh.greedy) v = sh.rt[n].argmax;
+    if (st || tid != n || sh.greedy) a.out_tokens[(size_t)i * (G + 1) + tid] = v;
+  }
+}
+
 // One 1024-thread workgroup per request does all of the request's work after the streaming:
 // the acceptance decision from the segment partials, the emit pass over the whole emit row pair
-// (16 waves), then finish_request from the range sums it keeps in LDS.  Used when there are
-// at least as many requests as compute units.
+// (16 waves), then sample_emit from the range sums it keeps in LDS.  Used when there are at
+// least as many requests as compute units.
 template <bool BF16>
 __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a) {
   __shared__ PassShared ps;
@@ -718,26 +910,39 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
   const int NR = num_ranges(a.V);
   init_t64(ps.T64);
   init_t64(fs.T64);
-  if (tid < SPEC_WAVE) decide_full(ps, a, i);
+  if (tid == 0) ps.amb_cnt = 0;
+  DecideIn din;
+  if (tid < 3 * SPEC_WAVE) din = decide_loads(a, i);
+  stage_partials(ps, a, i);
   __syncthreads();
+  if (tid < 3 * SPEC_WAVE) decide_stats(ps, a, i, din);
+  __syncthreads();
+  if (tid < SPEC_WAVE) decide_final(ps, a, i, din);
+  __syncthreads();
+  decided_outputs(ps, a, i);
   const int st = ps.st, n = ps.n;
-  if (!st && !a.greedy_only && a.temperature[i] != 0.f) {
-    run_pass<BF16>(ps, a, i, 0, n, fs.rg);
-    if (tid < SPEC_WAVE) {
-      double x = 0.0;
-      for (int r = tid; r < NR; r += SPEC_WAVE) x += fs.rg[r].t;
-      x = wave_sum(x);
-      if (tid == 0) {
-        double y = 0.0;
-        for (int w = 0; w < kFusedThreads / SPEC_WAVE; ++w) y += ps.red[1][w];
-        fs.St = x;
-        fs.Sd = y;
-        fs.na = atomicAdd(&a.ereq[i].amb_n, 0);   // read at L2, where the pass counted
-      }
+  if (st || ps.greedy) return;
+  // the table overwrites the staged partials: every wave is past the decision
+  EmitRows e = emit_rows_from<BF16>(a, i, n, ps.L, a.temperature[i], ps.rt[n], ps.rd[n < ps.L ? n : 0]);
+  e.amb_n = &ps.amb_cnt;
+  e.amb_v = ps.amb_list;
+  const int K = a.top_k ? a.top_k[i] : 0;
+  e.Qt = (BF16 && !(K > 0 && K < a.V)) ? ps.Qt : nullptr;   // the pass builds it for these rows
+  run_pass<BF16>(ps, a, i, 0, e, fs.rg);
+  if (tid < SPEC_WAVE) {
+    double x = 0.0;
+    for (int r = tid; r < NR; r += SPEC_WAVE) x += fs.rg[r].t;
+    x = wave_sum(x);
+    if (tid == 0) {
+      double y = 0.0;
+      for (int w = 0; w < kFusedThreads / SPEC_WAVE; ++w) y += ps.red[1][w];
+      fs.St = x;
+      fs.Sd = y;
+      fs.na = ps.amb_cnt;
     }
-    __syncthreads();
   }
-  finish_request<BF16>(fs, a, i, st, n);
+  __syncthreads();
+  sample_emit<BF16, kFusedThreads>(fs, a, i, n, e);
 }
 
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s) {

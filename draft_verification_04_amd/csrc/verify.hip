@@ -123,12 +123,25 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
       carry[tid] = run;
     }
     __syncthreads();
-    for (int k = 0; k <= G; ++k) {
-      const unsigned long long m = __ballot(L >= k);
-      if (L >= k) {
-        const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
-        a.items[idx] = (i << 7) | k;
-        a.items_x[idx] = (a.tokens && !a.overlap_only && k < L) ? a.tokens[(size_t)i * G + k] : -1;
+    // eight positions at a time: their draft tokens are loaded together, then the items written
+    const bool want_x = a.tokens && !a.overlap_only;
+    for (int k0 = 0; k0 <= G; k0 += 8) {
+      int xs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        xs[u] = (want_x && k < L) ? a.tokens[(size_t)i * G + k] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        if (k > G) break;
+        const unsigned long long m = __ballot(L >= k);
+        if (L >= k) {
+          const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
+          a.items[idx] = (i << 7) | k;
+          a.items_x[idx] = xs[u];
+        }
       }
     }
     __syncthreads();
@@ -765,7 +778,7 @@ struct WsLayout {
 // Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
 static int stream_segments(int V, int es) {
   const long long n = (long long)V * es / 49152;
-  return (int)(n < 1 ? 1 : (n > 16 ? 16 : n));
+  return (int)(n < 1 ? 1 : (n > kMaxStreamSegs ? kMaxStreamSegs : n));
 }
 
 static WsLayout ws_layout(int B, int G, int V, int nseg) {
@@ -826,18 +839,18 @@ int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size
 }
 
 size_t workspace_bytes(int B, int G, int V, bool emit) {
-  return ws_layout(B, G, emit ? V : 1, 16).total;   // the largest segment count, fp32 or bf16
+  return ws_layout(B, G, emit ? V : 1, kMaxStreamSegs).total;   // the largest segment count, fp32 or bf16
 }
 
 void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1) {
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
-  if (ev0) hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);
+  if (ev0) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);   // a failure shows on the caller's event query
   const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1) * a.nseg);
   if (dtype == SPEC_BF16)
     hipLaunchKernelGGL(stream_kernel<true>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   else
     hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
-  if (ev1) hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
+  if (ev1) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
 }
 
 void launch_combine(const VerifyArgs& a, hipStream_t s) {

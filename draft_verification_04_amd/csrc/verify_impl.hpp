@@ -85,6 +85,7 @@ struct VerifyArgs {
 };
 
 constexpr int kStreamThreads = 512;
+constexpr int kMaxStreamSegs = 16;   // segments per row in the streaming kernel, at most
 constexpr int kWorklistThreads = 1024;
 constexpr int kPassThreads = 512;    // emit pass workgroup
 constexpr int kEmitThreads = 256;    // emit final workgroup (x 8 tokens = one range)

@@ -97,16 +97,21 @@ def test_greedy_ties_and_fp32(sv):
         assert (to_np(out["out_tokens"]) == ref["out_tokens"]).all()
 
 
-def test_verify_edge_cases(sv):
+@pytest.mark.parametrize("rep,V,dtype", [
+    (1, 777, torch.float32),      # 16 requests: the split emit; odd V, rows off 16-byte boundaries
+    (16, 777, torch.float32),     # 256 requests: one fused workgroup per request
+    (1, 2600, torch.bfloat16),    # bf16, V a multiple of 8: the last, partial range read as vectors
+    (16, 2600, torch.bfloat16),
+])
+def test_verify_edge_cases(sv, rep, V, dtype):
     rng = np.random.default_rng(3)
-    B, G, V = 16, 4, 777
+    B, G = 16, 4
     t = rng.normal(0, 3, (B, G + 1, V)).astype(np.float32)
     d = t[:, :G] + rng.normal(0, 1, (B, G, V)).astype(np.float32)
     x = rng.integers(0, V, (B, G)).astype(np.int32)
     L = np.array([0, 1, 2, 3, 4] * 3 + [4], dtype=np.int32)
     T = np.ones(B, dtype=np.float32)
     K = np.zeros(B, dtype=np.int32)
-    seed = rng.integers(0, 2 ** 63, B).astype(np.int64)
     d[1] = t[1, :G]                        # identical distributions: everything accepted
     t[2, :, ::3] = -np.inf                 # masked tokens
     d[2, :, ::3] = -np.inf
@@ -125,18 +130,23 @@ def test_verify_edge_cases(sv):
     T[13] = 0.0                            # greedy rule inside spec_verify
     L[14] = G + 1                          # bad length
     K[15] = -2                             # bad top-k
-    tt = torch.from_numpy(t).to(DEV)
-    dd = torch.from_numpy(d).to(DEV)
+    # rep copies of the 16 cases, each copy with its own seeds
+    t, d, x = np.tile(t, (rep, 1, 1)), np.tile(d, (rep, 1, 1)), np.tile(x, (rep, 1))
+    L, T, K = np.tile(L, rep), np.tile(T, rep), np.tile(K, rep)
+    seed = rng.integers(0, 2 ** 63, B * rep).astype(np.int64)
+    tt = torch.from_numpy(t).to(DEV).to(dtype)
+    dd = torch.from_numpy(d).to(DEV).to(dtype)
     args = [torch.from_numpy(a).to(DEV) for a in (x, L, T, K, seed)]
     out = sv.verify(tt, dd, *args)
     torch.cuda.synchronize()
-    ref = oracle.verify(t, d, x, L, T, K, seed)
+    ref = oracle.verify(tt, dd, x, L, T, K, seed)
     compare_verify(out, ref)
-    st = to_np(out["status"])
-    assert st[8] == oracle.STATUS_BAD_TOKEN and st[9] == oracle.STATUS_BAD_TEMPERATURE
-    assert st[10] == oracle.STATUS_NONFINITE and st[11] == 0 and st[12] == oracle.STATUS_NONFINITE
-    assert st[14] == oracle.STATUS_BAD_LENGTH and st[15] == oracle.STATUS_BAD_TOPK
-    assert to_np(out["num_accepted"])[1] == L[1]
+    st = to_np(out["status"]).reshape(rep, B)
+    assert (st[:, 8] == oracle.STATUS_BAD_TOKEN).all() and (st[:, 9] == oracle.STATUS_BAD_TEMPERATURE).all()
+    assert (st[:, 10] == oracle.STATUS_NONFINITE).all() and (st[:, 11] == 0).all()
+    assert (st[:, 12] == oracle.STATUS_NONFINITE).all()
+    assert (st[:, 14] == oracle.STATUS_BAD_LENGTH).all() and (st[:, 15] == oracle.STATUS_BAD_TOPK).all()
+    assert (to_np(out["num_accepted"]).reshape(rep, B)[:, 1] == L[1]).all()
 
 
 def test_single_token_vocabulary(sv):
