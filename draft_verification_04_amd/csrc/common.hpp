@@ -40,6 +40,10 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Workgroup barrier for LDS data: the LDS writes issued before it are complete and seen by every
+// wave after it, while global loads in flight stay in flight (__syncthreads waits for those too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, SPEC_WAVE);

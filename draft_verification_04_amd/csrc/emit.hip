@@ -75,11 +75,15 @@ __device__ __forceinline__ void init_t64(double* T64) {
 // The table of Q over the tabulated bf16 values.  Entry 2 (m - m0) + s holds the value with sign
 // s and magnitude bits m (m0 the first tabulated magnitude): the index is the bf16 bit pattern
 // rotated left by one, less 2 m0, which two 16-bit integer instructions give for a pair of values.
-__device__ void build_qtab(double* Qt, double invT, double R, const double* T64) {
-  for (int idx = threadIdx.x; idx < kQsize; idx += blockDim.x) {
+__device__ void build_qtab_part(double* Qt, double invT, double R, const double* T64, int t0, int nthr) {
+  for (int idx = t0; idx < kQsize; idx += nthr) {
     const uint32_t bits = ((uint32_t)(idx & 1) << 15) | ((uint32_t)(kQefLo << 7) + ((uint32_t)idx >> 1));
     Qt[idx] = q_direct(__uint_as_float(bits << 16), invT, R, T64);
   }
+}
+
+__device__ __forceinline__ void build_qtab(double* Qt, double invT, double R, const double* T64) {
+  build_qtab_part(Qt, invT, R, T64, (int)threadIdx.x, (int)blockDim.x);
 }
 
 struct EmitRows {
@@ -190,26 +194,27 @@ constexpr int kMaxWaves = 1024 / SPEC_WAVE;  // largest emit workgroup, in waves
 
 struct PassShared {
   double T64[64];
-  union {
-    double Qt[kQsize];
-    // the fused decision's copy of the request's segment partials (target rows, then draft rows),
-    // used before the table is built
-    Partial stage[2 * (SPEC_MAX_GAMMA + 1) * kMaxStreamSegs];
-  };
+  double Qt[kQsize];
   double red[2][kMaxWaves];
-  // the fused decision, per draft position: row records, acceptance ratios, draft tokens
+  int st, n;
+};
+
+// The fused kernel's decision: the request's segment partials (target rows, then draft rows), per
+// draft position the row records, acceptance uniforms and ratios and draft tokens, the offset of
+// the table built meanwhile, and the list of uncertain-sign tokens of the pass.
+struct DecideShared {
+  Partial stage[2 * (SPEC_MAX_GAMMA + 1) * kMaxStreamSegs];
   RowStat rt[SPEC_MAX_GAMMA + 1], rd[SPEC_MAX_GAMMA];
   double accr[SPEC_MAX_GAMMA];
   double ua[SPEC_MAX_GAMMA];
   int tacc[SPEC_MAX_GAMMA];
   int x[SPEC_MAX_GAMMA];
   int st, n, L, greedy, bad_t, bad_d;
-  // the fused kernel's uncertain-sign tokens
+  double R0;
+  int table_ok;
   int amb_cnt;
   int amb_list[kAmbCap];
 };
-static_assert(sizeof(Partial) * 2 * (SPEC_MAX_GAMMA + 1) * kMaxStreamSegs <= sizeof(double) * kQsize,
-              "the staged partials fit in the table's memory");
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
@@ -239,8 +244,12 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
                                           double cdh, double cdl, int v0, const VerifyArgs& a, int i,
                                           const double* T64, const double* Qt, bool live = true) {
   constexpr bool resid = RESID;
-  const uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
-  const uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
+  uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
+  uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
+  if (MASK && !live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wt[q] = wd[q] = kFill2;
+  }
   us2 kt[4], kd[4];
   us2 kmax = (us2)(unsigned short)0;
 #pragma unroll
@@ -263,7 +272,7 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
       for (int j = 0; j < 4; ++j) {
         qt[j] = Qt[slot_of(kt, h + j)];
         qd[j] = resid ? Qt[slot_of(kd, h + j)] : 0.0;
-        if (MASK && !live) qt[j] = qd[j] = 0.0;
+        if (MASK && !live) qt[j] = qd[j] = 0.0;   // filler bits: tabulated, and worth nothing
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -296,11 +305,11 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
 
 // The ranges of request i that segment `seg` owns, each written as an EmitRange to out[r]
 // (global memory, or LDS when the same workgroup finishes the request); each wave's sum of
-// E_d goes to sh.red[1][wave].  bf16 rows without top-k build the Q table in sh.Qt here (the
-// whole workgroup calls this function).
+// E_d goes to sh.red[1][wave].  bf16 rows without top-k build the Q table in sh.Qt here unless
+// table_ready (the whole workgroup calls this function).
 template <bool BF16, bool TOPK>
 __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e,
-                            EmitRange* out) {
+                            EmitRange* out, bool table_ready) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int NWPB = (int)(blockDim.x >> 6);
   const int NWT = a.emit_segs * NWPB;
@@ -318,23 +327,23 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
     // of 8 the row's last, partial range is read the same way, lanes past the end masked.
     const int NRv = (aligned && (V & 7) == 0) ? NR : NRfull;
     uint4 bt[kSubPerRange], bd[kSubPerRange];
+    // every lane loads (a lane past the row's end reads the row's last vector, masked in its
+    // step): a load under a lane condition would make the compiler wait for it at once
     auto load = [&](int rr, int sub, uint4& t, uint4& d) {
-      const int v0 = rr * kRangeElems + sub * kSub + lane * 8;
-      if (v0 < V) {
-        const size_t off = (size_t)v0 * 2;
-        t = *reinterpret_cast<const uint4*>(e.t + off);
-        d = resid ? *reinterpret_cast<const uint4*>(e.d + off) : make_uint4(0, 0, 0, 0);
-      } else {
-        t = d = make_uint4(kFill2, kFill2, kFill2, kFill2);
-      }
+      const int v0 = min(rr * kRangeElems + sub * kSub + lane * 8, V - 8);
+      const size_t off = (size_t)v0 * 2;
+      t = *reinterpret_cast<const uint4*>(e.t + off);
+      d = resid ? *reinterpret_cast<const uint4*>(e.d + off) : make_uint4(0, 0, 0, 0);
     };
     if (r < NRv) {
 #pragma unroll
       for (int sub = 0; sub < kSubPerRange; ++sub) load(r, sub, bt[sub], bd[sub]);
     }
-    // the table of Q over the bf16 values, built while the first loads are in flight
-    build_qtab(sh.Qt, e.invT, e.R, sh.T64);
-    __syncthreads();
+    // the table of Q over the bf16 values (unless already built with offset e.R), built while the
+    // first loads are in flight (the barrier leaves them in flight: each wave waits only for the
+    // step it works on)
+    if (!table_ready) build_qtab(sh.Qt, e.invT, e.R, sh.T64);
+    lds_barrier();
     while (r < NRv) {
       const int rn = r + NWT;
       c.A = c.D = c.T = 0.0;
@@ -408,22 +417,23 @@ __device__ __forceinline__ void decide_into(PassShared& sh, const VerifyArgs& a,
 
 // The emit pass over segment `seg` of request i (after its decision, sampling only).
 template <bool BF16>
-__device__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e, EmitRange* out) {
-  const int K = a.top_k ? a.top_k[i] : 0;
-  if (K > 0 && K < a.V) pass_ranges<BF16, true>(sh, a, i, seg, e, out);
-  else pass_ranges<BF16, false>(sh, a, i, seg, e, out);
+__device__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e, EmitRange* out,
+                         int K, bool table_ready = false) {
+  if (K > 0 && K < a.V) pass_ranges<BF16, true>(sh, a, i, seg, e, out, false);
+  else pass_ranges<BF16, false>(sh, a, i, seg, e, out, table_ready);
   __syncthreads();
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kPassThreads) void emit_pass_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kPassThreads, 4) void emit_pass_kernel(VerifyArgs a) {
   __shared__ PassShared sh;
   const int i = a.r0 + (int)blockIdx.x / a.emit_segs, seg = (int)blockIdx.x % a.emit_segs;
   init_t64(sh.T64);
   decide_into(sh, a, i);
   const int st = sh.st, n = sh.n;
   if (st || a.temperature[i] == 0.f) return;
-  run_pass<BF16>(sh, a, i, seg, emit_rows<BF16>(a, i, n), a.ranges + (size_t)i * num_ranges(a.V));
+  run_pass<BF16>(sh, a, i, seg, emit_rows<BF16>(a, i, n), a.ranges + (size_t)i * num_ranges(a.V),
+                 a.top_k ? a.top_k[i] : 0);
   if (threadIdx.x == 0) {
     double y = 0.0;
     for (int w = 0; w < kPassThreads / SPEC_WAVE; ++w) y += sh.red[1][w];
@@ -741,7 +751,7 @@ __device__ __forceinline__ DecideIn decide_loads(const VerifyArgs& a, int i) {
 
 // The segment partials of every row of request i (target rows, then draft rows; those of rows
 // past L are read but not used) copied to sh.stage by the whole workgroup.
-__device__ __forceinline__ void stage_partials(PassShared& sh, const VerifyArgs& a, int i) {
+__device__ __forceinline__ void stage_partials(DecideShared& sh, const VerifyArgs& a, int i) {
   const int per = (a.G + 1) * a.nseg;
   const Partial* gt = a.part_t + (size_t)i * per;
   const Partial* gd = a.part_d + (size_t)i * per;
@@ -767,7 +777,7 @@ __device__ __forceinline__ int decide_status(const VerifyArgs& a, const DecideIn
 //           greedy rule; top-k rows were finished by the streaming kernel),
 //   wave 1: draft row statistics of positions k < L (top-k: the streaming kernel's test),
 //   wave 2: the acceptance uniforms of positions k < L (sampling rows without top-k).
-__device__ void decide_stats(PassShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+__device__ void decide_stats(DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int G = a.G, V = a.V, nseg = a.nseg;
   const int L = in.L;
@@ -824,7 +834,7 @@ __device__ void decide_stats(PassShared& sh, const VerifyArgs& a, int i, const D
 // Second half (wave 0, after a barrier): r = min(1, p_t(x)/p_d(x)) with the logits at x the
 // partials carry, the test, the first rejection.  Leaves in sh: st, n, L, greedy, and per position
 // the acceptance ratio and the draft token.
-__device__ void decide_final(PassShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+__device__ void decide_final(DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
   const int lane = threadIdx.x;
   const int G = a.G, V = a.V, nseg = a.nseg;
   const int L = in.L;
@@ -879,9 +889,42 @@ __device__ void decide_final(PassShared& sh, const VerifyArgs& a, int i, const D
   }
 }
 
+// The Q table of a sampling request without top-k, built by the waves the decision leaves idle
+// (waves 3 .. 15 of the fused workgroup) before the emit row is known.  Any offset R gives the
+// same probabilities (p = Q / sum Q over the row); this one is an upper bound of z/T over every
+// row the emit may read: a segment's reference m satisfies z log2(e)/T <= m + 32 for each of its
+// values (the streaming kernel raises m whenever a term would pass 2^32), so with
+// R0 = ln2 (max m + 40) every entry is below 2^-7.  The reference is also at most one above the
+// segment's largest value, so the emit row's own largest entries stay normal unless its lse lies
+// far below R0; the fused kernel then rebuilds the table with that lse.
+template <bool BF16>
+__device__ void early_table(PassShared& ps, DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+  const int t = (int)threadIdx.x - 3 * SPEC_WAVE, lane = threadIdx.x & 63;
+  const int nthr = (int)blockDim.x - 3 * SPEC_WAVE;
+  const int L = in.L, nseg = a.nseg;
+  const bool sampling = !decide_status(a, in) && in.T > 0.f && !(in.K0 > 0 && in.K0 < a.V);
+  if (!BF16 || !sampling) {
+    if (t == 0) sh.table_ok = 0;
+    return;
+  }
+  float mmax = -INFINITY;
+  for (int q = lane; q < (L + 1) * nseg; q += SPEC_WAVE) {
+    const Partial& p = sh.stage[q];
+    if (p.v > 0.0) mmax = fmaxf(mmax, p.m);
+  }
+  mmax = wave_max(mmax);
+  const bool ok = mmax > -INFINITY && mmax < INFINITY;
+  const double R0 = ((double)mmax + 40.0) * kLn2;
+  if (ok) build_qtab_part(ps.Qt, 1.0 / (double)in.T, R0, ps.T64, t, nthr);
+  if (t == 0) {
+    sh.table_ok = ok;
+    sh.R0 = R0;
+  }
+}
+
 // Status, num_accepted, accept_prob and the output tokens of request i from the fused decision
 // in sh (threads 0 .. G); the emitted token of a sampling request is left to sample_emit.
-__device__ __forceinline__ void decided_outputs(const PassShared& sh, const VerifyArgs& a, int i) {
+__device__ __forceinline__ void decided_outputs(const DecideShared& sh, const VerifyArgs& a, int i) {
   const int tid = threadIdx.x, G = a.G;
   const int st = sh.st, n = sh.n, L = sh.L;
   if (tid == 0) {
@@ -904,31 +947,40 @@ __device__ __forceinline__ void decided_outputs(const PassShared& sh, const Veri
 template <bool BF16>
 __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a) {
   __shared__ PassShared ps;
+  __shared__ DecideShared ds;
   __shared__ FinalShared fs;
   const int i = a.r0 + (int)blockIdx.x;
   const int tid = threadIdx.x;
   const int NR = num_ranges(a.V);
   init_t64(ps.T64);
   init_t64(fs.T64);
-  if (tid == 0) ps.amb_cnt = 0;
-  DecideIn din;
-  if (tid < 3 * SPEC_WAVE) din = decide_loads(a, i);
-  stage_partials(ps, a, i);
+  if (tid == 0) ds.amb_cnt = 0;
+  const DecideIn din = decide_loads(a, i);
+  stage_partials(ds, a, i);
   __syncthreads();
-  if (tid < 3 * SPEC_WAVE) decide_stats(ps, a, i, din);
+  if (tid < 3 * SPEC_WAVE) decide_stats(ds, a, i, din);
+  else early_table<BF16>(ps, ds, a, i, din);
   __syncthreads();
-  if (tid < SPEC_WAVE) decide_final(ps, a, i, din);
+  if (tid < SPEC_WAVE) decide_final(ds, a, i, din);
   __syncthreads();
-  decided_outputs(ps, a, i);
-  const int st = ps.st, n = ps.n;
-  if (st || ps.greedy) return;
-  // the table overwrites the staged partials: every wave is past the decision
-  EmitRows e = emit_rows_from<BF16>(a, i, n, ps.L, a.temperature[i], ps.rt[n], ps.rd[n < ps.L ? n : 0]);
-  e.amb_n = &ps.amb_cnt;
-  e.amb_v = ps.amb_list;
-  const int K = a.top_k ? a.top_k[i] : 0;
-  e.Qt = (BF16 && !(K > 0 && K < a.V)) ? ps.Qt : nullptr;   // the pass builds it for these rows
-  run_pass<BF16>(ps, a, i, 0, e, fs.rg);
+  const int st = ds.st, n = ds.n;
+  if (st || ds.greedy) {
+    decided_outputs(ds, a, i);
+    return;
+  }
+  EmitRows e = emit_rows_from<BF16>(a, i, n, ds.L, din.T, ds.rt[n], ds.rd[n < ds.L ? n : 0]);
+  e.amb_n = &ds.amb_cnt;
+  e.amb_v = ds.amb_list;
+  const bool table = BF16 && !(din.K0 > 0 && din.K0 < a.V);
+  e.Qt = table ? ps.Qt : nullptr;
+  // the early table serves unless the emit row's lse lies far below its offset (then the pass
+  // builds another with the row's own)
+  const bool ready = table && ds.table_ok && ds.R0 - e.R <= 600.0;
+  if (ready) e.R = ds.R0;
+  run_pass<BF16>(ps, a, i, 0, e, fs.rg, din.K0, ready);
+  // the outputs known since the decision, written once the pass's loads are under way (a later
+  // wait for a load would otherwise wait for these stores too)
+  decided_outputs(ds, a, i);
   if (tid < SPEC_WAVE) {
     double x = 0.0;
     for (int r = tid; r < NR; r += SPEC_WAVE) x += fs.rg[r].t;
@@ -938,7 +990,7 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
       for (int w = 0; w < kFusedThreads / SPEC_WAVE; ++w) y += ps.red[1][w];
       fs.St = x;
       fs.Sd = y;
-      fs.na = ps.amb_cnt;
+      fs.na = ds.amb_cnt;
     }
   }
   __syncthreads();
