@@ -100,8 +100,9 @@ def main():
         if greedy:
             sv.verify_greedy(tgt, w.draft_tokens, L, out=ver_out, workspace=ws, stream=stream)
         else:
+            # lengths from the scheduler: its token budget bounds sum (L_i + 1)
             sv.verify(tgt, drf, w.draft_tokens, L, w.temperature, w.top_k, w.seed, out=ver_out, workspace=ws,
-                      stream=stream, events=events)
+                      stream=stream, events=events, max_tokens=w.budget if w.conf is not None else None)
 
     for s in range(args.warmup):
         step(s)
@@ -213,7 +214,8 @@ def _kernel_sha():
 
 def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
     """Best rate of spec_read_ceiling (a plain 16-byte read kernel) over `nbytes` of the logits,
-    alternating the input copies as the timed steps do, over a few grid sizes."""
+    alternating the input copies as the timed steps do, over grid sizes up to a few vectors per
+    thread (the largest grids read fastest on this device)."""
     from draft_verification_04_amd.hipevents import HipEvent
     dev = copies[0][0].device
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -221,7 +223,7 @@ def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
     if src[0].numel() * src[0].element_size() < nbytes:  # more bytes than the target rows hold
         src = [torch.empty(nbytes + 16, dtype=torch.uint8, device=dev) for _ in range(len(copies))]
     best = None
-    for grid in (1024, 2048, 4096):
+    for grid in (2048, 4096, 8192, 16384, 32768):
         for r in range(2):   # warm-up
             sv.read_ceiling(src[r % len(src)], nbytes, grid, sink, stream)
         e0, e1 = HipEvent(), HipEvent()

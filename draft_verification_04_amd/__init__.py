@@ -48,6 +48,8 @@ EXPORTS = {
     "spec_verify": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_verify_profiled": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P,
                                   _P, _P]),
+    "spec_verify_bounded": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P,
+                                 _I, _P, _P]),
     "spec_verify_flat": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_verify_greedy_workspace_size": (_Z, [_I, _I]),
     "spec_verify_greedy": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
@@ -150,7 +152,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
            lengths: Optional[torch.Tensor] = None, temperature: Optional[torch.Tensor] = None,
            top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
            out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-           events=None) -> dict:
+           events=None, max_tokens: Optional[int] = None) -> dict:
     """spec_verify on torch tensors.  Returns dict(num_accepted, out_tokens, accept_prob, status).
 
     target [B, gamma+1, V] and draft [B, gamma, V] (float32 or bfloat16);
@@ -158,6 +160,8 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     float32 (default ones); top_k [B] int32 or None; seed [B] int64 holding
     the uint64 bit pattern (default zeros).  `events` = (before, after)
     torch.cuda.Event pair recorded around the row-streaming kernel.
+    `max_tokens` (spec_verify_bounded): the caller's bound on sum_i (L_i + 1),
+    e.g. the scheduler's token budget; it sizes the streaming grid only.
     """
     lib = load_library()
     _dev(target, "target", (torch.float32, torch.bfloat16), 3)
@@ -189,10 +193,14 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     if events is not None:
         ev0 = ctypes.c_void_p(events[0].cuda_event)
         ev1 = ctypes.c_void_p(events[1].cuda_event)
-    code = lib.spec_verify_profiled(
-        B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
-        _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
-        _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream), ev0, ev1)
+    args = (B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
+            _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+            _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream(stream))
+    if max_tokens is None:
+        code = lib.spec_verify_profiled(*args, ev0, ev1)
+    else:
+        code = lib.spec_verify_bounded(*args, int(max_tokens), ev0, ev1)
     _check("spec_verify", code)
     return out
 

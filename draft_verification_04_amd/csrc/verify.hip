@@ -38,6 +38,7 @@ namespace spec {
 __device__ __forceinline__ int last_item(const VerifyArgs& a, int i) {
   const int L = a.lengths ? a.lengths[i] : a.G;
   if (L < 0 || L > a.G) return -1;
+  if (a.max_items > 0 && (a.req_status[i] & SPEC_REQ_OVER_BUDGET)) return -1;
   return a.overlap_only ? L - 1 : L;
 }
 
@@ -83,9 +84,31 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
   }
   for (int t = tid; t < G + 2; t += blockDim.x) hist[t] = 0;
   for (int t = tid; t < G + 1; t += blockDim.x) carry[t] = 0;
-  __syncthreads();
+  if (a.max_items > 0) {
+    // token cap: requests are admitted in index order while sum (L_i + 1) stays within it; the
+    // rest are marked and get no work items
+    long long carry_n = 0;
+    for (int b0 = 0; b0 < B; b0 += blockDim.x) {
+      const int i = b0 + tid;
+      const int L = (i < B) ? (a.lengths ? a.lengths[i] : G) : -1;
+      const long long n = (L >= 0 && L <= G) ? L + 1 : 0;
+      const long long in = wave_inclusive_sum_i64(n, lane);
+      __syncthreads();
+      if (lane == 63) woff_t[wave] = in;
+      __syncthreads();
+      long long bt = carry_n, tt = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        if (w < wave) bt += woff_t[w];
+        tt += woff_t[w];
+      }
+      if (i < B) a.req_status[i] = (n > 0 && bt + in > (long long)a.max_items) ? SPEC_REQ_OVER_BUDGET : 0;
+      carry_n += tt;
+    }
+  } else {
+    for (int i = tid; i < B; i += blockDim.x) a.req_status[i] = 0;
+  }
+  __syncthreads();   // the marks are read below (global memory, this workgroup)
   for (int i = tid; i < B; i += blockDim.x) {
-    a.req_status[i] = 0;
     a.ereq[i].amb_n = 0;
     const int L = last_item(a, i);
     if (L >= 0) atomicAdd(&hist[L], 1);
@@ -145,6 +168,90 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
       }
     }
     __syncthreads();
+  }
+}
+
+// The same work list when every request has a thread of one workgroup (B <= kWorklistThreads,
+// padded layout): the length, the cap mark and the first draft tokens stay in registers, and the
+// per-position counts come from ballots, so the only global round trips are the lengths' and the
+// tokens'.  Items are ordered as by worklist_kernel.
+__global__ __launch_bounds__(kWorklistThreads) void worklist_small_kernel(VerifyArgs a) {
+  __shared__ int cnt[kWorklistThreads / SPEC_WAVE][SPEC_MAX_GAMMA + 1];
+  __shared__ int ctot[SPEC_MAX_GAMMA + 1];
+  __shared__ int off[SPEC_MAX_GAMMA + 2];
+  __shared__ long long wsum[kWorklistThreads / SPEC_WAVE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.G, B = a.B;
+  const int NW = (int)(blockDim.x >> 6);
+  const bool want_x = a.tokens && !a.overlap_only;
+  const int L = (tid < B) ? (a.lengths ? a.lengths[tid] : G) : -1;
+  const bool valid = L >= 0 && L <= G;
+  int xs[8];   // the first eight draft tokens, fetched while the counts are formed
+#pragma unroll
+  for (int u = 0; u < 8; ++u) xs[u] = (want_x && valid && u < L) ? a.tokens[(size_t)tid * G + u] : -1;
+  int drop = 0;
+  if (a.max_items > 0) {
+    // token cap: the running sum of L_i + 1 in request order
+    const long long n = valid ? L + 1 : 0;
+    const long long in = wave_inclusive_sum_i64(n, lane);
+    if (lane == 63) wsum[wave] = in;
+    __syncthreads();
+    long long before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    drop = (n > 0 && before + in > (long long)a.max_items);
+  }
+  if (tid < B) {
+    a.req_status[tid] = drop ? SPEC_REQ_OVER_BUDGET : 0;
+    a.ereq[tid].amb_n = 0;
+  }
+  const int last = (valid && !drop) ? (a.overlap_only ? L - 1 : L) : -1;
+  for (int k = 0; k <= G; ++k) {
+    const unsigned long long m = __ballot(last >= k);
+    if (lane == 0) cnt[wave][k] = __popcll(m);
+  }
+  __syncthreads();
+  if (tid <= G) {
+    // per-wave exclusive offsets within position tid, and its total c_k = #{i : last_i >= k}
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = cnt[w][tid];
+      cnt[w][tid] = run;
+      run += c;
+    }
+    ctot[tid] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // items of position k start at off[k] = c_0 + ... + c_{k-1}
+    const long long c = (lane <= G) ? ctot[lane] : 0;
+    const long long incl = wave_inclusive_sum_i64(c, lane);
+    if (lane <= G) off[lane] = (int)(incl - c);
+    const int total64 = (int)__shfl(incl, 63, SPEC_WAVE);
+    if (lane == 0) {
+      if (G == SPEC_WAVE) off[SPEC_WAVE] = total64;   // position 64 (gamma = 64)
+      const int nit = (G == SPEC_WAVE) ? total64 + ctot[SPEC_WAVE] : total64;
+      off[G + 1] = nit;
+      *a.nitems = nit;
+    }
+  }
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int k0 = 0; k0 <= G; k0 += 8) {
+    int x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      x[u] = (k0 == 0) ? xs[u] : ((want_x && valid && k0 + u < L) ? a.tokens[(size_t)tid * G + k0 + u] : -1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      if (k > G) break;
+      const unsigned long long m = __ballot(last >= k);
+      if (last >= k) {
+        const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
+        a.items[idx] = (tid << 7) | k;
+        a.items_x[idx] = x[u];
+      }
+    }
   }
 }
 
@@ -355,6 +462,7 @@ struct StreamShared {
   float lane_max[8][64];
   int cand_n[2];
   int cnt[2][8];
+  long long sum_q[8];   // per-wave fixed-point sums of the kept candidates
   float cand[2][kTopkCap];
 };
 
@@ -536,10 +644,26 @@ __device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, floa
   float S = 0.f;
   int b2 = 0;
   if (!overflow) {
+    // The candidates sit in LDS in arrival order, which varies from run to run: their terms
+    // (each at most about 1, at most kTopkCap of them) are added as fixed-point integers in units
+    // of 2^-48, exact in any order, and the row's total is rounded once.
+    long long q = 0;
     for (int s = lt; s < ncand; s += nthr) {
       const float z = cand[s];
-      if (z >= theta) S += __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -M)));
+      if (z >= theta) q += (long long)rint((double)__builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -M))) * 0x1p48);
     }
+    q = __shfl(wave_inclusive_sum_i64(q, lane), 63, SPEC_WAVE);
+    if (lane == 0) sh.sum_q[wave] = q;
+    __syncthreads();
+    if (lt == 0) {
+      long long tot = 0;
+      for (int w = first_wave; w < first_wave + nwaves; ++w) tot += sh.sum_q[w];
+      const double Sr = (double)tot * 0x1p-48;
+      // no finite kept logit, or a NaN / +inf: invalid row
+      sh.lse2[which] = (rbad || !(rmax < INFINITY) || !(Sr > 0.0)) ? NAN : (double)M + log2(Sr);
+      sh.theta[which] = theta;
+    }
+    return;
   } else {
     float Mt = M;
     for (int v = lt; v < g.nvec; v += nthr) {
@@ -617,9 +741,12 @@ __device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float
 // One workgroup per (work item, segment).  Target row k and, when k < L, draft row k of
 // the item are streamed together by the two halves of the workgroup; a lone target row uses
 // all eight waves.  combine_kernel then finishes each item from its segment partials.
-// Top-k items are not segmented (segment 0 takes the whole rows and finishes the item).
+// Top-k items are not segmented (segment 0 takes the whole rows and finishes the item).  The
+// grid holds the largest work list the call allows (every position of every request, or the
+// caller's token cap); workgroups past the actual list exit at once.
 template <bool BF16>
-__global__ __launch_bounds__(kStreamThreads) void stream_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void stream_kernel(VerifyArgs a) {
   __shared__ StreamShared sh;
   const int nseg = a.nseg;
   const int g = blockIdx.x / nseg, seg = blockIdx.x - g * nseg;
@@ -843,9 +970,14 @@ size_t workspace_bytes(int B, int G, int V, bool emit) {
 }
 
 void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1) {
-  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
+  if (!a.flat && a.B <= kWorklistThreads)
+    hipLaunchKernelGGL(worklist_small_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   if (ev0) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);   // a failure shows on the caller's event query
-  const unsigned grid = (unsigned)((size_t)a.B * (a.G + 1) * a.nseg);
+  size_t items = (size_t)a.B * (a.G + 1);
+  if (a.max_items > 0 && (size_t)a.max_items < items) items = (size_t)a.max_items;
+  const unsigned grid = (unsigned)(items * a.nseg);
   if (dtype == SPEC_BF16)
     hipLaunchKernelGGL(stream_kernel<true>, dim3(grid), dim3(kStreamThreads), 0, s, a);
   else
@@ -889,14 +1021,13 @@ extern "C" size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma) {
   return workspace_bytes(B, gamma, 1, false);
 }
 
-extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                                        const void* target_logits, const void* draft_logits,
-                                        const int32_t* draft_tokens, const int32_t* lengths,
-                                        const float* temperature, const int32_t* top_k, const uint64_t* seed,
-                                        int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
-                                        int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
-                                        void* event_before, void* event_after) {
-  if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
+static int32_t verify_entry(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens, const int32_t* lengths,
+                            const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                            int32_t* num_accepted, int32_t* out_tokens, float* accept_prob, int32_t* status,
+                            void* workspace, size_t workspace_bytes, void* stream, int32_t max_tokens,
+                            void* event_before, void* event_after) {
+  if (!shape_ok(B, gamma, V, dtype) || max_tokens < 0) return SPEC_ERR_INVALID_ARG;
   if (!target_logits || !draft_logits || !draft_tokens || !temperature || !seed || !num_accepted || !out_tokens)
     return SPEC_ERR_INVALID_ARG;
   if (!aligned16(target_logits) || !aligned16(draft_logits)) return SPEC_ERR_INVALID_ARG;
@@ -905,8 +1036,34 @@ extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int
   a.target = target_logits; a.draft = draft_logits; a.tokens = draft_tokens; a.lengths = lengths;
   a.temperature = temperature; a.top_k = top_k; a.seed = seed;
   a.num_accepted = num_accepted; a.out_tokens = out_tokens; a.accept_prob = accept_prob; a.status = status;
+  a.max_items = max_tokens;
   return launch_verify(a, dtype, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream), event_before,
                        event_after);
+}
+
+extern "C" int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                                        const void* target_logits, const void* draft_logits,
+                                        const int32_t* draft_tokens, const int32_t* lengths,
+                                        const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                                        int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                                        int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
+                                        void* event_before, void* event_after) {
+  return verify_entry(B, gamma, V, dtype, target_logits, draft_logits, draft_tokens, lengths, temperature, top_k,
+                      seed, num_accepted, out_tokens, accept_prob, status, workspace, workspace_bytes, stream, 0,
+                      event_before, event_after);
+}
+
+extern "C" int32_t spec_verify_bounded(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                                       const void* target_logits, const void* draft_logits,
+                                       const int32_t* draft_tokens, const int32_t* lengths,
+                                       const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                                       int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                                       int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
+                                       int32_t max_tokens, void* event_before, void* event_after) {
+  if (max_tokens < 1) return SPEC_ERR_INVALID_ARG;
+  return verify_entry(B, gamma, V, dtype, target_logits, draft_logits, draft_tokens, lengths, temperature, top_k,
+                      seed, num_accepted, out_tokens, accept_prob, status, workspace, workspace_bytes, stream,
+                      max_tokens, event_before, event_after);
 }
 
 extern "C" int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,

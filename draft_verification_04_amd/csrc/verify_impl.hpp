@@ -82,6 +82,7 @@ struct VerifyArgs {
   int64_t* d_off;      // [B] flattened layout: first draft row of request i
   int r0, r1;          // the emit kernels handle requests [r0, r1)
   int emit_segs;       // emit-pass workgroups per request (1 = one fused workgroup, else 2 .. kMaxEmitSegs)
+  int max_items;       // caller's bound on the number of work items (0: none); sizes the streaming grid
 };
 
 constexpr int kStreamThreads = 512;

@@ -86,6 +86,7 @@ enum {
 #define SPEC_REQ_BAD_LENGTH 8       /* lengths[i] outside [0, gamma] */
 #define SPEC_REQ_BAD_TOPK 16        /* top_k[i] < 0 */
 #define SPEC_REQ_BAD_CONFIDENCE 32  /* scheduler: a confidence outside [0, 1] or NaN */
+#define SPEC_REQ_OVER_BUDGET 64     /* spec_verify_bounded: the request's rows did not fit the token cap */
 
 /* Limits of this build. */
 #define SPEC_MAX_GAMMA 64
@@ -158,6 +159,31 @@ int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                              int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
                              int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
                              void* event_before, void* event_after);
+
+/*
+ * spec_verify_bounded -- spec_verify under a token cap, with the optional events
+ * of spec_verify_profiled.
+ *   max_tokens  >= 1: the batch's token budget.  Requests are taken in index
+ *               order, each with a valid length adding L_i + 1 to a running
+ *               sum; the first one that takes the sum past max_tokens, and
+ *               every later one with a valid length, get status
+ *               SPEC_REQ_OVER_BUDGET (when no other SPEC_REQ_* bit applies) and
+ *               the outputs of a failed request (num_accepted 0, out_tokens -1,
+ *               accept_prob NaN); their rows are not read.  Lengths from spec_schedule_lengths with
+ *               the same budget always fit, and then every output equals
+ *               spec_verify's.  The cap sizes the grid of the row-streaming
+ *               kernel, which otherwise holds B * (gamma + 1) items, most of
+ *               them empty under a tight budget.
+ * Everything else as for spec_verify_profiled; SPEC_ERR_INVALID_ARG when
+ * max_tokens < 1.
+ */
+int32_t spec_verify_bounded(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                            const void* target_logits, const void* draft_logits,
+                            const int32_t* draft_tokens, const int32_t* lengths,
+                            const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                            int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                            int32_t* status, void* workspace, size_t workspace_bytes, void* stream,
+                            int32_t max_tokens, void* event_before, void* event_after);
 
 /*
  * spec_verify_flat -- spec_verify on the flattened variable-length layout in

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
               "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size",
               "spec_read_ceiling", "spec_verify_flat", "spec_overlap_mass", "spec_schedule_capacity",
               "spec_schedule_topk", "spec_draft_markov", "spec_draft_workspace_size", "spec_sts_fit",
-              "spec_sts_apply", "spec_sts_workspace_size"):
+              "spec_sts_apply", "spec_sts_workspace_size", "spec_verify_bounded"):
         assert n in names, n
 
 
@@ -184,6 +184,15 @@ def test_verify_flat_requires_lengths(lib):
     assert lib.spec_verify_flat(*bad) == 1                       # no lengths
     bad = list(args); bad[5] = ctypes.c_void_p(p.value + 2)
     assert lib.spec_verify_flat(*bad) == 1                       # misaligned rows
+
+
+def test_verify_bounded_rejects_a_bound_below_one(lib):
+    keep, p = _fake()
+    ws = lib.spec_verify_workspace_size(2, 4, 100)
+    args = [2, 4, 100, 1, p, p, p, p, p, None, p, p, p, None, None, p, ws, None]
+    assert lib.spec_verify_bounded(*args, 0, None, None) == 1
+    assert lib.spec_verify_bounded(*args, -5, None, None) == 1
+    assert lib.spec_verify_bounded(*args, 10, None, None) == 2   # a valid bound; fake workspace refused
 
 
 def test_draft_rejects_bad_arguments(lib):

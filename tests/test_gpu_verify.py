@@ -19,6 +19,7 @@ from parity import compare_verify, run_oracle, to_np
 from workloads import make_workload
 
 DEV = "cuda:0"
+REQ_OVER_BUDGET = 64   # SPEC_REQ_OVER_BUDGET
 
 
 @pytest.fixture(scope="module")
@@ -184,13 +185,20 @@ def test_lossless_chi_square_on_gpu(sv, V):
     assert s["flagged_draws"] < 1e-4 * s["draws"], s
 
 
-def test_determinism(sv):
-    w = make_workload("mid", DEV, B=4, gamma=4, V=30000, seed=21)
+@pytest.mark.parametrize("name,kw", [
+    ("mid", dict(B=4, gamma=4, V=30000, seed=21)),
+    ("mixed", dict(B=12, gamma=4, V=30001, seed=9)),      # top-k rows: candidates gathered in LDS
+    ("mixed", dict(B=256, gamma=3, V=129280, seed=12)),   # ... and the fused emit
+])
+def test_determinism(sv, name, kw):
+    """The same inputs give bitwise-identical outputs, run after run."""
+    w = make_workload(name, DEV, **kw)
     a = _run(sv, w)
-    b = _run(sv, w)
-    for k in a:
-        assert torch.equal(a[k], b[k]) or (a[k].dtype.is_floating_point and
-                                           torch.equal(torch.nan_to_num(a[k]), torch.nan_to_num(b[k])))
+    for _ in range(3):
+        b = _run(sv, w)
+        for k in a:
+            assert torch.equal(a[k], b[k]) or (a[k].dtype.is_floating_point and
+                                               torch.equal(torch.nan_to_num(a[k]), torch.nan_to_num(b[k]))), k
 
 
 # ---- full workloads, sampled requests ----
@@ -307,3 +315,37 @@ def test_flat_layout_equals_padded(sv, name, kw):
         assert (np.abs(a[ok] - b[ok]) <= 1e-6 * np.abs(b[ok]) + 1e-12).all()
     o = run_oracle(w, lengths=L)
     compare_verify(got, o)
+
+
+@pytest.mark.parametrize("name,kw,bounds", [
+    ("scheduled", dict(B=300, gamma=8, V=4096, seed=11), (1, 37, 299, 10 ** 6)),
+    ("mid", dict(B=6, gamma=5, V=20011, seed=7), (1, 5, 36)),
+    ("mixed", dict(B=12, gamma=4, V=30001, seed=9), (3, 60)),
+])
+def test_token_cap(sv, name, kw, bounds):
+    """spec_verify_bounded: requests in index order add L_i + 1 (valid lengths only) to a running
+    sum; from the first that passes the cap on, requests with a valid length get OVER_BUDGET and
+    failed-request outputs.  Every request that fits must equal spec_verify's outputs bit for bit
+    (the cap also sizes the streaming grid, so both a tight and a loose cap are tried)."""
+    w = make_workload(name, DEV, **kw)
+    rng = np.random.default_rng(5)
+    Lh = rng.integers(0, w.gamma + 1, w.B).astype(np.int32)
+    Lh[rng.random(w.B) < 0.05] = w.gamma + 2            # bad lengths count as no rows
+    L = torch.from_numpy(Lh).to(DEV)
+    ref = sv.verify(w.target, w.draft, w.draft_tokens, L, w.temperature, w.top_k, w.seed)
+    torch.cuda.synchronize()
+    valid = (Lh >= 0) & (Lh <= w.gamma)
+    run = np.cumsum(np.where(valid, Lh.astype(np.int64) + 1, 0))
+    for b in bounds:
+        got = sv.verify(w.target, w.draft, w.draft_tokens, L, w.temperature, w.top_k, w.seed, max_tokens=b)
+        torch.cuda.synchronize()
+        over = valid & (run > b)
+        assert not over.any() or np.all(over[np.argmax(over):] == valid[np.argmax(over):])   # a suffix
+        keep = torch.from_numpy(~over).to(DEV)
+        for k in ("num_accepted", "out_tokens", "status"):
+            assert torch.equal(got[k][keep], ref[k][keep]), (b, k)
+        a_got = torch.nan_to_num(got["accept_prob"], nan=-1.0)
+        assert torch.equal(a_got[keep], torch.nan_to_num(ref["accept_prob"], nan=-1.0)[keep]), b
+        o = torch.from_numpy(over).to(DEV)
+        assert (got["status"][o] == REQ_OVER_BUDGET).all() and (got["num_accepted"][o] == 0).all()
+        assert (got["out_tokens"][o] == -1).all() and torch.isnan(got["accept_prob"][o]).all()
