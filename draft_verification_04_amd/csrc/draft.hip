@@ -10,14 +10,14 @@
 //       [B x r] (gathered embedding rows) x [r x V] (projection): MFMA 32x32x16 bf16 tiles with
 //       fp32 accumulation.  Each wave keeps the projection rows of its 32 tokens in registers and
 //       walks the requests 32 at a time; the epilogue adds U_k, rounds to the storage type, writes
-//       the draft logits and folds the stored values into per-(request, 128-token tile)
-//       statistics: the largest value and its first token, and, for sampling rows, an fp64 sum of
-//       2^(z log2(e)/T - m) against an integer reference m (so tiles combine by exact power-of-two
-//       scaling).
-//   markov_sample_kernel -- one wave per request combines its tiles, draws u from the request's
-//       counter-based stream, finds the tile where the running sum (ascending token order)
-//       passes u * total, re-reads that tile's 128 stored logits and picks the token.  T = 0
-//       takes the first-occurrence argmax.
+//       the draft logits and records per (request, 128-token tile) the largest stored value and
+//       whether a NaN or +inf was stored.
+//   markov_sample_kernel -- one 1024-thread workgroup per request.  T > 0: the weight of token v
+//       is Q(z_v) = exp(z_v/T - zmax/T) in fp64, looked up for bf16 rows in an LDS table over the
+//       bf16 values (evaluated once per value, the rest directly); one pass over the stored row
+//       sums Q per range of 2048 tokens, u * total (u from the request's counter-based stream)
+//       picks the range, and that range is walked again token by token in ascending order.  T = 0
+//       takes the first-occurrence argmax from the tile records and one tile.
 // After the last step markov_finish_kernel writes the confidences (fp64 dot products) and the
 // per-request status.
 #include <hip/hip_runtime.h>
@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "philox.hpp"
+#include "qtable.hpp"
 #include "spec_verify.h"
 
 namespace spec {
@@ -43,22 +44,19 @@ constexpr int kDraftThreads = 256;   // markov_logits_kernel: 4 waves
 constexpr int kTileTokens = 128;     // tokens per workgroup (32 per wave)
 constexpr int kReqBlock = 32;        // requests per MFMA block
 constexpr int kMaxSteps = 16;        // rank / 16 at most (r <= 256)
-constexpr int kSampleThreads = 256;  // markov_sample_kernel / markov_finish_kernel: a wave per item
+constexpr int kSampleThreads = 256;  // markov_finish_kernel: a wave per item
+constexpr int kDrawThreads = 1024;   // markov_sample_kernel: one workgroup per request
+constexpr int kDrawWaves = kDrawThreads / 64;
+constexpr int kDrawRange = 2048;     // tokens per range of the sampling pass (a wave step: 64 x 8)
+constexpr int kDrawMaxRanges = (SPEC_MAX_V + kDrawRange - 1) / kDrawRange;
 
 constexpr double kLog2eD = 1.44269504088896340736;
 
-// Statistics of the stored logits of one request over a set of tokens.
-struct Stat {
-  double s;     // sum of 2^(z c - m) (sampling rows), else 0
-  double m;     // integer reference of s (-inf while s == 0)
-  float zmax;   // largest stored value (-inf when none)
-  int32_t bad;  // NaN or +inf seen
-};
-
-struct alignas(16) DPart {
-  double s, m;
+// The stored logits of one request over one 128-token tile: the largest value (-inf when none)
+// and whether a NaN or +inf was stored.
+struct DPart {
   float zmax;
-  int32_t bad, pad0, pad1;
+  int32_t bad;
 };
 
 struct DraftArgs {
@@ -79,67 +77,6 @@ struct DraftArgs {
   DPart* part;               // [B, nwg] workspace
   int32_t* req_status;       // [B] workspace
 };
-
-__device__ __forceinline__ Stat stat_empty() {
-  Stat s;
-  s.s = 0.0;
-  s.m = -__builtin_inf();
-  s.zmax = -__builtin_inff();
-  s.bad = 0;
-  return s;
-}
-
-// a <- a (+) b.  Sums are brought to the larger reference by exact power-of-two scaling.
-__device__ __forceinline__ void stat_merge(Stat& a, const Stat& b) {
-  if (b.s > 0.0) {
-    if (a.s > 0.0) {
-      const double M = fmax(a.m, b.m);
-      a.s = ldexp(a.s, (int)fmax(a.m - M, -2000.0)) + ldexp(b.s, (int)fmax(b.m - M, -2000.0));
-      a.m = M;
-    } else {
-      a.s = b.s;
-      a.m = b.m;
-    }
-  }
-  a.zmax = fmaxf(a.zmax, b.zmax);
-  a.bad |= b.bad;
-}
-
-__device__ __forceinline__ Stat stat_shfl_xor(const Stat& a, int o) {
-  Stat b;
-  b.s = __shfl_xor(a.s, o, SPEC_WAVE);
-  b.m = __shfl_xor(a.m, o, SPEC_WAVE);
-  b.zmax = __shfl_xor(a.zmax, o, SPEC_WAVE);
-  b.bad = __shfl_xor(a.bad, o, SPEC_WAVE);
-  return b;
-}
-
-__device__ __forceinline__ Stat from_part(const DPart& p) {
-  Stat s;
-  s.s = p.s;
-  s.m = p.m;
-  s.zmax = p.zmax;
-  s.bad = p.bad;
-  return s;
-}
-
-// 2^t for t <= 0 in fp64, table-driven (P. T. P. Tang, "Table-driven implementation of the
-// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989): t = n + j/64 + r
-// with |r| <= 1/128, 2^t = 2^n * 2^(j/64) * 2^r; the 64 values 2^(j/64) come from `tab`, 2^r from
-// its Taylor series to degree 5 (truncation below 4e-17 relative).  t below -1100 (or -inf) gives 0.
-__device__ __forceinline__ double exp2_tab(double t, const double* tab) {
-  t = fmax(t, -1100.0);
-  const double N = rint(t * 64.0);
-  const double r = fma(N, -0.015625, t);  // exact
-  const int Ni = (int)N;
-  double p = 0x1.5d87fe78a6731p-10;       // (ln 2)^k / k!, k = 5 .. 0
-  p = fma(p, r, 0x1.3b2ab6fba4e77p-7);
-  p = fma(p, r, 0x1.c6b08d704a0c0p-5);
-  p = fma(p, r, 0x1.ebfbdff82c58fp-3);
-  p = fma(p, r, 0x1.62e42fefa39efp-1);
-  p = fma(p, r, 1.0);
-  return ldexp(tab[Ni & 63] * p, Ni >> 6);
-}
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(p));
@@ -174,8 +111,7 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
   constexpr int USB = kTileTokens * ES + 16;        // LDS row stride of the U/z tile (bytes)
   constexpr int UCPR = kTileTokens * ES / 16;       // 16-byte chunks per tile row
   constexpr int UPT = kReqBlock * UCPR / kDraftThreads;  // chunks per thread (2 bf16, 4 fp32)
-  __shared__ Stat sp[2][kDraftThreads / 64][kReqBlock];
-  __shared__ double tab[64];
+  __shared__ DPart sp[2][kDraftThreads / 64][kReqBlock];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kReqBlock * RS];
   __shared__ __attribute__((aligned(16))) unsigned char sU[3][kReqBlock * USB];
   __shared__ int sPrev[2][kReqBlock];
@@ -186,7 +122,6 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
   const int tile0 = blockIdx.x * kTileTokens;
   const int n0 = tile0 + wv * 32;
   const bf16x8 zero8 = {};
-  if (tid < 64) tab[tid] = exp2((double)tid * 0.015625);
 
   // Projection operand (MFMA A: row = token, 8 consecutive k per lane half): token n0 + tl.
   const uint16_t* w2 = a.W2t + (size_t)min(n0 + tl, V - 1) * r + 8 * h;
@@ -271,7 +206,7 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
     sPrev[1][tid] = prev_of(tid + kReqBlock);
   }
   if (fast_tile) load_tile(0);
-  __syncthreads();  // tab, sPrev
+  __syncthreads();  // sPrev
   load_rows(0);
   store_rows(0);
   if (fast_tile) store_tile_lds(0);
@@ -281,7 +216,6 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
     const int j = rb * kReqBlock + tl;
     const bool valid = j < B;
     const int buf = rb & 1, ub = rb % 3;
-    const float T = a.temperature[min(j, B - 1)];
     const bool more = rb + 1 < nrb;
     if (more) {
       load_rows(buf ^ 1);                 // rows of block rb + 1 (their ids were stored a block ago)
@@ -363,24 +297,13 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
         }
       }
     }
-    Stat st = stat_empty();
-    st.bad = bad;
     float zm = zq[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) zm = fmaxf(zm, zq[i]);
-    st.zmax = zm;
-    if (valid && T > 0.f && T < __builtin_inff() && zm > -__builtin_inff() && !bad) {
-      const double c = kLog2eD / (double)T;
-      const double m = ceil((double)zm * c);
-      double s = 0.0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s += exp2_tab(fma((double)zq[i], c, -m), tab);
-      st.s = s;
-      st.m = m;
-    }
     // the two lane halves hold the same request
-    stat_merge(st, stat_shfl_xor(st, 32));
-    if (h == 0) sp[buf][wv][tl] = st;
+    zm = fmaxf(zm, __shfl_xor(zm, 32, SPEC_WAVE));
+    bad |= __shfl_xor(bad, 32, SPEC_WAVE);
+    if (h == 0) sp[buf][wv][tl] = DPart{zm, bad};
     if (more) {
       store_rows(buf ^ 1);                            // read after the barrier below
       if (fast_tile) store_tile_lds((rb + 1) % 3);
@@ -389,31 +312,77 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
     __syncthreads();
     if (fast_tile) store_tile_global(rb, ub);
     if (wv == 3 && h == 0 && valid) {
-      Stat t = sp[buf][0][tl];
+      DPart t = sp[buf][0][tl];
 #pragma unroll
-      for (int w = 1; w < kDraftThreads / 64; ++w) stat_merge(t, sp[buf][w][tl]);
-      DPart p;
-      p.s = t.s;
-      p.m = t.m;
-      p.zmax = t.zmax;
-      p.bad = t.bad;
-      p.pad0 = p.pad1 = 0;
-      a.part[(size_t)j * a.nwg + blockIdx.x] = p;
+      for (int w = 1; w < kDraftThreads / 64; ++w) {
+        t.zmax = fmaxf(t.zmax, sp[buf][w][tl].zmax);
+        t.bad |= sp[buf][w][tl].bad;
+      }
+      a.part[(size_t)j * a.nwg + blockIdx.x] = t;
     }
   }
 }
 
-// Step k: draw x_k for every request (one workgroup each).  Every thread takes a contiguous run of
-// tiles; the workgroup finds the common reference, the total and the tile where the running sum
-// (tile order = token order) passes u * total; wave 0 then walks that tile's 128 tokens.
+// Step k: draw x_k for every request (one workgroup each).
+struct DrawShared {
+  double T64[64];
+  double Qt[kQsize];
+  double rsum[kDrawMaxRanges];  // Q summed per range of the row
+  double wsum[kDrawWaves];
+  float wz[kDrawWaves];
+  int wb[kDrawWaves], cross[kDrawWaves], lastl[kDrawWaves];
+  int sel, past, token;
+  double target, before;
+};
+
+// Exact weight Q(z_v) of token v of a stored row (table when given and the value is tabulated).
 template <int ES>
-__global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(DraftArgs a) {
-  constexpr int NW = kSampleThreads / 64;
-  __shared__ Stat red[NW];
-  __shared__ double wtot[NW];
-  __shared__ int hitw[NW], lastw[NW];
-  __shared__ int sel_w, first_max;
-  __shared__ double sel_before;
+__device__ __forceinline__ double draw_weight(const char* row, int v, double invT, double R, const double* T64,
+                                              const double* Qt) {
+  if constexpr (ES == 2) {
+    const uint32_t b = reinterpret_cast<const uint16_t*>(row)[v];
+    if (Qt) {
+      const uint32_t q = q_slot1(b);
+      if (q < (uint32_t)kQsize) return Qt[q];
+    }
+    return q_direct(__uint_as_float(b << 16), invT, R, T64);
+  } else {
+    return q_direct(reinterpret_cast<const float*>(row)[v], invT, R, T64);
+  }
+}
+
+// Sum of Q over the 8 bf16 tokens of one lane's 16-byte vector (lanes past the row's end hold
+// tabulated filler and add nothing when MASK).
+template <bool MASK>
+__device__ __forceinline__ double draw_step(const uint4& d, double invT, double R, const double* T64,
+                                            const double* Qt, bool live) {
+  uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  if (MASK && !live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = kFill2;
+  }
+  us2 kt[4];
+  us2 kmax = (us2)(unsigned short)0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    kt[q] = q_slots(w[q]);
+    kmax = __builtin_elementwise_max(kmax, kt[q]);
+  }
+  double s = 0.0;
+  if (max((uint32_t)kmax.x, (uint32_t)kmax.y) < (uint32_t)kQsize) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += Qt[slot_of(kt, j)];
+    if (MASK && !live) s = 0.0;
+  } else {
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) s += q_direct(__uint_as_float(half16(w, j) << 16), invT, R, T64);
+  }
+  return s;
+}
+
+template <int ES>
+__global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a) {
+  __shared__ DrawShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int j = blockIdx.x;
   const int k = a.k, V = a.V, nwg = a.nwg;
@@ -424,143 +393,241 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(DraftArgs
     const int x0 = a.anchor[j];
     if (x0 < 0 || x0 >= V) st |= SPEC_REQ_BAD_TOKEN;
   }
+  init_t64(sh.T64);
+  // the tile records: two per thread cover V <= 262144 (clamped indices, masked below)
   const DPart* P = a.part + (size_t)j * nwg;
-  const int per = (nwg + kSampleThreads - 1) / kSampleThreads;
-  const int w0 = min(nwg, tid * per), w1 = min(nwg, w0 + per);
-  Stat acc = stat_empty();
-  for (int w = w0; w < w1; ++w) stat_merge(acc, from_part(P[w]));
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) stat_merge(acc, stat_shfl_xor(acc, o));
-  if (lane == 0) red[wv] = acc;
+  const DPart p0 = P[min(tid, nwg - 1)], p1 = P[min(tid + kDrawThreads, nwg - 1)];
+  const char* row = reinterpret_cast<const char*>(a.logits) + ((size_t)j * a.G + k) * (size_t)V * ES;
+  const int NR = (V + kDrawRange - 1) / kDrawRange;
+  const bool vec = ES == 2 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && (V & 7) == 0 && V >= 8;
+  // a lane past the row's end loads a clamped address and is masked in its step
+  auto load = [&](int rr, int sub) -> uint4 {
+    const int v0 = min(rr * kDrawRange + sub * 512 + lane * 8, V - 8);
+    return *reinterpret_cast<const uint4*>(row + (size_t)v0 * 2);
+  };
+  // the row's largest stored value and bad flag
+  float zm = (tid < nwg) ? p0.zmax : -__builtin_inff();
+  int bad = (tid < nwg) ? p0.bad : 0;
+  if (tid + kDrawThreads < nwg) {
+    zm = fmaxf(zm, p1.zmax);
+    bad |= p1.bad;
+  }
+  for (int w = tid + 2 * kDrawThreads; w < nwg; w += kDrawThreads) {
+    const DPart p = P[w];
+    zm = fmaxf(zm, p.zmax);
+    bad |= p.bad;
+  }
+  zm = wave_max(zm);
+  bad = wave_or_i(bad);
+  if (lane == 0) {
+    sh.wz[wv] = zm;
+    sh.wb[wv] = bad;
+  }
   __syncthreads();
-  acc = red[0];
+  zm = sh.wz[0];
+  bad = sh.wb[0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) stat_merge(acc, red[w]);
-
-  if (st == 0 && (acc.bad || !(acc.zmax > -__builtin_inff()))) st |= SPEC_REQ_NONFINITE;
-  // the first tile holding the row's maximum (greedy rows; a fallback of the draw)
-  int myw = 0x7fffffff;
-  if (st == 0)
-    for (int w = w0; w < w1; ++w)
-      if (P[w].zmax == acc.zmax) {
+  for (int w = 1; w < kDrawWaves; ++w) {
+    zm = fmaxf(zm, sh.wz[w]);
+    bad |= sh.wb[w];
+  }
+  if (st == 0 && (bad || !(zm > -__builtin_inff()))) st |= SPEC_REQ_NONFINITE;
+  int x = -1;
+  if (st == 0 && T == 0.f) {
+    // the first tile holding the maximum, then its first token holding it
+    int myw = 0x7fffffff;
+    for (int w = tid; w < nwg; w += kDrawThreads)
+      if (P[w].zmax == zm) {
         myw = w;
         break;
       }
-  myw = wave_min_i(myw);
-  if (lane == 0) hitw[wv] = myw;
-  __syncthreads();
-  int wmax = hitw[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) wmax = min(wmax, hitw[w]);
-  __syncthreads();
-  const size_t row = ((size_t)j * a.G + k) * V;
-  // wave 0: the first token of tile w holding the maximum
-  auto first_max_token = [&](int w) -> int {
-    const int t0 = w * kTileTokens + 2 * lane;
-    const bool q0 = t0 < V && load_logit<ES>(a.logits, row + t0) == acc.zmax;
-    const bool q1 = t0 + 1 < V && load_logit<ES>(a.logits, row + t0 + 1) == acc.zmax;
-    const unsigned long long hb = __ballot(q0 || q1);
-    const int L = hb ? __ffsll((long long)hb) - 1 : 0;
-    return __shfl(q0 ? t0 : t0 + 1, L, SPEC_WAVE);
-  };
-
-  int x = -1;
-  if (st == 0 && T == 0.f && wv == 0) x = first_max_token(wmax);
-  if (st == 0 && T != 0.f) {  // uniform over the workgroup
-    const double M = acc.m;
-    const double c = kLog2eD / (double)T;
-    double ls = 0.0;
-    int mylast = -1;
-    for (int w = w0; w < w1; ++w) {
-      if (!(P[w].s > 0.0)) continue;
-      const double e = ldexp(P[w].s, (int)fmax(P[w].m - M, -2000.0));
-      ls += e;
-      if (e > 0.0) mylast = w;
-    }
-    const double iw = wave_inclusive_sum(ls, lane);
-    if (lane == 63) wtot[wv] = iw;
+    myw = wave_min_i(myw);
+    if (lane == 0) sh.cross[wv] = myw;
     __syncthreads();
-    double base = 0.0, S = 0.0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wv) base += wtot[w];
-      S += wtot[w];
-    }
-    const double incl = base + iw;
-    const uint64_t seed = a.seed ? a.seed[j] : 0ull;
-    const Philox4x64 blk = philox4x64_10((uint64_t)k + 1, (uint64_t)j, 1, 0, seed, 0);
-    const double target = uniform53(blk.w0) * S;
-    const unsigned long long hit = __ballot(incl > target);
-    const int wl = wave_max_i(mylast);
-    if (lane == 0) {
-      hitw[wv] = hit ? wv * 64 + (__ffsll((long long)hit) - 1) : 0x7fffffff;
-      lastw[wv] = wl;
-    }
-    __syncthreads();
-    int first = 0x7fffffff, lastt = -1;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      first = min(first, hitw[w]);
-      lastt = max(lastt, lastw[w]);
-    }
-    if (tid == 0) {
-      sel_w = lastt;                 // u * S rounded up to S: the last weighted tile,
-      sel_before = -__builtin_inf(); // and in it the last weighted token
-    }
-    __syncthreads();
-    if (tid == first) {  // the first thread whose running sum passes the target walks its tiles
-      double cum = incl - ls;
-      int ws = -1;
-      double before = 0.0;
-      for (int w = w0; w < w1; ++w) {
-        if (!(P[w].s > 0.0)) continue;
-        const double e = ldexp(P[w].s, (int)fmax(P[w].m - M, -2000.0));
-        if (!(e > 0.0)) continue;
-        if (cum + e > target) {
-          ws = w;
-          before = cum;
-          break;
-        }
-        cum += e;
-      }
-      if (ws >= 0) {
-        sel_w = ws;
-        sel_before = before;
-      } else if (mylast >= 0) {  // rounding: this run's last weighted tile, its last token
-        sel_w = mylast;
-      }
-    }
-    __syncthreads();
-    int wsel = sel_w;
-    const double before = sel_before;
-    if (wsel < 0) wsel = wmax;  // cannot happen when S > 0
     if (wv == 0) {
-      const int t0 = wsel * kTileTokens + 2 * lane;
-      double e0 = 0.0, e1 = 0.0;
-      if (t0 < V) e0 = exp2((double)load_logit<ES>(a.logits, row + t0) * c - M);
-      if (t0 + 1 < V) e1 = exp2((double)load_logit<ES>(a.logits, row + t0 + 1) * c - M);
-      const double pair = e0 + e1;
-      const double incl2 = wave_inclusive_sum(pair, lane);
-      double excl2 = __shfl_up(incl2, 1, SPEC_WAVE);
-      if (lane == 0) excl2 = 0.0;
-      const double c0 = before + (excl2 + e0);
-      const double c1 = before + ((excl2 + e0) + e1);
-      const bool p0 = e0 > 0.0 && c0 > target;
-      const bool p1 = e1 > 0.0 && c1 > target;
-      const unsigned long long hb = __ballot(p0 || p1);
-      if (hb) {
-        const int Lb = __ffsll((long long)hb) - 1;
-        x = __shfl(p0 ? t0 : t0 + 1, Lb, SPEC_WAVE);
-      } else {  // past the end of the tile: its last weighted token
-        const unsigned long long nz = __ballot(e0 > 0.0 || e1 > 0.0);
-        if (nz) {
-          const int Ln = 63 - __clzll((long long)nz);
-          x = __shfl(e1 > 0.0 ? t0 + 1 : t0, Ln, SPEC_WAVE);
-        } else {  // cannot happen: the tile's largest token has weight
-          x = first_max_token(wmax);
+      int w0 = sh.cross[0];
+#pragma unroll
+      for (int w = 1; w < kDrawWaves; ++w) w0 = min(w0, sh.cross[w]);
+      const int t0 = w0 * kTileTokens + 2 * lane;
+      const bool q0 = t0 < V && load_logit<ES>(row, t0) == zm;
+      const bool q1 = t0 + 1 < V && load_logit<ES>(row, t0 + 1) == zm;
+      const unsigned long long hb = __ballot(q0 || q1);
+      const int Lb = hb ? __ffsll((long long)hb) - 1 : 0;
+      x = __shfl(q0 ? t0 : t0 + 1, Lb, SPEC_WAVE);
+    }
+  } else if (st == 0) {  // uniform over the workgroup
+    const double invT = 1.0 / (double)T;
+    const double R = (double)zm * invT;      // the largest weight is exp(0) = 1
+    const double* Qt = (ES == 2) ? sh.Qt : nullptr;
+    // the first two ranges of each wave, in flight while the table is built
+    uint4 buf[8];
+    if (vec) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) buf[4 * h + sub] = load(wv + h * kDrawWaves, sub);
+    }
+    if (ES == 2) build_qtab(sh.Qt, invT, R, sh.T64);
+    lds_barrier();   // the table; the row loads stay in flight
+    if (vec) {
+      // the wave's ranges wv + q NS, q = 0 .. nq - 1, two in flight (8 vectors per lane): slots
+      // 0..3 hold the even q, 4..7 the odd q.  The main loop runs while both refills exist and
+      // refills unconditionally (a load under a condition would leave the compiler unsure of the
+      // order of the loads in flight, and it would then wait for all of them before every step);
+      // the last two or three ranges follow.  Only a wave's last range can be the row's partial one.
+      const int NS = kDrawWaves;
+      const int nq = (wv < NR) ? (NR - wv + NS - 1) / NS : 0;
+      auto range = [&](int rr, int h, bool refill, int rnext) {
+        double s = 0.0;
+        const bool tail = (rr + 1) * kDrawRange > V;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const int v0 = rr * kDrawRange + sub * 512 + lane * 8;
+          if (!tail) s += draw_step<false>(buf[4 * h + sub], invT, R, sh.T64, Qt, true);
+          else if (rr * kDrawRange + sub * 512 < V)
+            s += draw_step<true>(buf[4 * h + sub], invT, R, sh.T64, Qt, v0 < V);
+          if (refill) buf[4 * h + sub] = load(rnext, sub);
         }
+        s = wave_sum(s);
+        if (lane == 0) sh.rsum[rr] = s;
+      };
+      int q = 0;
+      for (; q + 3 < nq; q += 2) {
+        range(wv + q * NS, 0, true, wv + (q + 2) * NS);
+        range(wv + (q + 1) * NS, 1, true, wv + (q + 3) * NS);
+      }
+      if (q < nq) range(wv + q * NS, 0, q + 2 < nq, wv + (q + 2) * NS);
+      if (q + 1 < nq) range(wv + (q + 1) * NS, 1, false, 0);
+      if (q + 2 < nq) range(wv + (q + 2) * NS, 0, false, 0);
+    } else {
+      for (int rr = wv; rr < NR; rr += kDrawWaves) {
+        double s = 0.0;
+        const int e = min(V, (rr + 1) * kDrawRange);
+        for (int v = rr * kDrawRange + lane; v < e; v += 64) s += draw_weight<ES>(row, v, invT, R, sh.T64, Qt);
+        s = wave_sum(s);
+        if (lane == 0) sh.rsum[rr] = s;
       }
     }
+    __syncthreads();
+    // wave 0: prefix over the ranges (four per lane), the total, u * total and the first range
+    // whose prefix passes it
+    static_assert(kDrawMaxRanges <= 4 * SPEC_WAVE, "four ranges per lane");
+    if (wv == 0) {
+      double v4[4], pre[4], t = 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = lane * 4 + u;
+        v4[u] = (r < NR) ? sh.rsum[r] : 0.0;
+        t += v4[u];
+      }
+      const double incl = wave_inclusive_sum(t, lane);
+      double run = incl - t;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        run += v4[u];
+        pre[u] = run;
+      }
+      const double W = __shfl(incl, 63, SPEC_WAVE);
+      const uint64_t seed = a.seed ? a.seed[j] : 0ull;
+      const Philox4x64 blk = philox4x64_10((uint64_t)k + 1, (uint64_t)j, 1, 0, seed, 0);
+      const double target = uniform53(blk.w0) * W;
+      int f = 4;
+#pragma unroll
+      for (int u = 3; u >= 0; --u)
+        if (lane * 4 + u < NR && pre[u] > target) f = u;
+      const unsigned long long m = __ballot(f < 4);
+      int sel = NR;
+      double before = 0.0;
+      if (m) {
+        const int fl = (int)__ffsll((long long)m) - 1;
+        sel = fl * 4 + __shfl(f, fl, SPEC_WAVE);
+        if (sel > 0) {
+          const int ub = (sel - 1) & 3;
+          const double mine = ub == 0 ? pre[0] : ub == 1 ? pre[1] : ub == 2 ? pre[2] : pre[3];
+          before = __shfl(mine, (sel - 1) >> 2, SPEC_WAVE);
+        }
+      }
+      if (lane == 0) {
+        sh.target = target;
+        sh.sel = sel;
+        sh.past = (sel >= NR);
+        sh.before = before;
+        sh.token = -1;
+      }
+    }
+    __syncthreads();
+    const double target = sh.target;
+    if (sh.past) {
+      // u * total at or past the total (rounding): the last token with weight
+      for (int r = NR - 1; r >= 0; --r) {
+        int best = -1;
+        for (int v = r * kDrawRange + tid; v < min(V, (r + 1) * kDrawRange); v += kDrawThreads)
+          if (draw_weight<ES>(row, v, invT, R, sh.T64, Qt) > 0.0) best = v;
+        best = wave_max_i(best);
+        if (lane == 0) sh.lastl[wv] = best;
+        __syncthreads();
+        if (tid == 0) {
+          int b = -1;
+#pragma unroll
+          for (int w = 0; w < kDrawWaves; ++w) b = max(b, sh.lastl[w]);
+          if (b >= 0) sh.token = b;
+        }
+        __syncthreads();
+        if (sh.token >= 0) break;
+      }
+    } else {
+      // the selected range, two tokens per thread in ascending order
+      constexpr int TPT = kDrawRange / kDrawThreads;
+      const int base = sh.sel * kDrawRange + tid * TPT;
+      double wt[TPT];
+      double xs = 0.0;
+#pragma unroll
+      for (int q = 0; q < TPT; ++q) {
+        const int v = base + q;
+        wt[q] = (v < V) ? draw_weight<ES>(row, v, invT, R, sh.T64, Qt) : 0.0;
+        xs += wt[q];
+      }
+      const double incl = wave_inclusive_sum(xs, lane);
+      if (lane == 63) sh.wsum[wv] = incl;
+      __syncthreads();
+      double wb = 0.0;
+      for (int q = 0; q < wv; ++q) wb += sh.wsum[q];
+      const double Pb = sh.before + wb;
+      const double excl = incl - xs;
+      const unsigned long long m = __ballot(Pb + incl > target);
+      const unsigned long long pos = __ballot(xs > 0.0);
+      if (lane == 0) {
+        sh.cross[wv] = m ? (int)(__ffsll((long long)m) - 1) : 64;
+        sh.lastl[wv] = pos ? 63 - __clzll((long long)pos) : -1;
+      }
+      __syncthreads();
+      int cw = -1, cl = -1;
+      for (int q = 0; q < kDrawWaves && cw < 0; ++q)
+        if (sh.cross[q] < 64) {
+          cw = q;
+          cl = sh.cross[q];
+        }
+      if (cw < 0) {  // rounding left no crossing: the last thread with weight
+        for (int q = kDrawWaves - 1; q >= 0 && cw < 0; --q)
+          if (sh.lastl[q] >= 0) {
+            cw = q;
+            cl = sh.lastl[q];
+          }
+      }
+      if (wv == cw && lane == cl) {
+        double acc = Pb + excl;
+        int tok = -1, lastpos = -1;
+#pragma unroll
+        for (int q = 0; q < TPT; ++q) {
+          if (wt[q] > 0.0) lastpos = base + q;
+          acc += wt[q];
+          if (tok < 0 && acc > target && wt[q] > 0.0) tok = base + q;
+        }
+        sh.token = (tok >= 0) ? tok : lastpos;
+      }
+    }
+    __syncthreads();
+    x = sh.token;
   }
   if (tid == 0) {
     a.tokens[(size_t)j * a.G + k] = (st == 0) ? x : -1;
@@ -690,10 +757,10 @@ extern "C" int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_
     a.k = k;
     if (dtype == SPEC_BF16) {
       hipLaunchKernelGGL(markov_logits_kernel<2>, dim3(a.nwg), dim3(kDraftThreads), 0, s, a);
-      hipLaunchKernelGGL(markov_sample_kernel<2>, dim3(sgrid), dim3(kSampleThreads), 0, s, a);
+      hipLaunchKernelGGL(markov_sample_kernel<2>, dim3(sgrid), dim3(kDrawThreads), 0, s, a);
     } else {
       hipLaunchKernelGGL(markov_logits_kernel<4>, dim3(a.nwg), dim3(kDraftThreads), 0, s, a);
-      hipLaunchKernelGGL(markov_sample_kernel<4>, dim3(sgrid), dim3(kSampleThreads), 0, s, a);
+      hipLaunchKernelGGL(markov_sample_kernel<4>, dim3(sgrid), dim3(kDrawThreads), 0, s, a);
     }
   }
   const unsigned fgrid = (unsigned)(((size_t)B * gamma + 3) / 4);

@@ -32,6 +32,7 @@
 #include "common.hpp"
 #include "philox.hpp"
 #include "verify_impl.hpp"
+#include "qtable.hpp"
 
 #include <float.h>
 #include <math.h>
@@ -39,54 +40,11 @@
 namespace spec {
 
 constexpr double kAmbTol = 1e-5;
-constexpr int kQefLo = 107, kQefHi = 133;               // bf16 exponent fields tabulated
-constexpr int kQper = (kQefHi - kQefLo + 1) * 128;      // 3456 values per sign
-constexpr int kQsize = 2 * kQper;                       // 6912 entries, 55296 bytes
 constexpr int kSub = 512;                               // tokens per wave step (64 lanes x 8)
 constexpr int kSubPerRange = kRangeElems / kSub;        // 4
-constexpr uint32_t kFill2 = 0x3f803f80u;                // two bf16 ones: tabulated filler bits
-
-// exp(x) in fp64 by Tang's table-driven method (ACM TOMS 15(2), 1989), for
-// x in [-1000, 709]: x = k ln2/64 + r with |r| <= ln2/128 (two-part ln2/64),
-// e^x = 2^(k div 64) * 2^((k mod 64)/64) * e^r, e^r by its degree-5 Taylor
-// polynomial (truncation < 4e-17); T64[j] = 2^(j/64).  Underflows to 0.
-__device__ __forceinline__ double exp_tang(double x, const double* T64) {
-  const double k = rint(x * 92.332482616893657);
-  double r = fma(-k, 0.010830424696249145, x);
-  r = fma(-k, 3.623510646634843e-19, r);
-  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-  p = fma(r, p, 1.0 / 6.0);
-  p = fma(r, p, 0.5);
-  p = fma(r, p, 1.0);
-  p = fma(r, p, 1.0);
-  const int ki = (int)k;
-  return ldexp(T64[ki & 63] * p, ki >> 6);
-}
-
-// Q(z) = exp(z/T - R), z/T taken as the fp64 product z * (1/T); -inf -> 0.
-__device__ __forceinline__ double q_direct(float z, double invT, double R, const double* T64) {
-  return exp_tang(fmax(fma((double)z, invT, -R), -1000.0), T64);
-}
-
-__device__ __forceinline__ void init_t64(double* T64) {
-  if (threadIdx.x < 64) T64[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
-}
-
-// The table of Q over the tabulated bf16 values.  Entry 2 (m - m0) + s holds the value with sign
-// s and magnitude bits m (m0 the first tabulated magnitude): the index is the bf16 bit pattern
-// rotated left by one, less 2 m0, which two 16-bit integer instructions give for a pair of values.
-__device__ void build_qtab_part(double* Qt, double invT, double R, const double* T64, int t0, int nthr) {
-  for (int idx = t0; idx < kQsize; idx += nthr) {
-    const uint32_t bits = ((uint32_t)(idx & 1) << 15) | ((uint32_t)(kQefLo << 7) + ((uint32_t)idx >> 1));
-    Qt[idx] = q_direct(__uint_as_float(bits << 16), invT, R, T64);
-  }
-}
-
-__device__ __forceinline__ void build_qtab(double* Qt, double invT, double R, const double* T64) {
-  build_qtab_part(Qt, invT, R, T64, (int)threadIdx.x, (int)blockDim.x);
-}
 
 struct EmitRows {
+  int V;
   const char* t;
   const char* d;  // nullptr: single target row (appended / fresh token)
   double invT, R;
@@ -104,6 +62,7 @@ __device__ __forceinline__ EmitRows emit_rows_from(const VerifyArgs& a, int i, i
                                                    const RowStat& rt, const RowStat& rd) {
   constexpr int ES = BF16 ? 2 : 4;
   EmitRows e;
+  e.V = a.V;
   e.t = target_row<ES>(a, i, n);
   e.R = rt.lse2 * kLn2;
   e.tht = rt.theta;
@@ -129,11 +88,6 @@ __device__ __forceinline__ EmitRows emit_rows(const VerifyArgs& a, int i, int n)
   const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
   const RowStat rd = (n < L) ? a.rows_d[(size_t)i * G + n] : RowStat{0.0, -INFINITY, 0};
   return emit_rows_from<BF16>(a, i, n, L, a.temperature[i], rt, rd);
-}
-
-// Table slot of one bf16 value (see build_qtab); kQsize or more when it is not tabulated.
-__device__ __forceinline__ uint32_t q_slot1(uint32_t b) {
-  return (((b << 1) | (b >> 15)) - (uint32_t)(2 * (kQefLo << 7))) & 0xffffu;
 }
 
 // Q of token v of a row (any dtype, any alignment), kept-set aware; from the table Qt when given
@@ -216,23 +170,6 @@ struct DecideShared {
   int amb_list[kAmbCap];
 };
 
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-
-// Table slots of the two bf16 values of a word, one per 16-bit half; a slot is below kQsize
-// exactly when its value is tabulated (otherwise it wrapped past it).
-__device__ __forceinline__ us2 q_slots(uint32_t w) {
-  const us2 v = __builtin_bit_cast(us2, w);
-  return ((v << (unsigned short)1) | (v >> (unsigned short)15)) - (us2)(unsigned short)(2 * (kQefLo << 7));
-}
-
-__device__ __forceinline__ uint32_t slot_of(const us2 (&k)[4], int j) {
-  return (j & 1) ? (uint32_t)k[j >> 1].y : (uint32_t)k[j >> 1].x;
-}
-
-__device__ __forceinline__ uint32_t half16(const uint32_t (&w)[4], int j) {
-  return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
-}
-
 // One step (64 lanes x 8 tokens) of a bf16 row pair from registers.  A lane whose 16 tokens
 // are all tabulated reads Q from the table; otherwise (rare: |z| < 2^-20, |z| >= 128,
 // infinities) it evaluates the same formula directly for the whole step.  MASK: the step of a
@@ -241,8 +178,8 @@ __device__ __forceinline__ uint32_t half16(const uint32_t (&w)[4], int j) {
 // lane saw one and then finds and records it in a second look at its 8 tokens.
 template <bool RESID, bool MASK = false>
 __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& dd, const EmitRows& e,
-                                          double cdh, double cdl, int v0, const VerifyArgs& a, int i,
-                                          const double* T64, const double* Qt, bool live = true) {
+                                          double cdh, double cdl, int v0, const double* T64, const double* Qt,
+                                          bool live = true) {
   constexpr bool resid = RESID;
   uint32_t wt[4] = {dt.x, dt.y, dt.z, dt.w};
   uint32_t wd[4] = {dd.x, dd.y, dd.z, dd.w};
@@ -303,6 +240,73 @@ __device__ __forceinline__ void step_bf16(Acc& c, const uint4& dt, const uint4& 
   }
 }
 
+// The 16-byte vector path of a bf16 row pair (rows 16-byte aligned, V a multiple of 8): the wave's
+// ranges r, r + NWT, ... below NRv, the four steps of a range in flight at once.  Each register
+// slot is refilled with the same step of the wave's next range as soon as it has been consumed,
+// unconditionally inside the loop (the loop runs over ranges that have a successor; the wave's last
+// range is taken after it): loads under a condition would leave the compiler unsure of the order
+// of the loads in flight, and it would then wait for all of them before every step.  The row's
+// last, partial range (lanes past the end load a clamped address and are masked) is only ever a
+// wave's last.  The Q table is built (unless table_ready) while the first loads are in flight;
+// r is advanced past the ranges done.
+template <bool RESID>
+__device__ __forceinline__ void vec_ranges(PassShared& sh, const EmitRows& e, Acc& c, double cdh, double cdl,
+                                           EmitRange* out, int& r, int NRv, int NRfull, int NWT,
+                                           bool table_ready) {
+  const int lane = threadIdx.x & 63;
+  uint4 bt[kSubPerRange], bd[kSubPerRange];
+  const int Vt = e.V;
+  auto load = [&](int rr, int sub, uint4& t, uint4& d) {
+    const int v0 = min(rr * kRangeElems + sub * kSub + lane * 8, Vt - 8);
+    const size_t off = (size_t)v0 * 2;
+    t = *reinterpret_cast<const uint4*>(e.t + off);
+    if constexpr (RESID) d = *reinterpret_cast<const uint4*>(e.d + off);
+    else d = make_uint4(0, 0, 0, 0);
+  };
+  const bool any = r < NRv;
+  const int r0 = any ? r : 0;   // a wave without a range loads range 0 and leaves it unused
+  if (NRv > 0) {
+#pragma unroll
+    for (int sub = 0; sub < kSubPerRange; ++sub) load(r0, sub, bt[sub], bd[sub]);
+  }
+  if (!table_ready) build_qtab(sh.Qt, e.invT, e.R, sh.T64);
+  lds_barrier();   // the table; the loads stay in flight
+  auto finish = [&](int rr) {
+    const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
+    if (lane == 0) out[rr] = EmitRange{A, D, T};
+  };
+  for (; r + NWT < NRv; r += NWT) {   // a full range with a successor
+    const int rn = r + NWT;
+    c.A = c.D = c.T = 0.0;
+#pragma unroll
+    for (int sub = 0; sub < kSubPerRange; ++sub) {
+      const int v0 = r * kRangeElems + sub * kSub + lane * 8;
+      step_bf16<RESID>(c, bt[sub], bd[sub], e, cdh, cdl, v0, sh.T64, sh.Qt);
+      load(rn, sub, bt[sub], bd[sub]);
+    }
+    finish(r);
+  }
+  if (r < NRv) {   // the wave's last range
+    c.A = c.D = c.T = 0.0;
+    if (r < NRfull) {
+#pragma unroll
+      for (int sub = 0; sub < kSubPerRange; ++sub) {
+        const int v0 = r * kRangeElems + sub * kSub + lane * 8;
+        step_bf16<RESID>(c, bt[sub], bd[sub], e, cdh, cdl, v0, sh.T64, sh.Qt);
+      }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < kSubPerRange; ++sub) {
+        const int vs = r * kRangeElems + sub * kSub, v0 = vs + lane * 8;
+        if (vs >= Vt) break;
+        step_bf16<RESID, true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, sh.T64, sh.Qt, v0 < Vt);
+      }
+    }
+    finish(r);
+    r += NWT;
+  }
+}
+
 // The ranges of request i that segment `seg` owns, each written as an EmitRange to out[r]
 // (global memory, or LDS when the same workgroup finishes the request); each wave's sum of
 // E_d goes to sh.red[1][wave].  bf16 rows without top-k build the Q table in sh.Qt here unless
@@ -322,53 +326,9 @@ __device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg,
   Acc c{0.0, 0.0, 0.0, 0.0};
   int r = seg * NWPB + wave;
   if (BF16 && !TOPK) {
-    // the 4 steps of a range are in flight at once; each register slot is refilled with the
-    // same step of the wave's next range as soon as it has been consumed.  When V is a multiple
-    // of 8 the row's last, partial range is read the same way, lanes past the end masked.
-    const int NRv = (aligned && (V & 7) == 0) ? NR : NRfull;
-    uint4 bt[kSubPerRange], bd[kSubPerRange];
-    // every lane loads (a lane past the row's end reads the row's last vector, masked in its
-    // step): a load under a lane condition would make the compiler wait for it at once
-    auto load = [&](int rr, int sub, uint4& t, uint4& d) {
-      const int v0 = min(rr * kRangeElems + sub * kSub + lane * 8, V - 8);
-      const size_t off = (size_t)v0 * 2;
-      t = *reinterpret_cast<const uint4*>(e.t + off);
-      d = resid ? *reinterpret_cast<const uint4*>(e.d + off) : make_uint4(0, 0, 0, 0);
-    };
-    if (r < NRv) {
-#pragma unroll
-      for (int sub = 0; sub < kSubPerRange; ++sub) load(r, sub, bt[sub], bd[sub]);
-    }
-    // the table of Q over the bf16 values (unless already built with offset e.R), built while the
-    // first loads are in flight (the barrier leaves them in flight: each wave waits only for the
-    // step it works on)
-    if (!table_ready) build_qtab(sh.Qt, e.invT, e.R, sh.T64);
-    lds_barrier();
-    while (r < NRv) {
-      const int rn = r + NWT;
-      c.A = c.D = c.T = 0.0;
-      if (r < NRfull) {
-#pragma unroll
-        for (int sub = 0; sub < kSubPerRange; ++sub) {
-          const int v0 = r * kRangeElems + sub * kSub + lane * 8;
-          if (resid) step_bf16<true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
-          else step_bf16<false>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt);
-          if (rn < NRv) load(rn, sub, bt[sub], bd[sub]);
-        }
-      } else {
-        // the last range (rn is past it): steps wholly past the row's end are skipped
-#pragma unroll
-        for (int sub = 0; sub < kSubPerRange; ++sub) {
-          const int vs = r * kRangeElems + sub * kSub, v0 = vs + lane * 8;
-          if (vs >= V) break;
-          if (resid) step_bf16<true, true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt, v0 < V);
-          else step_bf16<false, true>(c, bt[sub], bd[sub], e, cdh, cdl, v0, a, i, sh.T64, sh.Qt, v0 < V);
-        }
-      }
-      const double A = wave_sum(c.A), D = wave_sum(c.D), T = wave_sum(c.T);
-      if (lane == 0) out[r] = EmitRange{A, D, T};
-      r = rn;
-    }
+    const int NRv = (aligned && (V & 7) == 0 && V >= 8) ? NR : NRfull;
+    if (resid) vec_ranges<true>(sh, e, c, cdh, cdl, out, r, NRv, NRfull, NWT, table_ready);
+    else vec_ranges<false>(sh, e, c, cdh, cdl, out, r, NRv, NRfull, NWT, table_ready);
   }
   // ranges with a ragged end, unaligned rows, fp32 rows and top-k rows: token by token
   for (; r < NR; r += NWT) {
