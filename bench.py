@@ -296,11 +296,13 @@ def draft_leg(sv, torch, oracle, dev, stream, reps=10, with_cpu=True):
     torch.cuda.synchronize()
     ms = e0.elapsed_ms(e1) / reps
     nwg = (V + 127) // 128
-    step_bytes = 2 * B * V * 2 + V * r * 2 + B * r * 2 + B * nwg * 32   # U_k in, z_k out, W2, W1 rows, tiles
+    step_bytes = 2 * B * V * 2 + V * r * 2 + B * r * 2 + B * nwg * 8    # U_k in, z_k out, W2, W1 rows, tiles
+    sample_bytes = B * V * 2 + B * nwg * 8                               # the sampler reads z_k and the tiles
     flops = 2.0 * B * V * r * G
     res = {"config": f"B={B} gamma={G} V={V} r={r} d={d} bf16", "ms_per_call": ms,
            "draft_tokens_per_s": B * G / (ms * 1e-3), "status_ok": int((out["status"] == 0).sum().item()),
-           "bytes_per_step_kernel": step_bytes, "gbps_per_call": G * step_bytes / (ms * 1e-3) / 1e9,
+           "bytes_per_step_kernel": step_bytes, "bytes_per_step_sampler": sample_bytes,
+           "gbps_per_call": G * (step_bytes + sample_bytes) / (ms * 1e-3) / 1e9,
            "mfma_tflops_per_call": flops / (ms * 1e-3) / 1e12}
     if with_cpu:
         from threadpoolctl import threadpool_limits
