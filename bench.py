@@ -1,10 +1,13 @@
 """Benchmark: one step = the whole hot path on the confidence-scheduled workload.
 
 Workload (B=256 requests, gamma=16, V=151936, bf16 logits, 2048-token verify
-budget): spec_schedule_lengths picks per-request verify lengths from the
-confidences and the engine cost table, then spec_verify verifies exactly the
+budget): one spec_schedule_verify call, in which the scheduler picks per-request
+verify lengths from the confidences and the engine cost table (its last kernel
+also writing the verify work list), then the verifier verifies exactly the
 selected prefixes (row statistics, acceptance tests, first rejection,
-correction / appended token).  Inputs are resident in HBM before timing.
+correction / appended token).  --two-calls makes the same step from
+spec_schedule_lengths and spec_verify_bounded.  Inputs are resident in HBM
+before timing.
 
 Prints ONE JSON line:
   value      verified draft positions per second (sum of scheduled lengths / step time)
@@ -46,6 +49,8 @@ def parse():
     p.add_argument("--no-overlap", action="store_true", help="skip the overlap-mass measurement")
     p.add_argument("--no-draft", action="store_true", help="skip the draft-sampler measurement")
     p.add_argument("--no-sts", action="store_true", help="skip the temperature-scaling measurement")
+    p.add_argument("--two-calls", action="store_true",
+                   help="scheduler and verification as two calls instead of spec_schedule_verify")
     p.add_argument("--pool", type=int, default=8, help="worker processes for the pooled CPU-oracle timing")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
@@ -90,8 +95,16 @@ def main():
                    status=torch.empty(B, dtype=torch.int32, device=dev))
     stream = torch.cuda.current_stream()
 
+    fused_out = dict(ver_out, lengths=sch_out["lengths"], theta=sch_out["theta"], sched_status=sch_out["status"])
+
     def step(idx, events=None):
         tgt, drf = copies[idx % len(copies)]
+        if w.conf is not None and not greedy and not args.two_calls:
+            # scheduler, then verification under its token budget, in one call
+            sv.schedule_verify(tgt, drf, w.draft_tokens, w.conf, sps, w.budget, sv.SPEC_SCHED_EARLY_STOP,
+                               w.temperature, w.top_k, w.seed, out=fused_out, workspace=ws,
+                               sched_workspace=sch_ws, stream=stream, events=events)
+            return
         if w.conf is not None:
             sv.schedule_lengths(w.conf, sps, w.budget, out=sch_out, stream=stream, workspace=sch_ws)
             L = sch_out["lengths"]

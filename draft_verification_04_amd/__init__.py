@@ -55,6 +55,8 @@ EXPORTS = {
     "spec_verify_greedy": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_schedule_workspace_size": (_Z, [_I, _I]),
     "spec_schedule_lengths": (_I, [_I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "spec_schedule_verify": (_I, [_I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _Z, _P, _Z, _P, _P, _P]),
     "spec_philox_uniforms": (_I, [_I, _P, _P, _P, _P, _P, _P]),
     "spec_read_ceiling": (_I, [_P, _Z, _I, _P, _P]),
     "spec_overlap_workspace_size": (_Z, [_I, _I, _I]),
@@ -148,22 +150,8 @@ def _workspace(nbytes: int, device, workspace=None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
-           lengths: Optional[torch.Tensor] = None, temperature: Optional[torch.Tensor] = None,
-           top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
-           out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-           events=None, max_tokens: Optional[int] = None) -> dict:
-    """spec_verify on torch tensors.  Returns dict(num_accepted, out_tokens, accept_prob, status).
-
-    target [B, gamma+1, V] and draft [B, gamma, V] (float32 or bfloat16);
-    draft_tokens [B, gamma] int32; lengths [B] int32 or None; temperature [B]
-    float32 (default ones); top_k [B] int32 or None; seed [B] int64 holding
-    the uint64 bit pattern (default zeros).  `events` = (before, after)
-    torch.cuda.Event pair recorded around the row-streaming kernel.
-    `max_tokens` (spec_verify_bounded): the caller's bound on sum_i (L_i + 1),
-    e.g. the scheduler's token budget; it sizes the streaming grid only.
-    """
-    lib = load_library()
+def _verify_inputs(target, draft, draft_tokens, lengths, temperature, top_k, seed):
+    """Checks the verify inputs; returns (B, gamma, V, temperature, seed) with the defaults filled in."""
     _dev(target, "target", (torch.float32, torch.bfloat16), 3)
     _dev(draft, "draft", target.dtype, 3)
     B, G1, V = target.shape
@@ -182,17 +170,47 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     _dev(temperature, "temperature", torch.float32, 1)
     _dev(top_k, "top_k", torch.int32, 1)
     _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
+    return B, G, V, temperature, seed
+
+
+def _verify_outputs(B, G, dev, out):
+    """A caller's `out` is used as given (a missing accept_prob or status is passed as NULL)."""
     if out is None:
         out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
                    accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
+    return out
+
+
+def _events(events):
+    if events is None:
+        return None, None
+    return ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event)
+
+
+def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+           lengths: Optional[torch.Tensor] = None, temperature: Optional[torch.Tensor] = None,
+           top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
+           out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+           events=None, max_tokens: Optional[int] = None) -> dict:
+    """spec_verify on torch tensors.  Returns dict(num_accepted, out_tokens, accept_prob, status).
+
+    target [B, gamma+1, V] and draft [B, gamma, V] (float32 or bfloat16);
+    draft_tokens [B, gamma] int32; lengths [B] int32 or None; temperature [B]
+    float32 (default ones); top_k [B] int32 or None; seed [B] int64 holding
+    the uint64 bit pattern (default zeros).  `events` = (before, after)
+    torch.cuda.Event pair recorded around the row-streaming kernel.
+    `max_tokens` (spec_verify_bounded): the caller's bound on sum_i (L_i + 1),
+    e.g. the scheduler's token budget; it sizes the streaming grid only.
+    """
+    lib = load_library()
+    B, G, V, temperature, seed = _verify_inputs(target, draft, draft_tokens, lengths, temperature, top_k, seed)
+    dev = target.device
+    out = _verify_outputs(B, G, dev, out)
     nbytes = int(lib.spec_verify_workspace_size(B, G, V))
     ws = _workspace(nbytes, dev, workspace)
-    ev0 = ev1 = None
-    if events is not None:
-        ev0 = ctypes.c_void_p(events[0].cuda_event)
-        ev1 = ctypes.c_void_p(events[1].cuda_event)
+    ev0, ev1 = _events(events)
     args = (B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
             _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
             _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
@@ -288,6 +306,43 @@ def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
                                      _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("status")),
                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("spec_schedule_lengths", code)
+    return out
+
+
+def schedule_verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor, conf: torch.Tensor,
+                    sps: torch.Tensor, budget_tokens: int, mode: int = SPEC_SCHED_EARLY_STOP,
+                    temperature: Optional[torch.Tensor] = None, top_k: Optional[torch.Tensor] = None,
+                    seed: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                    workspace: Optional[torch.Tensor] = None, sched_workspace: Optional[torch.Tensor] = None,
+                    stream=None, events=None) -> dict:
+    """spec_schedule_verify: the scheduler's lengths, then verification under the budget, in one call.
+
+    Inputs as for schedule_lengths (conf, sps, budget_tokens, mode) and verify (no lengths).
+    Returns dict(lengths, theta, sched_status, num_accepted, out_tokens, accept_prob, status).
+    """
+    lib = load_library()
+    B, G, V, temperature, seed = _verify_inputs(target, draft, draft_tokens, None, temperature, top_k, seed)
+    _dev(conf, "conf", torch.float32, 2)
+    _dev(sps, "sps", torch.float64, 1)
+    if tuple(conf.shape) != (B, G):
+        raise ValueError("conf must be [B, gamma]")
+    dev = target.device
+    if out is None:
+        out = _verify_outputs(B, G, dev, None)
+        out.update(lengths=torch.empty(B, dtype=torch.int32, device=dev),
+                   theta=torch.empty(1, dtype=torch.float64, device=dev),
+                   sched_status=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = _workspace(int(lib.spec_verify_workspace_size(B, G, V)), dev, workspace)
+    sws = _workspace(int(lib.spec_schedule_workspace_size(B, G)), dev, sched_workspace)
+    ev0, ev1 = _events(events)
+    code = lib.spec_schedule_verify(
+        B, G, V, _logit_dtype(target), _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode),
+        _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(temperature), _ptr(top_k), _ptr(seed),
+        _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("sched_status")), _ptr(out["num_accepted"]),
+        _ptr(out["out_tokens"]), _ptr(out.get("accept_prob")), _ptr(out.get("status")),
+        _ptr(sws), sws.numel() * sws.element_size(), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
+        ev0, ev1)
+    _check("spec_schedule_verify", code)
     return out
 
 

@@ -26,9 +26,12 @@
 //                 survivals, Theta(m), first non-rise (early stop) or first maximum
 //                 (global), and per-request counts from the key at m* (keys below it
 //                 are admitted, and of the keys equal to it the first ones in index
-//                 order, as many as the admission count leaves).
+//                 order, as many as the admission count leaves).  In the combined
+//                 schedule-and-verify call (B <= 1024) it also writes the verify work
+//                 list from the lengths it holds, in place of the work-list kernel.
 #include "common.hpp"
 #include "spec_verify.h"
+#include "verify_impl.hpp"
 
 #include <math.h>
 
@@ -211,9 +214,13 @@ __device__ __forceinline__ long long block_exclusive_sum(long long x, long long*
   return before + incl - x;
 }
 
-template <int K>
-__global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
+static_assert(kFinalThreads == kWorklistThreads, "one thread per request in the combined call");
+
+// WL: also build the verify work list of v from the lengths (B <= kFinalThreads).
+template <int K, bool WL>
+__global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, VerifyArgs v) {
   __shared__ FinalShared<K> sh;
+  __shared__ WorklistShared wsh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int B = a.B, G = a.G;
   const int N = B * G;
@@ -342,6 +349,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
   if (!a.lengths) return;
   if (mstar == 0) {
     for (int r = tid; r < B; r += kFinalThreads) a.lengths[r] = 0;
+    if constexpr (WL) worklist_from_lengths(wsh, v, 0);
     return;
   }
   // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
@@ -370,6 +378,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
   const int ties_admitted = mstar - sh.first;
   const bool split = ties_admitted < sh.last - sh.first + 1;  // uniform
   long long carry = 0;
+  int my_len = 0;   // request tid's length (B <= kFinalThreads)
   for (int r0 = 0; r0 < B; r0 += kFinalThreads) {
     const int r = r0 + tid;
     int lt = 0, eq = 0;
@@ -388,10 +397,22 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a) {
       len = lt + (int)max(0ll, min((long long)eq, (long long)ties_admitted - ex));
     }
     if (r < B) a.lengths[r] = len;
+    if (r0 == 0) my_len = len;
   }
+  if constexpr (WL) worklist_from_lengths(wsh, v, my_len);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <bool WL>
+void launch_final(const SchedArgs& a, const VerifyArgs& v, int n, hipStream_t s) {
+  const dim3 g(1), b(kFinalThreads);
+  if (n <= 1 * kFinalThreads) hipLaunchKernelGGL((final_kernel<1, WL>), g, b, 0, s, a, v);
+  else if (n <= 2 * kFinalThreads) hipLaunchKernelGGL((final_kernel<2, WL>), g, b, 0, s, a, v);
+  else if (n <= 4 * kFinalThreads) hipLaunchKernelGGL((final_kernel<4, WL>), g, b, 0, s, a, v);
+  else if (n <= 8 * kFinalThreads) hipLaunchKernelGGL((final_kernel<8, WL>), g, b, 0, s, a, v);
+  else hipLaunchKernelGGL((final_kernel<16, WL>), g, b, 0, s, a, v);
+}
 
 }  // namespace spec
 
@@ -403,7 +424,9 @@ extern "C" size_t spec_schedule_workspace_size(int32_t B, int32_t gamma) {
   return 3 * align256(n * sizeof(unsigned));
 }
 
-static int32_t launch_schedule(SchedArgs a, void* workspace, size_t workspace_bytes, hipStream_t s) {
+// v: the bound arguments of a verify call whose work list the final kernel writes, or NULL.
+static int32_t launch_schedule(SchedArgs a, void* workspace, size_t workspace_bytes, hipStream_t s,
+                               const VerifyArgs* v = nullptr) {
   const int B = a.B, gamma = a.G;
   if (!workspace || workspace_bytes < spec_schedule_workspace_size(B, gamma) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -416,11 +439,8 @@ static int32_t launch_schedule(SchedArgs a, void* workspace, size_t workspace_by
   a.sorted = reinterpret_cast<unsigned*>(ws + 2 * seg);
   hipLaunchKernelGGL(keys_kernel, dim3((n + kKeysThreads - 1) / kKeysThreads), dim3(kKeysThreads), 0, s, a);
   hipLaunchKernelGGL(rank_kernel, dim3((n + kChunk - 1) / kChunk), dim3(kChunk * kRankParts), 0, s, a);
-  if (n <= 1 * kFinalThreads) hipLaunchKernelGGL(final_kernel<1>, dim3(1), dim3(kFinalThreads), 0, s, a);
-  else if (n <= 2 * kFinalThreads) hipLaunchKernelGGL(final_kernel<2>, dim3(1), dim3(kFinalThreads), 0, s, a);
-  else if (n <= 4 * kFinalThreads) hipLaunchKernelGGL(final_kernel<4>, dim3(1), dim3(kFinalThreads), 0, s, a);
-  else if (n <= 8 * kFinalThreads) hipLaunchKernelGGL(final_kernel<8>, dim3(1), dim3(kFinalThreads), 0, s, a);
-  else hipLaunchKernelGGL(final_kernel<16>, dim3(1), dim3(kFinalThreads), 0, s, a);
+  if (v) launch_final<true>(a, *v, n, s);
+  else launch_final<false>(a, VerifyArgs{}, n, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
@@ -470,4 +490,40 @@ extern "C" int32_t spec_schedule_topk(int32_t B, int32_t gamma, const float* con
   SchedArgs a{B, gamma, 0, kSchedTopK, conf, nullptr, lengths_out, nullptr, status,
               nullptr, nullptr, nullptr, capacity, nullptr};
   return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const float* conf,
+                                        const double* sps, int32_t sps_len, int32_t budget_tokens, int32_t mode,
+                                        const void* target_logits, const void* draft_logits,
+                                        const int32_t* draft_tokens, const float* temperature,
+                                        const int32_t* top_k, const uint64_t* seed, int32_t* lengths_out,
+                                        double* theta_out, int32_t* sched_status, int32_t* num_accepted,
+                                        int32_t* out_tokens, float* accept_prob, int32_t* status,
+                                        void* sched_workspace, size_t sched_workspace_bytes,
+                                        void* verify_workspace, size_t verify_workspace_bytes, void* stream,
+                                        void* event_before, void* event_after) {
+  int32_t rc = check_search_args(B, gamma, conf, sps, sps_len, budget_tokens);
+  if (rc != SPEC_OK) return rc;
+  if (mode != SPEC_SCHED_EARLY_STOP && mode != SPEC_SCHED_GLOBAL) return SPEC_ERR_INVALID_ARG;
+  if (budget_tokens < 1 || !lengths_out) return SPEC_ERR_INVALID_ARG;
+  if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
+  if (!target_logits || !draft_logits || !draft_tokens || !temperature || !seed || !num_accepted || !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(target_logits) || !aligned16(draft_logits)) return SPEC_ERR_INVALID_ARG;
+  VerifyArgs v{};
+  v.B = B; v.G = gamma; v.V = V; v.greedy_only = 0;
+  v.target = target_logits; v.draft = draft_logits; v.tokens = draft_tokens; v.lengths = lengths_out;
+  v.temperature = temperature; v.top_k = top_k; v.seed = seed;
+  v.num_accepted = num_accepted; v.out_tokens = out_tokens; v.accept_prob = accept_prob; v.status = status;
+  v.max_items = budget_tokens;   // the schedule keeps sum (L_i + 1) within it unless the budget is below B
+  rc = bind_workspace(v, dtype, verify_workspace, verify_workspace_bytes, 0, nullptr);
+  if (rc != SPEC_OK) return rc;
+  SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, sched_status,
+              nullptr, nullptr, nullptr, nullptr, nullptr};
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool fuse = B <= kFinalThreads;
+  rc = launch_schedule(a, sched_workspace, sched_workspace_bytes, s, fuse ? &v : nullptr);
+  if (rc != SPEC_OK) return rc;
+  v.wl_ready = fuse ? 1 : 0;
+  return launch_verify_bound(v, dtype, s, event_before, event_after);
 }

@@ -176,83 +176,10 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
 // per-position counts come from ballots, so the only global round trips are the lengths' and the
 // tokens'.  Items are ordered as by worklist_kernel.
 __global__ __launch_bounds__(kWorklistThreads) void worklist_small_kernel(VerifyArgs a) {
-  __shared__ int cnt[kWorklistThreads / SPEC_WAVE][SPEC_MAX_GAMMA + 1];
-  __shared__ int ctot[SPEC_MAX_GAMMA + 1];
-  __shared__ int off[SPEC_MAX_GAMMA + 2];
-  __shared__ long long wsum[kWorklistThreads / SPEC_WAVE];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int G = a.G, B = a.B;
-  const int NW = (int)(blockDim.x >> 6);
-  const bool want_x = a.tokens && !a.overlap_only;
-  const int L = (tid < B) ? (a.lengths ? a.lengths[tid] : G) : -1;
-  const bool valid = L >= 0 && L <= G;
-  int xs[8];   // the first eight draft tokens, fetched while the counts are formed
-#pragma unroll
-  for (int u = 0; u < 8; ++u) xs[u] = (want_x && valid && u < L) ? a.tokens[(size_t)tid * G + u] : -1;
-  int drop = 0;
-  if (a.max_items > 0) {
-    // token cap: the running sum of L_i + 1 in request order
-    const long long n = valid ? L + 1 : 0;
-    const long long in = wave_inclusive_sum_i64(n, lane);
-    if (lane == 63) wsum[wave] = in;
-    __syncthreads();
-    long long before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    drop = (n > 0 && before + in > (long long)a.max_items);
-  }
-  if (tid < B) {
-    a.req_status[tid] = drop ? SPEC_REQ_OVER_BUDGET : 0;
-    a.ereq[tid].amb_n = 0;
-  }
-  const int last = (valid && !drop) ? (a.overlap_only ? L - 1 : L) : -1;
-  for (int k = 0; k <= G; ++k) {
-    const unsigned long long m = __ballot(last >= k);
-    if (lane == 0) cnt[wave][k] = __popcll(m);
-  }
-  __syncthreads();
-  if (tid <= G) {
-    // per-wave exclusive offsets within position tid, and its total c_k = #{i : last_i >= k}
-    int run = 0;
-    for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w][tid];
-      cnt[w][tid] = run;
-      run += c;
-    }
-    ctot[tid] = run;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // items of position k start at off[k] = c_0 + ... + c_{k-1}
-    const long long c = (lane <= G) ? ctot[lane] : 0;
-    const long long incl = wave_inclusive_sum_i64(c, lane);
-    if (lane <= G) off[lane] = (int)(incl - c);
-    const int total64 = (int)__shfl(incl, 63, SPEC_WAVE);
-    if (lane == 0) {
-      if (G == SPEC_WAVE) off[SPEC_WAVE] = total64;   // position 64 (gamma = 64)
-      const int nit = (G == SPEC_WAVE) ? total64 + ctot[SPEC_WAVE] : total64;
-      off[G + 1] = nit;
-      *a.nitems = nit;
-    }
-  }
-  __syncthreads();
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int k0 = 0; k0 <= G; k0 += 8) {
-    int x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      x[u] = (k0 == 0) ? xs[u] : ((want_x && valid && k0 + u < L) ? a.tokens[(size_t)tid * G + k0 + u] : -1);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u;
-      if (k > G) break;
-      const unsigned long long m = __ballot(last >= k);
-      if (last >= k) {
-        const int idx = off[k] + cnt[wave][k] + __popcll(m & below);
-        a.items[idx] = (tid << 7) | k;
-        a.items_x[idx] = x[u];
-      }
-    }
-  }
+  __shared__ WorklistShared sh;
+  const int tid = threadIdx.x;
+  const int L = (tid < a.B) ? (a.lengths ? a.lengths[tid] : a.G) : -1;
+  worklist_from_lengths(sh, a, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -970,7 +897,8 @@ size_t workspace_bytes(int B, int G, int V, bool emit) {
 }
 
 void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1) {
-  if (!a.flat && a.B <= kWorklistThreads)
+  if (a.wl_ready) {
+  } else if (!a.flat && a.B <= kWorklistThreads)
     hipLaunchKernelGGL(worklist_small_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   else
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
@@ -990,10 +918,7 @@ void launch_combine(const VerifyArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel, dim3(cgrid), dim3(256), 0, s, a);
 }
 
-static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
-                             void* ev1) {
-  const int32_t rc = bind_workspace(a, dtype, ws, ws_bytes, 0, nullptr);
-  if (rc != SPEC_OK) return rc;
+int32_t launch_verify_bound(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1) {
   launch_statistics(a, dtype, s, ev0, ev1);
   a.r0 = 0;
   a.r1 = a.B;
@@ -1005,6 +930,13 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
   if (!fused) launch_combine(a, s);
   launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes, hipStream_t s, void* ev0,
+                             void* ev1) {
+  const int32_t rc = bind_workspace(a, dtype, ws, ws_bytes, 0, nullptr);
+  if (rc != SPEC_OK) return rc;
+  return launch_verify_bound(a, dtype, s, ev0, ev1);
 }
 
 }  // namespace spec

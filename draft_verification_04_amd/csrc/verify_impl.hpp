@@ -83,6 +83,7 @@ struct VerifyArgs {
   int r0, r1;          // the emit kernels handle requests [r0, r1)
   int emit_segs;       // emit-pass workgroups per request (1 = one fused workgroup, else 2 .. kMaxEmitSegs)
   int max_items;       // caller's bound on the number of work items (0: none); sizes the streaming grid
+  int wl_ready;        // the work list was written by the scheduler's last kernel (no work-list kernel)
 };
 
 constexpr int kStreamThreads = 512;
@@ -192,6 +193,95 @@ __device__ inline const char* draft_row(const VerifyArgs& a, int i, int k) {
 // Launch the emitted-token kernels (defined in emit.hip).
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s);
 
+// Scratch of worklist_from_lengths.
+struct WorklistShared {
+  int cnt[kWorklistThreads / SPEC_WAVE][SPEC_MAX_GAMMA + 1];
+  int ctot[SPEC_MAX_GAMMA + 1];
+  int off[SPEC_MAX_GAMMA + 2];
+  long long wsum[kWorklistThreads / SPEC_WAVE];
+};
+
+// The position-major work list of a call with B <= kWorklistThreads (padded layout), by one
+// workgroup of kWorklistThreads threads in which thread t holds request t's length L (its raw value,
+// anything for t >= B): items (i << 7 | k) for every k <= L_i (k < L_i for overlap_only), ordered
+// by position, then request; each item's draft token (k < L_i); the item count; the request's
+// cap mark (token cap a.max_items > 0: from the first request whose running sum of L_i + 1 passes
+// the cap on, valid requests are marked SPEC_REQ_OVER_BUDGET and get no items) and its emit counter.
+__device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArgs& a, int L_raw) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.G, B = a.B;
+  const int NW = (int)(blockDim.x >> 6);
+  const bool want_x = a.tokens && !a.overlap_only;
+  const int L = (tid < B) ? L_raw : -1;
+  const bool valid = L >= 0 && L <= G;
+  int xs[8];   // the first eight draft tokens, fetched while the counts are formed
+#pragma unroll
+  for (int u = 0; u < 8; ++u) xs[u] = (want_x && valid && u < L) ? a.tokens[(size_t)tid * G + u] : -1;
+  int drop = 0;
+  if (a.max_items > 0) {
+    const long long n = valid ? L + 1 : 0;
+    const long long in = wave_inclusive_sum_i64(n, lane);
+    if (lane == 63) sh.wsum[wave] = in;
+    __syncthreads();
+    long long before = 0;
+    for (int w = 0; w < wave; ++w) before += sh.wsum[w];
+    drop = (n > 0 && before + in > (long long)a.max_items);
+  }
+  if (tid < B) {
+    a.req_status[tid] = drop ? SPEC_REQ_OVER_BUDGET : 0;
+    a.ereq[tid].amb_n = 0;
+  }
+  const int last = (valid && !drop) ? (a.overlap_only ? L - 1 : L) : -1;
+  for (int k = 0; k <= G; ++k) {
+    const unsigned long long m = __ballot(last >= k);
+    if (lane == 0) sh.cnt[wave][k] = __popcll(m);
+  }
+  __syncthreads();
+  if (tid <= G) {
+    // per-wave exclusive offsets within position tid, and its total c_k = #{i : last_i >= k}
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = sh.cnt[w][tid];
+      sh.cnt[w][tid] = run;
+      run += c;
+    }
+    sh.ctot[tid] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // items of position k start at off[k] = c_0 + ... + c_{k-1}
+    const long long c = (lane <= G) ? sh.ctot[lane] : 0;
+    const long long incl = wave_inclusive_sum_i64(c, lane);
+    if (lane <= G) sh.off[lane] = (int)(incl - c);
+    const int total64 = (int)__shfl(incl, 63, SPEC_WAVE);
+    if (lane == 0) {
+      if (G == SPEC_WAVE) sh.off[SPEC_WAVE] = total64;   // position 64 (gamma = 64)
+      const int nit = (G == SPEC_WAVE) ? total64 + sh.ctot[SPEC_WAVE] : total64;
+      sh.off[G + 1] = nit;
+      *a.nitems = nit;
+    }
+  }
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int k0 = 0; k0 <= G; k0 += 8) {
+    int x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      x[u] = (k0 == 0) ? xs[u] : ((want_x && valid && k0 + u < L) ? a.tokens[(size_t)tid * G + k0 + u] : -1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      if (k > G) break;
+      const unsigned long long m = __ballot(last >= k);
+      if (last >= k) {
+        const int idx = sh.off[k] + sh.cnt[wave][k] + __popcll(m & below);
+        a.items[idx] = (tid << 7) | k;
+        a.items_x[idx] = x[u];
+      }
+    }
+  }
+}
+
 // Host steps shared by the entry points (defined in verify.hip).
 bool shape_ok(int B, int G, int V, int dtype);
 bool aligned16(const void* p);
@@ -199,8 +289,12 @@ bool aligned16(const void* p);
 // 256-byte aligned); SPEC_ERR_WORKSPACE when it is missing, short or misaligned.
 int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size_t extra_bytes, char** extra);
 size_t workspace_bytes(int B, int G, int V, bool emit);
-// Work list, then the streaming statistics (events, when given, bracket the streaming kernel).
+// Work list (unless a.wl_ready), then the streaming statistics (events, when given, bracket the
+// streaming kernel).
 void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1);
+// Statistics, acceptance and emit of a call whose workspace is bound (the verify kernels of
+// spec_verify after the argument checks).
+int32_t launch_verify_bound(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1);
 // Segment partials -> row records and (with draft tokens) the acceptance test.
 void launch_combine(const VerifyArgs& a, hipStream_t s);
 

@@ -263,6 +263,36 @@ int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_schedule_verify -- one step of the scheduled path (paper §3.2.2, then
+ * §2.1): spec_schedule_lengths followed by spec_verify_bounded on the lengths
+ * it selects, with the budget as the token cap, enqueued as one call.
+ *   Scheduler arguments (conf, sps, sps_len, budget_tokens, mode) and outputs
+ *   (lengths_out [B] required, theta_out or NULL, sched_status [B] or NULL) as
+ *   for spec_schedule_lengths; budget_tokens >= 1.  Verify arguments (V, dtype,
+ *   target_logits, draft_logits, draft_tokens, temperature, top_k, seed) and
+ *   outputs (num_accepted, out_tokens, accept_prob, status) as for spec_verify,
+ *   with lengths = lengths_out; event_before / event_after as for
+ *   spec_verify_profiled.
+ *   Workspaces: sched_workspace of spec_schedule_workspace_size(B, gamma) bytes
+ *   and verify_workspace of spec_verify_workspace_size(B, gamma, V) bytes, both
+ *   256-byte aligned, distinct, owned by the caller.
+ *   Every output equals that of the two calls made one after the other on the
+ *   same stream.  With B <= 1024 the scheduler's last kernel also writes the
+ *   verify work list (one kernel fewer).
+ * Errors: those of the two calls, checked before anything is enqueued.
+ */
+int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const float* conf,
+                             const double* sps, int32_t sps_len, int32_t budget_tokens, int32_t mode,
+                             const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                             const uint64_t* seed, int32_t* lengths_out, double* theta_out,
+                             int32_t* sched_status, int32_t* num_accepted, int32_t* out_tokens,
+                             float* accept_prob, int32_t* status, void* sched_workspace,
+                             size_t sched_workspace_bytes, void* verify_workspace,
+                             size_t verify_workspace_bytes, void* stream, void* event_before,
+                             void* event_after);
+
+/*
  * Asynchronous scheduling (DSpark paper, §5.2): the admission capacity of a
  * step is fixed from confidences predicted two steps earlier (the global
  * search, without the early-stop break), and the step then admits its current

@@ -254,3 +254,32 @@ def test_sts_rejects_bad_arguments(lib):
     assert lib.spec_sts_apply(4, 4, None, p, p, None) == 1
     assert lib.spec_sts_apply(4, 4, p, None, p, None) == 1
     assert lib.spec_sts_apply(4, 4, p, p, None, None) == 1
+
+
+def test_schedule_verify_rejects_bad_arguments(lib):
+    keep, p = _fake()
+    vws = lib.spec_verify_workspace_size(4, 4, 10)
+    sws = lib.spec_schedule_workspace_size(4, 4)
+
+    # every pointer argument defaults to the fake buffer; the workspaces are refused as misaligned
+    def call(B=4, G=4, V=10, dt=1, conf=p, sps=p, sps_len=100, budget=10, mode=0, t=p, d=p, x=p, T=p, s=p,
+             L=p, n=p, o=p, sw=p, swb=sws, vw=p, vwb=vws):
+        return lib.spec_schedule_verify(B, G, V, dt, conf, sps, sps_len, budget, mode, t, d, x, T, None, s, L,
+                                        None, None, n, o, None, None, sw, swb, vw, vwb, None, None, None)
+    assert call(B=0) == 1
+    assert call(G=65) == 1
+    assert call(V=0) == 1
+    assert call(dt=7) == 1
+    assert call(mode=2) == 1
+    assert call(budget=0) == 1
+    assert call(sps_len=10) == 1                               # cost table short
+    assert call(conf=None) == 1
+    assert call(L=None) == 1
+    assert call(t=None) == 1
+    assert call(x=None) == 1
+    assert call(s=None) == 1
+    assert call(o=None) == 1
+    assert call(d=ctypes.c_void_p(p.value + 2)) == 1           # misaligned logits
+    assert call(B=2048, G=16, sps_len=10 ** 6) == 3
+    assert call() == 2                                         # workspaces
+    assert call(vwb=vws - 1) == 2
