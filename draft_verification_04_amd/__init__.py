@@ -200,7 +200,7 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     draft_tokens [B, gamma] int32; lengths [B] int32 or None; temperature [B]
     float32 (default ones); top_k [B] int32 or None; seed [B] int64 holding
     the uint64 bit pattern (default zeros).  `events` = (before, after)
-    torch.cuda.Event pair recorded around the row-streaming kernel.
+    HipEvent pair taking the start and end of the row-streaming kernel.
     `max_tokens` (spec_verify_bounded): the caller's bound on sum_i (L_i + 1),
     e.g. the scheduler's token budget; it sizes the streaming grid only.
     """

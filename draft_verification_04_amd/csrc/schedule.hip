@@ -221,6 +221,11 @@ template <int K, bool WL>
 __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, VerifyArgs v) {
   __shared__ FinalShared<K> sh;
   __shared__ WorklistShared wsh;
+  // the verify work list's draft tokens, fetched with the keys (the largest tile fetches them at
+  // the end: its registers are taken)
+  constexpr bool kEarlyTokens = WL && K <= 8;
+  int xp[kWlPre];
+  if constexpr (kEarlyTokens) worklist_prefetch(v, xp);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int B = a.B, G = a.G;
   const int N = B * G;
@@ -349,7 +354,10 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
   if (!a.lengths) return;
   if (mstar == 0) {
     for (int r = tid; r < B; r += kFinalThreads) a.lengths[r] = 0;
-    if constexpr (WL) worklist_from_lengths(wsh, v, 0);
+    if constexpr (WL) {
+      if constexpr (!kEarlyTokens) worklist_prefetch(v, xp);
+      worklist_from_lengths(wsh, v, 0, xp);
+    }
     return;
   }
   // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
@@ -399,7 +407,10 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     if (r < B) a.lengths[r] = len;
     if (r0 == 0) my_len = len;
   }
-  if constexpr (WL) worklist_from_lengths(wsh, v, my_len);
+  if constexpr (WL) {
+    if constexpr (!kEarlyTokens) worklist_prefetch(v, xp);
+    worklist_from_lengths(wsh, v, my_len, xp);
+  }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

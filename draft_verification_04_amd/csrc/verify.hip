@@ -20,6 +20,8 @@
 #include "common.hpp"
 #include "philox.hpp"
 #include "verify_impl.hpp"
+
+#include <hip/hip_ext.h>
 #include "spec_verify.h"
 
 #include <algorithm>
@@ -179,7 +181,9 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_small_kernel(Verify
   __shared__ WorklistShared sh;
   const int tid = threadIdx.x;
   const int L = (tid < a.B) ? (a.lengths ? a.lengths[tid] : a.G) : -1;
-  worklist_from_lengths(sh, a, L);
+  int xp[kWlPre];
+  worklist_prefetch(a, xp);
+  worklist_from_lengths(sh, a, L, xp);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,15 +906,16 @@ void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0,
     hipLaunchKernelGGL(worklist_small_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   else
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
-  if (ev0) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev0), s);   // a failure shows on the caller's event query
   size_t items = (size_t)a.B * (a.G + 1);
   if (a.max_items > 0 && (size_t)a.max_items < items) items = (size_t)a.max_items;
-  const unsigned grid = (unsigned)(items * a.nseg);
+  const dim3 grid((unsigned)(items * a.nseg)), block(kStreamThreads);
+  // The events take the dispatch's own start and end times (no marker packets around it, which
+  // would stall the stream before and after the kernel); a failure shows on the caller's event query.
+  const hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev0), e1 = reinterpret_cast<hipEvent_t>(ev1);
   if (dtype == SPEC_BF16)
-    hipLaunchKernelGGL(stream_kernel<true>, dim3(grid), dim3(kStreamThreads), 0, s, a);
+    hipExtLaunchKernelGGL(stream_kernel<true>, grid, block, 0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL(stream_kernel<false>, dim3(grid), dim3(kStreamThreads), 0, s, a);
-  if (ev1) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), s);
+    hipExtLaunchKernelGGL(stream_kernel<false>, grid, block, 0, s, e0, e1, 0, a);
 }
 
 void launch_combine(const VerifyArgs& a, hipStream_t s) {

@@ -201,30 +201,42 @@ struct WorklistShared {
   long long wsum[kWorklistThreads / SPEC_WAVE];
 };
 
+constexpr int kWlPre = 16;   // draft tokens per request fetched ahead of the work list
+
+// Request t's first min(gamma, kWlPre) draft tokens into thread t's registers (t < B; -1 elsewhere,
+// and everywhere when the work list carries no tokens).  They do not depend on the lengths, so a
+// caller issues these loads before it knows them.
+__device__ inline void worklist_prefetch(const VerifyArgs& a, int (&xp)[kWlPre]) {
+  const int tid = threadIdx.x;
+  const bool want = a.tokens && !a.overlap_only && tid < a.B;
+#pragma unroll
+  for (int u = 0; u < kWlPre; ++u) xp[u] = (want && u < a.G) ? a.tokens[(size_t)tid * a.G + u] : -1;
+}
+
 // The position-major work list of a call with B <= kWorklistThreads (padded layout), by one
 // workgroup of kWorklistThreads threads in which thread t holds request t's length L (its raw value,
-// anything for t >= B): items (i << 7 | k) for every k <= L_i (k < L_i for overlap_only), ordered
-// by position, then request; each item's draft token (k < L_i); the item count; the request's
-// cap mark (token cap a.max_items > 0: from the first request whose running sum of L_i + 1 passes
-// the cap on, valid requests are marked SPEC_REQ_OVER_BUDGET and get no items) and its emit counter.
-__device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArgs& a, int L_raw) {
+// anything for t >= B) and the tokens of worklist_prefetch: items (i << 7 | k) for every k <= L_i
+// (k < L_i for overlap_only), ordered by position, then request; each item's draft token (k < L_i);
+// the item count; the request's cap mark (token cap a.max_items > 0: from the first request whose
+// running sum of L_i + 1 passes the cap on, valid requests are marked SPEC_REQ_OVER_BUDGET and get
+// no items) and its emit counter.
+__device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArgs& a, int L_raw,
+                                             const int (&xp)[kWlPre]) {
+  constexpr int NW = kWorklistThreads / SPEC_WAVE;   // the workgroup is kWorklistThreads wide
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G, B = a.B;
-  const int NW = (int)(blockDim.x >> 6);
   const bool want_x = a.tokens && !a.overlap_only;
   const int L = (tid < B) ? L_raw : -1;
   const bool valid = L >= 0 && L <= G;
-  int xs[8];   // the first eight draft tokens, fetched while the counts are formed
-#pragma unroll
-  for (int u = 0; u < 8; ++u) xs[u] = (want_x && valid && u < L) ? a.tokens[(size_t)tid * G + u] : -1;
   int drop = 0;
   if (a.max_items > 0) {
     const long long n = valid ? L + 1 : 0;
     const long long in = wave_inclusive_sum_i64(n, lane);
     if (lane == 63) sh.wsum[wave] = in;
     __syncthreads();
-    long long before = 0;
-    for (int w = 0; w < wave; ++w) before += sh.wsum[w];
+    long long before = 0;   // the earlier waves' totals (independent reads, no loop-carried wait)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) before += (w < wave) ? sh.wsum[w] : 0;
     drop = (n > 0 && before + in > (long long)a.max_items);
   }
   if (tid < B) {
@@ -239,11 +251,14 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
   __syncthreads();
   if (tid <= G) {
     // per-wave exclusive offsets within position tid, and its total c_k = #{i : last_i >= k}
+    int c[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c[w] = sh.cnt[w][tid];
     int run = 0;
+#pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int c = sh.cnt[w][tid];
       sh.cnt[w][tid] = run;
-      run += c;
+      run += c[w];
     }
     sh.ctot[tid] = run;
   }
@@ -263,11 +278,8 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
   }
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int k0 = 0; k0 <= G; k0 += 8) {
-    int x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      x[u] = (k0 == 0) ? xs[u] : ((want_x && valid && k0 + u < L) ? a.tokens[(size_t)tid * G + k0 + u] : -1);
+  // positions k0 .. k0 + 7 (at most G): x[u] is the draft token of position k0 + u
+  auto put8 = [&](int k0, const int (&x)[8]) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u;
@@ -276,9 +288,25 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
       if (last >= k) {
         const int idx = sh.off[k] + sh.cnt[wave][k] + __popcll(m & below);
         a.items[idx] = (tid << 7) | k;
-        a.items_x[idx] = x[u];
+        a.items_x[idx] = (k < L) ? x[u] : -1;
       }
     }
+  };
+  int x0[8], x1[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    x0[u] = xp[u];
+    x1[u] = xp[8 + u];
+  }
+  put8(0, x0);
+  if (G >= 8) put8(8, x1);
+  static_assert(kWlPre == 16, "two groups of eight fetched ahead");
+  for (int k0 = kWlPre; k0 <= G; k0 += 8) {
+    int x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      x[u] = (want_x && valid && k0 + u < L) ? a.tokens[(size_t)tid * G + k0 + u] : -1;
+    put8(k0, x);
   }
 }
 

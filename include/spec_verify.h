@@ -147,10 +147,11 @@ int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * spec_verify_profiled -- spec_verify, recording two caller-created
- * hipEvent_t (passed as void*) on `stream` immediately before and after the
- * launch of the row-streaming kernel that reads the logits.  Either event
- * may be NULL.  For measurement only; results are identical to spec_verify.
+ * spec_verify_profiled -- spec_verify, with two caller-created hipEvent_t
+ * (passed as void*) that take the start and end times of the dispatch of the
+ * row-streaming kernel that reads the logits (hipExtLaunchKernel's events: no
+ * separate marker is enqueued).  Either event may be NULL.  For measurement
+ * only; results are identical to spec_verify.
  */
 int32_t spec_verify_profiled(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                              const void* target_logits, const void* draft_logits,
