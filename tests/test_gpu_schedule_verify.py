@@ -118,3 +118,14 @@ def test_bad_confidences(sv):
     L = to_np(f["lengths"])
     assert L[3] == 0 and L[7] == 0
     assert to_np(f["sched_status"])[[3, 7]].all()
+
+
+def test_fp32_logits_greedy_rows_and_top_k(sv):
+    # fp32 logits; every fourth request takes the greedy rule (T = 0), every third a top-k of 7
+    w = make_workload("tiny", DEV, B=64, gamma=6, V=2000, seed=78, with_schedule=True)
+    assert w.target.dtype == torch.float32
+    w.temperature[::4] = 0.0
+    w.top_k = torch.zeros(w.B, dtype=torch.int32, device=DEV)
+    w.top_k[::3] = 7
+    f = _check(sv, w, w.sps, w.budget, MODE_GLOBAL)
+    assert (to_np(f["status"]) == 0).all()
