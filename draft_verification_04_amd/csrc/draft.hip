@@ -7,8 +7,8 @@
 //
 // One draft step k is two kernels:
 //   markov_logits_kernel -- for every request at once, the bias is a dense product
-//       [B x r] (gathered embedding rows) x [r x V] (projection): MFMA 32x32x16 bf16 tiles with
-//       fp32 accumulation.  Each wave keeps the projection rows of its 32 tokens in registers and
+//       [B x r] (gathered embedding rows) x [r x V] (projection): MFMA 16x16x32 bf16 tiles with
+//       fp32 accumulation.  Each wave keeps the projection rows of its 16 tokens in registers and
 //       walks the requests 32 at a time; the epilogue adds U_k, rounds to the storage type, writes
 //       the draft logits and records per (request, 128-token tile) the largest stored value and
 //       whether a NaN or +inf was stored.
@@ -35,14 +35,14 @@ namespace spec {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kDraftThreads = 256;   // markov_logits_kernel: 4 waves
-constexpr int kTileTokens = 128;     // tokens per workgroup (32 per wave)
-constexpr int kReqBlock = 32;        // requests per MFMA block
+constexpr int kDraftThreads = 512;   // markov_logits_kernel: 8 waves
+constexpr int kTileTokens = 128;     // tokens per workgroup (16 per wave)
+constexpr int kReqBlock = 32;        // requests per block (two MFMA columns of 16)
 constexpr int kMaxSteps = 16;        // rank / 16 at most (r <= 256)
 constexpr int kSampleThreads = 256;  // markov_finish_kernel: a wave per item
 constexpr int kDrawThreads = 1024;   // markov_sample_kernel: one workgroup per request
@@ -74,7 +74,7 @@ struct DraftArgs {
   void* logits;              // [B, G, V]
   float* conf;               // [B, G] or null
   int32_t* status;           // [B]
-  DPart* part;               // [B, nwg] workspace
+  DPart* part;               // [B rounded up to kReqBlock, nwg] workspace
   int32_t* req_status;       // [B] workspace
 };
 
@@ -97,39 +97,44 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
 
 // Step k: draft logits z_k = U_k + W1[x_{k-1}] W2 for every request, and per-tile statistics.
 //
-// A workgroup owns 128 tokens (32 per wave) and walks the requests 32 at a time.  Per request
-// block: the MFMA chain multiplies the wave's projection rows (registers) by the block's embedding
-// rows (LDS); the epilogue reads U_k from an LDS tile, writes the rounded z_k back in place and
-// folds the values into statistics; after the block's barrier the workgroup stores the z_k tile
-// with whole-line 16-byte stores.  The embedding rows and the U_k tile of the next block are
-// loaded (whole lines, 16 bytes per thread) while the current block computes.  Tiles that are not
-// whole (the last one, or rows not 16-byte aligned) take per-element global accesses instead.
-// Operand steps beyond r/16 are zero on both sides (exact zeros).
+// A workgroup owns 128 tokens (16 per wave) and walks the requests 32 at a time.  Per request
+// block: each wave's MFMA 16x16x32 chain multiplies its projection rows (registers: 16 tokens x r,
+// 32 VGPRs at r = 256) by the block's embedding rows (LDS, two columns of 16 requests); the epilogue
+// reads U_k from an LDS tile, writes the rounded z_k back in place and folds the values into
+// statistics; after the block's barrier the workgroup stores the z_k tile with whole-line 16-byte
+// stores.  The embedding rows and the U_k tile of the next block are loaded (whole lines, 16 bytes
+// per thread) while the current block computes.  Tiles that are not whole (the last one, or rows
+// not 16-byte aligned) take per-element global accesses instead.  Operand k beyond r is zero on
+// both sides (exact zeros).  Sixteen tokens per wave keep the kernel within 128 VGPRs, so two
+// 8-wave workgroups share a CU.
 template <int ES>
-__global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs a) {
+__global__ __launch_bounds__(kDraftThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void markov_logits_kernel(DraftArgs a) {
   constexpr int RS = kMaxSteps * 16 + 8;            // LDS row stride of the embedding rows (bf16)
   constexpr int USB = kTileTokens * ES + 16;        // LDS row stride of the U/z tile (bytes)
   constexpr int UCPR = kTileTokens * ES / 16;       // 16-byte chunks per tile row
-  constexpr int UPT = kReqBlock * UCPR / kDraftThreads;  // chunks per thread (2 bf16, 4 fp32)
-  __shared__ DPart sp[2][kDraftThreads / 64][kReqBlock];
+  constexpr int UPT = kReqBlock * UCPR / kDraftThreads;  // chunks per thread (1 bf16, 2 fp32)
+  constexpr int NW = kDraftThreads / 64;
+  constexpr int NK = kMaxSteps / 2;                 // 16x16x32 steps at the largest rank
+  __shared__ DPart sp[2][NW][kReqBlock];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kReqBlock * RS];
   __shared__ __attribute__((aligned(16))) unsigned char sU[3][kReqBlock * USB];
-  __shared__ int sPrev[2][kReqBlock];
+  __shared__ int sPrev[4][kReqBlock];   // ids x_{k-1} of block b in sPrev[b % 4]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int tl = lane & 31, h = lane >> 5;
+  const int tn = lane & 15, q = lane >> 4;   // MFMA row (token) / column (request), and k or row group
   const int V = a.V, r = a.r, G = a.G, k = a.k, B = a.B;
-  const int nk = r >> 4;
   const int tile0 = blockIdx.x * kTileTokens;
-  const int n0 = tile0 + wv * 32;
+  const int n0 = tile0 + wv * 16;
   const bf16x8 zero8 = {};
 
-  // Projection operand (MFMA A: row = token, 8 consecutive k per lane half): token n0 + tl.
-  const uint16_t* w2 = a.W2t + (size_t)min(n0 + tl, V - 1) * r + 8 * h;
-  bf16x8 wop[kMaxSteps];
+  // Projection operand (MFMA A: row = token n0 + tn, k = 32 s + 8 q .. + 7).
+  const uint16_t* w2 = a.W2t + (size_t)min(n0 + tn, V - 1) * r;
+  bf16x8 wop[NK];
 #pragma unroll
-  for (int kk = 0; kk < kMaxSteps; ++kk) {
-    const bf16x8 v = load_bf16x8(w2 + min(kk, nk - 1) * 16);
-    wop[kk] = kk < nk ? v : zero8;
+  for (int s = 0; s < NK; ++s) {
+    const int kc = 32 * s + 8 * q;
+    const bf16x8 v = load_bf16x8(w2 + min(kc, r - 8));
+    wop[s] = kc < r ? v : zero8;
   }
 
   // x_{k-1} of request j (index clamped; a bad value selects row 0: a bad request's rows are
@@ -141,21 +146,19 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
   auto prev_of = [&](int j) -> int { return prev_ok(prev_raw(j)); };
   // Embedding rows W1[x_{k-1}] of a request block: 32 rows of r bf16, 16-byte chunks.
   const int cpr = r >> 3;
-  const int nchunk = kReqBlock * cpr;  // <= 1024: at most 4 per thread
-  v4u32 gw[4];
-  auto load_rows = [&](int pb) {
+  const int nchunk = kReqBlock * cpr;  // <= 1024: at most 2 per thread
+  v4u32 gw[2];
+  auto load_rows = [&](int pb) {   // unconditional: chunks past the rows reload the last one
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kDraftThreads;
-      if (c < nchunk) {
-        const int row = c / cpr, col = c - row * cpr;
-        gw[i] = *reinterpret_cast<const v4u32*>(a.W1 + (size_t)sPrev[pb][row] * r + col * 8);
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int c = min(tid + i * kDraftThreads, nchunk - 1);
+      const int row = c / cpr, col = c - row * cpr;
+      gw[i] = *reinterpret_cast<const v4u32*>(a.W1 + (size_t)sPrev[pb][row] * r + col * 8);
     }
   };
   auto store_rows = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int c = tid + i * kDraftThreads;
       if (c < nchunk) {
         const int row = c / cpr, col = c - row * cpr;
@@ -169,15 +172,14 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
   const char* ubase = reinterpret_cast<const char*>(a.base) + ((size_t)k * V + tile0) * ES;
   char* zbase = reinterpret_cast<char*>(a.logits) + ((size_t)k * V + tile0) * ES;
   v4u32 gu[UPT];
-  auto load_tile = [&](int rb) {
+  auto load_tile = [&](int rb) {   // unconditional: rows past B reload the last request's
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int c = tid + i * kDraftThreads;
       const int row = c / UCPR, col = c - row * UCPR;
-      const int j = rb * kReqBlock + row;
-      if (j < B)
-        gu[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u32*>(ubase + (size_t)j * rowstep * ES + col * 16));
+      const int j = min(rb * kReqBlock + row, B - 1);
+      gu[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4u32*>(ubase + (size_t)j * rowstep * ES + col * 16));
     }
   };
   auto store_tile_lds = [&](int ub) {
@@ -188,102 +190,117 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
       *reinterpret_cast<v4u32*>(&sU[ub][row * USB + col * 16]) = gu[i];
     }
   };
+  // Rows past B in the last block hold exactly request B-1's values (its id, its U_k row), so
+  // they are stored to row B-1 again, which keeps the stores unconditional.
   auto store_tile_global = [&](int rb, int ub) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int c = tid + i * kDraftThreads;
       const int row = c / UCPR, col = c - row * UCPR;
-      const int j = rb * kReqBlock + row;
-      if (j < B)
-        *reinterpret_cast<v4u32*>(zbase + (size_t)j * rowstep * ES + col * 16) =
-            *reinterpret_cast<const v4u32*>(&sU[ub][row * USB + col * 16]);
+      const int j = min(rb * kReqBlock + row, B - 1);
+      *reinterpret_cast<v4u32*>(zbase + (size_t)j * rowstep * ES + col * 16) =
+          *reinterpret_cast<const v4u32*>(&sU[ub][row * USB + col * 16]);
     }
   };
 
+  // The loads of block b + 2 are issued while block b computes and land in LDS at the end of
+  // block b + 1, a whole block later, so no block waits for its own loads; the ids of block b + 4
+  // are fetched by wave 1 during block b and stored during block b + 1.
   const int nrb = (B + kReqBlock - 1) / kReqBlock;
+  const bool idw = tid >= 64 && tid < 64 + kReqBlock;
   if (tid < kReqBlock) {
-    sPrev[0][tid] = prev_of(tid);
-    sPrev[1][tid] = prev_of(tid + kReqBlock);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) sPrev[b][tid] = prev_of(b * kReqBlock + tid);
   }
-  if (fast_tile) load_tile(0);
+  // every thread fetches the ids (only wave 1 stores them): no load under a condition in the loop
+  int pn = prev_raw(3 * kReqBlock + (tid & (kReqBlock - 1)));   // ids of block 3
+  typedef typename std::conditional<ES == 2, uint2, float4>::type UVec;
+  // whole tiles (FAST) and the rest take separate copies of the walk, so no branch on the tile
+  // kind sits inside it
+  auto walk = [&](auto fast_c) {
+  constexpr bool FAST = decltype(fast_c)::value;
+  if constexpr (FAST) load_tile(0);
   __syncthreads();  // sPrev
   load_rows(0);
   store_rows(0);
-  if (fast_tile) store_tile_lds(0);
+  if constexpr (FAST) store_tile_lds(0);
+  load_rows(1);     // block 1, in flight
+  if constexpr (FAST) load_tile(1);
   __syncthreads();
 
   for (int rb = 0; rb < nrb; ++rb) {
-    const int j = rb * kReqBlock + tl;
-    const bool valid = j < B;
     const int buf = rb & 1, ub = rb % 3;
     const bool more = rb + 1 < nrb;
-    if (more) {
-      load_rows(buf ^ 1);                 // rows of block rb + 1 (their ids were stored a block ago)
-      if (fast_tile) load_tile(rb + 1);
-    }
-    int pn2 = 0;  // wave 1 fetches the ids of block rb + 2; clamped when stored
-    const bool idw = tid >= 64 && tid < 64 + kReqBlock;
-    if (idw) pn2 = prev_raw((rb + 2) * kReqBlock + tid - 64);
-    // this lane's U_k values of the current block (stored in LDS before the last barrier)
-    unsigned char* urow = &sU[ub][tl * USB + (wv * 32 + 4 * h) * ES];
-    typedef typename std::conditional<ES == 2, uint2, float4>::type UVec;
-    UVec uv[4];
-    if (fast_tile) {
+    if (idw) sPrev[(rb + 3) & 3][tid - 64] = prev_ok(pn);    // ids of block rb + 3 (fetched a block ago)
+    pn = prev_raw((rb + 4) * kReqBlock + (tid & (kReqBlock - 1)));   // ids of block rb + 4
+    // this lane's U_k values of the current block (stored in LDS before the last barrier):
+    // requests 16 c + tn of the block (c = 0, 1), tokens n0 + 4 q .. + 3
+    unsigned char* urow[2];
+    UVec uv[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) uv[g] = *reinterpret_cast<const UVec*>(urow + 8 * g * ES);
+    for (int c = 0; c < 2; ++c) {
+      urow[c] = &sU[ub][(16 * c + tn) * USB + (wv * 16 + 4 * q) * ES];
+      if constexpr (FAST) uv[c] = *reinterpret_cast<const UVec*>(urow[c]);
     }
 
-    // Embedding operand (MFMA B: column = request, 8 consecutive k per lane half) from LDS.
-    const uint16_t* rowp = &sB[buf][tl * RS + 8 * h];
-    bf16x8 bop[kMaxSteps];  // every step's operand is read before the chain: the reads overlap
+    // Embedding operand (MFMA B: column = request 16 c + tn, k = 32 s + 8 q .. + 7) from LDS.
+    f32x4 acc[2] = {};
 #pragma unroll
-    for (int kk = 0; kk < kMaxSteps; ++kk)
-      bop[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(rowp + min(kk, nk - 1) * 16));
-    f32x16 acc = {};
+    for (int c = 0; c < 2; ++c) {
+      const uint16_t* rowp = &sB[buf][(16 * c + tn) * RS + 8 * q];
+      bf16x8 bop[NK];
 #pragma unroll
-    for (int kk = 0; kk < kMaxSteps; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kk], kk < nk ? bop[kk] : zero8, acc, 0, 0, 0);
+      for (int s = 0; s < NK; ++s) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u32*>(rowp + 32 * s));
+        bop[s] = 32 * s + 8 * q < r ? v : zero8;
+      }
+#pragma unroll
+      for (int s = 0; s < NK; ++s) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[s], bop[s], acc[c], 0, 0, 0);
+    }
 
-    // Epilogue: lane holds D[token n0 + 8g + 4h + p][request j] in acc[4g + p].
-    const size_t row = ((size_t)(valid ? j : 0) * G + k) * V;
-    float zq[16];
-    int bad = 0;
+    // Epilogue: lane holds D[token n0 + 4 q + p][request 16 c + tn] in acc[c][p].
+    float zm[2];
+    int bad[2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int t0 = n0 + 8 * g + 4 * h;
-      float zs[4];
-      if (fast_tile) {
-        unsigned char* q = urow + 8 * g * ES;
+    for (int c = 0; c < 2; ++c) {
+      const int j = rb * kReqBlock + 16 * c + tn;
+      const bool valid = j < B;
+      const size_t row = ((size_t)(valid ? j : 0) * G + k) * V;
+      const int t0 = n0 + 4 * q;
+      float zq[4];
+      int bd = 0;
+      if constexpr (FAST) {
+        float zs[4];
         if constexpr (ES == 2) {
-          const uint2 w = uv[g];
-          zs[0] = bf16_lo(w.x) + acc[4 * g];
-          zs[1] = bf16_hi(w.x) + acc[4 * g + 1];
-          zs[2] = bf16_lo(w.y) + acc[4 * g + 2];
-          zs[3] = bf16_hi(w.y) + acc[4 * g + 3];
+          const uint2 w = uv[c];
+          zs[0] = bf16_lo(w.x) + acc[c][0];
+          zs[1] = bf16_hi(w.x) + acc[c][1];
+          zs[2] = bf16_lo(w.y) + acc[c][2];
+          zs[3] = bf16_hi(w.y) + acc[c][3];
           uint2 o;
           const f32x2 v0 = {zs[0], zs[1]}, v1 = {zs[2], zs[3]};
           o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2));
           o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2));
-          *reinterpret_cast<uint2*>(q) = o;
+          *reinterpret_cast<uint2*>(urow[c]) = o;
           zs[0] = bf16_lo(o.x); zs[1] = bf16_hi(o.x); zs[2] = bf16_lo(o.y); zs[3] = bf16_hi(o.y);
         } else {
-          const float4 w = uv[g];
-          zs[0] = w.x + acc[4 * g];
-          zs[1] = w.y + acc[4 * g + 1];
-          zs[2] = w.z + acc[4 * g + 2];
-          zs[3] = w.w + acc[4 * g + 3];
-          *reinterpret_cast<float4*>(q) = make_float4(zs[0], zs[1], zs[2], zs[3]);
+          const float4 w = uv[c];
+          zs[0] = w.x + acc[c][0];
+          zs[1] = w.y + acc[c][1];
+          zs[2] = w.z + acc[c][2];
+          zs[3] = w.w + acc[c][3];
+          *reinterpret_cast<float4*>(urow[c]) = make_float4(zs[0], zs[1], zs[2], zs[3]);
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          zq[4 * g + p] = valid ? zs[p] : -__builtin_inff();
-          bad |= valid && __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
+          zq[p] = valid ? zs[p] : -__builtin_inff();
+          bd |= valid && __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
         }
       } else {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const bool in = valid && t0 + p < V;
-          float z = (in ? load_logit<ES>(a.base, row + t0 + p) : 0.f) + acc[4 * g + p];
+          float z = (in ? load_logit<ES>(a.base, row + t0 + p) : 0.f) + acc[c][p];
           if constexpr (ES == 2) {
             const f32x2 v = {z, 0.f};
             const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
@@ -292,35 +309,45 @@ __global__ __launch_bounds__(kDraftThreads) void markov_logits_kernel(DraftArgs 
           } else {
             if (in) reinterpret_cast<float*>(a.logits)[row + t0 + p] = z;
           }
-          zq[4 * g + p] = in ? z : -__builtin_inff();
-          bad |= in && __builtin_amdgcn_classf(z, 0x203);
+          zq[p] = in ? z : -__builtin_inff();
+          bd |= in && __builtin_amdgcn_classf(z, 0x203);
         }
       }
+      float m = fmaxf(fmaxf(zq[0], zq[1]), fmaxf(zq[2], zq[3]));
+      // the four lane groups hold the same request
+      m = fmaxf(m, __shfl_xor(m, 16, SPEC_WAVE));
+      m = fmaxf(m, __shfl_xor(m, 32, SPEC_WAVE));
+      bd |= __shfl_xor(bd, 16, SPEC_WAVE);
+      bd |= __shfl_xor(bd, 32, SPEC_WAVE);
+      zm[c] = m;
+      bad[c] = bd;
     }
-    float zm = zq[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) zm = fmaxf(zm, zq[i]);
-    // the two lane halves hold the same request
-    zm = fmaxf(zm, __shfl_xor(zm, 32, SPEC_WAVE));
-    bad |= __shfl_xor(bad, 32, SPEC_WAVE);
-    if (h == 0) sp[buf][wv][tl] = DPart{zm, bad};
+    if (q == 0) {
+      sp[buf][wv][tn] = DPart{zm[0], bad[0]};
+      sp[buf][wv][16 + tn] = DPart{zm[1], bad[1]};
+    }
     if (more) {
-      store_rows(buf ^ 1);                            // read after the barrier below
-      if (fast_tile) store_tile_lds((rb + 1) % 3);
+      store_rows(buf ^ 1);                            // block rb + 1, read after the barrier below
+      if constexpr (FAST) store_tile_lds((rb + 1) % 3);
     }
-    if (idw) sPrev[buf][tid - 64] = prev_ok(pn2);    // ids of block rb + 2
+    load_rows((rb + 2) & 3);                          // block rb + 2 (past the end: valid ids, unused)
+    if constexpr (FAST) load_tile(rb + 2);
     __syncthreads();
-    if (fast_tile) store_tile_global(rb, ub);
-    if (wv == 3 && h == 0 && valid) {
-      DPart t = sp[buf][0][tl];
+    if constexpr (FAST) store_tile_global(rb, ub);
+    // the block's tile records (rows padded to whole blocks: a row past B is never read)
+    if (wv == NW - 1 && lane < kReqBlock) {
+      DPart t = sp[buf][0][lane];
 #pragma unroll
-      for (int w = 1; w < kDraftThreads / 64; ++w) {
-        t.zmax = fmaxf(t.zmax, sp[buf][w][tl].zmax);
-        t.bad |= sp[buf][w][tl].bad;
+      for (int w = 1; w < NW; ++w) {
+        t.zmax = fmaxf(t.zmax, sp[buf][w][lane].zmax);
+        t.bad |= sp[buf][w][lane].bad;
       }
-      a.part[(size_t)j * a.nwg + blockIdx.x] = t;
+      a.part[(size_t)(rb * kReqBlock + lane) * a.nwg + blockIdx.x] = t;
     }
   }
+  };
+  if (fast_tile) walk(std::true_type{});
+  else walk(std::false_type{});
 }
 
 // Step k: draw x_k for every request (one workgroup each).
@@ -699,8 +726,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int num_tiles(int V) { return (V + kTileTokens - 1) / kTileTokens; }
 
+// Tile records [B rounded up to whole request blocks, tiles], then the request status.
+size_t draft_part_rows(int B) { return ((size_t)B + kReqBlock - 1) / kReqBlock * kReqBlock; }
 size_t draft_ws_bytes(int B, int V) {
-  return align256((size_t)B * num_tiles(V) * sizeof(DPart)) + align256((size_t)B * sizeof(int32_t));
+  return align256(draft_part_rows(B) * num_tiles(V) * sizeof(DPart)) + align256((size_t)B * sizeof(int32_t));
 }
 
 bool draft_shape_ok(int B, int G, int V, int r, int d, int dtype) {
@@ -750,7 +779,7 @@ extern "C" int32_t spec_draft_markov(int32_t B, int32_t gamma, int32_t V, int32_
   a.tokens = tokens; a.logits = draft_logits; a.conf = conf; a.status = status;
   char* ws = reinterpret_cast<char*>(workspace);
   a.part = reinterpret_cast<DPart*>(ws);
-  a.req_status = reinterpret_cast<int32_t*>(ws + align256((size_t)B * a.nwg * sizeof(DPart)));
+  a.req_status = reinterpret_cast<int32_t*>(ws + align256(draft_part_rows(B) * a.nwg * sizeof(DPart)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const unsigned sgrid = (unsigned)B;
   for (int k = 0; k < gamma; ++k) {
