@@ -32,12 +32,84 @@ __device__ __forceinline__ float load_elem(const void* row, int64_t v) {
   }
 }
 
-// ---- wave reductions (wave64) -------------------------------------------
+// ---- wave reductions and scans (wave64) -----------------------------------
+//
+// Lanes exchange values through DPP (the vector ALU's cross-lane operand modes of gfx9: quad
+// permutes, row mirrors, row shifts and row broadcasts within and across rows of 16 lanes) and
+// v_readlane, not through the LDS crossbar (ds_bpermute), which shares the LDS with table reads.
+
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowMirror = 0x140;      // lane i of a row takes lane 15 - i
+constexpr int kRowHalfMirror = 0x141;  // lane i of a half row takes lane 7 - i
+constexpr int kRowShr = 0x110;         // + n: lane i takes lane i - n of its row
+constexpr int kRowBcast15 = 0x142;     // lane 15 of each row, to the next row
+constexpr int kRowBcast31 = 0x143;     // lane 31, to rows 2 and 3
+}  // namespace dpp
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+// x of the lane CTRL selects, for a 4- or 8-byte T; a lane whose source lies outside its row, or
+// which lies outside the rows ROWS selects, keeps `old`.
+template <int CTRL, int ROWS = 0xF, class T>
+__device__ __forceinline__ T dpp_move(T x, T old) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp32<CTRL, ROWS>(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, old)));
+  } else {
+    const uint2 v = __builtin_bit_cast(uint2, x), o = __builtin_bit_cast(uint2, old);
+    uint2 r;
+    r.x = dpp32<CTRL, ROWS>(v.x, o.x);
+    r.y = dpp32<CTRL, ROWS>(v.y, o.y);
+    return __builtin_bit_cast(T, r);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ T read_lane(T x, int l) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  } else {
+    const int2 v = __builtin_bit_cast(int2, x);
+    int2 r;
+    r.x = __builtin_amdgcn_readlane(v.x, l);
+    r.y = __builtin_amdgcn_readlane(v.y, l);
+    return __builtin_bit_cast(T, r);
+  }
+}
+
+// Reduction over the wave (all lanes active); every lane gets the same result.  Within a row the
+// lanes are paired by quad permutes and mirrors, both lanes of a pair combining the same two values;
+// the rows' values (lanes 0, 16, 32, 48) are then combined as (r0 op r1) op (r2 op r3).
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  x = op(x, dpp_move<dpp::kQuadXor1>(x, x));
+  x = op(x, dpp_move<dpp::kQuadXor2>(x, x));
+  x = op(x, dpp_move<dpp::kRowHalfMirror>(x, x));
+  x = op(x, dpp_move<dpp::kRowMirror>(x, x));
+  return op(op(read_lane(x, 0), read_lane(x, 16)), op(read_lane(x, 32), read_lane(x, 48)));
+}
+
+// Inclusive prefix sum in lane order (all lanes active): shifts by 1, 2, 4, 8 within each row, then
+// the row totals carried by the row broadcasts.
+template <class T>
+__device__ __forceinline__ T wave_inclusive_scan(T x) {
+  const T z = T(0);
+  x += dpp_move<dpp::kRowShr + 1>(x, z);
+  x += dpp_move<dpp::kRowShr + 2>(x, z);
+  x += dpp_move<dpp::kRowShr + 4>(x, z);
+  x += dpp_move<dpp::kRowShr + 8>(x, z);
+  x += dpp_move<dpp::kRowBcast15, 0xA>(x, z);
+  x += dpp_move<dpp::kRowBcast31, 0xC>(x, z);
+  return x;
+}
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, SPEC_WAVE));
-  return x;
+  return wave_reduce(x, [](float p, float q) { return fmaxf(p, q); });
 }
 
 // Workgroup barrier for LDS data: the LDS writes issued before it are complete and seen by every
@@ -45,52 +117,28 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, SPEC_WAVE);
-  return x;
+  return wave_reduce(x, [](double p, double q) { return p + q; });
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, SPEC_WAVE);
-  return x;
+  return wave_reduce(x, [](int p, int q) { return p + q; });
 }
 
 __device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, SPEC_WAVE));
-  return x;
+  return wave_reduce(x, [](int p, int q) { return max(p, q); });
 }
 
 __device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, SPEC_WAVE));
-  return x;
+  return wave_reduce(x, [](int p, int q) { return min(p, q); });
 }
 
 __device__ __forceinline__ int wave_or_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x |= __shfl_xor(x, o, SPEC_WAVE);
-  return x;
+  return wave_reduce(x, [](int p, int q) { return p | q; });
 }
 
 // Inclusive prefix sum of a double across the wave (lane order).
-__device__ __forceinline__ double wave_inclusive_sum(double x, int lane) {
-#pragma unroll
-  for (int o = 1; o < SPEC_WAVE; o <<= 1) {
-    double y = __shfl_up(x, o, SPEC_WAVE);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
+__device__ __forceinline__ double wave_inclusive_sum(double x, int) { return wave_inclusive_scan(x); }
 
-__device__ __forceinline__ long long wave_inclusive_sum_i64(long long x, int lane) {
-#pragma unroll
-  for (int o = 1; o < SPEC_WAVE; o <<= 1) {
-    long long y = __shfl_up(x, o, SPEC_WAVE);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
+__device__ __forceinline__ long long wave_inclusive_sum_i64(long long x, int) { return wave_inclusive_scan(x); }
 
 }  // namespace spec

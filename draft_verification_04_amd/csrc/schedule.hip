@@ -240,9 +240,21 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
 #pragma unroll
   for (int e = 0; e < K; ++e) sps_m[e] = (!topk && p0 + e + 1 <= m_cap) ? a.sps[B + p0 + e + 1] : 0.0;
   if (tid == 0) sh.ncand = 0;
-  for (int x = tid; x < N; x += kFinalThreads) {
-    sh.sorted[x] = a.sorted[x];
-    sh.orig[x] = a.orig[x];
+  // N <= K * kFinalThreads: every thread's loads are issued before the first is stored
+  unsigned ks[K], ko[K];
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    const int x = min(tid + e * kFinalThreads, N - 1);
+    ks[e] = a.sorted[x];
+    ko[e] = a.orig[x];
+  }
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    const int x = tid + e * kFinalThreads;
+    if (x < N) {
+      sh.sorted[x] = ks[e];
+      sh.orig[x] = ko[e];
+    }
   }
   __syncthreads();
 

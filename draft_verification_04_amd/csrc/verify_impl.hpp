@@ -278,15 +278,22 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
   }
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // positions k0 .. k0 + 7 (at most G): x[u] is the draft token of position k0 + u
+  // positions k0 .. k0 + 7 (at most G): x[u] is the draft token of position k0 + u; the
+  // positions' offsets are read before the first ballot (independent reads, one wait)
   auto put8 = [&](int k0, const int (&x)[8]) {
+    int base[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = min(k0 + u, G);
+      base[u] = sh.off[k] + sh.cnt[wave][k];
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u;
       if (k > G) break;
       const unsigned long long m = __ballot(last >= k);
       if (last >= k) {
-        const int idx = sh.off[k] + sh.cnt[wave][k] + __popcll(m & below);
+        const int idx = base[u] + __popcll(m & below);
         a.items[idx] = (tid << 7) | k;
         a.items_x[idx] = (k < L) ? x[u] : -1;
       }
