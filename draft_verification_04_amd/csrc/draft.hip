@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
       const bool q1 = t0 + 1 < V && load_logit<ES>(row, t0 + 1) == zm;
       const unsigned long long hb = __ballot(q0 || q1);
       const int Lb = hb ? __ffsll((long long)hb) - 1 : 0;
-      x = __shfl(q0 ? t0 : t0 + 1, Lb, SPEC_WAVE);
+      x = read_lane(q0 ? t0 : t0 + 1, Lb);
     }
   } else if (st == 0) {  // uniform over the workgroup
     const double invT = 1.0 / (double)T;
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
         run += v4[u];
         pre[u] = run;
       }
-      const double W = __shfl(incl, 63, SPEC_WAVE);
+      const double W = read_lane(incl, 63);
       const uint64_t seed = a.seed ? a.seed[j] : 0ull;
       const Philox4x64 blk = philox4x64_10((uint64_t)k + 1, (uint64_t)j, 1, 0, seed, 0);
       const double target = uniform53(blk.w0) * W;
@@ -567,11 +567,11 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
       double before = 0.0;
       if (m) {
         const int fl = (int)__ffsll((long long)m) - 1;
-        sel = fl * 4 + __shfl(f, fl, SPEC_WAVE);
+        sel = fl * 4 + read_lane(f, fl);
         if (sel > 0) {
           const int ub = (sel - 1) & 3;
           const double mine = ub == 0 ? pre[0] : ub == 1 ? pre[1] : ub == 2 ? pre[2] : pre[3];
-          before = __shfl(mine, (sel - 1) >> 2, SPEC_WAVE);
+          before = read_lane(mine, (sel - 1) >> 2);
         }
       }
       if (lane == 0) {

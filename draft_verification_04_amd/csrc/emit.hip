@@ -541,7 +541,7 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
         run += v[u];
         pre[u] = run;
       }
-      const double W = __shfl(incl, 63, SPEC_WAVE);
+      const double W = read_lane(incl, 63);
       if (attempt == 0 && !use_t && !(W > 0.0)) {
         use_t = 1;   // no residual mass (rounding): fall back to p_t of the same row
         continue;
@@ -556,11 +556,11 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
       double before = 0.0;
       if (m) {
         const int fl = (int)__ffsll((long long)m) - 1;
-        sel = fl * 4 + __shfl(f, fl, SPEC_WAVE);
+        sel = fl * 4 + read_lane(f, fl);
         if (sel > 0) {
           const int ub = (sel - 1) & 3;
           const double mine = ub == 0 ? pre[0] : ub == 1 ? pre[1] : ub == 2 ? pre[2] : pre[3];
-          before = __shfl(mine, (sel - 1) >> 2, SPEC_WAVE);
+          before = read_lane(mine, (sel - 1) >> 2);
         }
       }
       if (lane == 0) {

@@ -195,6 +195,7 @@ struct FinalShared {
   long long wsum[kFinalWaves];
   double wth[kFinalWaves];
   int wm[kFinalWaves];
+  int wbm[kFinalWaves];
   int ncand, mstar, first, last;
 };
 
@@ -316,24 +317,27 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
       tp = tm;
     }
   }
-  // block reductions
-  const int wb = wave_min_i(brk);
-  double wbest = best;
-  int wbm = best_m;
+  // block reductions: the early stop needs the first break, the global search the first maximum
+  // (arrays of their own, so no barrier separates them from the scan's)
+  if (a.mode == SPEC_SCHED_EARLY_STOP) {
+    const int wb = wave_min_i(brk);
+    if (lane == 0) sh.wm[wave] = wb;
+  } else {
+    double wbest = best;
+    int wbm = best_m;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double ob = __shfl_xor(wbest, o, SPEC_WAVE);
-    const int om = __shfl_xor(wbm, o, SPEC_WAVE);
-    if (ob > wbest || (ob == wbest && om < wbm)) {
-      wbest = ob;
-      wbm = om;
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(wbest, o, SPEC_WAVE);
+      const int om = __shfl_xor(wbm, o, SPEC_WAVE);
+      if (ob > wbest || (ob == wbest && om < wbm)) {
+        wbest = ob;
+        wbm = om;
+      }
     }
-  }
-  __syncthreads();
-  if (lane == 0) {
-    sh.wm[wave] = wb;
-    sh.wth[wave] = wbest;
-    sh.wsum[wave] = wbm;
+    if (lane == 0) {
+      sh.wth[wave] = wbest;
+      sh.wbm[wave] = wbm;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
       int bm = 0;
       for (int w = 0; w < kFinalWaves; ++w) {
         const double t = sh.wth[w];
-        const int m = (int)sh.wsum[w];
+        const int m = sh.wbm[w];
         if (t > bt || (t == bt && m < bm)) {
           bt = t;
           bm = m;

@@ -583,7 +583,7 @@ __device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, floa
       const float z = cand[s];
       if (z >= theta) q += (long long)rint((double)__builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -M))) * 0x1p48);
     }
-    q = __shfl(wave_inclusive_sum_i64(q, lane), 63, SPEC_WAVE);
+    q = read_lane(wave_inclusive_sum_i64(q, lane), 63);
     if (lane == 0) sh.sum_q[wave] = q;
     __syncthreads();
     if (lt == 0) {

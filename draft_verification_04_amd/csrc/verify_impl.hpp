@@ -268,7 +268,7 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
     const long long c = (lane <= G) ? sh.ctot[lane] : 0;
     const long long incl = wave_inclusive_sum_i64(c, lane);
     if (lane <= G) sh.off[lane] = (int)(incl - c);
-    const int total64 = (int)__shfl(incl, 63, SPEC_WAVE);
+    const int total64 = (int)read_lane(incl, 63);
     if (lane == 0) {
       if (G == SPEC_WAVE) sh.off[SPEC_WAVE] = total64;   // position 64 (gamma = 64)
       const int nit = (G == SPEC_WAVE) ? total64 + sh.ctot[SPEC_WAVE] : total64;
