@@ -432,6 +432,16 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
     const int v0 = min(rr * kDrawRange + sub * 512 + lane * 8, V - 8);
     return *reinterpret_cast<const uint4*>(row + (size_t)v0 * 2);
   };
+  // A sampled row (T > 0) is read from the start: the first two ranges of each wave are in flight
+  // while the tile records are reduced and the table is built (a request found bad meanwhile leaves
+  // them unused).
+  uint4 buf[8];
+  if (vec && T > 0.f) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) buf[4 * h + sub] = load(wv + h * kDrawWaves, sub);
+  }
   // the row's largest stored value and bad flag
   float zm = (tid < nwg) ? p0.zmax : -__builtin_inff();
   int bad = (tid < nwg) ? p0.bad : 0;
@@ -486,14 +496,6 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
     const double invT = 1.0 / (double)T;
     const double R = (double)zm * invT;      // the largest weight is exp(0) = 1
     const double* Qt = (ES == 2) ? sh.Qt : nullptr;
-    // the first two ranges of each wave, in flight while the table is built
-    uint4 buf[8];
-    if (vec) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) buf[4 * h + sub] = load(wv + h * kDrawWaves, sub);
-    }
     if (ES == 2) build_qtab(sh.Qt, invT, R, sh.T64);
     lds_barrier();   // the table; the row loads stay in flight
     if (vec) {
