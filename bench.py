@@ -62,8 +62,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this path runs on one GPU: every GPU box here has one, and the "
-                                   "verification kernels need no collective; run with --gpus 1"}))
+        print(json.dumps({"error": "the benchmark measures one GPU (the verification kernels need no "
+                                   "collective; a batch shards by request); run with --gpus 1"}))
         sys.exit(2)
 
     import torch
