@@ -8,7 +8,7 @@ extern "C" const char* spec_status_string(int32_t status) {
     case SPEC_OK: return "ok";
     case SPEC_ERR_INVALID_ARG: return "invalid argument";
     case SPEC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
-    case SPEC_ERR_UNSUPPORTED: return "unsupported by this build";
+    case SPEC_ERR_UNSUPPORTED: return "unsupported by this library";
     case SPEC_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
   }

@@ -64,7 +64,7 @@ enum {
     SPEC_OK = 0,
     SPEC_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misalignment, bad enum */
     SPEC_ERR_WORKSPACE = 2,   /* workspace missing or smaller than the size query returned */
-    SPEC_ERR_UNSUPPORTED = 3, /* a valid request this build does not support (e.g. V too large) */
+    SPEC_ERR_UNSUPPORTED = 3, /* a valid request this library does not support (e.g. V too large) */
     SPEC_ERR_HIP = 4          /* a HIP launch reported an error */
 };
 
@@ -88,7 +88,7 @@ enum {
 #define SPEC_REQ_BAD_CONFIDENCE 32  /* scheduler: a confidence outside [0, 1] or NaN */
 #define SPEC_REQ_OVER_BUDGET 64     /* spec_verify_bounded: the request's rows did not fit the token cap */
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define SPEC_MAX_GAMMA 64
 #define SPEC_MAX_V 524288           /* bf16; fp32 rows are limited to SPEC_MAX_V / 2 */
 #define SPEC_MAX_SCHED_CANDIDATES 16384 /* B * gamma for spec_schedule_lengths */

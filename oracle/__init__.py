@@ -1,8 +1,8 @@
 """CPU oracle for lossless draft verification and confidence-scheduled lengths.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
-execute anything in this package: only the tests, the smoke check of the
-graft entry point and the CPU-baseline leg of the benchmark use it.  The HIP
+execute anything in this package: only the tests, the smoke check in
+`__graft_entry__.smoke()` and the CPU-baseline leg of the benchmark use it.  The HIP
 library never routes through it and shares no code with it.
 
 It is a plain, slow, fp64 restatement of what the method computes, written
