@@ -16,17 +16,16 @@
 // Candidates are ordered by the 32-bit key ~bits(a) (ascending key = descending
 // survival), ties by index r * gamma + j (request, then position).  One CU retires
 // only 64 lane operations per cycle, so the sort is spread over the chip:
-//   keys_kernel   one wave per chunk of 64 candidates: survivals, keys in index
-//                 order, and the chunk sorted by (key, index) in registers;
+//   keys_kernel   one wave per chunk of 64 candidates: survivals, and the chunk
+//                 sorted by (key, index) in registers, each key stored with its index;
 //   rank_kernel   one workgroup per chunk: each key's place in the whole pool is
 //                 its place in its chunk plus, for every other chunk, the number of
-//                 keys there that precede it (binary search in LDS), and it is
-//                 written straight to that place;
+//                 keys there that precede it (binary search in LDS), and the key and
+//                 its index are written straight to that place;
 //   final_kernel  one workgroup: exclusive int64 scan of the fixed-point
 //                 survivals, Theta(m), first non-rise (early stop) or first maximum
-//                 (global), and per-request counts from the key at m* (keys below it
-//                 are admitted, and of the keys equal to it the first ones in index
-//                 order, as many as the admission count leaves).  In the combined
+//                 (global), and per-request counts of the first m* entries of the
+//                 sorted pool, by their indices (LDS atomics).  In the combined
 //                 schedule-and-verify call (B <= 1024) it also writes the verify work
 //                 list from the lengths it holds, in place of the work-list kernel.
 #include "common.hpp"
@@ -52,9 +51,10 @@ struct SchedArgs {
   int32_t* lengths;
   double* theta;
   int32_t* status;
-  unsigned* orig;     // [N] keys in index order
-  unsigned* chunked;  // [N] keys, each chunk of 64 sorted
-  unsigned* sorted;   // [N] keys, whole pool sorted
+  unsigned* chunked;      // [N] keys, each chunk of 64 sorted
+  unsigned* chunked_idx;  // [N] the candidate index r * gamma + j of each key of `chunked`
+  unsigned* sorted;       // [N] keys, whole pool sorted
+  unsigned* sorted_idx;   // [N] the candidate index of each key of `sorted`
   const int32_t* capacity_in;  // top-K mode: [1] device, the number of candidates to admit
   int32_t* capacity_out;       // [1] device or NULL: the number admitted (m*)
 };
@@ -99,7 +99,6 @@ __global__ __launch_bounds__(kKeysThreads) void keys_kernel(SchedArgs a) {
     }
     key = bad ? kNoCandidate : surv_key(s);
     if (j == 0 && a.status) a.status[r] = bad ? SPEC_REQ_BAD_CONFIDENCE : 0;
-    a.orig[p] = key;
   }
   // bitonic sort of the wave's 64 (key, index) pairs, one per lane; padding sorts last
   unsigned long long x = ((unsigned long long)key << 32) | (unsigned)(p < N ? p : 0x7fffffff);
@@ -111,7 +110,10 @@ __global__ __launch_bounds__(kKeysThreads) void keys_kernel(SchedArgs a) {
       x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
     }
   }
-  if (p < N) a.chunked[p] = (unsigned)(x >> 32);
+  if (p < N) {
+    a.chunked[p] = (unsigned)(x >> 32);
+    a.chunked_idx[p] = (unsigned)x;
+  }
 }
 
 // ---- ranks -----------------------------------------------------------------
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(kChunk * kRankParts) void rank_kernel(SchedArgs a) 
   const int p = ck * kChunk + lane;
   const bool valid = p < N;
   const unsigned k = valid ? keys[p] : 0u;
+  const unsigned idx = a.chunked_idx[min(p, N - 1)];
   int cnt = 0;
   // this wave's share of the other chunks, eight searches in flight; chunks past the end are
   // replaced by the own chunk, which counts nothing
@@ -183,6 +186,7 @@ __global__ __launch_bounds__(kChunk * kRankParts) void rank_kernel(SchedArgs a) 
 #pragma unroll
     for (int w = 0; w < kRankParts; ++w) rank += part[w][lane];
     a.sorted[rank] = k;
+    a.sorted_idx[rank] = idx;
   }
 }
 
@@ -190,13 +194,13 @@ __global__ __launch_bounds__(kChunk * kRankParts) void rank_kernel(SchedArgs a) 
 
 template <int K>
 struct FinalShared {
-  unsigned sorted[K * kFinalThreads];
-  unsigned orig[K * kFinalThreads];
+  unsigned sorted[K * kFinalThreads];   // keys; after the search, the per-request counts
+  unsigned sidx[K * kFinalThreads];     // candidate index of each sorted key
   long long wsum[kFinalWaves];
   double wth[kFinalWaves];
   int wm[kFinalWaves];
   int wbm[kFinalWaves];
-  int ncand, mstar, first, last;
+  int ncand, mstar;
 };
 
 // Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
@@ -247,14 +251,14 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
   for (int e = 0; e < K; ++e) {
     const int x = min(tid + e * kFinalThreads, N - 1);
     ks[e] = a.sorted[x];
-    ko[e] = a.orig[x];
+    ko[e] = a.sorted_idx[x];
   }
 #pragma unroll
   for (int e = 0; e < K; ++e) {
     const int x = tid + e * kFinalThreads;
     if (x < N) {
       sh.sorted[x] = ks[e];
-      sh.orig[x] = ko[e];
+      sh.sidx[x] = ko[e];
     }
   }
   __syncthreads();
@@ -276,7 +280,6 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     if (tid == 0) {
       const int cap = *a.capacity_in;
       sh.mstar = cap < 0 ? 0 : (cap > E ? E : cap);
-      sh.first = sh.last = 0;
     }
 #pragma unroll
     for (int e = 0; e < K; ++e) q[e] = 0;
@@ -360,7 +363,6 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
       mstar = bm;
     }
     sh.mstar = mstar;
-    sh.first = sh.last = 0;
     if (mstar == 0 && a.theta) a.theta[0] = th0;
   }
   }  // search for m*
@@ -368,16 +370,8 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
   const int mstar = sh.mstar;
   if (tid == 0 && a.capacity_out) a.capacity_out[0] = mstar;
   if (!a.lengths) return;
-  if (mstar == 0) {
-    for (int r = tid; r < B; r += kFinalThreads) a.lengths[r] = 0;
-    if constexpr (WL) {
-      if constexpr (!kEarlyTokens) worklist_prefetch(v, xp);
-      worklist_from_lengths(wsh, v, 0, xp);
-    }
-    return;
-  }
   // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
-  if (!topk && mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
+  if (!topk && mstar > 0 && mstar - 1 >= p0 && mstar - 1 < p0 + K && a.theta) {
     long long t = tau_p0;
     double sp = 0.0;
 #pragma unroll
@@ -387,41 +381,22 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     }
     a.theta[0] = theta_of(t, sp);
   }
-  // the admitted candidates are the keys below thr plus the first (m* - first) keys equal to
-  // thr in index order, where [first, last] is thr's run in the sorted pool
-  const unsigned thr = sh.sorted[mstar - 1];
+  // The admitted candidates are the first m* of the pool sorted by (key, index): each request's
+  // length is its count among them, kept in LDS over the keys' storage (not read after the search).
+  unsigned* cnt = sh.sorted;
+  for (int r = tid; r < B; r += kFinalThreads) cnt[r] = 0;
+  __syncthreads();
 #pragma unroll
   for (int e = 0; e < K; ++e) {
     const int p = p0 + e;
-    if (p < N && key[e] == thr) {
-      if (p == 0 || sh.sorted[p - 1] != thr) sh.first = p;
-      if (p == N - 1 || sh.sorted[p + 1] != thr) sh.last = p;
-    }
+    if (p < mstar) atomicAdd(&cnt[sh.sidx[p] / (unsigned)G], 1u);
   }
   __syncthreads();
-  const int ties_admitted = mstar - sh.first;
-  const bool split = ties_admitted < sh.last - sh.first + 1;  // uniform
-  long long carry = 0;
   int my_len = 0;   // request tid's length (B <= kFinalThreads)
-  for (int r0 = 0; r0 < B; r0 += kFinalThreads) {
-    const int r = r0 + tid;
-    int lt = 0, eq = 0;
-    if (r < B) {
-      for (int j = 0; j < G; ++j) {
-        const unsigned k = sh.orig[(size_t)r * G + j];
-        lt += k < thr;
-        eq += k == thr;
-      }
-    }
-    int len = lt + eq;
-    if (split) {
-      long long chunk;
-      const long long ex = carry + block_exclusive_sum(eq, sh.wsum, &chunk);
-      carry += chunk;
-      len = lt + (int)max(0ll, min((long long)eq, (long long)ties_admitted - ex));
-    }
-    if (r < B) a.lengths[r] = len;
-    if (r0 == 0) my_len = len;
+  for (int r = tid; r < B; r += kFinalThreads) {
+    const int len = (int)cnt[r];
+    a.lengths[r] = len;
+    if (r == tid) my_len = len;
   }
   if constexpr (WL) {
     if constexpr (!kEarlyTokens) worklist_prefetch(v, xp);
@@ -448,7 +423,7 @@ using namespace spec;
 extern "C" size_t spec_schedule_workspace_size(int32_t B, int32_t gamma) {
   if (B < 1 || gamma < 1) return 0;
   const size_t n = (size_t)B * (size_t)gamma;
-  return 3 * align256(n * sizeof(unsigned));
+  return 4 * align256(n * sizeof(unsigned));
 }
 
 // v: the bound arguments of a verify call whose work list the final kernel writes, or NULL.
@@ -461,9 +436,10 @@ static int32_t launch_schedule(SchedArgs a, void* workspace, size_t workspace_by
   const int n = B * gamma;
   char* ws = static_cast<char*>(workspace);
   const size_t seg = align256((size_t)n * sizeof(unsigned));
-  a.orig = reinterpret_cast<unsigned*>(ws);
-  a.chunked = reinterpret_cast<unsigned*>(ws + seg);
+  a.chunked = reinterpret_cast<unsigned*>(ws);
+  a.chunked_idx = reinterpret_cast<unsigned*>(ws + seg);
   a.sorted = reinterpret_cast<unsigned*>(ws + 2 * seg);
+  a.sorted_idx = reinterpret_cast<unsigned*>(ws + 3 * seg);
   hipLaunchKernelGGL(keys_kernel, dim3((n + kKeysThreads - 1) / kKeysThreads), dim3(kKeysThreads), 0, s, a);
   hipLaunchKernelGGL(rank_kernel, dim3((n + kChunk - 1) / kChunk), dim3(kChunk * kRankParts), 0, s, a);
   if (v) launch_final<true>(a, *v, n, s);
@@ -492,7 +468,7 @@ extern "C" int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* 
   if (mode != SPEC_SCHED_EARLY_STOP && mode != SPEC_SCHED_GLOBAL) return SPEC_ERR_INVALID_ARG;
   if (!lengths_out) return SPEC_ERR_INVALID_ARG;
   SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, status,
-              nullptr, nullptr, nullptr, nullptr, nullptr};
+              nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -504,7 +480,7 @@ extern "C" int32_t spec_schedule_capacity(int32_t B, int32_t gamma, const float*
   if (rc != SPEC_OK) return rc;
   if (!capacity_out) return SPEC_ERR_INVALID_ARG;
   SchedArgs a{B, gamma, budget_tokens, SPEC_SCHED_GLOBAL, conf, sps, nullptr, theta_out, status,
-              nullptr, nullptr, nullptr, nullptr, capacity_out};
+              nullptr, nullptr, nullptr, nullptr, nullptr, capacity_out};
   return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -515,7 +491,7 @@ extern "C" int32_t spec_schedule_topk(int32_t B, int32_t gamma, const float* con
   if ((long long)B * gamma > SPEC_MAX_SCHED_CANDIDATES) return SPEC_ERR_UNSUPPORTED;
   if (!conf || !capacity || !lengths_out) return SPEC_ERR_INVALID_ARG;
   SchedArgs a{B, gamma, 0, kSchedTopK, conf, nullptr, lengths_out, nullptr, status,
-              nullptr, nullptr, nullptr, capacity, nullptr};
+              nullptr, nullptr, nullptr, nullptr, capacity, nullptr};
   return launch_schedule(a, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -546,7 +522,7 @@ extern "C" int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int
   rc = bind_workspace(v, dtype, verify_workspace, verify_workspace_bytes, 0, nullptr);
   if (rc != SPEC_OK) return rc;
   SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, sched_status,
-              nullptr, nullptr, nullptr, nullptr, nullptr};
+              nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool fuse = B <= kFinalThreads;
   rc = launch_schedule(a, sched_workspace, sched_workspace_bytes, s, fuse ? &v : nullptr);

@@ -248,9 +248,10 @@ int32_t spec_verify_greedy(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
  *   status        [B] int32 device or NULL: SPEC_REQ_BAD_CONFIDENCE when a
  *                 confidence of that request is outside [0, 1] or NaN; such a
  *                 request contributes no candidate (its length is 0)
- *   workspace     at least spec_schedule_workspace_size(B, gamma) bytes (12 per
+ *   workspace     at least spec_schedule_workspace_size(B, gamma) bytes (16 per
  *                 candidate, rounded up), 256-byte aligned, owned by the caller; it
- *                 carries the sort keys between the call's kernels and must not be
+ *                 carries the sort keys and their candidate indices between the
+ *                 call's kernels and must not be
  *                 touched by other work until they finish on `stream`
  * Errors (nothing is launched): SPEC_ERR_INVALID_ARG for the conditions above,
  *   SPEC_ERR_UNSUPPORTED beyond SPEC_MAX_SCHED_CANDIDATES, SPEC_ERR_WORKSPACE for a
