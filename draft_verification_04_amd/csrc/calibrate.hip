@@ -20,13 +20,14 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "common.hpp"
 #include "spec_verify.h"
 
 namespace spec {
 namespace {
 
 constexpr int kStsThreads = 256;   // grid temperatures per workgroup of sts_bins_kernel
-constexpr int kStsChunk = 1024;    // instances per workgroup of sts_bins_kernel
+constexpr int kStsChunk = 512;     // instances per workgroup of sts_bins_kernel (4 per CU at 15 bins)
 constexpr int kStsMaxBins = 32;
 constexpr int kStsMaxTaus = 4096;
 
@@ -84,28 +85,23 @@ __global__ __launch_bounds__(kStsThreads) void sts_bins_kernel(StsArgs a) {
   }
 }
 
-// One workgroup per grid temperature: per bin, the chunk partials in a fixed tree order.
+// One workgroup per grid temperature: per bin, the chunk partials summed in a fixed order (each
+// thread its strided share, then the wave by a DPP reduction, then the four waves in order).
 __global__ __launch_bounds__(256) void sts_ece_kernel(StsArgs a) {
-  __shared__ double red[256];
-  __shared__ double bin_sum[kStsMaxBins];
-  const int g = blockIdx.x, tid = threadIdx.x;
+  __shared__ double wpart[kStsMaxBins][4];
+  const int g = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int M = a.bins;
   for (int b = 0; b < M; ++b) {
     const double* p = a.part + ((size_t)g * M + b) * a.nchunk;
     double s = 0.0;
     for (int c = tid; c < a.nchunk; c += 256) s += p[c];
-    red[tid] = s;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) red[tid] += red[tid + o];
-      __syncthreads();
-    }
-    if (tid == 0) bin_sum[b] = red[0];
-    __syncthreads();
+    s = wave_sum(s);
+    if (lane == 0) wpart[b][wave] = s;
   }
+  __syncthreads();
   if (tid == 0) {
     double e = 0.0;
-    for (int b = 0; b < M; ++b) e += fabs(bin_sum[b]);
+    for (int b = 0; b < M; ++b) e += fabs((wpart[b][0] + wpart[b][1]) + (wpart[b][2] + wpart[b][3]));
     e /= (double)a.N;
     a.ece[g] = e;
     if (a.ece_out) a.ece_out[(size_t)a.k * a.ntau + g] = e;

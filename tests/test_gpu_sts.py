@@ -54,7 +54,7 @@ def _compare_fit(got, ref, G):
 @pytest.mark.parametrize("N,G,ntau,bins,seed", [
     (5000, 5, 64, 15, 1),
     (3077, 3, 300, 7, 2),      # a partial chunk; two workgroup rows of grid values, one partial
-    (1024, 4, 256, 32, 3),     # exactly one chunk; the largest bin count
+    (1024, 4, 256, 32, 3),     # two whole chunks; the largest bin count
     (1, 2, 5, 15, 4),          # a single instance
 ])
 def test_fit_matches_oracle(sv, N, G, ntau, bins, seed):
