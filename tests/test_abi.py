@@ -283,3 +283,22 @@ def test_schedule_verify_rejects_bad_arguments(lib):
     assert call(B=2048, G=16, sps_len=10 ** 6) == 3
     assert call() == 2                                         # workspaces
     assert call(vwb=vws - 1) == 2
+
+
+def test_binding_refuses_host_tensors(lib):
+    # the binding marshals device tensors only: host tensors are refused before any call
+    import pytest
+    import torch
+    import draft_verification_04_amd as sv
+    B, G, V = 2, 3, 16
+    t = torch.zeros((B, G + 1, V))
+    d = torch.zeros((B, G, V))
+    x = torch.zeros((B, G), dtype=torch.int32)
+    conf = torch.zeros((B, G))
+    sps = torch.zeros(B * (G + 1) + 1, dtype=torch.float64)
+    with pytest.raises(TypeError):
+        sv.verify(t, d, x)
+    with pytest.raises(TypeError):
+        sv.schedule_verify(t, d, x, conf, sps, 4)
+    with pytest.raises(TypeError):
+        sv.schedule_lengths(conf, sps, 4)
