@@ -620,7 +620,8 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
       if (lane == 63) sh.wsum[wv] = incl;
       __syncthreads();
       double wb = 0.0;
-      for (int q = 0; q < wv; ++q) wb += sh.wsum[q];
+#pragma unroll
+      for (int q = 0; q < kDrawWaves; ++q) wb += (q < wv) ? sh.wsum[q] : 0.0;   // reads issued together
       const double Pb = sh.before + wb;
       const double excl = incl - xs;
       const unsigned long long m = __ballot(Pb + incl > target);
@@ -630,18 +631,23 @@ __global__ __launch_bounds__(kDrawThreads) void markov_sample_kernel(DraftArgs a
         sh.lastl[wv] = pos ? 63 - __clzll((long long)pos) : -1;
       }
       __syncthreads();
-      int cw = -1, cl = -1;
-      for (int q = 0; q < kDrawWaves && cw < 0; ++q)
-        if (sh.cross[q] < 64) {
+      // the first wave with a crossing, else the last wave with weight (all records read at once)
+      int cw = -1, cl = -1, lw = -1, ll = -1;
+#pragma unroll
+      for (int q = kDrawWaves - 1; q >= 0; --q) {
+        const int c = sh.cross[q], l = sh.lastl[q];
+        if (c < 64) {
           cw = q;
-          cl = sh.cross[q];
+          cl = c;
         }
+        if (lw < 0 && l >= 0) {
+          lw = q;
+          ll = l;
+        }
+      }
       if (cw < 0) {  // rounding left no crossing: the last thread with weight
-        for (int q = kDrawWaves - 1; q >= 0 && cw < 0; --q)
-          if (sh.lastl[q] >= 0) {
-            cw = q;
-            cl = sh.lastl[q];
-          }
+        cw = lw;
+        cl = ll;
       }
       if (wv == cw && lane == cl) {
         double acc = Pb + excl;

@@ -609,8 +609,9 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
     const double incl = wave_inclusive_sum(x, lane);
     if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
-    double wb = 0.0;
-    for (int q = 0; q < wave; ++q) wb += sh.wsum[q];
+    double wb = 0.0;   // the earlier waves' totals, in wave order (reads issued together)
+#pragma unroll
+    for (int q = 0; q < NW; ++q) wb += (q < wave) ? sh.wsum[q] : 0.0;
     const double P = sh.before + wb, target = sh.target;
     const double excl = incl - x;
     // first thread whose running total passes the target; the last thread with weight
@@ -621,18 +622,23 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
       sh.last_lane[wave] = pos ? 63 - __clzll((long long)pos) : -1;
     }
     __syncthreads();
-    int cw = -1, cl = -1;
-    for (int q = 0; q < NW && cw < 0; ++q)
-      if (sh.cross_lane[q] < 64) {
+    // the first wave with a crossing, else the last wave with weight (all records read at once)
+    int cw = -1, cl = -1, lw = -1, ll = -1;
+#pragma unroll
+    for (int q = NW - 1; q >= 0; --q) {
+      const int c = sh.cross_lane[q], l = sh.last_lane[q];
+      if (c < 64) {
         cw = q;
-        cl = sh.cross_lane[q];
+        cl = c;
       }
+      if (lw < 0 && l >= 0) {
+        lw = q;
+        ll = l;
+      }
+    }
     if (cw < 0) {  // rounding left no crossing: the last thread with weight
-      for (int q = NW - 1; q >= 0 && cw < 0; --q)
-        if (sh.last_lane[q] >= 0) {
-          cw = q;
-          cl = sh.last_lane[q];
-        }
+      cw = lw;
+      cl = ll;
     }
     if (wave == cw && lane == cl) {
       double acc = P + excl;
