@@ -51,7 +51,9 @@ def parse():
     p.add_argument("--no-sts", action="store_true", help="skip the temperature-scaling measurement")
     p.add_argument("--two-calls", action="store_true",
                    help="scheduler and verification as two calls instead of spec_schedule_verify")
-    p.add_argument("--pool", type=int, default=8, help="worker processes for the pooled CPU-oracle timing")
+    p.add_argument("--pool", type=int, default=0,
+                   help="worker processes for the pooled CPU-oracle timing (0: the host cores this process "
+                        "may use, at most 16, the CPU share of a one-GPU box)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "stream_kernel_traffic.json"))
@@ -145,6 +147,9 @@ def main():
     rows = int((L + 1).sum()) if greedy else int((2 * L + 1).sum())
     alg_bytes = rows * V * es
     achieved = alg_bytes / (ms_stream * 1e-3) / 1e9
+    # the whole step (scheduler, streaming, acceptance, emit and every kernel boundary) against the
+    # same algorithmic bytes: the fused verify path's rate
+    path_gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     value = positions / (ms_step * 1e-3)
 
     ceiling = read_ceiling(sv, torch, copies, alg_bytes, stream)
@@ -192,13 +197,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: B={B} gamma={G} V={V} {w.dtype} logits, "
+        "config": {"workload": f"{args.config}: B={B} gamma={G} V={V} {w.dtype} logits ({recipe(args.config)}), "
                                f"schedule (budget {w.budget} tokens, early stop) + verify of the selected "
                                f"prefixes",
                    "B": B, "gamma": G, "V": V, "budget_tokens": w.budget,
                    "scheduled_positions": positions, "rows_streamed": rows},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "frac_scope": "the row-streaming kernel alone; path_frac covers the whole step",
+                     "path_achieved": path_gbps, "path_frac": path_gbps / PEAK_HBM_GBS,
                      "kernel": "stream_kernel<bf16>", "ms_per_launch": ms_stream,
                      "ms_per_launch_median": ms_stream_median,
                      "algorithmic_bytes_per_launch": alg_bytes,
@@ -214,6 +221,21 @@ def main():
         "ms_breakdown": {"stream_kernel": ms_stream, "rest_of_step": ms_step - ms_stream},
     }
     print(json.dumps(line), flush=True)
+
+
+def recipe(name):
+    """The workload's logit recipe in words (the generator's parameters)."""
+    from workloads import CONFIGS
+    c = CONFIGS[name]
+    t = f"target N(0,{c['target_std']:g})" + (f" + {c['spike']:g} on one token per row" if c["spike"] else "")
+    nz = c["noise"]
+    if nz is None:
+        d = "no draft logits"
+    elif nz[0] == "const":
+        d = f"draft = target + N(0,{nz[1]:g})"
+    else:
+        d = f"draft_k = target_k + N(0,{nz[1]:g}+{nz[2]:g}k)"
+    return f"{t}, {d}"
 
 
 def _kernel_sha():
@@ -322,8 +344,9 @@ def draft_leg(sv, torch, oracle, dev, stream, reps=10, with_cpu=True):
         sample = [0, 1]
         with threadpool_limits(1):
             t0 = time.perf_counter()
-            oracle.markov_draft(w.base, w.W1.cpu(), w.W2t.cpu(), w.anchor.cpu(), w.temperature.cpu(), w.seed.cpu(),
-                                w.hidden, w.conf_w.cpu(), requests=sample)
+            n = len(sample)   # the first requests of the batch, as a slice (the oracle's outputs are per row)
+            oracle.markov_draft(w.base[:n], w.W1.cpu(), w.W2t.cpu(), w.anchor[:n].cpu(), w.temperature[:n].cpu(),
+                                w.seed[:n].cpu(), w.hidden[:n], w.conf_w.cpu())
             el = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": len(sample) * G / el, "unit": "draft tokens/s", "cores": 1,
                                "kind": "oracle",
@@ -435,7 +458,8 @@ def cpu_baseline(w, oracle, budget_s, L, pool):
     # pooled: host copies once (bf16 -> fp32 is exact), workers forked with them; the workers
     # only run numpy and exit without touching the GPU
     import multiprocessing as mp
-    n = max(1, min(pool, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    n = max(1, min(pool if pool > 0 else 16, affinity))
     Lh = np.asarray(L)
     _POOL.update(oracle=oracle, target=w.target.float().cpu().numpy(), draft=w.draft.float().cpu().numpy(),
                  tokens=w.draft_tokens.cpu().numpy(), lengths=Lh,
@@ -450,9 +474,10 @@ def cpu_baseline(w, oracle, budget_s, L, pool):
         el_pool = time.perf_counter() - t0
     _POOL.clear()
     pooled = int(Lh.sum()) / (el_pool + t_sched)
-    return {"value": pooled, "unit": "positions/s", "cores": n, "kind": "oracle",
+    return {"value": pooled, "unit": "positions/s", "cores": n, "kind": "oracle", "host_affinity_cores": affinity,
             "sample": f"all {w.B} requests ({int(Lh.sum())} verified positions) over {n} forked numpy fp64 "
-                      f"worker processes in {el_pool:.1f} s, plus the scheduler ({t_sched:.2f} s, one thread)",
+                      f"worker processes (of {affinity} host cores in this process's affinity) in "
+                      f"{el_pool:.1f} s, plus the scheduler ({t_sched:.2f} s, one thread)",
             "single_thread": {"value": single, "cores": 1,
                               "sample": f"first {done} of {w.B} requests ({positions} verified positions), "
                                         f"verify {el:.1f} s + scheduler {t_sched:.2f} s pro rata"}}

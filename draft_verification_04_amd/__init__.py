@@ -36,6 +36,8 @@ REQ_NONFINITE = 4
 REQ_BAD_LENGTH = 8
 REQ_BAD_TOPK = 16
 REQ_BAD_CONFIDENCE = 32
+REQ_OVER_BUDGET = 64
+REQ_BAD_ROWS = 128
 
 # name -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -50,7 +52,8 @@ EXPORTS = {
                                   _P, _P]),
     "spec_verify_bounded": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P,
                                  _I, _P, _P]),
-    "spec_verify_flat": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "spec_verify_flat": (_I, [_I, _I, _I, _I, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                              _P, _P, _P, _Z, _P]),
     "spec_verify_greedy_workspace_size": (_Z, [_I, _I]),
     "spec_verify_greedy": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_schedule_workspace_size": (_Z, [_I, _I]),
@@ -111,6 +114,28 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _launch(stream, allocated, call):
+    """Run call(hip_stream) on `stream` (default: the current stream) and return its code.
+
+    The binding allocates and fills tensors (workspaces, default temperatures and seeds,
+    outputs) on the current stream.  When `stream` is another stream it first waits for that
+    work, and afterwards each tensor in `allocated` is marked as in use by it, so the caching
+    allocator does not hand the memory to other work before the call's kernels are done with it.
+    Tensors the caller passed in stay the caller's to order.
+    """
+    cur = torch.cuda.current_stream()
+    s = cur if stream is None else stream
+    side = s != cur
+    if side:
+        s.wait_stream(cur)
+    code = call(ctypes.c_void_p(s.cuda_stream))
+    if side:
+        for t in allocated:
+            if t is not None:
+                t.record_stream(s)
+    return code
+
+
 def _check(fn, code):
     if code != SPEC_OK:
         raise SpecError(fn, code)
@@ -130,6 +155,43 @@ def _dev(t, name, dtype=None, ndim=None):
     return t
 
 
+def _vec(t, name, n):
+    """A per-request vector must hold exactly n values (checked before the device checks)."""
+    if t is not None and (not isinstance(t, torch.Tensor) or t.dim() != 1 or t.numel() != n):
+        raise ValueError(f"{name} must be a 1-D tensor of {n} values")
+    return t
+
+
+def _shape(t, name, shape):
+    if t is not None and (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape)):
+        got = tuple(t.shape) if isinstance(t, torch.Tensor) else type(t).__name__
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {got}")
+    return t
+
+
+def _check_out(out, spec, device):
+    """Caller-supplied outputs: every tensor present must have the shape, dtype and device the
+    kernels write (a missing optional one is passed as NULL)."""
+    for key, (shape, dtype, required) in spec.items():
+        t = out.get(key)
+        if t is None:
+            if required:
+                raise ValueError(f"out[{key!r}] is required")
+            continue
+        _shape(t, f"out[{key!r}]", shape)
+        if t.dtype != dtype:
+            raise TypeError(f"out[{key!r}] has dtype {t.dtype}, expected {dtype}")
+        if t.device != device or not t.is_contiguous():
+            raise ValueError(f"out[{key!r}] must be a contiguous tensor on {device}")
+    return out
+
+
+def _on(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the logits on {device}")
+
+
 def _logit_dtype(t):
     if t.dtype == torch.float32:
         return SPEC_F32
@@ -142,44 +204,66 @@ def verify_workspace_bytes(B: int, gamma: int, V: int) -> int:
     return int(load_library().spec_verify_workspace_size(B, gamma, V))
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _workspace(nbytes: int, device, workspace=None, allocated=None):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if allocated is not None:
+        allocated.append(ws)
+    return ws
+
+
+_SEED_DTYPES = (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64
 
 
 def _verify_inputs(target, draft, draft_tokens, lengths, temperature, top_k, seed):
-    """Checks the verify inputs; returns (B, gamma, V, temperature, seed) with the defaults filled in."""
-    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
-    _dev(draft, "draft", target.dtype, 3)
+    """Checks the verify inputs (shapes first, then device and dtype); returns
+    (B, gamma, V, temperature, seed, allocated) with the defaults filled in."""
+    if not isinstance(target, torch.Tensor) or target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
     B, G1, V = target.shape
     G = G1 - 1
-    if tuple(draft.shape) != (B, G, V):
-        raise ValueError("draft must be [B, gamma, V]")
+    _shape(draft, "draft", (B, G, V))
+    _shape(draft_tokens, "draft_tokens", (B, G))
+    for name, t in (("lengths", lengths), ("temperature", temperature), ("top_k", top_k), ("seed", seed)):
+        _vec(t, name, B)
+    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
+    _dev(draft, "draft", target.dtype, 3)
     _dev(draft_tokens, "draft_tokens", torch.int32, 2)
-    if tuple(draft_tokens.shape) != (B, G):
-        raise ValueError("draft_tokens must be [B, gamma]")
-    dev = target.device
-    if temperature is None:
-        temperature = torch.ones(B, dtype=torch.float32, device=dev)
-    if seed is None:
-        seed = torch.zeros(B, dtype=torch.int64, device=dev)
     _dev(lengths, "lengths", torch.int32, 1)
     _dev(temperature, "temperature", torch.float32, 1)
     _dev(top_k, "top_k", torch.int32, 1)
-    _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
-    return B, G, V, temperature, seed
+    _dev(seed, "seed", _SEED_DTYPES, 1)
+    dev = target.device
+    _on(dev, draft=draft, draft_tokens=draft_tokens, lengths=lengths, temperature=temperature, top_k=top_k,
+        seed=seed)
+    allocated = []
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+        allocated.append(temperature)
+    if seed is None:
+        seed = torch.zeros(B, dtype=torch.int64, device=dev)
+        allocated.append(seed)
+    return B, G, V, temperature, seed, allocated
 
 
-def _verify_outputs(B, G, dev, out):
-    """A caller's `out` is used as given (a missing accept_prob or status is passed as NULL)."""
-    if out is None:
-        out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
-                   accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
-                   status=torch.empty(B, dtype=torch.int32, device=dev))
+def _verify_out_spec(B, G):
+    return dict(num_accepted=((B,), torch.int32, True), out_tokens=((B, G + 1), torch.int32, True),
+                accept_prob=((B, G), torch.float32, False), status=((B,), torch.int32, False))
+
+
+def _verify_outputs(B, G, dev, out, allocated):
+    """A caller's `out` is checked and used as given (a missing accept_prob or status is passed as
+    NULL); otherwise the outputs are allocated here."""
+    if out is not None:
+        return _check_out(out, _verify_out_spec(B, G), dev)
+    out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+               out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+               accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
+               status=torch.empty(B, dtype=torch.int32, device=dev))
+    allocated.extend(out.values())
     return out
 
 
@@ -203,23 +287,26 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     HipEvent pair taking the start and end of the row-streaming kernel.
     `max_tokens` (spec_verify_bounded): the caller's bound on sum_i (L_i + 1),
     e.g. the scheduler's token budget; it sizes the streaming grid only.
+    `stream`: a torch stream to enqueue on (default: the current stream).
     """
     lib = load_library()
-    B, G, V, temperature, seed = _verify_inputs(target, draft, draft_tokens, lengths, temperature, top_k, seed)
+    B, G, V, temperature, seed, mine = _verify_inputs(target, draft, draft_tokens, lengths, temperature, top_k,
+                                                      seed)
     dev = target.device
-    out = _verify_outputs(B, G, dev, out)
+    out = _verify_outputs(B, G, dev, out, mine)
     nbytes = int(lib.spec_verify_workspace_size(B, G, V))
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, mine)
     ev0, ev1 = _events(events)
-    args = (B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
-            _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
-            _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
-            _stream(stream))
-    if max_tokens is None:
-        code = lib.spec_verify_profiled(*args, ev0, ev1)
-    else:
-        code = lib.spec_verify_bounded(*args, int(max_tokens), ev0, ev1)
-    _check("spec_verify", code)
+
+    def call(sp):
+        args = (B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
+                _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+                _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
+                sp)
+        if max_tokens is None:
+            return lib.spec_verify_profiled(*args, ev0, ev1)
+        return lib.spec_verify_bounded(*args, int(max_tokens), ev0, ev1)
+    _check("spec_verify", _launch(stream, mine, call))
     return out
 
 
@@ -228,37 +315,52 @@ def verify_flat(target_rows: torch.Tensor, draft_rows: torch.Tensor, draft_token
                 top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
                 out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """spec_verify_flat on torch tensors: target_rows [sum(L+1), V], draft_rows [sum(L), V] hold only
-    the verified rows, request after request; draft_tokens [B, gamma]; lengths [B] int32."""
+    the verified rows, request after request; draft_tokens [B, gamma]; lengths [B] int32.  The row
+    counts of the two tensors are passed on: a request whose rows lie past them gets REQ_BAD_ROWS."""
     lib = load_library()
+    for name, t in (("target_rows", target_rows), ("draft_rows", draft_rows)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name} must be [rows, V]")
+    if not isinstance(draft_tokens, torch.Tensor) or draft_tokens.dim() != 2:
+        raise ValueError("draft_tokens must be [B, gamma]")
+    B, G = draft_tokens.shape
+    V = target_rows.shape[1]
+    if draft_rows.shape[1] != V:
+        raise ValueError("draft_rows must be [sum(L), V] with the target rows' V")
+    for name, t in (("lengths", lengths), ("temperature", temperature), ("top_k", top_k), ("seed", seed)):
+        _vec(t, name, B)
+    if lengths is None:
+        raise ValueError("lengths are required (they define the layout)")
     _dev(target_rows, "target_rows", (torch.float32, torch.bfloat16), 2)
     _dev(draft_rows, "draft_rows", target_rows.dtype, 2)
     _dev(draft_tokens, "draft_tokens", torch.int32, 2)
     _dev(lengths, "lengths", torch.int32, 1)
-    B, G = draft_tokens.shape
-    V = target_rows.shape[1]
-    if draft_rows.shape[1] != V or lengths.numel() != B:
-        raise ValueError("draft_rows must be [sum(L), V] and lengths [B]")
-    dev = target_rows.device
-    if temperature is None:
-        temperature = torch.ones(B, dtype=torch.float32, device=dev)
-    if seed is None:
-        seed = torch.zeros(B, dtype=torch.int64, device=dev)
     _dev(temperature, "temperature", torch.float32, 1)
     _dev(top_k, "top_k", torch.int32, 1)
-    _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
-    if out is None:
-        out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
-                   accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
-                   status=torch.empty(B, dtype=torch.int32, device=dev))
-    ws = _workspace(int(lib.spec_verify_workspace_size(B, G, V)), dev, workspace)
+    _dev(seed, "seed", _SEED_DTYPES, 1)
+    dev = target_rows.device
+    _on(dev, draft_rows=draft_rows, draft_tokens=draft_tokens, lengths=lengths, temperature=temperature,
+        top_k=top_k, seed=seed)
+    mine = []
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+        mine.append(temperature)
+    if seed is None:
+        seed = torch.zeros(B, dtype=torch.int64, device=dev)
+        mine.append(seed)
+    out = _verify_outputs(B, G, dev, out, mine)
+    ws = _workspace(int(lib.spec_verify_workspace_size(B, G, V)), dev, workspace, mine)
     # an empty draft_rows tensor (every length 0) still needs an aligned non-null pointer
-    drows = draft_rows if draft_rows.numel() else torch.empty((1, V), dtype=target_rows.dtype, device=dev)
-    code = lib.spec_verify_flat(
-        B, G, V, _logit_dtype(target_rows), _ptr(target_rows), _ptr(drows), _ptr(draft_tokens), _ptr(lengths),
-        _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
-        _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream))
+    n_drows = draft_rows.shape[0]
+    drows = draft_rows
+    if draft_rows.numel() == 0:
+        drows = torch.empty((1, V), dtype=target_rows.dtype, device=dev)
+        mine.append(drows)
+    code = _launch(stream, mine, lambda sp: lib.spec_verify_flat(
+        B, G, V, _logit_dtype(target_rows), _ptr(target_rows), target_rows.shape[0], _ptr(drows), n_drows,
+        _ptr(draft_tokens), _ptr(lengths), _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]),
+        _ptr(out["out_tokens"]), _ptr(out.get("accept_prob")), _ptr(out.get("status")), _ptr(ws),
+        ws.numel() * ws.element_size(), sp))
     _check("spec_verify_flat", code)
     return out
 
@@ -267,25 +369,50 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, lengths: Opt
                   out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """spec_verify_greedy on torch tensors.  Returns dict(num_accepted, out_tokens, status)."""
     lib = load_library()
-    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
+    if not isinstance(target, torch.Tensor) or target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
     B, G1, V = target.shape
     G = G1 - 1
+    _shape(draft_tokens, "draft_tokens", (B, G))
+    _vec(lengths, "lengths", B)
+    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
     _dev(draft_tokens, "draft_tokens", torch.int32, 2)
-    if tuple(draft_tokens.shape) != (B, G):
-        raise ValueError("draft_tokens must be [B, gamma]")
     _dev(lengths, "lengths", torch.int32, 1)
     dev = target.device
+    _on(dev, draft_tokens=draft_tokens, lengths=lengths)
+    mine = []
     if out is None:
         out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
                    out_tokens=torch.empty((B, G1), dtype=torch.int32, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
+        mine.extend(out.values())
+    else:
+        spec = _verify_out_spec(B, G)
+        del spec["accept_prob"]
+        _check_out(out, spec, dev)
     nbytes = int(lib.spec_verify_greedy_workspace_size(B, G))
-    ws = _workspace(nbytes, dev, workspace)
-    code = lib.spec_verify_greedy(B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft_tokens),
-                                  _ptr(lengths), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
-                                  _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    ws = _workspace(nbytes, dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_verify_greedy(
+        B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft_tokens), _ptr(lengths), _ptr(out["num_accepted"]),
+        _ptr(out["out_tokens"]), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), sp))
     _check("spec_verify_greedy", code)
     return out
+
+
+def _sched_inputs(conf, sps):
+    if not isinstance(conf, torch.Tensor) or conf.dim() != 2:
+        raise ValueError("conf must be [B, gamma]")
+    if not isinstance(sps, torch.Tensor) or sps.dim() != 1:
+        raise ValueError("sps must be a 1-D cost table")
+    _dev(conf, "conf", torch.float32, 2)
+    _dev(sps, "sps", torch.float64, 1)
+    _on(conf.device, sps=sps)
+    return conf.shape
+
+
+def _sched_out_spec(B):
+    return dict(lengths=((B,), torch.int32, True), theta=((1,), torch.float64, False),
+                status=((B,), torch.int32, False))
 
 
 def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
@@ -293,18 +420,20 @@ def schedule_lengths(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
                      workspace: Optional[torch.Tensor] = None) -> dict:
     """spec_schedule_lengths on torch tensors.  Returns dict(lengths, theta, status)."""
     lib = load_library()
-    _dev(conf, "conf", torch.float32, 2)
-    _dev(sps, "sps", torch.float64, 1)
-    B, G = conf.shape
+    B, G = _sched_inputs(conf, sps)
     dev = conf.device
+    mine = []
     if out is None:
         out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
                    theta=torch.empty(1, dtype=torch.float64, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
-    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace)
-    code = lib.spec_schedule_lengths(B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode),
-                                     _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("status")),
-                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        mine.extend(out.values())
+    else:
+        _check_out(out, _sched_out_spec(B), dev)
+    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_schedule_lengths(
+        B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode), _ptr(out["lengths"]),
+        _ptr(out.get("theta")), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), sp))
     _check("spec_schedule_lengths", code)
     return out
 
@@ -321,27 +450,33 @@ def schedule_verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: tor
     Returns dict(lengths, theta, sched_status, num_accepted, out_tokens, accept_prob, status).
     """
     lib = load_library()
-    B, G, V, temperature, seed = _verify_inputs(target, draft, draft_tokens, None, temperature, top_k, seed)
-    _dev(conf, "conf", torch.float32, 2)
-    _dev(sps, "sps", torch.float64, 1)
-    if tuple(conf.shape) != (B, G):
-        raise ValueError("conf must be [B, gamma]")
+    if isinstance(target, torch.Tensor) and target.dim() == 3:
+        _shape(conf, "conf", (target.shape[0], target.shape[1] - 1))
+    B, G, V, temperature, seed, mine = _verify_inputs(target, draft, draft_tokens, None, temperature, top_k, seed)
+    _sched_inputs(conf, sps)
     dev = target.device
+    _on(dev, conf=conf)
     if out is None:
-        out = _verify_outputs(B, G, dev, None)
-        out.update(lengths=torch.empty(B, dtype=torch.int32, device=dev),
-                   theta=torch.empty(1, dtype=torch.float64, device=dev),
-                   sched_status=torch.empty(B, dtype=torch.int32, device=dev))
-    ws = _workspace(int(lib.spec_verify_workspace_size(B, G, V)), dev, workspace)
-    sws = _workspace(int(lib.spec_schedule_workspace_size(B, G)), dev, sched_workspace)
+        out = _verify_outputs(B, G, dev, None, mine)
+        extra = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
+                     theta=torch.empty(1, dtype=torch.float64, device=dev),
+                     sched_status=torch.empty(B, dtype=torch.int32, device=dev))
+        out.update(extra)
+        mine.extend(extra.values())
+    else:
+        spec = _verify_out_spec(B, G)
+        spec.update(lengths=((B,), torch.int32, True), theta=((1,), torch.float64, False),
+                    sched_status=((B,), torch.int32, False))
+        _check_out(out, spec, dev)
+    ws = _workspace(int(lib.spec_verify_workspace_size(B, G, V)), dev, workspace, mine)
+    sws = _workspace(int(lib.spec_schedule_workspace_size(B, G)), dev, sched_workspace, mine)
     ev0, ev1 = _events(events)
-    code = lib.spec_schedule_verify(
+    code = _launch(stream, mine, lambda sp: lib.spec_schedule_verify(
         B, G, V, _logit_dtype(target), _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode),
         _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(temperature), _ptr(top_k), _ptr(seed),
         _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("sched_status")), _ptr(out["num_accepted"]),
         _ptr(out["out_tokens"]), _ptr(out.get("accept_prob")), _ptr(out.get("status")),
-        _ptr(sws), sws.numel() * sws.element_size(), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
-        ev0, ev1)
+        _ptr(sws), sws.numel() * sws.element_size(), _ptr(ws), ws.numel() * ws.element_size(), sp, ev0, ev1))
     _check("spec_schedule_verify", code)
     return out
 
@@ -351,25 +486,34 @@ def overlap_mass(target: torch.Tensor, draft: torch.Tensor, lengths: Optional[to
                  out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """spec_overlap_mass on torch tensors.  Returns dict(overlap [B, gamma] float64, status [B])."""
     lib = load_library()
+    if not isinstance(target, torch.Tensor) or target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
     B, G1, V = target.shape
     G = G1 - 1
-    _dev(target, "target", None, 3)
+    _shape(draft, "draft", (B, G, V))
+    for name, t in (("lengths", lengths), ("temperature", temperature), ("top_k", top_k)):
+        _vec(t, name, B)
+    _dev(target, "target", (torch.float32, torch.bfloat16), 3)
     _dev(draft, "draft", target.dtype, 3)
     _dev(lengths, "lengths", torch.int32, 1)
     _dev(temperature, "temperature", torch.float32, 1)
     _dev(top_k, "top_k", torch.int32, 1)
-    if tuple(draft.shape) != (B, G, V):
-        raise ValueError("draft must be [B, gamma, V] with target [B, gamma+1, V]")
     dev = target.device
+    _on(dev, draft=draft, lengths=lengths, temperature=temperature, top_k=top_k)
+    mine = []
     if temperature is None:
         temperature = torch.ones(B, dtype=torch.float32, device=dev)
+        mine.append(temperature)
     if out is None:
         out = dict(overlap=torch.empty((B, G), dtype=torch.float64, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
-    ws = _workspace(lib.spec_overlap_workspace_size(B, G, V), dev, workspace)
-    code = lib.spec_overlap_mass(B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(lengths),
-                                 _ptr(temperature), _ptr(top_k), _ptr(out["overlap"]), _ptr(out.get("status")),
-                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        mine.extend(out.values())
+    else:
+        _check_out(out, dict(overlap=((B, G), torch.float64, True), status=((B,), torch.int32, False)), dev)
+    ws = _workspace(lib.spec_overlap_workspace_size(B, G, V), dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_overlap_mass(
+        B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(lengths), _ptr(temperature), _ptr(top_k),
+        _ptr(out["overlap"]), _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), sp))
     _check("spec_overlap_mass", code)
     return out
 
@@ -389,45 +533,55 @@ def draft_markov(base: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, anchor
     `base`.
     """
     lib = load_library()
-    _dev(base, "base", (torch.float32, torch.bfloat16), 3)
+    if not isinstance(base, torch.Tensor) or base.dim() != 3:
+        raise ValueError("base must be [B, gamma, V]")
     B, G, V = base.shape
-    _dev(W1, "W1", torch.bfloat16, 2)
-    _dev(W2t, "W2t", torch.bfloat16, 2)
+    if not isinstance(W1, torch.Tensor) or W1.dim() != 2:
+        raise ValueError("W1 must be [V, r]")
     r = W1.shape[1]
-    if tuple(W1.shape) != (V, r) or tuple(W2t.shape) != (V, r):
-        raise ValueError("W1 and W2t must be [V, r]")
-    _dev(anchor, "anchor", torch.int32, 1)
-    dev = base.device
-    if temperature is None:
-        temperature = torch.ones(B, dtype=torch.float32, device=dev)
-    _dev(temperature, "temperature", torch.float32, 1)
-    _dev(seed, "seed", (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64, 1)
+    _shape(W1, "W1", (V, r))
+    _shape(W2t, "W2t", (V, r))
+    for name, t in (("anchor", anchor), ("temperature", temperature), ("seed", seed)):
+        _vec(t, name, B)
     d = 0
     if hidden is not None:
-        _dev(hidden, "hidden", base.dtype, 3)
-        if tuple(hidden.shape[:2]) != (B, G):
+        if not isinstance(hidden, torch.Tensor) or hidden.dim() != 3 or tuple(hidden.shape[:2]) != (B, G):
             raise ValueError("hidden must be [B, gamma, d]")
         d = hidden.shape[2]
     if conf_w is not None:
-        _dev(conf_w, "conf_w", torch.float32, 1)
-        if conf_w.numel() != d + r:
-            raise ValueError("conf_w must hold d + r values")
-    if conf_tau is not None:
-        _dev(conf_tau, "conf_tau", torch.float64, 1)
-        if conf_tau.numel() != G:
-            raise ValueError("conf_tau must hold gamma values")
+        _vec(conf_w, "conf_w (d + r values)", d + r)
+    _vec(conf_tau, "conf_tau (gamma values)", G)
+    _dev(base, "base", (torch.float32, torch.bfloat16), 3)
+    _dev(W1, "W1", torch.bfloat16, 2)
+    _dev(W2t, "W2t", torch.bfloat16, 2)
+    _dev(anchor, "anchor", torch.int32, 1)
+    _dev(temperature, "temperature", torch.float32, 1)
+    _dev(seed, "seed", _SEED_DTYPES, 1)
+    _dev(hidden, "hidden", base.dtype, 3)
+    _dev(conf_w, "conf_w", torch.float32, 1)
+    _dev(conf_tau, "conf_tau", torch.float64, 1)
+    dev = base.device
+    _on(dev, W1=W1, W2t=W2t, anchor=anchor, temperature=temperature, seed=seed, hidden=hidden, conf_w=conf_w,
+        conf_tau=conf_tau)
+    mine = []
+    if temperature is None:
+        temperature = torch.ones(B, dtype=torch.float32, device=dev)
+        mine.append(temperature)
     if out is None:
         out = dict(tokens=torch.empty((B, G), dtype=torch.int32, device=dev),
                    logits=base if in_place else torch.empty_like(base),
                    conf=torch.empty((B, G), dtype=torch.float32, device=dev) if conf_w is not None else None,
                    status=torch.empty(B, dtype=torch.int32, device=dev))
+        mine.extend(t for k, t in out.items() if not (in_place and k == "logits"))
+    else:
+        _check_out(out, dict(tokens=((B, G), torch.int32, True), logits=((B, G, V), base.dtype, True),
+                             conf=((B, G), torch.float32, False), status=((B,), torch.int32, True)), dev)
     nbytes = int(lib.spec_draft_workspace_size(B, G, V))
-    ws = _workspace(nbytes, dev, workspace)
-    code = lib.spec_draft_markov(B, G, V, r, _logit_dtype(base), _ptr(base), _ptr(W1), _ptr(W2t), _ptr(anchor),
-                                 _ptr(temperature), _ptr(seed), d, _ptr(hidden), _ptr(conf_w), _ptr(conf_tau),
-                                 _ptr(out["tokens"]),
-                                 _ptr(out["logits"]), _ptr(out.get("conf")), _ptr(out["status"]), _ptr(ws),
-                                 ws.numel() * ws.element_size(), _stream(stream))
+    ws = _workspace(nbytes, dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_draft_markov(
+        B, G, V, r, _logit_dtype(base), _ptr(base), _ptr(W1), _ptr(W2t), _ptr(anchor), _ptr(temperature),
+        _ptr(seed), d, _ptr(hidden), _ptr(conf_w), _ptr(conf_tau), _ptr(out["tokens"]), _ptr(out["logits"]),
+        _ptr(out.get("conf")), _ptr(out["status"]), _ptr(ws), ws.numel() * ws.element_size(), sp))
     _check("spec_draft_markov", code)
     return out
 
@@ -437,23 +591,32 @@ def sts_fit(conf_logits: torch.Tensor, labels: torch.Tensor, taus: torch.Tensor,
     """spec_sts_fit: conf_logits [N, gamma] float32, labels [N, gamma] uint8, taus [ntau] float64.
     Returns dict(tau [gamma] float64, index [gamma] int32, ece [gamma, ntau] float64)."""
     lib = load_library()
+    if not isinstance(conf_logits, torch.Tensor) or conf_logits.dim() != 2:
+        raise ValueError("conf_logits must be [N, gamma]")
+    N, G = conf_logits.shape
+    _shape(labels, "labels", (N, G))
+    if not isinstance(taus, torch.Tensor) or taus.dim() != 1:
+        raise ValueError("taus must be a 1-D grid")
     _dev(conf_logits, "conf_logits", torch.float32, 2)
     _dev(labels, "labels", torch.uint8, 2)
     _dev(taus, "taus", torch.float64, 1)
-    N, G = conf_logits.shape
-    if tuple(labels.shape) != (N, G):
-        raise ValueError("labels must be [N, gamma]")
     ntau = taus.numel()
     dev = conf_logits.device
+    _on(dev, labels=labels, taus=taus)
+    mine = []
     if out is None:
         out = dict(tau=torch.empty(G, dtype=torch.float64, device=dev),
                    index=torch.empty(G, dtype=torch.int32, device=dev),
                    ece=torch.empty((G, ntau), dtype=torch.float64, device=dev))
+        mine.extend(out.values())
+    else:
+        _check_out(out, dict(tau=((G,), torch.float64, True), index=((G,), torch.int32, False),
+                             ece=((G, ntau), torch.float64, False)), dev)
     nbytes = int(lib.spec_sts_workspace_size(N, ntau, bins))
-    ws = _workspace(nbytes, dev, workspace)
-    code = lib.spec_sts_fit(N, G, _ptr(conf_logits), _ptr(labels), ntau, _ptr(taus), bins, _ptr(out["tau"]),
-                            _ptr(out.get("index")), _ptr(out.get("ece")), _ptr(ws), ws.numel() * ws.element_size(),
-                            _stream(stream))
+    ws = _workspace(nbytes, dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_sts_fit(
+        N, G, _ptr(conf_logits), _ptr(labels), ntau, _ptr(taus), bins, _ptr(out["tau"]), _ptr(out.get("index")),
+        _ptr(out.get("ece")), _ptr(ws), ws.numel() * ws.element_size(), sp))
     _check("spec_sts_fit", code)
     return out
 
@@ -462,12 +625,21 @@ def sts_apply(conf_logits: torch.Tensor, tau: torch.Tensor, out: Optional[torch.
               stream=None) -> torch.Tensor:
     """spec_sts_apply: sigmoid(conf_logits / tau) per position, float32 [B, gamma]."""
     lib = load_library()
+    if not isinstance(conf_logits, torch.Tensor) or conf_logits.dim() != 2:
+        raise ValueError("conf_logits must be [B, gamma]")
+    B, G = conf_logits.shape
+    _vec(tau, "tau", G)
+    _shape(out, "out", (B, G))
     _dev(conf_logits, "conf_logits", torch.float32, 2)
     _dev(tau, "tau", torch.float64, 1)
-    B, G = conf_logits.shape
+    _dev(out, "out", torch.float32, 2)
+    _on(conf_logits.device, tau=tau, out=out)
+    mine = []
     if out is None:
         out = torch.empty_like(conf_logits)
-    _check("spec_sts_apply", lib.spec_sts_apply(B, G, _ptr(conf_logits), _ptr(tau), _ptr(out), _stream(stream)))
+        mine.append(out)
+    _check("spec_sts_apply", _launch(stream, mine, lambda sp: lib.spec_sts_apply(
+        B, G, _ptr(conf_logits), _ptr(tau), _ptr(out), sp)))
     return out
 
 
@@ -484,18 +656,21 @@ def schedule_capacity(conf: torch.Tensor, sps: torch.Tensor, budget_tokens: int,
                       stream=None, workspace: Optional[torch.Tensor] = None) -> dict:
     """spec_schedule_capacity: dict(capacity [1] int32, theta [1] float64, status [B])."""
     lib = load_library()
-    _dev(conf, "conf", torch.float32, 2)
-    _dev(sps, "sps", torch.float64, 1)
-    B, G = conf.shape
+    B, G = _sched_inputs(conf, sps)
     dev = conf.device
+    mine = []
     if out is None:
         out = dict(capacity=torch.empty(1, dtype=torch.int32, device=dev),
                    theta=torch.empty(1, dtype=torch.float64, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
-    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace)
-    code = lib.spec_schedule_capacity(B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens),
-                                      _ptr(out["capacity"]), _ptr(out.get("theta")), _ptr(out.get("status")),
-                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        mine.extend(out.values())
+    else:
+        _check_out(out, dict(capacity=((1,), torch.int32, True), theta=((1,), torch.float64, False),
+                             status=((B,), torch.int32, False)), dev)
+    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_schedule_capacity(
+        B, G, _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), _ptr(out["capacity"]), _ptr(out.get("theta")),
+        _ptr(out.get("status")), _ptr(ws), ws.numel() * ws.element_size(), sp))
     _check("spec_schedule_capacity", code)
     return out
 
@@ -504,16 +679,25 @@ def schedule_topk(conf: torch.Tensor, capacity: torch.Tensor, out: Optional[dict
                   workspace: Optional[torch.Tensor] = None) -> dict:
     """spec_schedule_topk: dict(lengths [B] int32, status [B]) admitting up to capacity[0] candidates."""
     lib = load_library()
+    if not isinstance(conf, torch.Tensor) or conf.dim() != 2:
+        raise ValueError("conf must be [B, gamma]")
+    B, G = conf.shape
+    _vec(capacity, "capacity", 1)
     _dev(conf, "conf", torch.float32, 2)
     _dev(capacity, "capacity", torch.int32, 1)
-    B, G = conf.shape
     dev = conf.device
+    _on(dev, capacity=capacity)
+    mine = []
     if out is None:
         out = dict(lengths=torch.empty(B, dtype=torch.int32, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev))
-    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace)
-    code = lib.spec_schedule_topk(B, G, _ptr(conf), _ptr(capacity), _ptr(out["lengths"]), _ptr(out.get("status")),
-                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        mine.extend(out.values())
+    else:
+        _check_out(out, dict(lengths=((B,), torch.int32, True), status=((B,), torch.int32, False)), dev)
+    ws = _workspace(lib.spec_schedule_workspace_size(B, G), dev, workspace, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_schedule_topk(
+        B, G, _ptr(conf), _ptr(capacity), _ptr(out["lengths"]), _ptr(out.get("status")), _ptr(ws),
+        ws.numel() * ws.element_size(), sp))
     _check("spec_schedule_topk", code)
     return out
 
@@ -521,13 +705,16 @@ def schedule_topk(conf: torch.Tensor, capacity: torch.Tensor, out: Optional[dict
 def philox_uniforms(seed: torch.Tensor, request: torch.Tensor, position: torch.Tensor, stream=None):
     """The library's (u_accept, u_emit) draws for each (seed, request, position) triple."""
     lib = load_library()
+    n = seed.numel() if isinstance(seed, torch.Tensor) else -1
+    for name, t in (("seed", seed), ("request", request), ("position", position)):
+        _vec(t, name, n)
     _dev(seed, "seed", torch.int64, 1)
     _dev(request, "request", torch.int32, 1)
     _dev(position, "position", torch.int32, 1)
-    n = seed.numel()
+    _on(seed.device, request=request, position=position)
     ua = torch.empty(n, dtype=torch.float64, device=seed.device)
     ue = torch.empty(n, dtype=torch.float64, device=seed.device)
-    code = lib.spec_philox_uniforms(n, _ptr(seed), _ptr(request), _ptr(position), _ptr(ua), _ptr(ue),
-                                    _stream(stream))
+    code = _launch(stream, [ua, ue], lambda sp: lib.spec_philox_uniforms(
+        n, _ptr(seed), _ptr(request), _ptr(position), _ptr(ua), _ptr(ue), sp))
     _check("spec_philox_uniforms", code)
     return ua, ue

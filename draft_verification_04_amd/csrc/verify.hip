@@ -40,7 +40,7 @@ namespace spec {
 __device__ __forceinline__ int last_item(const VerifyArgs& a, int i) {
   const int L = a.lengths ? a.lengths[i] : a.G;
   if (L < 0 || L > a.G) return -1;
-  if (a.max_items > 0 && (a.req_status[i] & SPEC_REQ_OVER_BUDGET)) return -1;
+  if (a.req_status[i] & (SPEC_REQ_OVER_BUDGET | SPEC_REQ_BAD_ROWS)) return -1;
   return a.overlap_only ? L - 1 : L;
 }
 
@@ -52,38 +52,6 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
   __shared__ long long woff_t[kWorklistThreads / SPEC_WAVE], woff_d[kWorklistThreads / SPEC_WAVE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G, B = a.B;
-  if (a.flat) {
-    // first target / draft row of every request in the flattened layout (a bad length counts
-    // as no rows): exclusive prefix sums of L_i + 1 and L_i, block by block
-    long long carry_t = 0, carry_d = 0;
-    for (int b0 = 0; b0 < B; b0 += blockDim.x) {
-      const int i = b0 + tid;
-      const int L = (i < B) ? (a.lengths ? a.lengths[i] : G) : -1;
-      const long long nt = (L >= 0 && L <= G) ? L + 1 : 0, nd = (L >= 0 && L <= G) ? L : 0;
-      const long long it = wave_inclusive_sum_i64(nt, lane), id = wave_inclusive_sum_i64(nd, lane);
-      __syncthreads();
-      if (lane == 63) {
-        woff_t[wave] = it;
-        woff_d[wave] = id;
-      }
-      __syncthreads();
-      long long bt = carry_t, bd = carry_d, tt = 0, td = 0;
-      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-        if (w < wave) {
-          bt += woff_t[w];
-          bd += woff_d[w];
-        }
-        tt += woff_t[w];
-        td += woff_d[w];
-      }
-      if (i < B) {
-        a.t_off[i] = bt + it - nt;
-        a.d_off[i] = bd + id - nd;
-      }
-      carry_t += tt;
-      carry_d += td;
-    }
-  }
   for (int t = tid; t < G + 2; t += blockDim.x) hist[t] = 0;
   for (int t = tid; t < G + 1; t += blockDim.x) carry[t] = 0;
   if (a.max_items > 0) {
@@ -108,6 +76,43 @@ __global__ __launch_bounds__(kWorklistThreads) void worklist_kernel(VerifyArgs a
     }
   } else {
     for (int i = tid; i < B; i += blockDim.x) a.req_status[i] = 0;
+  }
+  __syncthreads();
+  if (a.flat) {
+    // first target / draft row of every request in the flattened layout (a bad length counts
+    // as no rows): exclusive prefix sums of L_i + 1 and L_i, block by block.  Thread tid
+    // handles requests b0 + tid, as when the status words were set above.
+    long long carry_t = 0, carry_d = 0;
+    for (int b0 = 0; b0 < B; b0 += blockDim.x) {
+      const int i = b0 + tid;
+      const int L = (i < B) ? (a.lengths ? a.lengths[i] : G) : -1;
+      const long long nt = (L >= 0 && L <= G) ? L + 1 : 0, nd = (L >= 0 && L <= G) ? L : 0;
+      const long long it = wave_inclusive_sum_i64(nt, lane), id = wave_inclusive_sum_i64(nd, lane);
+      __syncthreads();
+      if (lane == 63) {
+        woff_t[wave] = it;
+        woff_d[wave] = id;
+      }
+      __syncthreads();
+      long long bt = carry_t, bd = carry_d, tt = 0, td = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        if (w < wave) {
+          bt += woff_t[w];
+          bd += woff_d[w];
+        }
+        tt += woff_t[w];
+        td += woff_d[w];
+      }
+      if (i < B) {
+        const long long t0 = bt + it - nt, d0 = bd + id - nd;
+        a.t_off[i] = t0;
+        a.d_off[i] = d0;
+        // rows the caller did not pass: the request is marked and gets no work items
+        if (t0 + nt > a.flat_trows || d0 + nd > a.flat_drows) a.req_status[i] |= SPEC_REQ_BAD_ROWS;
+      }
+      carry_t += tt;
+      carry_d += td;
+    }
   }
   __syncthreads();   // the marks are read below (global memory, this workgroup)
   for (int i = tid; i < B; i += blockDim.x) {
@@ -871,8 +876,19 @@ bool shape_ok(int B, int G, int V, int dtype) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A launch's work-item count (workgroups x threads) must fit the 32-bit grid size of the dispatch
+// packet.
+static bool grid_fits(uint64_t groups, uint64_t threads) { return groups * threads <= 0xffffffffull; }
+
 int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size_t extra_bytes, char** extra) {
   a.nseg = stream_segments(a.V, dtype == SPEC_BF16 ? 2 : 4);
+  // the largest grids of the call: the streaming kernel's (work items x segments), the fused
+  // emit's (a 1024-thread workgroup per request) and the combine's (a thread per item)
+  uint64_t items = (uint64_t)a.B * (uint64_t)(a.G + 1);
+  if (a.max_items > 0 && (uint64_t)a.max_items < items) items = (uint64_t)a.max_items;
+  if (!grid_fits(items * (uint64_t)a.nseg, kStreamThreads) || !grid_fits((uint64_t)a.B, kFusedThreads) ||
+      !grid_fits((uint64_t)a.B * (uint64_t)(a.G + 1), 1))
+    return SPEC_ERR_UNSUPPORTED;
   // greedy and overlap calls have no emit ranges
   const WsLayout l = ws_layout(a.B, a.G, (a.greedy_only || a.overlap_only) ? 1 : a.V, a.nseg);
   if (!ws || ws_bytes < l.total + extra_bytes) return SPEC_ERR_WORKSPACE;
@@ -1014,7 +1030,8 @@ extern "C" int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtyp
 }
 
 extern "C" int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_rows,
-                                    const void* draft_rows, const int32_t* draft_tokens, const int32_t* lengths,
+                                    int64_t target_row_count, const void* draft_rows, int64_t draft_row_count,
+                                    const int32_t* draft_tokens, const int32_t* lengths,
                                     const float* temperature, const int32_t* top_k, const uint64_t* seed,
                                     int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
                                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
@@ -1023,8 +1040,10 @@ extern "C" int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t
       !out_tokens)
     return SPEC_ERR_INVALID_ARG;
   if (!aligned16(target_rows) || !aligned16(draft_rows)) return SPEC_ERR_INVALID_ARG;
+  if (target_row_count < 0 || draft_row_count < 0) return SPEC_ERR_INVALID_ARG;
   VerifyArgs a{};
   a.B = B; a.G = gamma; a.V = V; a.greedy_only = 0; a.flat = 1;
+  a.flat_trows = target_row_count; a.flat_drows = draft_row_count;
   a.target = target_rows; a.draft = draft_rows; a.tokens = draft_tokens; a.lengths = lengths;
   a.temperature = temperature; a.top_k = top_k; a.seed = seed;
   a.num_accepted = num_accepted; a.out_tokens = out_tokens; a.accept_prob = accept_prob; a.status = status;

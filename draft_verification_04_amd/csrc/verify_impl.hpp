@@ -80,6 +80,8 @@ struct VerifyArgs {
   int32_t* amb;        // [B, kAmbCap]
   int64_t* t_off;      // [B] flattened layout: first target row of request i (else unused)
   int64_t* d_off;      // [B] flattened layout: first draft row of request i
+  int64_t flat_trows;  // flattened layout: target rows and draft rows the caller passed
+  int64_t flat_drows;
   int r0, r1;          // the emit kernels handle requests [r0, r1)
   int emit_segs;       // emit-pass workgroups per request (1 = one fused workgroup, else 2 .. kMaxEmitSegs)
   int max_items;       // caller's bound on the number of work items (0: none); sizes the streaming grid

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 /* Call status (return value of every entry point). */
 enum {
@@ -87,6 +87,7 @@ enum {
 #define SPEC_REQ_BAD_TOPK 16        /* top_k[i] < 0 */
 #define SPEC_REQ_BAD_CONFIDENCE 32  /* scheduler: a confidence outside [0, 1] or NaN */
 #define SPEC_REQ_OVER_BUDGET 64     /* spec_verify_bounded: the request's rows did not fit the token cap */
+#define SPEC_REQ_BAD_ROWS 128      /* spec_verify_flat: the request's rows lie past the row counts passed */
 
 /* Limits of this library. */
 #define SPEC_MAX_GAMMA 64
@@ -136,6 +137,12 @@ const char* spec_status_string(int32_t status);
  *   workspace        device scratch of at least spec_verify_workspace_size(B, gamma, V)
  *                    bytes, 256-byte aligned; owned by the caller; must not be used
  *                    by another call in flight.
+ * Size limit
+ *   SPEC_ERR_UNSUPPORTED (before anything is enqueued) when a launch would pass
+ *   2^32 work-items: the row-streaming kernel runs one 512-thread workgroup per
+ *   (row pair, segment of about 48 KB), so B * (gamma + 1) * max(1, V * elem /
+ *   49152, at most 16) must stay below 2^23 (e.g. B = 500000, gamma = 16,
+ *   V = 1000 fp32 is refused), and B below 2^22.
  */
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V);
 
@@ -196,12 +203,17 @@ int32_t spec_verify_bounded(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
  *               row D_i = sum_{j<i} L_j.
  * `lengths` is required (it defines the layout); a length outside [0, gamma]
  * makes that request BAD_LENGTH and counts as no rows.  The row offsets are
- * derived on the device.  Everything else -- arguments, outputs, status,
- * workspace (spec_verify_workspace_size), errors -- as for spec_verify, and the
- * results equal spec_verify's on the padded layout holding the same rows.
+ * derived on the device.  target_row_count and draft_row_count (>= 0) are the
+ * numbers of rows the two buffers hold: a request whose rows would lie past
+ * either is not read and gets SPEC_REQ_BAD_ROWS (the lengths live on the
+ * device, so the library cannot refuse the call up front without a sync).
+ * Everything else -- arguments, outputs, status, workspace
+ * (spec_verify_workspace_size), errors -- as for spec_verify, and the results
+ * equal spec_verify's on the padded layout holding the same rows.
  */
 int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_rows,
-                         const void* draft_rows, const int32_t* draft_tokens, const int32_t* lengths,
+                         int64_t target_row_count, const void* draft_rows, int64_t draft_row_count,
+                         const int32_t* draft_tokens, const int32_t* lengths,
                          const float* temperature, const int32_t* top_k, const uint64_t* seed,
                          int32_t* num_accepted, int32_t* out_tokens, float* accept_prob, int32_t* status,
                          void* workspace, size_t workspace_bytes, void* stream);

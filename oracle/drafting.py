@@ -32,15 +32,8 @@ infinite), bad token (anchor outside [0, V)), non-finite (a stored row with
 a NaN or +inf, or no finite logit).  A request with a status keeps tokens -1
 and confidences NaN; its logits are not defined.
 
-Flags (comparison aid, as in `verify`): a draw is flagged when u * W lies
-within `window` of either end of the chosen interval, window = 1e-10 * W
-plus, when an accumulation error bound e is given, twice the total weight the
-ambiguous elements could move.  An element is ambiguous when the rounding of
-its exact value to the storage type is not the same across [z - e, z + e];
-any stored value from round(z - e) to round(z + e) is then possible (near
-zero, where U and the bias cancel, that range can span several values).  A
-greedy decision is flagged when an ambiguous element could change the
-argmax.
+Flags (as in `verify`): a draw is flagged when u * W lies within 1e-10 * W of
+either end of the chosen CDF interval; `margin` reports that distance / W.
 """
 
 import numpy as np
@@ -92,38 +85,21 @@ def _inverse_cdf_margin(w, u):
     return tk, min(t - lo, C[tk] - t), W
 
 
-def _greedy_ambiguous(z, zlo, zhi, amb):
-    """True when some choice of values within the ambiguous elements' ranges could move the
-    first-occurrence argmax of z."""
-    top = int(np.argmax(z))
-    hi = np.where(amb, zhi, z)
-    lo_top = zlo[top] if amb[top] else z[top]
-    others = hi.copy()
-    others[top] = -np.inf
-    best = others.max()
-    if lo_top > best:
-        return False
-    if lo_top < best:
-        return True
-    return bool(np.any(np.nonzero(others == best)[0] < top))
-
-
 def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None, conf_w=None,
-                 store="bf16", acc_err_unit=None, requests=None, conf_tau=None):
+                 store="bf16", requests=None, conf_tau=None, first_request=0):
     """Draft G tokens per request (see the module docstring).
 
     base [B, G, V] (U); W1 [V, r]; W2t [V, r]; anchor [B]; temperature [B] (default 1);
     seed [B] uint64 bit patterns (default 0); hidden [B, G, d] and conf_w [d + r] (conf_w alone
-    when d = 0; no confidences without conf_w); store "bf16" | "fp32"; acc_err_unit: unit
-    roundoff u of the arithmetic being compared (None: no ambiguity), the bound per element
-    being (r + 2) u (sum_j |W1 W2t| + |U|).
+    when d = 0; no confidences without conf_w); store "bf16" | "fp32".
     `requests` restricts the work to a subset (others keep status 0, tokens -1); conf_tau [G]
-    the per-position temperatures of the confidences (default 1).
+    the per-position temperatures of the confidences (default 1); first_request: the batch
+    index of row 0 of these arrays (the draft uniform is keyed by the batch index, so a slice of
+    a batch gives that batch's draws).
 
     Returns a dict: tokens [B, G] int64, logits [B, G, V] fp64 (stored values; NaN where not
-    computed), amb_lo / amb_hi [B, G, V] (the range of possible stored values of ambiguous
-    elements, NaN elsewhere), conf [B, G], status [B], flag [B, G] bool, margin [B, G] (u*W
-    distance / W; inf for greedy).
+    computed), conf [B, G], status [B], flag [B, G] bool, margin [B, G] (u*W distance / W; inf
+    for greedy).
     """
     B, G, V = base.shape
     W1 = _as_np(W1).astype(np.float64)
@@ -141,8 +117,6 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
     ctau = np.ones(G) if conf_tau is None else _as_np(conf_tau).astype(np.float64)
     tokens = np.full((B, G), -1, dtype=np.int64)
     logits = np.full((B, G, V), np.nan)
-    amb_lo = np.full((B, G, V), np.nan)
-    amb_hi = np.full((B, G, V), np.nan)
     conf = np.full((B, G), np.nan)
     status = np.zeros(B, dtype=np.int64)
     flag = np.zeros((B, G), dtype=bool)
@@ -170,14 +144,6 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
             if _bad_rows(z[None])[0]:
                 st |= STATUS_NONFINITE
                 break
-            amb = np.zeros(V, dtype=bool)
-            zlo = zhi = z
-            if acc_err_unit is not None:
-                e = (r + 2) * acc_err_unit * (np.abs(W2t) @ np.abs(a) + np.abs(U[k]))
-                zlo, zhi = round_store(zx - e, store), round_store(zx + e, store)
-                amb = zlo != zhi
-                amb_lo[i, k] = np.where(amb, zlo, np.nan)
-                amb_hi[i, k] = np.where(amb, zhi, np.nan)
             if wc is not None:
                 dh = len(wc) - r
                 t = float(wc[dh:] @ a)                                       # Eq. 7
@@ -186,23 +152,18 @@ def markov_draft(base, W1, W2t, anchor, temperature=None, seed=None, hidden=None
                 conf[i, k] = 1.0 / (1.0 + np.exp(-t / ctau[k]))
             if T == 0.0:
                 xk = int(np.argmax(z))
-                flag[i, k] = bool(amb.any()) and _greedy_ambiguous(z, zlo, zhi, amb)
             else:
                 y = z / T
                 ymax = np.max(y)
                 w = np.exp(y - ymax)
-                u = float(draft_uniform(Ss[i], i, k))
+                u = float(draft_uniform(Ss[i], first_request + i, k))
                 xk, mg, W = _inverse_cdf_margin(w, u)
-                window = FLAG_EMIT_WINDOW * W
-                if amb.any():
-                    window += 2.0 * (np.exp(zhi[amb] / T - ymax) - np.exp(zlo[amb] / T - ymax)).sum()
                 margin[i, k] = mg / W
-                flag[i, k] = mg < window
+                flag[i, k] = mg < FLAG_EMIT_WINDOW * W
             tokens[i, k] = xk
             prev = xk
         status[i] = st
         if st:
             tokens[i] = -1
             conf[i] = np.nan
-    return dict(tokens=tokens, logits=logits, amb_lo=amb_lo, amb_hi=amb_hi, conf=conf, status=status,
-                flag=flag, margin=margin)
+    return dict(tokens=tokens, logits=logits, conf=conf, status=status, flag=flag, margin=margin)

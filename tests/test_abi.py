@@ -53,7 +53,7 @@ def test_binding_covers_every_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     for code, text in ((0, "ok"), (1, "invalid argument"), (2, "workspace"), (3, "unsupported"), (4, "HIP")):
         assert text in lib.spec_status_string(code).decode()
     assert lib.spec_status_string(99).decode() == "unknown status"
@@ -178,12 +178,37 @@ def test_async_scheduler_rejects_bad_arguments(lib):
 def test_verify_flat_requires_lengths(lib):
     keep, p = _fake()
     ws = lib.spec_verify_workspace_size(2, 4, 100)
-    args = [2, 4, 100, 1, p, p, p, p, p, None, p, p, p, None, None, p, ws, None]
+    # B, gamma, V, dtype, target_rows, n_target_rows, draft_rows, n_draft_rows, tokens, lengths, T, top_k,
+    # seed, n, out_tokens, accept_prob, status, ws, ws_bytes, stream
+    args = [2, 4, 100, 1, p, 10, p, 8, p, p, p, None, p, p, p, None, None, p, ws, None]
     assert lib.spec_verify_flat(*args) == 2                      # fake workspace is refused
-    bad = list(args); bad[7] = None
+    bad = list(args); bad[9] = None
     assert lib.spec_verify_flat(*bad) == 1                       # no lengths
-    bad = list(args); bad[5] = ctypes.c_void_p(p.value + 2)
+    bad = list(args); bad[6] = ctypes.c_void_p(p.value + 2)
     assert lib.spec_verify_flat(*bad) == 1                       # misaligned rows
+    bad = list(args); bad[5] = -1
+    assert lib.spec_verify_flat(*bad) == 1                       # negative row count
+    bad = list(args); bad[7] = -1
+    assert lib.spec_verify_flat(*bad) == 1
+
+
+def test_launch_size_bound(lib):
+    """A call whose streaming grid would pass 2^32 work-items (one 512-thread workgroup per row
+    pair and ~48 KB segment) is refused with SPEC_ERR_UNSUPPORTED before anything is enqueued,
+    here with a host buffer as every pointer (a launch would fault on it)."""
+    keep, p = _fake()
+    big = (500000, 16, 1000, 0)          # ~66 GB of fp32 logits: fits in HBM, not in one grid
+    ok = (250000, 15, 1000, 0)           # 4 M rows x 1 segment x 512 = 2^31 work-items
+    for (B, G, V, dt), want in ((big, 3), (ok, 2)):
+        args = [B, G, V, dt, p, p, p, None, p, None, p, p, p, None, None, p, 1 << 40, None]
+        assert lib.spec_verify(*args) == want, (B, G, V)
+        # the token cap sizes the grid: a small cap fits
+        assert lib.spec_verify_bounded(*args, 4096, None, None) == (2 if B < 4194304 else 3)
+    # the fused emit runs a 1024-thread workgroup per request: B >= 2^22 cannot launch
+    args = [1 << 22, 1, 8, 1, p, p, p, None, p, None, p, p, p, None, None, p, 1 << 40, None]
+    assert lib.spec_verify_bounded(*args, 16, None, None) == 3
+    assert lib.spec_verify_greedy(500000, 16, 1000, 0, p, p, None, p, p, None, p, 1 << 40, None) == 3
+    assert lib.spec_overlap_mass(500000, 16, 1000, 0, p, p, None, p, None, p, None, p, 1 << 40, None) == 3
 
 
 def test_verify_bounded_rejects_a_bound_below_one(lib):
@@ -302,3 +327,72 @@ def test_binding_refuses_host_tensors(lib):
         sv.schedule_verify(t, d, x, conf, sps, 4)
     with pytest.raises(TypeError):
         sv.schedule_lengths(conf, sps, 4)
+
+
+def test_binding_checks_shapes_before_devices(lib):
+    """Per-request vectors must hold B values and `out` tensors the shapes and dtypes the kernels
+    write: the binding raises ValueError before any device check (host tensors suffice here)."""
+    import torch
+    import draft_verification_04_amd as sv
+    B, G, V = 3, 4, 32
+    t = torch.zeros((B, G + 1, V))
+    d = torch.zeros((B, G, V))
+    x = torch.zeros((B, G), dtype=torch.int32)
+    L = torch.zeros(B, dtype=torch.int32)
+    for kw in (dict(lengths=torch.zeros(B + 1, dtype=torch.int32)), dict(temperature=torch.ones(B - 1)),
+               dict(top_k=torch.zeros((B, 1), dtype=torch.int32)), dict(seed=torch.zeros(2 * B, dtype=torch.int64))):
+        with pytest.raises(ValueError):
+            sv.verify(t, d, x, **kw)
+    with pytest.raises(ValueError):
+        sv.verify(t, d[:, :G - 1], x)
+    with pytest.raises(ValueError):
+        sv.verify(t, d, x[:, :G - 1])
+    with pytest.raises(ValueError):
+        sv.verify_greedy(t, x, lengths=torch.zeros(B - 1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sv.verify_flat(t[0], d[0], x, None)                  # lengths define the layout
+    with pytest.raises(ValueError):
+        sv.verify_flat(t[0], d[0], x, torch.zeros(B + 2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sv.verify_flat(t[0], d[0, :, :V - 1], x, L)
+    with pytest.raises(ValueError):
+        sv.overlap_mass(t, d, lengths=torch.zeros(B + 1, dtype=torch.int32))
+    conf = torch.zeros((B, G))
+    sps = torch.zeros(B * (G + 1) + 1, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        sv.schedule_verify(t, d, x, conf[:, :G - 1], sps, 8)
+    with pytest.raises(ValueError):
+        sv.schedule_topk(conf, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sv.sts_apply(conf, torch.ones(G + 1, dtype=torch.float64))
+    W = torch.zeros((V, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sv.draft_markov(d, W, W[:V - 1], torch.zeros(B, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sv.draft_markov(d, W, W, torch.zeros(B + 1, dtype=torch.int32))
+
+
+def test_binding_checks_caller_outputs():
+    """A caller's `out` tensors are checked for shape, dtype and device before the call."""
+    import torch
+    import draft_verification_04_amd as sv
+    B, G, dev = 3, 4, torch.device("cpu")
+    good = dict(num_accepted=torch.zeros(B, dtype=torch.int32), out_tokens=torch.zeros((B, G + 1), dtype=torch.int32),
+                accept_prob=torch.zeros((B, G)), status=torch.zeros(B, dtype=torch.int32))
+    spec = sv._verify_out_spec(B, G)
+    assert sv._check_out(dict(good), spec, dev) is not None
+    assert sv._check_out(dict(good, accept_prob=None, status=None), spec, dev) is not None   # optional
+    for key, bad in (("out_tokens", torch.zeros((B, G), dtype=torch.int32)),
+                     ("num_accepted", torch.zeros(B + 1, dtype=torch.int32)),
+                     ("accept_prob", torch.zeros((B, G + 1))),
+                     ("status", torch.zeros((B, 1), dtype=torch.int32))):
+        with pytest.raises(ValueError):
+            sv._check_out(dict(good, **{key: bad}), spec, dev)
+    with pytest.raises(TypeError):
+        sv._check_out(dict(good, out_tokens=torch.zeros((B, G + 1), dtype=torch.int64)), spec, dev)
+    with pytest.raises(TypeError):
+        sv._check_out(dict(good, accept_prob=torch.zeros((B, G), dtype=torch.float64)), spec, dev)
+    with pytest.raises(ValueError):
+        sv._check_out(dict(good, num_accepted=None), spec, dev)                   # required
+    with pytest.raises(ValueError):
+        sv._check_out(dict(good), spec, torch.device("meta"))                    # another device

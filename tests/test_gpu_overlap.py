@@ -12,7 +12,7 @@ import torch
 pytestmark = pytest.mark.gpu
 
 import oracle
-from parity import to_np
+from parity import _host, pool_map, request_blocks, to_np
 from workloads import make_workload
 
 DEV = "cuda:0"
@@ -102,8 +102,11 @@ def test_disjoint_top_k_supports(sv):
     assert abs(got[1, 0] - ref[1, 0]) <= RTOL * ref[1, 0] + ATOL
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["scheduled", "mixed"])
-def test_full_size_sampled(sv, name):
+def test_full_size_all_requests(sv, name):
+    """Every request of the full-size workload (the scheduled one at its scheduled lengths)
+    against the oracle, in blocks of requests over forked host processes."""
     w = make_workload(name, DEV)
     if w.conf is not None:
         s = sv.schedule_lengths(w.conf, torch.from_numpy(w.sps).to(DEV), w.budget)
@@ -111,9 +114,20 @@ def test_full_size_sampled(sv, name):
     else:
         L = None
     got, st = _gpu(sv, w, L)
-    rng = np.random.default_rng(63)
-    idx = np.sort(rng.choice(w.B, 24, replace=False))
-    sub = lambda x: None if x is None else x[torch.from_numpy(idx).to(x.device)]
-    ref = oracle.overlap_mass(sub(w.target), sub(w.draft), sub(L), sub(w.temperature), sub(w.top_k))
-    _check(got[idx], ref["overlap"], st[idx], ref["status"])
+    t, d = _host(w.target), _host(w.draft)
+    Lh = None if L is None else _host(L)
+    T = _host(w.temperature)
+    K = None if w.top_k is None else _host(w.top_k)
+    sl = lambda x, a, b: None if x is None else x[a:b]
+
+    def block(blk):
+        a, b = blk[0], blk[-1] + 1
+        return oracle.overlap_mass(t[a:b], d[a:b], sl(Lh, a, b), T[a:b], sl(K, a, b))
+
+    res = pool_map(block, request_blocks(w.B, 8))
+    ref = np.concatenate([r["overlap"] for r in res])
+    st_ref = np.concatenate([r["status"] for r in res])
+    _check(got, ref, st, st_ref)
     assert (st == 0).all()
+    print(f"overlap {name} full size: {int(np.isfinite(got).sum())} positions of {w.B} requests compared",
+          flush=True)

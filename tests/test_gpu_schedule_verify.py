@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle
 from oracle.scheduling import MODE_EARLY_STOP, MODE_GLOBAL
-from parity import to_np
+from parity import HostInputs, compare_verify, run_oracle_pooled, to_np
 from workloads import make_workload
 
 DEV = "cuda:0"
@@ -62,12 +62,20 @@ def test_scheduled_small(sv, mode):
     assert (to_np(f["status"]) == 0).all()
 
 
+@pytest.mark.timeout(900)
 def test_scheduled_full_size(sv):
-    # the scheduled workload at its full size (B = 256, gamma = 16, V = 151936, budget 2048)
+    """The scheduled workload at its full size (B = 256, gamma = 16, V = 151936, budget 2048), in
+    the very call the benchmark times: the lengths equal the oracle's schedule, and every request's
+    verification outputs are compared with the oracle's directly (not only with the two-call path)."""
     w = make_workload("scheduled", DEV)
     f = _check(sv, w, w.sps, w.budget, MODE_EARLY_STOP)
     assert (to_np(f["status"]) == 0).all()
     assert int((to_np(f["lengths"]) + 1).sum()) <= w.budget
+    L_ref, _ = oracle.schedule(w.conf.cpu().numpy(), w.sps, w.budget, MODE_EARLY_STOP)
+    h = HostInputs.of_workload(w, L_ref)
+    ref = run_oracle_pooled(h)
+    s = compare_verify(f, ref, inputs=h, bound=True)
+    print(f"scheduled full size: sum L = {int(L_ref.sum())}, {s}", flush=True)
 
 
 def test_mixed_recipe(sv):

@@ -2,8 +2,10 @@
 
 Small shapes run the oracle on every request; they span several 16-byte
 vectors per thread, several emit tiles, ragged rows (odd V, so rows start off
-16-byte boundaries) and every edge the method has.  The full workloads
-compare a sample of requests one by one.
+16-byte boundaries) and every edge the method has.  The full-size workloads
+compare every request with the oracle (run over a pool of host processes),
+check that each flagged request took an admissible outcome, and assert the
+flag bound (flagged draws under 1e-4 of draws).
 """
 
 import math
@@ -15,7 +17,7 @@ import torch
 pytestmark = pytest.mark.gpu
 
 import oracle
-from parity import compare_verify, run_oracle, to_np
+from parity import HostInputs, compare_verify, run_oracle, run_oracle_pooled, to_np
 from workloads import make_workload
 
 DEV = "cuda:0"
@@ -65,7 +67,7 @@ def test_verify_small_all_requests(sv, name, kw):
     w = make_workload(name, DEV, **kw)
     out = _run(sv, w)
     ref = run_oracle(w)
-    s = compare_verify(out, ref)
+    s = compare_verify(out, ref, inputs=HostInputs.of_workload(w))
     print(name, kw, s)
 
 
@@ -141,7 +143,7 @@ def test_verify_edge_cases(sv, rep, V, dtype):
     out = sv.verify(tt, dd, *args)
     torch.cuda.synchronize()
     ref = oracle.verify(tt, dd, x, L, T, K, seed)
-    compare_verify(out, ref)
+    compare_verify(out, ref, inputs=HostInputs.of(tt, dd, x, L, T, K, seed))
     st = to_np(out["status"]).reshape(rep, B)
     assert (st[:, 8] == oracle.STATUS_BAD_TOKEN).all() and (st[:, 9] == oracle.STATUS_BAD_TEMPERATURE).all()
     assert (st[:, 10] == oracle.STATUS_NONFINITE).all() and (st[:, 11] == 0).all()
@@ -181,8 +183,7 @@ def test_lossless_chi_square_on_gpu(sv, V):
         obs = np.bincount(tg[sel, k], minlength=V)
         assert stats.chisquare(obs, pt32[k] * sel.sum()).pvalue > 1e-4
     ref = oracle.verify(t, d, x)
-    s = compare_verify(out, ref)
-    assert s["flagged_draws"] < 1e-4 * s["draws"], s
+    compare_verify(out, ref, inputs=HostInputs.of(t, d, x), bound=True)
 
 
 @pytest.mark.parametrize("name,kw", [
@@ -201,52 +202,75 @@ def test_determinism(sv, name, kw):
                                                torch.equal(torch.nan_to_num(a[k]), torch.nan_to_num(b[k]))), k
 
 
-# ---- full workloads, sampled requests ----
+# ---- full workloads, every request ----
 
-def _sample(B, n, seed):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(B, size=min(n, B), replace=False))
+def _full(sv, name):
+    w = make_workload(name, DEV)
+    print(f"case {name}: B={w.B} gamma={w.gamma} V={w.V}", flush=True)
+    out = _run(sv, w)
+    h = HostInputs.of_workload(w)
+    ref = run_oracle_pooled(h)
+    s = compare_verify(out, ref, inputs=h, bound=True, check_prob=name != "greedy")
+    print(f"{name} full size: {s}", flush=True)
+    return s
 
 
+@pytest.mark.timeout(900)
 def test_full_mid_all_requests(sv):
-    w = make_workload("mid", DEV)
-    out = _run(sv, w)
-    ref = run_oracle(w)
-    s = compare_verify(out, ref)
-    print("mid", s)
+    _full(sv, "mid")
 
 
-def test_full_scheduled_sampled(sv):
-    w = make_workload("scheduled", DEV)
-    sps = torch.from_numpy(w.sps).to(DEV)
-    sch = sv.schedule_lengths(w.conf, sps, w.budget)
-    L = sch["lengths"]
-    out = sv.verify(w.target, w.draft, w.draft_tokens, L, w.temperature, None, w.seed)
-    torch.cuda.synchronize()
-    L_ref, th = oracle.schedule(w.conf.cpu().numpy(), w.sps, w.budget)
-    assert (to_np(L) == L_ref).all()
-    req = _sample(w.B, 24, 1)
-    ref = oracle.verify(w.target, w.draft, w.draft_tokens, L_ref, w.temperature, None, w.seed, requests=req)
-    s = compare_verify(out, ref, requests=req)
-    print("scheduled", int(L_ref.sum()), s)
-
-
-def test_full_greedy_sampled(sv):
-    w = make_workload("greedy", DEV)
-    out = _run(sv, w)
-    req = _sample(w.B, 48, 2)
-    ref = run_oracle(w, requests=req)
-    s = compare_verify(out, ref, requests=req, check_prob=False)
+@pytest.mark.timeout(900)
+def test_full_greedy_all_requests(sv):
+    s = _full(sv, "greedy")
     assert s["mismatches"] == 0
 
 
-def test_full_mixed_sampled(sv):
-    w = make_workload("mixed", DEV)
-    out = _run(sv, w)
-    req = _sample(w.B, 24, 3)
-    ref = run_oracle(w, requests=req)
-    s = compare_verify(out, ref, requests=req)
-    print("mixed", s)
+@pytest.mark.timeout(900)
+def test_full_mixed_all_requests(sv):
+    _full(sv, "mixed")
+
+
+def test_draft_token_outside_the_draft_top_k(sv):
+    """The edge rules of the ratio (DSpark paper, §2.1, with top-k): a draft token outside the
+    draft's kept set but inside the target's has p_d(x) = 0 < p_t(x), so r = 1 and it is always
+    accepted; one inside the draft's kept set but outside the target's has r = 0 and is always
+    rejected."""
+    rng = np.random.default_rng(44)
+    B, G, V, K = 64, 4, 5000, 5
+    t = rng.normal(0, 3, (B, G + 1, V)).astype(np.float32)
+    d = t[:, :G] + rng.normal(0, 0.5, (B, G, V)).astype(np.float32)
+    x = np.zeros((B, G), dtype=np.int32)
+    want = np.zeros((B, G))
+    for i in range(B):
+        for k in range(G):
+            top_t = np.argsort(-t[i, k], kind="stable")[:K]
+            if (i + k) % 2 == 0:
+                v = int(top_t[1])
+                d[i, k, v] = -20.0          # out of the draft's top-k, still in the target's
+                want[i, k] = 1.0
+            else:
+                v = int(np.argsort(-d[i, k], kind="stable")[0])
+                t[i, k, v] = -20.0          # in the draft's top-k, out of the target's
+                want[i, k] = 0.0
+            x[i, k] = v
+    Kv = np.full(B, K, dtype=np.int32)
+    T = rng.uniform(0.6, 1.2, B).astype(np.float32)
+    seed = rng.integers(0, 2 ** 63, B).astype(np.int64)
+    for dt in (torch.float32, torch.bfloat16):
+        tt = torch.from_numpy(t).to(DEV).to(dt)
+        dd = torch.from_numpy(d).to(DEV).to(dt)
+        args = [torch.from_numpy(a).to(DEV) for a in (x, np.full(B, G, np.int32), T, Kv, seed)]
+        out = sv.verify(tt, dd, *args)
+        torch.cuda.synchronize()
+        ref = oracle.verify(tt, dd, x, None, T, Kv, seed)
+        compare_verify(out, ref, inputs=HostInputs.of(tt, dd, x, None, T, Kv, seed))
+        r = to_np(out["accept_prob"])
+        assert (ref["accept_prob"] == want).all()
+        assert (r == want).all()
+        n = to_np(out["num_accepted"])
+        first = np.where((want == 0).any(axis=1), np.argmax(want == 0, axis=1), G)
+        assert (n == first).all()
 
 
 def test_nearly_identical_rows_take_the_exact_residual_path(sv):

@@ -8,7 +8,8 @@ design notes; the short form:
   tiny       B=1,    gamma=4,  V=1000,   fp32  target N(0,2); draft = target + N(0,0.5); T=1
   mid        B=32,   gamma=16, V=151936, bf16  target N(0,3) + 8 on one random token per row;
                                                 draft_k = target_k + N(0, 0.3 + 0.08 k)  (k from 0)
-  scheduled  B=256,  gamma=16, V=151936, bf16  logits as `mid`; c_k = sigmoid(N(1.5-0.15k, 1)), k from 1;
+  scheduled  B=256,  gamma=16, V=151936, bf16  logits as `tiny`: target N(0,2), draft = target + N(0,0.5);
+                                                c_k = sigmoid(N(1.5-0.15k, 1)), k from 1;
                                                 8-point concave throughput table; budget 2048 tokens
   greedy     B=512,  gamma=16, V=129280, bf16  target N(0,3); T=0; x_k = target argmax w.p. 0.9^k
                                                 (k from 1) else uniform over the vocabulary
@@ -33,8 +34,8 @@ CONFIGS = {
                  noise=("const", 0.5), temp=("const", 1.0), top_k=0, seeds="zero", seed=1001),
     "mid": dict(B=32, gamma=16, V=151936, dtype="bf16", target_std=3.0, spike=8.0,
                 noise=("linear", 0.3, 0.08), temp=("const", 1.0), top_k=0, seeds="zero", seed=1002),
-    "scheduled": dict(B=256, gamma=16, V=151936, dtype="bf16", target_std=3.0, spike=8.0,
-                      noise=("linear", 0.3, 0.08), temp=("const", 1.0), top_k=0, seeds="zero",
+    "scheduled": dict(B=256, gamma=16, V=151936, dtype="bf16", target_std=2.0, spike=0.0,
+                      noise=("const", 0.5), temp=("const", 1.0), top_k=0, seeds="zero",
                       seed=1003, budget=2048, table_seed=3003),
     "greedy": dict(B=512, gamma=16, V=129280, dtype="bf16", target_std=3.0, spike=0.0,
                    noise=None, temp=("const", 0.0), top_k=0, seeds="zero", seed=1004,
