@@ -219,10 +219,14 @@ int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t dtype, con
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * spec_verify_greedy -- greedy verification.  a_k = argmax of raw target row k
- * (lowest token id on ties); n = first k < L_i with x_k != a_k, else L_i;
- * out_tokens = x_0 .. x_{n-1}, a_n, then -1.  Draft logits are never read.
- * Arguments and outputs as for spec_verify (no temperature, top-k or seed).
+ * spec_verify_greedy -- greedy verification, the argmax rule the DSpark paper
+ * names beside rejection sampling in its related work (§6, parallel generation:
+ * a drafter without exact per-token probabilities is limited to it).
+ * a_k = argmax of raw target row k (lowest token id on ties); n = first
+ * k < L_i with x_k != a_k, else L_i; out_tokens = x_0 .. x_{n-1}, a_n, then -1.
+ * Draft logits are never read.  Arguments and outputs as for spec_verify (no
+ * temperature, top-k or seed); the workspace is sized by
+ * spec_verify_greedy_workspace_size.
  */
 size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma);
 

@@ -21,14 +21,17 @@ from oracle.verification import FLAG_EMIT_WINDOW
 FP32_UNIT = 2.0 ** -23
 
 
-def rounding_ranges(U_row, W1, W2t, prev, store, unit=FP32_UNIT):
+def rounding_ranges(U_row, W1, W2t, prev, store, unit=FP32_UNIT, absW2t=None):
     """(zlo, zhi, amb) for one row: the stored values of z - e and z + e, and the elements where
-    they differ (U_row [V], W1 and W2t [V, r] fp64, prev = x_{k-1})."""
+    they differ (U_row [V], W1 and W2t [V, r] fp64, prev = x_{k-1}; absW2t = |W2t| when the
+    caller keeps it)."""
     r = W1.shape[1]
     a = W1[prev]
+    if absW2t is None:
+        absW2t = np.abs(W2t)
     with np.errstate(all="ignore"):
         zx = U_row + W2t @ a
-        e = (r + 2) * unit * (np.abs(W2t) @ np.abs(a) + np.abs(U_row))
+        e = (r + 2) * unit * (absW2t @ np.abs(a) + np.abs(U_row))
     zlo, zhi = round_store(zx - e, store), round_store(zx + e, store)
     return zlo, zhi, zlo != zhi
 

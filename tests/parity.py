@@ -204,8 +204,11 @@ _POOL_FN = {}
 
 
 def _pool_task(i):
+    # one BLAS thread per worker: the pool already has a process per core
+    from threadpoolctl import threadpool_limits
     blk = _POOL_FN["blocks"][i]
-    return i, _POOL_FN["fn"](blk)
+    with threadpool_limits(1):
+        return i, _POOL_FN["fn"](blk)
 
 
 def pool_workers():
@@ -219,12 +222,18 @@ def pool_map(fn, blocks, workers=None):
     fn and whatever host arrays it closes over (nothing is pickled on the way in); they run numpy
     only and never touch the GPU."""
     import multiprocessing as mp
+    import sys
+    import time
     results = [None] * len(blocks)
     _POOL_FN.update(fn=fn, blocks=blocks)
+    t0 = time.time()
     try:
         with mp.get_context("fork").Pool(workers or pool_workers()) as p:
-            for i, res in p.imap_unordered(_pool_task, range(len(blocks)), chunksize=1):
+            for done, (i, res) in enumerate(p.imap_unordered(_pool_task, range(len(blocks)), chunksize=1), 1):
                 results[i] = res
+                if done % max(1, len(blocks) // 4) == 0:
+                    print(f"  oracle blocks {done}/{len(blocks)} in {time.time() - t0:.1f} s", flush=True)
+                    sys.stdout.flush()
     finally:
         _POOL_FN.clear()
     return results
