@@ -52,6 +52,7 @@ EXPORTS = {
                                   _P, _P]),
     "spec_verify_bounded": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P,
                                  _I, _P, _P]),
+    "spec_verify_static": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "spec_verify_flat": (_I, [_I, _I, _I, _I, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
                               _P, _P, _P, _Z, _P]),
     "spec_verify_greedy_workspace_size": (_Z, [_I, _I]),
@@ -307,6 +308,28 @@ def verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
             return lib.spec_verify_profiled(*args, ev0, ev1)
         return lib.spec_verify_bounded(*args, int(max_tokens), ev0, ev1)
     _check("spec_verify", _launch(stream, mine, call))
+    return out
+
+
+def verify_static(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                  lengths: Optional[torch.Tensor] = None, temperature: Optional[torch.Tensor] = None,
+                  top_k: Optional[torch.Tensor] = None, seed: Optional[torch.Tensor] = None,
+                  out: dict = None, stream=None) -> dict:
+    """spec_verify_static: spec_verify with the library's own device workspace (no allocation in
+    the call).  `out` (num_accepted, out_tokens, and optionally accept_prob and status) and the
+    temperature and seed tensors are required here, since the binding must not allocate either;
+    calls that overlap in time on one GPU race (see the header)."""
+    lib = load_library()
+    if out is None or temperature is None or seed is None:
+        raise ValueError("verify_static allocates nothing: pass out, temperature and seed")
+    B, G, V, temperature, seed, mine = _verify_inputs(target, draft, draft_tokens, lengths, temperature, top_k,
+                                                      seed)
+    out = _verify_outputs(B, G, target.device, out, mine)
+    code = _launch(stream, mine, lambda sp: lib.spec_verify_static(
+        B, G, V, _logit_dtype(target), _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(lengths),
+        _ptr(temperature), _ptr(top_k), _ptr(seed), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("accept_prob")), _ptr(out.get("status")), sp))
+    _check("spec_verify_static", code)
     return out
 
 

@@ -25,6 +25,7 @@
 #include "spec_verify.h"
 
 #include <algorithm>
+#include <mutex>
 
 #include <float.h>
 #include <math.h>
@@ -1027,6 +1028,60 @@ extern "C" int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtyp
   return spec_verify_profiled(B, gamma, V, dtype, target_logits, draft_logits, draft_tokens, lengths, temperature,
                               top_k, seed, num_accepted, out_tokens, accept_prob, status, workspace,
                               workspace_bytes, stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// spec_verify_static: spec_verify with its workspace in a file-scope device array
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// The workspace of spec_verify_static.  Each GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  Host code never uses this name as an address (on the host it
+// is a stand-in symbol): it asks the runtime for the device address once per device.
+static __device__ __align__(256) unsigned char scratch[SPEC_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the calling thread's current device, looked up on the first
+// call made with that device current and kept.
+int32_t static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return SPEC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SPEC_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t spec_verify_static(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,
+                                      const void* draft_logits, const int32_t* draft_tokens, const int32_t* lengths,
+                                      const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                                      int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                                      int32_t* status, void* stream) {
+  if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
+  if (!target_logits || !draft_logits || !draft_tokens || !temperature || !seed || !num_accepted || !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned16(target_logits) || !aligned16(draft_logits)) return SPEC_ERR_INVALID_ARG;
+  // a shape whose workspace does not fit the array is refused before any HIP call
+  if (workspace_bytes(B, gamma, V, true) > (size_t)SPEC_STATIC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int32_t rc = static_scratch(&ws);
+  if (rc != SPEC_OK) return rc;
+  // every workspace word the kernels read is written earlier in the same call (the work list
+  // sets the item count, the status words and the emit counters), so nothing is cleared here
+  return verify_entry(B, gamma, V, dtype, target_logits, draft_logits, draft_tokens, lengths, temperature, top_k,
+                      seed, num_accepted, out_tokens, accept_prob, status, ws, (size_t)SPEC_STATIC_SCRATCH_BYTES,
+                      stream, 0, nullptr, nullptr);
 }
 
 extern "C" int32_t spec_verify_flat(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_rows,

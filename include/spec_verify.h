@@ -25,7 +25,9 @@
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
  *     tensor's storage).  Scalars are passed by value.  The caller owns all
- *     memory; the library keeps no state between calls and never allocates.
+ *     memory; the library keeps no state between calls and never allocates
+ *     (spec_verify_static alone keeps its workspace in a device array of the
+ *     library, see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it asynchronously; nothing synchronises the host.
  *   - Return value: SPEC_OK, or an error code returned synchronously before
@@ -152,6 +154,37 @@ int32_t spec_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                     const float* temperature, const int32_t* top_k, const uint64_t* seed,
                     int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_static -- spec_verify for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, outputs, status words and results as
+ * spec_verify, without the workspace arguments.  The workspace is a
+ * file-scope device array of SPEC_STATIC_SCRATCH_BYTES bytes inside the
+ * library; each GPU holds its own copy until the process ends.  The call
+ * allocates nothing (no hipMalloc, no library allocation).
+ *   - It runs on the calling thread's current device, which must be the
+ *     device of `stream` and of every pointer.  The first call with a device
+ *     current looks up that device's copy of the array (hipGetSymbolAddress)
+ *     and keeps its address.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other threads) race and give wrong
+ *     results.  Calls on one stream are ordered and safe.  The array keeps
+ *     the last call's contents; the kernels write every word they read, so
+ *     nothing needs clearing between calls.
+ *   - SPEC_ERR_WORKSPACE, before any HIP call, when the shape needs more than
+ *     SPEC_STATIC_SCRATCH_BYTES of workspace (spec_verify_workspace_size(B,
+ *     gamma, V) > SPEC_STATIC_SCRATCH_BYTES; e.g. B = 256, gamma = 16,
+ *     V = 151936 needs 4.2 MiB and B = 1024, gamma = 8, V = 129280 9.9 MiB).
+ */
+#define SPEC_STATIC_SCRATCH_BYTES (32u << 20)
+
+int32_t spec_verify_static(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                           const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const int32_t* lengths,
+                           const float* temperature, const int32_t* top_k, const uint64_t* seed,
+                           int32_t* num_accepted, int32_t* out_tokens, float* accept_prob,
+                           int32_t* status, void* stream);
 
 /*
  * spec_verify_profiled -- spec_verify, with two caller-created hipEvent_t
