@@ -39,7 +39,10 @@
 
 namespace spec {
 
-constexpr double kAmbTol = 1e-5;
+// Relative margin of the residual-sign classification with the streaming normalisers.  Their ratio
+// rho = cd * S_d / S_t is checked to lie within half of it (measured |rho - 1| <= 2.3e-7 on the
+// verification workloads); a wider margin records more tokens for the exact second look.
+constexpr double kAmbTol = 2e-6;
 constexpr int kSub = 512;                               // tokens per wave step (64 lanes x 8)
 constexpr int kSubPerRange = kRangeElems / kSub;        // 4
 
@@ -418,14 +421,16 @@ struct FinalShared {
   double St, Sd, target, before;
 };
 
-// Exact weight of token v: residual (resid) or Q(z_t) (target row, any scale).
+// Exact weight of token v: residual (resid) or Q(z_t) (target row, any scale).  iSt and iSd are
+// the reciprocals of the row sums S_t and S_d: p = Q * (1/S) to one rounding more than Q / S,
+// far below the precision the draw needs (range weights and the token walk use the same form).
 template <bool BF16>
-__device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, double St, double Sd,
+__device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, double iSt, double iSd,
                                          const double* T64) {
   const double qt = q_at<BF16>(e.t, v, e.tht, e.invT, e.R, T64, e.Qt);
   if (!resid) return qt;
   const double qd = q_at<BF16>(e.d, v, e.thd, e.invT, e.R, T64, e.Qt);
-  return fmax(0.0, qt / St - qd / Sd);
+  return fmax(0.0, qt * iSt - qd * iSd);
 }
 
 template <bool BF16, int NT>
@@ -478,6 +483,7 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
   double ua, ue;
   verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
   const double St = sh.St, Sd = sh.Sd;
+  const double iSt = 1.0 / St, iSd = 1.0 / Sd;
   // the sign classification assumed cd * S_d / S_t = 1 to within half its margin
   const double rho = resid ? e.cd * Sd / St : 1.0;
   const bool slow = resid && (!(fabs(rho - 1.0) <= 0.5 * kAmbTol) || sh.na > kAmbCap);
@@ -489,23 +495,34 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
     for (int r = tid; r < NR; r += NT) sh.corr[r] = 0.0;
     __syncthreads();
     for (int q = tid; q < na; q += NT) {
+      // rank by token id (the tokens are distinct): eight comparisons per step, reads in flight
       const int v = sh.amb_v[q];
       int rank = 0;
-      for (int p = 0; p < na; ++p) rank += sh.amb_v[p] < v;
+      for (int p = 0; p < na; p += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (p + u < na) && sh.amb_v[min(p + u, na - 1)] < v;
+      }
       sh.amb_sorted[rank] = v;
-      sh.amb_w[rank] = weight<BF16>(e, v, true, St, Sd, sh.T64);
+      sh.amb_w[rank] = weight<BF16>(e, v, true, iSt, iSd, sh.T64);
     }
     __syncthreads();
-    if (tid == 0)
-      for (int q = 0; q < na; ++q) sh.corr[sh.amb_sorted[q] / kRangeElems] += sh.amb_w[q];
+    // each range's corrections summed in token order by the first of its tokens
+    for (int q = tid; q < na; q += NT) {
+      const int r = sh.amb_sorted[q] / kRangeElems;
+      if (q == 0 || sh.amb_sorted[q - 1] / kRangeElems != r) {
+        double x = 0.0;
+        for (int p = q; p < na && sh.amb_sorted[p] / kRangeElems == r; ++p) x += sh.amb_w[p];
+        sh.corr[r] = x;
+      }
+    }
     __syncthreads();
-    for (int r = tid; r < NR; r += NT) sh.R[r] = (sh.rg[r].a / St - sh.rg[r].d / Sd) + sh.corr[r];
+    for (int r = tid; r < NR; r += NT) sh.R[r] = (sh.rg[r].a * iSt - sh.rg[r].d * iSd) + sh.corr[r];
   } else if (resid && slow) {
     // exact weight of every token (rare: nearly identical target and draft rows)
     for (int r = 0; r < NR; ++r) {
       double x = 0.0;
       for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += NT)
-        x += weight<BF16>(e, v, true, St, Sd, sh.T64);
+        x += weight<BF16>(e, v, true, iSt, iSd, sh.T64);
       x = wave_sum(x);
       if (lane == 0) sh.wsum[wave] = x;
       __syncthreads();
@@ -583,7 +600,7 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
     for (int r = NR - 1; r >= 0; --r) {
       int best = -1;
       for (int v = r * kRangeElems + tid; v < min(V, (r + 1) * kRangeElems); v += NT)
-        if (weight<BF16>(e, v, wres, St, Sd, sh.T64) > 0.0) best = v;
+        if (weight<BF16>(e, v, wres, iSt, iSd, sh.T64) > 0.0) best = v;
       best = wave_max_i(best);
       if (lane == 0) sh.last_lane[wave] = best;
       __syncthreads();
@@ -603,7 +620,7 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int v = base + j;
-      w[j] = (v < V) ? weight<BF16>(e, v, wres, St, Sd, sh.T64) : 0.0;
+      w[j] = (v < V) ? weight<BF16>(e, v, wres, iSt, iSd, sh.T64) : 0.0;
       x += w[j];
     }
     const double incl = wave_inclusive_sum(x, lane);
