@@ -40,8 +40,9 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps first: the GPU's clocks reach their steady state within ~50 steps")
     p.add_argument("--config", default="scheduled")
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")

@@ -525,6 +525,10 @@ extern "C" int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int
               nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool fuse = B <= kFinalThreads;
+  // batches the fused emit serves (every compute unit gets a request) and a streaming workgroup's
+  // threads can cover (two requests each): no work list at all, the streaming workgroups derive
+  // their items from the lengths and the status words the scheduler's last kernel writes
+  v.derive_items = (fuse && B >= kFuseMinRequests && B <= 2 * kStreamThreads && gamma < SPEC_WAVE) ? 1 : 0;
   rc = launch_schedule(a, sched_workspace, sched_workspace_bytes, s, fuse ? &v : nullptr);
   if (rc != SPEC_OK) return rc;
   v.wl_ready = fuse ? 1 : 0;

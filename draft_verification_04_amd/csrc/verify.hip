@@ -673,6 +673,37 @@ __device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float
   }
 }
 
+// Work item g of a call whose work list is request-major (a.derive_items): items[r] holds request
+// r's first item (the items of request r are its positions 0 .. L_r, one after another; a request
+// with no items has the next one's first item) and *nitems the total.  Each wave finds g's request
+// by itself: the number of requests whose first item is <= g, counted with ballots over the B <=
+// 2 * kStreamThreads first-item words (one load each, all issued together; no barrier).  Returns
+// false when g lies past the last item.
+__device__ __forceinline__ bool derive_item(const VerifyArgs& a, int g, int& i_out, int& k_out) {
+  constexpr int NQ = 2 * kStreamThreads / SPEC_WAVE;   // chunks of 64 requests
+  const int lane = threadIdx.x & 63;
+  const int B = a.B;
+  if (g >= *a.nitems) return false;
+  int o[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int r = q * SPEC_WAVE + lane;
+    o[q] = (q * SPEC_WAVE < B) ? a.items[min(r, B - 1)] : 0x7fffffff;
+    if (r >= B) o[q] = 0x7fffffff;
+  }
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) n += (int)__popcll(__ballot(o[q] <= g));
+  const int i = n - 1;                 // a request with no items shares its first item with the next
+  int first = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+    if (q == (i >> 6)) first = __builtin_amdgcn_readlane(o[q], i & 63);
+  i_out = i;
+  k_out = g - first;
+  return true;
+}
+
 // log2-sum-exp of a row from its segment partials (fixed segment order); NaN when invalid.
 
 // One workgroup per (work item, segment).  Target row k and, when k < L, draft row k of
@@ -687,16 +718,22 @@ void stream_kernel(VerifyArgs a) {
   __shared__ StreamShared sh;
   const int nseg = a.nseg;
   const int g = blockIdx.x / nseg, seg = blockIdx.x - g * nseg;
-  if (g >= *a.nitems) return;
-  const int item = a.items[g];
-  const int i = item >> 7, k = item & 127;
+  int i, k;
+  if (a.derive_items) {
+    if (!derive_item(a, g, i, k)) return;
+  } else {
+    if (g >= *a.nitems) return;
+    const int item = a.items[g];
+    i = item >> 7;
+    k = item & 127;
+  }
   const int G = a.G, V = a.V;
   constexpr int ES = BF16 ? 2 : 4;
   const float T = a.greedy_only ? 0.f : a.temperature[i];
   if (!(T >= 0.f && T < INFINITY)) return;          // reported by emit_final_kernel
   int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
   if (K < 0) return;
-  if (K >= V) K = 0;
+  if (K >= V || T == 0.f) K = 0;   // the greedy rule reads raw rows: no kept set
   const int L = a.lengths ? a.lengths[i] : G;
   const bool greedy = (T == 0.f);
   if (greedy && a.overlap_only) return;   // no draft distribution to overlap with
@@ -760,7 +797,7 @@ void stream_kernel(VerifyArgs a) {
     // acceptance test needs (its load overlaps the streaming)
     float zx = NAN;
     if (seg == 0 && two && lt == 0) {
-      const int x = a.items_x[g];
+      const int x = a.derive_items ? a.tokens[(size_t)i * G + k] : a.items_x[g];
       if (x >= 0 && x < V) zx = load_elem<BF16>(row, x);
     }
     float M = -0x1p30f, S = 0.f;
@@ -780,7 +817,7 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a) {
   const int G = a.G, V = a.V, nseg = a.nseg;
   const float T = a.greedy_only ? 0.f : a.temperature[i];
   if (!(T >= 0.f && T < INFINITY)) return;
-  const int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+  const int K = (a.top_k && !a.greedy_only && T > 0.f) ? a.top_k[i] : 0;   // greedy: no kept set
   if (K < 0 || (K > 0 && K < V)) return;
   const int L = a.lengths ? a.lengths[i] : G;
   const Partial* pt = a.part_t + ((size_t)i * (G + 1) + k) * nseg;

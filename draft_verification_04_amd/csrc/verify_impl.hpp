@@ -86,6 +86,8 @@ struct VerifyArgs {
   int emit_segs;       // emit-pass workgroups per request (1 = one fused workgroup, else 2 .. kMaxEmitSegs)
   int max_items;       // caller's bound on the number of work items (0: none); sizes the streaming grid
   int wl_ready;        // the work list was written by the scheduler's last kernel (no work-list kernel)
+  int derive_items;    // request-major work list: items[r] = request r's first item, *nitems the total
+                       // (B <= 2 * kStreamThreads); each streaming workgroup finds its own request
 };
 
 constexpr int kStreamThreads = 512;
@@ -201,6 +203,7 @@ struct WorklistShared {
   int ctot[SPEC_MAX_GAMMA + 1];
   int off[SPEC_MAX_GAMMA + 2];
   long long wsum[kWorklistThreads / SPEC_WAVE];
+  long long wsum2[kWorklistThreads / SPEC_WAVE];   // a second scan's wave totals
 };
 
 constexpr int kWlPre = 16;   // draft tokens per request fetched ahead of the work list
@@ -210,7 +213,7 @@ constexpr int kWlPre = 16;   // draft tokens per request fetched ahead of the wo
 // caller issues these loads before it knows them.
 __device__ inline void worklist_prefetch(const VerifyArgs& a, int (&xp)[kWlPre]) {
   const int tid = threadIdx.x;
-  const bool want = a.tokens && !a.overlap_only && tid < a.B;
+  const bool want = a.tokens && !a.overlap_only && !a.derive_items && tid < a.B;
 #pragma unroll
   for (int u = 0; u < kWlPre; ++u) xp[u] = (want && u < a.G) ? a.tokens[(size_t)tid * a.G + u] : -1;
 }
@@ -246,6 +249,23 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
     a.ereq[tid].amb_n = 0;
   }
   const int last = (valid && !drop) ? (a.overlap_only ? L - 1 : L) : -1;
+  if (a.derive_items) {
+    // request-major: request tid's first item is the exclusive prefix of (last + 1) over the
+    // requests before it; the streaming workgroups find their requests from these words
+    const long long n = last + 1;
+    const long long in = wave_inclusive_sum_i64(n, lane);
+    if (lane == 63) sh.wsum2[wave] = in;
+    __syncthreads();
+    long long before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += (w < wave) ? sh.wsum2[w] : 0;
+      total += sh.wsum2[w];
+    }
+    if (tid < B) a.items[tid] = (int)(before + in - n);
+    if (tid == 0) *a.nitems = (int)total;
+    return;
+  }
   for (int k = 0; k <= G; ++k) {
     const unsigned long long m = __ballot(last >= k);
     if (lane == 0) sh.cnt[wave][k] = __popcll(m);

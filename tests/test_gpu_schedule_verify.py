@@ -3,7 +3,8 @@ the two calls it stands for, spec_schedule_lengths then spec_verify_bounded with
 the same stream.  Both are pinned to the oracle elsewhere; here every output must agree bit for bit
 (accept_prob compared as bit patterns, so NaN marks must match too), and the lengths must also equal
 the oracle's schedule.  B <= 1024 takes the path in which the scheduler writes the verify work list;
-B = 1100 takes the path with the separate work-list kernel.
+B = 1100 takes the path with the separate work-list kernel; 256 <= B <= 1024 (gamma < 64) takes the
+path with no work list at all, in which each streaming workgroup derives its item from the lengths.
 """
 
 import numpy as np
@@ -14,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle
 from oracle.scheduling import MODE_EARLY_STOP, MODE_GLOBAL
-from parity import HostInputs, compare_verify, run_oracle_pooled, to_np
+from parity import HostInputs, compare_verify, run_oracle_pooled, to_np  # noqa: F401
 from workloads import make_workload
 
 DEV = "cuda:0"
@@ -52,7 +53,27 @@ def _check(sv, w, sps, budget, mode, with_oracle=True):
     if with_oracle:
         L_ref, _ = oracle.schedule(w.conf.cpu().numpy(), sps, budget, mode)
         assert np.array_equal(to_np(fused["lengths"]), L_ref)
+        if w.V * w.B <= 1 << 22:   # the verification outputs too (the full-size case has its own test)
+            h = HostInputs.of_workload(w, L_ref)
+            ref = run_oracle_pooled(h)
+            over = _over_budget(L_ref, budget)
+            for key in ("status", "accept_flags", "emit_flag", "draws"):
+                ref[key] = ref[key].copy()
+            ref["status"][over] = 64          # the token cap, which the oracle does not model
+            ref["num_accepted"][over] = 0
+            ref["out_tokens"][over] = -1
+            ref["accept_prob"][over] = np.nan
+            ref["accept_flags"][over] = 0
+            ref["emit_flag"][over] = False
+            ref["draws"][over] = 0
+            compare_verify(fused, ref, inputs=h)
     return fused
+
+
+def _over_budget(L, budget):
+    """Requests past the token cap (index order, L + 1 tokens each): SPEC_REQ_OVER_BUDGET."""
+    run = np.cumsum(L.astype(np.int64) + 1)
+    return run > budget
 
 
 @pytest.mark.parametrize("mode", [MODE_EARLY_STOP, MODE_GLOBAL])
@@ -133,6 +154,36 @@ def test_fp32_logits_greedy_rows_and_top_k(sv):
     w = make_workload("tiny", DEV, B=64, gamma=6, V=2000, seed=78, with_schedule=True)
     assert w.target.dtype == torch.float32
     w.temperature[::4] = 0.0
+    w.top_k = torch.zeros(w.B, dtype=torch.int32, device=DEV)
+    w.top_k[::3] = 7
+    f = _check(sv, w, w.sps, w.budget, MODE_GLOBAL)
+    assert (to_np(f["status"]) == 0).all()
+
+
+@pytest.mark.parametrize("B,gamma,V,budget,mode", [
+    (256, 16, 3001, None, MODE_EARLY_STOP),     # one request per streaming thread
+    (700, 12, 2003, None, MODE_GLOBAL),         # two requests per thread, a ragged last chunk
+    (1024, 8, 1000, None, MODE_EARLY_STOP),     # every thread's two requests
+    (600, 6, 999, 450, MODE_EARLY_STOP),        # budget below the batch: the cap marks requests
+    (256, 63, 500, 5000, MODE_GLOBAL),          # the most positions the derived items allow
+])
+def test_derived_items(sv, B, gamma, V, budget, mode):
+    """Batches the fused emit serves: the streaming workgroups find their items without a work list."""
+    w = make_workload("scheduled", DEV, B=B, gamma=gamma, V=V, seed=80 + B)
+    b = w.budget if budget is None else budget
+    f = _check(sv, w, w.sps, b, mode)
+    st = to_np(f["status"])
+    if b < B:
+        assert (st[:b] == 0).all() and (st[b:] == 64).all()
+    else:
+        assert (st == 0).all()
+
+
+def test_derived_items_with_greedy_rows_and_top_k(sv):
+    # fp32 logits; every fourth request greedy, every third a top-k of 7; mixed temperatures
+    w = make_workload("tiny", DEV, B=320, gamma=6, V=2000, seed=88, with_schedule=True)
+    w.temperature[::4] = 0.0
+    w.temperature[1::4] = 0.7
     w.top_k = torch.zeros(w.B, dtype=torch.int32, device=DEV)
     w.top_k[::3] = 7
     f = _check(sv, w, w.sps, w.budget, MODE_GLOBAL)
