@@ -315,7 +315,7 @@ __device__ __forceinline__ void vec_ranges(PassShared& sh, const EmitRows& e, Ac
 // E_d goes to sh.red[1][wave].  bf16 rows without top-k build the Q table in sh.Qt here unless
 // table_ready (the whole workgroup calls this function).
 template <bool BF16, bool TOPK>
-__device__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e,
+__device__ __forceinline__ void pass_ranges(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e,
                             EmitRange* out, bool table_ready) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int NWPB = (int)(blockDim.x >> 6);
@@ -380,11 +380,193 @@ __device__ __forceinline__ void decide_into(PassShared& sh, const VerifyArgs& a,
 
 // The emit pass over segment `seg` of request i (after its decision, sampling only).
 template <bool BF16>
-__device__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e, EmitRange* out,
+__device__ __forceinline__ void run_pass(PassShared& sh, const VerifyArgs& a, int i, int seg, const EmitRows& e, EmitRange* out,
                          int K, bool table_ready = false) {
   if (K > 0 && K < a.V) pass_ranges<BF16, true>(sh, a, i, seg, e, out, false);
   else pass_ranges<BF16, false>(sh, a, i, seg, e, out, table_ready);
   __syncthreads();
+}
+
+// ---- top-k requests whose kept tokens are all in their segment lists ----
+
+struct TopkEmitShared {
+  int32_t id[2][kTopkEmitKept];   // the kept entries of target row n and draft row n: token ids
+  float z[2][kTopkEmitKept];      //   and raw logits
+  double w[kTopkEmitKept];        // the target's kept tokens' weights in ascending token order
+  int32_t sorted[kTopkEmitKept];  //   and their ids
+  int nk[2];
+  double sd;                      // S_d
+  int token;
+};
+
+// Whether request i's emit at position n can draw from the segment lists: a sampling request with
+// 0 < K < V whose target row n (and draft row n after a rejection) had its kept tokens listed with
+// their logits, at most kTopkEmitKept of them (RowStat's third field; set only by the merge of
+// segmented top-k rows).
+__device__ __forceinline__ bool topk_lists_complete(const VerifyArgs& a, int i, int n, int L, float T, int K,
+                                                    const RowStat& rt, const RowStat& rd) {
+  return T > 0.f && K > 0 && K < a.V && rt.argmax == 1 && (n >= L || rd.argmax == 1);
+}
+
+// The emitted token of top-k request i at position n from the segment lists: the kept entries (listed
+// values at or above the row's threshold) of target row n and, after a rejection, draft row n;
+// Q = exp(z / T - R) in fp64 (R the target row's log-normaliser); S_t, S_d the kept Q sums; weights
+// w = max(0, Q_t / S_t - Q_d / S_d) after a rejection (Q_d = 0 outside the draft's kept set),
+// w = Q_t for the appended token; the token is the first in ascending token order whose running sum
+// of w passes u * W (u the emit uniform of position n), or the last with w > 0 when rounding leaves
+// no crossing.  With W <= 0 after a rejection, w = Q_t (as the row-based path).  These are the weights
+// the row-based path gives every token (zero outside the target's kept set), so the draw is the same.
+// Wave 0 gathers the target's entries, wave 1 the draft's (and S_d); wave 0 then ranks the target's
+// by token id, joins the draft's logits and walks the weights.  Called by a whole workgroup of at
+// least two waves; every thread gets the token.
+template <bool BF16>
+__device__ __forceinline__ int emit_topk_lists(TopkEmitShared& sh, const VerifyArgs& a, int i, int n, int L,
+                                               float T, const RowStat& rt, const RowStat& rd, const double* T64) {
+  constexpr int J = kTopkEmitKept / SPEC_WAVE;
+  static_assert(kTopkSegCap <= 2 * SPEC_WAVE, "two list entries per lane");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const bool resid = n < L;
+  const double invT = 1.0 / (double)T, R = rt.lse2 * kLn2;
+  if (wave < (resid ? 2 : 1)) {
+    // row `wave`'s kept entries, compacted in list order
+    const size_t slot = topk_slot(a.G, i, n, wave);
+    const float th = wave ? rd.theta : rt.theta;
+    const int nsk = a.nseg_topk;
+    const int ns = (lane < nsk) ? a.tk_seg[slot + lane].n : 0;
+    float zl[kTopkSegs][2];
+    int il[kTopkSegs][2];
+#pragma unroll
+    for (int s = 0; s < kTopkSegs; ++s) {
+      const int nss = read_lane(ns, s);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = lane + h * SPEC_WAVE;
+        const bool on = s < nsk && q < nss;
+        zl[s][h] = on ? a.tk_val[(slot + s) * kTopkSegCap + q] : -INFINITY;
+        il[s][h] = on ? a.tk_ids[(slot + s) * kTopkSegCap + q] : -1;
+      }
+    }
+    int m = 0;
+    double sd = 0.0;
+#pragma unroll
+    for (int s = 0; s < kTopkSegs; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool keep = il[s][h] >= 0 && zl[s][h] >= th;
+        const unsigned long long mk = __ballot(keep);
+        const int q = m + (int)__popcll(mk & below);
+        if (keep && q < kTopkEmitKept) {
+          sh.id[wave][q] = il[s][h];
+          sh.z[wave][q] = zl[s][h];
+        }
+        if (keep && wave == 1) sd += q_direct(zl[s][h], invT, R, T64);
+        m += (int)__popcll(mk);
+      }
+    if (wave == 1) sd = wave_sum(sd);   // a fixed lane per entry: the same sum run after run
+    if (lane == 0) {
+      sh.nk[wave] = m;
+      if (wave == 1) sh.sd = sd;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int nkt = sh.nk[0], nkd = resid ? sh.nk[1] : 0;
+    // entry lane + 64 j of each row in registers
+    int it[J], id[J];
+    float zt[J], zd[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = lane + j * SPEC_WAVE;
+      it[j] = (q < nkt) ? sh.id[0][q] : 0x7fffffff;
+      zt[j] = (q < nkt) ? sh.z[0][q] : -INFINITY;
+      id[j] = (q < nkd) ? sh.id[1][q] : -1;
+      zd[j] = (q < nkd) ? sh.z[1][q] : -INFINITY;
+    }
+    // rank of each target entry among the target's (ids are distinct) and its draft logit, if the
+    // draft kept the token (else -inf: Q_d = 0)
+    int rank[J];
+    float zj[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      rank[j] = 0;
+      zj[j] = -INFINITY;
+    }
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      if (jj * SPEC_WAVE >= max(nkt, nkd)) break;
+      for (int src = 0; src < SPEC_WAVE; ++src) {
+        const int ot = read_lane(it[jj], src), od = read_lane(id[jj], src);
+        const float oz = read_lane(zd[jj], src);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          rank[j] += ot < it[j];
+          if (od == it[j]) zj[j] = oz;
+        }
+      }
+    }
+    double qt[J], st = 0.0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      qt[j] = (lane + j * SPEC_WAVE < nkt) ? q_direct(zt[j], invT, R, T64) : 0.0;
+      st += qt[j];
+    }
+    st = wave_sum(st);
+    const double iSt = 1.0 / st, iSd = resid ? 1.0 / sh.sd : 0.0;
+    double tot = 0.0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const double qd = (resid && zj[j] > -INFINITY) ? q_direct(zj[j], invT, R, T64) : 0.0;
+      const double w = resid ? fmax(0.0, qt[j] * iSt - qd * iSd) : qt[j];
+      tot += w;
+      if (lane + j * SPEC_WAVE < nkt) {
+        sh.w[rank[j]] = w;
+        sh.sorted[rank[j]] = it[j];
+      }
+    }
+    // no residual mass (rounding): p_t of the same row
+    const bool plain = resid && !(wave_sum(tot) > 0.0);
+    if (plain) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (lane + j * SPEC_WAVE < nkt) sh.w[rank[j]] = qt[j];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane l walks ranks l * JJ .. l * JJ + JJ - 1
+    const int nkt = sh.nk[0];
+    const int JJ = (nkt + SPEC_WAVE - 1) / SPEC_WAVE;
+    double w[J], tot = 0.0;
+    int vid[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int r = lane * JJ + j;
+      const bool on = j < JJ && r < nkt;
+      w[j] = on ? sh.w[r] : 0.0;
+      vid[j] = on ? sh.sorted[r] : -1;
+      tot += w[j];
+    }
+    const double W = wave_sum(tot);
+    double ua, ue;
+    verify_uniforms(a.seed[i], (uint64_t)i, (uint64_t)n, &ua, &ue);
+    const double target = ue * W;
+    double run = wave_inclusive_sum(tot, lane) - tot;
+    int cross = -1, lastpos = -1;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (w[j] > 0.0) lastpos = vid[j];
+      run += w[j];
+      if (cross < 0 && w[j] > 0.0 && run > target) cross = vid[j];
+    }
+    const unsigned long long mc = __ballot(cross >= 0), mp = __ballot(lastpos >= 0);
+    int tok;
+    if (mc) tok = read_lane(cross, (int)__ffsll((long long)mc) - 1);
+    else tok = mp ? read_lane(lastpos, 63 - __clzll((long long)mp)) : -1;
+    if (lane == 0) sh.token = tok;
+  }
+  __syncthreads();
+  return sh.token;
 }
 
 template <bool BF16>
@@ -395,6 +577,13 @@ __global__ __launch_bounds__(kPassThreads, 4) void emit_pass_kernel(VerifyArgs a
   decide_into(sh, a, i);
   const int st = sh.st, n = sh.n;
   if (st || a.temperature[i] == 0.f) return;
+  {
+    const int L = a.lengths ? a.lengths[i] : a.G;
+    const int K = a.top_k ? a.top_k[i] : 0;
+    const RowStat rt = a.rows_t[(size_t)i * (a.G + 1) + n];
+    const RowStat rd = (n < L) ? a.rows_d[(size_t)i * a.G + n] : RowStat{0.0, -INFINITY, 0};
+    if (topk_lists_complete(a, i, n, L, a.temperature[i], K, rt, rd)) return;   // drawn from the lists
+  }
   run_pass<BF16>(sh, a, i, seg, emit_rows<BF16>(a, i, n), a.ranges + (size_t)i * num_ranges(a.V),
                  a.top_k ? a.top_k[i] : 0);
   if (threadIdx.x == 0) {
@@ -434,12 +623,12 @@ __device__ __forceinline__ double weight(const EmitRows& e, int v, bool resid, d
 }
 
 template <bool BF16, int NT>
-__device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, const EmitRows& e);
+__device__ __forceinline__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, const EmitRows& e);
 
 // Everything after request i's decision (st, n): status and outputs, then, for a sampling
 // request, the emitted token (sample_emit).
 template <bool BF16>
-__device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int st, int n) {
+__device__ __forceinline__ void finish_request(FinalShared& sh, TopkEmitShared& tes, const VerifyArgs& a, int i, int st, int n) {
   const int tid = threadIdx.x;
   const int G = a.G;
   const int L = a.lengths ? a.lengths[i] : G;
@@ -464,6 +653,16 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
     if (tid == 0) a.out_tokens[(size_t)i * (G + 1) + n] = a.rows_t[(size_t)i * (G + 1) + n].argmax;
     return;
   }
+  {
+    const int K = a.top_k ? a.top_k[i] : 0;
+    const RowStat rt = a.rows_t[(size_t)i * (G + 1) + n];
+    const RowStat rd = (n < L) ? a.rows_d[(size_t)i * G + n] : RowStat{0.0, -INFINITY, 0};
+    if (topk_lists_complete(a, i, n, L, a.temperature[i], K, rt, rd)) {
+      const int tok = emit_topk_lists<BF16>(tes, a, i, n, L, a.temperature[i], rt, rd, sh.T64);
+      if (tid == 0) a.out_tokens[(size_t)i * (G + 1) + n] = tok;
+      return;
+    }
+  }
   sample_emit<BF16, kEmitThreads>(sh, a, i, n, emit_rows<BF16>(a, i, n));
 }
 
@@ -472,7 +671,7 @@ __device__ void finish_request(FinalShared& sh, const VerifyArgs& a, int i, int 
 // out_tokens.  Called by a block of NT threads; each holds kRangeElems / NT consecutive tokens
 // of the range where the draw lands.
 template <bool BF16, int NT>
-__device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, const EmitRows& e) {
+__device__ __forceinline__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, const EmitRows& e) {
   constexpr int TPT = kRangeElems / NT;
   constexpr int NW = NT / SPEC_WAVE;
   static_assert(TPT * NT == kRangeElems && NW * SPEC_WAVE == NT && NW <= kMaxWaves, "block shape");
@@ -676,6 +875,7 @@ __device__ void sample_emit(FinalShared& sh, const VerifyArgs& a, int i, int n, 
 template <bool BF16>
 __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) {
   __shared__ FinalShared sh;
+  __shared__ TopkEmitShared tes;
   const int i = a.r0 + (int)blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G, V = a.V;
@@ -709,7 +909,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
     if (tid == 0) sh.St = x;
   }
   __syncthreads();
-  finish_request<BF16>(sh, a, i, sh.st, sh.n);
+  finish_request<BF16>(sh, tes, a, i, sh.st, sh.n);
 }
 
 // What the fused decision of request i reads besides the segment partials: loaded by wave 0 before
@@ -757,10 +957,10 @@ __device__ __forceinline__ int decide_status(const VerifyArgs& a, const DecideIn
 // First half of the fused decision of request i, three waves at once (lane per position), from
 // the staged segment partials:
 //   wave 0: target row statistics of positions k <= L (log2-sum-exp, or the argmax for the
-//           greedy rule; top-k rows were finished by the streaming kernel),
+//           greedy rule; top-k rows were finished by the streaming or merging kernel),
 //   wave 1: draft row statistics of positions k < L (top-k: the streaming kernel's test),
 //   wave 2: the acceptance uniforms of positions k < L (sampling rows without top-k).
-__device__ void decide_stats(DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+__device__ __forceinline__ void decide_stats(DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int G = a.G, V = a.V, nseg = a.nseg;
   const int L = in.L;
@@ -817,7 +1017,7 @@ __device__ void decide_stats(DecideShared& sh, const VerifyArgs& a, int i, const
 // Second half (wave 0, after a barrier): r = min(1, p_t(x)/p_d(x)) with the logits at x the
 // partials carry, the test, the first rejection.  Leaves in sh: st, n, L, greedy, and per position
 // the acceptance ratio and the draft token.
-__device__ void decide_final(DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+__device__ __forceinline__ void decide_final(DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
   const int lane = threadIdx.x;
   const int G = a.G, V = a.V, nseg = a.nseg;
   const int L = in.L;
@@ -881,7 +1081,7 @@ __device__ void decide_final(DecideShared& sh, const VerifyArgs& a, int i, const
 // segment's largest value, so the emit row's own largest entries stay normal unless its lse lies
 // far below R0; the fused kernel then rebuilds the table with that lse.
 template <bool BF16>
-__device__ void early_table(PassShared& ps, DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
+__device__ __forceinline__ void early_table(PassShared& ps, DecideShared& sh, const VerifyArgs& a, int i, const DecideIn& in) {
   const int t = (int)threadIdx.x - 3 * SPEC_WAVE, lane = threadIdx.x & 63;
   const int nthr = (int)blockDim.x - 3 * SPEC_WAVE;
   const int L = in.L, nseg = a.nseg;
@@ -950,6 +1150,19 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
   if (st || ds.greedy) {
     decided_outputs(ds, a, i);
     return;
+  }
+  {
+    const RowStat rd = ds.rd[n < ds.L ? n : 0];
+    if (topk_lists_complete(a, i, n, ds.L, din.T, din.K0, ds.rt[n], rd)) {
+      // a top-k request with its kept tokens listed: no pass over the rows (the Q table is unused
+      // by top-k requests, so its storage holds the lists)
+      static_assert(sizeof(TopkEmitShared) <= sizeof(ps.Qt), "the lists fit the table's storage");
+      decided_outputs(ds, a, i);
+      const int tok = emit_topk_lists<BF16>(*reinterpret_cast<TopkEmitShared*>(ps.Qt), a, i, n, ds.L, din.T,
+                                            ds.rt[n], rd, ps.T64);
+      if (threadIdx.x == 0) a.out_tokens[(size_t)i * (a.G + 1) + n] = tok;
+      return;
+    }
   }
   EmitRows e = emit_rows_from<BF16>(a, i, n, ds.L, din.T, ds.rt[n], ds.rd[n < ds.L ? n : 0]);
   e.amb_n = &ds.amb_cnt;

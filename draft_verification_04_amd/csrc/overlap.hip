@@ -136,7 +136,7 @@ using namespace spec;
 
 extern "C" size_t spec_overlap_workspace_size(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_V) return 0;
-  return workspace_bytes(B, gamma, V, false) + part_bytes(B, gamma);
+  return workspace_bytes(B, gamma, V, false, true) + part_bytes(B, gamma);
 }
 
 extern "C" int32_t spec_overlap_mass(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,

@@ -400,8 +400,93 @@ struct StreamShared {
   int cand_n[2];
   int cnt[2][8];
   long long sum_q[8];   // per-wave fixed-point sums of the kept candidates
-  float cand[2][kTopkCap];
+  // segmented top-k rows
+  int wcnt[8];          // candidates per LDS region (a wave's; in the merge, a segment's entries)
+  int over[2];          // merge: a segment of the row could not be listed
+  int lists[2];         // merge: the row's kept entries are few enough for the emit to draw from
+  int last;             // this workgroup finished its item's last segment
+  union {
+    float cand[2][kTopkCap];
+    char tkr[8][kTopkRegionBytes];   // segmented top-k: wave w's region (see topk_segment)
+  };
 };
+
+// Wave w's region of a segmented top-k row: while streaming, the raw vectors holding a candidate and
+// their vector indices; afterwards the candidates, values from tk_cand_z and token ids from tk_cand_id.
+__device__ __forceinline__ uint4* tk_hits(StreamShared& sh, int w) { return reinterpret_cast<uint4*>(sh.tkr[w]); }
+__device__ __forceinline__ int32_t* tk_hit_idx(StreamShared& sh, int w) {
+  return reinterpret_cast<int32_t*>(sh.tkr[w] + kTopkWaveHits * 16);
+}
+__device__ __forceinline__ float* tk_cand_z(StreamShared& sh, int w) { return reinterpret_cast<float*>(sh.tkr[w]); }
+__device__ __forceinline__ int32_t* tk_cand_id(StreamShared& sh, int w) {
+  return reinterpret_cast<int32_t*>(sh.tkr[w] + kTopkWaveCand * 4);
+}
+
+// Wave-wide: the largest key t such that at least `need` lanes hold a key >= t (bitwise from the top).
+// bf16 keys have a zero low half (positive values) or 0xffff (negative ones): the search stops at bit
+// 16, and the low half of a negative result is filled in.
+template <bool BF16>
+__device__ __forceinline__ uint32_t wave_kth_key(uint32_t key, int need) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+    const uint32_t trial = t | (1u << bit);
+    if ((int)__popcll(__ballot(key >= trial)) >= need) t = trial;
+  }
+  if (BF16 && t < 0x80000000u) t |= 0xffffu;
+  return t;
+}
+
+// One wave: the K-th largest key (ties counted) among the values in LDS regions w0 .. w0 + nw - 1 of
+// z (region w holds cnt[w] of them from w * stride; nw <= 8).  Key 0 marks an empty slot (no value
+// has it: it would be a NaN).  0 when there are fewer than K values.  Up to 512 values are searched
+// in registers (eight per lane, over the regions one after another) when REGS, more (or all) from LDS.
+template <bool BF16, bool REGS = true>
+__device__ __forceinline__ uint32_t kth_region_key(const float* z, int stride, const int* cnt, int w0, int nw,
+                                                   int K, int lane) {
+  int off[9];   // region w's values are entries off[w] .. off[w + 1] - 1 of the concatenation
+  off[0] = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) off[w + 1] = off[w] + ((w < nw) ? cnt[w0 + w] : 0);
+  const int n = off[8];
+  const int lo = BF16 ? 16 : 0;
+  uint32_t t = 0;
+  if (REGS && n <= 8 * SPEC_WAVE) {
+    uint32_t kr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = lane + j * SPEC_WAVE;
+      int r = 0;
+#pragma unroll
+      for (int w = 1; w < 8; ++w) r += q >= off[w];
+      int base = 0;
+#pragma unroll
+      for (int w = 1; w < 8; ++w)
+        if (r == w) base = off[w];
+      kr[j] = (q < n) ? fkey(z[(w0 + r) * stride + (q - base)]) : 0u;
+    }
+    for (int bit = 31; bit >= lo; --bit) {
+      const uint32_t trial = t | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c += (int)__popcll(__ballot(kr[j] >= trial));
+      if (c >= K) t = trial;
+    }
+  } else {
+    for (int bit = 31; bit >= lo; --bit) {
+      const uint32_t trial = t | (1u << bit);
+      int c = 0;
+      for (int w = 0; w < nw; ++w) {
+        const int nr = cnt[w0 + w];
+        const float* zr = z + (w0 + w) * stride;
+        for (int q0 = 0; q0 < nr; q0 += SPEC_WAVE)
+          c += (int)__popcll(__ballot(q0 + lane < nr && fkey(zr[q0 + lane]) >= trial));
+      }
+      if (c >= K) t = trial;
+    }
+  }
+  if (BF16 && t != 0u && t < 0x80000000u) t |= 0xffffu;
+  return t;
+}
 
 // Combine the per-thread (M, S) of one row's waves; result in sh.lse2[which].
 __device__ __forceinline__ void row_combine_sum(StreamShared& sh, float M, float S, int bad, int wave, int lane,
@@ -438,7 +523,7 @@ __device__ __forceinline__ void row_combine_sum(StreamShared& sh, float M, float
 // logits are >= tau.  If more than kTopkCap candidates arrive, the threshold
 // is found by counting passes over the row instead.
 template <bool BF16>
-__device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, float c_hi, float c_lo, int lt,
+__device__ __forceinline__ void topk_stats(StreamShared& sh, const char* row, int V, int K, float c_hi, float c_lo, int lt,
                            int nthr, int wave, int lane, int first_wave, int nwaves, int which) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
@@ -625,14 +710,17 @@ __device__ void topk_stats(StreamShared& sh, const char* row, int V, int K, floa
 }
 
 // Acceptance test of item (i, k) from finished row statistics; one thread.
+// lists_t, lists_d: 1 when the target / draft row's kept tokens are listed with their logits, few
+// enough for the emit to draw from (RowStat's third field, which the emit reads for top-k rows).
 template <bool BF16>
-__device__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double c64, double l2t, float tht,
-                            double l2d, float thd, const char* trow, const char* drow) {
+__device__ __forceinline__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double c64, double l2t, float tht,
+                            double l2d, float thd, const char* trow, const char* drow, int lists_t = 0,
+                            int lists_d = 0) {
   const int G = a.G, V = a.V;
-  a.rows_t[(size_t)i * (G + 1) + k] = RowStat{l2t, tht, 0};
+  a.rows_t[(size_t)i * (G + 1) + k] = RowStat{l2t, tht, lists_t};
   bool bad = !(l2t == l2t);
   if (two) {
-    a.rows_d[(size_t)i * G + k] = RowStat{l2d, thd, 0};
+    a.rows_d[(size_t)i * G + k] = RowStat{l2d, thd, lists_d};
     bad |= !(l2d == l2d);
     const int x = (a.tokens && !a.overlap_only) ? a.tokens[(size_t)i * G + k] : -1;
     if (!bad && x >= 0 && x < V) {
@@ -644,6 +732,370 @@ __device__ void accept_item(const VerifyArgs& a, int i, int k, bool two, double 
     }
   }
   if (bad) atomicOr(&a.req_status[i], SPEC_REQ_NONFINITE);
+}
+
+// One segment of a top-k row with K <= kTopkSegMaxK: vectors [vb, ve) of the row's 16-byte body, plus
+// the scalar head and tail when `ends`.  Lists the segment's values at or above its K-th largest value
+// theta_s (ties counted) with their token ids into vals / ids, and records theta_s, the segment's
+// largest value and whether it holds a NaN or +inf in *rec.  The row's K-th largest is at least
+// theta_s, so the list holds every kept token of the segment.
+// Candidates are the values >= tau, tau the smallest over the row's waves of each wave's
+// ceil(K / waves)-th largest lane maximum over the lanes' first vectors: every wave has that many
+// values >= its own bound, so at least K values are >= tau and theta_s >= tau.  While streaming, a
+// lane whose vector holds a candidate only copies the raw vector and its index to its wave's LDS
+// region (slot by ballot); after the segment each wave expands its vectors into (value, token id)
+// candidates in place, and the row's first wave finds theta_s among them.  A region overflowing, or
+// more than kTopkSegCap values at the cut, sets rec->n = kTopkSegCap + 1: the merge then counts over
+// the row.  Called by the nthr threads of one row (both rows of the workgroup call it: it contains
+// workgroup barriers); the streaming loop's trip count is the same in every lane of a wave (its
+// ballots need the whole wave).
+template <bool BF16>
+__device__ __forceinline__ void topk_segment(StreamShared& sh, const char* row, int V, int vb, int ve, bool ends,
+                                             int K, int lt, int nthr, int wave, int lane, int first_wave,
+                                             int nwaves, TopkSeg* rec, float* vals, int32_t* ids) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  constexpr int U = 4;                               // vectors per thread in flight
+  constexpr int RF = kTopkRegionBytes / 4;           // region stride in floats
+  constexpr int HJ = kTopkWaveHits / SPEC_WAVE;      // stored vectors per lane when expanding
+  static_assert(HJ * SPEC_WAVE == kTopkWaveHits, "whole waves of stored vectors");
+  const RowGeom g = row_geom<BF16>(row, V);
+  const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int vlast = max(ve - 1, 0);
+  const int base0 = vb + (lt - lane);   // the wave's first vector
+  // the scalar head and tail (segment 0), loaded early
+  const bool hv = ends && lt < g.head, tv = ends && lt < g.tail;
+  const int ttok = g.head + g.nvec * EPV + lt;
+  const float zh = hv ? load_elem<BF16>(row, lt) : NAN;
+  const float zt = tv ? load_elem<BF16>(row, ttok) : NAN;
+  uint4 d[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) d[u] = load_nt(vp + min(base0 + lane + u * nthr, vlast));
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (base0 + lane + u * nthr < ve) {
+      float z[EPV];
+      unpack<BF16>(d[u], z);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) tmax = fmaxf(tmax, z[j]);
+    }
+  {
+    const float tw = key_to_float(wave_kth_key<BF16>(fkey(tmax), (K + nwaves - 1) / nwaves));
+    if (lane == 0) sh.tau_w[wave] = tw;
+  }
+  __syncthreads();
+  float tau = INFINITY;
+  for (int w = first_wave; w < first_wave + nwaves; ++w) tau = fminf(tau, sh.tau_w[w]);
+  uint4* hvec = tk_hits(sh, wave);
+  int32_t* hidx = tk_hit_idx(sh, wave);
+  int nh = 0;   // the wave's stored vectors (the same in every lane)
+  int bad = 0;
+  float vmax = -INFINITY;
+  auto scan_vec = [&](const uint4& dv, int v) {
+    const bool valid = v < ve;
+    float z[EPV];
+    unpack<BF16>(dv, z);
+    float m = z[0];
+    int nb = 0;
+#pragma unroll
+    for (int j = 1; j < EPV; ++j) m = fmaxf(m, z[j]);
+#pragma unroll
+    for (int j = 0; j < EPV; j += 2) nb |= __builtin_isunordered(z[j], z[j + 1]);
+    nb |= m == INFINITY;
+    if (valid) {
+      bad |= nb;
+      vmax = fmaxf(vmax, m);
+    }
+    const bool hit = valid && m >= tau;
+    const unsigned long long mh = __ballot(hit);
+    if (mh) {
+      const int slot = nh + (int)__popcll(mh & below);
+      if (hit && slot < kTopkWaveHits) {
+        hvec[slot] = dv;
+        hidx[slot] = v;
+      }
+      nh += (int)__popcll(mh);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) scan_vec(d[u], base0 + lane + u * nthr);
+  for (int b = base0 + U * nthr; b < ve; b += U * nthr) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = load_nt(vp + min(b + lane + u * nthr, vlast));
+#pragma unroll
+    for (int u = 0; u < U; ++u) scan_vec(d[u], b + lane + u * nthr);
+  }
+  if (hv) {
+    bad |= !(zh < INFINITY);
+    vmax = fmaxf(vmax, zh);
+  }
+  if (tv) {
+    bad |= !(zt < INFINITY);
+    vmax = fmaxf(vmax, zt);
+  }
+  {
+    const float wm = wave_max(vmax);
+    const int wb = wave_or_i(bad);
+    if (lane == 0) {
+      sh.M[wave] = wm;
+      sh.bad[wave] = wb;
+    }
+  }
+  // expand the stored vectors into candidates, in place: read them all, then write
+  const int nhv = min(nh, kTopkWaveHits);
+  uint4 hx[HJ];
+  int hi[HJ];
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int q = lane + j * SPEC_WAVE;
+    hi[j] = (q < nhv) ? hidx[q] : -1;
+    if (q < nhv) hx[j] = hvec[q];
+  }
+  int c = (zh >= tau) + (zt >= tau);
+#pragma unroll
+  for (int j = 0; j < HJ; ++j)
+    if (hi[j] >= 0) {
+      float z[EPV];
+      unpack<BF16>(hx[j], z);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) c += z[e] >= tau;
+    }
+  // each lane's first slot: the lower lanes' counts, bit plane by bit plane (c < 32)
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int bb = 0; bb < 5; ++bb) {
+    const unsigned long long mb = __ballot((c >> bb) & 1);
+    pre += (int)__popcll(mb & below) << bb;
+    tot += (int)__popcll(mb) << bb;
+  }
+  // the region is the wave's own: its reads are done before it is rewritten
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  {
+    float* cz = tk_cand_z(sh, wave);
+    int32_t* cv = tk_cand_id(sh, wave);
+    int slot = pre;
+    auto put = [&](float z, int tok) {
+      if (z >= tau) {
+        if (slot < kTopkWaveCand) {
+          cz[slot] = z;
+          cv[slot] = tok;
+        }
+        ++slot;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < HJ; ++j)
+      if (hi[j] >= 0) {
+        float z[EPV];
+        unpack<BF16>(hx[j], z);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) put(z[e], g.head + hi[j] * EPV + e);
+      }
+    put(zh, lt);
+    put(zt, ttok);
+    if (lane == 0) sh.wcnt[wave] = (nh > kTopkWaveHits || tot > kTopkWaveCand) ? kTopkWaveCand + 1 : tot;
+  }
+  __syncthreads();
+  if (wave != first_wave) return;
+  // the row's first wave: theta_s and the list
+  float rmax = -INFINITY;
+  int rbad = 0, total = 0, full = 0;
+  for (int w = first_wave; w < first_wave + nwaves; ++w) {
+    rmax = fmaxf(rmax, sh.M[w]);
+    rbad |= sh.bad[w];
+    total += sh.wcnt[w];
+    full |= sh.wcnt[w] > kTopkWaveCand;
+  }
+  TopkSeg r{kTopkSegCap + 1, -INFINITY, rmax, rbad};
+  // fewer than K candidates happens only when every value was one (no bound): all are listed
+  const bool all = total < K && tau == -INFINITY;
+  if (!full && total <= 8 * SPEC_WAVE && (total >= K || all)) {
+    // the row's candidates in registers, eight per lane over the waves' regions one after another:
+    // theta_s by a bitwise search on their keys, then the list straight from the registers
+    int off[9];
+    off[0] = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) off[w + 1] = off[w] + ((w < nwaves) ? sh.wcnt[first_wave + w] : 0);
+    uint32_t kr[8];
+    int32_t ir[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = lane + j * SPEC_WAVE;
+      int rg = 0, base = 0;
+#pragma unroll
+      for (int w = 1; w < 8; ++w)
+        if (q >= off[w]) {
+          rg = w;
+          base = off[w];
+        }
+      const bool on = q < total;
+      kr[j] = on ? fkey(tk_cand_z(sh, first_wave + rg)[q - base]) : 0u;
+      ir[j] = on ? tk_cand_id(sh, first_wave + rg)[q - base] : 0;
+    }
+    uint32_t t = 0;
+    if (!all)
+      for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+        const uint32_t trial = t | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c += (int)__popcll(__ballot(kr[j] >= trial));
+        if (c >= K) t = trial;
+      }
+    if (BF16 && t != 0u && t < 0x80000000u) t |= 0xffffu;
+    const float th = all ? -INFINITY : key_to_float(t);
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool keep = kr[j] != 0u && kr[j] >= t;
+      const unsigned long long mk = __ballot(keep);
+      const int slot = m + (int)__popcll(mk & below);
+      if (keep && slot < kTopkSegCap) {
+        vals[slot] = key_to_float(kr[j]);
+        ids[slot] = ir[j];
+      }
+      m += (int)__popcll(mk);
+    }
+    if (m <= kTopkSegCap) r = TopkSeg{m, th, rmax, rbad};
+  } else if (!full && (total >= K || all)) {
+    const float* z0 = tk_cand_z(sh, 0);
+    const uint32_t t = all ? 0u : kth_region_key<BF16, false>(z0, RF, sh.wcnt, first_wave, nwaves, K, lane);
+    const float th = all ? -INFINITY : key_to_float(t);
+    int m = 0;
+    for (int w = first_wave; w < first_wave + nwaves; ++w) {
+      const int nw = sh.wcnt[w];
+      const float* zr = tk_cand_z(sh, w);
+      const int32_t* vr = tk_cand_id(sh, w);
+      for (int q0 = 0; q0 < nw; q0 += SPEC_WAVE) {
+        const int q = q0 + lane;
+        const float z = (q < nw) ? zr[q] : NAN;
+        const bool keep = q < nw && fkey(z) >= t;
+        const unsigned long long mk = __ballot(keep);
+        const int slot = m + (int)__popcll(mk & below);
+        if (keep && slot < kTopkSegCap) {
+          vals[slot] = z;
+          ids[slot] = vr[q];
+        }
+        m += (int)__popcll(mk);
+      }
+    }
+    if (m <= kTopkSegCap) r = TopkSeg{m, th, rmax, rbad};
+  }
+  if (lane == 0) *rec = r;
+}
+
+struct MergeShared {
+  float z[2][kTopkSegs * kTopkSegCap];   // per row: its listed values, segment s's from s * kTopkSegCap
+  int cnt[2][kTopkSegs];
+  double lse2[2];
+  float theta[2];
+  int lists[2];
+};
+
+// One wave: row statistics of a segmented top-k row from its segment records (row `which` of item
+// (i, k)): the row's K-th largest raw logit theta and the log2-sum-exp over the values >= theta (terms
+// as 2^-48 fixed-point integers referenced at M = ceil(max * c_hi), exact in any order: the value
+// topk_stats gives), into sh.lse2 / sh.theta / sh.lists[w] (lists: every segment was listed and the
+// row keeps at most kTopkEmitKept entries, so the emit may draw from the lists).  theta is the K-th
+// largest over the union of the segments' lists when every segment was listed (the union holds every
+// value >= theta); otherwise the wave finds it by counting passes over the row itself.
+template <bool BF16>
+__device__ __forceinline__ void merge_row(MergeShared& sh, const VerifyArgs& a, int i, int k, int which,
+                                          const char* row, int K, float c_hi, float c_lo, int w, int lane) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  static_assert(kTopkSegCap <= 2 * SPEC_WAVE, "two list entries per lane");
+  const int nsk = a.nseg_topk;
+  const size_t slot = topk_slot(a.G, i, k, which);
+  const TopkSeg r = (lane < nsk) ? a.tk_seg[slot + lane] : TopkSeg{0, -INFINITY, -INFINITY, 0};
+  const bool over = __ballot(r.n > kTopkSegCap) != 0ull;
+  const float rmax = wave_max(r.vmax);
+  const int rbad = wave_or_i(r.bad);
+  const float M = ceilf(rmax * c_hi);
+  float* zs = sh.z[w];
+  uint32_t t = 0;
+  long long q64 = 0;
+  int kept = 0;
+  if (!over) {
+    // the segments' values into LDS region s (loads of every segment issued together)
+    float zl[kTopkSegs][2];
+#pragma unroll
+    for (int s = 0; s < kTopkSegs; ++s) {
+      const int ns = (s < nsk) ? read_lane(r.n, s) : 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = lane + h * SPEC_WAVE;
+        zl[s][h] = (q < ns) ? a.tk_val[(slot + s) * kTopkSegCap + q] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kTopkSegs; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = lane + h * SPEC_WAVE;
+        if (q < kTopkSegCap) zs[s * kTopkSegCap + q] = zl[s][h];
+      }
+    if (lane < kTopkSegs) sh.cnt[w][lane] = (lane < nsk) ? r.n : 0;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    t = kth_region_key<BF16>(zs, kTopkSegCap, sh.cnt[w], 0, nsk, K, lane);
+    for (int s = 0; s < nsk; ++s) {
+      const int ns = sh.cnt[w][s];
+      for (int q0 = 0; q0 < ns; q0 += SPEC_WAVE) {
+        const int q = q0 + lane;
+        const float z = (q < ns) ? zs[s * kTopkSegCap + q] : -INFINITY;
+        const bool keep = q < ns && fkey(z) >= t;
+        kept += (int)__popcll(__ballot(keep));
+        if (keep)
+          q64 += (long long)rint((double)__builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -M))) * 0x1p48);
+      }
+    }
+  } else {
+    // counting passes over the row: t = the largest key with at least K values' keys >= t
+    const RowGeom g = row_geom<BF16>(row, a.V);
+    const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
+    auto count_ge = [&](uint32_t trial) {
+      int c = 0;
+      for (int v = lane; v < g.nvec; v += SPEC_WAVE) {
+        float z[EPV];
+        unpack<BF16>(vp[v], z);
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) c += (z[j] == z[j]) && fkey(z[j]) >= trial;
+      }
+      for (int e = lane; e < g.head + g.tail; e += SPEC_WAVE) {
+        const float z = load_elem<BF16>(row, e < g.head ? e : g.nvec * EPV + e);
+        c += (z == z) && fkey(z) >= trial;
+      }
+      return wave_sum_i(c);
+    };
+    for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+      const uint32_t trial = t | (1u << bit);
+      if (count_ge(trial) >= K) t = trial;
+    }
+    if (BF16 && t != 0u && t < 0x80000000u) t |= 0xffffu;
+    for (int v = lane; v < g.nvec; v += SPEC_WAVE) {
+      float z[EPV];
+      unpack<BF16>(vp[v], z);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j)
+        if (z[j] == z[j] && fkey(z[j]) >= t)
+          q64 += (long long)rint((double)__builtin_amdgcn_exp2f(fmaf(z[j], c_lo, fmaf(z[j], c_hi, -M))) * 0x1p48);
+    }
+    for (int e = lane; e < g.head + g.tail; e += SPEC_WAVE) {
+      const float z = load_elem<BF16>(row, e < g.head ? e : g.nvec * EPV + e);
+      if (z == z && fkey(z) >= t)
+        q64 += (long long)rint((double)__builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -M))) * 0x1p48);
+    }
+  }
+  q64 = read_lane(wave_inclusive_sum_i64(q64, lane), 63);
+  if (lane == 0) {
+    const double Sr = (double)q64 * 0x1p-48;
+    sh.lse2[w] = (rbad || !(rmax < INFINITY) || !(Sr > 0.0)) ? NAN : (double)M + log2(Sr);
+    sh.theta[w] = (t == 0u) ? -INFINITY : key_to_float(t);   // t = 0: fewer than K values, all kept
+    sh.lists[w] = !over && kept <= kTopkEmitKept;
+  }
 }
 
 // Reduce the per-thread (M, S, bad) of one row's waves into a segment Partial (written by lt == 0).
@@ -709,10 +1161,13 @@ __device__ __forceinline__ bool derive_item(const VerifyArgs& a, int g, int& i_o
 // One workgroup per (work item, segment).  Target row k and, when k < L, draft row k of
 // the item are streamed together by the two halves of the workgroup; a lone target row uses
 // all eight waves.  combine_kernel then finishes each item from its segment partials.
-// Top-k items are not segmented (segment 0 takes the whole rows and finishes the item).  The
-// grid holds the largest work list the call allows (every position of every request, or the
-// caller's token cap); workgroups past the actual list exit at once.
-template <bool BF16>
+// Top-k items with top_k <= kTopkSegMaxK list their segments' largest values (at most kTopkSegs
+// segments) for topk_merge_kernel; with a larger top_k, segment 0 streams the whole rows and
+// finishes the item.  The grid holds the largest work list the call allows (every position of
+// every request, or the caller's token cap); workgroups past the actual list exit at once.
+// TOPK: the call passes top_k (a separate instance, so that the register budget of calls without
+// top-k rows is not set by the top-k code).
+template <bool BF16, bool TOPK>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void stream_kernel(VerifyArgs a) {
   __shared__ StreamShared sh;
@@ -731,7 +1186,7 @@ void stream_kernel(VerifyArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
   const float T = a.greedy_only ? 0.f : a.temperature[i];
   if (!(T >= 0.f && T < INFINITY)) return;          // reported by emit_final_kernel
-  int K = (a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
+  int K = (TOPK && a.top_k && !a.greedy_only) ? a.top_k[i] : 0;
   if (K < 0) return;
   if (K >= V || T == 0.f) K = 0;   // the greedy rule reads raw rows: no kept set
   const int L = a.lengths ? a.lengths[i] : G;
@@ -750,7 +1205,19 @@ void stream_kernel(VerifyArgs a) {
   const float c_hi = __double2float_rz(c64);
   const float c_lo = fmaxf((float)(c64 - (double)c_hi), 1e-30f);
 
-  if (K > 0) {
+  if (TOPK && K > 0) {
+    const int nsk = a.nseg_topk;
+    if (nsk > 1 && K <= kTopkSegMaxK) {
+      // one of the row's nsk segments, listed; topk_merge_kernel finishes the item
+      if (seg >= nsk) return;
+      const RowGeom geo = row_geom<BF16>(row, V);
+      const int vb = (int)((long long)geo.nvec * seg / nsk);
+      const int ve = (int)((long long)geo.nvec * (seg + 1) / nsk);
+      const size_t slot = topk_slot(G, i, k, which) + seg;
+      topk_segment<BF16>(sh, row, V, vb, ve, seg == 0, K, lt, nthr, wave, lane, first_wave, nwaves,
+                         a.tk_seg + slot, a.tk_val + slot * kTopkSegCap, a.tk_ids + slot * kTopkSegCap);
+      return;
+    }
     if (seg != 0) return;
     topk_stats<BF16>(sh, row, V, K, c_hi, c_lo, lt, nthr, wave, lane, first_wave, nwaves, which);
     __syncthreads();
@@ -807,8 +1274,44 @@ void stream_kernel(VerifyArgs a) {
   }
 }
 
+// The segmented top-k items (0 < K <= kTopkSegMaxK, rows in more than one segment), one 128-thread
+// workgroup each: wave 0 merges the target row's segments, wave 1 the draft row's (k < L), then the
+// acceptance test.  Other items exit at once.
+template <bool BF16>
+__global__ __launch_bounds__(2 * SPEC_WAVE) void topk_merge_kernel(VerifyArgs a) {
+  __shared__ MergeShared sh;
+  int i, k;
+  if (a.derive_items) {
+    if (!derive_item(a, (int)blockIdx.x, i, k)) return;
+  } else {
+    if ((int)blockIdx.x >= *a.nitems) return;
+    const int item = a.items[blockIdx.x];
+    i = item >> 7;
+    k = item & 127;
+  }
+  const int G = a.G, V = a.V;
+  constexpr int ES = BF16 ? 2 : 4;
+  const float T = a.temperature[i];
+  if (!(T > 0.f && T < INFINITY)) return;
+  const int K = a.top_k[i];
+  if (!(K > 0 && K < V && K <= kTopkSegMaxK)) return;
+  const int L = a.lengths ? a.lengths[i] : G;
+  const bool two = k < L;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const char* trow = target_row<ES>(a, i, k);
+  const char* drow = two ? draft_row<ES>(a, i, k) : nullptr;
+  const double c64 = kLog2e / (double)T;
+  const float c_hi = __double2float_rz(c64);
+  const float c_lo = fmaxf((float)(c64 - (double)c_hi), 1e-30f);
+  if (wave == 0 || two) merge_row<BF16>(sh, a, i, k, wave, wave ? drow : trow, K, c_hi, c_lo, wave, lane);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    accept_item<BF16>(a, i, k, two, c64, sh.lse2[0], sh.theta[0], two ? sh.lse2[1] : 0.0,
+                      two ? sh.theta[1] : -INFINITY, trow, drow, sh.lists[0], two ? sh.lists[1] : 0);
+}
+
 // Finish every segmented work item: combine its segment partials and run the acceptance
-// test (one thread per item).  Top-k items were finished by the streaming kernel.
+// test (one thread per item).  Top-k items were finished by the streaming or merging kernel.
 __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a) {
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= *a.nitems) return;
@@ -873,7 +1376,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t rows_t, rows_d, acc, items, items_x, nitems, req_status, ereq, ranges, amb, part_t, part_d, t_off, d_off,
-      total;
+      tk_seg, tk_val, tk_ids, total;
 };
 
 // Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
@@ -882,7 +1385,8 @@ static int stream_segments(int V, int es) {
   return (int)(n < 1 ? 1 : (n > kMaxStreamSegs ? kMaxStreamSegs : n));
 }
 
-static WsLayout ws_layout(int B, int G, int V, int nseg) {
+// V = 1 for calls with no emit ranges; topk = false for calls that never stream top-k rows (greedy).
+static WsLayout ws_layout(int B, int G, int V, int nseg, bool topk) {
   WsLayout l;
   size_t o = 0;
   l.rows_t = o; o = align256(o + sizeof(RowStat) * (size_t)B * (G + 1));
@@ -899,6 +1403,10 @@ static WsLayout ws_layout(int B, int G, int V, int nseg) {
   l.part_d = o; o = align256(o + sizeof(Partial) * (size_t)B * (G + 1) * nseg);
   l.t_off = o; o = align256(o + sizeof(int64_t) * (size_t)B);
   l.d_off = o; o = align256(o + sizeof(int64_t) * (size_t)B);
+  const size_t tk = topk ? topk_slot(G, B, 0, 0) : 0;   // records: every (item, row, segment)
+  l.tk_seg = o; o = align256(o + sizeof(TopkSeg) * tk);
+  l.tk_val = o; o = align256(o + sizeof(float) * tk * kTopkSegCap);
+  l.tk_ids = o; o = align256(o + sizeof(int32_t) * tk * kTopkSegCap);
   l.total = o;
   return l;
 }
@@ -928,7 +1436,7 @@ int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size
       !grid_fits((uint64_t)a.B * (uint64_t)(a.G + 1), 1))
     return SPEC_ERR_UNSUPPORTED;
   // greedy and overlap calls have no emit ranges
-  const WsLayout l = ws_layout(a.B, a.G, (a.greedy_only || a.overlap_only) ? 1 : a.V, a.nseg);
+  const WsLayout l = ws_layout(a.B, a.G, (a.greedy_only || a.overlap_only) ? 1 : a.V, a.nseg, !a.greedy_only);
   if (!ws || ws_bytes < l.total + extra_bytes) return SPEC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return SPEC_ERR_WORKSPACE;
   char* w = reinterpret_cast<char*>(ws);
@@ -946,12 +1454,16 @@ int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size
   a.part_d = reinterpret_cast<Partial*>(w + l.part_d);
   a.t_off = reinterpret_cast<int64_t*>(w + l.t_off);
   a.d_off = reinterpret_cast<int64_t*>(w + l.d_off);
+  a.tk_seg = reinterpret_cast<TopkSeg*>(w + l.tk_seg);
+  a.tk_val = reinterpret_cast<float*>(w + l.tk_val);
+  a.tk_ids = reinterpret_cast<int32_t*>(w + l.tk_ids);
+  a.nseg_topk = std::min(a.nseg, kTopkSegs);
   if (extra) *extra = w + l.total;
   return SPEC_OK;
 }
 
-size_t workspace_bytes(int B, int G, int V, bool emit) {
-  return ws_layout(B, G, emit ? V : 1, kMaxStreamSegs).total;   // the largest segment count, fp32 or bf16
+size_t workspace_bytes(int B, int G, int V, bool emit, bool topk) {
+  return ws_layout(B, G, emit ? V : 1, kMaxStreamSegs, topk).total;   // the largest segment count, fp32 or bf16
 }
 
 void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1) {
@@ -966,10 +1478,22 @@ void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0,
   // The events take the dispatch's own start and end times (no marker packets around it, which
   // would stall the stream before and after the kernel); a failure shows on the caller's event query.
   const hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev0), e1 = reinterpret_cast<hipEvent_t>(ev1);
-  if (dtype == SPEC_BF16)
-    hipExtLaunchKernelGGL(stream_kernel<true>, grid, block, 0, s, e0, e1, 0, a);
-  else
-    hipExtLaunchKernelGGL(stream_kernel<false>, grid, block, 0, s, e0, e1, 0, a);
+  const bool topk = a.top_k && !a.greedy_only;
+  if (dtype == SPEC_BF16) {
+    if (topk) hipExtLaunchKernelGGL((stream_kernel<true, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((stream_kernel<true, false>), grid, block, 0, s, e0, e1, 0, a);
+  } else {
+    if (topk) hipExtLaunchKernelGGL((stream_kernel<false, true>), grid, block, 0, s, e0, e1, 0, a);
+    else hipExtLaunchKernelGGL((stream_kernel<false, false>), grid, block, 0, s, e0, e1, 0, a);
+  }
+  // segmented top-k rows are merged before anything reads their statistics
+  if (topk && a.nseg_topk > 1) {
+    const dim3 mgrid((unsigned)items), mblock(2 * SPEC_WAVE);
+    if (dtype == SPEC_BF16)
+      hipLaunchKernelGGL(topk_merge_kernel<true>, mgrid, mblock, 0, s, a);
+    else
+      hipLaunchKernelGGL(topk_merge_kernel<false>, mgrid, mblock, 0, s, a);
+  }
 }
 
 void launch_combine(const VerifyArgs& a, hipStream_t s) {
@@ -1004,12 +1528,12 @@ using namespace spec;
 
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_V) return 0;
-  return workspace_bytes(B, gamma, V, true);
+  return workspace_bytes(B, gamma, V, true, true);
 }
 
 extern "C" size_t spec_verify_greedy_workspace_size(int32_t B, int32_t gamma) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA) return 0;
-  return workspace_bytes(B, gamma, 1, false);
+  return workspace_bytes(B, gamma, 1, false, false);
 }
 
 static int32_t verify_entry(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const void* target_logits,
@@ -1110,7 +1634,7 @@ extern "C" int32_t spec_verify_static(int32_t B, int32_t gamma, int32_t V, int32
     return SPEC_ERR_INVALID_ARG;
   if (!aligned16(target_logits) || !aligned16(draft_logits)) return SPEC_ERR_INVALID_ARG;
   // a shape whose workspace does not fit the array is refused before any HIP call
-  if (workspace_bytes(B, gamma, V, true) > (size_t)SPEC_STATIC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  if (workspace_bytes(B, gamma, V, true, true) > (size_t)SPEC_STATIC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
   void* ws = nullptr;
   const int32_t rc = static_scratch(&ws);
   if (rc != SPEC_OK) return rc;

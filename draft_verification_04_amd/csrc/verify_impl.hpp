@@ -48,6 +48,30 @@ struct EmitReq {
   int32_t pad;
 };
 
+// Top-k rows (sampling requests with 0 < top_k <= kTopkSegMaxK) are streamed in up to kTopkSegs
+// segments.  Each segment lists its values at or above its own K-th largest value, with their token
+// ids: a superset of the row's kept tokens inside it, since a segment's K-th largest is at most the
+// row's.  The last of an item's segment workgroups to finish merges the lists into the row's exact
+// threshold and normaliser, and the emit draws from the lists instead of reading the rows again.
+constexpr int kTopkSegs = 4;        // segments of a top-k row, at most
+constexpr int kTopkSegMaxK = 64;    // larger top_k: the row is streamed whole by one workgroup
+constexpr int kTopkSegCap = 96;     // (value, id) entries kept per (row, segment)
+// A wave's LDS region while streaming a segment: the raw 16-byte vectors holding a candidate (and
+// their vector indices), then, expanded in place, the candidates (value, token id).
+constexpr int kTopkWaveHits = 192;                       // candidate vectors a wave may keep
+constexpr int kTopkRegionBytes = kTopkWaveHits * 20;     // 16-byte vector + 4-byte index each
+constexpr int kTopkWaveCand = kTopkRegionBytes / 8;      // candidates a region holds (480)
+constexpr int kTopkSegCand = 8 * kTopkWaveCand;          // the workgroup's candidate buffer (8 waves)
+constexpr int kTopkEmitKept = 2 * SPEC_WAVE;      // kept entries per row the emit draws from, at most
+
+struct TopkSeg {
+  int32_t n;      // entries stored; kTopkSegCap + 1 when the segment could not be listed (too many
+                  // values at its cut, or too many candidates)
+  float theta;    // the segment's K-th largest raw logit (ties counted)
+  float vmax;     // the segment's largest raw logit
+  int32_t bad;    // NaN or +inf seen in the segment
+};
+
 struct VerifyArgs {
   int B, G, V;
   int greedy_only;
@@ -88,7 +112,16 @@ struct VerifyArgs {
   int wl_ready;        // the work list was written by the scheduler's last kernel (no work-list kernel)
   int derive_items;    // request-major work list: items[r] = request r's first item, *nitems the total
                        // (B <= 2 * kStreamThreads); each streaming workgroup finds its own request
+  int nseg_topk;       // segments of a top-k row (1: top-k rows are streamed whole)
+  TopkSeg* tk_seg;     // [B, G+1, 2, kTopkSegs] per (item, target/draft row, segment)
+  float* tk_val;       // [B, G+1, 2, kTopkSegs, kTopkSegCap] raw logits at or above each segment's cut
+  int32_t* tk_ids;     // same shape: their token ids
 };
+
+// Index of the TopkSeg record of (request i, position k, row `which` (0 target, 1 draft), segment 0).
+__host__ __device__ inline size_t topk_slot(int G, int i, int k, int which) {
+  return (((size_t)i * (G + 1) + k) * 2 + which) * kTopkSegs;
+}
 
 constexpr int kStreamThreads = 512;
 constexpr int kMaxStreamSegs = 16;   // segments per row in the streaming kernel, at most
@@ -345,7 +378,7 @@ bool aligned16(const void* p);
 // Point the workspace arrays of `a` into ws (after `extra_bytes` more for the caller at *extra,
 // 256-byte aligned); SPEC_ERR_WORKSPACE when it is missing, short or misaligned.
 int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size_t extra_bytes, char** extra);
-size_t workspace_bytes(int B, int G, int V, bool emit);
+size_t workspace_bytes(int B, int G, int V, bool emit, bool topk);
 // Work list (unless a.wl_ready), then the streaming statistics (events, when given, bracket the
 // streaming kernel).
 void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1);

@@ -52,6 +52,7 @@ def _check(got, ref, st_got, st_ref):
     ("mid", dict(B=6, gamma=5, V=20011, seed=7)),
     ("mid", dict(B=4, gamma=3, V=60000, seed=8)),
     ("mixed", dict(B=12, gamma=4, V=30001, seed=9)),
+    ("mixed", dict(B=8, gamma=3, V=129280, seed=12)),      # segmented top-k rows
     ("scheduled", dict(B=16, gamma=16, V=151936, seed=10)),
 ])
 def test_small_all_requests(sv, name, kw):

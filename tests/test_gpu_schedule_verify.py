@@ -41,7 +41,7 @@ def _both(sv, w, sps, budget, mode):
     return fused, sch, two
 
 
-def _check(sv, w, sps, budget, mode, with_oracle=True):
+def _check(sv, w, sps, budget, mode, with_oracle=True, verify_oracle=None):
     print(f"case B={w.B} gamma={w.gamma} V={w.V} budget={budget} mode={mode}", flush=True)
     fused, sch, two = _both(sv, w, sps, budget, mode)
     assert torch.equal(fused["lengths"], sch["lengths"])
@@ -53,7 +53,9 @@ def _check(sv, w, sps, budget, mode, with_oracle=True):
     if with_oracle:
         L_ref, _ = oracle.schedule(w.conf.cpu().numpy(), sps, budget, mode)
         assert np.array_equal(to_np(fused["lengths"]), L_ref)
-        if w.V * w.B <= 1 << 22:   # the verification outputs too (the full-size case has its own test)
+        if verify_oracle is None:   # the verification outputs too (the full-size case has its own test)
+            verify_oracle = w.V * w.B <= 1 << 22
+        if verify_oracle:
             h = HostInputs.of_workload(w, L_ref)
             ref = run_oracle_pooled(h)
             over = _over_budget(L_ref, budget)
@@ -103,6 +105,14 @@ def test_mixed_recipe(sv):
     # temperatures, top-k 50 and per-request seeds, with a schedule
     w = make_workload("mixed", DEV, B=300, V=3000, seed=72, with_schedule=True)
     _check(sv, w, w.sps, w.budget, MODE_GLOBAL)
+
+
+@pytest.mark.timeout(600)
+def test_mixed_recipe_segmented_top_k(sv):
+    # rows of 129280 bf16 logits: top-k 50 rows split into four segments whose id lists are
+    # merged; 300 requests take the fused emit and the request-major work list
+    w = make_workload("mixed", DEV, B=300, gamma=4, V=129280, seed=79, with_schedule=True)
+    _check(sv, w, w.sps, w.budget, MODE_GLOBAL, verify_oracle=True)
 
 
 def test_beyond_one_workgroup(sv):

@@ -297,6 +297,89 @@ def test_nearly_identical_rows_take_the_exact_residual_path(sv):
 
 
 
+def _segmented_topk_case(rng, B, G, V):
+    """Sampling requests with top-k, on rows long enough to be split into segments (top_k <= 64
+    merges per-segment id lists; larger top_k streams rows whole), with the rows that take the
+    fall-backs: candidate and id-list overflow, ties at the cut, the kept set inside one segment,
+    invalid values in a later segment, greedy requests with a top-k."""
+    t = rng.normal(0, 3, (B, G + 1, V)).astype(np.float32)
+    d = t[:, :G] + rng.normal(0, 0.8, (B, G, V)).astype(np.float32)
+    Ks = [1, 2, 17, 50, 64, 65, 200, 0, V - 1, V]
+    K = np.array([Ks[i % len(Ks)] for i in range(B)], dtype=np.int32)
+    T = rng.uniform(0.6, 1.2, B).astype(np.float32)
+    L = rng.integers(0, G + 1, B).astype(np.int32)
+    q = V // 4
+    for base in range(0, B, 16):
+        if base + 15 >= B:
+            break
+        r = base
+        T[r], K[r] = 0.0, 50                                        # greedy rule: top-k ignored
+        r += 1
+        t[r] = rng.integers(-3, 4, t[r].shape)                      # massive ties: candidate overflow
+        d[r] = rng.integers(-3, 4, d[r].shape)
+        K[r] = 50
+        r += 1
+        t[r, :, 2 * q:2 * q + 100] = t[r].max() + 5.0                # 100 tokens tie at the cut: id overflow
+        K[r] = 50
+        r += 1
+        t[r, :, V - 200:] += 10.0                                    # every kept token in the last segment
+        d[r, :, V - 200:] += 10.0
+        K[r] = 40
+        r += 1
+        t[r, 0, 3 * q + 7] = np.nan                                  # NaN in a later segment
+        K[r], L[r] = 50, G
+        r += 1
+        d[r, 0, q + 3] = np.inf                                      # +inf in a draft row's second segment
+        K[r], L[r] = 50, G
+        r += 1
+        K[r], L[r] = 1, 0                                            # top-1, appended token only
+        r += 1
+        d[r] = t[r, :G]                                              # identical rows: all accepted
+        K[r], L[r] = 64, G
+        r += 1
+        K[r] = 64                                                    # 11 values tie at the 60th largest,
+        for k in range(G + 1):                                       # spread over the segments
+            v60 = np.sort(t[r, k])[::-1][59]
+            t[r, k, rng.choice(V, 10, replace=False)] = v60
+    x = np.zeros((B, G), dtype=np.int32)
+    for i in range(B):
+        for k in range(G):
+            if K[i] > 0 and rng.random() < 0.7:     # mostly inside the draft's kept set
+                x[i, k] = int(np.argsort(-d[i, k], kind="stable")[rng.integers(0, min(int(K[i]), 5))])
+            else:
+                x[i, k] = int(rng.integers(0, V))
+    for base in range(0, B - 15, 16):
+        x[base + 7] = np.argmax(d[base + 7], axis=-1)              # in the kept set of both rows
+    seed = rng.integers(0, 2 ** 63, B).astype(np.int64)
+    return t, d, x, L, T, K, seed
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,V,dtype", [
+    (32, 129280, torch.bfloat16),    # four segments per row; split emit
+    (256, 129280, torch.bfloat16),   # fused emit
+    (32, 65536, torch.float32),      # fp32 rows, four segments
+    (48, 30001, torch.float32),      # fp32, two segments, rows off 16-byte boundaries
+])
+def test_segmented_topk_all_requests(sv, B, V, dtype):
+    rng = np.random.default_rng(B + V)
+    G = 4 if B <= 48 else 2
+    t, d, x, L, T, K, seed = _segmented_topk_case(rng, B, G, V)
+    tt = torch.from_numpy(t).to(DEV).to(dtype)
+    dd = torch.from_numpy(d).to(DEV).to(dtype)
+    args = [torch.from_numpy(a).to(DEV) for a in (x, L, T, K, seed)]
+    out = sv.verify(tt, dd, *args)
+    torch.cuda.synchronize()
+    h = HostInputs.of(tt, dd, x, L, T, K, seed)
+    ref = run_oracle_pooled(h)
+    s = compare_verify(out, ref, inputs=h)
+    print(B, V, dtype, s, flush=True)
+    st = to_np(out["status"])
+    for base in range(0, B - 15, 16):
+        assert st[base + 4] == oracle.STATUS_NONFINITE and st[base + 5] == oracle.STATUS_NONFINITE
+        assert int(to_np(out["num_accepted"])[base + 7]) == G
+
+
 def _flatten(w, L):
     Lh = to_np(L).astype(np.int64)
     G = w.gamma
@@ -311,6 +394,7 @@ def _flatten(w, L):
     ("tiny", dict(B=40, gamma=6, V=999, seed=5)),
     ("mid", dict(B=6, gamma=5, V=20011, seed=7)),
     ("mixed", dict(B=12, gamma=4, V=30001, seed=9)),
+    ("mixed", dict(B=8, gamma=3, V=129280, seed=12)),     # segmented top-k rows
     ("scheduled", dict(B=300, gamma=8, V=4096, seed=11)),
 ])
 def test_flat_layout_equals_padded(sv, name, kw):
@@ -345,6 +429,7 @@ def test_flat_layout_equals_padded(sv, name, kw):
     ("scheduled", dict(B=300, gamma=8, V=4096, seed=11), (1, 37, 299, 10 ** 6)),
     ("mid", dict(B=6, gamma=5, V=20011, seed=7), (1, 5, 36)),
     ("mixed", dict(B=12, gamma=4, V=30001, seed=9), (3, 60)),
+    ("mixed", dict(B=8, gamma=3, V=129280, seed=12), (2, 17)),   # segmented top-k rows
 ])
 def test_token_cap(sv, name, kw, bounds):
     """spec_verify_bounded: requests in index order add L_i + 1 (valid lengths only) to a running
