@@ -8,7 +8,7 @@
 // One draft step k is two kernels:
 //   markov_logits_kernel -- for every request at once, the bias is a dense product
 //       [B x r] (gathered embedding rows) x [r x V] (projection): MFMA 16x16x32 bf16 tiles with
-//       fp32 accumulation.  Each wave keeps the projection rows of its 16 tokens in registers and
+//       fp32 accumulation.  Each wave keeps the projection rows of its 32 tokens in registers and
 //       walks the requests 32 at a time; the epilogue adds U_k, rounds to the storage type, writes
 //       the draft logits and records per (request, 128-token tile) the largest stored value and
 //       whether a NaN or +inf was stored.
@@ -40,8 +40,9 @@ typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kDraftThreads = 512;   // markov_logits_kernel: 8 waves
-constexpr int kTileTokens = 128;     // tokens per workgroup (16 per wave)
+constexpr int kDraftThreads = 256;   // markov_logits_kernel: 4 waves
+constexpr int kTileTokens = 128;     // tokens per workgroup (32 per wave)
+constexpr int kWaveTokens = kTileTokens / (kDraftThreads / 64);
 constexpr int kReqBlock = 32;        // requests per block (two MFMA columns of 16)
 constexpr int kMaxSteps = 16;        // rank / 16 at most (r <= 256)
 constexpr int kSampleThreads = 256;  // markov_finish_kernel: a wave per item
@@ -97,44 +98,50 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
 
 // Step k: draft logits z_k = U_k + W1[x_{k-1}] W2 for every request, and per-tile statistics.
 //
-// A workgroup owns 128 tokens (16 per wave) and walks the requests 32 at a time.  Per request
-// block: each wave's MFMA 16x16x32 chain multiplies its projection rows (registers: 16 tokens x r,
-// 32 VGPRs at r = 256) by the block's embedding rows (LDS, two columns of 16 requests); the epilogue
-// reads U_k from an LDS tile, writes the rounded z_k back in place and folds the values into
-// statistics; after the block's barrier the workgroup stores the z_k tile with whole-line 16-byte
-// stores.  The embedding rows and the U_k tile of the next block are loaded (whole lines, 16 bytes
-// per thread) while the current block computes.  Tiles that are not whole (the last one, or rows
-// not 16-byte aligned) take per-element global accesses instead.  Operand k beyond r is zero on
-// both sides (exact zeros).  Sixteen tokens per wave keep the kernel within 128 VGPRs, so two
-// 8-wave workgroups share a CU.
+// A workgroup owns 128 tokens (32 per wave) and walks the requests 32 at a time.  Per request
+// block: each wave multiplies its projection rows (registers: two MFMA tiles of 16 tokens x r,
+// 64 VGPRs at r = 256) by the block's embedding rows (LDS, two columns of 16 requests), each
+// embedding operand read from LDS once for both token tiles (LDS reads of the operand bound this
+// kernel: 32 tokens per wave halve them against 16); the epilogue reads U_k from an LDS tile,
+// writes the rounded z_k back in place and folds the values into statistics; after the block's
+// barrier the workgroup stores the z_k tile with whole-line 16-byte stores.  The embedding rows and
+// the U_k tile of the next block are loaded (whole lines, 16 bytes per thread) while the current
+// block computes.  Tiles that are not whole (the last one, or rows not 16-byte aligned) take
+// per-element global accesses instead.  Operand k beyond r is zero on both sides (exact zeros).
+// About 51 KB of LDS (bf16) and at most 168 VGPRs let three 4-wave workgroups share a CU.
 template <int ES>
-__global__ __launch_bounds__(kDraftThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kDraftThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void markov_logits_kernel(DraftArgs a) {
   constexpr int RS = kMaxSteps * 16 + 8;            // LDS row stride of the embedding rows (bf16)
   constexpr int USB = kTileTokens * ES + 16;        // LDS row stride of the U/z tile (bytes)
   constexpr int UCPR = kTileTokens * ES / 16;       // 16-byte chunks per tile row
-  constexpr int UPT = kReqBlock * UCPR / kDraftThreads;  // chunks per thread (1 bf16, 2 fp32)
+  constexpr int UPT = kReqBlock * UCPR / kDraftThreads;  // chunks per thread (2 bf16, 4 fp32)
   constexpr int NW = kDraftThreads / 64;
   constexpr int NK = kMaxSteps / 2;                 // 16x16x32 steps at the largest rank
+  constexpr int RPT = kReqBlock * (kMaxSteps * 16 / 8) / kDraftThreads;   // embedding chunks per thread
+  static_assert(kWaveTokens == 32, "two 16-token MFMA tiles per wave");
   __shared__ DPart sp[2][NW][kReqBlock];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kReqBlock * RS];
-  __shared__ __attribute__((aligned(16))) unsigned char sU[3][kReqBlock * USB];
+  __shared__ __attribute__((aligned(16))) unsigned char sU[2][kReqBlock * USB];
   __shared__ int sPrev[4][kReqBlock];   // ids x_{k-1} of block b in sPrev[b % 4]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int tn = lane & 15, q = lane >> 4;   // MFMA row (token) / column (request), and k or row group
   const int V = a.V, r = a.r, G = a.G, k = a.k, B = a.B;
   const int tile0 = blockIdx.x * kTileTokens;
-  const int n0 = tile0 + wv * 16;
+  const int n0 = tile0 + wv * kWaveTokens;
   const bf16x8 zero8 = {};
 
-  // Projection operand (MFMA A: row = token n0 + tn, k = 32 s + 8 q .. + 7).
-  const uint16_t* w2 = a.W2t + (size_t)min(n0 + tn, V - 1) * r;
-  bf16x8 wop[NK];
+  // Projection operands (MFMA A of token tile t: row = token n0 + 16 t + tn, k = 32 s + 8 q .. + 7).
+  bf16x8 wop[2][NK];
 #pragma unroll
-  for (int s = 0; s < NK; ++s) {
-    const int kc = 32 * s + 8 * q;
-    const bf16x8 v = load_bf16x8(w2 + min(kc, r - 8));
-    wop[s] = kc < r ? v : zero8;
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* w2 = a.W2t + (size_t)min(n0 + 16 * t + tn, V - 1) * r;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const int kc = 32 * s + 8 * q;
+      const bf16x8 v = load_bf16x8(w2 + min(kc, r - 8));
+      wop[t][s] = kc < r ? v : zero8;
+    }
   }
 
   // x_{k-1} of request j (index clamped; a bad value selects row 0: a bad request's rows are
@@ -146,11 +153,11 @@ void markov_logits_kernel(DraftArgs a) {
   auto prev_of = [&](int j) -> int { return prev_ok(prev_raw(j)); };
   // Embedding rows W1[x_{k-1}] of a request block: 32 rows of r bf16, 16-byte chunks.
   const int cpr = r >> 3;
-  const int nchunk = kReqBlock * cpr;  // <= 1024: at most 2 per thread
-  v4u32 gw[2];
+  const int nchunk = kReqBlock * cpr;  // <= kReqBlock * 32: at most RPT per thread
+  v4u32 gw[RPT];
   auto load_rows = [&](int pb) {   // unconditional: chunks past the rows reload the last one
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < RPT; ++i) {
       const int c = min(tid + i * kDraftThreads, nchunk - 1);
       const int row = c / cpr, col = c - row * cpr;
       gw[i] = *reinterpret_cast<const v4u32*>(a.W1 + (size_t)sPrev[pb][row] * r + col * 8);
@@ -158,7 +165,7 @@ void markov_logits_kernel(DraftArgs a) {
   };
   auto store_rows = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < RPT; ++i) {
       const int c = tid + i * kDraftThreads;
       if (c < nchunk) {
         const int row = c / cpr, col = c - row * cpr;
@@ -182,6 +189,8 @@ void markov_logits_kernel(DraftArgs a) {
           reinterpret_cast<const v4u32*>(ubase + (size_t)j * rowstep * ES + col * 16));
     }
   };
+  // the same thread mapping for the tile's LDS writes and the global stores' LDS reads, so that a
+  // slot rewritten a block after its global store is ordered by program order
   auto store_tile_lds = [&](int ub) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
@@ -205,7 +214,9 @@ void markov_logits_kernel(DraftArgs a) {
 
   // The loads of block b + 2 are issued while block b computes and land in LDS at the end of
   // block b + 1, a whole block later, so no block waits for its own loads; the ids of block b + 4
-  // are fetched by wave 1 during block b and stored during block b + 1.
+  // are fetched by wave 1 during block b and stored during block b + 1.  Tile slot b % 2 is
+  // rewritten at the end of block b + 1, after its global store (issued after the barrier ending
+  // block b) by the same threads.
   const int nrb = (B + kReqBlock - 1) / kReqBlock;
   const bool idw = tid >= 64 && tid < 64 + kReqBlock;
   if (tid < kReqBlock) {
@@ -214,7 +225,6 @@ void markov_logits_kernel(DraftArgs a) {
   }
   // every thread fetches the ids (only wave 1 stores them): no load under a condition in the loop
   int pn = prev_raw(3 * kReqBlock + (tid & (kReqBlock - 1)));   // ids of block 3
-  typedef typename std::conditional<ES == 2, uint2, float4>::type UVec;
   // whole tiles (FAST) and the rest take separate copies of the walk, so no branch on the tile
   // kind sits inside it
   auto walk = [&](auto fast_c) {
@@ -229,22 +239,19 @@ void markov_logits_kernel(DraftArgs a) {
   __syncthreads();
 
   for (int rb = 0; rb < nrb; ++rb) {
-    const int buf = rb & 1, ub = rb % 3;
+    const int buf = rb & 1, ub = rb & 1;
     const bool more = rb + 1 < nrb;
     if (idw) sPrev[(rb + 3) & 3][tid - 64] = prev_ok(pn);    // ids of block rb + 3 (fetched a block ago)
     pn = prev_raw((rb + 4) * kReqBlock + (tid & (kReqBlock - 1)));   // ids of block rb + 4
     // this lane's U_k values of the current block (stored in LDS before the last barrier):
-    // requests 16 c + tn of the block (c = 0, 1), tokens n0 + 4 q .. + 3
-    unsigned char* urow[2];
-    UVec uv[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      urow[c] = &sU[ub][(16 * c + tn) * USB + (wv * 16 + 4 * q) * ES];
-      if constexpr (FAST) uv[c] = *reinterpret_cast<const UVec*>(urow[c]);
-    }
+    // requests 16 c + tn of the block (c = 0, 1), tokens n0 + 16 t + 4 q .. + 3
+    auto urow = [&](int t, int c) -> unsigned char* {
+      return &sU[ub][(16 * c + tn) * USB + (wv * kWaveTokens + 16 * t + 4 * q) * ES];
+    };
 
-    // Embedding operand (MFMA B: column = request 16 c + tn, k = 32 s + 8 q .. + 7) from LDS.
-    f32x4 acc[2] = {};
+    // Embedding operand (MFMA B: column = request 16 c + tn, k = 32 s + 8 q .. + 7) from LDS,
+    // each one used for both token tiles.
+    f32x4 acc[2][2] = {};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint16_t* rowp = &sB[buf][(16 * c + tn) * RS + 8 * q];
@@ -255,10 +262,13 @@ void markov_logits_kernel(DraftArgs a) {
         bop[s] = 32 * s + 8 * q < r ? v : zero8;
       }
 #pragma unroll
-      for (int s = 0; s < NK; ++s) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[s], bop[s], acc[c], 0, 0, 0);
+      for (int s = 0; s < NK; ++s) {
+        acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[0][s], bop[s], acc[0][c], 0, 0, 0);
+        acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[1][s], bop[s], acc[1][c], 0, 0, 0);
+      }
     }
 
-    // Epilogue: lane holds D[token n0 + 4 q + p][request 16 c + tn] in acc[c][p].
+    // Epilogue: lane holds D[token n0 + 16 t + 4 q + p][request 16 c + tn] in acc[t][c][p].
     float zm[2];
     int bad[2];
 #pragma unroll
@@ -266,54 +276,58 @@ void markov_logits_kernel(DraftArgs a) {
       const int j = rb * kReqBlock + 16 * c + tn;
       const bool valid = j < B;
       const size_t row = ((size_t)(valid ? j : 0) * G + k) * V;
-      const int t0 = n0 + 4 * q;
-      float zq[4];
+      float m = -__builtin_inff();
       int bd = 0;
-      if constexpr (FAST) {
-        float zs[4];
-        if constexpr (ES == 2) {
-          const uint2 w = uv[c];
-          zs[0] = bf16_lo(w.x) + acc[c][0];
-          zs[1] = bf16_hi(w.x) + acc[c][1];
-          zs[2] = bf16_lo(w.y) + acc[c][2];
-          zs[3] = bf16_hi(w.y) + acc[c][3];
-          uint2 o;
-          const f32x2 v0 = {zs[0], zs[1]}, v1 = {zs[2], zs[3]};
-          o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2));
-          o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2));
-          *reinterpret_cast<uint2*>(urow[c]) = o;
-          zs[0] = bf16_lo(o.x); zs[1] = bf16_hi(o.x); zs[2] = bf16_lo(o.y); zs[3] = bf16_hi(o.y);
-        } else {
-          const float4 w = uv[c];
-          zs[0] = w.x + acc[c][0];
-          zs[1] = w.y + acc[c][1];
-          zs[2] = w.z + acc[c][2];
-          zs[3] = w.w + acc[c][3];
-          *reinterpret_cast<float4*>(urow[c]) = make_float4(zs[0], zs[1], zs[2], zs[3]);
-        }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          zq[p] = valid ? zs[p] : -__builtin_inff();
-          bd |= valid && __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const bool in = valid && t0 + p < V;
-          float z = (in ? load_logit<ES>(a.base, row + t0 + p) : 0.f) + acc[c][p];
+      for (int t = 0; t < 2; ++t) {
+        const int t0 = n0 + 16 * t + 4 * q;
+        float zq[4];
+        if constexpr (FAST) {
+          float zs[4];
           if constexpr (ES == 2) {
-            const f32x2 v = {z, 0.f};
-            const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-            z = bf16_lo(o);
-            if (in) reinterpret_cast<uint16_t*>(a.logits)[row + t0 + p] = (uint16_t)o;
+            const uint2 w = *reinterpret_cast<const uint2*>(urow(t, c));
+            zs[0] = bf16_lo(w.x) + acc[t][c][0];
+            zs[1] = bf16_hi(w.x) + acc[t][c][1];
+            zs[2] = bf16_lo(w.y) + acc[t][c][2];
+            zs[3] = bf16_hi(w.y) + acc[t][c][3];
+            uint2 o;
+            const f32x2 v0 = {zs[0], zs[1]}, v1 = {zs[2], zs[3]};
+            o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2));
+            o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2));
+            *reinterpret_cast<uint2*>(urow(t, c)) = o;
+            zs[0] = bf16_lo(o.x); zs[1] = bf16_hi(o.x); zs[2] = bf16_lo(o.y); zs[3] = bf16_hi(o.y);
           } else {
-            if (in) reinterpret_cast<float*>(a.logits)[row + t0 + p] = z;
+            const float4 w = *reinterpret_cast<const float4*>(urow(t, c));
+            zs[0] = w.x + acc[t][c][0];
+            zs[1] = w.y + acc[t][c][1];
+            zs[2] = w.z + acc[t][c][2];
+            zs[3] = w.w + acc[t][c][3];
+            *reinterpret_cast<float4*>(urow(t, c)) = make_float4(zs[0], zs[1], zs[2], zs[3]);
           }
-          zq[p] = in ? z : -__builtin_inff();
-          bd |= in && __builtin_amdgcn_classf(z, 0x203);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            zq[p] = valid ? zs[p] : -__builtin_inff();
+            bd |= valid && __builtin_amdgcn_classf(zs[p], 0x203);  // NaN or +inf
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const bool in = valid && t0 + p < V;
+            float z = (in ? load_logit<ES>(a.base, row + t0 + p) : 0.f) + acc[t][c][p];
+            if constexpr (ES == 2) {
+              const f32x2 v = {z, 0.f};
+              const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+              z = bf16_lo(o);
+              if (in) reinterpret_cast<uint16_t*>(a.logits)[row + t0 + p] = (uint16_t)o;
+            } else {
+              if (in) reinterpret_cast<float*>(a.logits)[row + t0 + p] = z;
+            }
+            zq[p] = in ? z : -__builtin_inff();
+            bd |= in && __builtin_amdgcn_classf(z, 0x203);
+          }
         }
+        m = fmaxf(m, fmaxf(fmaxf(zq[0], zq[1]), fmaxf(zq[2], zq[3])));
       }
-      float m = fmaxf(fmaxf(zq[0], zq[1]), fmaxf(zq[2], zq[3]));
       // the four lane groups hold the same request
       m = fmaxf(m, __shfl_xor(m, 16, SPEC_WAVE));
       m = fmaxf(m, __shfl_xor(m, 32, SPEC_WAVE));
@@ -328,7 +342,7 @@ void markov_logits_kernel(DraftArgs a) {
     }
     if (more) {
       store_rows(buf ^ 1);                            // block rb + 1, read after the barrier below
-      if constexpr (FAST) store_tile_lds((rb + 1) % 3);
+      if constexpr (FAST) store_tile_lds((rb + 1) & 1);
     }
     load_rows((rb + 2) & 3);                          // block rb + 2 (past the end: valid ids, unused)
     if constexpr (FAST) load_tile(rb + 2);
