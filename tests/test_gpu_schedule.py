@@ -96,6 +96,22 @@ def test_bad_confidences(sv):
     L, th, st = _gpu(sv, conf, sps, 100, MODE_EARLY_STOP)
     assert st.tolist() == [0, oracle_bad(), oracle_bad(), 0]
     assert L[1] == 0 and L[2] == 0 and L[0] == 3 and L[3] == 3
+    # pools on both sides of the size the last kernel sorts by itself (4096 candidates): a bad
+    # request has no candidates, and the others are scheduled as the oracle schedules them
+    rng = np.random.default_rng(35)
+    for B, G in ((300, 13), (600, 8)):
+        conf = make_confidences(B, G, int(rng.integers(1 << 30))).numpy()
+        bad = rng.random(B) < 0.05
+        conf[bad, rng.integers(0, G, int(bad.sum()))] = np.where(rng.random(int(bad.sum())) < 0.5, np.nan, 1.25)
+        sps = make_sps_table(B * (G + 1) + 1, int(rng.integers(1 << 30)))
+        budget = B * (G + 1) // 2
+        ref_conf = conf.copy()
+        ref_conf[bad] = 0.0
+        for mode in (MODE_EARLY_STOP, MODE_GLOBAL):
+            L, th, st = _gpu(sv, conf, sps, budget, mode)
+            L_ref, th_ref = oracle.schedule(ref_conf, sps, budget, mode)
+            assert (st == np.where(bad, oracle_bad(), 0)).all(), (B, G, mode)
+            assert (L == L_ref).all() and th == th_ref, (B, G, mode)
 
 
 def oracle_bad():
