@@ -273,6 +273,17 @@ __device__ __forceinline__ void accum(const float (&z)[N], float c_hi, float c_l
   S += s;
 }
 
+// The largest of a vector's values by the IEEE 754-2019 maximum (v_maximum3_f32), which returns
+// NaN when any operand is NaN: the result is NaN or +inf exactly when a value is, so one compare
+// screens the vector for bad values.  Unlike fmaxf it needs no canonicalising of its operands.
+template <int N>
+__device__ __forceinline__ float vec_maximum(const float (&z)[N]) {
+  float m = z[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) m = __builtin_elementwise_maximum(m, z[j]);
+  return m;
+}
+
 // Vectors [vb, ve) of a row's 16-byte body, plus its scalar head and tail when `ends`.
 template <bool BF16>
 __device__ void stream_sum(const char* row, int V, int vb, int ve, bool ends, float c_hi, float c_lo, int lt,
@@ -324,13 +335,10 @@ __device__ void stream_argmax(const char* row, int V, int vb, int ve, bool ends,
   const RowGeom g = row_geom<BF16>(row, V);
   const uint4* vp = reinterpret_cast<const uint4*>(row + (size_t)g.head * ES);
   auto take = [&](const float (&z)[EPV], int vbase) {
-    float vmax = z[0];
-#pragma unroll
-    for (int j = 1; j < EPV; ++j) vmax = fmaxf(vmax, z[j]);
-    int nb = 0;
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) nb |= !(z[j] <= FLT_MAX);
-    bad |= nb;
+    // the NaN-propagating maximum: NaN or +inf exactly when the vector holds one (a bad row,
+    // whose argmax is never used)
+    const float vmax = vec_maximum<EPV>(z);
+    bad |= !(vmax <= FLT_MAX);
     if (vmax > best) {  // vectors of one thread arrive in increasing token order
       int j = 0;
       while (j < EPV - 1 && !(z[j] == vmax)) ++j;
@@ -797,21 +805,18 @@ __device__ __forceinline__ void topk_segment(StreamShared& sh, const char* row, 
     const bool valid = v < ve;
     float z[EPV];
     unpack<BF16>(dv, z);
-    float m = z[0];
-    int nb = 0;
-#pragma unroll
-    for (int j = 1; j < EPV; ++j) m = fmaxf(m, z[j]);
-#pragma unroll
-    for (int j = 0; j < EPV; j += 2) nb |= __builtin_isunordered(z[j], z[j + 1]);
-    nb |= m == INFINITY;
+    // NaN or +inf exactly when the vector holds one; then the row is bad and its list, maximum
+    // and hits are never used
+    const float m = vec_maximum<EPV>(z);
     if (valid) {
-      bad |= nb;
-      vmax = fmaxf(vmax, m);
+      bad |= !(m < INFINITY);
+      vmax = __builtin_elementwise_maximum(vmax, m);
     }
     const bool hit = valid && m >= tau;
     const unsigned long long mh = __ballot(hit);
     if (mh) {
-      const int slot = nh + (int)__popcll(mh & below);
+      const int slot = nh + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mh >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((unsigned)mh, 0u));
       if (hit && slot < kTopkWaveHits) {
         hvec[slot] = dv;
         hidx[slot] = v;
