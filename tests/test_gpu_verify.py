@@ -341,6 +341,22 @@ def _segmented_topk_case(rng, B, G, V):
         for k in range(G + 1):                                       # spread over the segments
             v60 = np.sort(t[r, k])[::-1][59]
             t[r, k, rng.choice(V, 10, replace=False)] = v60
+        r += 1
+        t[r, :, ::97] = -np.inf                                      # -inf logits (valid) in every segment,
+        d[r, :, ::89] = -np.inf                                      # whole 16-byte vectors of them too
+        t[r, :, q:q + 64] = -np.inf
+        d[r, :, 3 * q:3 * q + 64] = -np.inf
+        K[r], L[r] = 50, G
+        r += 1
+        T[r], L[r] = 0.0, G                                          # greedy rows: NaN in a later segment,
+        t[r, 0, 2 * q + 11] = np.nan
+        r += 1
+        T[r], L[r] = 0.0, G                                          # +inf in target row 1's last segment,
+        t[r, 1, 3 * q + 5] = np.inf
+        r += 1
+        T[r], L[r] = 0.0, G                                          # -inf logits, valid
+        t[r, :, ::5] = -np.inf
+        t[r, :, 2 * q:2 * q + 64] = -np.inf
     x = np.zeros((B, G), dtype=np.int32)
     for i in range(B):
         for k in range(G):
@@ -378,6 +394,8 @@ def test_segmented_topk_all_requests(sv, B, V, dtype):
     for base in range(0, B - 15, 16):
         assert st[base + 4] == oracle.STATUS_NONFINITE and st[base + 5] == oracle.STATUS_NONFINITE
         assert int(to_np(out["num_accepted"])[base + 7]) == G
+        assert st[base + 9] == 0 and st[base + 12] == 0                      # -inf is a valid logit
+        assert st[base + 10] == oracle.STATUS_NONFINITE and st[base + 11] == oracle.STATUS_NONFINITE
 
 
 def _flatten(w, L):
