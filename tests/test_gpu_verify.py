@@ -476,3 +476,35 @@ def test_token_cap(sv, name, kw, bounds):
         o = torch.from_numpy(over).to(DEV)
         assert (got["status"][o] == REQ_OVER_BUDGET).all() and (got["num_accepted"][o] == 0).all()
         assert (got["out_tokens"][o] == -1).all() and torch.isnan(got["accept_prob"][o]).all()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("dtype,V,G", [
+    (torch.bfloat16, 524288, 64),    # the largest bf16 rows and the longest block the library takes
+    (torch.float32, 262144, 8),      # the largest fp32 rows
+])
+def test_maximum_vocabulary_and_block(sv, dtype, V, G):
+    """Every position verified on rows of the largest vocabulary: a sampling request, a top-k of 64
+    (segmented rows, which at this size take the counting fall-back of the merge) and the greedy
+    rule, against the oracle."""
+    rng = np.random.default_rng(V + G)
+    B = 3
+    t = rng.standard_normal((B, G + 1, V), dtype=np.float32) * np.float32(3.0)
+    d = t[:, :G] + rng.standard_normal((B, G, V), dtype=np.float32) * np.float32(0.5)
+    T = np.array([1.0, 0.8, 0.0], dtype=np.float32)
+    K = np.array([0, 64, 0], dtype=np.int32)
+    L = np.full(B, G, dtype=np.int32)
+    x = np.argmax(d, axis=-1).astype(np.int32)            # the draft's top token: mostly accepted
+    x[:, 1::3] = rng.integers(0, V, (B, len(range(1, G, 3))))   # a random token: mostly rejected
+    seed = rng.integers(0, 2 ** 63, B).astype(np.int64)
+    tt = torch.from_numpy(t).to(DEV).to(dtype)
+    dd = torch.from_numpy(d).to(DEV).to(dtype)
+    del t, d
+    args = [torch.from_numpy(a).to(DEV) for a in (x, L, T, K, seed)]
+    out = sv.verify(tt, dd, *args)
+    torch.cuda.synchronize()
+    h = HostInputs.of(tt, dd, x, L, T, K, seed)
+    ref = run_oracle_pooled(h, block=1)
+    s = compare_verify(out, ref, inputs=h)
+    print(dtype, V, G, s, flush=True)
+    assert (to_np(out["status"]) == 0).all()
