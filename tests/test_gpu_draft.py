@@ -119,6 +119,7 @@ def _compare(got, ref, requests, G, exact_logits=True, rng=None, row0=0):
     (5, 8, 131, 16, 16, 3),        # two tiles, the second with 3 tokens; smallest rank
     (3, 4, 1, 32, 8, 4),           # a one-token vocabulary
     (9, 2, 20000, 256, 0, 5),
+    (3, 3, 262144, 256, 16, 6),    # the largest fp32 vocabulary (half of the largest bf16 one)
 ])
 def test_grid_inputs_exact(sv, dtype, B, G, V, r, d, seed):
     w = make_draft_inputs(B, G, V, r, d, dtype, "grid", "mixed", seed, DEV)
@@ -126,6 +127,17 @@ def test_grid_inputs_exact(sv, dtype, B, G, V, r, d, seed):
     ref = _oracle(w)
     stopped = _compare(got, ref, list(range(B)), G, exact_logits=True)
     assert stopped == 0
+
+
+@pytest.mark.timeout(600)
+def test_grid_inputs_exact_largest_vocabulary(sv):
+    """The largest vocabulary the sampler takes (bf16 rows), with the longest block: exact logits,
+    tokens and confidences."""
+    B, G, V = 2, 64, 524288
+    w = make_draft_inputs(B, G, V, 64, 0, "bf16", "grid", "mixed", 7, DEV)
+    got = _gpu(sv, w)
+    ref = _oracle(w)
+    assert _compare(got, ref, list(range(B)), G, exact_logits=True) == 0
 
 
 @pytest.mark.parametrize("B,G,V,seed,T", [

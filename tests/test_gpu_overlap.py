@@ -54,6 +54,8 @@ def _check(got, ref, st_got, st_ref):
     ("mixed", dict(B=12, gamma=4, V=30001, seed=9)),
     ("mixed", dict(B=8, gamma=3, V=129280, seed=12)),      # segmented top-k rows
     ("scheduled", dict(B=16, gamma=16, V=151936, seed=10)),
+    ("mid", dict(B=3, gamma=8, V=524288, seed=13)),        # the largest bf16 vocabulary
+    ("mid", dict(B=2, gamma=64, V=8192, seed=14)),         # the longest block
 ])
 def test_small_all_requests(sv, name, kw):
     w = make_workload(name, DEV, **kw)
