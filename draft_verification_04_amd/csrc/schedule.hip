@@ -15,7 +15,12 @@
 //
 // Candidates are ordered by the 32-bit key ~bits(a) (ascending key = descending
 // survival), ties by index r * gamma + j (request, then position).  One CU retires
-// only 64 lane operations per cycle, so the sort is spread over the chip:
+// only 64 lane operations per cycle, so the sort is spread over the chip.  Pools of at
+// most 8192 candidates (and few enough requests) take one kernel for it:
+//   runs_rank_kernel  every workgroup rebuilds all keys in LDS (each request's keys
+//                 form an ascending run) and places 16 candidates, each by binary
+//                 searches in the other requests' runs;
+// larger pools take two:
 //   keys_kernel   one wave per chunk of 64 candidates: survivals, and the chunk
 //                 sorted by (key, index) in registers, each key stored with its index;
 //   rank_kernel   one workgroup per chunk: each key's place in the whole pool is
@@ -25,7 +30,8 @@
 //   final_kernel  one workgroup: exclusive int64 scan of the fixed-point
 //                 survivals, Theta(m), first non-rise (early stop) or first maximum
 //                 (global), and per-request counts of the first m* entries of the
-//                 sorted pool, by their indices (LDS atomics).  In the combined
+//                 sorted pool, by their indices (LDS atomics); each thread reads its
+//                 own positions of the sorted pool straight from memory.  In the combined
 //                 schedule-and-verify call (B <= 1024) it also writes the verify work
 //                 list from the lengths it holds, in place of the work-list kernel.
 #include "common.hpp"
@@ -190,24 +196,143 @@ __global__ __launch_bounds__(kChunk * kRankParts) void rank_kernel(SchedArgs a) 
   }
 }
 
+// ---- keys and ranks in one kernel, for pools of at most kRunsMaxN ---------
+
+// A request's survivals never rise from one position to the next (each is the one before times a
+// factor in [0, 1], rounded to nearest, which cannot exceed it), so its keys form an ascending
+// run; a request with a bad confidence has kNoCandidate throughout, and once a survival reaches
+// 0 the rest of the run is kNoCandidate too.  The place of candidate p = (request rp, position jp)
+// in the pool sorted by (key, index) is then jp (the keys of its own run before it, ties broken by
+// position) plus, for every other request r, the number of r's keys below key(p) + [r < rp],
+// found by binary search in r's run.  Every workgroup rebuilds all keys in LDS from the
+// confidences (the same products as keys_kernel) and places kRunsCand candidates, each with
+// kRunsLanes threads that share out the other requests' runs.
+constexpr int kRunsThreads = 512;
+constexpr int kRunsLanes = 32;                           // threads per candidate
+constexpr int kRunsCand = kRunsThreads / kRunsLanes;     // candidates per workgroup
+constexpr int kRunsMaxN = 8192;                          // LDS words for the runs
+
+// Whether the one-kernel sort serves a pool of B runs of gamma keys: the keys fit in LDS (each run
+// gamma + 1 words apart when gamma is even, so that the stride is odd and threads reading the same
+// place of consecutive runs meet no bank conflict) and each thread's binary searches stay few
+// (B / kRunsLanes runs, floor(log2 gamma) + 1 steps each).
+inline bool runs_sort_fits(int B, int gamma) {
+  const int steps = 32 - __builtin_clz((unsigned)gamma);
+  return (long long)B * (gamma | 1) <= kRunsMaxN && (long long)B * steps <= 128ll * kRunsLanes;
+}
+
+__global__ __launch_bounds__(kRunsThreads) void runs_rank_kernel(SchedArgs a) {
+  __shared__ unsigned keys[kRunsMaxN + 1];   // the last word: a spare slot for discarded keys
+  const int B = a.B, G = a.G, N = B * G;
+  const int RS = G | 1;   // LDS stride of a run: G, or G + 1 when G is even
+  const int tid = threadIdx.x;
+  // the confidences, every thread's loads in flight together; candidate x = r G + j goes to
+  // r RS + j, with r = floor(x / G) as the high word of x * ceil(2^32 / G) (exact: x (G - 1) < 2^32;
+  // odd G, G = 1 among them, keeps x in place)
+  {
+    constexpr int PER = kRunsMaxN / kRunsThreads;
+    const unsigned magic = G > 1 ? (unsigned)((0x100000000ull + (unsigned)G - 1) / (unsigned)G) : 0u;
+    float cv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int x = tid + e * kRunsThreads;
+      cv[e] = x < N ? a.conf[x] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int x = tid + e * kRunsThreads;
+      const int r = (int)__umulhi((unsigned)x, magic);
+      if (x < N) keys[x + r * (RS - G)] = __float_as_uint(cv[e]);
+    }
+  }
+  __syncthreads();
+  // each request's run of keys, in place, sixteen confidences at a time (without branches: reads
+  // past the run repeat its last word, and keys past it go to a spare slot)
+  for (int r = tid; r < B; r += kRunsThreads) {
+    unsigned* run = keys + r * RS;
+    bool bad = false;
+    float sv = 0.f;
+    for (int t0 = 0; t0 < G; t0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = __uint_as_float(run[min(t0 + u, G - 1)]);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const bool in = t0 + u < G;
+        bad |= in && !(v[u] >= 0.f && v[u] <= 1.f);
+        const float nx = (t0 + u == 0) ? v[u] : __fmul_rn(sv, v[u]);
+        sv = in ? nx : sv;
+        keys[in ? r * RS + t0 + u : kRunsMaxN] = surv_key(sv);
+      }
+    }
+    if (bad)
+      for (int t = 0; t < G; ++t) run[t] = kNoCandidate;
+    if (blockIdx.x == 0 && a.status) a.status[r] = bad ? SPEC_REQ_BAD_CONFIDENCE : 0;
+  }
+  __syncthreads();
+  const int c = tid / kRunsLanes, t = tid % kRunsLanes;
+  const int p = blockIdx.x * kRunsCand + c;
+  const bool valid = p < N;
+  const int pc = valid ? p : 0;
+  const int rp = pc / G, jp = pc - rp * G;
+  const unsigned kp = keys[rp * RS + jp];
+  // run r's keys that precede p: those <= kp when r < rp (ties go to the lower index), else those
+  // < kp, i.e. <= kp - 1 (no key is 0: a key is ~bits of a positive float, or kNoCandidate)
+  const unsigned lim_lo = kp, lim_hi = kp - 1u;
+  // binary lifting: the count n of keys <= lim in a sorted run is built from the powers of two
+  // below 2^steps > G, adding h when key n + h - 1 is still <= lim
+  const int top = 1 << (31 - __clz(G));   // the largest power of two <= G
+  constexpr int S = 8;                    // searches in flight per thread
+  int cnt = 0;
+  for (int r0 = t; r0 < B; r0 += kRunsLanes * S) {
+    int base[S], n[S];
+    unsigned lim[S];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      // a run not to count searches run 0 with limit 0, which no key is at or below
+      const int r = r0 + u * kRunsLanes;
+      const bool on = r < B && r != rp;
+      base[u] = on ? r * RS : 0;
+      n[u] = 0;
+      lim[u] = on ? (r < rp ? lim_lo : lim_hi) : 0u;
+    }
+    for (int h = top; h > 0; h >>= 1) {
+      unsigned v[S];
+#pragma unroll
+      for (int u = 0; u < S; ++u) v[u] = keys[base[u] + min(n[u] + h, G) - 1];
+#pragma unroll
+      for (int u = 0; u < S; ++u) n[u] += (n[u] + h <= G && v[u] <= lim[u]) ? h : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < S; ++u) cnt += n[u];
+  }
+#pragma unroll
+  for (int o = kRunsLanes / 2; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, SPEC_WAVE);
+  const int rank = jp + cnt;   // below N: each run counts at most its G keys
+  if (t == 0 && valid && rank < N) {
+    a.sorted[rank] = kp;
+    a.sorted_idx[rank] = (unsigned)p;
+  }
+}
+
 // ---- Theta path and lengths -----------------------------------------------
 
 template <int K>
 struct FinalShared {
-  unsigned sorted[K * kFinalThreads];   // keys; after the search, the per-request counts
-  unsigned sidx[K * kFinalThreads];     // candidate index of each sorted key
+  unsigned cnt[K * kFinalThreads];      // per-request admitted counts (B <= N <= K * kFinalThreads)
   long long wsum[kFinalWaves];
   double wth[kFinalWaves];
   int wm[kFinalWaves];
   int wbm[kFinalWaves];
-  int ncand, mstar;
+  int wn[kFinalWaves];
+  int mstar;
 };
 
-// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.  Called once per
+// kernel (wsum is written without a barrier before it).
 __device__ __forceinline__ long long block_exclusive_sum(long long x, long long* wsum, long long* total) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const long long incl = wave_inclusive_sum_i64(x, lane);
-  __syncthreads();
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   long long before = 0, all = 0;
@@ -217,6 +342,27 @@ __device__ __forceinline__ long long block_exclusive_sum(long long x, long long*
   }
   *total = all;
   return before + incl - x;
+}
+
+// K consecutive words from src + p0 (p0 a multiple of K, src 256-byte aligned), as 16-byte loads
+// when K >= 4; words at or past n read as `fill`.
+template <int K>
+__device__ __forceinline__ void load_words(const unsigned* src, int p0, int n, unsigned fill, unsigned (&w)[K]) {
+  if (p0 + K <= n) {
+    if constexpr (K >= 4) {
+#pragma unroll
+      for (int e = 0; e < K; e += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + p0 + e);
+        w[e] = v.x; w[e + 1] = v.y; w[e + 2] = v.z; w[e + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < K; ++e) w[e] = src[p0 + e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < K; ++e) w[e] = (p0 + e < n) ? src[p0 + e] : fill;
+  }
 }
 
 static_assert(kFinalThreads == kWorklistThreads, "one thread per request in the combined call");
@@ -244,38 +390,26 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
   double sps_m[K];
 #pragma unroll
   for (int e = 0; e < K; ++e) sps_m[e] = (!topk && p0 + e + 1 <= m_cap) ? a.sps[B + p0 + e + 1] : 0.0;
-  if (tid == 0) sh.ncand = 0;
-  // N <= K * kFinalThreads: every thread's loads are issued before the first is stored
-  unsigned ks[K], ko[K];
-#pragma unroll
-  for (int e = 0; e < K; ++e) {
-    const int x = min(tid + e * kFinalThreads, N - 1);
-    ks[e] = a.sorted[x];
-    ko[e] = a.sorted_idx[x];
-  }
-#pragma unroll
-  for (int e = 0; e < K; ++e) {
-    const int x = tid + e * kFinalThreads;
-    if (x < N) {
-      sh.sorted[x] = ks[e];
-      sh.sidx[x] = ko[e];
-    }
-  }
-  __syncthreads();
-
-  unsigned key[K];
+  // this thread's sorted positions p0 .. p0 + K - 1: keys, and candidate indices (fetched with the
+  // keys up to four per thread; the larger tiles fetch them once m* is known: their registers are
+  // taken)
+  constexpr bool kEarlyIdx = K <= 4;
+  unsigned key[K], idx[K];
+  load_words<K>(a.sorted, p0, N, kNoCandidate, key);
+  if constexpr (kEarlyIdx) load_words<K>(a.sorted_idx, p0, N, 0u, idx);
   int nvalid = 0;
 #pragma unroll
-  for (int e = 0; e < K; ++e) {
-    key[e] = (p0 + e < N) ? sh.sorted[p0 + e] : kNoCandidate;
-    nvalid += key[e] != kNoCandidate;
-  }
+  for (int e = 0; e < K; ++e) nvalid += key[e] != kNoCandidate;
   nvalid = wave_sum_i(nvalid);
-  if (lane == 0 && nvalid) atomicAdd(&sh.ncand, nvalid);
+  if (lane == 0) sh.wn[wave] = nvalid;
+  for (int r = tid; r < B; r += kFinalThreads) sh.cnt[r] = 0;
   __syncthreads();
-  const int E = sh.ncand;
+  int E = 0;   // candidates in the pool
+#pragma unroll
+  for (int w = 0; w < kFinalWaves; ++w) E += sh.wn[w];
   long long q[K];
   long long tau_p0 = 0;
+  int mstar;
   if (topk) {
     if (tid == 0) {
       const int cap = *a.capacity_in;
@@ -283,6 +417,8 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     }
 #pragma unroll
     for (int e = 0; e < K; ++e) q[e] = 0;
+    __syncthreads();
+    mstar = sh.mstar;
   } else {
   int m_max = a.budget - B;
   if (m_max > E) m_max = E;
@@ -321,7 +457,8 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     }
   }
   // block reductions: the early stop needs the first break, the global search the first maximum
-  // (arrays of their own, so no barrier separates them from the scan's)
+  // (arrays of their own, so no barrier separates them from the scan's); every thread then
+  // reads the waves' results and finds m* itself
   if (a.mode == SPEC_SCHED_EARLY_STOP) {
     const int wb = wave_min_i(brk);
     if (lane == 0) sh.wm[wave] = wb;
@@ -343,31 +480,27 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int mstar;
-    if (a.mode == SPEC_SCHED_EARLY_STOP) {
-      int b = 0x7fffffff;
-      for (int w = 0; w < kFinalWaves; ++w) b = min(b, sh.wm[w]);
-      mstar = (b == 0x7fffffff) ? m_max : b - 1;
-    } else {
-      double bt = th0;
-      int bm = 0;
-      for (int w = 0; w < kFinalWaves; ++w) {
-        const double t = sh.wth[w];
-        const int m = sh.wbm[w];
-        if (t > bt || (t == bt && m < bm)) {
-          bt = t;
-          bm = m;
-        }
+  if (a.mode == SPEC_SCHED_EARLY_STOP) {
+    int b = 0x7fffffff;
+#pragma unroll
+    for (int w = 0; w < kFinalWaves; ++w) b = min(b, sh.wm[w]);
+    mstar = (b == 0x7fffffff) ? m_max : b - 1;
+  } else {
+    double bt = th0;
+    int bm = 0;
+#pragma unroll
+    for (int w = 0; w < kFinalWaves; ++w) {
+      const double t = sh.wth[w];
+      const int m = sh.wbm[w];
+      if (t > bt || (t == bt && m < bm)) {
+        bt = t;
+        bm = m;
       }
-      mstar = bm;
     }
-    sh.mstar = mstar;
-    if (mstar == 0 && a.theta) a.theta[0] = th0;
+    mstar = bm;
   }
+  if (tid == 0 && mstar == 0 && a.theta) a.theta[0] = th0;
   }  // search for m*
-  __syncthreads();
-  const int mstar = sh.mstar;
   if (tid == 0 && a.capacity_out) a.capacity_out[0] = mstar;
   if (!a.lengths) return;
   // Theta at m*: the thread holding sorted position m*-1 recomputes tau from its chunk
@@ -382,25 +515,27 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(SchedArgs a, Verif
     a.theta[0] = theta_of(t, sp);
   }
   // The admitted candidates are the first m* of the pool sorted by (key, index): each request's
-  // length is its count among them, kept in LDS over the keys' storage (not read after the search).
-  unsigned* cnt = sh.sorted;
-  for (int r = tid; r < B; r += kFinalThreads) cnt[r] = 0;
-  __syncthreads();
+  // length is its count among them.
+  if constexpr (!kEarlyIdx) load_words<K>(a.sorted_idx, p0, N, 0u, idx);
 #pragma unroll
   for (int e = 0; e < K; ++e) {
     const int p = p0 + e;
-    if (p < mstar) atomicAdd(&cnt[sh.sidx[p] / (unsigned)G], 1u);
+    if (p < mstar) atomicAdd(&sh.cnt[idx[e] / (unsigned)G], 1u);
   }
   __syncthreads();
   int my_len = 0;   // request tid's length (B <= kFinalThreads)
   for (int r = tid; r < B; r += kFinalThreads) {
-    const int len = (int)cnt[r];
+    const int len = (int)sh.cnt[r];
     a.lengths[r] = len;
     if (r == tid) my_len = len;
   }
   if constexpr (WL) {
     if constexpr (!kEarlyTokens) worklist_prefetch(v, xp);
-    worklist_from_lengths(wsh, v, my_len, xp);
+    // the schedule admits at most budget - B candidates, so with budget >= B the lengths keep
+    // sum (L_i + 1) within the budget and the work list's token cap drops nothing: it is skipped
+    VerifyArgs vw = v;
+    if (!topk && a.budget >= B) vw.max_items = 0;
+    worklist_from_lengths(wsh, vw, my_len, xp);
   }
 }
 
@@ -440,8 +575,12 @@ static int32_t launch_schedule(SchedArgs a, void* workspace, size_t workspace_by
   a.chunked_idx = reinterpret_cast<unsigned*>(ws + seg);
   a.sorted = reinterpret_cast<unsigned*>(ws + 2 * seg);
   a.sorted_idx = reinterpret_cast<unsigned*>(ws + 3 * seg);
-  hipLaunchKernelGGL(keys_kernel, dim3((n + kKeysThreads - 1) / kKeysThreads), dim3(kKeysThreads), 0, s, a);
-  hipLaunchKernelGGL(rank_kernel, dim3((n + kChunk - 1) / kChunk), dim3(kChunk * kRankParts), 0, s, a);
+  if (runs_sort_fits(B, gamma)) {
+    hipLaunchKernelGGL(runs_rank_kernel, dim3((n + kRunsCand - 1) / kRunsCand), dim3(kRunsThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(keys_kernel, dim3((n + kKeysThreads - 1) / kKeysThreads), dim3(kKeysThreads), 0, s, a);
+    hipLaunchKernelGGL(rank_kernel, dim3((n + kChunk - 1) / kChunk), dim3(kChunk * kRankParts), 0, s, a);
+  }
   if (v) launch_final<true>(a, *v, n, s);
   else launch_final<false>(a, VerifyArgs{}, n, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
