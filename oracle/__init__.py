@@ -12,6 +12,9 @@ from the DSpark pages:
                        bonus token (DSpark paper, §1 and §2.1; appendix
                        counterexample for a length of zero);
   * `verify_greedy` -- the greedy (argmax) verification rule;
+  * `verify_left_to_right` -- the same verification taken position by
+                       position, stopping at the first rejection (§2.1);
+                       what it never reaches is never examined;
   * `schedule`      -- survival products and the budgeted length selector
                        (DSpark paper, §3.2.2; Algorithm 1 as printed in the
                        Chinese translation of the paper);
@@ -47,6 +50,7 @@ from .verification import (  # noqa: F401
     log_probs,
     verify,
     verify_greedy,
+    verify_left_to_right,
 )
 from .overlap import overlap_mass  # noqa: F401
 from .drafting import markov_draft, round_bf16  # noqa: F401

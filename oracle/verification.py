@@ -275,3 +275,128 @@ def verify_greedy(target, draft_tokens, lengths=None, requests=None):
     """Greedy verification of a batch: the greedy rule for every request."""
     B = target.shape[0]
     return verify(target, None, draft_tokens, lengths, np.zeros(B), None, None, requests)
+
+
+def verify_left_to_right(target, draft, draft_tokens, lengths=None, temperature=None, top_k=None, seed=None,
+                         requests=None):
+    """Verification as a walk over the draft positions that stops at the first rejection.
+
+    DSpark paper, §2.1: positions are verified left to right, and the first rejection discards
+    every later draft token whatever it is, so nothing after it is examined.  This function
+    takes those steps one request and one position at a time:
+
+      for k = 0 .. L-1: target row k and draft row k are examined (a row with a NaN, a +inf or
+        no finite logit ends the walk with STATUS_NONFINITE); r_k is computed and tested
+        against u_acc(k) as in `verify`; a rejection ends the walk with n = k and the token
+        drawn from the residual of row pair k;
+      if all L drafts pass, target row L is examined and the token drawn from it.
+
+    Everything `verify` computes for the positions the walk reaches is the same (one row at a
+    time through the same `log_probs`, `uniforms` and `inverse_cdf`).  What differs is what the
+    walk never reaches: accept_prob is NaN for k > n, and a bad row after the first rejection
+    does not set STATUS_NONFINITE.  The argument checks (length, temperature, top-k and the draft
+    tokens of every k < L) are made up front, as in `verify`.  Greedy requests (T = 0) walk the
+    same way with r_k = [x_k == first-occurrence argmax of target row k].
+    """
+    B, G1, V = target.shape
+    G = G1 - 1
+    tok = _as_np(draft_tokens).astype(np.int64).reshape(B, G)
+    Ls = np.full(B, G, dtype=np.int64) if lengths is None else _as_np(lengths).astype(np.int64)
+    Ts = np.ones(B) if temperature is None else _as_np(temperature).astype(np.float64)
+    Ks = np.zeros(B, dtype=np.int64) if top_k is None else _as_np(top_k).astype(np.int64)
+    if seed is None:
+        Ss = np.zeros(B, dtype=np.uint64)
+    else:
+        s = _as_np(seed)
+        Ss = s.view(np.uint64) if s.dtype == np.int64 else s.astype(np.uint64)
+    out = dict(num_accepted=np.zeros(B, dtype=np.int64), out_tokens=np.full((B, G1), -1, dtype=np.int64),
+               accept_prob=np.full((B, G), np.nan), status=np.zeros(B, dtype=np.int64),
+               accept_flags=np.zeros(B, dtype=np.int64), emit_flag=np.zeros(B, dtype=bool),
+               draws=np.zeros(B, dtype=np.int64))
+    idx = range(B) if requests is None else sorted(set(int(i) for i in requests))
+    with np.errstate(all="ignore"):
+        for i in idx:
+            _walk_request(i, target, draft, tok[i], int(Ls[i]), float(Ts[i]), int(Ks[i]), Ss[i], V, G, out)
+    return out
+
+
+def _walk_request(i, target, draft, x, L, T, K, seed, V, G, out):
+    """One request of `verify_left_to_right`; writes its entries of `out`."""
+    # argument checks, made before anything is read (as in `verify`)
+    if L < 0 or L > G:
+        out["status"][i] = STATUS_BAD_LENGTH
+        return
+    st = 0
+    if not (np.isfinite(T) and T >= 0.0):
+        st |= STATUS_BAD_TEMPERATURE
+    if K < 0:
+        st |= STATUS_BAD_TOPK
+    if ((x[:L] < 0) | (x[:L] >= V)).any():
+        st |= STATUS_BAD_TOKEN
+    if st:
+        out["status"][i] = st
+        return
+    greedy = T == 0.0
+    if not greedy and draft is None:
+        raise ValueError("draft logits are required for requests with temperature != 0")
+
+    def row(a, k):
+        return _as_np(a[i, k]).astype(np.float64)
+
+    tokens = out["out_tokens"][i]
+    tested = 0
+    for k in range(L):
+        zt = row(target, k)
+        zd = None if greedy else row(draft, k)
+        if _bad_rows(zt) or (zd is not None and _bad_rows(zd)):
+            out["status"][i] = STATUS_NONFINITE
+            out["accept_prob"][i] = np.nan
+            tokens[:] = -1
+            return
+        if greedy:
+            a_k = int(np.argmax(zt))
+            out["accept_prob"][i, k] = 1.0 if x[k] == a_k else 0.0
+            if x[k] != a_k:
+                out["num_accepted"][i] = k
+                tokens[k] = a_k
+                return
+            tokens[k] = x[k]
+            continue
+        lp_t = log_probs(zt[None], np.array([T]), np.array([K]))[0]
+        lp_d = log_probs(zd[None], np.array([T]), np.array([K]))[0]
+        a, b = lp_t[x[k]], lp_d[x[k]]
+        r = 0.0 if a == -np.inf else (1.0 if b == -np.inf else min(1.0, float(np.exp(a - b))))
+        out["accept_prob"][i, k] = r
+        u_acc, u_emit = uniforms(np.array([seed]), np.array([i]), np.array([k]))
+        tested += 1
+        out["accept_flags"][i] += int(abs(u_acc[0] - r) < FLAG_ACCEPT_WINDOW)
+        if not (u_acc[0] < r):
+            # rejected: the residual of row pair k
+            p_t, p_d = np.exp(lp_t), np.exp(lp_d)
+            w = np.maximum(0.0, p_t - p_d)
+            if not (w.sum() > 0.0):
+                w = p_t
+            t, _, flag = inverse_cdf(w[None], u_emit)
+            out["num_accepted"][i] = k
+            tokens[k] = int(t[0])
+            out["emit_flag"][i] = bool(flag[0])
+            out["draws"][i] = tested + 1
+            return
+        tokens[k] = x[k]
+    # every draft passed: target row L gives the appended token
+    zt = row(target, L)
+    if _bad_rows(zt):
+        out["status"][i] = STATUS_NONFINITE
+        out["accept_prob"][i] = np.nan
+        tokens[:] = -1
+        return
+    out["num_accepted"][i] = L
+    if greedy:
+        tokens[L] = int(np.argmax(zt))
+        return
+    p_t = np.exp(log_probs(zt[None], np.array([T]), np.array([K]))[0])
+    _, u_emit = uniforms(np.array([seed]), np.array([i]), np.array([L]))
+    t, _, flag = inverse_cdf(p_t[None], u_emit)
+    tokens[L] = int(t[0])
+    out["emit_flag"][i] = bool(flag[0])
+    out["draws"][i] = tested + 1
