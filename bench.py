@@ -55,6 +55,10 @@ def parse():
     p.add_argument("--no-sts", action="store_true", help="skip the temperature-scaling measurement")
     p.add_argument("--two-calls", action="store_true",
                    help="scheduler and verification as two calls instead of spec_schedule_verify")
+    p.add_argument("--left-to-right", action="store_true",
+                   help="time the step as spec_schedule_verify with SPEC_VERIFY_LEFT_TO_RIGHT: the walk that stops "
+                        "at the first rejection, streamed in two passes (rows after the first rejection not read)")
+    p.add_argument("--no-ltr", action="store_true", help="skip the left-to-right side measurement")
     p.add_argument("--pool", type=int, default=0,
                    help="worker processes for the pooled CPU-oracle timing (0: the host cores this process "
                         "may use, at most 16, the CPU share of a one-GPU box)")
@@ -109,7 +113,8 @@ def main():
             # scheduler, then verification under its token budget, in one call
             sv.schedule_verify(tgt, drf, w.draft_tokens, w.conf, sps, w.budget, sv.SPEC_SCHED_EARLY_STOP,
                                w.temperature, w.top_k, w.seed, out=fused_out, workspace=ws,
-                               sched_workspace=sch_ws, stream=stream, events=events)
+                               sched_workspace=sch_ws, stream=stream, events=events,
+                               left_to_right=args.left_to_right)
             return
         if w.conf is not None:
             sv.schedule_lengths(w.conf, sps, w.budget, out=sch_out, stream=stream, workspace=sch_ws)
@@ -150,6 +155,10 @@ def main():
     L = sch_out["lengths"].cpu().numpy().astype(np.int64) if w.conf is not None else np.full(B, G)
     positions = int(L.sum())
     rows = int((L + 1).sum()) if greedy else int((2 * L + 1).sum())
+    rows_scheduled = rows
+    ltr = args.left_to_right and w.conf is not None and not greedy and not args.two_calls
+    if ltr:
+        rows = ltr_rows(L, ver_out["num_accepted"].cpu().numpy(), G)
     alg_bytes = rows * V * es
     achieved = alg_bytes / (ms_stream * 1e-3) / 1e9
     # the whole step (scheduler, streaming, acceptance, emit and every kernel boundary) against the
@@ -162,6 +171,10 @@ def main():
     if not args.no_overlap and not greedy:
         overlap = overlap_leg(sv, torch, w, copies, sch_out["lengths"] if w.conf is not None else None, stream)
     async_sched = async_scheduler_leg(sv, torch, w, sps, stream) if w.conf is not None else None
+    walk = None
+    if not args.no_ltr and not ltr and w.conf is not None and not greedy and w.top_k is None \
+            and 256 <= B <= 1024 and G < 64:
+        walk = ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_step, L)
     draft = None
     if not args.no_draft:
         draft = draft_leg(sv, torch, oracle, dev, stream, with_cpu=not args.no_cpu)
@@ -206,7 +219,10 @@ def main():
                                f"schedule (budget {w.budget} tokens, early stop) + verify of the selected "
                                f"prefixes",
                    "B": B, "gamma": G, "V": V, "budget_tokens": w.budget,
-                   "scheduled_positions": positions, "rows_streamed": rows},
+                   "scheduled_positions": positions, "rows_streamed": rows,
+                   "verification": ("left to right, stopping at the first rejection (two streaming passes)"
+                                    if ltr else "every scheduled position"),
+                   "rows_scheduled": rows_scheduled},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "frac_scope": "the row-streaming kernel alone; path_frac covers the whole step",
@@ -218,6 +234,7 @@ def main():
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": achieved / ceiling["gbps"]},
         "cpu_baseline": cpu,
+        "left_to_right": walk,
         "overlap_mass": overlap,
         "async_scheduler": async_sched,
         "draft_sampler": draft,
@@ -279,6 +296,63 @@ def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
         if best is None or gbps > best["gbps"]:
             best = {"gbps": gbps, "ms": ms, "grid": grid, "bytes": nbytes, "kernel": "spec_read_ceiling"}
     return best
+
+
+def ltr_rows(L, n_acc, G, cap=2):
+    """Rows the two passes of a left-to-right call read: positions 0 .. cap-1 of every request (both
+    rows of a draft position, the target row alone at k = L), then positions cap .. L of the requests
+    whose walk passed every one of those (accepted length >= cap; the bench's rows are all valid)."""
+    L = np.asarray(L, dtype=np.int64)
+    n_acc = np.asarray(n_acc, dtype=np.int64)
+    cap = min(cap, G)
+    first = np.minimum(L + 1, cap)
+    rows1 = 2 * np.minimum(first, L) + (first > L)
+    more = (L >= cap) & (n_acc >= cap)
+    return int(rows1.sum() + np.where(more, 2 * (L - cap) + 1, 0).sum())
+
+
+def ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_full, L, reps=100):
+    """The same step as spec_schedule_verify with SPEC_VERIFY_LEFT_TO_RIGHT (DSpark paper §2.1: the
+    walk stops at the first rejection, so rows after it are not read; accept_prob is NaN after it).
+    Two streaming passes, positions 0 and 1 of every request, then positions 2 .. L of the requests
+    whose walk passed both; HIP events around the whole loop and around the two passes of every
+    tenth call.  Not the headline step."""
+    from draft_verification_04_amd.hipevents import HipEvent
+    B, G = w.B, w.gamma
+    dev = w.target.device
+    out = dict(num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+               out_tokens=torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+               accept_prob=torch.empty((B, G), dtype=torch.float32, device=dev),
+               status=torch.empty(B, dtype=torch.int32, device=dev),
+               lengths=torch.empty(B, dtype=torch.int32, device=dev),
+               theta=torch.empty(1, dtype=torch.float64, device=dev),
+               sched_status=torch.empty(B, dtype=torch.int32, device=dev))
+
+    def call(r, events=None):
+        tgt, drf = copies[r % len(copies)]
+        sv.schedule_verify(tgt, drf, w.draft_tokens, w.conf, sps, w.budget, sv.SPEC_SCHED_EARLY_STOP,
+                           w.temperature, w.top_k, w.seed, out=out, workspace=ws, sched_workspace=sch_ws,
+                           stream=stream, events=events, left_to_right=True)
+    for r in range(20):
+        call(r)
+    evs = [(HipEvent(), HipEvent()) if r % 10 == 0 else None for r in range(reps)]
+    e0, e1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for r in range(reps):
+        call(r, evs[r])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    ms_passes = float(np.mean([e[0].elapsed_ms(e[1]) for e in evs if e is not None]))
+    rows = ltr_rows(L, out["num_accepted"].cpu().numpy(), G)
+    row_bytes = w.V * w.elem_bytes
+    pos = int(np.asarray(L).sum())
+    return {"ms_per_step": ms, "positions_per_s": pos / (ms * 1e-3), "vs_full_step": ms_full / ms,
+            "rows_streamed": rows, "rows_scheduled": int((2 * np.asarray(L) + 1).sum()),
+            "ms_two_passes": ms_passes,
+            "gbps_two_passes": rows * row_bytes / (ms_passes * 1e-3) / 1e9,
+            "note": "first pass start to second pass end, the walk kernel between them included"}
 
 
 def overlap_leg(sv, torch, w, copies, lengths, stream, reps=20):

@@ -29,6 +29,7 @@ SPEC_F32 = 0
 SPEC_BF16 = 1
 SPEC_SCHED_EARLY_STOP = 0
 SPEC_SCHED_GLOBAL = 1
+SPEC_VERIFY_LEFT_TO_RIGHT = 0x100
 
 REQ_BAD_TOKEN = 1
 REQ_BAD_TEMPERATURE = 2
@@ -466,10 +467,12 @@ def schedule_verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: tor
                     temperature: Optional[torch.Tensor] = None, top_k: Optional[torch.Tensor] = None,
                     seed: Optional[torch.Tensor] = None, out: Optional[dict] = None,
                     workspace: Optional[torch.Tensor] = None, sched_workspace: Optional[torch.Tensor] = None,
-                    stream=None, events=None) -> dict:
+                    stream=None, events=None, left_to_right: bool = False) -> dict:
     """spec_schedule_verify: the scheduler's lengths, then verification under the budget, in one call.
 
     Inputs as for schedule_lengths (conf, sps, budget_tokens, mode) and verify (no lengths).
+    left_to_right: OR SPEC_VERIFY_LEFT_TO_RIGHT into the mode (the walk that stops at the first
+    rejection; accept_prob NaN after it, rows after it not read).
     Returns dict(lengths, theta, sched_status, num_accepted, out_tokens, accept_prob, status).
     """
     lib = load_library()
@@ -495,7 +498,8 @@ def schedule_verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: tor
     sws = _workspace(int(lib.spec_schedule_workspace_size(B, G)), dev, sched_workspace, mine)
     ev0, ev1 = _events(events)
     code = _launch(stream, mine, lambda sp: lib.spec_schedule_verify(
-        B, G, V, _logit_dtype(target), _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens), int(mode),
+        B, G, V, _logit_dtype(target), _ptr(conf), _ptr(sps), sps.numel(), int(budget_tokens),
+        int(mode) | (SPEC_VERIFY_LEFT_TO_RIGHT if left_to_right else 0),
         _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(temperature), _ptr(top_k), _ptr(seed),
         _ptr(out["lengths"]), _ptr(out.get("theta")), _ptr(out.get("sched_status")), _ptr(out["num_accepted"]),
         _ptr(out["out_tokens"]), _ptr(out.get("accept_prob")), _ptr(out.get("status")),

@@ -167,6 +167,7 @@ struct DecideShared {
   int tacc[SPEC_MAX_GAMMA];
   int x[SPEC_MAX_GAMMA];
   int st, n, L, greedy, bad_t, bad_d;
+  unsigned long long badm_t, badm_d;   // positions 0 .. 63 whose target / draft row is bad
   double R0;
   int table_ok;
   int amb_cnt;
@@ -917,6 +918,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_final_kernel(VerifyArgs a) 
 struct DecideIn {
   uint64_t seed;
   int L, K0, rs, x;
+  int P;   // positions whose rows were streamed (left-to-right calls; else every position)
   float T;
 };
 
@@ -929,6 +931,7 @@ __device__ __forceinline__ DecideIn decide_loads(const VerifyArgs& a, int i) {
   d.K0 = a.top_k ? a.top_k[i] : 0;
   d.rs = a.req_status[i];
   d.x = (lane < a.G) ? a.tokens[(size_t)i * a.G + lane] : 0;
+  d.P = a.ltr ? a.npos[i] : a.G + 1;
   return d;
 }
 
@@ -969,8 +972,8 @@ __device__ __forceinline__ void decide_stats(DecideShared& sh, const VerifyArgs&
   const bool greedy = (T == 0.f);
   const bool topk = !greedy && in.K0 > 0 && in.K0 < V;
   if (wave == 0) {
-    int bad = 0;
-    for (int k = lane; k <= L; k += SPEC_WAVE) {
+    int bad = 0, bad0 = 0;
+    for (int k = lane; k <= L && k < in.P; k += SPEC_WAVE) {
       const Partial* pt = sh.stage + k * nseg;
       if (topk) {
         const RowStat rt = a.rows_t[(size_t)i * (G + 1) + k];
@@ -985,13 +988,18 @@ __device__ __forceinline__ void decide_stats(DecideShared& sh, const VerifyArgs&
         bad |= !(l2t == l2t);
         sh.rt[k] = RowStat{l2t, -INFINITY, 0};
       }
+      if (k == lane) bad0 = bad;
     }
-    const int any = __ballot(bad) != 0ull;
-    if (lane == 0) sh.bad_t = any;
+    const unsigned long long m = __ballot(bad);
+    const unsigned long long m0 = __ballot(bad0);
+    if (lane == 0) {
+      sh.bad_t = m != 0ull;
+      sh.badm_t = m0;
+    }
   } else if (wave == 1) {
-    int bad = 0;
+    int bad = 0, bad0 = 0;
     const Partial* stage_d = sh.stage + (G + 1) * nseg;
-    for (int k = lane; k < L; k += SPEC_WAVE) {
+    for (int k = lane; k < L && k < in.P; k += SPEC_WAVE) {
       if (topk) {
         const AccRec ar = a.acc[(size_t)i * G + k];
         sh.tacc[k] = ar.accept;
@@ -1002,9 +1010,14 @@ __device__ __forceinline__ void decide_stats(DecideShared& sh, const VerifyArgs&
         bad |= !(l2d == l2d);
         sh.rd[k] = RowStat{l2d, -INFINITY, 0};
       }
+      if (k == lane) bad0 = bad;
     }
-    const int any = __ballot(bad) != 0ull;
-    if (lane == 0) sh.bad_d = any;
+    const unsigned long long m = __ballot(bad);
+    const unsigned long long m0 = __ballot(bad0);
+    if (lane == 0) {
+      sh.bad_d = m != 0ull;
+      sh.badm_d = m0;
+    }
   } else if (!greedy && !topk) {
     for (int k = lane; k < L; k += SPEC_WAVE) {
       double ua, ue;
@@ -1034,7 +1047,7 @@ __device__ __forceinline__ void decide_final(DecideShared& sh, const VerifyArgs&
     }
     return;
   }
-  if (sh.bad_t | sh.bad_d) {
+  if (!a.ltr && (sh.bad_t | sh.bad_d)) {
     if (lane == 0) {
       sh.st = SPEC_REQ_NONFINITE;
       sh.n = 0;
@@ -1047,7 +1060,7 @@ __device__ __forceinline__ void decide_final(DecideShared& sh, const VerifyArgs&
   const double c64 = greedy ? 0.0 : kLog2e / (double)T;
   const Partial* stage_d = sh.stage + (G + 1) * nseg;
   int accept = 1;
-  if (lane < L) {   // L <= 64: one position per lane
+  if (lane < L && lane < in.P) {   // L <= 64: one position per lane
     const int k = lane;
     int acc_k;
     double r;
@@ -1064,6 +1077,28 @@ __device__ __forceinline__ void decide_final(DecideShared& sh, const VerifyArgs&
     }
     accept = acc_k;
     sh.accr[k] = r;
+  }
+  if (a.ltr) {
+    // the walk: the first position that is bad or rejected ends it (gamma < 64: one ballot)
+    const unsigned long long badm = sh.badm_t | sh.badm_d;
+    const unsigned long long rej = __ballot(lane < L && lane < in.P && !accept) & ~badm;
+    const int j = rej ? (int)__ffsll((long long)rej) - 1 : SPEC_WAVE;
+    const int b = badm ? (int)__ffsll((long long)badm) - 1 : SPEC_WAVE;
+    if (lane == 0) {
+      if (j < b) {
+        sh.st = 0;
+        sh.n = j;
+      } else if (b < SPEC_WAVE || in.P <= L) {
+        // a bad row the walk reaches (or, never with the first pass's split, a walk that passed
+        // every streamed position without reaching row L)
+        sh.st = SPEC_REQ_NONFINITE;
+        sh.n = 0;
+      } else {
+        sh.st = 0;
+        sh.n = L;
+      }
+    }
+    return;
   }
   const unsigned long long rej = __ballot(lane < L && !accept);
   if (lane == 0) {
@@ -1091,7 +1126,7 @@ __device__ __forceinline__ void early_table(PassShared& ps, DecideShared& sh, co
     return;
   }
   float mmax = -INFINITY;
-  for (int q = lane; q < (L + 1) * nseg; q += SPEC_WAVE) {
+  for (int q = lane; q < min(L + 1, in.P) * nseg; q += SPEC_WAVE) {
     const Partial& p = sh.stage[q];
     if (p.v > 0.0) mmax = fmaxf(mmax, p.m);
   }
@@ -1114,7 +1149,8 @@ __device__ __forceinline__ void decided_outputs(const DecideShared& sh, const Ve
     if (a.status) a.status[i] = st;
     a.num_accepted[i] = st ? 0 : n;
   }
-  if (a.accept_prob && tid < G) a.accept_prob[(size_t)i * G + tid] = (!st && tid < L) ? (float)sh.accr[tid] : NAN;
+  if (a.accept_prob && tid < G)
+    a.accept_prob[(size_t)i * G + tid] = (!st && tid < L && (!a.ltr || tid <= n)) ? (float)sh.accr[tid] : NAN;
   if (tid <= G) {
     int v = -1;
     if (!st && tid < n) v = sh.x[tid];
@@ -1191,6 +1227,88 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
   }
   __syncthreads();
   sample_emit<BF16, kFusedThreads>(fs, a, i, n, e);
+}
+
+// Between the two streaming passes of a left-to-right call: request r walks the positions
+// k < min(L, phase_cap) that the first pass streamed, with the acceptance test the fused emit makes
+// (the same partials, combined in the same order, the same arithmetic), and npos[r] records the
+// positions whose rows are streamed in all: L + 1 when the walk passed every one of them with
+// valid rows and L >= phase_cap (the second pass then streams positions phase_cap .. L), else
+// min(L + 1, phase_cap).  A request with bad arguments gets 0 (the fused emit reports it).
+// One wave per request: lane l loads segment l & 15 of row (l >> 4) & 1 (target, draft) of position
+// l >> 5, so every load of the walk is in flight at once; the first lane of each row combines its
+// segments in segment order, and lane 32 k makes position k's test.
+constexpr int kWalkThreads = 256;
+static_assert(kLtrFirstPass <= 2 && kMaxStreamSegs <= 16, "a wave holds every partial the walk reads");
+
+__global__ __launch_bounds__(kWalkThreads) void ltr_walk_kernel(VerifyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = (int)blockIdx.x * (kWalkThreads / SPEC_WAVE) + ((int)threadIdx.x >> 6);
+  if (r >= a.B) return;   // whole waves
+  const int G = a.G, V = a.V, nseg = a.nseg, cap = a.phase_cap;
+  const int k = lane >> 5, row = (lane >> 4) & 1, sg = lane & 15;
+  const int L = a.lengths[r];
+  const float T = a.temperature[r];
+  const int rs = a.req_status[r];
+  const uint64_t seed = a.seed[r];
+  const int x = a.tokens[(size_t)r * G + min(k, G - 1)];
+  const Partial* ps = (row ? a.part_d : a.part_t) + ((size_t)r * (G + 1) + k) * nseg + min(sg, nseg - 1);
+  const double v = ps->v;
+  const float m = ps->m;
+  const int idx = ps->idx, bad = ps->bad;
+  const float zx = ps->zx;
+  // the row's first lane: combine_sum's and combine_argmax's steps over segments 0 .. nseg-1
+  const int base = lane & ~15;
+  float Mr = -INFINITY, rb = -INFINITY;
+  int bd = 0, ri = 0x7fffffff;
+  for (int t = 0; t < nseg; ++t) {
+    const double vt = __shfl(v, base + t, SPEC_WAVE);
+    const float mt = __shfl(m, base + t, SPEC_WAVE);
+    const int it = __shfl(idx, base + t, SPEC_WAVE);
+    bd |= __shfl(bad, base + t, SPEC_WAVE);
+    if (vt > 0.0) Mr = fmaxf(Mr, mt);
+    const float xt = (float)vt;
+    if (xt > rb) {
+      rb = xt;
+      ri = it;
+    } else if (xt == rb) {
+      ri = min(ri, it);
+    }
+  }
+  double Sr = 0.0;
+  for (int t = 0; t < nseg; ++t) {
+    const double vt = __shfl(v, base + t, SPEC_WAVE);
+    const float mt = __shfl(m, base + t, SPEC_WAVE);
+    if (vt > 0.0) Sr += ldexp(vt, (int)fmaxf(mt - Mr, -2000.f));
+  }
+  const double l2 = (bd || !(Sr > 0.0)) ? __builtin_nan("") : (double)Mr + log2(Sr);
+  const int am = (bd || !(rb > -INFINITY)) ? -1 : ri;
+  // position k's test by lane 32 k, with its draft row's values from lane 32 k + 16
+  const double l2d = __shfl(l2, lane + 16, SPEC_WAVE);
+  const float zxd = __shfl(zx, lane + 16, SPEC_WAVE);
+  const bool valid = L >= 0 && L <= G && rs == 0 && T >= 0.f && T < INFINITY;
+  int ok = 0;
+  if ((lane & 31) == 0 && k < cap && k < L && valid && x >= 0 && x < V) {
+    if (T == 0.f) {
+      ok = am == x;   // -1 (a bad row) never matches
+    } else if (l2 == l2 && l2d == l2d) {
+      const double rr = acceptance_ratio(zx, zxd, kLog2e / (double)T, l2, -INFINITY, l2d, -INFINITY);
+      double ua, ue;
+      verify_uniforms(seed, (uint64_t)r, (uint64_t)k, &ua, &ue);
+      ok = ua < rr;
+    }
+  }
+  const unsigned long long okm = __ballot(ok);
+  if (lane == 0) {
+    bool more = valid && L >= cap;
+    for (int q = 0; q < cap; ++q) more = more && ((okm >> (32 * q)) & 1ull);
+    a.npos[r] = valid ? (more ? L + 1 : min(L + 1, cap)) : 0;
+  }
+}
+
+void launch_ltr_walk(const VerifyArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.B + kWalkThreads / SPEC_WAVE - 1) / (kWalkThreads / SPEC_WAVE));
+  hipLaunchKernelGGL(ltr_walk_kernel, dim3(grid), dim3(kWalkThreads), 0, s, a);
 }
 
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s) {

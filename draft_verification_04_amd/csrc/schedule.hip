@@ -646,12 +646,22 @@ extern "C" int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int
                                         void* event_before, void* event_after) {
   int32_t rc = check_search_args(B, gamma, conf, sps, sps_len, budget_tokens);
   if (rc != SPEC_OK) return rc;
+  const bool ltr = (mode & SPEC_VERIFY_LEFT_TO_RIGHT) != 0;
+  mode &= ~SPEC_VERIFY_LEFT_TO_RIGHT;
   if (mode != SPEC_SCHED_EARLY_STOP && mode != SPEC_SCHED_GLOBAL) return SPEC_ERR_INVALID_ARG;
   if (budget_tokens < 1 || !lengths_out) return SPEC_ERR_INVALID_ARG;
   if (!shape_ok(B, gamma, V, dtype)) return SPEC_ERR_INVALID_ARG;
   if (!target_logits || !draft_logits || !draft_tokens || !temperature || !seed || !num_accepted || !out_tokens)
     return SPEC_ERR_INVALID_ARG;
   if (!aligned16(target_logits) || !aligned16(draft_logits)) return SPEC_ERR_INVALID_ARG;
+  const bool fuse = B <= kFinalThreads;
+  // batches the fused emit serves (every compute unit gets a request) and a streaming workgroup's
+  // threads can cover (two requests each): no work list at all, the streaming workgroups derive
+  // their items from the lengths and the status words the scheduler's last kernel writes
+  const bool derive = fuse && B >= kFuseMinRequests && B <= 2 * kStreamThreads && gamma < SPEC_WAVE;
+  // the left-to-right walk runs where the request-major work list and the fused emit do, on rows
+  // without top-k; a budget below B (requests dropped by the token cap) is left out too
+  if (ltr && (!derive || top_k || budget_tokens < B)) return SPEC_ERR_UNSUPPORTED;
   VerifyArgs v{};
   v.B = B; v.G = gamma; v.V = V; v.greedy_only = 0;
   v.target = target_logits; v.draft = draft_logits; v.tokens = draft_tokens; v.lengths = lengths_out;
@@ -663,13 +673,14 @@ extern "C" int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int
   SchedArgs a{B, gamma, budget_tokens, mode, conf, sps, lengths_out, theta_out, sched_status,
               nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool fuse = B <= kFinalThreads;
-  // batches the fused emit serves (every compute unit gets a request) and a streaming workgroup's
-  // threads can cover (two requests each): no work list at all, the streaming workgroups derive
-  // their items from the lengths and the status words the scheduler's last kernel writes
-  v.derive_items = (fuse && B >= kFuseMinRequests && B <= 2 * kStreamThreads && gamma < SPEC_WAVE) ? 1 : 0;
+  v.derive_items = derive ? 1 : 0;
+  if (ltr) {
+    v.ltr = 1;
+    v.phase_cap = std::min(kLtrFirstPass, gamma);   // B <= 1024 here, as the split kernel needs
+  }
   rc = launch_schedule(a, sched_workspace, sched_workspace_bytes, s, fuse ? &v : nullptr);
   if (rc != SPEC_OK) return rc;
   v.wl_ready = fuse ? 1 : 0;
+  if (ltr) return launch_verify_ltr(v, dtype, s, event_before, event_after);
   return launch_verify_bound(v, dtype, s, event_before, event_after);
 }

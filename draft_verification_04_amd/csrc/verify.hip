@@ -1131,34 +1131,41 @@ __device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float
 }
 
 // Work item g of a call whose work list is request-major (a.derive_items): items[r] holds request
-// r's first item (the items of request r are its positions 0 .. L_r, one after another; a request
-// with no items has the next one's first item) and *nitems the total.  Each wave finds g's request
+// r's first item (the items of request r are its positions k_base, k_base + 1, ... one after
+// another; a request with no items has the next one's first item) and *nitems the total.  Each wave finds g's request
 // by itself: the number of requests whose first item is <= g, counted with ballots over the B <=
 // 2 * kStreamThreads first-item words (one load each, all issued together; no barrier).  Returns
-// false when g lies past the last item.
+// false when g lies past the last item, or, in the second pass of a left-to-right call (k_base > 0),
+// when the request's walk ended before the item's position (npos, loaded with the first-item words).
 __device__ __forceinline__ bool derive_item(const VerifyArgs& a, int g, int& i_out, int& k_out) {
   constexpr int NQ = 2 * kStreamThreads / SPEC_WAVE;   // chunks of 64 requests
   const int lane = threadIdx.x & 63;
   const int B = a.B;
   if (g >= *a.nitems) return false;
-  int o[NQ];
+  const bool second = a.k_base > 0;   // second pass of a left-to-right call: npos read alongside
+  int o[NQ], np[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int r = q * SPEC_WAVE + lane;
     o[q] = (q * SPEC_WAVE < B) ? a.items[min(r, B - 1)] : 0x7fffffff;
+    np[q] = (second && q * SPEC_WAVE < B) ? a.npos[min(r, B - 1)] : 0;
     if (r >= B) o[q] = 0x7fffffff;
   }
   int n = 0;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) n += (int)__popcll(__ballot(o[q] <= g));
   const int i = n - 1;                 // a request with no items shares its first item with the next
-  int first = 0;
+  int first = 0, P = 0;
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
-    if (q == (i >> 6)) first = __builtin_amdgcn_readlane(o[q], i & 63);
+    if (q == (i >> 6)) {
+      first = __builtin_amdgcn_readlane(o[q], i & 63);
+      P = __builtin_amdgcn_readlane(np[q], i & 63);
+    }
   i_out = i;
-  k_out = g - first;
-  return true;
+  k_out = a.k_base + g - first;
+  // the second pass streams a position only when the request's walk reached it
+  return !second || k_out < P;
 }
 
 // log2-sum-exp of a row from its segment partials (fixed segment order); NaN when invalid.
@@ -1381,7 +1388,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t rows_t, rows_d, acc, items, items_x, nitems, req_status, ereq, ranges, amb, part_t, part_d, t_off, d_off,
-      tk_seg, tk_val, tk_ids, total;
+      tk_seg, tk_val, tk_ids, npos, items2, nitems2, total;
 };
 
 // Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
@@ -1412,6 +1419,9 @@ static WsLayout ws_layout(int B, int G, int V, int nseg, bool topk) {
   l.tk_seg = o; o = align256(o + sizeof(TopkSeg) * tk);
   l.tk_val = o; o = align256(o + sizeof(float) * tk * kTopkSegCap);
   l.tk_ids = o; o = align256(o + sizeof(int32_t) * tk * kTopkSegCap);
+  l.npos = o; o = align256(o + sizeof(int32_t) * (size_t)B);
+  l.items2 = o; o = align256(o + sizeof(int32_t) * (size_t)B);
+  l.nitems2 = o; o = align256(o + sizeof(int32_t));
   l.total = o;
   return l;
 }
@@ -1462,6 +1472,9 @@ int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size
   a.tk_seg = reinterpret_cast<TopkSeg*>(w + l.tk_seg);
   a.tk_val = reinterpret_cast<float*>(w + l.tk_val);
   a.tk_ids = reinterpret_cast<int32_t*>(w + l.tk_ids);
+  a.npos = reinterpret_cast<int32_t*>(w + l.npos);
+  a.items2 = reinterpret_cast<int32_t*>(w + l.items2);
+  a.nitems2 = reinterpret_cast<int32_t*>(w + l.nitems2);
   a.nseg_topk = std::min(a.nseg, kTopkSegs);
   if (extra) *extra = w + l.total;
   return SPEC_OK;
@@ -1471,7 +1484,7 @@ size_t workspace_bytes(int B, int G, int V, bool emit, bool topk) {
   return ws_layout(B, G, emit ? V : 1, kMaxStreamSegs, topk).total;   // the largest segment count, fp32 or bf16
 }
 
-void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1) {
+void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1, size_t item_bound) {
   if (a.wl_ready) {
   } else if (!a.flat && a.B <= kWorklistThreads)
     hipLaunchKernelGGL(worklist_small_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
@@ -1479,6 +1492,7 @@ void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0,
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kWorklistThreads), 0, s, a);
   size_t items = (size_t)a.B * (a.G + 1);
   if (a.max_items > 0 && (size_t)a.max_items < items) items = (size_t)a.max_items;
+  if (item_bound > 0 && item_bound < items) items = item_bound;
   const dim3 grid((unsigned)(items * a.nseg)), block(kStreamThreads);
   // The events take the dispatch's own start and end times (no marker packets around it, which
   // would stall the stream before and after the kernel); a failure shows on the caller's event query.
@@ -1516,6 +1530,28 @@ int32_t launch_verify_bound(VerifyArgs a, int dtype, hipStream_t s, void* ev0, v
   const bool fused = !a.greedy_only && a.B >= kFuseMinRequests;
   a.emit_segs = fused ? 1 : std::max(2, std::min(kMaxEmitSegs, (512 + a.B - 1) / a.B));
   if (!fused) launch_combine(a, s);
+  launch_emit(a, dtype == SPEC_BF16, s);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// A left-to-right call (fused emit; the scheduler's last kernel writes both request-major work
+// lists: positions 0 .. phase_cap - 1 of every request, and positions phase_cap .. L): the first
+// streaming pass, the walk over its positions (ltr_walk_kernel: npos), the second pass, whose
+// workgroups of requests whose walk ended exit at once, then the fused emit.  ev0 takes the start
+// of the first pass's dispatch, ev1 the end of the second's.
+int32_t launch_verify_ltr(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1) {
+  a.k_base = 0;
+  launch_statistics(a, dtype, s, ev0, nullptr, (size_t)a.B * (size_t)a.phase_cap);
+  launch_ltr_walk(a, s);
+  VerifyArgs b = a;   // the second pass: the scheduler's second list; items of ended walks exit
+  b.items = a.items2;
+  b.nitems = a.nitems2;
+  b.k_base = a.phase_cap;
+  b.wl_ready = 1;
+  launch_statistics(b, dtype, s, nullptr, ev1, (size_t)a.B * (size_t)(a.G + 1 - a.phase_cap));
+  a.r0 = 0;
+  a.r1 = a.B;
+  a.emit_segs = 1;
   launch_emit(a, dtype == SPEC_BF16, s);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -116,6 +116,13 @@ struct VerifyArgs {
   TopkSeg* tk_seg;     // [B, G+1, 2, kTopkSegs] per (item, target/draft row, segment)
   float* tk_val;       // [B, G+1, 2, kTopkSegs, kTopkSegCap] raw logits at or above each segment's cut
   int32_t* tk_ids;     // same shape: their token ids
+  // left-to-right verification (the walk stops at the first rejection; rows after it are not read)
+  int ltr;             // the decision follows the walk: accept_prob and NONFINITE only up to it
+  int phase_cap;       // > 0: the first streaming pass takes positions 0 .. phase_cap - 1 only
+  int k_base;          // the streaming pass's first position (derived work lists)
+  int32_t* npos;       // [B] positions whose rows were streamed (written between the two passes)
+  int32_t* items2;     // [B] the second pass's request-major list: request r's first item (positions
+  int32_t* nitems2;    //     phase_cap .. L_r of every request with L_r >= phase_cap) and the total
 };
 
 // Index of the TopkSeg record of (request i, position k, row `which` (0 target, 1 draft), segment 0).
@@ -230,6 +237,10 @@ __device__ inline const char* draft_row(const VerifyArgs& a, int i, int k) {
 // Launch the emitted-token kernels (defined in emit.hip).
 void launch_emit(const VerifyArgs& a, int bf16, hipStream_t s);
 
+// Between the two streaming passes of a left-to-right call: the walk over the first pass's positions
+// (defined in emit.hip).
+void launch_ltr_walk(const VerifyArgs& a, hipStream_t s);
+
 // Scratch of worklist_from_lengths.
 struct WorklistShared {
   int cnt[kWorklistThreads / SPEC_WAVE][SPEC_MAX_GAMMA + 1];
@@ -237,6 +248,7 @@ struct WorklistShared {
   int off[SPEC_MAX_GAMMA + 2];
   long long wsum[kWorklistThreads / SPEC_WAVE];
   long long wsum2[kWorklistThreads / SPEC_WAVE];   // a second scan's wave totals
+  long long wsum3[kWorklistThreads / SPEC_WAVE];   // and a third's
 };
 
 constexpr int kWlPre = 16;   // draft tokens per request fetched ahead of the work list
@@ -284,8 +296,9 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
   const int last = (valid && !drop) ? (a.overlap_only ? L - 1 : L) : -1;
   if (a.derive_items) {
     // request-major: request tid's first item is the exclusive prefix of (last + 1) over the
-    // requests before it; the streaming workgroups find their requests from these words
-    const long long n = last + 1;
+    // requests before it (at most phase_cap items each in the first of two passes); the streaming
+    // workgroups find their requests from these words
+    const long long n = (a.phase_cap > 0) ? min(last + 1, a.phase_cap) : last + 1;
     const long long in = wave_inclusive_sum_i64(n, lane);
     if (lane == 63) sh.wsum2[wave] = in;
     __syncthreads();
@@ -297,6 +310,22 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
     }
     if (tid < B) a.items[tid] = (int)(before + in - n);
     if (tid == 0) *a.nitems = (int)total;
+    if (a.phase_cap > 0) {
+      // the second pass of a left-to-right call: positions phase_cap .. L of every request that has
+      // them (a request whose walk ends in the first pass has its workgroups exit at once)
+      const long long n2 = max(last + 1 - a.phase_cap, 0);
+      const long long in2 = wave_inclusive_sum_i64(n2, lane);
+      if (lane == 63) sh.wsum3[wave] = in2;
+      __syncthreads();
+      long long before2 = 0, total2 = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        before2 += (w < wave) ? sh.wsum3[w] : 0;
+        total2 += sh.wsum3[w];
+      }
+      if (tid < B) a.items2[tid] = (int)(before2 + in2 - n2);
+      if (tid == 0) *a.nitems2 = (int)total2;
+    }
     return;
   }
   for (int k = 0; k <= G; ++k) {
@@ -380,11 +409,15 @@ bool aligned16(const void* p);
 int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size_t extra_bytes, char** extra);
 size_t workspace_bytes(int B, int G, int V, bool emit, bool topk);
 // Work list (unless a.wl_ready), then the streaming statistics (events, when given, bracket the
-// streaming kernel).
-void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1);
+// streaming kernel); item_bound > 0 caps the streaming grid's work items further.
+void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0, void* ev1, size_t item_bound = 0);
 // Statistics, acceptance and emit of a call whose workspace is bound (the verify kernels of
 // spec_verify after the argument checks).
 int32_t launch_verify_bound(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1);
+// The same for a left-to-right call (two streaming passes; see verify.hip).
+int32_t launch_verify_ltr(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1);
+// Positions of every request that the first pass of a left-to-right call streams.
+constexpr int kLtrFirstPass = 2;
 // Segment partials -> row records and (with draft tokens) the acceptance test.
 void launch_combine(const VerifyArgs& a, hipStream_t s);
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 /* Call status (return value of every entry point). */
 enum {
@@ -80,6 +80,10 @@ enum {
     SPEC_SCHED_GLOBAL = 1      /* smallest admitted count maximising Theta over the whole
                                   budget (the no-break search of paper §5.2) */
 };
+
+/* Verification order, OR-ed into the mode of spec_schedule_verify (DSpark paper §2.1: positions
+   are verified left to right and the first rejection discards every later draft token). */
+#define SPEC_VERIFY_LEFT_TO_RIGHT 0x100
 
 /* Per-request data status bits (the `status` outputs). */
 #define SPEC_REQ_BAD_TOKEN 1        /* a needed draft token outside [0, V) */
@@ -330,6 +334,20 @@ int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const
  *   Every output equals that of the two calls made one after the other on the
  *   same stream.  With B <= 1024 the scheduler's last kernel also writes the
  *   verify work list (one kernel fewer).
+ * Left to right (mode | SPEC_VERIFY_LEFT_TO_RIGHT; DSpark paper §2.1: positions
+ *   are verified in order and the first rejection discards every later draft):
+ *   each request's verification is the walk k = 0, 1, ... that stops at the
+ *   first rejection n, so rows after n are never examined.  num_accepted,
+ *   out_tokens and the drawn tokens are those of the call without the flag;
+ *   accept_prob is min(1, p_t/p_d) for k <= n (k < L) and NaN after n; status
+ *   NONFINITE is raised only for a bad row the walk reaches (target and draft
+ *   rows 0 .. n, target row L when every draft passed).  The argument checks
+ *   (length, temperature, every draft token k < L) stay up front.  The rows are
+ *   streamed in two passes: positions 0 and 1 of every request, then positions
+ *   2 .. L of the requests whose walk passed both; rows after an earlier
+ *   rejection are not read.  Supported for 256 <= B <= 1024, gamma < 64,
+ *   top_k == NULL and budget_tokens >= B; else SPEC_ERR_UNSUPPORTED before
+ *   anything is enqueued.
  * Errors: those of the two calls, checked before anything is enqueued.
  */
 int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int32_t dtype, const float* conf,

@@ -136,12 +136,14 @@ def admissible_outcomes(h: HostInputs, i: int):
 
 
 def compare_verify(gpu, ref, requests=None, check_prob=True, inputs: Optional[HostInputs] = None,
-                   bound=False):
+                   bound=False, left_to_right=False):
     """Compare GPU outputs with oracle outputs on `requests` (default all).
 
     Unflagged requests must agree bit for bit.  A flagged request that differs must have taken
     an admissible outcome (needs `inputs`; without them a flagged request is only counted).
-    bound=True asserts flagged draws < 1e-4 of draws.
+    bound=True asserts flagged draws < 1e-4 of draws.  left_to_right: the reference is the walk that
+    stops at the first rejection, whose accept_prob is NaN after it; a flagged request that stopped
+    elsewhere is compared on the positions both tested.
     Returns dict(compared, flagged_requests, flagged_draws, draws, mismatches, admissible).
     """
     n_g = to_np(gpu["num_accepted"]).astype(np.int64)
@@ -176,6 +178,14 @@ def compare_verify(gpu, ref, requests=None, check_prob=True, inputs: Optional[Ho
     if check_prob and gpu.get("accept_prob") is not None:
         r_g = to_np(gpu["accept_prob"]).astype(np.float64)[idx]
         r_o = ref["accept_prob"][idx]
+        if left_to_right and (differ & flagged).any():
+            # positions past the shorter of the two walks are left out of the comparison
+            r_g, r_o = r_g.copy(), r_o.copy()
+            G = r_g.shape[1]
+            for j in np.nonzero(differ & flagged)[0]:
+                stop = min(int(n_g[idx][j]), int(ref["num_accepted"][idx][j])) + 1
+                r_g[j, stop:G] = np.nan
+                r_o[j, stop:G] = np.nan
         assert (np.isnan(r_g) == np.isnan(r_o)).all(), "NaN pattern of accept_prob differs"
         m = ~np.isnan(r_o)
         err = np.abs(r_g[m] - r_o[m])
@@ -244,14 +254,18 @@ def request_blocks(B, block=4, requests=None):
     return [idx[a:a + block].tolist() for a in range(0, len(idx), block)]
 
 
-def run_oracle_pooled(h: HostInputs, requests=None, block=4, workers=None):
-    """oracle.verify over `requests` (default every request) of the host inputs h, in blocks of
-    consecutive requests spread over forked workers.  Returns the oracle's dict of arrays."""
+def run_oracle_pooled(h: HostInputs, requests=None, block=4, workers=None, left_to_right=False):
+    """oracle.verify (oracle.verify_left_to_right with left_to_right) over `requests` (default every
+    request) of the host inputs h, in blocks of consecutive requests spread over forked workers.
+    Returns the oracle's dict of arrays."""
     B, G1, _ = h.target.shape
     blocks = request_blocks(B, block, requests)
 
     def fn(blk):
-        if h.draft is None:
+        if left_to_right:
+            res = oracle.verify_left_to_right(h.target, h.draft, h.tokens, h.lengths, h.temperature, h.top_k,
+                                              h.seed, requests=blk)
+        elif h.draft is None:
             res = oracle.verify_greedy(h.target, h.tokens, h.lengths, requests=blk)
         else:
             res = oracle.verify(h.target, h.draft, h.tokens, h.lengths, h.temperature, h.top_k, h.seed,

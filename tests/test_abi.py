@@ -53,7 +53,7 @@ def test_binding_covers_every_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.spec_abi_version() == 2
+    assert lib.spec_abi_version() == 3
     for code, text in ((0, "ok"), (1, "invalid argument"), (2, "workspace"), (3, "unsupported"), (4, "HIP")):
         assert text in lib.spec_status_string(code).decode()
     assert lib.spec_status_string(99).decode() == "unknown status"
@@ -308,6 +308,21 @@ def test_schedule_verify_rejects_bad_arguments(lib):
     assert call(B=2048, G=16, sps_len=10 ** 6) == 3
     assert call() == 2                                         # workspaces
     assert call(vwb=vws - 1) == 2
+    # the left-to-right walk: refused up front outside 256 <= B <= 1024, gamma < 64, rows without
+    # top-k and a budget of at least B (the fake workspaces would be refused after that check)
+    ltr = 0x100
+    assert call(mode=ltr) == 3                                  # B = 4
+    assert call(mode=ltr | 1) == 3
+    assert call(mode=ltr | 2) == 1                              # still a bad scheduler mode
+    big = dict(B=256, G=16, V=1000, sps_len=10 ** 5, budget=2048)
+    assert call(mode=ltr, **big) == 2                           # supported: reaches the workspaces
+    assert call(mode=0, **big) == 2
+    assert call(mode=ltr, **dict(big, budget=255)) == 3         # budget below B
+    assert call(mode=ltr, **dict(big, B=1025, G=8, sps_len=10 ** 6, budget=4096)) == 3
+    assert call(mode=0, **dict(big, B=1025, G=8, sps_len=10 ** 6, budget=4096)) == 2
+    assert call(mode=ltr, **dict(big, G=64, sps_len=10 ** 6)) == 3
+    assert lib.spec_schedule_verify(256, 16, 1000, 1, p, p, 10 ** 5, 2048, ltr, p, p, p, p, p, p, p, None, None,
+                                    p, p, None, None, p, sws, p, vws, None, None, None) == 3   # top_k
 
 
 def test_binding_refuses_host_tensors(lib):
