@@ -508,3 +508,72 @@ def test_maximum_vocabulary_and_block(sv, dtype, V, G):
     s = compare_verify(out, ref, inputs=h)
     print(dtype, V, G, s, flush=True)
     assert (to_np(out["status"]) == 0).all()
+
+
+# ---- a closed form at the workloads' vocabulary size ----
+
+def _closed_form_case(B, G, V, seed):
+    """Target rows uniform (logits 0); draft row k of request i uniform on a set S of |S| tokens
+    (logit 0 there, -inf elsewhere), |S| cycling through V/100, V/2 and V-1; draft tokens from S.
+    Then r_k = |S|/V exactly, and the emitted token has a closed form: after a rejection at n the
+    residual max(0, 1/V - 1/|S|) is 1/V on the complement of S, so the token is the complement token
+    of rank floor(u_emit * (V - |S|)); after full acceptance it is floor(u_emit * V)."""
+    rng = np.random.default_rng(seed)
+    sizes = np.array([V // 100, V // 2, V - 1])
+    target = torch.zeros((B, G + 1, V), dtype=torch.bfloat16)
+    draft = torch.full((B, G, V), float("-inf"), dtype=torch.bfloat16)
+    tokens = np.empty((B, G), dtype=np.int64)
+    sets = {}
+    for i in range(B):
+        s = int(sizes[i % 3])
+        for k in range(G):
+            S = np.sort(rng.choice(V, size=s, replace=False))
+            sets[i, k] = S
+            draft[i, k, torch.from_numpy(S)] = 0.0
+            tokens[i, k] = S[rng.integers(s)]
+    seeds = rng.integers(0, 2**63, B, dtype=np.int64)
+    return target, draft, tokens, sets, seeds, sizes
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B", [256, 40])   # the fused emit, and the split emit of smaller batches
+def test_residual_closed_form_at_large_vocabulary(sv, B):
+    G, V = 3, 151936
+    target, draft, tokens, sets, seeds, sizes = _closed_form_case(B, G, V, 900 + B)
+    print(f"case closed form B={B} G={G} V={V}", flush=True)
+    out = sv.verify(target.to(DEV), draft.to(DEV), torch.from_numpy(tokens.astype(np.int32)).to(DEV), None,
+                    torch.ones(B, device=DEV), None, torch.from_numpy(seeds).to(DEV))
+    torch.cuda.synchronize()
+    n_g, t_g, r_g, st = (to_np(out[k]) for k in ("num_accepted", "out_tokens", "accept_prob", "status"))
+    assert (st == 0).all()
+    flagged = checked = 0
+    kinds = set()
+    for i in range(B):
+        s = int(sizes[i % 3])
+        r = s / V
+        np.testing.assert_allclose(r_g[i], r, rtol=1e-5)
+        u_acc, u_emit = oracle.uniforms(np.full(G + 1, seeds[i], dtype=np.int64).view(np.uint64),
+                                        np.full(G + 1, i), np.arange(G + 1))
+        if (np.abs(u_acc[:G] - r) < oracle.FLAG_ACCEPT_WINDOW).any():
+            flagged += 1
+            continue
+        n = next((k for k in range(G) if not u_acc[k] < r), G)
+        assert n_g[i] == n, (i, n_g[i], n)
+        if n < G:
+            m = V - s
+            pos = u_emit[n] * m
+            want = int(np.setdiff1d(np.arange(V), sets[i, n])[int(np.floor(pos))])
+        else:
+            m = V
+            pos = u_emit[G] * V
+            want = int(np.floor(pos))
+        if abs(pos - round(pos)) < oracle.FLAG_EMIT_WINDOW * m:
+            flagged += 1
+            continue
+        assert t_g[i, n] == want, (i, n, t_g[i, n], want)
+        assert (t_g[i, :n] == tokens[i, :n]).all() and (t_g[i, n + 1:] == -1).all()
+        checked += 1
+        kinds.add((s, n < G))
+    print(f"closed form B={B}: {checked} requests checked, {flagged} flagged, outcomes {sorted(kinds)}", flush=True)
+    assert flagged <= 1 and checked >= B - 1
+    assert any(rej for _, rej in kinds) and any(not rej for _, rej in kinds)

@@ -207,6 +207,58 @@ def test_inverse_cdf_uniform_weights_is_floor():
     assert tok[0] == 3
 
 
+def _complement_inputs(B, G, V, S_size, seed):
+    """Target rows uniform (all logits 0); draft rows uniform on a random set S of S_size tokens
+    (logit 0 there, -inf elsewhere); draft tokens drawn from S."""
+    rng = np.random.default_rng(seed)
+    target = np.zeros((B, G + 1, V), dtype=np.float32)
+    draft = np.full((B, G, V), -np.inf, dtype=np.float32)
+    sets = np.empty((B, G, S_size), dtype=np.int64)
+    tokens = np.empty((B, G), dtype=np.int64)
+    for i in range(B):
+        for k in range(G):
+            S = np.sort(rng.choice(V, size=S_size, replace=False))
+            sets[i, k] = S
+            draft[i, k, S] = 0.0
+            tokens[i, k] = S[rng.integers(S_size)]
+    seeds = rng.integers(0, 2**63, B, dtype=np.int64)
+    return target, draft, tokens, sets, seeds
+
+
+def complement_token(V, S, u):
+    """The closed form of the emitted token when p_t is uniform over V tokens and p_d uniform over
+    S: the residual max(0, 1/V - 1/|S|) is 1/V on the complement of S and 0 on S, so the inverse CDF
+    in ascending order at u lands on the complement token of rank floor(u * (V - |S|))."""
+    comp = np.setdiff1d(np.arange(V), S)
+    return int(comp[int(np.floor(u * len(comp)))])
+
+
+def test_residual_closed_form_at_large_vocabulary():
+    """At V = 151936: uniform target against a draft uniform on |S| = 1519 tokens.  Every acceptance
+    ratio is |S| / V; after a rejection the token is the complement token of rank
+    floor(u * (V - |S|)); after full acceptance it is floor(u * V).  Pins the residual, its
+    normalisation and the inverse CDF at the vocabulary size of the workloads."""
+    B, G, V, Ss = 8, 3, 151936, 1519
+    target, draft, tokens, sets, seeds = _complement_inputs(B, G, V, Ss, 41)
+    out = oracle.verify(target, draft, tokens, seed=seeds)
+    assert (out["status"] == 0).all()
+    r = Ss / V
+    seen_rej = seen_all = 0
+    for i in range(B):
+        n = int(out["num_accepted"][i])
+        np.testing.assert_allclose(out["accept_prob"][i, :], r, rtol=1e-12)
+        u_acc, u_emit = oracle.uniforms(np.full(G + 1, seeds[i], dtype=np.int64).view(np.uint64),
+                                        np.full(G + 1, i), np.arange(G + 1))
+        # the acceptance tests themselves: u < |S| / V
+        first_rej = next((k for k in range(G) if not u_acc[k] < r), G)
+        assert n == first_rej
+        want = complement_token(V, sets[i, n], u_emit[n]) if n < G else int(np.floor(u_emit[G] * V))
+        assert int(out["out_tokens"][i, n]) == want or out["emit_flag"][i]
+        seen_rej += n < G
+        seen_all += n == G
+    assert seen_rej > 0
+
+
 def test_greedy_constructed_mismatch_and_ties():
     rng = np.random.default_rng(16)
     B, G, V = 40, 6, 50
