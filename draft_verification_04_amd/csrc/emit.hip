@@ -1234,7 +1234,8 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
 // (the same partials, combined in the same order, the same arithmetic), and npos[r] records the
 // positions whose rows are streamed in all: L + 1 when the walk passed every one of them with
 // valid rows and L >= phase_cap (the second pass then streams positions phase_cap .. L), else
-// min(L + 1, phase_cap).  A request with bad arguments gets 0 (the fused emit reports it).
+// min(L + 1, phase_cap).  A request with bad arguments gets 0 (the fused emit reports it).  The
+// second pass's item count, L + 1 - phase_cap per request that goes on, is summed into *nwalk.
 // One wave per request: lane l loads segment l & 15 of row (l >> 4) & 1 (target, draft) of position
 // l >> 5, so every load of the walk is in flight at once; the first lane of each row combines its
 // segments in segment order, and lane 32 k makes position k's test.
@@ -1303,6 +1304,7 @@ __global__ __launch_bounds__(kWalkThreads) void ltr_walk_kernel(VerifyArgs a) {
     bool more = valid && L >= cap;
     for (int q = 0; q < cap; ++q) more = more && ((okm >> (32 * q)) & 1ull);
     a.npos[r] = valid ? (more ? L + 1 : min(L + 1, cap)) : 0;
+    if (more) atomicAdd(a.nwalk, L + 1 - cap);   // the second pass's items (cleared by the list)
   }
 }
 

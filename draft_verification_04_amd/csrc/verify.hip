@@ -1135,37 +1135,67 @@ __device__ __forceinline__ void row_partial_sum(StreamShared& sh, float M, float
 // another; a request with no items has the next one's first item) and *nitems the total.  Each wave finds g's request
 // by itself: the number of requests whose first item is <= g, counted with ballots over the B <=
 // 2 * kStreamThreads first-item words (one load each, all issued together; no barrier).  Returns
-// false when g lies past the last item, or, in the second pass of a left-to-right call (k_base > 0),
-// when the request's walk ended before the item's position (npos, loaded with the first-item words).
+// false when g lies past the last item.
 __device__ __forceinline__ bool derive_item(const VerifyArgs& a, int g, int& i_out, int& k_out) {
   constexpr int NQ = 2 * kStreamThreads / SPEC_WAVE;   // chunks of 64 requests
   const int lane = threadIdx.x & 63;
   const int B = a.B;
   if (g >= *a.nitems) return false;
-  const bool second = a.k_base > 0;   // second pass of a left-to-right call: npos read alongside
-  int o[NQ], np[NQ];
+  int o[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int r = q * SPEC_WAVE + lane;
     o[q] = (q * SPEC_WAVE < B) ? a.items[min(r, B - 1)] : 0x7fffffff;
-    np[q] = (second && q * SPEC_WAVE < B) ? a.npos[min(r, B - 1)] : 0;
     if (r >= B) o[q] = 0x7fffffff;
   }
   int n = 0;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) n += (int)__popcll(__ballot(o[q] <= g));
   const int i = n - 1;                 // a request with no items shares its first item with the next
-  int first = 0, P = 0;
+  int first = 0;
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
-    if (q == (i >> 6)) {
-      first = __builtin_amdgcn_readlane(o[q], i & 63);
-      P = __builtin_amdgcn_readlane(np[q], i & 63);
-    }
+    if (q == (i >> 6)) first = __builtin_amdgcn_readlane(o[q], i & 63);
   i_out = i;
   k_out = a.k_base + g - first;
-  // the second pass streams a position only when the request's walk reached it
-  return !second || k_out < P;
+  return true;
+}
+
+// Work item g of the second streaming pass of a left-to-right call: the positions k_base .. npos_r - 1
+// of every request r whose walk went past the first pass, request after request.  Each wave forms
+// the list itself from the B <= 2 * kStreamThreads npos words (one load each, all issued
+// together): per 64 requests a prefix sum of their item counts, and a ballot for the request whose
+// items hold g.  Returns false when g lies past the last item (*nwalk, summed by the walk).
+__device__ __forceinline__ bool derive_item_walk(const VerifyArgs& a, int g, int& i_out, int& k_out) {
+  constexpr int NQ = 2 * kStreamThreads / SPEC_WAVE;   // chunks of 64 requests
+  const int lane = threadIdx.x & 63;
+  const int B = a.B, cap = a.k_base;
+  if (g >= *a.nwalk) return false;
+  int c[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int r = q * SPEC_WAVE + lane;
+    c[q] = (q * SPEC_WAVE < B) ? max(a.npos[min(r, B - 1)] - cap, 0) : 0;
+    if (r >= B) c[q] = 0;
+  }
+  int base = 0, i = -1, first = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (q * SPEC_WAVE >= B) break;
+    const int incl = wave_inclusive_scan(c[q]);
+    const int excl = base + incl - c[q];
+    const unsigned long long m = __ballot(excl <= g && g < excl + c[q]);
+    if (m) {
+      const int l = (int)__ffsll((long long)m) - 1;
+      i = q * SPEC_WAVE + l;
+      first = __builtin_amdgcn_readlane(excl, l);
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (i < 0) return false;
+  i_out = i;
+  k_out = cap + g - first;
+  return true;
 }
 
 // log2-sum-exp of a row from its segment partials (fixed segment order); NaN when invalid.
@@ -1187,7 +1217,11 @@ void stream_kernel(VerifyArgs a) {
   const int g = blockIdx.x / nseg, seg = blockIdx.x - g * nseg;
   int i, k;
   if (a.derive_items) {
-    if (!derive_item(a, g, i, k)) return;
+    if (a.k_base > 0) {
+      if (!derive_item_walk(a, g, i, k)) return;
+    } else if (!derive_item(a, g, i, k)) {
+      return;
+    }
   } else {
     if (g >= *a.nitems) return;
     const int item = a.items[g];
@@ -1388,7 +1422,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t rows_t, rows_d, acc, items, items_x, nitems, req_status, ereq, ranges, amb, part_t, part_d, t_off, d_off,
-      tk_seg, tk_val, tk_ids, npos, items2, nitems2, total;
+      tk_seg, tk_val, tk_ids, npos, nwalk, total;
 };
 
 // Segments per row in the streaming kernel: about 48 KB of logits each, 1 .. 16.
@@ -1420,8 +1454,7 @@ static WsLayout ws_layout(int B, int G, int V, int nseg, bool topk) {
   l.tk_val = o; o = align256(o + sizeof(float) * tk * kTopkSegCap);
   l.tk_ids = o; o = align256(o + sizeof(int32_t) * tk * kTopkSegCap);
   l.npos = o; o = align256(o + sizeof(int32_t) * (size_t)B);
-  l.items2 = o; o = align256(o + sizeof(int32_t) * (size_t)B);
-  l.nitems2 = o; o = align256(o + sizeof(int32_t));
+  l.nwalk = o; o = align256(o + sizeof(int32_t));
   l.total = o;
   return l;
 }
@@ -1473,8 +1506,7 @@ int32_t bind_workspace(VerifyArgs& a, int dtype, void* ws, size_t ws_bytes, size
   a.tk_val = reinterpret_cast<float*>(w + l.tk_val);
   a.tk_ids = reinterpret_cast<int32_t*>(w + l.tk_ids);
   a.npos = reinterpret_cast<int32_t*>(w + l.npos);
-  a.items2 = reinterpret_cast<int32_t*>(w + l.items2);
-  a.nitems2 = reinterpret_cast<int32_t*>(w + l.nitems2);
+  a.nwalk = reinterpret_cast<int32_t*>(w + l.nwalk);
   a.nseg_topk = std::min(a.nseg, kTopkSegs);
   if (extra) *extra = w + l.total;
   return SPEC_OK;
@@ -1534,18 +1566,17 @@ int32_t launch_verify_bound(VerifyArgs a, int dtype, hipStream_t s, void* ev0, v
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
-// A left-to-right call (fused emit; the scheduler's last kernel writes both request-major work
-// lists: positions 0 .. phase_cap - 1 of every request, and positions phase_cap .. L): the first
-// streaming pass, the walk over its positions (ltr_walk_kernel: npos), the second pass, whose
-// workgroups of requests whose walk ended exit at once, then the fused emit.  ev0 takes the start
-// of the first pass's dispatch, ev1 the end of the second's.
+// A left-to-right call (fused emit; the scheduler's last kernel writes the first pass's request-major
+// work list, positions 0 .. phase_cap - 1 of every request): the first streaming pass, the walk over
+// its positions (ltr_walk_kernel: npos), the second pass over positions phase_cap .. npos - 1 (each
+// of its workgroups forms that list from npos), then the fused emit.  The second pass's grid holds
+// the largest list the budget allows; workgroups past the actual list exit at once.  ev0 takes the
+// start of the first pass's dispatch, ev1 the end of the second's.
 int32_t launch_verify_ltr(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1) {
   a.k_base = 0;
   launch_statistics(a, dtype, s, ev0, nullptr, (size_t)a.B * (size_t)a.phase_cap);
   launch_ltr_walk(a, s);
-  VerifyArgs b = a;   // the second pass: the scheduler's second list; items of ended walks exit
-  b.items = a.items2;
-  b.nitems = a.nitems2;
+  VerifyArgs b = a;   // the second pass: its workgroups list the items from npos themselves
   b.k_base = a.phase_cap;
   b.wl_ready = 1;
   launch_statistics(b, dtype, s, nullptr, ev1, (size_t)a.B * (size_t)(a.G + 1 - a.phase_cap));

@@ -121,8 +121,8 @@ struct VerifyArgs {
   int phase_cap;       // > 0: the first streaming pass takes positions 0 .. phase_cap - 1 only
   int k_base;          // the streaming pass's first position (derived work lists)
   int32_t* npos;       // [B] positions whose rows were streamed (written between the two passes)
-  int32_t* items2;     // [B] the second pass's request-major list: request r's first item (positions
-  int32_t* nitems2;    //     phase_cap .. L_r of every request with L_r >= phase_cap) and the total
+  int32_t* nwalk;      // [1] the second pass's item count (cleared by the first pass's list, summed by
+                       //     the walk)
 };
 
 // Index of the TopkSeg record of (request i, position k, row `which` (0 target, 1 draft), segment 0).
@@ -248,7 +248,6 @@ struct WorklistShared {
   int off[SPEC_MAX_GAMMA + 2];
   long long wsum[kWorklistThreads / SPEC_WAVE];
   long long wsum2[kWorklistThreads / SPEC_WAVE];   // a second scan's wave totals
-  long long wsum3[kWorklistThreads / SPEC_WAVE];   // and a third's
 };
 
 constexpr int kWlPre = 16;   // draft tokens per request fetched ahead of the work list
@@ -309,22 +308,9 @@ __device__ inline void worklist_from_lengths(WorklistShared& sh, const VerifyArg
       total += sh.wsum2[w];
     }
     if (tid < B) a.items[tid] = (int)(before + in - n);
-    if (tid == 0) *a.nitems = (int)total;
-    if (a.phase_cap > 0) {
-      // the second pass of a left-to-right call: positions phase_cap .. L of every request that has
-      // them (a request whose walk ends in the first pass has its workgroups exit at once)
-      const long long n2 = max(last + 1 - a.phase_cap, 0);
-      const long long in2 = wave_inclusive_sum_i64(n2, lane);
-      if (lane == 63) sh.wsum3[wave] = in2;
-      __syncthreads();
-      long long before2 = 0, total2 = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        before2 += (w < wave) ? sh.wsum3[w] : 0;
-        total2 += sh.wsum3[w];
-      }
-      if (tid < B) a.items2[tid] = (int)(before2 + in2 - n2);
-      if (tid == 0) *a.nitems2 = (int)total2;
+    if (tid == 0) {
+      *a.nitems = (int)total;
+      if (a.phase_cap > 0) *a.nwalk = 0;   // the walk between the passes adds the second's items
     }
     return;
   }
