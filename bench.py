@@ -158,7 +158,7 @@ def main():
     rows_scheduled = rows
     ltr = args.left_to_right and w.conf is not None and not greedy and not args.two_calls
     if ltr:
-        rows = ltr_rows(L, ver_out["num_accepted"].cpu().numpy(), G)
+        rows = ltr_rows(L, ver_out["num_accepted"].cpu().numpy(), G, ltr_first_pass(G, V, es))
     alg_bytes = rows * V * es
     achieved = alg_bytes / (ms_stream * 1e-3) / 1e9
     # the whole step (scheduler, streaming, acceptance, emit and every kernel boundary) against the
@@ -298,13 +298,20 @@ def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
     return best
 
 
-def ltr_rows(L, n_acc, G, cap=2):
+def ltr_first_pass(G, V, elem_bytes):
+    """Positions the first pass of a left-to-right call streams, by the library's rule: 3, at most
+    gamma, and at most 2 when a row spans more than 8 streaming segments of about 48 KB (the walk
+    kernel's wave holds every partial of the first pass)."""
+    nseg = max(1, min(16, V * elem_bytes // 49152))
+    return min(3, G, 4 if nseg <= 8 else 2)
+
+
+def ltr_rows(L, n_acc, G, cap):
     """Rows the two passes of a left-to-right call read: positions 0 .. cap-1 of every request (both
     rows of a draft position, the target row alone at k = L), then positions cap .. L of the requests
     whose walk passed every one of those (accepted length >= cap; the bench's rows are all valid)."""
     L = np.asarray(L, dtype=np.int64)
     n_acc = np.asarray(n_acc, dtype=np.int64)
-    cap = min(cap, G)
     first = np.minimum(L + 1, cap)
     rows1 = 2 * np.minimum(first, L) + (first > L)
     more = (L >= cap) & (n_acc >= cap)
@@ -314,9 +321,9 @@ def ltr_rows(L, n_acc, G, cap=2):
 def ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_full, L, reps=100):
     """The same step as spec_schedule_verify with SPEC_VERIFY_LEFT_TO_RIGHT (DSpark paper §2.1: the
     walk stops at the first rejection, so rows after it are not read; accept_prob is NaN after it).
-    Two streaming passes, positions 0 and 1 of every request, then positions 2 .. L of the requests
-    whose walk passed both; HIP events around the whole loop and around the two passes of every
-    tenth call.  Not the headline step."""
+    Two streaming passes, positions 0 .. c-1 of every request (c = ltr_first_pass), then positions
+    c .. L of the requests whose walk passed all of them; HIP events around the whole loop and around
+    the two passes of every tenth call.  Not the headline step."""
     from draft_verification_04_amd.hipevents import HipEvent
     B, G = w.B, w.gamma
     dev = w.target.device
@@ -345,7 +352,7 @@ def ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_full, L, reps=100)
     torch.cuda.synchronize()
     ms = e0.elapsed_ms(e1) / reps
     ms_passes = float(np.mean([e[0].elapsed_ms(e[1]) for e in evs if e is not None]))
-    rows = ltr_rows(L, out["num_accepted"].cpu().numpy(), G)
+    rows = ltr_rows(L, out["num_accepted"].cpu().numpy(), G, ltr_first_pass(G, w.V, w.elem_bytes))
     row_bytes = w.V * w.elem_bytes
     pos = int(np.asarray(L).sum())
     return {"ms_per_step": ms, "positions_per_s": pos / (ms * 1e-3), "vs_full_step": ms_full / ms,

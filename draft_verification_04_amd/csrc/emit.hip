@@ -1236,30 +1236,36 @@ __global__ __launch_bounds__(kFusedThreads) void emit_fused_kernel(VerifyArgs a)
 // valid rows and L >= phase_cap (the second pass then streams positions phase_cap .. L), else
 // min(L + 1, phase_cap).  A request with bad arguments gets 0 (the fused emit reports it).  The
 // second pass's item count, L + 1 - phase_cap per request that goes on, is summed into *nwalk.
-// One wave per request: lane l loads segment l & 15 of row (l >> 4) & 1 (target, draft) of position
-// l >> 5, so every load of the walk is in flight at once; the first lane of each row combines its
-// segments in segment order, and lane 32 k makes position k's test.
+// One wave per request: with b = 3 segment bits (rows of at most 8 segments) or 4 (at most 16), lane
+// l loads segment l mod 2^b of row (l >> b) & 1 (target, draft) of position l >> (b + 1), so every
+// load of the walk is in flight at once (phase_cap <= 2^(5 - b) positions); the first lane of each
+// row combines its segments in segment order, and the first lane of each position makes its test.
 constexpr int kWalkThreads = 256;
-static_assert(kLtrFirstPass <= 2 && kMaxStreamSegs <= 16, "a wave holds every partial the walk reads");
+static_assert(kMaxStreamSegs <= 16, "a row's partials fit 16 lanes");
+
+__host__ __device__ inline int walk_seg_bits(int nseg) { return nseg > 8 ? 4 : 3; }
+__host__ __device__ inline int walk_max_cap(int nseg) { return SPEC_WAVE >> (walk_seg_bits(nseg) + 1); }
 
 __global__ __launch_bounds__(kWalkThreads) void ltr_walk_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = (int)blockIdx.x * (kWalkThreads / SPEC_WAVE) + ((int)threadIdx.x >> 6);
   if (r >= a.B) return;   // whole waves
   const int G = a.G, V = a.V, nseg = a.nseg, cap = a.phase_cap;
-  const int k = lane >> 5, row = (lane >> 4) & 1, sg = lane & 15;
+  const int sb = walk_seg_bits(nseg), grp = 1 << sb;
+  const int k = lane >> (sb + 1), row = (lane >> sb) & 1, sg = lane & (grp - 1);
   const int L = a.lengths[r];
   const float T = a.temperature[r];
   const int rs = a.req_status[r];
   const uint64_t seed = a.seed[r];
+  const int kc = min(k, G);   // positions past gamma load position gamma's partials (unused)
   const int x = a.tokens[(size_t)r * G + min(k, G - 1)];
-  const Partial* ps = (row ? a.part_d : a.part_t) + ((size_t)r * (G + 1) + k) * nseg + min(sg, nseg - 1);
+  const Partial* ps = (row ? a.part_d : a.part_t) + ((size_t)r * (G + 1) + kc) * nseg + min(sg, nseg - 1);
   const double v = ps->v;
   const float m = ps->m;
   const int idx = ps->idx, bad = ps->bad;
   const float zx = ps->zx;
   // the row's first lane: combine_sum's and combine_argmax's steps over segments 0 .. nseg-1
-  const int base = lane & ~15;
+  const int base = lane & ~(grp - 1);
   float Mr = -INFINITY, rb = -INFINITY;
   int bd = 0, ri = 0x7fffffff;
   for (int t = 0; t < nseg; ++t) {
@@ -1284,12 +1290,12 @@ __global__ __launch_bounds__(kWalkThreads) void ltr_walk_kernel(VerifyArgs a) {
   }
   const double l2 = (bd || !(Sr > 0.0)) ? __builtin_nan("") : (double)Mr + log2(Sr);
   const int am = (bd || !(rb > -INFINITY)) ? -1 : ri;
-  // position k's test by lane 32 k, with its draft row's values from lane 32 k + 16
-  const double l2d = __shfl(l2, lane + 16, SPEC_WAVE);
-  const float zxd = __shfl(zx, lane + 16, SPEC_WAVE);
+  // position k's test by its first lane, with its draft row's values from the lane grp above
+  const double l2d = __shfl(l2, lane + grp, SPEC_WAVE);
+  const float zxd = __shfl(zx, lane + grp, SPEC_WAVE);
   const bool valid = L >= 0 && L <= G && rs == 0 && T >= 0.f && T < INFINITY;
   int ok = 0;
-  if ((lane & 31) == 0 && k < cap && k < L && valid && x >= 0 && x < V) {
+  if ((lane & (2 * grp - 1)) == 0 && k < cap && k < L && valid && x >= 0 && x < V) {
     if (T == 0.f) {
       ok = am == x;   // -1 (a bad row) never matches
     } else if (l2 == l2 && l2d == l2d) {
@@ -1302,11 +1308,13 @@ __global__ __launch_bounds__(kWalkThreads) void ltr_walk_kernel(VerifyArgs a) {
   const unsigned long long okm = __ballot(ok);
   if (lane == 0) {
     bool more = valid && L >= cap;
-    for (int q = 0; q < cap; ++q) more = more && ((okm >> (32 * q)) & 1ull);
+    for (int q = 0; q < cap; ++q) more = more && ((okm >> (q << (sb + 1))) & 1ull);
     a.npos[r] = valid ? (more ? L + 1 : min(L + 1, cap)) : 0;
     if (more) atomicAdd(a.nwalk, L + 1 - cap);   // the second pass's items (cleared by the list)
   }
 }
+
+int ltr_first_pass(int gamma, int nseg) { return std::min(std::min(kLtrFirstPass, gamma), walk_max_cap(nseg)); }
 
 void launch_ltr_walk(const VerifyArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.B + kWalkThreads / SPEC_WAVE - 1) / (kWalkThreads / SPEC_WAVE));

@@ -676,7 +676,7 @@ extern "C" int32_t spec_schedule_verify(int32_t B, int32_t gamma, int32_t V, int
   v.derive_items = derive ? 1 : 0;
   if (ltr) {
     v.ltr = 1;
-    v.phase_cap = std::min(kLtrFirstPass, gamma);   // B <= 1024 here, as the split kernel needs
+    v.phase_cap = ltr_first_pass(gamma, v.nseg);
   }
   rc = launch_schedule(a, sched_workspace, sched_workspace_bytes, s, fuse ? &v : nullptr);
   if (rc != SPEC_OK) return rc;

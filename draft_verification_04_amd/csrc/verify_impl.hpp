@@ -402,8 +402,10 @@ void launch_statistics(const VerifyArgs& a, int dtype, hipStream_t s, void* ev0,
 int32_t launch_verify_bound(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1);
 // The same for a left-to-right call (two streaming passes; see verify.hip).
 int32_t launch_verify_ltr(VerifyArgs a, int dtype, hipStream_t s, void* ev0, void* ev1);
-// Positions of every request that the first pass of a left-to-right call streams.
-constexpr int kLtrFirstPass = 2;
+// Positions of every request that the first pass of a left-to-right call streams (at most, and at
+// most what the walk kernel's wave holds: ltr_first_pass).
+constexpr int kLtrFirstPass = 3;
+int ltr_first_pass(int gamma, int nseg);
 // Segment partials -> row records and (with draft tokens) the acceptance test.
 void launch_combine(const VerifyArgs& a, hipStream_t s);
 

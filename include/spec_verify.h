@@ -343,9 +343,10 @@ int32_t spec_schedule_lengths(int32_t B, int32_t gamma, const float* conf, const
  *   NONFINITE is raised only for a bad row the walk reaches (target and draft
  *   rows 0 .. n, target row L when every draft passed).  The argument checks
  *   (length, temperature, every draft token k < L) stay up front.  The rows are
- *   streamed in two passes: positions 0 and 1 of every request, then positions
- *   2 .. L of the requests whose walk passed both; rows after an earlier
- *   rejection are not read.  Supported for 256 <= B <= 1024, gamma < 64,
+ *   streamed in two passes: positions 0 .. c-1 of every request (c = 3, at most
+ *   gamma, and 2 when a row spans more than 8 of the streaming kernel's ~48 KB
+ *   segments), then positions c .. L of the requests whose walk passed all of
+ *   them; rows after an earlier rejection are not read.  Supported for 256 <= B <= 1024, gamma < 64,
  *   top_k == NULL and budget_tokens >= B; else SPEC_ERR_UNSUPPORTED before
  *   anything is enqueued.
  * Errors: those of the two calls, checked before anything is enqueued.

@@ -1,6 +1,6 @@
 """GPU: spec_schedule_verify with SPEC_VERIFY_LEFT_TO_RIGHT -- the walk that stops at the first
-rejection (DSpark paper §2.1), streamed in two passes (positions 0 and 1 of every request, then the
-rest of the requests whose walk goes on) -- against oracle.verify_left_to_right on the same inputs
+rejection (DSpark paper §2.1), streamed in two passes (positions 0 .. c-1 of every request, then the
+rest of the requests whose walk goes on; c = 3, or 2 for rows of more than 8 segments) -- against oracle.verify_left_to_right on the same inputs
 and the lengths of the oracle's schedule: accepted lengths and tokens bit for bit except flagged
 draws (each checked to be an admissible outcome), accept_prob within 1e-5 up to the first
 rejection and NaN after it, status words equal.  Bad rows are planted after, at and before the
@@ -71,8 +71,8 @@ def test_full_size_every_request(sv):
     assert (to_np(out["status"]) == 0).all()
     L = h.lengths
     n = ref["num_accepted"]
-    print(f"left-to-right full size: sum L = {int(L.sum())}, rejected before position 2: "
-          f"{int(((n < 2) & (n < L)).sum())}, {s}", flush=True)
+    print(f"left-to-right full size: sum L = {int(L.sum())}, rejected before position 3: "
+          f"{int(((n < 3) & (n < L)).sum())}, {s}", flush=True)
 
 
 @pytest.mark.parametrize("B,gamma,V,mode,seed", [
@@ -81,8 +81,10 @@ def test_full_size_every_request(sv):
     (700, 12, 2003, MODE_GLOBAL, 303),       # two requests per thread
     (1024, 8, 1000, MODE_EARLY_STOP, 304),   # every thread's two requests
     (256, 63, 500, MODE_GLOBAL, 305),        # the most positions the derived items allow
-    (256, 2, 999, MODE_GLOBAL, 306),         # the first pass holds every draft position
+    (256, 3, 999, MODE_GLOBAL, 308),         # the first pass holds every draft position
+    (256, 2, 999, MODE_GLOBAL, 306),         # a first pass of two positions
     (256, 1, 999, MODE_GLOBAL, 307),         # one draft position: a first pass of one position
+    (256, 4, 262144, MODE_EARLY_STOP, 309),  # rows of 10 segments: a first pass of two positions
 ])
 def test_shapes(sv, B, gamma, V, mode, seed):
     w = make_workload("scheduled", DEV, B=B, gamma=gamma, V=V, seed=seed)
@@ -91,7 +93,7 @@ def test_shapes(sv, B, gamma, V, mode, seed):
     out, ref, h, s = _check(sv, w, mode)
     assert (to_np(out["status"]) == 0).all()
     L = h.lengths
-    assert (L >= min(2, gamma)).any()   # some walks reach the second pass
+    assert (L >= min(3, gamma)).any()   # some walks reach the second pass
 
 
 def test_fp32_greedy_rows_and_temperatures(sv):
@@ -114,8 +116,8 @@ def test_bad_rows_after_at_and_before_the_first_rejection(sv):
     plans = []   # (request, row kind, position, value, walk reaches it)
     picks = {
         "after_rej_first_pass": np.nonzero((n == 0) & (L >= 2))[0],      # row 1 streamed, never reached
-        "after_rej_second_pass": np.nonzero((n >= 2) & (n + 1 < L))[0],  # rows past a later rejection
-        "at_rej_second_pass": np.nonzero((n >= 2) & (n < L))[0],
+        "after_rej_second_pass": np.nonzero((n >= 3) & (n + 1 < L))[0],  # rows past a later rejection
+        "at_rej_second_pass": np.nonzero((n >= 3) & (n < L))[0],
         "before_rej": np.nonzero((n >= 1) & (n < L))[0],
         "bonus_row": np.nonzero((n == L) & (L >= 1))[0],
         "bonus_row_first_pass": np.nonzero((n == L) & (L == 1))[0],
