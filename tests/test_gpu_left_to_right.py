@@ -172,3 +172,47 @@ def test_repeat_calls_are_bitwise_identical(sv):
     for k in ("lengths", "num_accepted", "out_tokens", "status"):
         assert torch.equal(a[k], b[k]), k
     assert torch.equal(a["accept_prob"].view(torch.int32), b["accept_prob"].view(torch.int32))
+
+
+def test_nothing_admitted_every_walk_is_the_fresh_token(sv):
+    """A cost table that falls faster than tau can rise: every length is 0, the first pass streams
+    target row 0 alone, no walk goes on (the second pass has no items) and every request draws its
+    fresh token from target row 0."""
+    w = make_workload("scheduled", DEV, B=300, gamma=8, V=2500, seed=341)
+    b = np.arange(len(w.sps), dtype=np.float64)
+    sps = np.zeros_like(b)
+    sps[1:] = 1.0 / b[1:] ** 3
+    w.sps = sps
+    out, ref, h, s = _check(sv, w, MODE_EARLY_STOP)
+    assert (to_np(out["lengths"]) == 0).all() and (to_np(out["status"]) == 0).all()
+    assert (to_np(out["num_accepted"]) == 0).all() and np.isnan(to_np(out["accept_prob"])).all()
+
+
+def test_bad_rows_with_every_thread_holding_two_requests(sv):
+    """B = 1024 (each streaming workgroup's thread covers two requests' first-item words): NaN rows
+    planted in a quarter of the requests, at positions before, at and after their first rejection."""
+    w = make_workload("scheduled", DEV, B=1024, gamma=8, V=1500, seed=351)
+    L_ref, _ = oracle.schedule(w.conf.cpu().numpy(), w.sps, w.budget, MODE_EARLY_STOP)
+    clean = run_oracle_pooled(HostInputs.of_workload(w, L_ref), left_to_right=True)
+    n = clean["num_accepted"]
+    rng = np.random.default_rng(5)
+    planted = []
+    for i in rng.choice(w.B, size=256, replace=False):
+        i = int(i)
+        L = int(L_ref[i])
+        k = int(rng.integers(0, L + 1))
+        kind = "draft" if (k < L and rng.random() < 0.5) else "target"
+        (w.target if kind == "target" else w.draft)[i, k, int(rng.integers(w.V))] = float("nan")
+        planted.append((i, kind, k, k <= int(n[i])))
+    out, ref, h, s = _check(sv, w, MODE_EARLY_STOP)
+    st = to_np(out["status"])
+    for i, kind, k, reached in planted:
+        assert st[i] == (oracle.STATUS_NONFINITE if reached else 0), (i, kind, k, reached)
+    assert any(r for *_, r in planted) and any(not r for *_, r in planted)
+
+
+def test_top_k_is_refused(sv):
+    w = make_workload("scheduled", DEV, B=256, gamma=4, V=1000, seed=361)
+    w.top_k = torch.full((w.B,), 7, dtype=torch.int32, device=DEV)
+    with pytest.raises(sv.SpecError):
+        _run(sv, w)
