@@ -166,15 +166,16 @@ def main():
     path_gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     value = positions / (ms_step * 1e-3)
 
+    # the walk's step right after the headline's, under the same conditions
+    walk = None
+    if not args.no_ltr and not ltr and w.conf is not None and not greedy and w.top_k is None \
+            and 256 <= B <= 1024 and G < 64:
+        walk = ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_step, L)
     ceiling = read_ceiling(sv, torch, copies, alg_bytes, stream)
     overlap = None
     if not args.no_overlap and not greedy:
         overlap = overlap_leg(sv, torch, w, copies, sch_out["lengths"] if w.conf is not None else None, stream)
     async_sched = async_scheduler_leg(sv, torch, w, sps, stream) if w.conf is not None else None
-    walk = None
-    if not args.no_ltr and not ltr and w.conf is not None and not greedy and w.top_k is None \
-            and 256 <= B <= 1024 and G < 64:
-        walk = ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_step, L)
     draft = None
     if not args.no_draft:
         draft = draft_leg(sv, torch, oracle, dev, stream, with_cpu=not args.no_cpu)
@@ -318,7 +319,7 @@ def ltr_rows(L, n_acc, G, cap):
     return int(rows1.sum() + np.where(more, 2 * (L - cap) + 1, 0).sum())
 
 
-def ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_full, L, reps=100):
+def ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_full, L, reps=200):
     """The same step as spec_schedule_verify with SPEC_VERIFY_LEFT_TO_RIGHT (DSpark paper §2.1: the
     walk stops at the first rejection, so rows after it are not read; accept_prob is NaN after it).
     Two streaming passes, positions 0 .. c-1 of every request (c = ltr_first_pass), then positions
@@ -340,7 +341,7 @@ def ltr_leg(sv, torch, w, copies, sps, ws, sch_ws, stream, ms_full, L, reps=100)
         sv.schedule_verify(tgt, drf, w.draft_tokens, w.conf, sps, w.budget, sv.SPEC_SCHED_EARLY_STOP,
                            w.temperature, w.top_k, w.seed, out=out, workspace=ws, sched_workspace=sch_ws,
                            stream=stream, events=events, left_to_right=True)
-    for r in range(20):
+    for r in range(100):   # the headline step's warm-up
         call(r)
     evs = [(HipEvent(), HipEvent()) if r % 10 == 0 else None for r in range(reps)]
     e0, e1 = HipEvent(), HipEvent()
