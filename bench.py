@@ -300,11 +300,9 @@ def read_ceiling(sv, torch, copies, nbytes, stream, reps=20):
 
 
 def ltr_first_pass(G, V, elem_bytes):
-    """Positions the first pass of a left-to-right call streams, by the library's rule: 3, at most
-    gamma, and at most 2 when a row spans more than 8 streaming segments of about 48 KB (the walk
-    kernel's wave holds every partial of the first pass)."""
-    nseg = max(1, min(16, V * elem_bytes // 49152))
-    return min(3, G, 4 if nseg <= 8 else 2)
+    """Positions the first pass of a left-to-right call streams (the library's own answer)."""
+    import draft_verification_04_amd as sv
+    return int(sv.load_library().spec_left_to_right_first_pass(G, V, 1 if elem_bytes == 2 else 0))
 
 
 def ltr_rows(L, n_acc, G, cap):

@@ -64,6 +64,7 @@ EXPORTS = {
                                   _P, _P, _P, _P, _Z, _P, _Z, _P, _P, _P]),
     "spec_philox_uniforms": (_I, [_I, _P, _P, _P, _P, _P, _P]),
     "spec_read_ceiling": (_I, [_P, _Z, _I, _P, _P]),
+    "spec_left_to_right_first_pass": (_I, [_I, _I, _I]),
     "spec_overlap_workspace_size": (_Z, [_I, _I, _I]),
     "spec_schedule_capacity": (_I, [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "spec_schedule_topk": (_I, [_I, _I, _P, _P, _P, _P, _P, _Z, _P]),

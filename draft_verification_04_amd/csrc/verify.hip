@@ -1598,6 +1598,11 @@ static int32_t launch_verify(VerifyArgs a, int dtype, void* ws, size_t ws_bytes,
 
 using namespace spec;
 
+extern "C" int32_t spec_left_to_right_first_pass(int32_t gamma, int32_t V, int32_t dtype) {
+  if (!shape_ok(1, gamma, V, dtype)) return 0;
+  return ltr_first_pass(gamma, stream_segments(V, dtype == SPEC_BF16 ? 2 : 4));
+}
+
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V) {
   if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_V) return 0;
   return workspace_bytes(B, gamma, V, true, true);

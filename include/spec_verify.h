@@ -556,6 +556,18 @@ int32_t spec_sts_apply(int32_t B, int32_t gamma, const float* conf_logits, const
  */
 int32_t spec_read_ceiling(const void* data, size_t bytes, int32_t grid, uint32_t* sink, void* stream);
 
+/*
+ * spec_left_to_right_first_pass -- the number of positions c that the first
+ * streaming pass of a left-to-right spec_schedule_verify call (mode |
+ * SPEC_VERIFY_LEFT_TO_RIGHT) reads for every request, for rows of V logits of
+ * `dtype`: 3, at most gamma, and 2 when a row spans more than 8 of the
+ * streaming kernel's ~48 KB segments.  A host-side query with no device work,
+ * for callers that account for the rows a call reads (the second pass reads
+ * positions c .. L of the requests whose walk passed all c).  0 for arguments
+ * spec_verify would refuse.
+ */
+int32_t spec_left_to_right_first_pass(int32_t gamma, int32_t V, int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

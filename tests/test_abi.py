@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ("spec_verify", "spec_verify_greedy", "spec_schedule_lengths", "spec_verify_workspace_size",
               "spec_schedule_workspace_size", "spec_abi_version", "spec_status_string",
               "spec_philox_uniforms", "spec_verify_profiled", "spec_verify_greedy_workspace_size",
-              "spec_read_ceiling", "spec_verify_flat", "spec_overlap_mass", "spec_schedule_capacity",
+              "spec_read_ceiling", "spec_left_to_right_first_pass", "spec_verify_flat", "spec_overlap_mass", "spec_schedule_capacity",
               "spec_schedule_topk", "spec_draft_markov", "spec_draft_workspace_size", "spec_sts_fit",
               "spec_sts_apply", "spec_sts_workspace_size", "spec_verify_bounded"):
         assert n in names, n
@@ -57,6 +57,18 @@ def test_version_and_strings(lib):
     for code, text in ((0, "ok"), (1, "invalid argument"), (2, "workspace"), (3, "unsupported"), (4, "HIP")):
         assert text in lib.spec_status_string(code).decode()
     assert lib.spec_status_string(99).decode() == "unknown status"
+
+
+def test_left_to_right_first_pass(lib):
+    assert lib.spec_left_to_right_first_pass(16, 151936, 1) == 3     # rows of 6 segments
+    assert lib.spec_left_to_right_first_pass(2, 151936, 1) == 2      # at most gamma
+    assert lib.spec_left_to_right_first_pass(1, 1000, 0) == 1
+    assert lib.spec_left_to_right_first_pass(16, 262144, 1) == 2     # rows of 10 segments
+    assert lib.spec_left_to_right_first_pass(16, 196608, 1) == 3     # exactly 8 segments
+    assert lib.spec_left_to_right_first_pass(16, 196608, 0) == 2     # fp32: 16 segments
+    assert lib.spec_left_to_right_first_pass(0, 1000, 1) == 0
+    assert lib.spec_left_to_right_first_pass(16, 0, 1) == 0
+    assert lib.spec_left_to_right_first_pass(16, 1000, 7) == 0
 
 
 def test_workspace_sizes(lib):
