@@ -29,6 +29,13 @@
 // emit_final_kernel  one workgroup per request: S_t, S_d, range weights
 //   A/S_t - D/S_d (+ recorded tokens), prefix scan, and the range holding
 //   u * W recomputed token by token.  It also writes every output.
+// emit_fused_kernel  one 1024-thread workgroup per request (batches that
+//   give every CU a request): the acceptance decision from the streaming
+//   kernel's segment partials, the pass and the finish above, in one kernel.
+// ltr_walk_kernel  between the two streaming passes of a left-to-right call:
+//   each request's walk over the first pass's positions (DSpark paper §2.1:
+//   the first rejection discards every later draft), so that the second
+//   pass streams only the positions the walk can still reach.
 #include "common.hpp"
 #include "philox.hpp"
 #include "verify_impl.hpp"
