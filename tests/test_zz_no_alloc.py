@@ -91,3 +91,32 @@ def test_too_large_a_shape_is_refused(sv):
     z = torch.zeros(16, dtype=torch.int32, device=DEV)
     p = ctypes.c_void_p(z.data_ptr())
     assert lib.spec_verify_static(B, G, V, 1, p, p, p, None, p, None, p, p, p, None, None, None) == sv.SPEC_ERR_WORKSPACE
+
+
+def test_static_call_replayed_from_a_captured_graph(sv):
+    """The use the entry point is for: spec_verify_static recorded into a HIP graph (no allocation,
+    no memset node: the kernels write every workspace word they read) and replayed three times,
+    with eager work between the replays; every replay's outputs equal the eager call's bit for bit.
+    The first eager call looks the array's address up, outside the capture."""
+    w = make_workload("mixed", DEV, B=256, gamma=6, V=30011, seed=91)   # the fused emit, top-k
+    L = torch.from_numpy(np.random.default_rng(92).integers(0, 7, 256).astype(np.int32)).to(DEV)
+    s = torch.cuda.Stream()
+    ref = _outs(w.B, w.gamma)
+    with torch.cuda.stream(s):
+        assert _static_call(sv, w, L, ref, s) == 0
+    s.synchronize()
+    out = _outs(w.B, w.gamma)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        code = _static_call(sv, w, L, out, s)
+    assert code == 0
+    other = make_workload("mid", DEV, B=16, gamma=3, V=5003, seed=93)
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(-7)                      # a fill kernel, between the replays
+        sv.verify(other.target, other.draft, other.draft_tokens, None, other.temperature, None, other.seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"graph replay {rep}", flush=True)
+        _same(out, ref)
